@@ -1,0 +1,236 @@
+"""Quantise, pack, dequantise, attention logits and top-k search (fp64).
+
+Page "TurboQuant 설명: 무엇인지와 LLM 메모리 6배 절약 구현 방법":
+* "1단계: 무작위 회전 + PolarQuant 압축": normalise the vector, rotate it with
+  Pi, map every rotated coordinate to the nearest Lloyd-Max centroid of the
+  Beta law (a few bits per coordinate).
+* "2단계: QJL 잔차 보정": keep one sign bit per projected coordinate of the
+  stage-1 residual; this removes the inner-product bias without extra memory
+  beyond the bit budget.
+* closing paragraphs of "2단계" and "TurboQuant 구현 방법": logits are computed
+  from the compressed indices against a query rotated once, without
+  reconstructing the keys; reconstructed vectors reach cosine about 0.983 at
+  3 bits.
+* "벤치마크 및 실제 성능" and "응용 분야 및 미래 영향": top-k inner-product search
+  over a quantised database.
+
+Packed format (reading R4 in the design doc; the page fixes no layout):
+* MSE mode: b' = b Lloyd-Max bits per coordinate.  Inner-product ("prod")
+  mode: b' = b - 1 Lloyd-Max bits plus one QJL sign bit per coordinate.
+* ``codes`` row: b' bit planes of ceil(d/8) bytes each; bit i of byte k of
+  plane p is bit p of the index of coordinate 8k + i.
+* ``signs`` row (prod): ceil(d/8) bytes, bit j = [z_j >= 0], z = S r.
+* ``norm``: fp16 (round to nearest even) of ||x||_2; ``rnorm`` (prod): fp16 of
+  gamma = ||u - Pi^T c_hat||_2, the residual norm of the unit vector u.
+* Index of coordinate j: idx_j = #{k : y_j >= t_k}, y = Pi x / ||x||, t the
+  Lloyd-Max boundaries (ties go to the upper cell).
+* Zero vector: u = 0 (so every index is 2^(b'-1)); in prod mode the residual
+  stage is skipped: every sign bit is 1 and gamma = 0.
+
+Reconstruction: x_hat = n16 * (Pi^T c_hat + kappa * gamma16 * S^T s) with
+s = 2 * bit - 1 and kappa = sqrt(pi/2) / m (m = d rows of S).  Because
+E[(s.q) sgn(s.r)] = sqrt(2/pi) <q, r> / ||r|| for s ~ N(0, I), the QJL term
+is an unbiased estimate of <q, r> (reading R6).  Logit: scale * <q, x_hat>.
+"""
+
+import math
+
+import numpy as np
+
+MODE_MSE = 0
+MODE_PROD = 1
+
+
+def lloyd_bits(bits, mode):
+    """Lloyd-Max bits b' for a total budget of ``bits`` per coordinate."""
+    if mode == MODE_MSE:
+        return bits
+    if mode == MODE_PROD:
+        if bits < 2:
+            raise ValueError("inner-product mode needs at least 2 bits")
+        return bits - 1
+    raise ValueError("unknown mode")
+
+
+def qjl_kappa(m):
+    """sqrt(pi/2) / m, the scale of the sign-sketch inner-product estimate."""
+    return math.sqrt(math.pi / 2.0) / m
+
+
+def to_fp16_bits(values):
+    """Round fp64 values to fp16 (nearest even) and return the raw bits.
+
+    Values at or past 65520 round to +inf, as fp16 rounding prescribes.
+    """
+    with np.errstate(over="ignore"):
+        return np.asarray(values, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def from_fp16_bits(bits):
+    """Exact fp64 value of raw fp16 bits."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def plane_bytes(d):
+    return (d + 7) // 8
+
+
+def pack_planes(idx, nbits):
+    """[n, d] indices -> [n, nbits * ceil(d/8)] bit-plane rows (LSB first)."""
+    idx = np.asarray(idx, dtype=np.int64)
+    planes = [np.packbits(((idx >> p) & 1).astype(np.uint8), axis=1, bitorder="little")
+              for p in range(nbits)]
+    return np.concatenate(planes, axis=1)
+
+
+def unpack_planes(codes, nbits, d):
+    """Inverse of ``pack_planes``."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    pb = plane_bytes(d)
+    idx = np.zeros((codes.shape[0], d), dtype=np.int64)
+    for p in range(nbits):
+        bits = np.unpackbits(codes[:, p * pb:(p + 1) * pb], axis=1, bitorder="little")[:, :d]
+        idx |= bits.astype(np.int64) << p
+    return idx
+
+
+def pack_signs(bits):
+    """[n, d] booleans -> [n, ceil(d/8)] bytes (LSB first)."""
+    return np.packbits(np.asarray(bits, dtype=np.uint8), axis=1, bitorder="little")
+
+
+def unpack_signs(signs, d):
+    return np.unpackbits(np.asarray(signs, dtype=np.uint8), axis=1, bitorder="little")[:, :d]
+
+
+def quantize(x, pi, centroids, boundaries, mode, s_mat=None):
+    """Quantise rows of ``x`` (any float dtype, converted exactly to fp64).
+
+    Returns a dict with the packed outputs (``codes``, ``signs``, ``norm``,
+    ``rnorm``) and the intermediate fp64 values the parity rules need
+    (``idx``, ``u_rot`` = y / n, ``z``, ``gamma``).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    n_vec, d = x.shape
+    c = np.asarray(centroids, dtype=np.float64)
+    t = np.asarray(boundaries, dtype=np.float64)
+    nbits = int(round(math.log2(c.size)))
+    norm = np.sqrt(np.einsum("ij,ij->i", x, x))
+    safe = np.where(norm > 0.0, norm, 1.0)
+    u = np.where(norm[:, None] > 0.0, x / safe[:, None], 0.0)
+    u_rot = u @ pi.T                                   # y / n = Pi u
+    idx = np.sum(u_rot[:, :, None] >= t[None, None, :], axis=2)
+    out = {
+        "idx": idx,
+        "u_rot": u_rot,
+        "codes": pack_planes(idx, nbits),
+        "norm": to_fp16_bits(norm),
+        "norm64": norm,
+        "signs": None,
+        "rnorm": None,
+    }
+    if mode == MODE_PROD:
+        if s_mat is None:
+            raise ValueError("inner-product mode needs S")
+        c_hat = c[idx]
+        resid = u - c_hat @ pi                         # u - Pi^T c_hat (rows)
+        gamma = np.sqrt(np.einsum("ij,ij->i", resid, resid))
+        z = resid @ s_mat.T                            # S r
+        bits = z >= 0.0
+        zero = norm == 0.0
+        bits[zero, :] = True
+        gamma = np.where(zero, 0.0, gamma)
+        out.update(signs=pack_signs(bits), rnorm=to_fp16_bits(gamma), gamma=gamma,
+                   z=z, sign_bits=bits)
+    return out
+
+
+def dequantize(codes, norm, pi, centroids, mode, signs=None, rnorm=None, s_mat=None):
+    """x_hat = n16 (Pi^T c_hat + kappa gamma16 S^T s) for every packed row."""
+    c = np.asarray(centroids, dtype=np.float64)
+    d = pi.shape[0]
+    nbits = int(round(math.log2(c.size)))
+    idx = unpack_planes(codes, nbits, d)
+    xhat = c[idx] @ pi
+    if mode == MODE_PROD:
+        s = 2.0 * unpack_signs(signs, d).astype(np.float64) - 1.0
+        gamma = from_fp16_bits(rnorm)
+        xhat = xhat + qjl_kappa(s_mat.shape[0]) * gamma[:, None] * (s @ s_mat)
+    return from_fp16_bits(norm)[:, None] * xhat
+
+
+def logits_dequant(q, codes, norm, pi, centroids, mode, scale, signs=None, rnorm=None,
+                   s_mat=None):
+    """Plain definition: scale * <q_h, x_hat_t> for queries [H, d] and keys [T]."""
+    xhat = dequantize(codes, norm, pi, centroids, mode, signs, rnorm, s_mat)
+    return scale * (np.asarray(q, dtype=np.float64) @ xhat.T)
+
+
+def logits_rotated(q, codes, norm, pi, centroids, mode, scale, signs=None, rnorm=None,
+                   s_mat=None):
+    """Same value through the pre-rotated query (page: query rotated once).
+
+    <q, Pi^T c_hat> = <Pi q, c_hat> and <q, S^T s> = <S q, s>, so the keys are
+    never reconstructed.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    c = np.asarray(centroids, dtype=np.float64)
+    d = pi.shape[0]
+    nbits = int(round(math.log2(c.size)))
+    idx = unpack_planes(codes, nbits, d)
+    q_rot = q @ pi.T                                   # rows of Pi q
+    acc = q_rot @ c[idx].T
+    if mode == MODE_PROD:
+        s = 2.0 * unpack_signs(signs, d).astype(np.float64) - 1.0
+        q_proj = q @ s_mat.T                           # rows of S q
+        gamma = from_fp16_bits(rnorm)
+        acc = acc + qjl_kappa(s_mat.shape[0]) * gamma[None, :] * (q_proj @ s.T)
+    return scale * from_fp16_bits(norm)[None, :] * acc
+
+
+def gqa_logits(q, cache, pi, centroids, mode, scale, s_mat=None, seq_len=None,
+               form="rotated"):
+    """Logits [B, Hq, T] for queries [B, Hq, d] over a packed cache.
+
+    ``cache`` holds ``codes`` [B, Hkv, T, row], ``norm`` [B, Hkv, T] and, in
+    prod mode, ``signs`` / ``rnorm``.  Query head h reads KV head
+    h // (Hq / Hkv).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    bsz, hq, _ = q.shape
+    hkv = cache["codes"].shape[1]
+    t_len = cache["codes"].shape[2] if seq_len is None else seq_len
+    group = hq // hkv
+    fn = logits_rotated if form == "rotated" else logits_dequant
+    out = np.zeros((bsz, hq, t_len))
+    for b in range(bsz):
+        for h in range(hkv):
+            sl = slice(0, t_len)
+            kw = {}
+            if mode == MODE_PROD:
+                kw = dict(signs=cache["signs"][b, h, sl], rnorm=cache["rnorm"][b, h, sl],
+                          s_mat=s_mat)
+            out[b, h * group:(h + 1) * group] = fn(
+                q[b, h * group:(h + 1) * group], cache["codes"][b, h, sl],
+                cache["norm"][b, h, sl], pi, centroids, mode, scale, **kw)
+    return out
+
+
+def topk(scores, k):
+    """Per row, the k largest scores; equal scores go to the smaller index."""
+    scores = np.asarray(scores, dtype=np.float64)
+    cols = np.arange(scores.shape[1])
+    out_idx = np.empty((scores.shape[0], k), dtype=np.int64)
+    for r in range(scores.shape[0]):
+        order = np.lexsort((cols, -scores[r]))
+        out_idx[r] = order[:k]
+    return np.take_along_axis(scores, out_idx, axis=1), out_idx
+
+
+def recall_at_k(found, exact):
+    """Mean over queries of |found ∩ exact| / k."""
+    found = np.asarray(found)
+    exact = np.asarray(exact)
+    k = exact.shape[1]
+    hits = [len(set(f.tolist()) & set(e.tolist())) for f, e in zip(found, exact)]
+    return float(np.mean(hits)) / k
