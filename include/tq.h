@@ -1,0 +1,165 @@
+/* tq.h - C ABI of the MI355X (gfx950) online KV-cache vector quantizer.
+ *
+ * Method: page "TurboQuant 설명: 무엇인지와 LLM 메모리 6배 절약 구현 방법"
+ * (a2a-mcp.org).  Stage 1 ("1단계: 무작위 회전 + PolarQuant 압축"): normalise
+ * each vector, rotate it with one seeded random orthogonal matrix (QR of a
+ * Gaussian matrix), map every rotated coordinate to the nearest Lloyd-Max
+ * centroid of the Beta((d-1)/2,(d-1)/2) law.  Stage 2 ("2단계: QJL 잔차 보정"):
+ * keep the sign of each coordinate of a Gaussian projection of the stage-1
+ * residual, which makes inner products unbiased.  Attention logits are formed
+ * straight from the packed indices against a query rotated once (closing
+ * paragraphs of "2단계" and "TurboQuant 구현 방법").
+ *
+ * Conventions shared by every call
+ *   - Every call returns tq_status (TQ_OK = 0, negative = error) and never
+ *     throws.  Arguments are validated on the host before anything is
+ *     launched; a failed validation launches nothing and writes nothing.
+ *   - Pointers are owned by the caller and borrowed for the duration of the
+ *     call (device pointers until the work queued on `stream` completes).
+ *     Host pointers are plain host memory; device pointers are HIP device
+ *     memory of the current device.
+ *   - Device work is queued asynchronously on the caller's `stream` (a
+ *     hipStream_t passed as void*, NULL = the null stream).  Launch errors
+ *     return TQ_ERR_HIP; faults inside a kernel surface at the caller's next
+ *     synchronisation, as with any HIP launch.
+ *   - tq_attn_logits may take temporary device memory from HIP's
+ *     stream-ordered allocator on `stream`; it is released on the same stream.
+ *   - The library keeps no global state; calls are thread-safe.
+ *
+ * Packed format of one vector (d coordinates, b total bits per coordinate)
+ *   mode TQ_MODE_MSE : b' = b Lloyd-Max bits.     1 <= b <= 4
+ *   mode TQ_MODE_PROD: b' = b - 1 Lloyd-Max bits + 1 QJL sign bit. 2 <= b <= 5
+ *   codes : b' bit planes of d/8 bytes; bit i of byte k of plane p is bit p of
+ *           the index of coordinate 8k+i.  idx_j = #{k : y_j >= t_k} with
+ *           y = Pi x / ||x|| and t the Lloyd-Max boundaries.
+ *   signs : (PROD) d/8 bytes, bit j = [(S r)_j >= 0], r = u - Pi^T c_hat,
+ *           u = x / ||x||.
+ *   norm  : fp16 bits (round to nearest even) of ||x||_2.
+ *   rnorm : (PROD) fp16 bits of gamma = ||r||_2.
+ *   A zero vector gets idx_j = 2^(b'-1), all sign bits 1 and gamma = 0.
+ *   Reconstruction: x_hat = norm * (Pi^T c_hat + sqrt(pi/2)/d * rnorm * S^T s),
+ *   s = 2*sign_bit - 1.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t tq_status;
+
+enum {
+  TQ_OK = 0,
+  TQ_ERR_INVALID = -1,        /* NULL pointer, negative size, bad enum value   */
+  TQ_ERR_UNSUPPORTED = -2,    /* valid request this build has no kernel for    */
+  TQ_ERR_NO_CONVERGENCE = -3, /* Lloyd-Max solver did not settle               */
+  TQ_ERR_HIP = -4             /* a HIP runtime call or launch failed           */
+};
+
+enum { TQ_MODE_MSE = 0, TQ_MODE_PROD = 1 };
+enum { TQ_F32 = 0, TQ_BF16 = 1 };
+enum { TQ_KIND_PI = 0, TQ_KIND_S = 1, TQ_KIND_M = 2 };
+
+/* Lloyd-Max codebook for one coordinate of a rotated unit vector in R^d
+ * (page section "1단계": Beta((d-1)/2,(d-1)/2) law on [-1,1], codebook
+ * precomputed per dimension and bit width; section "TurboQuant 구현 방법").
+ * Host only, fp64.  The density is integrated numerically (composite
+ * Gauss-Legendre in the angle x = sin(phi)); the fixed point is found by
+ * Lloyd iterations followed by Newton steps and is returned exactly
+ * antisymmetric (c[k] = -c[K-1-k], middle boundary 0).
+ *   d            dimension, d >= 3
+ *   bits         Lloyd-Max bits b', 1..8; K = 2^bits levels
+ *   centroids    out, K doubles, ascending
+ *   boundaries   out, K-1 doubles, midpoints of adjacent centroids
+ *   mse_per_coord out (may be NULL): E[(X - Q(X))^2] of one coordinate
+ * Errors: TQ_ERR_INVALID (bad d/bits/NULL), TQ_ERR_NO_CONVERGENCE. */
+tq_status tq_make_codebook(int32_t d, int32_t bits, double *centroids, double *boundaries,
+                           double *mse_per_coord);
+
+/* Seeded random matrices (page sections "1단계" and "2단계").  Host only, fp64,
+ * row-major d x d written to `out`.
+ *   kind TQ_KIND_PI: Pi = Q diag(sign R_ii) (sign(0)=+1) from the QR
+ *                    factorisation G = QR of the Gaussian matrix of stream 0;
+ *                    Haar distributed; the rotation is y = Pi x.
+ *   kind TQ_KIND_S : S, i.i.d. N(0,1) from stream 1 (m = d rows, no QR).
+ *   kind TQ_KIND_M : M = S Pi^T (QJL projection in the rotated domain).
+ * Gaussian stream k of seed s: SplitMix64 started at state 2s+k, uniforms
+ * ((w >> 11) + 0.5) * 2^-53, Box-Muller pairs (cos first), row-major fill.
+ * Errors: TQ_ERR_INVALID (d < 2, d > 4096, bad kind, NULL). */
+tq_status tq_make_rotation(int32_t d, uint64_t seed, int32_t kind, double *out);
+
+/* Device-side parameters of one quantizer: fp32 copies of the host tables.
+ * All pointers are device memory, row-major d x d matrices. */
+typedef struct tq_params {
+  int32_t d;                /* 64, 128 or 256 (see each call for support)  */
+  int32_t bits;             /* total bits per coordinate b                 */
+  int32_t mode;             /* TQ_MODE_MSE or TQ_MODE_PROD                 */
+  int32_t reserved;         /* must be 0                                   */
+  const float *pi;          /* Pi                                          */
+  const float *qjl;         /* S (PROD; may be NULL in MSE)                */
+  const float *qjl_rot;     /* M = S Pi^T (PROD; may be NULL in MSE)       */
+  const float *centroids;   /* 2^b' ascending, antisymmetric               */
+  const float *boundaries;  /* 2^b' - 1 ascending                          */
+} tq_params;
+
+/* Packed vectors, structure of arrays.  Vector i occupies codes[i*b'*d/8 ..],
+ * signs[i*d/8 ..], norm[i], rnorm[i] (device memory). */
+typedef struct tq_packed {
+  uint8_t *codes;
+  uint8_t *signs;           /* PROD only; NULL in MSE                      */
+  uint16_t *norm;
+  uint16_t *rnorm;          /* PROD only; NULL in MSE                      */
+} tq_packed;
+
+/* Quantise n_vec vectors (page sections "1단계" and "2단계"; quantisation on
+ * every cache update: "TurboQuant 구현 방법").
+ *   x            device, n_vec rows of d elements (x_dtype TQ_F32 or
+ *                TQ_BF16), consecutive rows x_row_stride elements apart
+ *   out          packed arrays; vector i is written at index out_offset + i
+ * Supported: d in {64,128} for both modes, d = 256 in MSE mode; b' <= 4.
+ * n_vec == 0 is a no-op.  Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED,
+ * TQ_ERR_HIP. */
+tq_status tq_quantize_kv(const tq_params *p, const void *x, int32_t x_dtype, int64_t n_vec,
+                         int64_t x_row_stride, const tq_packed *out, int64_t out_offset,
+                         void *stream);
+
+/* Attention logits straight from packed keys (page: the query is rotated
+ * once and logits come from the indices without reconstructing the keys).
+ *   q            device [batch][n_q_heads][d], q_dtype TQ_F32 or TQ_BF16
+ *   k            packed keys laid out [batch][n_kv_heads][row_tokens]
+ *   seq_len      valid tokens per (batch, kv head) stream, <= row_tokens
+ *   scale        logit scale (e.g. 1/sqrt(d))
+ *   topk == 0 :  logits  device fp32 [batch][n_q_heads][seq_len],
+ *                logit = scale * <q, x_hat>; topk_idx unused (may be NULL)
+ *   topk  > 0 :  vector search: for every query the topk largest logits,
+ *                ties to the smaller token index, descending; logits is
+ *                fp32 [batch][n_q_heads][topk] and topk_idx int32 of the same
+ *                shape.  Needs seq_len >= topk.
+ * GQA: query head h reads KV head h / (n_q_heads / n_kv_heads); n_q_heads
+ * must be a multiple of n_kv_heads.  Dense logits support d in {128, 256}
+ * and up to 16 query heads per KV head; top-k supports MSE mode, d in
+ * {128, 256}, topk <= 16.  seq_len == 0 is a no-op.
+ * Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED, TQ_ERR_HIP. */
+tq_status tq_attn_logits(const tq_params *p, const void *q, int32_t q_dtype, int32_t batch,
+                         int32_t n_q_heads, int32_t n_kv_heads, const tq_packed *k,
+                         int64_t row_tokens, int64_t seq_len, float scale, float *logits,
+                         int32_t topk, int32_t *topk_idx, void *stream);
+
+/* Reconstruct n_vec vectors (page section "2단계": reconstructed vectors).
+ *   out          device [n_vec][d], out_dtype TQ_F32 or TQ_BF16
+ * Supported: d in {64, 128, 256} MSE, d in {64, 128} PROD.
+ * Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED, TQ_ERR_HIP. */
+tq_status tq_dequantize(const tq_params *p, const tq_packed *k, int64_t n_vec, void *out,
+                        int32_t out_dtype, void *stream);
+
+/* Human-readable name of a status code (static string). */
+const char *tq_status_string(tq_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

@@ -1,0 +1,74 @@
+// Internal launch interface between the C ABI (tq_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq.h"
+
+namespace tqi {
+
+struct QuantizeArgs {
+  const void *x;
+  int64_t n_vec;
+  int64_t x_stride;      // elements
+  const float *pi;
+  const float *m;        // qjl_rot (PROD)
+  const float *centroids;
+  const float *boundaries;
+  uint8_t *codes;
+  uint8_t *signs;
+  uint16_t *norm;
+  uint16_t *rnorm;
+  int64_t out_offset;
+};
+
+hipError_t launch_quantize(int d, int lbits, bool prod, bool in_f32, const QuantizeArgs &a,
+                           hipStream_t s, bool *supported);
+
+struct LogitArgs {
+  const void *q;
+  bool q_f32;
+  int batch, n_q_heads, n_kv_heads;
+  const float *pi;
+  const float *s_mat;    // S (PROD)
+  const float *centroids;
+  const uint8_t *codes;
+  const uint8_t *signs;
+  const uint16_t *norm;
+  const uint16_t *rnorm;
+  int64_t row_tokens, seq_len;
+  float scale;
+  float *logits;
+};
+
+hipError_t launch_logits(int d, int lbits, bool prod, const LogitArgs &a, hipStream_t s,
+                         bool *supported);
+
+struct SearchArgs {
+  LogitArgs base;
+  int topk;
+  int32_t *topk_idx;
+};
+
+hipError_t launch_search(int d, int lbits, const SearchArgs &a, hipStream_t s, bool *supported);
+
+struct DequantArgs {
+  const float *pi;
+  const float *s_mat;
+  const float *centroids;
+  const uint8_t *codes;
+  const uint8_t *signs;
+  const uint16_t *norm;
+  const uint16_t *rnorm;
+  int64_t n_vec;
+  void *out;
+  bool out_f32;
+};
+
+hipError_t launch_dequant(int d, int lbits, bool prod, const DequantArgs &a, hipStream_t s,
+                          bool *supported);
+
+int device_cu_count();
+
+}  // namespace tqi

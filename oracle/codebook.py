@@ -105,27 +105,20 @@ def lloyd_max(d, bits, init=None, tol=1e-15, max_iter=1_000_000):
 
 
 def distortion_per_coord(d, centroids):
-    """E[(X - Q(X))^2] for the nearest-centroid quantiser of ``centroids``."""
+    """E[(X - Q(X))^2] for the nearest-centroid quantiser of ``centroids``.
+
+    Sum over cells of E[X^2; cell] - 2 c mu + c^2 P, with the cell second
+    moments summed in closed form to E[X^2] = 1/d:
+    D = 1/d - sum_k c_k (2 mu_k - c_k P_k).  (At the fixed point mu = c P and
+    this is 1/d - sum P c^2.)  Summing 1/d once avoids the cancellation of
+    per-cell second moments near x = 0.
+    """
     c = np.asarray(centroids, dtype=np.float64)
     t = 0.5 * (c[:-1] + c[1:])
     edges = np.concatenate(([-1.0], t, [1.0]))
     mass = cell_mass(edges[:-1], edges[1:], d)
     mom = cell_first_moment(edges[:-1], edges[1:], d)
-    # E[(X-c)^2 ; cell] = E[X^2; cell] - 2 c mu + c^2 P; at the fixed point
-    # mu = c P, so the total is E[X^2] - sum P c^2.  Use the general form so a
-    # non-converged codebook is still scored correctly.
-    second = _cell_second_moment(edges[:-1], edges[1:], d)
-    return float(np.sum(second - 2.0 * c * mom + c * c * mass))
-
-
-def _cell_second_moment(lo, hi, d):
-    """int_lo^hi x^2 f_d(x) dx.
-
-    Write x^2 = 1 - (1 - x^2) and use (1 - x^2) f_d(x) = (C_d / C_{d+2}) f_{d+2}(x):
-    int x^2 f_d = P_d(cell) - (C_d / C_{d+2}) P_{d+2}(cell).
-    """
-    ratio = math.exp(log_norm_const(d) - log_norm_const(d + 2))
-    return cell_mass(lo, hi, d) - ratio * cell_mass(lo, hi, d + 2)
+    return float(1.0 / d - np.sum(c * (2.0 * mom - c * mass)))
 
 
 @functools.lru_cache(maxsize=None)

@@ -1,0 +1,114 @@
+"""Shared helpers of the GPU parity tests: oracle tables, tolerance rules.
+
+Tolerance rules ("Parity rules"):
+* codes: bit-exact, except coordinates whose oracle value u = y/n lies within
+  1e-5 of a decision boundary; those are counted and must stay under 0.01%
+  of all coordinates.  QJL signs the same with value z/gamma and boundary 0.
+* norm: bit-exact fp16.  rnorm: within one fp16 ulp (the residual is formed
+  from fp32 sums on the device); flips counted.
+* logits from identical (oracle-packed) codes: |l_gpu - l_orc| <= 1e-4 *
+  max(|l_orc|, 1e-2 * |scale| * n16 * ||q||).
+* dequantize: ||x_gpu - x_orc|| <= 1e-4 ||x_orc|| per vector (fp32 output).
+"""
+
+import numpy as np
+import torch
+
+from oracle import codebook as ocb
+from oracle import quantizer as oqz
+from oracle import rotation as orot
+
+CODE_WINDOW = 1e-5
+MAX_MISMATCH_FRAC = 1e-4
+LOGIT_RTOL = 1e-4
+LOGIT_FLOOR = 1e-2
+DEQUANT_RTOL = 1e-4
+
+
+class OracleTables:
+    def __init__(self, d, bits, mode, seed=0):
+        self.d, self.bits, self.mode = d, bits, mode
+        self.lb = oqz.lloyd_bits(bits, mode)
+        self.c, self.t, self.dist = ocb.codebook(d, self.lb)
+        self.pi = orot.haar_rotation(d, seed)
+        self.s = orot.qjl_matrix(d, seed) if mode == oqz.MODE_PROD else None
+
+    def quantize(self, x64):
+        return oqz.quantize(x64, self.pi, self.c, self.t, self.mode, s_mat=self.s)
+
+
+def dev_u16(arr, device):
+    return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(device)
+
+
+def dev_bf16(bits, device):
+    return dev_u16(bits, device).view(torch.bfloat16)
+
+
+def cache_from_oracle(tq, ref, d, bits, mode, device):
+    return tq.PackedKV.from_tensors(
+        d, bits, mode, torch.from_numpy(ref["codes"]).to(device), dev_u16(ref["norm"], device),
+        torch.from_numpy(ref["signs"]).to(device) if ref["signs"] is not None else None,
+        dev_u16(ref["rnorm"], device) if ref["rnorm"] is not None else None)
+
+
+def check_codes(gpu_codes, ref, lb, d, t):
+    """Codes rule; returns (mismatched coordinates, total coordinates)."""
+    g = oqz.unpack_planes(gpu_codes, lb, d)
+    o = ref["idx"]
+    bad = g != o
+    n_bad = int(bad.sum())
+    if n_bad:
+        u = ref["u_rot"][bad]
+        dist = np.min(np.abs(u[:, None] - t[None, :]), axis=1)
+        assert np.all(dist < CODE_WINDOW), "mismatch far from a boundary: %g" % dist.max()
+        assert np.all(np.abs(g[bad] - o[bad]) == 1)
+    assert n_bad <= MAX_MISMATCH_FRAC * o.size, "%d of %d codes differ" % (n_bad, o.size)
+    return n_bad, o.size
+
+
+def check_signs(gpu_signs, ref, d):
+    g = oqz.unpack_signs(gpu_signs, d).astype(bool)
+    o = ref["sign_bits"]
+    bad = g != o
+    n_bad = int(bad.sum())
+    if n_bad:
+        gam = np.where(ref["gamma"] > 0, ref["gamma"], 1.0)
+        zr = np.abs(ref["z"] / gam[:, None])[bad]
+        assert np.all(zr < CODE_WINDOW), "sign mismatch far from 0: %g" % zr.max()
+    assert n_bad <= MAX_MISMATCH_FRAC * o.size, "%d of %d signs differ" % (n_bad, o.size)
+    return n_bad
+
+
+def check_norms(gpu_norm, ref):
+    g = np.asarray(gpu_norm).view(np.uint16)
+    assert np.array_equal(g, ref["norm"]), "norm differs in %d rows" % int(np.sum(g != ref["norm"]))
+
+
+def check_rnorm(gpu_rnorm, ref):
+    g = np.asarray(gpu_rnorm).view(np.uint16).astype(np.int64)
+    o = ref["rnorm"].astype(np.int64)
+    diff = np.abs(g - o)
+    assert diff.max() <= 1, "rnorm off by %d ulp" % diff.max()
+    return int(np.sum(diff > 0))
+
+
+def logit_floor(scale, norm16, q):
+    qn = np.linalg.norm(np.asarray(q, dtype=np.float64), axis=-1)
+    return LOGIT_FLOOR * abs(scale) * oqz.from_fp16_bits(norm16)[None, :] * qn[:, None]
+
+
+def check_logits(gpu, want, scale, norm16, q):
+    """gpu/want: [H, T] for queries q [H, d] over keys with fp16 norms norm16 [T]."""
+    den = np.maximum(np.abs(want), logit_floor(scale, norm16, q))
+    err = np.abs(np.asarray(gpu, dtype=np.float64) - want) / den
+    assert err.max() <= LOGIT_RTOL, "logit error %.3g" % err.max()
+    return float(err.max())
+
+
+def check_dequant(gpu, want):
+    num = np.linalg.norm(np.asarray(gpu, dtype=np.float64) - want, axis=1)
+    den = np.maximum(np.linalg.norm(want, axis=1), 1e-30)
+    rel = np.where(np.linalg.norm(want, axis=1) > 0, num / den, num)
+    assert rel.max() <= DEQUANT_RTOL, "dequant error %.3g" % rel.max()
+    return float(rel.max())

@@ -1,0 +1,237 @@
+"""GPU parity of every entry point against the fp64 oracle (small and ragged sizes).
+
+All inputs are seeded synthetic data; the GPU logit / dequantize / search
+kernels are fed oracle-packed codes, so they are judged on identical codes.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import quantizer as oqz
+from synthetic import bf16_bits, bf16_to_f32, channel_scales, kv_block, search_vectors, tiny_keys_queries
+
+from parity import (OracleTables, cache_from_oracle, check_codes, check_dequant, check_logits,
+                    check_norms, check_rnorm, check_signs, dev_bf16)
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def tq():
+    import online_vector_quantization_amd as pkg
+    return pkg
+
+
+def _keys_bf16(d, n, seed=0, head=0):
+    scales = channel_scales(seed, 2, "k", 2, d) if d == 128 else \
+        np.exp(np.random.default_rng(seed).standard_normal((2, d)))
+    return kv_block(seed, 2, "k", 0, head, n, scales)
+
+
+def _special_rows(x64):
+    x64 = x64.copy()
+    x64[3] = 0.0                     # zero vector
+    x64[7] = 0.0
+    x64[7, 5] = 2.5                  # one nonzero coordinate
+    return x64
+
+
+QUANT_CASES = [(128, b, "mse", dt) for b in (1, 2, 3, 4) for dt in ("bf16", "f32")] + \
+              [(128, b, "prod", dt) for b in (2, 3, 4, 5) for dt in ("bf16", "f32")] + \
+              [(64, 3, "mse", "bf16"), (64, 3, "prod", "bf16"), (64, 5, "prod", "f32"),
+               (256, 2, "mse", "f32"), (256, 4, "mse", "f32"), (256, 3, "mse", "bf16")]
+
+
+@pytest.mark.parametrize("d,bits,mode,dtype", QUANT_CASES)
+def test_quantize_parity(tq, d, bits, mode, dtype):
+    mcode = oqz.MODE_PROD if mode == "prod" else oqz.MODE_MSE
+    n = 1000                                      # 31 full tiles + a ragged one
+    if dtype == "bf16":
+        xb = _keys_bf16(d, n)
+        x64 = _special_rows(bf16_to_f32(xb).astype(np.float64))
+        xb = bf16_bits(x64.astype(np.float32))
+        stride = d + 8                            # rows further apart than d
+        buf = np.zeros((n, stride), dtype=np.uint16)
+        buf[:, :d] = xb
+        xt = dev_bf16(buf, DEV)[:, :d]
+    else:
+        rng = np.random.default_rng(d + bits)
+        x32 = (rng.standard_normal((n, d)) * np.where(np.arange(d) % 37 == 0, 10.0, 1.0)).astype(np.float32)
+        x64 = _special_rows(x32.astype(np.float64))
+        xt = torch.from_numpy(x64.astype(np.float32)).to(DEV)
+    ot = OracleTables(d, bits, mcode)
+    ref = ot.quantize(x64)
+    qz = tq.Quantizer(d, bits, mcode, seed=0, device=DEV)
+    off = 5
+    cache = qz.new_cache(n + 9)
+    qz.quantize(xt, out=cache, out_offset=off)
+    torch.cuda.synchronize()
+    codes = cache.codes.cpu().numpy()[off:off + n]
+    check_codes(codes, ref, ot.lb, d, ot.t)
+    check_norms(cache.norm.cpu().numpy()[off:off + n], ref)
+    assert np.all(oqz.unpack_planes(codes[3:4], ot.lb, d) == 1 << (ot.lb - 1))
+    if mcode == oqz.MODE_PROD:
+        check_signs(cache.signs.cpu().numpy()[off:off + n], ref, d)
+        check_rnorm(cache.rnorm.cpu().numpy()[off:off + n], ref)
+        assert np.all(cache.signs.cpu().numpy()[off + 3] == 0xFF)
+        assert cache.rnorm.cpu().numpy()[off + 3] == 0
+
+
+def _gqa_case(d, bits, mode, bsz, hkv, group, seq, qdtype, seed=0, row_tokens=None):
+    """Oracle-packed cache [bsz, hkv, row_tokens] and queries; returns everything."""
+    mcode = oqz.MODE_PROD if mode == "prod" else oqz.MODE_MSE
+    ot = OracleTables(d, bits, mcode, seed=seed)
+    row_tokens = seq if row_tokens is None else row_tokens
+    rng = np.random.default_rng(100 + seq + group)
+    scales = np.exp(rng.standard_normal((hkv, d)))
+    keys = (rng.standard_normal((bsz, hkv, row_tokens, d)) * scales[None, :, None, :]).astype(np.float32)
+    keys = bf16_to_f32(bf16_bits(keys)).astype(np.float64)
+    q = rng.standard_normal((bsz, hkv * group, d)) * np.repeat(scales, group, axis=0)[None]
+    if qdtype == "bf16":
+        qb = bf16_bits(q.astype(np.float32))
+        q64 = bf16_to_f32(qb).astype(np.float64)
+        qt = dev_bf16(qb, DEV)
+    else:
+        q64 = q.astype(np.float32).astype(np.float64)
+        qt = torch.from_numpy(q64.astype(np.float32)).to(DEV)
+    ref = ot.quantize(keys.reshape(-1, d))
+    return ot, mcode, keys, q64, qt, ref
+
+
+LOGIT_CASES = [
+    # d, bits, mode, batch, kv heads, group, seq, q dtype
+    (128, 3, "prod", 1, 2, 4, 3000, "bf16"),
+    (128, 4, "prod", 2, 2, 4, 2049, "bf16"),
+    (128, 2, "prod", 1, 1, 4, 700, "f32"),
+    (128, 5, "prod", 1, 1, 2, 513, "f32"),
+    (128, 3, "mse", 1, 1, 16, 4096, "f32"),
+    (128, 1, "mse", 1, 3, 1, 1000, "bf16"),
+    (128, 2, "mse", 2, 1, 3, 999, "bf16"),
+    (128, 4, "mse", 1, 2, 8, 1500, "f32"),
+    (128, 3, "prod", 1, 1, 13, 300, "f32"),
+    (256, 2, "mse", 1, 1, 4, 1100, "f32"),
+    (256, 3, "prod", 1, 2, 4, 777, "bf16"),
+]
+
+
+@pytest.mark.parametrize("d,bits,mode,bsz,hkv,group,seq,qdtype", LOGIT_CASES)
+def test_logits_parity(tq, d, bits, mode, bsz, hkv, group, seq, qdtype):
+    ot, mcode, keys, q64, qt, ref = _gqa_case(d, bits, mode, bsz, hkv, group, seq, qdtype)
+    qz = tq.Quantizer(d, bits, mcode, seed=0, device=DEV)
+    cache = cache_from_oracle(tq, ref, d, bits, mcode, DEV)
+    scale = 1.0 / np.sqrt(d)
+    out = qz.attn_logits(qt, cache, n_kv_heads=hkv, seq_len=seq, scale=scale).cpu().numpy()
+    codes = ref["codes"].reshape(bsz, hkv, seq, -1)
+    norm = ref["norm"].reshape(bsz, hkv, seq)
+    for b in range(bsz):
+        for h in range(hkv):
+            kw = {}
+            if mcode == oqz.MODE_PROD:
+                kw = dict(signs=ref["signs"].reshape(bsz, hkv, seq, -1)[b, h],
+                          rnorm=ref["rnorm"].reshape(bsz, hkv, seq)[b, h], s_mat=ot.s)
+            qq = q64[b, h * group:(h + 1) * group]
+            want = oqz.logits_rotated(qq, codes[b, h], norm[b, h], ot.pi, ot.c, mcode, scale, **kw)
+            check_logits(out[b, h * group:(h + 1) * group], want, scale, norm[b, h], qq)
+
+
+def test_logits_row_tokens_capacity(tq):
+    """Streams of capacity 600 holding 437 valid tokens: tokens past seq_len are never read into results."""
+    d, bits, hkv, group, cap, seq = 128, 3, 2, 4, 600, 437
+    ot, mcode, keys, q64, qt, ref = _gqa_case(d, bits, "prod", 1, hkv, group, seq, "bf16", row_tokens=cap)
+    qz = tq.Quantizer(d, bits, mcode, seed=0, device=DEV)
+    cache = cache_from_oracle(tq, ref, d, bits, mcode, DEV)
+    out = qz.attn_logits(qt, cache, n_kv_heads=hkv, seq_len=seq, scale=0.5, row_tokens=cap).cpu().numpy()
+    assert out.shape == (1, hkv * group, seq)
+    for h in range(hkv):
+        sl = slice(h * cap, h * cap + seq)
+        qq = q64[0, h * group:(h + 1) * group]
+        want = oqz.logits_rotated(qq, ref["codes"][sl], ref["norm"][sl], ot.pi, ot.c, mcode, 0.5,
+                                  signs=ref["signs"][sl], rnorm=ref["rnorm"][sl], s_mat=ot.s)
+        check_logits(out[0, h * group:(h + 1) * group], want, 0.5, ref["norm"][sl], qq)
+
+
+DEQ_CASES = [(128, b, "mse") for b in (1, 2, 3, 4)] + [(128, b, "prod") for b in (2, 3, 4, 5)] + \
+            [(64, 3, "mse"), (64, 4, "prod"), (256, 2, "mse"), (256, 4, "mse")]
+
+
+@pytest.mark.parametrize("d,bits,mode", DEQ_CASES)
+def test_dequantize_parity(tq, d, bits, mode):
+    mcode = oqz.MODE_PROD if mode == "prod" else oqz.MODE_MSE
+    ot = OracleTables(d, bits, mcode)
+    n = 777
+    x64 = _special_rows(np.random.default_rng(d * bits).standard_normal((n, d)) * 3.0)
+    ref = ot.quantize(x64)
+    qz = tq.Quantizer(d, bits, mcode, seed=0, device=DEV)
+    cache = cache_from_oracle(tq, ref, d, bits, mcode, DEV)
+    want = oqz.dequantize(ref["codes"], ref["norm"], ot.pi, ot.c, mcode, signs=ref["signs"],
+                          rnorm=ref["rnorm"], s_mat=ot.s)
+    got = qz.dequantize(cache, n).cpu().numpy()
+    check_dequant(got, want)
+    assert np.all(got[3] == 0.0)
+    gotb = qz.dequantize(cache, n, out_dtype=torch.bfloat16).float().cpu().numpy()
+    assert np.max(np.abs(gotb - want)) <= 2.0 ** -8 * np.max(np.abs(want)) + 1e-6
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_search_parity(tq, bits):
+    d, n_db, n_q, k = 256, 20000, 300, 10
+    db = search_vectors(0, "db", 0, n_db)
+    qv = search_vectors(0, "dbq", 0, n_q)
+    ot = OracleTables(d, bits, oqz.MODE_MSE)
+    ref = ot.quantize(db.astype(np.float64))
+    qz = tq.Quantizer(d, bits, oqz.MODE_MSE, seed=0, device=DEV)
+    cache = cache_from_oracle(tq, ref, d, bits, oqz.MODE_MSE, DEV)
+    qt = torch.from_numpy(qv.reshape(1, n_q, d)).to(DEV)
+    vals, idx = qz.search(qt, cache, n_kv_heads=1, seq_len=n_db, topk=k)
+    vals, idx = vals.cpu().numpy()[0], idx.cpu().numpy()[0]
+    scores = oqz.logits_rotated(qv.astype(np.float64), ref["codes"], ref["norm"], ot.pi, ot.c,
+                                oqz.MODE_MSE, 1.0)
+    ov, oi = oqz.topk(scores, k)
+    for r in range(n_q):
+        # returned pairs carry the oracle's score for that index
+        assert np.all(np.abs(vals[r] - scores[r, idx[r]]) <= 1e-4 * np.maximum(np.abs(scores[r, idx[r]]), 1e-3))
+        assert np.all(np.diff(vals[r]) <= 1e-6)
+        # same set, up to near-ties with the oracle's 10th score
+        tol = 1e-4 * max(abs(ov[r, -1]), 1e-3)
+        diff = set(idx[r].tolist()) ^ set(oi[r].tolist())
+        for i in diff:
+            assert abs(scores[r, i] - ov[r, -1]) <= tol, (r, i)
+
+
+def test_end_to_end_quantize_then_logits(tq):
+    """GPU quantise -> GPU logits vs oracle quantise -> oracle logits (keys with identical codes)."""
+    d, bits, seq, group = 128, 3, 2000, 4
+    kb = _keys_bf16(d, seq)
+    k64 = bf16_to_f32(kb).astype(np.float64)
+    ot = OracleTables(d, bits, oqz.MODE_PROD)
+    ref = ot.quantize(k64)
+    qz = tq.Quantizer(d, bits, oqz.MODE_PROD, seed=0, device=DEV)
+    cache = qz.quantize(dev_bf16(kb, DEV))
+    q64 = bf16_to_f32(bf16_bits(np.random.default_rng(5).standard_normal((group, d)).astype(np.float32)))
+    q64 = q64.astype(np.float64)
+    out = qz.attn_logits(torch.from_numpy(q64.astype(np.float32)).reshape(1, group, d).to(DEV), cache,
+                         n_kv_heads=1, seq_len=seq, scale=1 / np.sqrt(d)).cpu().numpy()[0]
+    same = np.all(cache.codes.cpu().numpy() == ref["codes"], axis=1) & \
+        np.all(cache.signs.cpu().numpy() == ref["signs"], axis=1) & \
+        (cache.rnorm.cpu().numpy().view(np.uint16) == ref["rnorm"])
+    assert same.mean() > 0.99
+    want = oqz.logits_rotated(q64, ref["codes"], ref["norm"], ot.pi, ot.c, oqz.MODE_PROD, 1 / np.sqrt(d),
+                              signs=ref["signs"], rnorm=ref["rnorm"], s_mat=ot.s)
+    check_logits(out[:, same], want[:, same], 1 / np.sqrt(d), ref["norm"][same], q64)
+
+
+def test_empty_and_single(tq):
+    qz = tq.Quantizer(128, 3, oqz.MODE_PROD, seed=0, device=DEV)
+    cache = qz.new_cache(4)
+    qz.quantize(torch.zeros((0, 128), dtype=torch.bfloat16, device=DEV), out=cache)
+    x = torch.zeros((1, 128), dtype=torch.float32, device=DEV)
+    x[0, 0] = 1.0
+    qz.quantize(x, out=cache)
+    lg = qz.attn_logits(torch.ones((1, 4, 128), device=DEV), cache, n_kv_heads=1, seq_len=1, scale=1.0)
+    torch.cuda.synchronize()
+    assert lg.shape == (1, 4, 1) and torch.isfinite(lg).all()
+    empty = qz.attn_logits(torch.ones((1, 4, 128), device=DEV), cache, n_kv_heads=1, seq_len=0, scale=1.0)
+    assert empty.shape == (1, 4, 0)
