@@ -22,23 +22,31 @@
  *     hipStream_t passed as void*, NULL = the null stream).  Launch errors
  *     return TQ_ERR_HIP; faults inside a kernel surface at the caller's next
  *     synchronisation, as with any HIP launch.
- *   - tq_attn_logits may take temporary device memory from HIP's
- *     stream-ordered allocator on `stream`; it is released on the same stream.
- *   - The library keeps no global state; calls are thread-safe.
+ *   - tq_attn_logits needs device scratch memory (query tables, partial top-k
+ *     lists).  The library keeps one scratch buffer per (device, stream) pair
+ *     between calls: the first call on a stream, or a call that needs more,
+ *     synchronises that stream and allocates with hipMalloc; the buffer lives
+ *     until the process ends.  Work on one stream runs in order, so calls on
+ *     the same stream share their buffer safely; other streams get their own.
+ *   - Apart from that cache the library keeps no state; calls are thread-safe.
  *
  * Packed format of one vector (d coordinates, b total bits per coordinate)
  *   mode TQ_MODE_MSE : b' = b Lloyd-Max bits.     1 <= b <= 4
  *   mode TQ_MODE_PROD: b' = b - 1 Lloyd-Max bits + 1 QJL sign bit. 2 <= b <= 5
- *   codes : b' bit planes of d/8 bytes; bit i of byte k of plane p is bit p of
- *           the index of coordinate 8k+i.  idx_j = #{k : y_j >= t_k} with
- *           y = Pi x / ||x|| and t the Lloyd-Max boundaries.
- *   signs : (PROD) d/8 bytes, bit j = [(S r)_j >= 0], r = u - Pi^T c_hat,
- *           u = x / ||x||.
+ *   record: every coordinate carries b bits: bits 0..b'-1 hold its Lloyd-Max
+ *           index idx_j = #{k : y_j >= t_k} (y = Pi x / ||x||, t the Lloyd-Max
+ *           boundaries) and, in PROD mode, bit b' holds its QJL sign bit
+ *           [(S r)_j >= 0] with r = u - Pi^T c_hat, u = x / ||x||.
+ *   codes : b * d/8 bytes: the records as word-interleaved bit planes.
+ *           Coordinates go in groups of 32; group g holds b little-endian
+ *           32-bit words, one per plane, at bytes 4(b g + p) .. 4(b g + p) + 3,
+ *           and bit i of the word of plane p is bit p of the record of
+ *           coordinate 32g + i.
  *   norm  : fp16 bits (round to nearest even) of ||x||_2.
  *   rnorm : (PROD) fp16 bits of gamma = ||r||_2.
  *   A zero vector gets idx_j = 2^(b'-1), all sign bits 1 and gamma = 0.
  *   Reconstruction: x_hat = norm * (Pi^T c_hat + sqrt(pi/2)/d * rnorm * S^T s),
- *   s = 2*sign_bit - 1.
+ *   s = 2*sign_bit - 1.  A row is b*d/8 + 2 (MSE) or b*d/8 + 4 (PROD) bytes.
  */
 #ifndef TQ_H
 #define TQ_H
@@ -105,11 +113,10 @@ typedef struct tq_params {
   const float *boundaries;  /* 2^b' - 1 ascending                          */
 } tq_params;
 
-/* Packed vectors, structure of arrays.  Vector i occupies codes[i*b'*d/8 ..],
- * signs[i*d/8 ..], norm[i], rnorm[i] (device memory). */
+/* Packed vectors, structure of arrays.  Vector i occupies codes[i*b*d/8 ..]
+ * (4-byte aligned rows), norm[i] and rnorm[i] (device memory). */
 typedef struct tq_packed {
   uint8_t *codes;
-  uint8_t *signs;           /* PROD only; NULL in MSE                      */
   uint16_t *norm;
   uint16_t *rnorm;          /* PROD only; NULL in MSE                      */
 } tq_packed;
@@ -139,9 +146,10 @@ tq_status tq_quantize_kv(const tq_params *p, const void *x, int32_t x_dtype, int
  *                fp32 [batch][n_q_heads][topk] and topk_idx int32 of the same
  *                shape.  Needs seq_len >= topk.
  * GQA: query head h reads KV head h / (n_q_heads / n_kv_heads); n_q_heads
- * must be a multiple of n_kv_heads.  Dense logits support d in {128, 256}
- * and up to 16 query heads per KV head; top-k supports MSE mode, d in
- * {128, 256}, topk <= 16.  seq_len == 0 is a no-op.
+ * must be a multiple of n_kv_heads.  Dense logits support d in {128, 256},
+ * up to 16 query heads per KV head, and streams whose packed codes and
+ * logits each stay under 4 GiB; top-k supports MSE mode, d in {128, 256},
+ * topk <= 16.  seq_len == 0 is a no-op.
  * Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED, TQ_ERR_HIP. */
 tq_status tq_attn_logits(const tq_params *p, const void *q, int32_t q_dtype, int32_t batch,
                          int32_t n_q_heads, int32_t n_kv_heads, const tq_packed *k,

@@ -51,8 +51,7 @@ class Params(ctypes.Structure):
 
 
 class Packed(ctypes.Structure):
-    _fields_ = [("codes", ctypes.c_void_p), ("signs", ctypes.c_void_p), ("norm", ctypes.c_void_p),
-                ("rnorm", ctypes.c_void_p)]
+    _fields_ = [("codes", ctypes.c_void_p), ("norm", ctypes.c_void_p), ("rnorm", ctypes.c_void_p)]
 
 
 def _load():
@@ -135,32 +134,26 @@ class PackedKV:
 
     def __init__(self, d, bits, mode, capacity, device="cuda"):
         torch = _torch()
-        lb = lloyd_bits(bits, mode)
         self.d, self.bits, self.mode, self.capacity = d, bits, mode, capacity
-        self.codes = torch.empty((capacity, lb * d // 8), dtype=torch.uint8, device=device)
+        # b bits per coordinate: b' Lloyd-Max planes (+ the QJL sign plane)
+        self.codes = torch.empty((capacity, bits * d // 8), dtype=torch.uint8, device=device)
         self.norm = torch.empty((capacity,), dtype=torch.int16, device=device)
-        if mode == MODE_PROD:
-            self.signs = torch.empty((capacity, d // 8), dtype=torch.uint8, device=device)
-            self.rnorm = torch.empty((capacity,), dtype=torch.int16, device=device)
-        else:
-            self.signs = None
-            self.rnorm = None
+        self.rnorm = torch.empty((capacity,), dtype=torch.int16, device=device) \
+            if mode == MODE_PROD else None
 
     @classmethod
-    def from_tensors(cls, d, bits, mode, codes, norm, signs=None, rnorm=None):
+    def from_tensors(cls, d, bits, mode, codes, norm, rnorm=None):
         obj = cls.__new__(cls)
         obj.d, obj.bits, obj.mode, obj.capacity = d, bits, mode, codes.shape[0]
-        obj.codes, obj.norm, obj.signs, obj.rnorm = codes, norm, signs, rnorm
+        obj.codes, obj.norm, obj.rnorm = codes, norm, rnorm
         return obj
 
     def struct(self):
-        return Packed(self.codes.data_ptr(), self.signs.data_ptr() if self.signs is not None else None,
-                      self.norm.data_ptr(), self.rnorm.data_ptr() if self.rnorm is not None else None)
+        return Packed(self.codes.data_ptr(), self.norm.data_ptr(),
+                      self.rnorm.data_ptr() if self.rnorm is not None else None)
 
     def bytes_per_vector(self):
-        lb = lloyd_bits(self.bits, self.mode)
-        extra = (self.d // 8 + 2) if self.mode == MODE_PROD else 0
-        return lb * self.d // 8 + 2 + extra
+        return self.bits * self.d // 8 + (4 if self.mode == MODE_PROD else 2)
 
 
 class Quantizer:

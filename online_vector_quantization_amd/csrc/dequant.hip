@@ -53,6 +53,8 @@ __global__ __launch_bounds__(DLayout<D>::NT) void dequant_kernel(tqi::DequantArg
   using L = DLayout<D>;
   constexpr int K = 1 << LB;
   constexpr int PB = D / 8;
+  constexpr int NPL = LB + (PROD ? 1 : 0);  // planes per record (sign on top)
+  constexpr int RB = NPL * PB;
   __shared__ __attribute__((aligned(16))) _Float16 ch[32 * L::PITCH];
   __shared__ __attribute__((aligned(16))) _Float16 cl[32 * L::PITCH];
   __shared__ __attribute__((aligned(16))) _Float16 sg[PROD ? 32 * L::PITCH : 8];
@@ -92,9 +94,10 @@ __global__ __launch_bounds__(DLayout<D>::NT) void dequant_kernel(tqi::DequantArg
       uint32_t pw[LB];
 #pragma unroll
       for (int p = 0; p < LB; ++p)
-        pw[p] = valid ? *(const uint16_t *)(a.codes + gv * (LB * PB) + p * PB + 2 * c) : 0u;
+        pw[p] = valid ? *(const uint16_t *)(a.codes + gv * RB + 4 * ((c >> 1) * NPL + p) + 2 * (c & 1)) : 0u;
       uint32_t sw = 0;
-      if constexpr (PROD) sw = valid ? *(const uint16_t *)(a.signs + gv * PB + 2 * c) : 0u;
+      if constexpr (PROD)
+        sw = valid ? *(const uint16_t *)(a.codes + gv * RB + 4 * ((c >> 1) * NPL + LB) + 2 * (c & 1)) : 0u;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         uint32_t idx = 0;

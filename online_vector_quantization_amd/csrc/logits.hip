@@ -69,24 +69,27 @@ struct LLayout {
   static constexpr int PB = D / 8;
 };
 
+// Query preparation for one (stream, row tile, part): part 0 builds the
+// Walsh-plane chunks from q' = Pi q, part 1 the sign chunks from q'' = S q.
+// 256 threads; projections in fp64 from fp32 matrices.
 template <int D, int LB, bool PROD>
 __global__ __launch_bounds__(256) void logit_prep_kernel(PrepArgs a) {
   using L = LLayout<D, LB, PROD>;
   constexpr int K = 1 << LB;
   constexpr int P = L::P;
-  __shared__ float qin[4][D];
-  __shared__ double qr[4][D];
-  __shared__ double qs[PROD ? 4 : 1][D];
+  __shared__ __attribute__((aligned(16))) double qin[4][D];
+  __shared__ double proj[4][D];
   __shared__ double beta[P];
-  __shared__ int fexp[4][2];
+  __shared__ double red_max[4][4], red_sum[4][4];
 
   const int stream = blockIdx.x;
   const int rt = blockIdx.y;
+  const int part = blockIdx.z;              // 0: MSE planes, 1: QJL signs
   const int b = stream / a.n_kv_heads;
   const int kvh = stream % a.n_kv_heads;
   const int tid = threadIdx.x;
 
-  for (int i = tid; i < 4 * D; i += blockDim.x) {
+  for (int i = tid; i < 4 * D; i += 256) {
     const int g = i / D, k = i % D;
     const int gg = 4 * rt + g;
     float v = 0.0f;
@@ -94,96 +97,133 @@ __global__ __launch_bounds__(256) void logit_prep_kernel(PrepArgs a) {
       const int64_t off = ((int64_t)b * a.n_q_heads + (int64_t)kvh * a.group + gg) * D + k;
       v = a.q_f32 ? ((const float *)a.q)[off] : bf16_to_f32(((const uint16_t *)a.q)[off]);
     }
-    qin[g][k] = v;
+    qin[g][k] = (double)v;
   }
-  if (tid < P) {
+  if (part == 0 && tid < P) {
     const int sub = Walsh<LB>::subset(tid);
     double acc = 0.0;
     for (int i = 0; i < K; ++i) {
-      const int sg = (__builtin_popcount(i & sub) + __builtin_popcount(sub)) & 1;
       // sigma_S(i) = prod_{p in S} (2 b_p - 1) = (-1)^(|S| - popcount(i & S))
+      const int sg = (__builtin_popcount(i & sub) + __builtin_popcount(sub)) & 1;
       acc += sg ? -(double)a.centroids[i] : (double)a.centroids[i];
     }
     beta[tid] = acc / K;
   }
   __syncthreads();
-  for (int i = tid; i < 4 * D; i += blockDim.x) {
-    const int g = i / D, j = i % D;
-    const float *row = a.pi + (size_t)j * D;
-    double acc = 0.0;
-    for (int k = 0; k < D; ++k) acc += (double)row[k] * (double)qin[g][k];
-    qr[g][j] = acc;
-    if constexpr (PROD) {
-      const float *srow = a.s_mat + (size_t)j * D;
-      double acc2 = 0.0;
-      for (int k = 0; k < D; ++k) acc2 += (double)srow[k] * (double)qin[g][k];
-      qs[g][j] = acc2;
-    }
-  }
-  __syncthreads();
-  if (tid < 4) {
-    const int g = tid;
-    double mq = 0.0, sq = 0.0, mqs = 0.0, sqs = 0.0, mb = 0.0, sb = 0.0;
-    for (int j = 0; j < D; ++j) {
-      mq = fmax(mq, fabs(qr[g][j]));
-      sq += qr[g][j];
-      if constexpr (PROD) {
-        mqs = fmax(mqs, fabs(qs[g][j]));
-        sqs += qs[g][j];
+  // thread (j, gp): coordinate j, queries 2 gp and 2 gp + 1 (D = 128); for
+  // D = 256 each thread also takes j + 128.
+  const float *mat = part == 0 ? a.pi : a.s_mat;
+  const int gp = tid >> 7;
+  double mx[2] = {0, 0}, sm[2] = {0, 0};
+  for (int j = tid & 127; j < D; j += 128) {
+    const f32x4 *row = (const f32x4 *)(mat + (size_t)j * D);
+    double acc0 = 0.0, acc1 = 0.0;
+#pragma unroll 8
+    for (int k4 = 0; k4 < D / 4; ++k4) {
+      const f32x4 m4 = row[k4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc0 = fma((double)m4[i], qin[2 * gp][4 * k4 + i], acc0);
+        acc1 = fma((double)m4[i], qin[2 * gp + 1][4 * k4 + i], acc1);
       }
     }
+    proj[2 * gp][j] = acc0;
+    proj[2 * gp + 1][j] = acc1;
+    mx[0] = fmax(mx[0], fabs(acc0));
+    mx[1] = fmax(mx[1], fabs(acc1));
+    sm[0] += acc0;
+    sm[1] += acc1;
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      mx[h] = fmax(mx[h], __shfl_xor(mx[h], off, 64));
+      sm[h] += __shfl_xor(sm[h], off, 64);
+    }
+  }
+  if ((tid & 63) == 0) {
+    const int wv = (tid >> 6) & 1;
+    red_max[2 * gp][wv] = mx[0];
+    red_max[2 * gp + 1][wv] = mx[1];
+    red_sum[2 * gp][wv] = sm[0];
+    red_sum[2 * gp + 1][wv] = sm[1];
+  }
+  __syncthreads();
+  double mb = 0.0, sb = 0.0;
+  if (part == 0) {
     for (int r = 0; r < P; ++r) {
       mb = fmax(mb, fabs(beta[r]));
       sb += beta[r];
     }
-    int e1 = 0, e2 = 0;
-    if (mq * mb > 0.0) frexp(mq * mb, &e1);
-    if (mqs > 0.0) frexp(mqs, &e2);
-    const int f1 = 30 - e1, f2 = 30 - e2;
-    fexp[g][0] = f1;
-    fexp[g][1] = f2;
+  }
+  int fexp[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const double mq = fmax(red_max[g][0], red_max[g][1]);
+    const double sq = red_sum[g][0] + red_sum[g][1];
+    const double top = part == 0 ? mq * mb : mq;
+    int e = 0;
+    if (top > 0.0) frexp(top, &e);
+    fexp[g] = 30 - e;               // largest weight * 2^F < 2^30
     const int gg = 4 * rt + g;
-    if (gg < a.group) {
+    if (tid == 0 && gg < a.group) {
       const double kappa = sqrt(M_PI / 2.0) / D;
       float *cst = a.consts + ((int64_t)stream * a.group + gg) * 4;
-      cst[0] = (float)ldexp(2.0, -f1);
-      cst[1] = (float)(sb * sq);
-      cst[2] = PROD ? (float)(ldexp(2.0, -f2) * kappa) : 0.0f;
-      cst[3] = PROD ? (float)(kappa * sqs) : 0.0f;
+      if (part == 0) {
+        cst[0] = (float)ldexp(2.0, -fexp[g]);
+        cst[1] = (float)(sb * sq);
+        if (!PROD) {
+          cst[2] = 0.0f;
+          cst[3] = 0.0f;
+        }
+      } else {
+        cst[2] = (float)(ldexp(2.0, -fexp[g]) * kappa);
+        cst[3] = (float)(kappa * sq);
+      }
     }
   }
-  __syncthreads();
+  // A-operand chunks of this part.  Lane l = 16 kg + 4 g + piece supplies
+  // row (query g, byte piece); its byte e = 4 t + i pairs with coordinate
+  // 32 (kg + 4 q) + 8 i + 4 h + t, whose key byte carries weight 2^(4 h + t)
+  // (see the kernel comment).  One thread per (chunk, kg, g) computes the
+  // 32-bit fixed-point weights once and writes the four piece rows.
   int8_t *tab = a.table + ((int64_t)stream * a.row_tiles + rt) * (L::NCH * 64 * 16);
-  for (int i = tid; i < L::NCH * 64; i += blockDim.x) {
-    const int cidx = i / 64, l = i % 64;
-    const int row = l & 15, kg = l >> 4;
-    const int g = row >> 2, piece = row & 3;
+  const int c_begin = part == 0 ? 0 : P * L::CPP;
+  const int c_end = part == 0 ? P * L::CPP : L::NCH;
+  for (int i = c_begin * 16 + tid; i < c_end * 16; i += 256) {
+    const int cidx = i / 16, kg = (i >> 2) & 3, g = i & 3;
     const int r = cidx / L::CPP, c = cidx % L::CPP;
     const int q = c >> 1, hh = c & 1;
-    int8_t out[16];
+    const double wgt = part == 0 ? beta[r < P ? r : 0] : 1.0;
+    const bool live = 4 * rt + g < a.group;
+    uint32_t words[4][4];   // [piece][t]
+#pragma unroll
+    for (int pc = 0; pc < 4; ++pc)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) words[pc][t] = 0u;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int t = e >> 2, ib = e & 3;
       const int j = 32 * (kg + 4 * q) + 8 * ib + 4 * hh + t;
       const int s = 4 * hh + t;
-      const bool sign_plane = r >= P;
-      const double av = sign_plane ? qs[PROD ? g : 0][j] : beta[r < P ? r : 0] * qr[g][j];
-      const int f = fexp[g][sign_plane ? 1 : 0];
-      long long n = llrint(ldexp(av, f - s));
+      int n = (int)rint(ldexp(wgt * proj[g][j], fexp[g] - s));
       if (s == 7) n = -n;
-      long long rem = n;
-      int digit = 0;
+      if (!live) n = 0;
+      // balanced signed-byte digits: n = sum_p digit_p 256^p, digit_p in [-128, 127]
 #pragma unroll
       for (int pc = 0; pc < 4; ++pc) {
-        const int dgt = (int)(int8_t)(rem & 0xFF);
-        if (pc == piece) digit = dgt;
-        rem = (rem - dgt) >> 8;
+        const int dd = (int)(int8_t)(n & 0xFF);
+        words[pc][t] |= (uint32_t)(uint8_t)dd << (8 * ib);
+        n = (n - dd) >> 8;
       }
-      out[e] = (4 * rt + g < a.group) ? (int8_t)digit : (int8_t)0;
     }
-    int8_t *dst = tab + ((int64_t)cidx * 64 + l) * 16;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) dst[e] = out[e];
+    for (int pc = 0; pc < 4; ++pc) {
+      const int l = 16 * kg + 4 * g + pc;
+      *(i32x4 *)(tab + ((int64_t)cidx * 64 + l) * 16) =
+          i32x4{(int)words[pc][0], (int)words[pc][1], (int)words[pc][2], (int)words[pc][3]};
+    }
   }
 }
 
@@ -191,13 +231,31 @@ struct StreamArgs {
   const int8_t *table;
   const float *consts;
   const uint8_t *codes;
-  const uint8_t *signs;
   const uint16_t *norm;
   const uint16_t *rnorm;
   int64_t row_tokens, seq_len, tokens_per_block;
   int n_splits, n_kv_heads, n_q_heads, group, row_tiles;
   float scale;
   float *logits;
+};
+
+#ifndef TQ_LOGIT_GROUPS
+#define TQ_LOGIT_GROUPS 4
+#endif
+
+// Registers of one 16-token group as loaded by one lane: the plane words of
+// its 32-coordinate group(s); in inner-product mode the last word of each
+// group is the sign plane.
+template <int NPL, int NQ>
+struct KeyGroup {
+  uint32_t w[NQ][NPL];
+};
+
+// fp16 norm and residual norm of 64 consecutive tokens, one token per lane.
+// Kept apart until they are consumed, so no instruction touches a load
+// result before the loop has moved on to computing.
+struct NormBlock {
+  uint32_t n, g;
 };
 
 template <int D, int LB, bool PROD, int RT>
@@ -207,7 +265,13 @@ __global__ __launch_bounds__(256) void logit_kernel(StreamArgs a) {
   constexpr int CPP = L::CPP;
   constexpr int NCH = L::NCH;
   constexpr int PB = L::PB;
-  constexpr int NQ = D / 128;  // plane dwords per lane group
+  constexpr int NPL = LB + (PROD ? 1 : 0);  // planes per record (sign on top)
+  constexpr int RB = NPL * PB;              // bytes per packed row
+  constexpr int NQ = D / 128;            // plane words per lane and plane
+  constexpr int U = TQ_LOGIT_GROUPS;     // 16-token groups per wave and iteration
+  constexpr int NB = U / 4;              // 64-token norm blocks per iteration
+  static_assert(U % 4 == 0, "groups come in fours (64 tokens)");
+  __shared__ __attribute__((aligned(16))) float stage[4][4 * RT][16 * U];
 
   int bid = blockIdx.x;
   if ((gridDim.x & 7) == 0) {  // keep a stream's blocks on one XCD (L2)
@@ -242,79 +306,129 @@ __global__ __launch_bounds__(256) void logit_kernel(StreamArgs a) {
     cst[rt] = g < a.group ? *(const f32x4 *)(a.consts + ((int64_t)stream * a.group + g) * 4)
                           : f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const int64_t key0 = (int64_t)stream * a.row_tokens;
-  float *out_base = a.logits + ((int64_t)b * a.n_q_heads + (int64_t)kvh * a.group) * a.seq_len;
 
-  for (int64_t tok0 = t_begin + 16 * w; tok0 < t_end; tok0 += 64) {
-    const int64_t tok = tok0 + n;
-    const bool valid = tok < t_end;
-    const int64_t key = key0 + (valid ? tok : t_end - 1);
-    uint32_t wp[LB][NQ];
+  // Per-stream buffer resources: SGPR bases, 32-bit per-lane offsets.  The
+  // ranges end at seq_len, so loads of tokens past the stream read zeros and
+  // stores past it are dropped.
+  const int64_t key0 = (int64_t)stream * a.row_tokens;
+  const uint32_t nvalid = (uint32_t)a.seq_len;
+  const i32x4 rc = make_rsrc(a.codes + key0 * RB, nvalid * RB);
+  const i32x4 rn = make_rsrc(a.norm + key0, nvalid * 2);
+  const i32x4 rg = make_rsrc(PROD ? a.rnorm + key0 : a.norm, PROD ? nvalid * 2 : 0u);
+  const i32x4 ro = make_rsrc(a.logits + ((int64_t)b * a.n_q_heads + (int64_t)kvh * a.group) * a.seq_len,
+                             (uint32_t)(a.group * a.seq_len * 4));
+  const uint32_t t_end32 = (uint32_t)t_end;
+
+  // Lane (n, kg) reads, for token n of each group, the NPL plane words of
+  // 32-coordinate group kg + 4 qd (one contiguous load: 16 bytes at b = 4);
+  // lane l reads the two fp16 scalars of token l of each 64-token block.
+  auto load = [&](uint32_t tok0, KeyGroup<NPL, NQ>(&kgp)[U], NormBlock(&nb)[NB]) {
 #pragma unroll
-    for (int p = 0; p < LB; ++p)
+    for (int u = 0; u < U; ++u) {
+      const uint32_t tok = tok0 + 16 * u + n;
 #pragma unroll
       for (int qd = 0; qd < NQ; ++qd)
-        wp[p][qd] = *(const uint32_t *)(a.codes + key * (LB * PB) + p * PB + 4 * (kg + 4 * qd));
-    uint32_t ws[NQ];
-    float gam = 0.0f;
-    if constexpr (PROD) {
-#pragma unroll
-      for (int qd = 0; qd < NQ; ++qd) ws[qd] = *(const uint32_t *)(a.signs + key * PB + 4 * (kg + 4 * qd));
-      gam = f16_bits_to_f32(a.rnorm[key]);
+        buf_load_words<NPL>(rc, tok * RB + 4 * NPL * (kg + 4 * qd), kgp[u].w[qd]);
     }
-    const float nrm = f16_bits_to_f32(a.norm[key]);
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const uint32_t tok = tok0 + 64 * q + l;
+      nb[q].n = buf_load_u16(rn, 2 * tok);
+      if constexpr (PROD) nb[q].g = buf_load_u16(rg, 2 * tok);
+    }
+  };
 
-    i32x4 am[RT], aq[RT];
+  auto compute = [&](uint32_t tok0, const KeyGroup<NPL, NQ>(&kgp)[U], const NormBlock(&nb)[NB]) {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) { am[rt] = i32x4{0, 0, 0, 0}; aq[rt] = i32x4{0, 0, 0, 0}; }
+    for (int u = 0; u < U; ++u) {
+      i32x4 am[RT], aq[RT];
 #pragma unroll
-    for (int r = 0; r < P; ++r) {
-      constexpr int dummy = 0;
-      (void)dummy;
-      const int sub = Walsh<LB>::subset(r);
-      uint32_t wr[NQ];
+      for (int rt = 0; rt < RT; ++rt) { am[rt] = i32x4{0, 0, 0, 0}; aq[rt] = i32x4{0, 0, 0, 0}; }
 #pragma unroll
-      for (int qd = 0; qd < NQ; ++qd) {
-        uint32_t x = 0;
+      for (int r = 0; r < P; ++r) {
+        const int sub = Walsh<LB>::subset(r);
 #pragma unroll
-        for (int p = 0; p < LB; ++p)
-          if (sub & (1 << p)) x ^= wp[p][qd];
-        wr[qd] = x;
+        for (int c = 0; c < CPP; ++c) {
+          uint32_t x = 0;
+#pragma unroll
+          for (int p = 0; p < LB; ++p)
+            if (sub & (1 << p)) x ^= kgp[u].w[c >> 1][p];
+          const int sh = 4 * (c & 1);
+          const i32x4 bv = {(int)(x & (0x01010101u << sh)), (int)(x & (0x01010101u << (sh + 1))),
+                            (int)(x & (0x01010101u << (sh + 2))), (int)(x & (0x01010101u << (sh + 3)))};
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) am[rt] = mfma_i8(areg[rt][r * CPP + c], bv, am[rt]);
+        }
       }
+      if constexpr (PROD) {
 #pragma unroll
-      for (int c = 0; c < CPP; ++c) {
-        const uint32_t x = wr[c >> 1];
-        const int sh = 4 * (c & 1);
-        i32x4 bv = {(int)(x & (0x01010101u << sh)), (int)(x & (0x01010101u << (sh + 1))),
-                    (int)(x & (0x01010101u << (sh + 2))), (int)(x & (0x01010101u << (sh + 3)))};
+        for (int c = 0; c < CPP; ++c) {
+          const uint32_t x = kgp[u].w[c >> 1][LB];
+          const int sh = 4 * (c & 1);
+          const i32x4 bv = {(int)(x & (0x01010101u << sh)), (int)(x & (0x01010101u << (sh + 1))),
+                            (int)(x & (0x01010101u << (sh + 2))), (int)(x & (0x01010101u << (sh + 3)))};
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) am[rt] = mfma_i8(areg[rt][r * CPP + c], bv, am[rt]);
+          for (int rt = 0; rt < RT; ++rt) aq[rt] = mfma_i8(areg[rt][P * CPP + c], bv, aq[rt]);
+        }
+      }
+      // scalars of token 16u + n live in lane 16 (u % 4) + n of block u / 4
+      const int src = 16 * (u & 3) + n;
+      const float nrm = a.scale * f16_bits_to_f32((uint16_t)__shfl((int)nb[u >> 2].n, src, 64));
+      const float gam = PROD ? f16_bits_to_f32((uint16_t)__shfl((int)nb[u >> 2].g, src, 64)) : 0.0f;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const float sm = (((float)am[rt][3] * 256.0f + (float)am[rt][2]) * 256.0f + (float)am[rt][1]) * 256.0f +
+                         (float)am[rt][0];
+        float v = cst[rt][0] * sm - cst[rt][1];
+        if constexpr (PROD) {
+          const float sq = (((float)aq[rt][3] * 256.0f + (float)aq[rt][2]) * 256.0f + (float)aq[rt][1]) * 256.0f +
+                           (float)aq[rt][0];
+          v += gam * (cst[rt][2] * sq - cst[rt][3]);
+        }
+        stage[w][4 * rt + kg][16 * u + n] = nrm * v;
       }
     }
-    if constexpr (PROD) {
-#pragma unroll
-      for (int c = 0; c < CPP; ++c) {
-        const uint32_t x = ws[c >> 1];
-        const int sh = 4 * (c & 1);
-        i32x4 bv = {(int)(x & (0x01010101u << sh)), (int)(x & (0x01010101u << (sh + 1))),
-                    (int)(x & (0x01010101u << (sh + 2))), (int)(x & (0x01010101u << (sh + 3)))};
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) aq[rt] = mfma_i8(areg[rt][P * CPP + c], bv, aq[rt]);
-      }
-    }
+    // each lane stores 4 consecutive logits of one query: 16-byte stores
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      const int g = 4 * rt + kg;
-      const float sm = (((float)am[rt][3] * 256.0f + (float)am[rt][2]) * 256.0f + (float)am[rt][1]) * 256.0f +
-                       (float)am[rt][0];
-      float v = cst[rt][0] * sm - cst[rt][1];
-      if constexpr (PROD) {
-        const float sq = (((float)aq[rt][3] * 256.0f + (float)aq[rt][2]) * 256.0f + (float)aq[rt][1]) * 256.0f +
-                         (float)aq[rt][0];
-        v += gam * (cst[rt][2] * sq - cst[rt][3]);
+#pragma unroll
+      for (int c = 0; c < U / 4; ++c) {
+        const int g = 4 * rt + kg;
+        const uint32_t t4 = 4 * n + 64 * c;          // token offset within the iteration
+        const f32x4 v = *(const f32x4 *)&stage[w][4 * rt + kg][t4];
+        const uint32_t tok = tok0 + t4;
+        if (g < a.group) {
+          if (tok + 3 < t_end32) {
+            buf_store_f32x4(ro, 4u * ((uint32_t)g * nvalid + tok), v);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (tok + e < t_end32) buf_store_f32(ro, 4u * ((uint32_t)g * nvalid + tok + e), v[e]);
+          }
+        }
       }
-      if (valid && g < a.group) out_base[(int64_t)g * a.seq_len + tok] = a.scale * nrm * v;
     }
+  };
+
+  // Ping-pong over two register sets: the next iteration's loads are issued
+  // before the current one is consumed.
+  const uint32_t stride = 4 * 16 * U;
+  uint32_t base = (uint32_t)t_begin + 16 * U * w;
+  KeyGroup<NPL, NQ> bufa[U], bufb[U];
+  NormBlock na[NB], nbb[NB];
+  // The scheduling barriers keep each prefetch ahead of the compute that
+  // hides its latency.
+  load(base, bufa, na);
+  while (base < t_end32) {
+    load(base + stride, bufb, nbb);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(base, bufa, na);
+    base += stride;
+    if (base >= t_end32) break;
+    load(base + stride, bufa, na);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(base, bufb, nbb);
+    base += stride;
   }
 }
 
@@ -327,7 +441,7 @@ hipError_t launch_t(const tqi::LogitArgs &a, hipStream_t s) {
   const size_t table_bytes = (size_t)n_streams * rts * L::NCH * 64 * 16;
   const size_t const_bytes = (size_t)n_streams * group * 4 * sizeof(float);
   void *ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, table_bytes + const_bytes, s);
+  hipError_t e = tqi::workspace(s, table_bytes + const_bytes, &ws);
   if (e != hipSuccess) return e;
   PrepArgs pa;
   pa.q = a.q;
@@ -341,14 +455,14 @@ hipError_t launch_t(const tqi::LogitArgs &a, hipStream_t s) {
   pa.centroids = a.centroids;
   pa.table = (int8_t *)ws;
   pa.consts = (float *)((char *)ws + table_bytes);
-  hipLaunchKernelGGL((logit_prep_kernel<D, LB, PROD>), dim3(n_streams, rts), dim3(256), 0, s, pa);
+  hipLaunchKernelGGL((logit_prep_kernel<D, LB, PROD>), dim3(n_streams, rts, PROD ? 2 : 1), dim3(256), 0,
+                     s, pa);
   e = hipGetLastError();
   if (e == hipSuccess) {
     StreamArgs sa;
     sa.table = pa.table;
     sa.consts = pa.consts;
     sa.codes = a.codes;
-    sa.signs = a.signs;
     sa.norm = a.norm;
     sa.rnorm = a.rnorm;
     sa.row_tokens = a.row_tokens;
@@ -360,10 +474,13 @@ hipError_t launch_t(const tqi::LogitArgs &a, hipStream_t s) {
     sa.scale = a.scale;
     sa.logits = a.logits;
     const int64_t total = (int64_t)n_streams * a.seq_len;
-    const int64_t target_blocks = 4LL * tqi::device_cu_count();
+#ifndef TQ_LOGIT_BLOCKS_PER_CU
+#define TQ_LOGIT_BLOCKS_PER_CU 4
+#endif
+    const int64_t target_blocks = (int64_t)TQ_LOGIT_BLOCKS_PER_CU * tqi::device_cu_count();
     int64_t tpb = (total + target_blocks - 1) / target_blocks;
     tpb = (tpb + 63) / 64 * 64;
-    if (tpb < 256) tpb = 256;
+    if (tpb < 512) tpb = 512;
     if (tpb > 16384) tpb = 16384;
     sa.tokens_per_block = tpb;
     sa.n_splits = (int)((a.seq_len + tpb - 1) / tpb);
@@ -376,8 +493,7 @@ hipError_t launch_t(const tqi::LogitArgs &a, hipStream_t s) {
     }
     e = hipGetLastError();
   }
-  hipError_t e2 = hipFreeAsync(ws, s);
-  return e != hipSuccess ? e : e2;
+  return e;
 }
 
 template <int D, bool PROD>
@@ -400,7 +516,13 @@ namespace tqi {
 hipError_t launch_logits(int d, int lbits, bool prod, const LogitArgs &a, hipStream_t s,
                          bool *supported) {
   *supported = false;
-  if (a.n_q_heads / a.n_kv_heads > 16) return hipSuccess;
+  const int64_t group = a.n_q_heads / a.n_kv_heads;
+  if (group > 16) return hipSuccess;
+  // the streaming kernel addresses one stream's codes and logits with 32-bit
+  // byte offsets
+  if (a.seq_len * (int64_t)((lbits + (prod ? 1 : 0)) * d / 8) >= (1LL << 32) ||
+      group * a.seq_len * 4 >= (1LL << 32))
+    return hipSuccess;
   if (d == 128) return prod ? launch_lb<128, true>(lbits, a, s, supported)
                             : launch_lb<128, false>(lbits, a, s, supported);
   if (d == 256) return prod ? launch_lb<256, true>(lbits, a, s, supported)

@@ -25,7 +25,8 @@
 //   (plane p = XOR of the masks for boundaries (k*2^p - 1)).
 // * Inner-product mode: the rotated residual y/n - c_hat is written to LDS
 //   as fp16 hi + lo, then z = (y/n - c_hat) M^T runs on MFMA against the
-//   stationary M slice; sign masks are ballots of z >= 0.
+//   stationary M slice; sign masks are ballots of z >= 0 and become the top
+//   bit plane of each coordinate's record.
 #include "tq_device.h"
 #include "tq_internal.h"
 
@@ -73,6 +74,8 @@ __global__ __launch_bounds__(QLayout<D>::NT) void quantize_kernel(tqi::QuantizeA
   using L = QLayout<D>;
   constexpr int K = 1 << LB;                  // centroids
   constexpr int PB = D / 8;                   // bytes per plane
+  constexpr int NPL = LB + (PROD ? 1 : 0);    // planes per record (sign on top)
+  constexpr int RB = NPL * PB;                // bytes per packed row
   __shared__ __attribute__((aligned(16))) _Float16 xh[32 * L::PITCH];
   __shared__ __attribute__((aligned(16))) _Float16 xl[IN_F32 ? 32 * L::PITCH : 1];
   __shared__ __attribute__((aligned(16))) _Float16 rh[PROD ? 32 * L::PITCH : 1];
@@ -228,7 +231,7 @@ __global__ __launch_bounds__(QLayout<D>::NT) void quantize_kernel(tqi::QuantizeA
         const int v = 8 * (r >> 2) + 4 * hh + (r & 3);
         const int64_t gv = base + v;
         if (gv < a.n_vec) {
-          uint32_t *dst = (uint32_t *)(a.codes + (a.out_offset + gv) * (LB * PB) + p * PB + 4 * w);
+          uint32_t *dst = (uint32_t *)(a.codes + (a.out_offset + gv) * RB + 4 * (w * NPL + p));
           *dst = outw[g];
         }
       }
@@ -257,7 +260,7 @@ __global__ __launch_bounds__(QLayout<D>::NT) void quantize_kernel(tqi::QuantizeA
         const int r = l >> 1, hh = l & 1;
         const int v = 8 * (r >> 2) + 4 * hh + (r & 3);
         const int64_t gv = base + v;
-        if (gv < a.n_vec) *(uint32_t *)(a.signs + (a.out_offset + gv) * PB + 4 * w) = sw;
+        if (gv < a.n_vec) *(uint32_t *)(a.codes + (a.out_offset + gv) * RB + 4 * (w * NPL + LB)) = sw;
       }
       // residual norm of the unit vector from the staged residual tile
       {

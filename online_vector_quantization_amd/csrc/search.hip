@@ -164,7 +164,7 @@ __global__ __launch_bounds__(256) void search_score_kernel(ScoreArgs a) {
       const int64_t key = key0 + (valid ? t : k_end - 1);
       uint32_t pw[LB];
 #pragma unroll
-      for (int p = 0; p < LB; ++p) pw[p] = *(const uint16_t *)(a.codes + key * (LB * PB) + p * PB + 2 * c);
+      for (int p = 0; p < LB; ++p) pw[p] = *(const uint16_t *)(a.codes + key * (LB * PB) + 4 * ((c >> 1) * LB + p) + 2 * (c & 1));
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         uint32_t idx = 0;
@@ -289,7 +289,7 @@ hipError_t launch_t(const tqi::SearchArgs &sa, hipStream_t s) {
   const size_t bytes = 2 * qbytes + (size_t)n_queries * sizeof(float) +
                        (size_t)splits * n_rows * kTop * (sizeof(float) + sizeof(int32_t)) + 256;
   char *ws = nullptr;
-  hipError_t e = hipMallocAsync((void **)&ws, bytes, s);
+  hipError_t e = tqi::workspace(s, bytes, (void **)&ws);
   if (e != hipSuccess) return e;
   QPrepArgs pa;
   pa.q = a.q;
@@ -342,8 +342,7 @@ hipError_t launch_t(const tqi::SearchArgs &sa, hipStream_t s) {
     hipLaunchKernelGGL(search_merge_kernel, dim3((unsigned)((n_rows + 255) / 256)), dim3(256), 0, s, ma);
     e = hipGetLastError();
   }
-  hipError_t e2 = hipFreeAsync(ws, s);
-  return e != hipSuccess ? e : e2;
+  return e;
 }
 
 template <int D>

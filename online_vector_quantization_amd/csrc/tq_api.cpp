@@ -4,6 +4,9 @@
 
 #include <atomic>
 #include <cstdint>
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "tq.h"
 #include "tq_internal.h"
@@ -23,6 +26,40 @@ int device_cu_count() {
     cu = 256;
   if (dev < 64) cache[dev].store(cu, std::memory_order_relaxed);
   return cu;
+}
+
+hipError_t workspace(hipStream_t s, size_t bytes, void **out) {
+  struct Buf {
+    void *ptr = nullptr;
+    size_t size = 0;
+  };
+  static std::mutex mu;
+  static std::map<std::pair<int, hipStream_t>, Buf> bufs;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  Buf &b = bufs[std::make_pair(dev, s)];
+  if (b.size < bytes) {
+    if (b.ptr != nullptr) {
+      e = hipStreamSynchronize(s);
+      if (e != hipSuccess) return e;
+      e = hipFree(b.ptr);
+      if (e != hipSuccess) return e;
+      b.ptr = nullptr;
+      b.size = 0;
+    }
+    size_t want = bytes + bytes / 4;
+    want = (want + (1u << 20) - 1) & ~(size_t)((1u << 20) - 1);
+    e = hipMalloc(&b.ptr, want);
+    if (e != hipSuccess) {
+      b.ptr = nullptr;
+      return e;
+    }
+    b.size = want;
+  }
+  *out = b.ptr;
+  return hipSuccess;
 }
 
 }  // namespace tqi
@@ -61,11 +98,10 @@ extern "C" tq_status tq_quantize_kv(const tq_params *p, const void *x, int32_t x
   if (n_vec == 0) return TQ_OK;
   if (x == nullptr || out->codes == nullptr || out->norm == nullptr) return TQ_ERR_INVALID;
   if (x_row_stride < p->d) return TQ_ERR_INVALID;
-  if (prod && (p->qjl_rot == nullptr || out->signs == nullptr || out->rnorm == nullptr))
-    return TQ_ERR_INVALID;
+  if (prod && (p->qjl_rot == nullptr || out->rnorm == nullptr)) return TQ_ERR_INVALID;
   const int esz = x_dtype == TQ_F32 ? 4 : 2;
   if (!aligned16(x) || (x_row_stride * esz) % 16 != 0) return TQ_ERR_UNSUPPORTED;
-  if (((uintptr_t)out->codes & 3u) || (prod && ((uintptr_t)out->signs & 3u))) return TQ_ERR_UNSUPPORTED;
+  if ((uintptr_t)out->codes & 3u) return TQ_ERR_UNSUPPORTED;
   tqi::QuantizeArgs a;
   a.x = x;
   a.n_vec = n_vec;
@@ -75,7 +111,6 @@ extern "C" tq_status tq_quantize_kv(const tq_params *p, const void *x, int32_t x
   a.centroids = p->centroids;
   a.boundaries = p->boundaries;
   a.codes = out->codes;
-  a.signs = out->signs;
   a.norm = out->norm;
   a.rnorm = out->rnorm;
   a.out_offset = out_offset;
@@ -100,9 +135,9 @@ extern "C" tq_status tq_attn_logits(const tq_params *p, const void *q, int32_t q
   if (seq_len < 0 || row_tokens < seq_len) return TQ_ERR_INVALID;
   if (batch == 0 || seq_len == 0) return TQ_OK;
   if (q == nullptr || logits == nullptr || k->codes == nullptr || k->norm == nullptr) return TQ_ERR_INVALID;
-  if (prod && (p->qjl == nullptr || k->signs == nullptr || k->rnorm == nullptr)) return TQ_ERR_INVALID;
+  if (prod && (p->qjl == nullptr || k->rnorm == nullptr)) return TQ_ERR_INVALID;
   if (topk > 0 && (topk_idx == nullptr || seq_len < topk)) return TQ_ERR_INVALID;
-  if (((uintptr_t)k->codes & 3u) || (prod && ((uintptr_t)k->signs & 3u))) return TQ_ERR_UNSUPPORTED;
+  if ((uintptr_t)k->codes & 3u) return TQ_ERR_UNSUPPORTED;
   tqi::LogitArgs a;
   a.q = q;
   a.q_f32 = q_dtype == TQ_F32;
@@ -113,7 +148,6 @@ extern "C" tq_status tq_attn_logits(const tq_params *p, const void *q, int32_t q
   a.s_mat = p->qjl;
   a.centroids = p->centroids;
   a.codes = k->codes;
-  a.signs = k->signs;
   a.norm = k->norm;
   a.rnorm = k->rnorm;
   a.row_tokens = row_tokens;
@@ -145,13 +179,12 @@ extern "C" tq_status tq_dequantize(const tq_params *p, const tq_packed *k, int64
   if (out_dtype != TQ_F32 && out_dtype != TQ_BF16) return TQ_ERR_INVALID;
   if (n_vec == 0) return TQ_OK;
   if (out == nullptr || k->codes == nullptr || k->norm == nullptr) return TQ_ERR_INVALID;
-  if (prod && (p->qjl == nullptr || k->signs == nullptr || k->rnorm == nullptr)) return TQ_ERR_INVALID;
+  if (prod && (p->qjl == nullptr || k->rnorm == nullptr)) return TQ_ERR_INVALID;
   tqi::DequantArgs a;
   a.pi = p->pi;
   a.s_mat = p->qjl;
   a.centroids = p->centroids;
   a.codes = k->codes;
-  a.signs = k->signs;
   a.norm = k->norm;
   a.rnorm = k->rnorm;
   a.n_vec = n_vec;

@@ -102,6 +102,76 @@ __device__ __forceinline__ uint32_t write_lane(uint32_t old, uint32_t val, int l
   return (uint32_t)tq_llvm_writelane((int)val, lane, (int)old);
 }
 
+// Raw buffer access (MUBUF): a 128-bit resource (base, byte range, format
+// word) in SGPRs plus a 32-bit per-lane byte offset.  Loads past `bytes`
+// return 0 and stores past it are dropped by the hardware range check.  The
+// format word 0x00020000 selects 32-bit raw data on gfx9-family parts.
+typedef int i32x3 __attribute__((ext_vector_type(3)));
+__device__ int tq_llvm_buf_ld_b32(i32x4 rsrc, int voff, int soff, int aux) __asm("llvm.amdgcn.raw.buffer.load.i32");
+__device__ i32x3 tq_llvm_buf_ld_b96(i32x4 rsrc, int voff, int soff, int aux) __asm("llvm.amdgcn.raw.buffer.load.v3i32");
+__device__ i32x4 tq_llvm_buf_ld_b128(i32x4 rsrc, int voff, int soff, int aux) __asm("llvm.amdgcn.raw.buffer.load.v4i32");
+__device__ short tq_llvm_buf_ld_b16(i32x4 rsrc, int voff, int soff, int aux) __asm("llvm.amdgcn.raw.buffer.load.i16");
+__device__ void tq_llvm_buf_st_f32(float v, i32x4 rsrc, int voff, int soff, int aux) __asm("llvm.amdgcn.raw.buffer.store.f32");
+__device__ void tq_llvm_buf_st_v4f32(f32x4 v, i32x4 rsrc, int voff, int soff, int aux) __asm("llvm.amdgcn.raw.buffer.store.v4f32");
+
+__device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  i32x4 r;
+  r[0] = (int)(uint32_t)a;
+  r[1] = (int)((uint32_t)(a >> 32) & 0xFFFFu);  // stride 0
+  r[2] = (int)bytes;
+  r[3] = 0x00020000;
+  return r;
+}
+
+// Cache-policy bits of the buffer instructions.  Streams that are read or
+// written exactly once use the non-temporal policy (bit 1), which keeps them
+// from displacing reused data in L2 and lifts streaming bandwidth.
+#ifndef TQ_STREAM_POLICY
+#define TQ_STREAM_POLICY 2
+#endif
+constexpr int kStream = TQ_STREAM_POLICY;
+
+template <int N, int AUX = kStream>
+__device__ __forceinline__ void buf_load_words(i32x4 rsrc, uint32_t off, uint32_t (&out)[N]) {
+  if constexpr (N == 1) {
+    out[0] = (uint32_t)tq_llvm_buf_ld_b32(rsrc, (int)off, 0, AUX);
+  } else if constexpr (N == 2) {
+    out[0] = (uint32_t)tq_llvm_buf_ld_b32(rsrc, (int)off, 0, AUX);
+    out[1] = (uint32_t)tq_llvm_buf_ld_b32(rsrc, (int)(off + 4), 0, AUX);
+  } else if constexpr (N == 3) {
+    const i32x3 v = tq_llvm_buf_ld_b96(rsrc, (int)off, 0, AUX);
+    out[0] = (uint32_t)v[0]; out[1] = (uint32_t)v[1]; out[2] = (uint32_t)v[2];
+  } else if constexpr (N == 4) {
+    const i32x4 v = tq_llvm_buf_ld_b128(rsrc, (int)off, 0, AUX);
+    out[0] = (uint32_t)v[0]; out[1] = (uint32_t)v[1]; out[2] = (uint32_t)v[2]; out[3] = (uint32_t)v[3];
+  } else {
+    static_assert(N > 4 && N <= 8, "1..8 words");
+    uint32_t lo[4], hi[N - 4];
+    buf_load_words<4, AUX>(rsrc, off, lo);
+    buf_load_words<N - 4, AUX>(rsrc, off + 16, hi);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = lo[i];
+#pragma unroll
+    for (int i = 0; i < N - 4; ++i) out[4 + i] = hi[i];
+  }
+}
+
+template <int AUX = kStream>
+__device__ __forceinline__ uint16_t buf_load_u16(i32x4 rsrc, uint32_t off) {
+  return (uint16_t)tq_llvm_buf_ld_b16(rsrc, (int)off, 0, AUX);
+}
+
+template <int AUX = kStream>
+__device__ __forceinline__ void buf_store_f32(i32x4 rsrc, uint32_t off, float v) {
+  tq_llvm_buf_st_f32(v, rsrc, (int)off, 0, AUX);
+}
+
+template <int AUX = kStream>
+__device__ __forceinline__ void buf_store_f32x4(i32x4 rsrc, uint32_t off, f32x4 v) {
+  tq_llvm_buf_st_v4f32(v, rsrc, (int)off, 0, AUX);
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_xor(T v, int mask) {
   return __shfl_xor(v, mask, kWave);

@@ -17,7 +17,6 @@ struct QuantizeArgs {
   const float *centroids;
   const float *boundaries;
   uint8_t *codes;
-  uint8_t *signs;
   uint16_t *norm;
   uint16_t *rnorm;
   int64_t out_offset;
@@ -34,7 +33,6 @@ struct LogitArgs {
   const float *s_mat;    // S (PROD)
   const float *centroids;
   const uint8_t *codes;
-  const uint8_t *signs;
   const uint16_t *norm;
   const uint16_t *rnorm;
   int64_t row_tokens, seq_len;
@@ -58,7 +56,6 @@ struct DequantArgs {
   const float *s_mat;
   const float *centroids;
   const uint8_t *codes;
-  const uint8_t *signs;
   const uint16_t *norm;
   const uint16_t *rnorm;
   int64_t n_vec;
@@ -70,5 +67,12 @@ hipError_t launch_dequant(int d, int lbits, bool prod, const DequantArgs &a, hip
                           bool *supported);
 
 int device_cu_count();
+
+// Scratch memory for one call on stream `s` of the current device.  The
+// library keeps one buffer per (device, stream), grows it with hipMalloc when
+// a call needs more (after synchronising that stream, whose queued work may
+// still read the old buffer) and keeps it until the process ends.  Work on
+// one stream runs in order, so successive calls on it can share the buffer.
+hipError_t workspace(hipStream_t s, size_t bytes, void **out);
 
 }  // namespace tqi

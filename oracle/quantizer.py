@@ -17,9 +17,13 @@ Page "TurboQuant 설명: 무엇인지와 LLM 메모리 6배 절약 구현 방법
 Packed format (reading R4 in the design doc; the page fixes no layout):
 * MSE mode: b' = b Lloyd-Max bits per coordinate.  Inner-product ("prod")
   mode: b' = b - 1 Lloyd-Max bits plus one QJL sign bit per coordinate.
-* ``codes`` row: b' bit planes of ceil(d/8) bytes each; bit i of byte k of
-  plane p is bit p of the index of coordinate 8k + i.
-* ``signs`` row (prod): ceil(d/8) bytes, bit j = [z_j >= 0], z = S r.
+* Every coordinate carries a b-bit record: bits 0..b'-1 hold its Lloyd-Max
+  index and, in prod mode, bit b' holds its QJL sign bit [z_j >= 0], z = S r.
+* ``codes`` row: the records as word-interleaved bit planes.  Coordinates are
+  taken in groups of 32 (the last group zero-padded); group g holds b
+  little-endian 32-bit words, one per plane, at bytes 4 (b g + p) ..
+  4 (b g + p) + 3, and bit i of the word of plane p is bit p of the record of
+  coordinate 32 g + i.  A row is 4 b ceil(d/32) bytes.
 * ``norm``: fp16 (round to nearest even) of ||x||_2; ``rnorm`` (prod): fp16 of
   gamma = ||u - Pi^T c_hat||_2, the residual norm of the unit vector u.
 * Index of coordinate j: idx_j = #{k : y_j >= t_k}, y = Pi x / ||x||, t the
@@ -75,40 +79,43 @@ def plane_bytes(d):
     return (d + 7) // 8
 
 
+def code_row_bytes(d, nbits):
+    return 4 * nbits * ((d + 31) // 32)
+
+
 def pack_planes(idx, nbits):
-    """[n, d] indices -> [n, nbits * ceil(d/8)] bit-plane rows (LSB first)."""
+    """[n, d] indices -> [n, 4 nbits ceil(d/32)] word-interleaved bit planes."""
     idx = np.asarray(idx, dtype=np.int64)
-    planes = [np.packbits(((idx >> p) & 1).astype(np.uint8), axis=1, bitorder="little")
-              for p in range(nbits)]
-    return np.concatenate(planes, axis=1)
+    n, d = idx.shape
+    groups = (d + 31) // 32
+    pad = np.zeros((n, 32 * groups), dtype=np.int64)
+    pad[:, :d] = idx
+    bits = np.stack([(pad >> p) & 1 for p in range(nbits)], axis=1)       # [n, p, 32 G]
+    bits = bits.reshape(n, nbits, groups, 32).transpose(0, 2, 1, 3)        # [n, G, p, 32]
+    words = np.packbits(bits.astype(np.uint8), axis=3, bitorder="little")  # [n, G, p, 4]
+    return words.reshape(n, groups * nbits * 4)
 
 
 def unpack_planes(codes, nbits, d):
     """Inverse of ``pack_planes``."""
     codes = np.asarray(codes, dtype=np.uint8)
-    pb = plane_bytes(d)
-    idx = np.zeros((codes.shape[0], d), dtype=np.int64)
+    n = codes.shape[0]
+    groups = (d + 31) // 32
+    words = codes.reshape(n, groups, nbits, 4)
+    bits = np.unpackbits(words, axis=3, bitorder="little")                 # [n, G, p, 32]
+    bits = bits.transpose(0, 2, 1, 3).reshape(n, nbits, 32 * groups)[:, :, :d]
+    idx = np.zeros((n, d), dtype=np.int64)
     for p in range(nbits):
-        bits = np.unpackbits(codes[:, p * pb:(p + 1) * pb], axis=1, bitorder="little")[:, :d]
-        idx |= bits.astype(np.int64) << p
+        idx |= bits[:, p].astype(np.int64) << p
     return idx
-
-
-def pack_signs(bits):
-    """[n, d] booleans -> [n, ceil(d/8)] bytes (LSB first)."""
-    return np.packbits(np.asarray(bits, dtype=np.uint8), axis=1, bitorder="little")
-
-
-def unpack_signs(signs, d):
-    return np.unpackbits(np.asarray(signs, dtype=np.uint8), axis=1, bitorder="little")[:, :d]
 
 
 def quantize(x, pi, centroids, boundaries, mode, s_mat=None):
     """Quantise rows of ``x`` (any float dtype, converted exactly to fp64).
 
-    Returns a dict with the packed outputs (``codes``, ``signs``, ``norm``,
-    ``rnorm``) and the intermediate fp64 values the parity rules need
-    (``idx``, ``u_rot`` = y / n, ``z``, ``gamma``).
+    Returns a dict with the packed outputs (``codes``, ``norm``, ``rnorm``) and
+    the intermediate fp64 values the parity rules need (``idx``, ``u_rot`` =
+    y / n, ``sign_bits``, ``z``, ``gamma``).
     """
     x = np.asarray(x, dtype=np.float64)
     n_vec, d = x.shape
@@ -123,10 +130,8 @@ def quantize(x, pi, centroids, boundaries, mode, s_mat=None):
     out = {
         "idx": idx,
         "u_rot": u_rot,
-        "codes": pack_planes(idx, nbits),
         "norm": to_fp16_bits(norm),
         "norm64": norm,
-        "signs": None,
         "rnorm": None,
     }
     if mode == MODE_PROD:
@@ -140,34 +145,42 @@ def quantize(x, pi, centroids, boundaries, mode, s_mat=None):
         zero = norm == 0.0
         bits[zero, :] = True
         gamma = np.where(zero, 0.0, gamma)
-        out.update(signs=pack_signs(bits), rnorm=to_fp16_bits(gamma), gamma=gamma,
-                   z=z, sign_bits=bits)
+        out.update(rnorm=to_fp16_bits(gamma), gamma=gamma, z=z, sign_bits=bits)
+        out["codes"] = pack_planes(idx | (bits.astype(np.int64) << nbits), nbits + 1)
+    else:
+        out["codes"] = pack_planes(idx, nbits)
     return out
 
 
-def dequantize(codes, norm, pi, centroids, mode, signs=None, rnorm=None, s_mat=None):
+def unpack_records(codes, nbits, mode, d):
+    """Lloyd-Max indices [n, d] and, in prod mode, sign bits [n, d] of a row."""
+    if mode == MODE_PROD:
+        rec = unpack_planes(codes, nbits + 1, d)
+        return rec & ((1 << nbits) - 1), (rec >> nbits) & 1
+    return unpack_planes(codes, nbits, d), None
+
+
+def dequantize(codes, norm, pi, centroids, mode, rnorm=None, s_mat=None):
     """x_hat = n16 (Pi^T c_hat + kappa gamma16 S^T s) for every packed row."""
     c = np.asarray(centroids, dtype=np.float64)
     d = pi.shape[0]
     nbits = int(round(math.log2(c.size)))
-    idx = unpack_planes(codes, nbits, d)
+    idx, sbits = unpack_records(codes, nbits, mode, d)
     xhat = c[idx] @ pi
     if mode == MODE_PROD:
-        s = 2.0 * unpack_signs(signs, d).astype(np.float64) - 1.0
+        s = 2.0 * sbits.astype(np.float64) - 1.0
         gamma = from_fp16_bits(rnorm)
         xhat = xhat + qjl_kappa(s_mat.shape[0]) * gamma[:, None] * (s @ s_mat)
     return from_fp16_bits(norm)[:, None] * xhat
 
 
-def logits_dequant(q, codes, norm, pi, centroids, mode, scale, signs=None, rnorm=None,
-                   s_mat=None):
+def logits_dequant(q, codes, norm, pi, centroids, mode, scale, rnorm=None, s_mat=None):
     """Plain definition: scale * <q_h, x_hat_t> for queries [H, d] and keys [T]."""
-    xhat = dequantize(codes, norm, pi, centroids, mode, signs, rnorm, s_mat)
+    xhat = dequantize(codes, norm, pi, centroids, mode, rnorm, s_mat)
     return scale * (np.asarray(q, dtype=np.float64) @ xhat.T)
 
 
-def logits_rotated(q, codes, norm, pi, centroids, mode, scale, signs=None, rnorm=None,
-                   s_mat=None):
+def logits_rotated(q, codes, norm, pi, centroids, mode, scale, rnorm=None, s_mat=None):
     """Same value through the pre-rotated query (page: query rotated once).
 
     <q, Pi^T c_hat> = <Pi q, c_hat> and <q, S^T s> = <S q, s>, so the keys are
@@ -177,11 +190,11 @@ def logits_rotated(q, codes, norm, pi, centroids, mode, scale, signs=None, rnorm
     c = np.asarray(centroids, dtype=np.float64)
     d = pi.shape[0]
     nbits = int(round(math.log2(c.size)))
-    idx = unpack_planes(codes, nbits, d)
+    idx, sbits = unpack_records(codes, nbits, mode, d)
     q_rot = q @ pi.T                                   # rows of Pi q
     acc = q_rot @ c[idx].T
     if mode == MODE_PROD:
-        s = 2.0 * unpack_signs(signs, d).astype(np.float64) - 1.0
+        s = 2.0 * sbits.astype(np.float64) - 1.0
         q_proj = q @ s_mat.T                           # rows of S q
         gamma = from_fp16_bits(rnorm)
         acc = acc + qjl_kappa(s_mat.shape[0]) * gamma[None, :] * (q_proj @ s.T)
@@ -193,7 +206,7 @@ def gqa_logits(q, cache, pi, centroids, mode, scale, s_mat=None, seq_len=None,
     """Logits [B, Hq, T] for queries [B, Hq, d] over a packed cache.
 
     ``cache`` holds ``codes`` [B, Hkv, T, row], ``norm`` [B, Hkv, T] and, in
-    prod mode, ``signs`` / ``rnorm``.  Query head h reads KV head
+    prod mode, ``rnorm`` [B, Hkv, T].  Query head h reads KV head
     h // (Hq / Hkv).
     """
     q = np.asarray(q, dtype=np.float64)
@@ -208,8 +221,7 @@ def gqa_logits(q, cache, pi, centroids, mode, scale, s_mat=None, seq_len=None,
             sl = slice(0, t_len)
             kw = {}
             if mode == MODE_PROD:
-                kw = dict(signs=cache["signs"][b, h, sl], rnorm=cache["rnorm"][b, h, sl],
-                          s_mat=s_mat)
+                kw = dict(rnorm=cache["rnorm"][b, h, sl], s_mat=s_mat)
             out[b, h * group:(h + 1) * group] = fn(
                 q[b, h * group:(h + 1) * group], cache["codes"][b, h, sl],
                 cache["norm"][b, h, sl], pi, centroids, mode, scale, **kw)

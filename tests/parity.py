@@ -1,9 +1,11 @@
 """Shared helpers of the GPU parity tests: oracle tables, tolerance rules.
 
 Tolerance rules ("Parity rules"):
-* codes: bit-exact, except coordinates whose oracle value u = y/n lies within
+* codes (the per-coordinate records): Lloyd-Max indices bit-exact, except
+  coordinates whose oracle value u = y/n lies within
   1e-5 of a decision boundary; those are counted and must stay under 0.01%
-  of all coordinates.  QJL signs the same with value z/gamma and boundary 0.
+  of all coordinates.  QJL sign bits the same with value z/gamma and
+  boundary 0.
 * norm: bit-exact fp16.  rnorm: within one fp16 ulp (the residual is formed
   from fp32 sums on the device); flips counted.
 * logits from identical (oracle-packed) codes: |l_gpu - l_orc| <= 1e-4 *
@@ -48,13 +50,12 @@ def dev_bf16(bits, device):
 def cache_from_oracle(tq, ref, d, bits, mode, device):
     return tq.PackedKV.from_tensors(
         d, bits, mode, torch.from_numpy(ref["codes"]).to(device), dev_u16(ref["norm"], device),
-        torch.from_numpy(ref["signs"]).to(device) if ref["signs"] is not None else None,
         dev_u16(ref["rnorm"], device) if ref["rnorm"] is not None else None)
 
 
-def check_codes(gpu_codes, ref, lb, d, t):
+def check_codes(gpu_codes, ref, lb, d, t, mode=oqz.MODE_MSE):
     """Codes rule; returns (mismatched coordinates, total coordinates)."""
-    g = oqz.unpack_planes(gpu_codes, lb, d)
+    g, _ = oqz.unpack_records(gpu_codes, lb, mode, d)
     o = ref["idx"]
     bad = g != o
     n_bad = int(bad.sum())
@@ -67,8 +68,8 @@ def check_codes(gpu_codes, ref, lb, d, t):
     return n_bad, o.size
 
 
-def check_signs(gpu_signs, ref, d):
-    g = oqz.unpack_signs(gpu_signs, d).astype(bool)
+def check_signs(gpu_codes, ref, lb, d):
+    g = oqz.unpack_records(gpu_codes, lb, oqz.MODE_PROD, d)[1].astype(bool)
     o = ref["sign_bits"]
     bad = g != o
     n_bad = int(bad.sum())

@@ -70,13 +70,14 @@ def test_quantize_parity(tq, d, bits, mode, dtype):
     qz.quantize(xt, out=cache, out_offset=off)
     torch.cuda.synchronize()
     codes = cache.codes.cpu().numpy()[off:off + n]
-    check_codes(codes, ref, ot.lb, d, ot.t)
+    check_codes(codes, ref, ot.lb, d, ot.t, mcode)
     check_norms(cache.norm.cpu().numpy()[off:off + n], ref)
-    assert np.all(oqz.unpack_planes(codes[3:4], ot.lb, d) == 1 << (ot.lb - 1))
+    idx3, sg3 = oqz.unpack_records(codes[3:4], ot.lb, mcode, d)
+    assert np.all(idx3 == 1 << (ot.lb - 1))
     if mcode == oqz.MODE_PROD:
-        check_signs(cache.signs.cpu().numpy()[off:off + n], ref, d)
+        check_signs(codes, ref, ot.lb, d)
         check_rnorm(cache.rnorm.cpu().numpy()[off:off + n], ref)
-        assert np.all(cache.signs.cpu().numpy()[off + 3] == 0xFF)
+        assert np.all(sg3 == 1)
         assert cache.rnorm.cpu().numpy()[off + 3] == 0
 
 
@@ -130,8 +131,7 @@ def test_logits_parity(tq, d, bits, mode, bsz, hkv, group, seq, qdtype):
         for h in range(hkv):
             kw = {}
             if mcode == oqz.MODE_PROD:
-                kw = dict(signs=ref["signs"].reshape(bsz, hkv, seq, -1)[b, h],
-                          rnorm=ref["rnorm"].reshape(bsz, hkv, seq)[b, h], s_mat=ot.s)
+                kw = dict(rnorm=ref["rnorm"].reshape(bsz, hkv, seq)[b, h], s_mat=ot.s)
             qq = q64[b, h * group:(h + 1) * group]
             want = oqz.logits_rotated(qq, codes[b, h], norm[b, h], ot.pi, ot.c, mcode, scale, **kw)
             check_logits(out[b, h * group:(h + 1) * group], want, scale, norm[b, h], qq)
@@ -149,7 +149,7 @@ def test_logits_row_tokens_capacity(tq):
         sl = slice(h * cap, h * cap + seq)
         qq = q64[0, h * group:(h + 1) * group]
         want = oqz.logits_rotated(qq, ref["codes"][sl], ref["norm"][sl], ot.pi, ot.c, mcode, 0.5,
-                                  signs=ref["signs"][sl], rnorm=ref["rnorm"][sl], s_mat=ot.s)
+                                  rnorm=ref["rnorm"][sl], s_mat=ot.s)
         check_logits(out[0, h * group:(h + 1) * group], want, 0.5, ref["norm"][sl], qq)
 
 
@@ -166,8 +166,8 @@ def test_dequantize_parity(tq, d, bits, mode):
     ref = ot.quantize(x64)
     qz = tq.Quantizer(d, bits, mcode, seed=0, device=DEV)
     cache = cache_from_oracle(tq, ref, d, bits, mcode, DEV)
-    want = oqz.dequantize(ref["codes"], ref["norm"], ot.pi, ot.c, mcode, signs=ref["signs"],
-                          rnorm=ref["rnorm"], s_mat=ot.s)
+    want = oqz.dequantize(ref["codes"], ref["norm"], ot.pi, ot.c, mcode, rnorm=ref["rnorm"],
+                          s_mat=ot.s)
     got = qz.dequantize(cache, n).cpu().numpy()
     check_dequant(got, want)
     assert np.all(got[3] == 0.0)
@@ -215,11 +215,10 @@ def test_end_to_end_quantize_then_logits(tq):
     out = qz.attn_logits(torch.from_numpy(q64.astype(np.float32)).reshape(1, group, d).to(DEV), cache,
                          n_kv_heads=1, seq_len=seq, scale=1 / np.sqrt(d)).cpu().numpy()[0]
     same = np.all(cache.codes.cpu().numpy() == ref["codes"], axis=1) & \
-        np.all(cache.signs.cpu().numpy() == ref["signs"], axis=1) & \
         (cache.rnorm.cpu().numpy().view(np.uint16) == ref["rnorm"])
     assert same.mean() > 0.99
     want = oqz.logits_rotated(q64, ref["codes"], ref["norm"], ot.pi, ot.c, oqz.MODE_PROD, 1 / np.sqrt(d),
-                              signs=ref["signs"], rnorm=ref["rnorm"], s_mat=ot.s)
+                              rnorm=ref["rnorm"], s_mat=ot.s)
     check_logits(out[:, same], want[:, same], 1 / np.sqrt(d), ref["norm"][same], q64)
 
 

@@ -82,7 +82,7 @@ def test_device_calls_validate_before_launch(tq):
     lib = tq.LIB
     dummy = ctypes.c_void_p(16)
     p = tq.Params(128, 3, tq.MODE_MSE, 0, dummy, None, None, dummy, dummy)
-    pk = tq.Packed(dummy, None, dummy, None)
+    pk = tq.Packed(dummy, dummy, None)
     # NULL params / bad bits / bad mode / reserved
     assert lib.tq_quantize_kv(None, dummy, 0, 1, 128, ctypes.byref(pk), 0, None) == tq.TQ_ERR_INVALID
     bad = tq.Params(128, 9, tq.MODE_MSE, 0, dummy, None, None, dummy, dummy)
@@ -117,6 +117,6 @@ def test_device_calls_validate_before_launch(tq):
                               None) == tq.TQ_ERR_UNSUPPORTED
     # d without a kernel (prod at d = 256) is reported before any launch
     p256 = tq.Params(256, 3, tq.MODE_PROD, 0, dummy, dummy, dummy, dummy, dummy)
-    pk2 = tq.Packed(dummy, dummy, dummy, dummy)
+    pk2 = tq.Packed(dummy, dummy, dummy)
     assert lib.tq_quantize_kv(ctypes.byref(p256), dummy, 0, 1, 256, ctypes.byref(pk2), 0,
                               None) == tq.TQ_ERR_UNSUPPORTED

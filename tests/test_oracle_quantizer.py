@@ -44,11 +44,11 @@ def test_worked_example_prod():
     out = qz.quantize(np.array([g["x"]]), np.eye(3), c, t, qz.MODE_PROD, s_mat=np.eye(3))
     assert out["idx"].tolist() == [e["idx"]]
     assert out["codes"].tolist() == [e["codes"]]
-    assert out["signs"].tolist() == [e["signs"]]
+    assert out["sign_bits"].astype(int).tolist() == [e["sign_bits"]]
     assert out["gamma"][0] == pytest.approx(e["gamma"], rel=1e-15)
     assert out["rnorm"].tolist() == [e["rnorm_fp16_bits"]]
     assert qz.qjl_kappa(3) == pytest.approx(e["kappa"], rel=1e-15)
-    kw = dict(signs=out["signs"], rnorm=out["rnorm"], s_mat=np.eye(3))
+    kw = dict(rnorm=out["rnorm"], s_mat=np.eye(3))
     xh = qz.dequantize(out["codes"], out["norm"], np.eye(3), c, qz.MODE_PROD, **kw)
     assert np.allclose(xh, [e["x_hat"]], atol=1e-9)
     lg = qz.logits_rotated(np.array([g["q"]]), out["codes"], out["norm"], np.eye(3), c,
@@ -57,26 +57,42 @@ def test_worked_example_prod():
 
 
 def test_plane_bit_order_by_hand():
-    # d = 10, 3 planes of 2 bytes: coordinate j sits at bit j % 8 of byte j // 8.
-    idx = np.array([[5, 0, 0, 0, 0, 0, 0, 0, 6, 1]])
+    # d = 40 (two 32-coordinate groups, the second zero-padded), 3 planes:
+    # group g holds one little-endian word per plane; bit i of the plane-p word
+    # is bit p of the index of coordinate 32 g + i.
+    idx = np.zeros((1, 40), dtype=np.int64)
+    idx[0, 0] = 5          # planes 0 and 2, group 0, bit 0
+    idx[0, 9] = 1          # plane 0, group 0, bit 9 -> byte 1 bit 1
+    idx[0, 33] = 6         # planes 1 and 2, group 1, bit 1
     codes = qz.pack_planes(idx, 3)
-    # plane 0: coords 0 and 9 -> byte0 bit0, byte1 bit1
-    # plane 1: coord 8      -> byte1 bit0
-    # plane 2: coords 0, 8  -> byte0 bit0, byte1 bit0
-    assert codes.tolist() == [[0x01, 0x02, 0x00, 0x01, 0x01, 0x01]]
+    want = [0x01, 0x02, 0, 0,   0, 0, 0, 0,   0x01, 0, 0, 0,      # group 0: p0, p1, p2
+            0, 0, 0, 0,   0x02, 0, 0, 0,   0x02, 0, 0, 0]         # group 1: p0, p1, p2
+    assert codes.tolist() == [want]
+    assert qz.code_row_bytes(40, 3) == 24
+
+
+def test_prod_record_puts_sign_on_top_plane():
+    # prod mode, b' = 2: record = idx | sign << 2, three planes per group.
+    c, t, _ = cb.codebook(32, 2)
+    x = np.zeros((1, 32))
+    x[0, 0] = 1.0
+    out = qz.quantize(x, np.eye(32), c, t, qz.MODE_PROD, s_mat=np.eye(32))
+    rec = qz.unpack_planes(out["codes"], 3, 32)
+    assert np.array_equal(rec & 3, out["idx"])
+    assert np.array_equal(rec >> 2, out["sign_bits"].astype(np.int64))
+    assert out["codes"].shape[1] == 12
 
 
 @pytest.mark.parametrize("nbits", [1, 2, 3, 4])
 def test_pack_roundtrip_bijective(nbits):
     d = 3 if nbits <= 3 else 2
     allidx = np.array(list(itertools.product(range(1 << nbits), repeat=d)))
+    assert qz.pack_planes(allidx, nbits).shape[1] == qz.code_row_bytes(d, nbits)
     codes = qz.pack_planes(allidx, nbits)
     assert np.array_equal(qz.unpack_planes(codes, nbits, d), allidx)
     assert len({bytes(r) for r in codes}) == allidx.shape[0]
     big = np.random.default_rng(nbits).integers(0, 1 << nbits, (50, 128))
     assert np.array_equal(qz.unpack_planes(qz.pack_planes(big, nbits), nbits, 128), big)
-    bits = np.random.default_rng(9).integers(0, 2, (50, 128)).astype(bool)
-    assert np.array_equal(qz.unpack_signs(qz.pack_signs(bits), 128).astype(bool), bits)
 
 
 def _setup(d, bits, mode, seed=0):
@@ -165,7 +181,7 @@ def test_qjl_estimator_unbiased():
     out = qz.quantize(x[None], pi, c2, t2, qz.MODE_PROD, s_mat=s_mat)
     assert out["gamma"][0] == pytest.approx(gamma, rel=1e-12)
     lg = qz.logits_rotated(q[None], out["codes"], out["norm"], pi, c2, qz.MODE_PROD, 1.0,
-                           signs=out["signs"], rnorm=out["rnorm"], s_mat=s_mat)
+                           rnorm=out["rnorm"], s_mat=s_mat)
     s_bits = np.where(s_mat @ r >= 0, 1.0, -1.0)
     by_hand = q_rot @ c_hat + qz.qjl_kappa(d) * qz.from_fp16_bits(out["rnorm"])[0] * ((s_mat @ q) @ s_bits)
     assert lg[0, 0] == pytest.approx(by_hand * qz.from_fp16_bits(out["norm"])[0], rel=1e-12)
@@ -178,7 +194,7 @@ def test_rotated_logits_equal_dequantize_then_dot(mode, bits):
     x = np.random.default_rng(4).standard_normal((300, d)) * 3
     q = np.random.default_rng(6).standard_normal((4, d))
     out = qz.quantize(x, pi, c, t, mode, s_mat=s_mat)
-    kw = dict(signs=out["signs"], rnorm=out["rnorm"], s_mat=s_mat) if mode == qz.MODE_PROD else {}
+    kw = dict(rnorm=out["rnorm"], s_mat=s_mat) if mode == qz.MODE_PROD else {}
     a = qz.logits_rotated(q, out["codes"], out["norm"], pi, c, mode, 0.125, **kw)
     b = qz.logits_dequant(q, out["codes"], out["norm"], pi, c, mode, 0.125, **kw)
     assert np.max(np.abs(a - b)) <= 1e-12 * np.max(np.abs(b))
@@ -192,8 +208,9 @@ def test_zero_gamma_reduces_to_mse():
     out = qz.quantize(x, pi, c, t, qz.MODE_PROD, s_mat=s_mat)
     zero = np.zeros_like(out["rnorm"])
     a = qz.logits_rotated(q, out["codes"], out["norm"], pi, c, qz.MODE_PROD, 1.0,
-                          signs=out["signs"], rnorm=zero, s_mat=s_mat)
-    b = qz.logits_rotated(q, out["codes"], out["norm"], pi, c, qz.MODE_MSE, 1.0)
+                          rnorm=zero, s_mat=s_mat)
+    # the same indices packed without the sign plane, read in MSE mode
+    b = qz.logits_rotated(q, qz.pack_planes(out["idx"], 2), out["norm"], pi, c, qz.MODE_MSE, 1.0)
     assert np.array_equal(a, b)
 
 
@@ -205,9 +222,10 @@ def test_zero_vector():
     out = qz.quantize(x, pi, c, t, qz.MODE_PROD, s_mat=s_mat)
     assert np.all(out["idx"][0] == 2)        # 2^(b'-1): the upper middle cell
     assert out["norm"][0] == 0 and out["rnorm"][0] == 0
-    assert np.all(out["signs"][0] == 0xFF)
-    xh = qz.dequantize(out["codes"], out["norm"], pi, c, qz.MODE_PROD, signs=out["signs"],
-                       rnorm=out["rnorm"], s_mat=s_mat)
+    assert np.all(out["sign_bits"][0])
+    idx, sb = qz.unpack_records(out["codes"], 2, qz.MODE_PROD, d)
+    assert np.all(sb[0] == 1) and np.all(idx[0] == 2)
+    xh = qz.dequantize(out["codes"], out["norm"], pi, c, qz.MODE_PROD, rnorm=out["rnorm"], s_mat=s_mat)
     assert np.all(xh[0] == 0.0)
 
 
