@@ -69,6 +69,12 @@ __device__ void load_stationary(const float *__restrict__ mat, int w, half8 (&hi
   }
 }
 
+// Raw input of one staging thread: 16 consecutive elements of one vector.
+template <bool IN_F32>
+struct RawInput {
+  i32x4 q[IN_F32 ? 4 : 2];
+};
+
 template <int D, int LB, bool PROD, bool IN_F32>
 __global__ __launch_bounds__(QLayout<D>::NT) void quantize_kernel(tqi::QuantizeArgs a) {
   using L = QLayout<D>;
@@ -76,17 +82,23 @@ __global__ __launch_bounds__(QLayout<D>::NT) void quantize_kernel(tqi::QuantizeA
   constexpr int PB = D / 8;                   // bytes per plane
   constexpr int NPL = LB + (PROD ? 1 : 0);    // planes per record (sign on top)
   constexpr int RB = NPL * PB;                // bytes per packed row
-  __shared__ __attribute__((aligned(16))) _Float16 xh[32 * L::PITCH];
-  __shared__ __attribute__((aligned(16))) _Float16 xl[IN_F32 ? 32 * L::PITCH : 1];
-  __shared__ __attribute__((aligned(16))) _Float16 rh[PROD ? 32 * L::PITCH : 1];
-  __shared__ __attribute__((aligned(16))) _Float16 rl[PROD ? 32 * L::PITCH : 1];
-  __shared__ __attribute__((aligned(16))) float vinv[32];
+  constexpr int TILE = 32 * L::PITCH;
+  // Two LDS buffers, alternated per tile: a tile's staging never overwrites
+  // data that the previous tile may still read, so one barrier per stage
+  // suffices.
+  __shared__ __attribute__((aligned(16))) _Float16 xh[2][TILE];
+  __shared__ __attribute__((aligned(16))) _Float16 xl[IN_F32 ? 2 : 1][IN_F32 ? TILE : 8];
+  __shared__ __attribute__((aligned(16))) _Float16 rh[PROD ? 2 : 1][PROD ? TILE : 8];
+  __shared__ __attribute__((aligned(16))) _Float16 rl[PROD ? 2 : 1][PROD ? TILE : 8];
+  __shared__ __attribute__((aligned(16))) float vinv[2][32];
 
   const int tid = threadIdx.x;
   const int w = tid / kWave;
   const int l = lane_id();
   const int m = l & 31;          // MFMA row (A) / column (B, C) of this lane
   const int h = l >> 5;          // K group / row group
+  const int sv_v = tid / L::TPV; // staging: vector within the tile
+  const int sv_c = tid % L::TPV; //          16-element chunk of it
 
   half8 pih[L::KS], pil[L::KS];
   load_stationary<D>(a.pi, w, pih, pil);
@@ -101,45 +113,51 @@ __global__ __launch_bounds__(QLayout<D>::NT) void quantize_kernel(tqi::QuantizeA
   for (int k = 0; k < K; ++k) cen[k] = PROD ? a.centroids[k] : 0.0f;
 
   const int64_t n_tiles = (a.n_vec + 31) / 32;
-  for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
-    const int64_t base = tile * 32;
-    // ---------------------------------------------------------------- stage
+
+  // Buffer resources over this call's rows.  The host keeps every range below
+  // 2^31 bytes (large calls are split), so rows past n_vec and kNoStore fall
+  // outside: such loads return 0 and such stores are dropped by the hardware.
+  // No load or store sits behind a branch, which lets the compiler wait for
+  // the next tile's loads without also waiting for this tile's stores.
+  constexpr int ESZ = IN_F32 ? 4 : 2;
+  const i32x4 rx = make_rsrc(a.x, (uint32_t)(((a.n_vec - 1) * a.x_stride + D) * ESZ));
+  const i32x4 rc = make_rsrc(a.codes + a.out_offset * RB, (uint32_t)(a.n_vec * RB));
+  const i32x4 rn = make_rsrc(a.norm + a.out_offset, (uint32_t)(a.n_vec * 2));
+  const i32x4 rr = make_rsrc(PROD ? a.rnorm + a.out_offset : a.norm, PROD ? (uint32_t)(a.n_vec * 2) : 0u);
+
+  // Non-temporal loads of a tile's inputs (16 elements per staging thread).
+  auto load_raw = [&](int64_t tile, RawInput<IN_F32> &r) {
+    const int64_t gv = tile * 32 + sv_v;
+    const uint32_t off = gv < a.n_vec ? (uint32_t)((gv * a.x_stride + 16 * sv_c) * ESZ) : kNoStore;
+#pragma unroll
+    for (int q = 0; q < (IN_F32 ? 4 : 2); ++q) r.q[q] = tq_llvm_buf_ld_b128(rx, (int)(off + 16 * q), 0, kStream);
+  };
+
+  // Stages a tile into LDS buffer `buf`; returns this thread's fp16 norm
+  // bits, stored by the caller once the next tile's loads are in flight.
+  auto stage = [&](int64_t tile, const RawInput<IN_F32> &r, int buf) -> uint16_t {
     {
-      const int v = tid / L::TPV;
-      const int c = tid % L::TPV;
-      const int64_t gv = base + v;
-      const bool valid = gv < a.n_vec;
       float xv[16];
-      if (valid) {
-        if constexpr (IN_F32) {
-          const f32x4 *p = (const f32x4 *)((const float *)a.x + gv * a.x_stride + 16 * c);
+      if constexpr (IN_F32) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            f32x4 t = p[q];
-            xv[4 * q] = t[0]; xv[4 * q + 1] = t[1]; xv[4 * q + 2] = t[2]; xv[4 * q + 3] = t[3];
-          }
-        } else {
-          const i32x4 *p = (const i32x4 *)((const uint16_t *)a.x + gv * a.x_stride + 16 * c);
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            i32x4 t = p[q];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              uint32_t u = (uint32_t)t[e];
-              xv[8 * q + 2 * e] = __uint_as_float(u << 16);
-              xv[8 * q + 2 * e + 1] = __uint_as_float(u & 0xFFFF0000u);
-            }
-          }
-        }
+          for (int e = 0; e < 4; ++e) xv[4 * q + e] = __int_as_float(r.q[q][e]);
       } else {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) xv[i] = 0.0f;
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t u = (uint32_t)r.q[q][e];
+            xv[8 * q + 2 * e] = __uint_as_float(u << 16);
+            xv[8 * q + 2 * e + 1] = __uint_as_float(u & 0xFFFF0000u);
+          }
       }
       double ss = 0.0;
       float mx = 0.0f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        ss += (double)xv[i] * (double)xv[i];
+        ss = fma((double)xv[i], (double)xv[i], ss);
         mx = fmaxf(mx, fabsf(xv[i]));
       }
 #pragma unroll
@@ -153,27 +171,40 @@ __global__ __launch_bounds__(QLayout<D>::NT) void quantize_kernel(tqi::QuantizeA
         e = e < -140 ? -140 : (e > 127 ? 127 : e);
       }
       const float sc = ldexpf(1.0f, 14 - e);
-      const double nrm = sqrt(ss);
+      half8 hv[2], lv[2];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float sv = xv[i] * sc;
-        _Float16 hv = (_Float16)sv;
-        xh[v * L::PITCH + 16 * c + i] = hv;
-        if constexpr (IN_F32) xl[v * L::PITCH + 16 * c + i] = (_Float16)(sv - (float)hv);
+        const float sv = xv[i] * sc;
+        const _Float16 hh = (_Float16)sv;
+        hv[i >> 3][i & 7] = hh;
+        if constexpr (IN_F32) lv[i >> 3][i & 7] = (_Float16)(sv - (float)hh);
       }
-      if (c == 0) {
-        vinv[v] = nrm > 0.0 ? (float)(1.0 / ((double)sc * (double)kPiScale * nrm)) : 0.0f;
-        if (valid) a.norm[a.out_offset + gv] = f64_to_f16_bits(nrm);
+      half8 *dh = (half8 *)&xh[buf][sv_v * L::PITCH + 16 * sv_c];
+      dh[0] = hv[0];
+      dh[1] = hv[1];
+      if constexpr (IN_F32) {
+        half8 *dl = (half8 *)&xl[buf][sv_v * L::PITCH + 16 * sv_c];
+        dl[0] = lv[0];
+        dl[1] = lv[1];
       }
+      // 1 / (sc * 2^8 * |x|): the scaled sum of squares lies in [2^28, 2^37),
+      // so fp32 holds it; v_rsq_f32 is good to about one ulp.
+      const float ss_sc = (float)(ss * ((double)sc * (double)sc));
+      const float inv_n = ss > 0.0 ? __builtin_amdgcn_rsqf(ss_sc) * (1.0f / kPiScale) : 0.0f;
+      if (sv_c == 0) vinv[buf][sv_v] = inv_n;
+      return f64_to_f16_bits(sqrt(ss));
     }
-    __syncthreads();
+  };
+
+  auto compute = [&](int64_t tile, int buf) {
+    const int64_t base = tile * 32;
     // ---------------------------------------------------------- y = X Pi^T
     f32x16 acc = {};
 #pragma unroll
     for (int s = 0; s < L::KS; ++s) {
-      half8 ah = *(const half8 *)&xh[m * L::PITCH + 16 * s + 8 * h];
+      half8 ah = *(const half8 *)&xh[buf][m * L::PITCH + 16 * s + 8 * h];
       if constexpr (IN_F32) {
-        half8 al = *(const half8 *)&xl[m * L::PITCH + 16 * s + 8 * h];
+        half8 al = *(const half8 *)&xl[buf][m * L::PITCH + 16 * s + 8 * h];
         acc = mfma32(al, pih[s], acc);
       }
       acc = mfma32(ah, pil[s], acc);
@@ -183,7 +214,7 @@ __global__ __launch_bounds__(QLayout<D>::NT) void quantize_kernel(tqi::QuantizeA
     float inv[16];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      f32x4 t = *(const f32x4 *)&vinv[8 * g + 4 * h];
+      f32x4 t = *(const f32x4 *)&vinv[buf][8 * g + 4 * h];
       inv[4 * g] = t[0]; inv[4 * g + 1] = t[1]; inv[4 * g + 2] = t[2]; inv[4 * g + 3] = t[3];
     }
     uint32_t outw[2] = {0u, 0u};   // up to 128 plane words per wave
@@ -193,15 +224,26 @@ __global__ __launch_bounds__(QLayout<D>::NT) void quantize_kernel(tqi::QuantizeA
       uint64_t planes[LB];
 #pragma unroll
       for (int p = 0; p < LB; ++p) planes[p] = 0;
-      float chat = cen[0];
+      uint64_t ge[K - 1];   // thermometer masks: bit l = (u >= t_k) in lane l
 #pragma unroll
       for (int k = 0; k < K - 1; ++k) {
-        const bool ge = u >= bnd[k];
-        const uint64_t mk = __ballot(ge);
-        if constexpr (PROD) chat = ge ? cen[k + 1] : chat;
+        ge[k] = __ballot(u >= bnd[k]);
 #pragma unroll
         for (int p = 0; p < LB; ++p)
-          if (((k + 1) & ((1 << p) - 1)) == 0) planes[p] ^= mk;
+          if (((k + 1) & ((1 << p) - 1)) == 0) planes[p] ^= ge[k];
+      }
+      // Centroid of the chosen cell from the thermometer masks, using the
+      // codebook's antisymmetry c[K/2-1-j] = -c[K/2+j]: pick the magnitude
+      // level j (|idx - K/2 + 1/2| - 1/2 >= j  <=>  idx >= K/2+j or
+      // idx <= K/2-1-j), then the sign (idx >= K/2  <=>  u >= t[K/2-1]).
+      float chat = 0.0f;
+      if constexpr (PROD) {
+        constexpr int MID = K / 2;
+        float mag = cen[MID];
+#pragma unroll
+        for (int j = 1; j < MID; ++j)   // mask logic stays on the scalar unit
+          mag = __builtin_amdgcn_inverse_ballot_w64(ge[MID - 1 + j] | ~ge[MID - 1 - j]) ? cen[MID + j] : mag;
+        chat = __builtin_amdgcn_inverse_ballot_w64(ge[MID - 1]) ? mag : -mag;
       }
 #pragma unroll
       for (int p = 0; p < LB; ++p) {
@@ -216,24 +258,23 @@ __global__ __launch_bounds__(QLayout<D>::NT) void quantize_kernel(tqi::QuantizeA
         const int v = 8 * (r >> 2) + 4 * h + (r & 3);
         const float rs = (u - chat) * kResScale;
         const _Float16 hv = (_Float16)rs;
-        rh[v * L::PITCH + 32 * w + m] = hv;
-        rl[v * L::PITCH + 32 * w + m] = (_Float16)(rs - (float)hv);
+        rh[buf][v * L::PITCH + 32 * w + m] = hv;
+        rl[buf][v * L::PITCH + 32 * w + m] = (_Float16)(rs - (float)hv);
       }
     }
     // store plane words: slot = (r*LB + p)*2 + hh -> vector 8(r/4)+4hh+r%4
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      const int slot = 64 * g + l;
-      if (slot < 32 * LB) {
+      if (64 * g < 32 * LB) {
+        const int slot = 64 * g + l;
         const int hh = slot & 1;
         const int p = (slot >> 1) % LB;
         const int r = (slot >> 1) / LB;
         const int v = 8 * (r >> 2) + 4 * hh + (r & 3);
         const int64_t gv = base + v;
-        if (gv < a.n_vec) {
-          uint32_t *dst = (uint32_t *)(a.codes + (a.out_offset + gv) * RB + 4 * (w * NPL + p));
-          *dst = outw[g];
-        }
+        const uint32_t off =
+            (slot < 32 * LB && gv < a.n_vec) ? (uint32_t)(gv * RB + 4 * (w * NPL + p)) : kNoStore;
+        buf_store_u32(rc, off, outw[g]);
       }
     }
     if constexpr (PROD) {
@@ -242,8 +283,8 @@ __global__ __launch_bounds__(QLayout<D>::NT) void quantize_kernel(tqi::QuantizeA
       f32x16 acc2 = {};
 #pragma unroll
       for (int s = 0; s < L::KS; ++s) {
-        half8 ah = *(const half8 *)&rh[m * L::PITCH + 16 * s + 8 * h];
-        half8 al = *(const half8 *)&rl[m * L::PITCH + 16 * s + 8 * h];
+        half8 ah = *(const half8 *)&rh[buf][m * L::PITCH + 16 * s + 8 * h];
+        half8 al = *(const half8 *)&rl[buf][m * L::PITCH + 16 * s + 8 * h];
         acc2 = mfma32(al, mh[s], acc2);
         acc2 = mfma32(ah, ml[s], acc2);
         acc2 = mfma32(ah, mh[s], acc2);
@@ -251,54 +292,100 @@ __global__ __launch_bounds__(QLayout<D>::NT) void quantize_kernel(tqi::QuantizeA
       uint32_t sw = 0u;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const uint64_t mk = __ballot(acc2[r] >= 0.0f || inv[r] == 0.0f);
+        const uint64_t mk = __ballot(acc2[r] >= 0.0f);
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-          sw = write_lane(sw, (uint32_t)(mk >> (32 * hh)), 2 * r + hh);
+        for (int hh = 0; hh < 2; ++hh) sw = write_lane(sw, (uint32_t)(mk >> (32 * hh)), 2 * r + hh);
       }
-      if (l < 32) {
-        const int r = l >> 1, hh = l & 1;
+      {
+        const int r = (l >> 1) & 15, hh = l & 1;
         const int v = 8 * (r >> 2) + 4 * hh + (r & 3);
         const int64_t gv = base + v;
-        if (gv < a.n_vec) *(uint32_t *)(a.codes + (a.out_offset + gv) * RB + 4 * (w * NPL + LB)) = sw;
+        if (vinv[buf][v] == 0.0f) sw = 0xFFFFFFFFu;   // zero vector: all signs +1
+        const uint32_t off = (l < 32 && gv < a.n_vec) ? (uint32_t)(gv * RB + 4 * (w * NPL + LB)) : kNoStore;
+        buf_store_u32(rc, off, sw);
       }
       // residual norm of the unit vector from the staged residual tile
       {
-        const int v = tid / L::TPV;
-        const int c = tid % L::TPV;
-        float ss = 0.0f;
+        // sum of (hi + lo)^2 = hi.hi + 2 hi.lo + lo.lo, each term a
+        // two-wide fp16 dot product accumulated in fp32 (v_dot2_f32_f16)
+        float s_hh = 0.0f, s_hl = 0.0f, s_ll = 0.0f;
+        const half8 *ph = (const half8 *)&rh[buf][sv_v * L::PITCH + 16 * sv_c];
+        const half8 *pl = (const half8 *)&rl[buf][sv_v * L::PITCH + 16 * sv_c];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float r = (float)rh[v * L::PITCH + 16 * c + i] + (float)rl[v * L::PITCH + 16 * c + i];
-          ss += r * r;
+        for (int q = 0; q < 2; ++q) {
+          const half8 hq = ph[q], lq = pl[q];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const half2 h2 = {hq[2 * i], hq[2 * i + 1]}, l2 = {lq[2 * i], lq[2 * i + 1]};
+            s_hh = __builtin_amdgcn_fdot2(h2, h2, s_hh, false);
+            s_hl = __builtin_amdgcn_fdot2(h2, l2, s_hl, false);
+            s_ll = __builtin_amdgcn_fdot2(l2, l2, s_ll, false);
+          }
         }
+        float ss = s_hh + (2.0f * s_hl + s_ll);
 #pragma unroll
         for (int off = 1; off < L::TPV; off <<= 1) ss += wave_xor(ss, off);
-        const int64_t gv = base + v;
-        if (c == 0 && gv < a.n_vec) {
-          const float gam = vinv[v] == 0.0f ? 0.0f : sqrtf(ss) * (1.0f / kResScale);
-          a.rnorm[a.out_offset + gv] = f32_to_f16_bits(gam);
-        }
+        const int64_t gv = base + sv_v;
+        const float gam = vinv[buf][sv_v] == 0.0f ? 0.0f : sqrtf(ss) * (1.0f / kResScale);
+        buf_store_u16(rr, (sv_c == 0 && gv < a.n_vec) ? (uint32_t)(2 * gv) : kNoStore, f32_to_f16_bits(gam));
       }
     }
+  };
+
+  // One register set of raw input: the next tile's loads are issued as soon
+  // as the current tile has been staged, so they fly during its GEMMs and
+  // coding.
+  const int64_t step = gridDim.x;
+  int64_t tile = blockIdx.x;
+  RawInput<IN_F32> raw;
+  load_raw(tile, raw);
+  // Range-dropped stores: with them, on entry as on every later iteration,
+  // stores follow the pending input loads, so the compiler can wait for
+  // those loads alone (it merges the counts of both paths into the loop).
+#pragma unroll
+  for (int i = 0; i < 5; ++i) buf_store_u32(rn, kNoStore + 4 * i, 0u);
+  int buf = 0;
+  for (; tile < n_tiles; tile += step, buf ^= 1) {
+    const uint16_t n16 = stage(tile, raw, buf);
+    load_raw(tile + step, raw);
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t gv = tile * 32 + sv_v;
+    buf_store_u16(rn, (sv_c == 0 && gv < a.n_vec) ? (uint32_t)(2 * gv) : kNoStore, n16);
     __syncthreads();
+    compute(tile, buf);
   }
 }
 
 template <int D, int LB, bool PROD, bool IN_F32>
 hipError_t launch_t(const tqi::QuantizeArgs &a, hipStream_t s) {
   using L = QLayout<D>;
-  const int64_t n_tiles = (a.n_vec + 31) / 32;
+  constexpr int64_t ESZ = IN_F32 ? 4 : 2;
+  constexpr int64_t RB = (LB + (PROD ? 1 : 0)) * D / 8;
+  constexpr int64_t kRange = (int64_t{1} << 31) - 1;   // kernel byte ranges stay below 2^31
+  if (a.x_stride * ESZ > kRange) return hipErrorInvalidValue;
+  // Rows per launch so that the input, code and norm ranges fit.
+  int64_t rows = kRange / (a.x_stride * ESZ);
+  if (rows > kRange / RB) rows = kRange / RB;
+  if (rows >= 32) rows &= ~int64_t{31};
   int blocks_per_cu = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
       &blocks_per_cu, quantize_kernel<D, LB, PROD, IN_F32>, L::NT, 0);
   if (e != hipSuccess) return e;
   if (blocks_per_cu < 1) blocks_per_cu = 1;
-  int64_t grid = (int64_t)tqi::device_cu_count() * blocks_per_cu;
-  if (grid > n_tiles) grid = n_tiles;
-  hipLaunchKernelGGL((quantize_kernel<D, LB, PROD, IN_F32>), dim3((unsigned)grid), dim3(L::NT),
-                     0, s, a);
-  return hipGetLastError();
+  for (int64_t start = 0; start < a.n_vec; start += rows) {
+    tqi::QuantizeArgs c = a;
+    c.x = (const char *)a.x + start * a.x_stride * ESZ;
+    c.n_vec = a.n_vec - start < rows ? a.n_vec - start : rows;
+    c.out_offset = a.out_offset + start;
+    const int64_t n_tiles = (c.n_vec + 31) / 32;
+    int64_t grid = (int64_t)tqi::device_cu_count() * blocks_per_cu;
+    if (grid > n_tiles) grid = n_tiles;
+    hipLaunchKernelGGL((quantize_kernel<D, LB, PROD, IN_F32>), dim3((unsigned)grid), dim3(L::NT),
+                       0, s, c);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <int D, int LB, bool PROD>

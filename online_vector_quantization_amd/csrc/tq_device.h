@@ -7,6 +7,7 @@
 namespace tqd {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -54,41 +55,24 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
   return (uint16_t)(u >> 16);
 }
 
-// Correctly rounded (nearest even) fp64 -> fp16 bits, including subnormal
-// results and overflow to infinity.  Avoids the double rounding of
-// fp64 -> fp32 -> fp16.
+// Correctly rounded (nearest even) fp64 -> fp16 bits.  The value is first
+// rounded to fp32 with round-to-odd (round to nearest, step back toward zero
+// if that went up, then set the last bit when anything was dropped) and then
+// converted to fp16 by the hardware in nearest-even mode.  Rounding to odd at
+// a precision at least two bits finer than the target makes the second
+// rounding equal to a direct one (Boldo and Melquiond, "Emulation of FMA and
+// correctly rounded sums: proved algorithms using rounding to odd", IEEE
+// Trans. Computers 57(4), 2008); fp32 keeps 24 bits against fp16's 11.
+// Branch-free; overflow gives infinity, NaN stays NaN.
 __device__ __forceinline__ uint16_t f64_to_f16_bits(double v) {
-  uint64_t b = (uint64_t)__double_as_longlong(v);
-  uint16_t sign = (uint16_t)((b >> 48) & 0x8000u);
-  b &= 0x7FFFFFFFFFFFFFFFull;
-  if (b >= 0x7FF0000000000000ull) {  // inf or nan
-    return sign | (b > 0x7FF0000000000000ull ? 0x7E00u : 0x7C00u);
-  }
-  int e = (int)(b >> 52) - 1023;
-  uint64_t mant = (b & 0x000FFFFFFFFFFFFFull) | 0x0010000000000000ull;
-  if ((b >> 52) == 0) return sign;  // fp64 subnormal -> 0 in fp16
-  if (e > 15) return sign | 0x7C00u;
-  int shift;
-  uint32_t base;
-  if (e >= -14) {
-    shift = 42;  // keep 11 significant bits
-    base = (uint32_t)(e + 15) << 10;
-  } else {
-    shift = 42 + (-14 - e);  // subnormal: units of 2^-24
-    base = 0;
-    if (shift > 63) return sign;
-  }
-  uint64_t q = mant >> shift;
-  uint64_t rem = mant & ((1ull << shift) - 1);
-  uint64_t half = 1ull << (shift - 1);
-  if (rem > half || (rem == half && (q & 1))) q += 1;
-  uint32_t res;
-  if (e >= -14)
-    res = base + (uint32_t)(q - 1024);  // carry into the exponent is correct
-  else
-    res = (uint32_t)q;                  // may round up into the smallest normal
-  if (res >= 0x7C00u) res = 0x7C00u;
-  return sign | (uint16_t)res;
+  const double av = fabs(v);
+  const float f = (float)av;
+  const double back = (double)f;
+  uint32_t u = __float_as_uint(f);
+  u -= back > av ? 1u : 0u;
+  u |= back != av ? 1u : 0u;
+  const uint16_t sign = (uint16_t)((__double_as_longlong(v) >> 48) & 0x8000);
+  return sign | f32_to_f16_bits(__uint_as_float(u));
 }
 
 // Write a wave-uniform 32-bit value into one lane of a VGPR (v_writelane_b32).
@@ -113,6 +97,12 @@ __device__ i32x4 tq_llvm_buf_ld_b128(i32x4 rsrc, int voff, int soff, int aux) __
 __device__ short tq_llvm_buf_ld_b16(i32x4 rsrc, int voff, int soff, int aux) __asm("llvm.amdgcn.raw.buffer.load.i16");
 __device__ void tq_llvm_buf_st_f32(float v, i32x4 rsrc, int voff, int soff, int aux) __asm("llvm.amdgcn.raw.buffer.store.f32");
 __device__ void tq_llvm_buf_st_v4f32(f32x4 v, i32x4 rsrc, int voff, int soff, int aux) __asm("llvm.amdgcn.raw.buffer.store.v4f32");
+__device__ void tq_llvm_buf_st_b32(int v, i32x4 rsrc, int voff, int soff, int aux) __asm("llvm.amdgcn.raw.buffer.store.i32");
+__device__ void tq_llvm_buf_st_b16(short v, i32x4 rsrc, int voff, int soff, int aux) __asm("llvm.amdgcn.raw.buffer.store.i16");
+
+// A byte offset that every resource built here treats as out of range (the
+// ranges are kept below 2^31), so a lane can drop its store without a branch.
+constexpr uint32_t kNoStore = 0x80000000u;
 
 __device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t bytes) {
   const uint64_t a = (uint64_t)base;
@@ -170,6 +160,16 @@ __device__ __forceinline__ void buf_store_f32(i32x4 rsrc, uint32_t off, float v)
 template <int AUX = kStream>
 __device__ __forceinline__ void buf_store_f32x4(i32x4 rsrc, uint32_t off, f32x4 v) {
   tq_llvm_buf_st_v4f32(v, rsrc, (int)off, 0, AUX);
+}
+
+template <int AUX = kStream>
+__device__ __forceinline__ void buf_store_u32(i32x4 rsrc, uint32_t off, uint32_t v) {
+  tq_llvm_buf_st_b32((int)v, rsrc, (int)off, 0, AUX);
+}
+
+template <int AUX = kStream>
+__device__ __forceinline__ void buf_store_u16(i32x4 rsrc, uint32_t off, uint16_t v) {
+  tq_llvm_buf_st_b16((short)v, rsrc, (int)off, 0, AUX);
 }
 
 template <typename T>
