@@ -71,16 +71,27 @@ struct LLayout {
 
 // Query preparation for one (stream, row tile, part): part 0 builds the
 // Walsh-plane chunks from q' = Pi q, part 1 the sign chunks from q'' = S q.
-// 256 threads; projections in fp64 from fp32 matrices.
+// 512 threads; RL = 512 / D consecutive lanes share matrix row j and read
+// its 16-byte pieces p, p + RL, ... (coalesced), each for all four queries,
+// then combine their partial sums with xor shuffles.  fp64 arithmetic from
+// the fp32 matrix and the queries (exact in fp32).
+template <int D>
+constexpr int prep_threads() { return 512; }
+
 template <int D, int LB, bool PROD>
-__global__ __launch_bounds__(256) void logit_prep_kernel(PrepArgs a) {
+__global__ __launch_bounds__(prep_threads<D>()) void logit_prep_kernel(PrepArgs a) {
   using L = LLayout<D, LB, PROD>;
   constexpr int K = 1 << LB;
   constexpr int P = L::P;
-  __shared__ __attribute__((aligned(16))) double qin[4][D];
+  constexpr int NT = prep_threads<D>();
+  constexpr int RL = NT / D;                // lanes per matrix row
+  constexpr int NP = D / 4 / RL;            // 16-byte pieces per lane
+  constexpr int NW = NT / 64;               // waves
+  static_assert(RL >= 1 && RL <= 64 && NP >= 1, "prep layout");
+  __shared__ __attribute__((aligned(16))) float qin[4][D];
   __shared__ double proj[4][D];
   __shared__ double beta[P];
-  __shared__ double red_max[4][4], red_sum[4][4];
+  __shared__ double red_max[4][NW], red_sum[4][NW];
 
   const int stream = blockIdx.x;
   const int rt = blockIdx.y;
@@ -88,8 +99,19 @@ __global__ __launch_bounds__(256) void logit_prep_kernel(PrepArgs a) {
   const int b = stream / a.n_kv_heads;
   const int kvh = stream % a.n_kv_heads;
   const int tid = threadIdx.x;
+  const int j = tid / RL;
+  const int pl = tid % RL;
 
-  for (int i = tid; i < 4 * D; i += 256) {
+  const float *mat = part == 0 ? a.pi : a.s_mat;
+  const f32x4 *mrow = (const f32x4 *)(mat + (size_t)j * D);
+  // d <= 128: the whole row slice is loaded before the first barrier; larger
+  // d streams it inside the loop (register budget)
+  constexpr int PRE = D <= 128 ? NP : 1;
+  f32x4 row[PRE];
+#pragma unroll
+  for (int i = 0; i < PRE; ++i) row[i] = mrow[pl + RL * i];
+
+  for (int i = tid; i < 4 * D; i += NT) {
     const int g = i / D, k = i % D;
     const int gg = 4 * rt + g;
     float v = 0.0f;
@@ -97,7 +119,7 @@ __global__ __launch_bounds__(256) void logit_prep_kernel(PrepArgs a) {
       const int64_t off = ((int64_t)b * a.n_q_heads + (int64_t)kvh * a.group + gg) * D + k;
       v = a.q_f32 ? ((const float *)a.q)[off] : bf16_to_f32(((const uint16_t *)a.q)[off]);
     }
-    qin[g][k] = (double)v;
+    qin[g][k] = v;
   }
   if (part == 0 && tid < P) {
     const int sub = Walsh<LB>::subset(tid);
@@ -110,44 +132,51 @@ __global__ __launch_bounds__(256) void logit_prep_kernel(PrepArgs a) {
     beta[tid] = acc / K;
   }
   __syncthreads();
-  // thread (j, gp): coordinate j, queries 2 gp and 2 gp + 1 (D = 128); for
-  // D = 256 each thread also takes j + 128.
-  const float *mat = part == 0 ? a.pi : a.s_mat;
-  const int gp = tid >> 7;
-  double mx[2] = {0, 0}, sm[2] = {0, 0};
-  for (int j = tid & 127; j < D; j += 128) {
-    const f32x4 *row = (const f32x4 *)(mat + (size_t)j * D);
-    double acc0 = 0.0, acc1 = 0.0;
-#pragma unroll 8
-    for (int k4 = 0; k4 < D / 4; ++k4) {
-      const f32x4 m4 = row[k4];
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll (D <= 128 ? NP : 4)
+  for (int i = 0; i < NP; ++i) {
+    const int k0 = 4 * (pl + RL * i);
+    const f32x4 m4 = D <= 128 ? row[i < PRE ? i : 0] : mrow[pl + RL * i];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc0 = fma((double)m4[i], qin[2 * gp][4 * k4 + i], acc0);
-        acc1 = fma((double)m4[i], qin[2 * gp + 1][4 * k4 + i], acc1);
-      }
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 qv = *(const f32x4 *)&qin[g][k0];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[g] = fma((double)m4[e], (double)qv[e], acc[g]);
     }
-    proj[2 * gp][j] = acc0;
-    proj[2 * gp + 1][j] = acc1;
-    mx[0] = fmax(mx[0], fabs(acc0));
-    mx[1] = fmax(mx[1], fabs(acc1));
-    sm[0] += acc0;
-    sm[1] += acc1;
   }
+  // full row sums in every lane of the row, then max |.| and sum over the
+  // rows of this wave
+  double mx[4], sm[4];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int g = 0; g < 4; ++g) {
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      mx[h] = fmax(mx[h], __shfl_xor(mx[h], off, 64));
-      sm[h] += __shfl_xor(sm[h], off, 64);
+    for (int off = 1; off < RL; off <<= 1) acc[g] += __shfl_xor(acc[g], off, 64);
+    if (pl == 0) proj[g][j] = acc[g];
+    mx[g] = fabs(acc[g]);
+    sm[g] = pl == 0 ? acc[g] : 0.0;
+#pragma unroll
+    for (int off = RL; off < 64; off <<= 1) {
+      mx[g] = fmax(mx[g], __shfl_xor(mx[g], off, 64));
+      sm[g] += __shfl_xor(sm[g], off, 64);
     }
   }
   if ((tid & 63) == 0) {
-    const int wv = (tid >> 6) & 1;
-    red_max[2 * gp][wv] = mx[0];
-    red_max[2 * gp + 1][wv] = mx[1];
-    red_sum[2 * gp][wv] = sm[0];
-    red_sum[2 * gp + 1][wv] = sm[1];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      red_max[g][tid >> 6] = mx[g];
+      red_sum[g][tid >> 6] = sm[g];
+    }
+  }
+  __syncthreads();
+  // thread g < 4 folds the per-wave results of query g
+  if (tid < 4) {
+    double mq = 0.0, sq = 0.0;
+    for (int wv = 0; wv < NW; ++wv) {
+      mq = fmax(mq, red_max[tid][wv]);
+      sq += red_sum[tid][wv];
+    }
+    red_max[tid][0] = mq;
+    red_sum[tid][0] = sq;
   }
   __syncthreads();
   double mb = 0.0, sb = 0.0;
@@ -160,8 +189,7 @@ __global__ __launch_bounds__(256) void logit_prep_kernel(PrepArgs a) {
   int fexp[4];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    const double mq = fmax(red_max[g][0], red_max[g][1]);
-    const double sq = red_sum[g][0] + red_sum[g][1];
+    const double mq = red_max[g][0], sq = red_sum[g][0];
     const double top = part == 0 ? mq * mb : mq;
     int e = 0;
     if (top > 0.0) frexp(top, &e);
@@ -186,27 +214,23 @@ __global__ __launch_bounds__(256) void logit_prep_kernel(PrepArgs a) {
   // A-operand chunks of this part.  Lane l = 16 kg + 4 g + piece supplies
   // row (query g, byte piece); its byte e = 4 t + i pairs with coordinate
   // 32 (kg + 4 q) + 8 i + 4 h + t, whose key byte carries weight 2^(4 h + t)
-  // (see the kernel comment).  One thread per (chunk, kg, g) computes the
-  // 32-bit fixed-point weights once and writes the four piece rows.
+  // (see the kernel comment).  One thread per (chunk, kg, g, t) computes
+  // the 32-bit fixed-point weights of bytes 4 t .. 4 t + 3 and writes word t
+  // of the four piece rows.
   int8_t *tab = a.table + ((int64_t)stream * a.row_tiles + rt) * (L::NCH * 64 * 16);
   const int c_begin = part == 0 ? 0 : P * L::CPP;
   const int c_end = part == 0 ? P * L::CPP : L::NCH;
-  for (int i = c_begin * 16 + tid; i < c_end * 16; i += 256) {
-    const int cidx = i / 16, kg = (i >> 2) & 3, g = i & 3;
+  for (int i = c_begin * 64 + tid; i < c_end * 64; i += NT) {
+    const int cidx = i / 64, kg = (i >> 4) & 3, g = (i >> 2) & 3, t = i & 3;
     const int r = cidx / L::CPP, c = cidx % L::CPP;
     const int q = c >> 1, hh = c & 1;
     const double wgt = part == 0 ? beta[r < P ? r : 0] : 1.0;
     const bool live = 4 * rt + g < a.group;
-    uint32_t words[4][4];   // [piece][t]
+    const int s = 4 * hh + t;
+    uint32_t words[4] = {0u, 0u, 0u, 0u};   // [piece]
 #pragma unroll
-    for (int pc = 0; pc < 4; ++pc)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) words[pc][t] = 0u;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int t = e >> 2, ib = e & 3;
+    for (int ib = 0; ib < 4; ++ib) {
       const int j = 32 * (kg + 4 * q) + 8 * ib + 4 * hh + t;
-      const int s = 4 * hh + t;
       int n = (int)rint(ldexp(wgt * proj[g][j], fexp[g] - s));
       if (s == 7) n = -n;
       if (!live) n = 0;
@@ -214,15 +238,14 @@ __global__ __launch_bounds__(256) void logit_prep_kernel(PrepArgs a) {
 #pragma unroll
       for (int pc = 0; pc < 4; ++pc) {
         const int dd = (int)(int8_t)(n & 0xFF);
-        words[pc][t] |= (uint32_t)(uint8_t)dd << (8 * ib);
+        words[pc] |= (uint32_t)(uint8_t)dd << (8 * ib);
         n = (n - dd) >> 8;
       }
     }
 #pragma unroll
     for (int pc = 0; pc < 4; ++pc) {
       const int l = 16 * kg + 4 * g + pc;
-      *(i32x4 *)(tab + ((int64_t)cidx * 64 + l) * 16) =
-          i32x4{(int)words[pc][0], (int)words[pc][1], (int)words[pc][2], (int)words[pc][3]};
+      *(uint32_t *)(tab + ((int64_t)cidx * 64 + l) * 16 + 4 * t) = words[pc];
     }
   }
 }
@@ -233,8 +256,9 @@ struct StreamArgs {
   const uint8_t *codes;
   const uint16_t *norm;
   const uint16_t *rnorm;
-  int64_t row_tokens, seq_len, tokens_per_block;
-  int n_splits, n_kv_heads, n_q_heads, group, row_tiles;
+  int64_t row_tokens, seq_len;
+  int n_splits;   // blocks per stream; block j takes chunks j, j + n_splits, ...
+  int n_kv_heads, n_q_heads, group, row_tiles;
   float scale;
   float *logits;
 };
@@ -242,6 +266,7 @@ struct StreamArgs {
 #ifndef TQ_LOGIT_GROUPS
 #define TQ_LOGIT_GROUPS 4
 #endif
+
 
 // Registers of one 16-token group as loaded by one lane: the plane words of
 // its 32-coordinate group(s); in inner-product mode the last word of each
@@ -282,10 +307,6 @@ __global__ __launch_bounds__(256) void logit_kernel(StreamArgs a) {
   const int split = bid % a.n_splits;
   const int b = stream / a.n_kv_heads;
   const int kvh = stream % a.n_kv_heads;
-  const int64_t t_begin = (int64_t)split * a.tokens_per_block;
-  int64_t t_end = t_begin + a.tokens_per_block;
-  if (t_end > a.seq_len) t_end = a.seq_len;
-  if (t_begin >= t_end) return;
 
   const int w = threadIdx.x >> 6;
   const int l = lane_id();
@@ -317,7 +338,7 @@ __global__ __launch_bounds__(256) void logit_kernel(StreamArgs a) {
   const i32x4 rg = make_rsrc(PROD ? a.rnorm + key0 : a.norm, PROD ? nvalid * 2 : 0u);
   const i32x4 ro = make_rsrc(a.logits + ((int64_t)b * a.n_q_heads + (int64_t)kvh * a.group) * a.seq_len,
                              (uint32_t)(a.group * a.seq_len * 4));
-  const uint32_t t_end32 = (uint32_t)t_end;
+  const uint32_t t_end32 = nvalid;
 
   // Lane (n, kg) reads, for token n of each group, the NPL plane words of
   // 32-coordinate group kg + 4 qd (one contiguous load: 16 bytes at b = 4);
@@ -388,7 +409,12 @@ __global__ __launch_bounds__(256) void logit_kernel(StreamArgs a) {
         stage[w][4 * rt + kg][16 * u + n] = nrm * v;
       }
     }
-    // each lane stores 4 consecutive logits of one query: 16-byte stores
+    // Each lane stores 4 consecutive logits of one query: one 16-byte store,
+    // plus three 4-byte stores that only the lane straddling the end of the
+    // sequence uses (its first 1-3 tokens).  Every other unused store gets an
+    // out-of-range offset and is dropped, so the same stores are issued on
+    // every path: the compiler then waits for the next iteration's loads
+    // without also waiting for these stores.
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
@@ -397,28 +423,35 @@ __global__ __launch_bounds__(256) void logit_kernel(StreamArgs a) {
         const uint32_t t4 = 4 * n + 64 * c;          // token offset within the iteration
         const f32x4 v = *(const f32x4 *)&stage[w][4 * rt + kg][t4];
         const uint32_t tok = tok0 + t4;
-        if (g < a.group) {
-          if (tok + 3 < t_end32) {
-            buf_store_f32x4(ro, 4u * ((uint32_t)g * nvalid + tok), v);
-          } else {
+        const uint32_t off = 4u * ((uint32_t)g * nvalid + tok);
+        const bool live = g < a.group;
+        const bool all4 = tok + 3 < t_end32;
+        buf_store_f32x4(ro, live && all4 ? off : kNoStore, v);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (tok + e < t_end32) buf_store_f32(ro, 4u * ((uint32_t)g * nvalid + tok + e), v[e]);
-          }
-        }
+        for (int e = 0; e < 3; ++e)
+          buf_store_f32(ro, (live && !all4 && tok + e < t_end32) ? off + 4 * e : kNoStore, v[e]);
       }
     }
   };
 
+  // The blocks of a stream take its chunks of 4 x 16U tokens round-robin
+  // (block j: chunks j, j + n_splits, ...), so the blocks running at any
+  // moment stream through adjacent memory instead of n_splits distant
+  // ranges in lockstep.  Wave w of a block takes the w-th 16U tokens of each
+  // chunk.  Loop bounds are wave-uniform (scalar).
+  const uint32_t stride = 4 * 16 * U * (uint32_t)a.n_splits;
+  uint32_t base = (uint32_t)__builtin_amdgcn_readfirstlane((int)(16 * U * (4 * split + w)));
   // Ping-pong over two register sets: the next iteration's loads are issued
-  // before the current one is consumed.
-  const uint32_t stride = 4 * 16 * U;
-  uint32_t base = (uint32_t)t_begin + 16 * U * w;
+  // before the current one is consumed.  The scheduling barriers keep each
+  // prefetch ahead of the compute that hides its latency.
   KeyGroup<NPL, NQ> bufa[U], bufb[U];
   NormBlock na[NB], nbb[NB];
-  // The scheduling barriers keep each prefetch ahead of the compute that
-  // hides its latency.
   load(base, bufa, na);
+  // Range-dropped stores: on entry, as on every later iteration, stores
+  // follow the pending loads, so the first wait counts them too (the
+  // compiler merges the counts of both paths into the loop).
+#pragma unroll
+  for (int i = 0; i < RT * U; ++i) buf_store_f32(ro, kNoStore + 4 * i, 0.0f);
   while (base < t_end32) {
     load(base + stride, bufb, nbb);
     __builtin_amdgcn_sched_barrier(0);
@@ -455,7 +488,8 @@ hipError_t launch_t(const tqi::LogitArgs &a, hipStream_t s) {
   pa.centroids = a.centroids;
   pa.table = (int8_t *)ws;
   pa.consts = (float *)((char *)ws + table_bytes);
-  hipLaunchKernelGGL((logit_prep_kernel<D, LB, PROD>), dim3(n_streams, rts, PROD ? 2 : 1), dim3(256), 0,
+  hipLaunchKernelGGL((logit_prep_kernel<D, LB, PROD>), dim3(n_streams, rts, PROD ? 2 : 1),
+                     dim3(prep_threads<D>()), 0,
                      s, pa);
   e = hipGetLastError();
   if (e == hipSuccess) {
@@ -473,17 +507,15 @@ hipError_t launch_t(const tqi::LogitArgs &a, hipStream_t s) {
     sa.row_tiles = rts;
     sa.scale = a.scale;
     sa.logits = a.logits;
-    const int64_t total = (int64_t)n_streams * a.seq_len;
 #ifndef TQ_LOGIT_BLOCKS_PER_CU
-#define TQ_LOGIT_BLOCKS_PER_CU 4
+#define TQ_LOGIT_BLOCKS_PER_CU 8
 #endif
     const int64_t target_blocks = (int64_t)TQ_LOGIT_BLOCKS_PER_CU * tqi::device_cu_count();
-    int64_t tpb = (total + target_blocks - 1) / target_blocks;
-    tpb = (tpb + 63) / 64 * 64;
-    if (tpb < 512) tpb = 512;
-    if (tpb > 16384) tpb = 16384;
-    sa.tokens_per_block = tpb;
-    sa.n_splits = (int)((a.seq_len + tpb - 1) / tpb);
+    const int64_t n_chunks = (a.seq_len + 4 * 16 * TQ_LOGIT_GROUPS - 1) / (4 * 16 * TQ_LOGIT_GROUPS);
+    int64_t splits = (target_blocks + n_streams - 1) / n_streams;
+    if (splits > n_chunks) splits = n_chunks;
+    if (splits < 1) splits = 1;
+    sa.n_splits = (int)splits;
     const int64_t blocks = (int64_t)n_streams * sa.n_splits;
     switch (rts) {
       case 1: hipLaunchKernelGGL((logit_kernel<D, LB, PROD, 1>), dim3((unsigned)blocks), dim3(256), 0, s, sa); break;
@@ -518,9 +550,10 @@ hipError_t launch_logits(int d, int lbits, bool prod, const LogitArgs &a, hipStr
   *supported = false;
   const int64_t group = a.n_q_heads / a.n_kv_heads;
   if (group > 16) return hipSuccess;
-  // the streaming kernel addresses one stream's codes and logits with 32-bit
-  // byte offsets
-  if (a.seq_len * (int64_t)((lbits + (prod ? 1 : 0)) * d / 8) >= (1LL << 32) ||
+  // The streaming kernel addresses one stream's codes and logits with 32-bit
+  // byte offsets; its prefetch runs up to one block stride (<= seq_len + 255
+  // tokens) past the end, which must not wrap either.
+  if ((2 * a.seq_len + 256) * (int64_t)((lbits + (prod ? 1 : 0)) * d / 8) >= (1LL << 32) ||
       group * a.seq_len * 4 >= (1LL << 32))
     return hipSuccess;
   if (d == 128) return prod ? launch_lb<128, true>(lbits, a, s, supported)
