@@ -95,21 +95,6 @@ class Timer:
         return start.elapsed_time(end) * 1e-3 / n
 
 
-def _device_kv(torch, seed, cfg, tensor, batch, heads, tokens, d, device):
-    """bf16 [batch*heads*tokens, d] drawn on the device: channel scales from the
-    shared recipe (lognormal, 1% outliers x20), body N(0,1) from torch's seeded
-    Philox generator.  Used only where the oracle never needs the same values."""
-    from synthetic import channel_scales
-    sc = torch.tensor(channel_scales(seed, cfg, tensor, heads, d), dtype=torch.float32, device=device)
-    gen = torch.Generator(device=device)
-    gen.manual_seed(1000 * seed + cfg)
-    out = torch.empty((batch, heads, tokens, d), dtype=torch.bfloat16, device=device)
-    for b in range(batch):
-        z = torch.randn((heads, tokens, d), generator=gen, device=device)
-        out[b] = (z * sc[:, None, :]).to(torch.bfloat16)
-    return out.view(-1, d)
-
-
 def _host_kv(torch, seed, cfg, tensor, heads, tokens, d, device):
     """bf16 [heads*tokens, d] from the shared numpy recipe (reproducible on the host)."""
     import numpy as np
@@ -201,13 +186,12 @@ def cpu_baseline_decode(budget_s=12.0):
 
 def long_context_leg(torch, tq, timer, reps, device):
     d, batch, heads, qheads, seq, bits = 128, 8, 8, 32, 131072, 4
-    x = _device_kv(torch, 0, 3, "k", batch, heads, seq, d, device)
+    from synthetic import device_kv, device_queries
+    x = device_kv(torch, 0, 3, "k", batch, heads, seq, d, device)
     qz = tq.Quantizer(d, bits, tq.MODE_PROD, seed=0, device=device)
     cache = qz.quantize(x)
     del x
-    gen = torch.Generator(device=device)
-    gen.manual_seed(7)
-    q = torch.randn((batch, qheads, d), generator=gen, device=device).to(torch.bfloat16)
+    q = device_queries(torch, 0, 3, batch, qheads, heads, d, device)
     out = torch.empty((batch, qheads, seq), dtype=torch.float32, device=device)
     call = lambda: qz.attn_logits(q, cache, heads, seq, 1.0 / math.sqrt(d), out=out)
     call()

@@ -135,3 +135,32 @@ def search_vectors(seed, tensor, start, count, d=200, d_pad=256, block=65536):
         out[pos:pos + hi - lo, :d] = v[lo:hi].astype(np.float32)
         pos += hi - lo
     return out
+
+
+# ------------------------------------------------- device-side draws (torch)
+def device_kv(torch, seed, cfg, tensor, batch, heads, tokens, d, device):
+    """bf16 [batch * heads * tokens, d] drawn on the device: the channel scales
+    of ``channel_scales`` (lognormal, 1% outliers x20) times N(0,1) from torch's
+    seeded Philox generator, rounded to bf16 (nearest even).  For workloads too
+    large to draw on the host; a test that needs some of the values for the
+    oracle copies those rows back."""
+    sc = torch.tensor(channel_scales(seed, cfg, tensor, heads, d), dtype=torch.float32, device=device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(1000 * seed + 10 * cfg + TENSOR_CODES[tensor])
+    out = torch.empty((batch, heads, tokens, d), dtype=torch.bfloat16, device=device)
+    for b in range(batch):
+        z = torch.randn((heads, tokens, d), generator=gen, device=device)
+        out[b] = (z * sc[:, None, :]).to(torch.bfloat16)
+        del z
+    return out.view(-1, d)
+
+
+def device_queries(torch, seed, cfg, batch, q_heads, kv_heads, d, device):
+    """bf16 [batch, q_heads, d] on the device, query head h scaled like KV head
+    h // (q_heads / kv_heads) (same channel scales as the keys)."""
+    group = q_heads // kv_heads
+    sc = torch.tensor(channel_scales(seed, cfg, "k", kv_heads, d), dtype=torch.float32, device=device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(1000 * seed + 10 * cfg + TENSOR_CODES["q"])
+    z = torch.randn((batch, q_heads, d), generator=gen, device=device)
+    return (z * sc.repeat_interleave(group, dim=0)[None]).to(torch.bfloat16)

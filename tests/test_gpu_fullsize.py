@@ -1,0 +1,219 @@
+"""GPU parity at the full sizes of the five workloads, launched as bench.py launches them.
+
+Where the oracle finishes in seconds it checks every output (configs 1, 2 and
+the config-5 database codes); elsewhere it checks outputs sampled across the
+whole range (every stream, first and last rows, tile edges), each one
+recomputed by the oracle from the seeded inputs.  Logit, dequantize and
+search kernels are judged on identical codes: either they read oracle-packed
+codes, or only tokens whose GPU codes equal the oracle's are compared.  No
+oracle input comes from a GPU kernel: large inputs are drawn on the device by
+the seeded generators of ``synthetic`` and the sampled rows are copied back.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import quantizer as oqz
+from synthetic import (bf16_to_f32, channel_scales, device_kv, device_queries, gqa_queries, kv_block,
+                       search_vectors, tiny_keys_queries)
+
+from parity import (OracleTables, cache_from_oracle, check_codes, check_dequant, check_logits,
+                    check_norms, check_rnorm, check_signs)
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def tq():
+    import online_vector_quantization_amd as pkg
+    return pkg
+
+
+def _sample_rows(n, count, seed, tile=32):
+    """Sorted unique row indices: first / last rows, both sides of tile edges, random."""
+    rng = np.random.default_rng(seed)
+    edges = np.arange(tile, n, tile * max(1, n // (tile * 64)))
+    picks = np.concatenate([[0, 1, n - 2, n - 1], edges - 1, edges, rng.integers(0, n, count)])
+    return np.unique(np.clip(picks, 0, n - 1))
+
+
+def _host_stream_keys(seed, cfg, tensor, heads, tokens, d):
+    sc = channel_scales(seed, cfg, tensor, heads, d)
+    return np.concatenate([kv_block(seed, cfg, tensor, 0, h, tokens, sc) for h in range(heads)]), sc
+
+
+def _dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def _check_quantized(cache, ref, rows, ot):
+    codes = cache.codes.cpu().numpy()[rows]
+    check_codes(codes, ref, ot.lb, ot.d, ot.t, ot.mode)
+    check_norms(cache.norm.cpu().numpy()[rows], ref)
+    if ot.mode == oqz.MODE_PROD:
+        check_signs(codes, ref, ot.lb, ot.d)
+        check_rnorm(cache.rnorm.cpu().numpy()[rows], ref)
+    same = np.all(codes == ref["codes"], axis=1)
+    if ot.mode == oqz.MODE_PROD:
+        same &= cache.rnorm.cpu().numpy().view(np.uint16)[rows] == ref["rnorm"]
+    return same
+
+
+def test_config1_tiny_full(tq):
+    """4096 fp32 keys (2 of 128 channels x10), MSE b=3, 16 fp32 queries: every output."""
+    k, q = tiny_keys_queries(0)
+    d, bits = 128, 3
+    ot = OracleTables(d, bits, oqz.MODE_MSE)
+    ref = ot.quantize(k.astype(np.float64))
+    qz = tq.Quantizer(d, bits, oqz.MODE_MSE, seed=0, device=DEV)
+    cache = qz.quantize(torch.from_numpy(k).to(DEV))
+    _check_quantized(cache, ref, np.arange(len(k)), ot)
+    ocache = cache_from_oracle(tq, ref, d, bits, oqz.MODE_MSE, DEV)
+    scale = 1.0 / math.sqrt(d)
+    lg = qz.attn_logits(torch.from_numpy(q).reshape(1, 16, d).to(DEV), ocache, n_kv_heads=1,
+                        seq_len=len(k), scale=scale).cpu().numpy()[0]
+    want = oqz.logits_rotated(q.astype(np.float64), ref["codes"], ref["norm"], ot.pi, ot.c,
+                              oqz.MODE_MSE, scale)
+    check_logits(lg, want, scale, ref["norm"], q.astype(np.float64))
+
+
+def test_config2_decode_full(tq):
+    """8 heads x 32768 bf16 tokens: keys prod b=3, values MSE b=3, 32 GQA queries.
+
+    Every code, norm and logit; dequantized values on sampled rows."""
+    d, heads, qheads, seq, bits = 128, 8, 32, 32768, 3
+    n = heads * seq
+    group = qheads // heads
+    kb, ksc = _host_stream_keys(0, 2, "k", heads, seq, d)
+    vb, _ = _host_stream_keys(0, 2, "v", heads, seq, d)
+    qb = gqa_queries(0, 2, 1, qheads, heads, ksc)
+    q64 = bf16_to_f32(qb).astype(np.float64)[0]
+    otk = OracleTables(d, bits, oqz.MODE_PROD)
+    otv = OracleTables(d, bits, oqz.MODE_MSE)
+    refk = otk.quantize(bf16_to_f32(kb).astype(np.float64))
+    qk = tq.Quantizer(d, bits, oqz.MODE_PROD, seed=0, device=DEV)
+    qv = tq.Quantizer(d, bits, oqz.MODE_MSE, seed=0, device=DEV)
+    ck, cv = qk.new_cache(n), qv.new_cache(n)
+    qk.quantize(_dev_bf16(kb), out=ck)
+    qv.quantize(_dev_bf16(vb), out=cv)
+    _check_quantized(ck, refk, np.arange(n), otk)
+    del refk["u_rot"], refk["z"]
+    refv = otv.quantize(bf16_to_f32(vb).astype(np.float64))
+    _check_quantized(cv, refv, np.arange(n), otv)
+    # logits of all 32 heads over the whole cache, from oracle-packed keys
+    okc = cache_from_oracle(tq, refk, d, bits, oqz.MODE_PROD, DEV)
+    scale = 1.0 / math.sqrt(d)
+    out = torch.empty((1, qheads, seq), dtype=torch.float32, device=DEV)
+    qk.attn_logits(_dev_bf16(qb), okc, heads, seq, scale, out=out)
+    out = out.cpu().numpy()[0]
+    for h in range(heads):
+        sl = slice(h * seq, (h + 1) * seq)
+        qq = q64[h * group:(h + 1) * group]
+        want = oqz.logits_rotated(qq, refk["codes"][sl], refk["norm"][sl], otk.pi, otk.c, oqz.MODE_PROD,
+                                  scale, rnorm=refk["rnorm"][sl], s_mat=otk.s)
+        check_logits(out[h * group:(h + 1) * group], want, scale, refk["norm"][sl], qq)
+    # dequantized values (bf16, as in the decode step, and fp32) on sampled rows
+    ovc = cache_from_oracle(tq, refv, d, bits, oqz.MODE_MSE, DEV)
+    rows = _sample_rows(n, 3000, 21)
+    want = oqz.dequantize(refv["codes"][rows], refv["norm"][rows], otv.pi, otv.c, oqz.MODE_MSE)
+    got32 = qv.dequantize(ovc, n).cpu().numpy()[rows]
+    check_dequant(got32, want)
+    got16 = qv.dequantize(ovc, n, out_dtype=torch.bfloat16).float().cpu().numpy()[rows]
+    assert np.all(np.abs(got16 - want) <= 2.0 ** -8 * np.abs(want) + 1e-3 * np.abs(want).max(axis=1, keepdims=True))
+
+
+def test_config3_long_context_full(tq):
+    """Batch 8 x 8 heads x 131072 tokens, keys prod b=4, 32 GQA queries: 8.4M keys.
+
+    Codes, logits and fp32 dequantized keys on 4096 sampled tokens spread
+    over every stream (the 8.4M-row calls span more than one launch)."""
+    d, batch, heads, qheads, seq, bits = 128, 8, 8, 32, 131072, 4
+    group = qheads // heads
+    n = batch * heads * seq
+    x = device_kv(torch, 0, 3, "k", batch, heads, seq, d, DEV)
+    q = device_queries(torch, 0, 3, batch, qheads, heads, d, DEV)
+    qz = tq.Quantizer(d, bits, oqz.MODE_PROD, seed=0, device=DEV)
+    cache = qz.new_cache(n)
+    qz.quantize(x, out=cache)
+    out = torch.empty((batch, qheads, seq), dtype=torch.float32, device=DEV)
+    scale = 1.0 / math.sqrt(d)
+    qz.attn_logits(q, cache, heads, seq, scale, out=out)
+    rows = _sample_rows(n, 4000, 31)
+    idx = torch.from_numpy(rows).to(DEV)
+    xs = x.index_select(0, idx).float().cpu().numpy().astype(np.float64)   # seeded inputs
+    del x
+    ot = OracleTables(d, bits, oqz.MODE_PROD)
+    ref = ot.quantize(xs)
+    same = _check_quantized(cache, ref, rows, ot)
+    assert same.mean() > 0.98
+    q64 = q.float().cpu().numpy().astype(np.float64)
+    lg = out.cpu().numpy()
+    stream, tok = rows // seq, rows % seq
+    for s in np.unique(stream):
+        sel = np.nonzero((stream == s) & same)[0]
+        b, h = divmod(int(s), heads)
+        qq = q64[b, h * group:(h + 1) * group]
+        want = oqz.logits_rotated(qq, ref["codes"][sel], ref["norm"][sel], ot.pi, ot.c, oqz.MODE_PROD,
+                                  scale, rnorm=ref["rnorm"][sel], s_mat=ot.s)
+        check_logits(lg[b, h * group:(h + 1) * group][:, tok[sel]], want, scale, ref["norm"][sel], qq)
+    # all 8.4M keys dequantized to fp32 (4.3 GB, more than one launch's range)
+    del out
+    xhat = qz.dequantize(cache, n).index_select(0, idx).cpu().numpy()
+    want = oqz.dequantize(ref["codes"][same], ref["norm"][same], ot.pi, ot.c, oqz.MODE_PROD,
+                          rnorm=ref["rnorm"][same], s_mat=ot.s)
+    check_dequant(xhat[same], want)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_config4_prefill_full(tq, bits):
+    """65536 new tokens x 8 heads, K (prod) and V (MSE) in bf16: sampled rows of all 524288."""
+    d, heads, tokens = 128, 8, 65536
+    n = heads * tokens
+    rows = _sample_rows(n, 6000, 40 + bits)
+    for tensor, mode in (("k", oqz.MODE_PROD), ("v", oqz.MODE_MSE)):
+        xb, _ = _host_stream_keys(0, 4, tensor, heads, tokens, d)
+        qz = tq.Quantizer(d, bits, mode, seed=0, device=DEV)
+        cache = qz.new_cache(n)
+        qz.quantize(_dev_bf16(xb), out=cache)
+        ot = OracleTables(d, bits, mode)
+        ref = ot.quantize(bf16_to_f32(xb[rows]).astype(np.float64))
+        _check_quantized(cache, ref, rows, ot)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_config5_search_full(tq, bits):
+    """10^6 unit vectors (d=200 padded to 256), MSE b=2/4, 10^4 queries, top-10.
+
+    GPU codes of the whole database against the oracle's; top-10 of sampled
+    queries over the whole database from oracle-packed codes."""
+    d, n_db, n_q, k = 256, 1_000_000, 10_000, 10
+    db = search_vectors(0, "db", 0, n_db)
+    ot = OracleTables(d, bits, oqz.MODE_MSE)
+    ref = ot.quantize(db.astype(np.float64))
+    qz = tq.Quantizer(d, bits, oqz.MODE_MSE, seed=0, device=DEV)
+    gcache = qz.new_cache(n_db)
+    qz.quantize(torch.from_numpy(db).to(DEV), out=gcache)
+    del db
+    check_codes(gcache.codes.cpu().numpy(), ref, ot.lb, d, ot.t, oqz.MODE_MSE)
+    check_norms(gcache.norm.cpu().numpy(), ref)
+    del gcache, ref["u_rot"], ref["idx"]
+    cache = cache_from_oracle(tq, ref, d, bits, oqz.MODE_MSE, DEV)
+    qv = search_vectors(0, "dbq", 0, n_q)
+    vals, idx = qz.search(torch.from_numpy(qv.reshape(1, n_q, d)).to(DEV), cache, n_kv_heads=1,
+                          seq_len=n_db, topk=k)
+    vals, idx = vals.cpu().numpy()[0], idx.cpu().numpy()[0]
+    picks = np.unique(np.concatenate([[0, n_q - 1], np.random.default_rng(50 + bits).integers(0, n_q, 14)]))
+    scores = oqz.logits_rotated(qv[picks].astype(np.float64), ref["codes"], ref["norm"], ot.pi, ot.c,
+                                oqz.MODE_MSE, 1.0)
+    for r, qi in enumerate(picks):
+        sv, si = oqz.topk(scores[r:r + 1], k)
+        got = scores[r, idx[qi]]
+        assert np.all(np.abs(vals[qi] - got) <= 1e-4 * np.maximum(np.abs(got), 1e-3))
+        tol = 1e-4 * max(abs(sv[0, -1]), 1e-3)
+        for i in set(idx[qi].tolist()) ^ set(si[0].tolist()):
+            assert abs(scores[r, i] - sv[0, -1]) <= tol, (qi, i)
