@@ -1,6 +1,6 @@
 """Benchmark of the online KV-cache quantizer hot path on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|search]
 
 A step is one pass of the whole path over one batch of synthetic input:
 quantise the keys (inner-product mode) and the values (MSE mode), compute the
@@ -14,6 +14,13 @@ resident in HBM.  The line also carries the roofline of the dominant kernel
 on the launch stream), the fp64 CPU oracle timed on a bounded sample of the
 same workload, a per-call breakdown and the long-context logit leg (batch 8,
 8 KV heads, 131072 tokens, 4-bit keys).
+
+Two more workloads print a line of the same form: ``prefill`` quantises
+65536 new bf16 tokens x 8 KV heads (keys inner-product, values MSE) at b = 2,
+3 and 4 (value: vectors/s, roofline against the fp16 MFMA peak), and
+``search`` scores 10^4 queries against 10^6 quantised unit vectors (d = 200
+padded to 256, MSE b = 2 and 4) with a fused top-10 (value: query-key scores
+per second, roofline against the fp16 MFMA peak).
 
 Only one GPU is used; --gpus above 1 exits with a message.
 """
@@ -144,6 +151,110 @@ def decode_workload(torch, tq, args, device):
     return calls, work, cfg, n
 
 
+def prefill_workload(torch, tq, args, device):
+    d, heads, tokens = 128, 8, 65536
+    n = heads * tokens
+    k, _ = _host_kv(torch, 0, 4, "k", heads, tokens, d, device)
+    v, _ = _host_kv(torch, 0, 4, "v", heads, tokens, d, device)
+    calls, work = {}, {}
+    src = ["quantize.hip", "tq_device.h"]
+    for b in (2, 3, 4):
+        qk = tq.Quantizer(d, b, tq.MODE_PROD, seed=0, device=device)
+        qv = tq.Quantizer(d, b, tq.MODE_MSE, seed=0, device=device)
+        ck, cv = qk.new_cache(n), qv.new_cache(n)
+        calls["quantize_k_b%d" % b] = lambda qk=qk, ck=ck: qk.quantize(k, out=ck)
+        calls["quantize_v_b%d" % b] = lambda qv=qv, cv=cv: qv.quantize(v, out=cv)
+        rb = b * d // 8
+        work["quantize_k_b%d" % b] = (n * (2 * d + rb + 4), n * 4 * d * d, "quantize_kernel", src)
+        work["quantize_v_b%d" % b] = (n * (2 * d + rb + 2), n * 2 * d * d, "quantize_kernel", src)
+    cfg = {"workload": "prefill quantisation: 65536 new bf16 tokens x 8 KV heads x 128; keys "
+                       "inner-product and values MSE at b = 2, 3, 4 (six calls per step)",
+           "tokens": tokens, "kv_heads": heads, "head_dim": d, "bits": [2, 3, 4],
+           "units_per_step": 6 * n}
+    return calls, work, cfg, 6 * n
+
+
+def search_workload(torch, tq, args, device):
+    from synthetic import search_vectors
+    d, n_db, n_q, k = 256, 1_000_000, 10_000, 10
+    db = torch.from_numpy(search_vectors(0, "db", 0, n_db)).to(device)
+    q = torch.from_numpy(search_vectors(0, "dbq", 0, n_q).reshape(1, n_q, d)).to(device)
+    calls, work = {}, {}
+    for b in (2, 4):
+        qz = tq.Quantizer(d, b, tq.MODE_MSE, seed=0, device=device)
+        cache = qz.quantize(db)          # the index is built once, outside the step
+        calls["search_b%d" % b] = lambda qz=qz, cache=cache: qz.search(q, cache, 1, n_db, k)
+        byts = n_db * (b * d // 8 + 2) + n_q * d * 4 + n_q * k * 8
+        work["search_b%d" % b] = (byts, 2 * d * n_db * n_q, "search_score_kernel",
+                                  ["search.hip", "tq_device.h"])
+    del db
+    cfg = {"workload": "vector search: 10^4 queries x 10^6 unit vectors (d = 200 padded to 256), "
+                       "MSE b = 2 and 4, fused top-10 (two calls per step)",
+           "n_db": n_db, "n_queries": n_q, "head_dim": d, "bits": [2, 4], "topk": k,
+           "units_per_step": 2 * n_q * n_db}
+    return calls, work, cfg, 2 * n_q * n_db
+
+
+def _oracle_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max((i.get("num_threads") or 0) for i in threadpool_info()) or os.cpu_count()
+    except Exception:
+        return os.cpu_count()
+
+
+def cpu_baseline_prefill(budget_s=12.0):
+    """The oracle quantising whole KV heads of the prefill workload (b = 3) until the budget is spent."""
+    import numpy as np
+    from oracle import codebook as ocb
+    from oracle import quantizer as oqz
+    from oracle import rotation as orot
+    from synthetic import bf16_to_f32, channel_scales, kv_block
+    d, tokens, b = 128, 65536, 3
+    pi, s = orot.haar_rotation(d, 0), orot.qjl_matrix(d, 0)
+    ck, tk, _ = ocb.codebook(d, b - 1)
+    cv, tv, _ = ocb.codebook(d, b)
+    ksc, vsc = channel_scales(0, 4, "k", 8, d), channel_scales(0, 4, "v", 8, d)
+    done, heads, t_used = 0, 0, 0.0
+    while heads < 8 and (t_used < budget_s or heads == 0):
+        kx = bf16_to_f32(kv_block(0, 4, "k", 0, heads, tokens, ksc)).astype(np.float64)
+        vx = bf16_to_f32(kv_block(0, 4, "v", 0, heads, tokens, vsc)).astype(np.float64)
+        t0 = time.perf_counter()
+        oqz.quantize(kx, pi, ck, tk, oqz.MODE_PROD, s_mat=s)
+        oqz.quantize(vx, pi, cv, tv, oqz.MODE_MSE)
+        t_used += time.perf_counter() - t0
+        done += 2 * tokens
+        heads += 1
+    return {"value": done / t_used, "unit": "vectors/s", "cores": _oracle_threads(), "kind": "oracle",
+            "sample": "%d of 8 KV heads (%d tokens each), keys prod b=3 and values MSE b=3; %.1f s of "
+                      "CPU time" % (heads, tokens, t_used)}
+
+
+def cpu_baseline_search(budget_s=12.0):
+    """The oracle scoring queries against 65536 database vectors (MSE b=2) with top-10."""
+    import numpy as np
+    from oracle import codebook as ocb
+    from oracle import quantizer as oqz
+    from oracle import rotation as orot
+    from synthetic import search_vectors
+    d, n_db, k = 256, 65536, 10
+    pi = orot.haar_rotation(d, 0)
+    c, t, _ = ocb.codebook(d, 2)
+    ref = oqz.quantize(search_vectors(0, "db", 0, n_db).astype(np.float64), pi, c, t, oqz.MODE_MSE)
+    qs = search_vectors(0, "dbq", 0, 256).astype(np.float64)
+    done, t_used, i = 0, 0.0, 0
+    while i < len(qs) and (t_used < budget_s or i == 0):
+        t0 = time.perf_counter()
+        sc = oqz.logits_rotated(qs[i:i + 8], ref["codes"], ref["norm"], pi, c, oqz.MODE_MSE, 1.0)
+        oqz.topk(sc, k)
+        t_used += time.perf_counter() - t0
+        done += 8 * n_db
+        i += 8
+    return {"value": done / t_used, "unit": "keys/s", "cores": _oracle_threads(), "kind": "oracle",
+            "sample": "%d queries x the first %d database vectors (MSE b=2): oracle scores and top-10; "
+                      "%.1f s of CPU time" % (i, n_db, t_used)}
+
+
 def cpu_baseline_decode(budget_s=12.0):
     """The fp64 oracle on whole KV heads of the same decode workload until the budget is spent."""
     import numpy as np
@@ -171,13 +282,7 @@ def cpu_baseline_decode(budget_s=12.0):
         t_used += time.perf_counter() - t0
         done += seq
         heads += 1
-    threads = None
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads") or 0) for i in threadpool_info()) or None
-    except Exception:
-        pass
-    return {"value": done / t_used, "unit": "keys/s", "cores": threads or os.cpu_count(),
+    return {"value": done / t_used, "unit": "keys/s", "cores": _oracle_threads(),
             "kind": "oracle",
             "sample": "%d of 8 KV heads (%d tokens each): oracle quantise K (prod b=3) and V (MSE b=3), "
                       "logits of the 4 GQA query heads, dequantise V; %.1f s of CPU time" %
@@ -224,7 +329,9 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    calls, work, cfg, units = decode_workload(torch, tq, args, device)
+    build = {"decode": decode_workload, "prefill": prefill_workload, "search": search_workload}
+    calls, work, cfg, units = build[args.workload](torch, tq, args, device)
+    unit = {"decode": "keys/s", "prefill": "vectors/s", "search": "keys/s"}[args.workload]
     step = lambda: [fn() for fn in calls.values()]
     for _ in range(args.warmup):
         step()
@@ -245,19 +352,26 @@ def main():
     byts, flops, kern, src = work[dom]
     tdom = breakdown[dom]["us"] * 1e-6
     traffic = _traffic(kern + ":" + dom, src)
-    roofline = {"kernel": kern, "call": dom, "bound": "hbm", "achieved": byts / tdom / 1e9,
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": byts / tdom / 1e9 / HBM_PEAK_GBS,
-                "traffic": traffic, "algorithmic_bytes_per_launch": byts}
+    if args.workload == "decode":
+        roofline = {"kernel": kern, "call": dom, "bound": "hbm", "achieved": byts / tdom / 1e9,
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": byts / tdom / 1e9 / HBM_PEAK_GBS,
+                    "traffic": traffic, "algorithmic_bytes_per_launch": byts}
+    else:   # fp16 MFMA contraction: algorithmic flops of the call against the dense fp16 peak
+        roofline = {"kernel": kern, "call": dom, "bound": "mfma", "achieved": flops / tdom / 1e12,
+                    "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s", "frac": flops / tdom / 1e12 / MFMA_F16_PEAK_TFS,
+                    "traffic": traffic, "algorithmic_flops_per_launch": flops,
+                    "algorithmic_bytes_per_launch": byts}
 
-    line = {"metric": METRIC, "value": units / t_step, "unit": "keys/s", "n_gpus": 1,
+    line = {"metric": METRIC, "value": units / t_step, "unit": unit, "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": t_step * 1e3,
             "wall_s_timed": wall, "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "bf16 in; f16 split + i8 MFMA, f32/i32 accumulate",
             "data": "synthetic", "config": cfg, "roofline": roofline, "breakdown": breakdown}
-    if not args.no_long_context:
+    if args.workload == "decode" and not args.no_long_context:
         line["long_context_logits"] = long_context_leg(torch, tq, timer, args.steps, device)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline_decode()
+        line["cpu_baseline"] = {"decode": cpu_baseline_decode, "prefill": cpu_baseline_prefill,
+                                "search": cpu_baseline_search}[args.workload]()
     print(json.dumps(line), flush=True)
 
 

@@ -69,6 +69,11 @@ __device__ void load_stationary(const float *__restrict__ mat, int w, half8 (&hi
   }
 }
 
+// Codes, norms and signs leave as scattered 2- and 4-byte pieces of rows:
+// stored with the default (write-back) policy so that L2 merges them into
+// whole lines; with the streaming policy each piece reaches HBM on its own.
+constexpr int kWriteBack = 0;
+
 // Raw input of one staging thread: 16 consecutive elements of one vector.
 template <bool IN_F32>
 struct RawInput {
@@ -274,7 +279,7 @@ __global__ __launch_bounds__(QLayout<D>::NT) void quantize_kernel(tqi::QuantizeA
         const int64_t gv = base + v;
         const uint32_t off =
             (slot < 32 * LB && gv < a.n_vec) ? (uint32_t)(gv * RB + 4 * (w * NPL + p)) : kNoStore;
-        buf_store_u32(rc, off, outw[g]);
+        buf_store_u32<kWriteBack>(rc, off, outw[g]);
       }
     }
     if constexpr (PROD) {
@@ -302,7 +307,7 @@ __global__ __launch_bounds__(QLayout<D>::NT) void quantize_kernel(tqi::QuantizeA
         const int64_t gv = base + v;
         if (vinv[buf][v] == 0.0f) sw = 0xFFFFFFFFu;   // zero vector: all signs +1
         const uint32_t off = (l < 32 && gv < a.n_vec) ? (uint32_t)(gv * RB + 4 * (w * NPL + LB)) : kNoStore;
-        buf_store_u32(rc, off, sw);
+        buf_store_u32<kWriteBack>(rc, off, sw);
       }
       // residual norm of the unit vector from the staged residual tile
       {
@@ -327,7 +332,7 @@ __global__ __launch_bounds__(QLayout<D>::NT) void quantize_kernel(tqi::QuantizeA
         for (int off = 1; off < L::TPV; off <<= 1) ss += wave_xor(ss, off);
         const int64_t gv = base + sv_v;
         const float gam = vinv[buf][sv_v] == 0.0f ? 0.0f : sqrtf(ss) * (1.0f / kResScale);
-        buf_store_u16(rr, (sv_c == 0 && gv < a.n_vec) ? (uint32_t)(2 * gv) : kNoStore, f32_to_f16_bits(gam));
+        buf_store_u16<kWriteBack>(rr, (sv_c == 0 && gv < a.n_vec) ? (uint32_t)(2 * gv) : kNoStore, f32_to_f16_bits(gam));
       }
     }
   };
@@ -343,14 +348,14 @@ __global__ __launch_bounds__(QLayout<D>::NT) void quantize_kernel(tqi::QuantizeA
   // stores follow the pending input loads, so the compiler can wait for
   // those loads alone (it merges the counts of both paths into the loop).
 #pragma unroll
-  for (int i = 0; i < 5; ++i) buf_store_u32(rn, kNoStore + 4 * i, 0u);
+  for (int i = 0; i < 5; ++i) buf_store_u32<kWriteBack>(rn, kNoStore + 4 * i, 0u);
   int buf = 0;
   for (; tile < n_tiles; tile += step, buf ^= 1) {
     const uint16_t n16 = stage(tile, raw, buf);
     load_raw(tile + step, raw);
     __builtin_amdgcn_sched_barrier(0);
     const int64_t gv = tile * 32 + sv_v;
-    buf_store_u16(rn, (sv_c == 0 && gv < a.n_vec) ? (uint32_t)(2 * gv) : kNoStore, n16);
+    buf_store_u16<kWriteBack>(rn, (sv_c == 0 && gv < a.n_vec) ? (uint32_t)(2 * gv) : kNoStore, n16);
     __syncthreads();
     compute(tile, buf);
   }
