@@ -10,10 +10,10 @@
 //   M = S Pi^T.
 //
 // Design (gfx950):
-// * One workgroup = D/32 waves; wave w owns the output coordinates
-//   [32w, 32w+32).  Its slice of Pi (and of M) stays in VGPRs as fp16
-//   hi + lo pairs (22 significant bits) for the whole launch: the rotation is
-//   "weight stationary" and the inputs stream through.
+// * A wave owns 32 output coordinates and keeps its 32-row slice of Pi (or
+//   of M) in VGPRs as fp16 hi + lo pairs (22 significant bits) for the whole
+//   launch: the matrices are "weight stationary", the inputs stream through
+//   a persistent grid.
 // * Inputs are staged once per tile in LDS as fp16, scaled per vector by a
 //   power of two so the largest element sits in [2^14, 2^15); bf16 inputs
 //   are then exact, fp32 inputs are split into hi + lo.  The norm is
@@ -27,6 +27,13 @@
 //   as fp16 hi + lo, then z = (y/n - c_hat) M^T runs on MFMA against the
 //   stationary M slice; sign masks are ballots of z >= 0 and become the top
 //   bit plane of each coordinate's record.
+// * Two kernels share those steps.  quantize_kernel (MSE mode, and d = 256):
+//   D/32 waves, each tile staged, rotated and coded by the same waves.
+//   quantize_pc_kernel (inner-product mode, d <= 128): D/32 "producer" waves
+//   hold Pi and rotate + code tile k while D/32 "consumer" waves hold M,
+//   stage tile k+1 and run the QJL projection of tile k-1; one barrier per
+//   tile.  Each wave then carries one stationary matrix instead of two, and
+//   the VALU-heavy coding overlaps the MFMA-heavy projection on every SIMD.
 #include "tq_device.h"
 #include "tq_internal.h"
 
@@ -37,13 +44,26 @@ using namespace tqd;
 constexpr float kPiScale = 256.0f;   // Pi and M are scaled by 2^8 before the fp16 split
 constexpr float kResScale = 1024.0f; // residual scale before its fp16 split
 
+// Codes, norms and signs leave as scattered 2- and 4-byte pieces of rows:
+// stored with the default (write-back) policy so that L2 merges them into
+// whole lines; with the streaming policy each piece reaches HBM on its own.
+constexpr int kWriteBack = 0;
+
 template <int D>
 struct QLayout {
-  static constexpr int NW = D / 32;          // waves per workgroup
-  static constexpr int NT = NW * kWave;      // threads
+  static constexpr int NW = D / 32;          // waves per 32-coordinate split
+  static constexpr int NT = NW * kWave;      // threads of the fused kernel
   static constexpr int KS = D / 16;          // K steps of the 32x32x16 MFMA
   static constexpr int PITCH = D + 8;        // halves per LDS row (16 B pad)
   static constexpr int TPV = D / 16;         // staging threads per vector
+  static constexpr int TILE = 32 * PITCH;    // halves per LDS tile
+};
+
+template <int D, int LB, bool PROD>
+struct QFormat {
+  static constexpr int K = 1 << LB;                  // centroids
+  static constexpr int NPL = LB + (PROD ? 1 : 0);    // planes per record (sign on top)
+  static constexpr int RB = NPL * D / 8;             // bytes per packed row
 };
 
 // Load this lane's B fragments (hi, lo) of rows [32w, 32w+32) of a d x d
@@ -69,25 +89,284 @@ __device__ void load_stationary(const float *__restrict__ mat, int w, half8 (&hi
   }
 }
 
-// Codes, norms and signs leave as scattered 2- and 4-byte pieces of rows:
-// stored with the default (write-back) policy so that L2 merges them into
-// whole lines; with the streaming policy each piece reaches HBM on its own.
-constexpr int kWriteBack = 0;
-
 // Raw input of one staging thread: 16 consecutive elements of one vector.
 template <bool IN_F32>
 struct RawInput {
   i32x4 q[IN_F32 ? 4 : 2];
 };
 
+// Non-temporal loads of a staging thread's inputs of `tile`; rows past n_vec
+// (and tiles past the end) read zeros through the range check.
+template <bool IN_F32>
+__device__ __forceinline__ void load_raw(const i32x4 &rx, int64_t n_vec, int64_t x_stride, int64_t tile,
+                                         int sv_v, int sv_c, RawInput<IN_F32> &r) {
+  constexpr int ESZ = IN_F32 ? 4 : 2;
+  const int64_t gv = tile * 32 + sv_v;
+  const uint32_t off = gv < n_vec ? (uint32_t)((gv * x_stride + 16 * sv_c) * ESZ) : kNoStore;
+#pragma unroll
+  for (int q = 0; q < (IN_F32 ? 4 : 2); ++q) r.q[q] = tq_llvm_buf_ld_b128(rx, (int)(off + 16 * q), 0, kStream);
+}
+
+// Stages 16 elements of vector sv_v into an LDS tile (fp16, and fp16 lo for
+// fp32 inputs) after the per-vector power-of-two scale; the first thread of
+// a vector writes 1 / (scale * 2^8 * |x|) to vinv.  Returns the fp16 norm.
+template <int D, bool IN_F32>
+__device__ __forceinline__ uint16_t stage_vector(const RawInput<IN_F32> &r, _Float16 *xh, _Float16 *xl,
+                                                 float *vinv, int sv_v, int sv_c) {
+  using L = QLayout<D>;
+  float xv[16];
+  if constexpr (IN_F32) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xv[4 * q + e] = __int_as_float(r.q[q][e]);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t u = (uint32_t)r.q[q][e];
+        xv[8 * q + 2 * e] = __uint_as_float(u << 16);
+        xv[8 * q + 2 * e + 1] = __uint_as_float(u & 0xFFFF0000u);
+      }
+  }
+  double ss = 0.0;
+  float mx = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    ss = fma((double)xv[i], (double)xv[i], ss);
+    mx = fmaxf(mx, fabsf(xv[i]));
+  }
+#pragma unroll
+  for (int off = 1; off < L::TPV; off <<= 1) {
+    ss += wave_xor(ss, off);
+    mx = fmaxf(mx, wave_xor(mx, off));
+  }
+  int e = 0;
+  if (mx > 0.0f) {
+    e = ilogbf(mx);
+    e = e < -140 ? -140 : (e > 127 ? 127 : e);
+  }
+  const float sc = ldexpf(1.0f, 14 - e);
+  half8 hv[2], lv[2];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float sv = xv[i] * sc;
+    const _Float16 hh = (_Float16)sv;
+    hv[i >> 3][i & 7] = hh;
+    if constexpr (IN_F32) lv[i >> 3][i & 7] = (_Float16)(sv - (float)hh);
+  }
+  half8 *dh = (half8 *)&xh[sv_v * L::PITCH + 16 * sv_c];
+  dh[0] = hv[0];
+  dh[1] = hv[1];
+  if constexpr (IN_F32) {
+    half8 *dl = (half8 *)&xl[sv_v * L::PITCH + 16 * sv_c];
+    dl[0] = lv[0];
+    dl[1] = lv[1];
+  }
+  // 1 / (sc * 2^8 * |x|): the scaled sum of squares lies in [2^28, 2^37),
+  // so fp32 holds it; v_rsq_f32 is good to about one ulp.
+  const float ss_sc = (float)(ss * ((double)sc * (double)sc));
+  const float inv_n = ss > 0.0 ? __builtin_amdgcn_rsqf(ss_sc) * (1.0f / kPiScale) : 0.0f;
+  if (sv_c == 0) vinv[sv_v] = inv_n;
+  return f64_to_f16_bits(sqrt(ss));
+}
+
+// y = X Pi^T for the wave's 32 columns of a staged tile.
+template <int D, bool IN_F32>
+__device__ __forceinline__ f32x16 rotate_tile(const _Float16 *xh, const _Float16 *xl,
+                                              const half8 (&pih)[D / 16], const half8 (&pil)[D / 16], int m,
+                                              int h) {
+  using L = QLayout<D>;
+  f32x16 acc = {};
+#pragma unroll
+  for (int s = 0; s < L::KS; ++s) {
+    half8 ah = *(const half8 *)&xh[m * L::PITCH + 16 * s + 8 * h];
+    if constexpr (IN_F32) {
+      half8 al = *(const half8 *)&xl[m * L::PITCH + 16 * s + 8 * h];
+      acc = mfma32(al, pih[s], acc);
+    }
+    acc = mfma32(ah, pil[s], acc);
+    acc = mfma32(ah, pih[s], acc);
+  }
+  return acc;
+}
+
+// Codes of the wave's 32 x 32 block: plane words go to outw (lane slot
+// (r*LB + p)*2 + hh holds plane p of vector 8(r/4)+4hh+r%4); in
+// inner-product mode the residual y/n - c_hat (scaled 2^10, fp16 hi + lo) is
+// written to column 32w + m of rh/rl.
+template <int D, int LB, bool PROD>
+__device__ __forceinline__ void code_block(const f32x16 &acc, const float *vinv, const float *bnd,
+                                           const float *cen, _Float16 *rh, _Float16 *rl, int w, int m, int h,
+                                           uint32_t (&outw)[2]) {
+  using L = QLayout<D>;
+  constexpr int K = 1 << LB;
+  float inv[16];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    f32x4 t = *(const f32x4 *)&vinv[8 * g + 4 * h];
+    inv[4 * g] = t[0]; inv[4 * g + 1] = t[1]; inv[4 * g + 2] = t[2]; inv[4 * g + 3] = t[3];
+  }
+  outw[0] = 0u;
+  outw[1] = 0u;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float u = acc[r] * inv[r];
+    uint64_t planes[LB];
+#pragma unroll
+    for (int p = 0; p < LB; ++p) planes[p] = 0;
+    uint64_t ge[K - 1];   // thermometer masks: bit l = (u >= t_k) in lane l
+#pragma unroll
+    for (int k = 0; k < K - 1; ++k) {
+      ge[k] = __ballot(u >= bnd[k]);
+#pragma unroll
+      for (int p = 0; p < LB; ++p)
+        if (((k + 1) & ((1 << p) - 1)) == 0) planes[p] ^= ge[k];
+    }
+#pragma unroll
+    for (int p = 0; p < LB; ++p) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int slot = (r * LB + p) * 2 + hh;
+        const uint32_t word = (uint32_t)(planes[p] >> (32 * hh));
+        outw[slot >> 6] = write_lane(outw[slot >> 6], word, slot & 63);
+      }
+    }
+    if constexpr (PROD) {
+      // Centroid of the chosen cell from the thermometer masks, using the
+      // codebook's antisymmetry c[K/2-1-j] = -c[K/2+j]: pick the magnitude
+      // level j (idx >= K/2+j or idx <= K/2-1-j), then the sign
+      // (idx >= K/2  <=>  u >= t[K/2-1]); the mask logic stays on the scalar
+      // unit.
+      constexpr int MID = K / 2;
+      float mag = cen[MID];
+#pragma unroll
+      for (int j = 1; j < MID; ++j)
+        mag = __builtin_amdgcn_inverse_ballot_w64(ge[MID - 1 + j] | ~ge[MID - 1 - j]) ? cen[MID + j] : mag;
+      const float chat = __builtin_amdgcn_inverse_ballot_w64(ge[MID - 1]) ? mag : -mag;
+      const int v = 8 * (r >> 2) + 4 * h + (r & 3);
+      const float rs = (u - chat) * kResScale;
+      const _Float16 hv = (_Float16)rs;
+      rh[v * L::PITCH + 32 * w + m] = hv;
+      rl[v * L::PITCH + 32 * w + m] = (_Float16)(rs - (float)hv);
+    }
+  }
+}
+
+// Plane words of the block into their rows (rows past n_vec or a `live`
+// of false are dropped).
+template <int D, int LB, bool PROD>
+__device__ __forceinline__ void store_planes(const i32x4 &rc, const uint32_t (&outw)[2], int64_t base,
+                                             int64_t n_vec, bool live, int w, int l) {
+  using F = QFormat<D, LB, PROD>;
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    if (64 * g < 32 * LB) {
+      const int slot = 64 * g + l;
+      const int hh = slot & 1;
+      const int p = (slot >> 1) % LB;
+      const int r = (slot >> 1) / LB;
+      const int v = 8 * (r >> 2) + 4 * hh + (r & 3);
+      const int64_t gv = base + v;
+      const uint32_t off = (live && slot < 32 * LB && gv < n_vec)
+                               ? (uint32_t)(gv * F::RB + 4 * (w * F::NPL + p)) : kNoStore;
+      buf_store_u32<kWriteBack>(rc, off, outw[g]);
+    }
+  }
+}
+
+// z = R M^T for rows [32wq, 32wq+32) of M, and the sign words of the block:
+// lane 2r + hh holds the word of vector 8(r/4)+4hh+r%4.
+template <int D>
+__device__ __forceinline__ uint32_t sign_words(const _Float16 *rh, const _Float16 *rl,
+                                               const half8 (&mh)[D / 16], const half8 (&ml)[D / 16], int m,
+                                               int h) {
+  using L = QLayout<D>;
+  f32x16 acc2 = {};
+#pragma unroll
+  for (int s = 0; s < L::KS; ++s) {
+    half8 ah = *(const half8 *)&rh[m * L::PITCH + 16 * s + 8 * h];
+    half8 al = *(const half8 *)&rl[m * L::PITCH + 16 * s + 8 * h];
+    acc2 = mfma32(al, mh[s], acc2);
+    acc2 = mfma32(ah, ml[s], acc2);
+    acc2 = mfma32(ah, mh[s], acc2);
+  }
+  uint32_t sw = 0u;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const uint64_t mk = __ballot(acc2[r] >= 0.0f);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) sw = write_lane(sw, (uint32_t)(mk >> (32 * hh)), 2 * r + hh);
+  }
+  return sw;
+}
+
+// Sign words into the top plane of group wq (lanes 0..31; zero vectors get
+// all signs +1).
+template <int D, int LB>
+__device__ __forceinline__ void store_signs(const i32x4 &rc, uint32_t sw, const float *vinv, int64_t base,
+                                            int64_t n_vec, bool live, int wq, int l) {
+  using F = QFormat<D, LB, true>;
+  const int r = (l >> 1) & 15, hh = l & 1;
+  const int v = 8 * (r >> 2) + 4 * hh + (r & 3);
+  const int64_t gv = base + v;
+  if (vinv[v] == 0.0f) sw = 0xFFFFFFFFu;
+  const uint32_t off = (live && l < 32 && gv < n_vec) ? (uint32_t)(gv * F::RB + 4 * (wq * F::NPL + LB)) : kNoStore;
+  buf_store_u32<kWriteBack>(rc, off, sw);
+}
+
+// gamma = |residual| of the unit vector sv_v from its staged residual row:
+// sum of (hi + lo)^2 = hi.hi + 2 hi.lo + lo.lo, each a two-wide fp16 dot
+// product accumulated in fp32 (v_dot2_f32_f16), reduced over the vector's
+// TPV threads.
+template <int D>
+__device__ __forceinline__ float residual_norm(const _Float16 *rh, const _Float16 *rl, const float *vinv,
+                                               int sv_v, int sv_c) {
+  using L = QLayout<D>;
+  float s_hh = 0.0f, s_hl = 0.0f, s_ll = 0.0f;
+  const half8 *ph = (const half8 *)&rh[sv_v * L::PITCH + 16 * sv_c];
+  const half8 *pl = (const half8 *)&rl[sv_v * L::PITCH + 16 * sv_c];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const half8 hq = ph[q], lq = pl[q];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const half2 h2 = {hq[2 * i], hq[2 * i + 1]}, l2 = {lq[2 * i], lq[2 * i + 1]};
+      s_hh = __builtin_amdgcn_fdot2(h2, h2, s_hh, false);
+      s_hl = __builtin_amdgcn_fdot2(h2, l2, s_hl, false);
+      s_ll = __builtin_amdgcn_fdot2(l2, l2, s_ll, false);
+    }
+  }
+  float ss = s_hh + (2.0f * s_hl + s_ll);
+#pragma unroll
+  for (int off = 1; off < L::TPV; off <<= 1) ss += wave_xor(ss, off);
+  return vinv[sv_v] == 0.0f ? 0.0f : sqrtf(ss) * (1.0f / kResScale);
+}
+
+// Buffer resources over one call's rows.  The host keeps every range below
+// 2^31 bytes (large calls are split), so rows past n_vec and kNoStore fall
+// outside: such loads return 0 and such stores are dropped by the hardware.
+// No load or store sits behind a branch, which lets the compiler wait for
+// the next tile's loads without also waiting for this tile's stores.
+template <int D, int LB, bool PROD, bool IN_F32>
+struct QResources {
+  i32x4 rx, rc, rn, rr;
+  __device__ __forceinline__ explicit QResources(const tqi::QuantizeArgs &a) {
+    using F = QFormat<D, LB, PROD>;
+    constexpr int ESZ = IN_F32 ? 4 : 2;
+    rx = make_rsrc(a.x, (uint32_t)(((a.n_vec - 1) * a.x_stride + D) * ESZ));
+    rc = make_rsrc(a.codes + a.out_offset * F::RB, (uint32_t)(a.n_vec * F::RB));
+    rn = make_rsrc(a.norm + a.out_offset, (uint32_t)(a.n_vec * 2));
+    rr = make_rsrc(PROD ? a.rnorm + a.out_offset : a.norm, PROD ? (uint32_t)(a.n_vec * 2) : 0u);
+  }
+};
+
 template <int D, int LB, bool PROD, bool IN_F32>
 __global__ __launch_bounds__(QLayout<D>::NT) void quantize_kernel(tqi::QuantizeArgs a) {
   using L = QLayout<D>;
-  constexpr int K = 1 << LB;                  // centroids
-  constexpr int PB = D / 8;                   // bytes per plane
-  constexpr int NPL = LB + (PROD ? 1 : 0);    // planes per record (sign on top)
-  constexpr int RB = NPL * PB;                // bytes per packed row
-  constexpr int TILE = 32 * L::PITCH;
+  constexpr int K = 1 << LB;
+  constexpr int TILE = L::TILE;
   // Two LDS buffers, alternated per tile: a tile's staging never overwrites
   // data that the previous tile may still read, so one barrier per stage
   // suffices.
@@ -118,224 +397,7 @@ __global__ __launch_bounds__(QLayout<D>::NT) void quantize_kernel(tqi::QuantizeA
   for (int k = 0; k < K; ++k) cen[k] = PROD ? a.centroids[k] : 0.0f;
 
   const int64_t n_tiles = (a.n_vec + 31) / 32;
-
-  // Buffer resources over this call's rows.  The host keeps every range below
-  // 2^31 bytes (large calls are split), so rows past n_vec and kNoStore fall
-  // outside: such loads return 0 and such stores are dropped by the hardware.
-  // No load or store sits behind a branch, which lets the compiler wait for
-  // the next tile's loads without also waiting for this tile's stores.
-  constexpr int ESZ = IN_F32 ? 4 : 2;
-  const i32x4 rx = make_rsrc(a.x, (uint32_t)(((a.n_vec - 1) * a.x_stride + D) * ESZ));
-  const i32x4 rc = make_rsrc(a.codes + a.out_offset * RB, (uint32_t)(a.n_vec * RB));
-  const i32x4 rn = make_rsrc(a.norm + a.out_offset, (uint32_t)(a.n_vec * 2));
-  const i32x4 rr = make_rsrc(PROD ? a.rnorm + a.out_offset : a.norm, PROD ? (uint32_t)(a.n_vec * 2) : 0u);
-
-  // Non-temporal loads of a tile's inputs (16 elements per staging thread).
-  auto load_raw = [&](int64_t tile, RawInput<IN_F32> &r) {
-    const int64_t gv = tile * 32 + sv_v;
-    const uint32_t off = gv < a.n_vec ? (uint32_t)((gv * a.x_stride + 16 * sv_c) * ESZ) : kNoStore;
-#pragma unroll
-    for (int q = 0; q < (IN_F32 ? 4 : 2); ++q) r.q[q] = tq_llvm_buf_ld_b128(rx, (int)(off + 16 * q), 0, kStream);
-  };
-
-  // Stages a tile into LDS buffer `buf`; returns this thread's fp16 norm
-  // bits, stored by the caller once the next tile's loads are in flight.
-  auto stage = [&](int64_t tile, const RawInput<IN_F32> &r, int buf) -> uint16_t {
-    {
-      float xv[16];
-      if constexpr (IN_F32) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) xv[4 * q + e] = __int_as_float(r.q[q][e]);
-      } else {
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t u = (uint32_t)r.q[q][e];
-            xv[8 * q + 2 * e] = __uint_as_float(u << 16);
-            xv[8 * q + 2 * e + 1] = __uint_as_float(u & 0xFFFF0000u);
-          }
-      }
-      double ss = 0.0;
-      float mx = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        ss = fma((double)xv[i], (double)xv[i], ss);
-        mx = fmaxf(mx, fabsf(xv[i]));
-      }
-#pragma unroll
-      for (int off = 1; off < L::TPV; off <<= 1) {
-        ss += wave_xor(ss, off);
-        mx = fmaxf(mx, wave_xor(mx, off));
-      }
-      int e = 0;
-      if (mx > 0.0f) {
-        e = ilogbf(mx);
-        e = e < -140 ? -140 : (e > 127 ? 127 : e);
-      }
-      const float sc = ldexpf(1.0f, 14 - e);
-      half8 hv[2], lv[2];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float sv = xv[i] * sc;
-        const _Float16 hh = (_Float16)sv;
-        hv[i >> 3][i & 7] = hh;
-        if constexpr (IN_F32) lv[i >> 3][i & 7] = (_Float16)(sv - (float)hh);
-      }
-      half8 *dh = (half8 *)&xh[buf][sv_v * L::PITCH + 16 * sv_c];
-      dh[0] = hv[0];
-      dh[1] = hv[1];
-      if constexpr (IN_F32) {
-        half8 *dl = (half8 *)&xl[buf][sv_v * L::PITCH + 16 * sv_c];
-        dl[0] = lv[0];
-        dl[1] = lv[1];
-      }
-      // 1 / (sc * 2^8 * |x|): the scaled sum of squares lies in [2^28, 2^37),
-      // so fp32 holds it; v_rsq_f32 is good to about one ulp.
-      const float ss_sc = (float)(ss * ((double)sc * (double)sc));
-      const float inv_n = ss > 0.0 ? __builtin_amdgcn_rsqf(ss_sc) * (1.0f / kPiScale) : 0.0f;
-      if (sv_c == 0) vinv[buf][sv_v] = inv_n;
-      return f64_to_f16_bits(sqrt(ss));
-    }
-  };
-
-  auto compute = [&](int64_t tile, int buf) {
-    const int64_t base = tile * 32;
-    // ---------------------------------------------------------- y = X Pi^T
-    f32x16 acc = {};
-#pragma unroll
-    for (int s = 0; s < L::KS; ++s) {
-      half8 ah = *(const half8 *)&xh[buf][m * L::PITCH + 16 * s + 8 * h];
-      if constexpr (IN_F32) {
-        half8 al = *(const half8 *)&xl[buf][m * L::PITCH + 16 * s + 8 * h];
-        acc = mfma32(al, pih[s], acc);
-      }
-      acc = mfma32(ah, pil[s], acc);
-      acc = mfma32(ah, pih[s], acc);
-    }
-    // ------------------------------------------ codes: compares + bit planes
-    float inv[16];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      f32x4 t = *(const f32x4 *)&vinv[buf][8 * g + 4 * h];
-      inv[4 * g] = t[0]; inv[4 * g + 1] = t[1]; inv[4 * g + 2] = t[2]; inv[4 * g + 3] = t[3];
-    }
-    uint32_t outw[2] = {0u, 0u};   // up to 128 plane words per wave
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float u = acc[r] * inv[r];
-      uint64_t planes[LB];
-#pragma unroll
-      for (int p = 0; p < LB; ++p) planes[p] = 0;
-      uint64_t ge[K - 1];   // thermometer masks: bit l = (u >= t_k) in lane l
-#pragma unroll
-      for (int k = 0; k < K - 1; ++k) {
-        ge[k] = __ballot(u >= bnd[k]);
-#pragma unroll
-        for (int p = 0; p < LB; ++p)
-          if (((k + 1) & ((1 << p) - 1)) == 0) planes[p] ^= ge[k];
-      }
-      // Centroid of the chosen cell from the thermometer masks, using the
-      // codebook's antisymmetry c[K/2-1-j] = -c[K/2+j]: pick the magnitude
-      // level j (|idx - K/2 + 1/2| - 1/2 >= j  <=>  idx >= K/2+j or
-      // idx <= K/2-1-j), then the sign (idx >= K/2  <=>  u >= t[K/2-1]).
-      float chat = 0.0f;
-      if constexpr (PROD) {
-        constexpr int MID = K / 2;
-        float mag = cen[MID];
-#pragma unroll
-        for (int j = 1; j < MID; ++j)   // mask logic stays on the scalar unit
-          mag = __builtin_amdgcn_inverse_ballot_w64(ge[MID - 1 + j] | ~ge[MID - 1 - j]) ? cen[MID + j] : mag;
-        chat = __builtin_amdgcn_inverse_ballot_w64(ge[MID - 1]) ? mag : -mag;
-      }
-#pragma unroll
-      for (int p = 0; p < LB; ++p) {
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int slot = (r * LB + p) * 2 + hh;
-          const uint32_t word = (uint32_t)(planes[p] >> (32 * hh));
-          outw[slot >> 6] = write_lane(outw[slot >> 6], word, slot & 63);
-        }
-      }
-      if constexpr (PROD) {
-        const int v = 8 * (r >> 2) + 4 * h + (r & 3);
-        const float rs = (u - chat) * kResScale;
-        const _Float16 hv = (_Float16)rs;
-        rh[buf][v * L::PITCH + 32 * w + m] = hv;
-        rl[buf][v * L::PITCH + 32 * w + m] = (_Float16)(rs - (float)hv);
-      }
-    }
-    // store plane words: slot = (r*LB + p)*2 + hh -> vector 8(r/4)+4hh+r%4
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      if (64 * g < 32 * LB) {
-        const int slot = 64 * g + l;
-        const int hh = slot & 1;
-        const int p = (slot >> 1) % LB;
-        const int r = (slot >> 1) / LB;
-        const int v = 8 * (r >> 2) + 4 * hh + (r & 3);
-        const int64_t gv = base + v;
-        const uint32_t off =
-            (slot < 32 * LB && gv < a.n_vec) ? (uint32_t)(gv * RB + 4 * (w * NPL + p)) : kNoStore;
-        buf_store_u32<kWriteBack>(rc, off, outw[g]);
-      }
-    }
-    if constexpr (PROD) {
-      __syncthreads();
-      // ------------------------------------ z = (y/n - c_hat) M^T, sign bits
-      f32x16 acc2 = {};
-#pragma unroll
-      for (int s = 0; s < L::KS; ++s) {
-        half8 ah = *(const half8 *)&rh[buf][m * L::PITCH + 16 * s + 8 * h];
-        half8 al = *(const half8 *)&rl[buf][m * L::PITCH + 16 * s + 8 * h];
-        acc2 = mfma32(al, mh[s], acc2);
-        acc2 = mfma32(ah, ml[s], acc2);
-        acc2 = mfma32(ah, mh[s], acc2);
-      }
-      uint32_t sw = 0u;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const uint64_t mk = __ballot(acc2[r] >= 0.0f);
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) sw = write_lane(sw, (uint32_t)(mk >> (32 * hh)), 2 * r + hh);
-      }
-      {
-        const int r = (l >> 1) & 15, hh = l & 1;
-        const int v = 8 * (r >> 2) + 4 * hh + (r & 3);
-        const int64_t gv = base + v;
-        if (vinv[buf][v] == 0.0f) sw = 0xFFFFFFFFu;   // zero vector: all signs +1
-        const uint32_t off = (l < 32 && gv < a.n_vec) ? (uint32_t)(gv * RB + 4 * (w * NPL + LB)) : kNoStore;
-        buf_store_u32<kWriteBack>(rc, off, sw);
-      }
-      // residual norm of the unit vector from the staged residual tile
-      {
-        // sum of (hi + lo)^2 = hi.hi + 2 hi.lo + lo.lo, each term a
-        // two-wide fp16 dot product accumulated in fp32 (v_dot2_f32_f16)
-        float s_hh = 0.0f, s_hl = 0.0f, s_ll = 0.0f;
-        const half8 *ph = (const half8 *)&rh[buf][sv_v * L::PITCH + 16 * sv_c];
-        const half8 *pl = (const half8 *)&rl[buf][sv_v * L::PITCH + 16 * sv_c];
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const half8 hq = ph[q], lq = pl[q];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const half2 h2 = {hq[2 * i], hq[2 * i + 1]}, l2 = {lq[2 * i], lq[2 * i + 1]};
-            s_hh = __builtin_amdgcn_fdot2(h2, h2, s_hh, false);
-            s_hl = __builtin_amdgcn_fdot2(h2, l2, s_hl, false);
-            s_ll = __builtin_amdgcn_fdot2(l2, l2, s_ll, false);
-          }
-        }
-        float ss = s_hh + (2.0f * s_hl + s_ll);
-#pragma unroll
-        for (int off = 1; off < L::TPV; off <<= 1) ss += wave_xor(ss, off);
-        const int64_t gv = base + sv_v;
-        const float gam = vinv[buf][sv_v] == 0.0f ? 0.0f : sqrtf(ss) * (1.0f / kResScale);
-        buf_store_u16<kWriteBack>(rr, (sv_c == 0 && gv < a.n_vec) ? (uint32_t)(2 * gv) : kNoStore, f32_to_f16_bits(gam));
-      }
-    }
-  };
+  const QResources<D, LB, PROD, IN_F32> res(a);
 
   // One register set of raw input: the next tile's loads are issued as soon
   // as the current tile has been staged, so they fly during its GEMMs and
@@ -343,54 +405,168 @@ __global__ __launch_bounds__(QLayout<D>::NT) void quantize_kernel(tqi::QuantizeA
   const int64_t step = gridDim.x;
   int64_t tile = blockIdx.x;
   RawInput<IN_F32> raw;
-  load_raw(tile, raw);
+  load_raw<IN_F32>(res.rx, a.n_vec, a.x_stride, tile, sv_v, sv_c, raw);
   // Range-dropped stores: with them, on entry as on every later iteration,
   // stores follow the pending input loads, so the compiler can wait for
   // those loads alone (it merges the counts of both paths into the loop).
 #pragma unroll
-  for (int i = 0; i < 5; ++i) buf_store_u32<kWriteBack>(rn, kNoStore + 4 * i, 0u);
+  for (int i = 0; i < 5; ++i) buf_store_u32<kWriteBack>(res.rn, kNoStore + 4 * i, 0u);
   int buf = 0;
   for (; tile < n_tiles; tile += step, buf ^= 1) {
-    const uint16_t n16 = stage(tile, raw, buf);
-    load_raw(tile + step, raw);
+    const uint16_t n16 = stage_vector<D, IN_F32>(raw, xh[buf], xl[IN_F32 ? buf : 0], vinv[buf], sv_v, sv_c);
+    load_raw<IN_F32>(res.rx, a.n_vec, a.x_stride, tile + step, sv_v, sv_c, raw);
     __builtin_amdgcn_sched_barrier(0);
-    const int64_t gv = tile * 32 + sv_v;
-    buf_store_u16<kWriteBack>(rn, (sv_c == 0 && gv < a.n_vec) ? (uint32_t)(2 * gv) : kNoStore, n16);
+    const int64_t base = tile * 32;
+    buf_store_u16<kWriteBack>(res.rn, (sv_c == 0 && base + sv_v < a.n_vec) ? (uint32_t)(2 * (base + sv_v)) : kNoStore,
+                              n16);
     __syncthreads();
-    compute(tile, buf);
+    const f32x16 acc = rotate_tile<D, IN_F32>(xh[buf], xl[IN_F32 ? buf : 0], pih, pil, m, h);
+    uint32_t outw[2];
+    code_block<D, LB, PROD>(acc, vinv[buf], bnd, cen, rh[PROD ? buf : 0], rl[PROD ? buf : 0], w, m, h, outw);
+    store_planes<D, LB, PROD>(res.rc, outw, base, a.n_vec, true, w, l);
+    if constexpr (PROD) {
+      __syncthreads();
+      const uint32_t sw = sign_words<D>(rh[buf], rl[buf], mh, ml, m, h);
+      store_signs<D, LB>(res.rc, sw, vinv[buf], base, a.n_vec, true, w, l);
+      const float gam = residual_norm<D>(rh[buf], rl[buf], vinv[buf], sv_v, sv_c);
+      buf_store_u16<kWriteBack>(res.rr, (sv_c == 0 && base + sv_v < a.n_vec) ? (uint32_t)(2 * (base + sv_v)) : kNoStore,
+                                f32_to_f16_bits(gam));
+    }
   }
 }
 
-template <int D, int LB, bool PROD, bool IN_F32>
-hipError_t launch_t(const tqi::QuantizeArgs &a, hipStream_t s) {
+// Inner-product mode, producer / consumer split.  Waves [0, D/32) produce:
+// rotate and code tile k from xh[k%2] (staged in the previous iteration) and
+// write its residual to rh/rl[k%2].  Waves [D/32, D/16) consume: stage tile
+// k+1 into xh[(k+1)%2] and run the QJL projection, signs and residual norm
+// of tile k-1 from rh/rl[(k+1)%2].  Every buffer a side writes in iteration k
+// is read by the other side in iteration k+1, so one barrier per iteration
+// orders everything.  The loop runs one iteration past the last tile to
+// drain the consumers; work on a side's missing tile is done on stale data
+// and its stores are dropped, which keeps the loop free of branches.
+template <int D, int LB, bool IN_F32>
+__global__ __launch_bounds__(2 * QLayout<D>::NT) void quantize_pc_kernel(tqi::QuantizeArgs a) {
   using L = QLayout<D>;
+  constexpr int K = 1 << LB;
+  constexpr int TILE = L::TILE;
+  constexpr int NWP = L::NW;        // producer waves
+  __shared__ __attribute__((aligned(16))) _Float16 xh[2][TILE];
+  __shared__ __attribute__((aligned(16))) _Float16 xl[IN_F32 ? 2 : 1][IN_F32 ? TILE : 8];
+  __shared__ __attribute__((aligned(16))) _Float16 rh[2][TILE];
+  __shared__ __attribute__((aligned(16))) _Float16 rl[2][TILE];
+  __shared__ __attribute__((aligned(16))) float vinv[2][32];   // written by the stagers
+  __shared__ __attribute__((aligned(16))) float rinv[2][32];   // copy that travels with rh/rl
+
+  const int tid = threadIdx.x;
+  const int w = tid / kWave;
+  const int l = lane_id();
+  const int m = l & 31;
+  const int h = l >> 5;
+  const bool producer = w < NWP;                // wave-uniform
+  const int wq = producer ? w : w - NWP;        // 32-row slice of Pi (producer) or M (consumer)
+  const int ct = tid - NWP * kWave;             // consumer thread: staging / residual-norm mapping
+  const int sv_v = ct / L::TPV;
+  const int sv_c = ct % L::TPV;
+
+  half8 sh[L::KS], sl[L::KS];
+  load_stationary<D>(producer ? a.pi : a.m, wq, sh, sl);
+  float bnd[K - 1];
+#pragma unroll
+  for (int k = 0; k < K - 1; ++k) bnd[k] = a.boundaries[k];
+  float cen[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) cen[k] = a.centroids[k];
+
+  const int64_t n_tiles = (a.n_vec + 31) / 32;
+  const QResources<D, LB, true, IN_F32> res(a);
+  const int64_t step = gridDim.x;
+  const int64_t t0 = blockIdx.x;
+
+  RawInput<IN_F32> raw;
+  if (!producer) {
+    load_raw<IN_F32>(res.rx, a.n_vec, a.x_stride, t0, sv_v, sv_c, raw);
+    const uint16_t n16 = stage_vector<D, IN_F32>(raw, xh[0], xl[0], vinv[0], sv_v, sv_c);
+    buf_store_u16<kWriteBack>(res.rn, (sv_c == 0 && t0 * 32 + sv_v < a.n_vec) ? (uint32_t)(2 * (t0 * 32 + sv_v)) : kNoStore,
+                              n16);
+    load_raw<IN_F32>(res.rx, a.n_vec, a.x_stride, t0 + step, sv_v, sv_c, raw);
+  }
+  __syncthreads();
+  for (int k = 0;; ++k) {
+    const int64_t tp = t0 + k * step;               // the producers' tile
+    if (tp >= n_tiles + step) break;                // consumers have drained
+    const int kb = k & 1;
+    if (producer) {
+      const f32x16 acc = rotate_tile<D, IN_F32>(xh[kb], xl[IN_F32 ? kb : 0], sh, sl, m, h);
+      uint32_t outw[2];
+      code_block<D, LB, true>(acc, vinv[kb], bnd, cen, rh[kb], rl[kb], wq, m, h, outw);
+      store_planes<D, LB, true>(res.rc, outw, tp * 32, a.n_vec, tp < n_tiles, wq, l);
+      if (tid < 32) rinv[kb][tid] = vinv[kb][tid];
+    } else {
+      // stage tile tp + step (zeros past the end), prefetch the one after
+      const int64_t ts = tp + step;
+      const uint16_t n16 = stage_vector<D, IN_F32>(raw, xh[kb ^ 1], xl[IN_F32 ? kb ^ 1 : 0], vinv[kb ^ 1], sv_v, sv_c);
+      load_raw<IN_F32>(res.rx, a.n_vec, a.x_stride, ts + step, sv_v, sv_c, raw);
+      __builtin_amdgcn_sched_barrier(0);
+      buf_store_u16<kWriteBack>(res.rn, (sv_c == 0 && ts * 32 + sv_v < a.n_vec) ? (uint32_t)(2 * (ts * 32 + sv_v)) : kNoStore,
+                                n16);
+      // QJL projection of tile tp - step (from the previous iteration)
+      const int64_t tc = tp - step;
+      const bool live = k > 0;
+      const uint32_t sw = sign_words<D>(rh[kb ^ 1], rl[kb ^ 1], sh, sl, m, h);
+      store_signs<D, LB>(res.rc, sw, rinv[kb ^ 1], tc * 32, a.n_vec, live, wq, l);
+      const float gam = residual_norm<D>(rh[kb ^ 1], rl[kb ^ 1], rinv[kb ^ 1], sv_v, sv_c);
+      buf_store_u16<kWriteBack>(res.rr, (live && sv_c == 0 && tc * 32 + sv_v < a.n_vec) ? (uint32_t)(2 * (tc * 32 + sv_v)) : kNoStore,
+                                f32_to_f16_bits(gam));
+    }
+    __syncthreads();
+  }
+}
+
+// Rows per launch so that the input, code and norm byte ranges stay below
+// 2^31; 0 if one row's input is already too wide.
+template <int D, int LB, bool PROD, bool IN_F32>
+int64_t rows_per_launch(int64_t x_stride) {
   constexpr int64_t ESZ = IN_F32 ? 4 : 2;
-  constexpr int64_t RB = (LB + (PROD ? 1 : 0)) * D / 8;
-  constexpr int64_t kRange = (int64_t{1} << 31) - 1;   // kernel byte ranges stay below 2^31
-  if (a.x_stride * ESZ > kRange) return hipErrorInvalidValue;
-  // Rows per launch so that the input, code and norm ranges fit.
-  int64_t rows = kRange / (a.x_stride * ESZ);
-  if (rows > kRange / RB) rows = kRange / RB;
+  constexpr int64_t kRange = (int64_t{1} << 31) - 1;
+  if (x_stride * ESZ > kRange) return 0;
+  int64_t rows = kRange / (x_stride * ESZ);
+  if (rows > kRange / QFormat<D, LB, PROD>::RB) rows = kRange / QFormat<D, LB, PROD>::RB;
   if (rows >= 32) rows &= ~int64_t{31};
+  return rows;
+}
+
+template <typename Kernel>
+hipError_t launch_chunks(Kernel kernel, int threads, int64_t rows, int64_t esz, const tqi::QuantizeArgs &a,
+                         hipStream_t s) {
+  if (rows <= 0) return hipErrorInvalidValue;
   int blocks_per_cu = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      &blocks_per_cu, quantize_kernel<D, LB, PROD, IN_F32>, L::NT, 0);
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks_per_cu, kernel, threads, 0);
   if (e != hipSuccess) return e;
   if (blocks_per_cu < 1) blocks_per_cu = 1;
   for (int64_t start = 0; start < a.n_vec; start += rows) {
     tqi::QuantizeArgs c = a;
-    c.x = (const char *)a.x + start * a.x_stride * ESZ;
+    c.x = (const char *)a.x + start * a.x_stride * esz;
     c.n_vec = a.n_vec - start < rows ? a.n_vec - start : rows;
     c.out_offset = a.out_offset + start;
     const int64_t n_tiles = (c.n_vec + 31) / 32;
     int64_t grid = (int64_t)tqi::device_cu_count() * blocks_per_cu;
     if (grid > n_tiles) grid = n_tiles;
-    hipLaunchKernelGGL((quantize_kernel<D, LB, PROD, IN_F32>), dim3((unsigned)grid), dim3(L::NT),
-                       0, s, c);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(threads), 0, s, c);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+template <int D, int LB, bool PROD, bool IN_F32>
+hipError_t launch_t(const tqi::QuantizeArgs &a, hipStream_t s) {
+  using L = QLayout<D>;
+  const int64_t rows = rows_per_launch<D, LB, PROD, IN_F32>(a.x_stride);
+  const int64_t esz = IN_F32 ? 4 : 2;
+  if constexpr (PROD && D <= 128)
+    return launch_chunks(quantize_pc_kernel<D, LB, IN_F32>, 2 * L::NT, rows, esz, a, s);
+  else
+    return launch_chunks(quantize_kernel<D, LB, PROD, IN_F32>, L::NT, rows, esz, a, s);
 }
 
 template <int D, int LB, bool PROD>
