@@ -21,8 +21,11 @@ SOURCES = ["host_math.cpp", "tq_api.cpp", "quantize.hip", "logits.hip", "dequant
 
 # Packed-fp32 VALU ops are disabled for all device code (they are avoided on
 # this hardware); the host pass warns that it does not know the feature.
+# -amdgpu-mfma-vgpr-form: MFMA results land in VGPRs, not accumulation
+# registers, so the epilogues read them without v_accvgpr_read copies.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-mllvm", "-amdgpu-mfma-vgpr-form",
              "-Wno-unused-command-line-argument"]
 
 
