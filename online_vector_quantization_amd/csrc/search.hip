@@ -28,6 +28,9 @@ namespace {
 using namespace tqd;
 
 constexpr int kTop = 16;               // list length kept per lane (topk <= 16)
+constexpr int kCand = 16;              // candidate slots per lane between list updates
+constexpr int kSearchThreads = 512;    // 8 waves
+constexpr int kSearchQueries = 32 * (kSearchThreads / 64);   // queries per workgroup
 constexpr float kCenScale = 1024.0f;
 
 struct QPrepArgs {
@@ -94,18 +97,80 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
+// Sorted (descending) running list of one lane.  Entries arrive in increasing
+// key order, so an equal score never displaces an entry already present.
+struct TopList {
+  float v[kTop];
+  int i[kTop];
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int j = 0; j < kTop; ++j) { v[j] = -FLT_MAX; i[j] = 0x7FFFFFFF; }
+  }
+  __device__ __forceinline__ void insert(float x, int xi) {
+    bool c[kTop];
+#pragma unroll
+    for (int j = 0; j < kTop; ++j) c[j] = x > v[j];
+#pragma unroll
+    for (int j = kTop - 1; j > 0; --j) {
+      v[j] = c[j - 1] ? v[j - 1] : (c[j] ? x : v[j]);
+      i[j] = c[j - 1] ? i[j - 1] : (c[j] ? xi : i[j]);
+    }
+    v[0] = c[0] ? x : v[0];
+    i[0] = c[0] ? xi : i[0];
+  }
+};
+
 template <int D, int LB>
-__global__ __launch_bounds__(256) void search_score_kernel(ScoreArgs a) {
-  constexpr int K = 1 << LB;
-  constexpr int PB = D / 8;
+struct SearchTile {
+  static constexpr int K = 1 << LB;
+  static constexpr int PITCH = D + 8;      // halves per decoded key row (16-byte pad)
+  static constexpr int CPT = D / 16;       // coordinates a thread decodes per tile
+  static constexpr int ROWB = LB * D / 8;  // packed bytes per key
+};
+
+// Decode the coordinates [CPT*c, CPT*c + CPT) of one key from its bit-plane
+// words into fp16 hi and lo halves through the pair table.
+template <int D, int LB>
+__device__ __forceinline__ void decode_pairs(const uint32_t (&pw)[LB], int c, const uint2 *ptab,
+                                             _Float16 *hrow, _Float16 *lrow) {
+  constexpr int CPT = SearchTile<D, LB>::CPT;
+  const int boff = (CPT * c) & 31;
+  uint32_t u[LB];
+#pragma unroll
+  for (int p = 0; p < LB; ++p) u[p] = pw[p] >> boff;
+  uint32_t hw[CPT / 2], lw[CPT / 2];
+#pragma unroll
+  for (int k = 0; k < CPT / 2; ++k) {
+    uint32_t pidx = 0;
+#pragma unroll
+    for (int p = 0; p < LB; ++p) pidx |= ((u[p] >> (2 * k)) & 3u) << (2 * p);
+    const uint2 e = ptab[pidx];
+    hw[k] = e.x;
+    lw[k] = e.y;
+  }
+#pragma unroll
+  for (int k = 0; k < CPT / 2; k += 4) {
+    *(uint4 *)(hrow + 2 * k) = make_uint4(hw[k], hw[k + 1], hw[k + 2], hw[k + 3]);
+    *(uint4 *)(lrow + 2 * k) = make_uint4(lw[k], lw[k + 1], lw[k + 2], lw[k + 3]);
+  }
+}
+
+template <int D, int LB>
+__global__ __launch_bounds__(kSearchThreads) void search_score_kernel(ScoreArgs a) {
+  using T = SearchTile<D, LB>;
+  constexpr int K = T::K;
   constexpr int KS = D / 16;
-  constexpr int PITCH = D + 8;
-  __shared__ __attribute__((aligned(16))) _Float16 ch[32 * PITCH];
-  __shared__ __attribute__((aligned(16))) _Float16 cl[32 * PITCH];
-  __shared__ float kn[32];
-  __shared__ uint32_t ctab[K];
-  __shared__ float mval[4][32][2][kTop];
-  __shared__ int midx[4][32][2][kTop];
+  constexpr int PITCH = T::PITCH;
+  constexpr int CPT = T::CPT;
+  constexpr int ROWB = T::ROWB;
+  constexpr int NW = kSearchThreads / 64;
+  __shared__ __attribute__((aligned(16))) _Float16 ch[2][32 * PITCH];
+  __shared__ __attribute__((aligned(16))) _Float16 cl[2][32 * PITCH];
+  __shared__ __attribute__((aligned(16))) float kn[2][32];
+  __shared__ uint2 ptab[K * K];
+  // Per-lane candidate slots, lane-minor so a row of slots is one 512-byte
+  // line per wave; reused for the final half-list merge.
+  __shared__ uint2 cbuf[NW * kCand * 64];
 
   const int split = blockIdx.x % a.n_splits;
   const int rest = blockIdx.x / a.n_splits;
@@ -114,14 +179,16 @@ __global__ __launch_bounds__(256) void search_score_kernel(ScoreArgs a) {
   const int b = stream / a.n_kv_heads;
   const int kvh = stream % a.n_kv_heads;
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = lane_id();
   const int m = l & 31;
   const int h = l >> 5;
 
-  const int gq = qt * 128 + 32 * w + m;               // query within the GQA group
+  const int gq0 = qt * kSearchQueries + 32 * w;          // first query of this wave
+  const bool wave_live = gq0 < a.group;
+  const int gq = gq0 + m;
   const bool qvalid = gq < a.group;
-  const int64_t qglob = ((int64_t)b * a.n_q_heads + (int64_t)kvh * a.group + (qvalid ? gq : 0));
+  const int64_t qglob = (int64_t)b * a.n_q_heads + (int64_t)kvh * a.group + (qvalid ? gq : 0);
   half8 qh[KS], ql[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
@@ -134,100 +201,150 @@ __global__ __launch_bounds__(256) void search_score_kernel(ScoreArgs a) {
     }
   }
   const float qf = qvalid ? a.qfac[qglob] * a.scale : 0.0f;
-  if (tid < K) {
-    const float cv = a.centroids[tid] * kCenScale;
-    const _Float16 hv = (_Float16)cv;
-    const _Float16 lv = (_Float16)(cv - (float)hv);
-    uint16_t hb, lb;
-    __builtin_memcpy(&hb, &hv, 2);
-    __builtin_memcpy(&lb, &lv, 2);
-    ctab[tid] = (uint32_t)hb | ((uint32_t)lb << 16);
-  }
-  float tv[kTop];
-  int ti[kTop];
+
+  // pair table: bits 2p and 2p+1 of the entry index are plane p of the even
+  // and of the odd coordinate of a pair
+  if (tid < K * K) {
+    uint32_t i0 = 0, i1 = 0;
 #pragma unroll
-  for (int i = 0; i < kTop; ++i) { tv[i] = -FLT_MAX; ti[i] = 0x7FFFFFFF; }
+    for (int p = 0; p < LB; ++p) {
+      i0 |= ((tid >> (2 * p)) & 1u) << p;
+      i1 |= ((tid >> (2 * p + 1)) & 1u) << p;
+    }
+    uint32_t hw = 0, lw = 0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float cv = a.centroids[j ? i1 : i0] * kCenScale;
+      const _Float16 hv = (_Float16)cv;
+      const _Float16 lv = (_Float16)(cv - (float)hv);
+      uint16_t hb, lb;
+      __builtin_memcpy(&hb, &hv, 2);
+      __builtin_memcpy(&lb, &lv, 2);
+      hw |= (uint32_t)hb << (16 * j);
+      lw |= (uint32_t)lb << (16 * j);
+    }
+    ptab[tid] = make_uint2(hw, lw);
+  }
 
   const int64_t k_begin = (int64_t)split * a.keys_per_split;
   int64_t k_end = k_begin + a.keys_per_split;
   if (k_end > a.seq_len) k_end = a.seq_len;
-  const int64_t key0 = (int64_t)stream * a.row_tokens;
-  __syncthreads();
+  const int n_keys = (int)(k_end - k_begin);
+  const int64_t key0 = (int64_t)stream * a.row_tokens + k_begin;
+  // Keys past the split's end fall outside these ranges and load as zero.
+  const i32x4 rcode = make_rsrc(a.codes + key0 * ROWB, (uint32_t)n_keys * ROWB);
+  const i32x4 rnrm = make_rsrc(a.norm + key0, (uint32_t)n_keys * 2u);
 
-  for (int64_t t0 = k_begin; t0 < k_end; t0 += 32) {
-    // decode 32 keys: 2*D chunks of 16 coordinates over 256 threads
-    for (int ci = tid; ci < 2 * D; ci += 256) {
-      const int v = ci / (D / 16);
-      const int c = ci % (D / 16);
-      const int64_t t = t0 + v;
-      const bool valid = t < k_end;
-      const int64_t key = key0 + (valid ? t : k_end - 1);
-      uint32_t pw[LB];
+  // decode role: key v of a tile, coordinates [CPT*c, CPT*c + CPT)
+  const int dv = tid >> 4;
+  const int dc = tid & 15;
+  const uint32_t code_off = (uint32_t)dv * ROWB + 4u * LB * (uint32_t)((CPT * dc) >> 5);
+  uint32_t pw[LB];
+  uint16_t nb = 0;
+  auto load_tile = [&](int t0) {
+    buf_load_words<LB, 0>(rcode, (uint32_t)t0 * ROWB + code_off, pw);
+    if (dc == 0) nb = buf_load_u16<0>(rnrm, 2u * (uint32_t)(t0 + dv));
+  };
+  auto decode_tile = [&](int buf) {
+    decode_pairs<D, LB>(pw, dc, ptab, &ch[buf][dv * PITCH + CPT * dc], &cl[buf][dv * PITCH + CPT * dc]);
+    if (dc == 0) kn[buf][dv] = f16_bits_to_f32(nb);
+  };
+
+  TopList top;
+  top.init();
+  float thr = qvalid ? -FLT_MAX : FLT_MAX;
+  int cnt = 0;
+  uint2 *slot = cbuf + (w * kCand) * 64 + l;
+  auto flush = [&]() {
+#pragma unroll 1
+    for (int j = 0; j < kCand; ++j) {
+      const uint2 e = slot[64 * j];
+      top.insert(j < cnt ? __uint_as_float(e.x) : -FLT_MAX, (int)e.y);
+    }
+    cnt = 0;
+    thr = qvalid ? top.v[kTop - 1] : FLT_MAX;
+  };
+
+  load_tile(0);
+  __syncthreads();                     // pair table ready
+  decode_tile(0);
+  load_tile(32);
+  __syncthreads();
+  int buf = 0;
+  for (int t0 = 0; t0 < n_keys; t0 += 32, buf ^= 1) {
+    decode_tile(buf ^ 1);              // tile t0 + 32 (zeros past the end)
+    load_tile(t0 + 64);
+    if (wave_live) {
+      f32x16 acc = {};
+      const _Float16 *hb = &ch[buf][m * PITCH + 8 * h];
+      const _Float16 *lb = &cl[buf][m * PITCH + 8 * h];
 #pragma unroll
-      for (int p = 0; p < LB; ++p) pw[p] = *(const uint16_t *)(a.codes + key * (LB * PB) + 4 * ((c >> 1) * LB + p) + 2 * (c & 1));
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        uint32_t idx = 0;
-#pragma unroll
-        for (int p = 0; p < LB; ++p) idx |= ((pw[p] >> i) & 1u) << p;
-        const uint32_t e = ctab[idx];
-        const uint16_t hb = (uint16_t)(e & 0xFFFF), lb = (uint16_t)(e >> 16);
-        __builtin_memcpy(&ch[v * PITCH + 16 * c + i], &hb, 2);
-        __builtin_memcpy(&cl[v * PITCH + 16 * c + i], &lb, 2);
+      for (int s = 0; s < KS; ++s) {
+        const half8 ah = *(const half8 *)(hb + 16 * s);
+        const half8 al = *(const half8 *)(lb + 16 * s);
+        acc = mfma32(al, qh[s], acc);
+        acc = mfma32(ah, ql[s], acc);
+        acc = mfma32(ah, qh[s], acc);
       }
-      if (c == 0) kn[v] = valid ? f16_bits_to_f32(a.norm[key]) : 0.0f;
-    }
-    __syncthreads();
-    f32x16 acc = {};
+      // lane (m, h) holds query m and keys 8*(r/4) + 4*h + r%4 of the tile
+      const int nval = n_keys - t0;
+      float sc[16];
+      bool cd[16];
+      int nc = 0;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const half8 ah = *(const half8 *)&ch[m * PITCH + 16 * s + 8 * h];
-      const half8 al = *(const half8 *)&cl[m * PITCH + 16 * s + 8 * h];
-      acc = mfma32(al, qh[s], acc);
-      acc = mfma32(ah, ql[s], acc);
-      acc = mfma32(ah, qh[s], acc);
-    }
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 k4 = *(const f32x4 *)&kn[buf][8 * g + 4 * h];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int v = 8 * (r >> 2) + 4 * h + (r & 3);
-      const int64_t t = t0 + v;
-      const float sc = acc[r] * kn[v] * qf;
-      const int ki = (int)t;
-      const bool cand = t < k_end && better(sc, ki, tv[kTop - 1], ti[kTop - 1]);
-      if (cand) {
-        float nv[kTop];
-        int ni[kTop];
+        for (int j = 0; j < 4; ++j) {
+          const int r = 4 * g + j;
+          sc[r] = acc[r] * k4[j] * qf;
+          cd[r] = (8 * g + 4 * h + j < nval) && sc[r] > thr;
+          nc += cd[r] ? 1 : 0;
+        }
+      }
+      if (__ballot(nc > 0) != 0) {
+        if (__ballot(cnt + nc > kCand) != 0) {
+          flush();
+          nc = 0;
 #pragma unroll
-        for (int i = 0; i < kTop; ++i) {
-          const bool here = better(sc, ki, tv[i], ti[i]);
-          const bool prev = i > 0 && better(sc, ki, tv[i - 1], ti[i - 1]);
-          nv[i] = prev ? tv[i - 1] : (here ? sc : tv[i]);
-          ni[i] = prev ? ti[i - 1] : (here ? ki : ti[i]);
+          for (int r = 0; r < 16; ++r) {
+            cd[r] = cd[r] && sc[r] > thr;
+            nc += cd[r] ? 1 : 0;
+          }
         }
 #pragma unroll
-        for (int i = 0; i < kTop; ++i) { tv[i] = nv[i]; ti[i] = ni[i]; }
+        for (int r = 0; r < 16; ++r) {
+          if (cd[r]) {
+            const int key = (int)k_begin + t0 + 8 * (r >> 2) + 4 * h + (r & 3);
+            slot[64 * cnt] = make_uint2(__float_as_uint(sc[r]), (uint32_t)key);
+            ++cnt;
+          }
+        }
       }
     }
     __syncthreads();
   }
-  // merge the two half-wave lists of each query
+  if (wave_live && __ballot(cnt > 0) != 0) flush();
+  // merge the two half-wave lists of each query (slots are private per wave)
 #pragma unroll
-  for (int i = 0; i < kTop; ++i) {
-    mval[w][m][h][i] = tv[i];
-    midx[w][m][h][i] = ti[i];
-  }
+  for (int j = 0; j < kTop; ++j) slot[64 * j] = make_uint2(__float_as_uint(top.v[j]), (uint32_t)top.i[j]);
   __syncthreads();
   if (h == 0 && qvalid) {
+    const uint2 *la = cbuf + (w * kCand) * 64 + m;
+    const uint2 *lb = la + 32;
     int pa = 0, pb = 0;
     const int64_t qrow = (int64_t)stream * a.group + gq;
     float *outv = a.part_val + ((int64_t)split * a.n_rows + qrow) * kTop;
     int32_t *outi = a.part_idx + ((int64_t)split * a.n_rows + qrow) * kTop;
 #pragma unroll
     for (int i = 0; i < kTop; ++i) {
-      const float va = mval[w][m][0][pa], vb = mval[w][m][1][pb];
-      const int ia = midx[w][m][0][pa], ib = midx[w][m][1][pb];
-      if (better(va, ia, vb, ib)) { outv[i] = va; outi[i] = ia; ++pa; }
-      else { outv[i] = vb; outi[i] = ib; ++pb; }
+      const uint2 ea = la[64 * pa], eb = lb[64 * pb];
+      const float va = __uint_as_float(ea.x), vb = __uint_as_float(eb.x);
+      const bool ta = better(va, (int)ea.y, vb, (int)eb.y);
+      outv[i] = ta ? va : vb;
+      outi[i] = (int32_t)(ta ? ea.y : eb.y);
+      pa += ta ? 1 : 0;
+      pb += ta ? 0 : 1;
     }
   }
 }
@@ -274,16 +391,27 @@ hipError_t launch_t(const tqi::SearchArgs &sa, hipStream_t s) {
   const int group = a.n_q_heads / a.n_kv_heads;
   const int64_t n_streams = (int64_t)a.batch * a.n_kv_heads;
   const int64_t n_queries = (int64_t)a.batch * a.n_q_heads;
-  const int q_tiles = (group + 127) / 128;
+  const int q_tiles = (group + kSearchQueries - 1) / kSearchQueries;
   const int64_t base_blocks = n_streams * q_tiles;
-  int64_t splits = (4LL * tqi::device_cu_count() + base_blocks - 1) / base_blocks;
-  const int64_t max_splits = (a.seq_len + 1023) / 1024;
-  if (splits > max_splits) splits = max_splits;
-  if (splits > 64) splits = 64;
-  if (splits < 1) splits = 1;
+  // Split the keys so that the workgroups fill the chip in whole rounds: the
+  // cost of a split count is (rounds of resident workgroups) x (tiles per
+  // split + a fixed allowance for filling the lists).
+  const int64_t cus = tqi::device_cu_count();
+  const int64_t n_tiles = (a.seq_len + 31) / 32;
+  int64_t max_splits = (a.seq_len + 4095) / 4096;
+  if (max_splits > 64) max_splits = 64;
+  if (max_splits < 1) max_splits = 1;
+  int64_t splits = 1, best = -1;
+  for (int64_t sp = 1; sp <= max_splits; ++sp) {
+    const int64_t rounds = (base_blocks * sp + cus - 1) / cus;
+    const int64_t cost = rounds * ((n_tiles + sp - 1) / sp + 16);
+    if (best < 0 || cost < best) { best = cost; splits = sp; }
+  }
   int64_t kps = (a.seq_len + splits - 1) / splits;
   kps = (kps + 31) / 32 * 32;
   splits = (a.seq_len + kps - 1) / kps;
+  // Per-split byte offsets of the packed codes stay below 2^31.
+  if ((kps + 64) * (int64_t)(LB * D / 8) >= (1LL << 31)) return hipErrorInvalidValue;
   const int64_t n_rows = n_streams * group;
   const size_t qbytes = (size_t)n_queries * D * sizeof(_Float16);
   const size_t bytes = 2 * qbytes + (size_t)n_queries * sizeof(float) +
@@ -323,7 +451,7 @@ hipError_t launch_t(const tqi::SearchArgs &sa, hipStream_t s) {
     sc.scale = a.scale;
     sc.part_val = pv;
     sc.part_idx = pi;
-    hipLaunchKernelGGL((search_score_kernel<D, LB>), dim3((unsigned)(base_blocks * splits)), dim3(256),
+    hipLaunchKernelGGL((search_score_kernel<D, LB>), dim3((unsigned)(base_blocks * splits)), dim3(kSearchThreads),
                        0, s, sc);
     e = hipGetLastError();
   }
