@@ -28,7 +28,8 @@ namespace {
 using namespace tqd;
 
 constexpr int kTop = 16;               // list length kept per lane (topk <= 16)
-constexpr int kCand = 16;              // candidate slots per lane between list updates
+constexpr int kCand = 8;               // candidate slots per lane between list updates
+constexpr int kEmptyKey = 0x3FFFFFFF;  // key index of an empty list entry (score -FLT_MAX)
 constexpr int kSearchThreads = 512;    // 8 waves
 constexpr int kSearchQueries = 32 * (kSearchThreads / 64);   // queries per workgroup
 constexpr float kCenScale = 1024.0f;
@@ -97,28 +98,31 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
-// Sorted (descending) running list of one lane.  Entries arrive in increasing
-// key order, so an equal score never displaces an entry already present.
-struct TopList {
-  float v[kTop];
-  int i[kTop];
-  __device__ __forceinline__ void init() {
+// A list entry (score s, key index i < 2^30) packed into one 64-bit word
+// whose unsigned order is the list order: higher score first, then the
+// smaller index.  The top two bits are clear and the exponent field is never
+// all ones or zero for finite or infinite scores, so the word read as an fp64
+// value is a positive normal number and fp64 max/min order it the same way.
+__device__ __forceinline__ double pack_entry(float s, int i) {
+  const uint32_t b = __float_as_uint(s + 0.0f);      // -0 -> +0: equal scores tie on the index
+  const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  const uint64_t w = ((uint64_t)ord << 30) | (uint64_t)(0x3FFFFFFFu - ((uint32_t)i & 0x3FFFFFFFu));
+  return __longlong_as_double((long long)w);
+}
+
+__device__ __forceinline__ void unpack_entry(double e, float &s, int &i) {
+  const uint64_t w = (uint64_t)__double_as_longlong(e);
+  const uint32_t ord = (uint32_t)(w >> 30);
+  s = __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+  i = (int)(0x3FFFFFFFu - ((uint32_t)w & 0x3FFFFFFFu));
+}
+
+// Insert x into a descending list of packed entries (branch-free).
+__device__ __forceinline__ void list_insert(double (&e)[kTop], double x) {
 #pragma unroll
-    for (int j = 0; j < kTop; ++j) { v[j] = -FLT_MAX; i[j] = 0x7FFFFFFF; }
-  }
-  __device__ __forceinline__ void insert(float x, int xi) {
-    bool c[kTop];
-#pragma unroll
-    for (int j = 0; j < kTop; ++j) c[j] = x > v[j];
-#pragma unroll
-    for (int j = kTop - 1; j > 0; --j) {
-      v[j] = c[j - 1] ? v[j - 1] : (c[j] ? x : v[j]);
-      i[j] = c[j - 1] ? i[j - 1] : (c[j] ? xi : i[j]);
-    }
-    v[0] = c[0] ? x : v[0];
-    i[0] = c[0] ? xi : i[0];
-  }
-};
+  for (int j = kTop - 1; j > 0; --j) e[j] = fmax(e[j], fmin(x, e[j - 1]));
+  e[0] = fmax(e[0], x);
+}
 
 template <int D, int LB>
 struct SearchTile {
@@ -128,28 +132,46 @@ struct SearchTile {
   static constexpr int ROWB = LB * D / 8;  // packed bytes per key
 };
 
+// Spread the 2-bit groups of the low 2*NP bits of x to a 4-bit pitch.
+template <int NP>
+__device__ __forceinline__ uint32_t spread2(uint32_t x) {
+  if constexpr (NP == 8) {
+    x &= 0xFFFFu;
+    x = (x | (x << 8)) & 0x00FF00FFu;
+  } else {
+    x &= 0xFFu;
+  }
+  x = (x | (x << 4)) & 0x0F0F0F0Fu;
+  x = (x | (x << 2)) & 0x33333333u;
+  return x;
+}
+
 // Decode the coordinates [CPT*c, CPT*c + CPT) of one key from its bit-plane
-// words into fp16 hi and lo halves through the pair table.
+// words into fp16 hi and lo halves through the pair tables (hi table at
+// tab[0, K*K), lo table at tab[K*K, 2*K*K)).
 template <int D, int LB>
-__device__ __forceinline__ void decode_pairs(const uint32_t (&pw)[LB], int c, const uint2 *ptab,
+__device__ __forceinline__ void decode_pairs(const uint32_t (&pw)[LB], int c, const uint32_t *tab,
                                              _Float16 *hrow, _Float16 *lrow) {
   constexpr int CPT = SearchTile<D, LB>::CPT;
+  constexpr int NP = CPT / 2;
+  constexpr int KK = 1 << (2 * LB);
   const int boff = (CPT * c) & 31;
-  uint32_t u[LB];
+  // z01 (and z23) hold the pair index bits of planes 0-1 (2-3) at a 4-bit pitch
+  uint32_t z01 = spread2<NP>(pw[0] >> boff);
+  if constexpr (LB >= 2) z01 |= spread2<NP>(pw[1] >> boff) << 2;
+  uint32_t z23 = 0;
+  if constexpr (LB >= 3) z23 = spread2<NP>(pw[2] >> boff);
+  if constexpr (LB >= 4) z23 |= spread2<NP>(pw[3] >> boff) << 2;
+  uint32_t hw[NP], lw[NP];
 #pragma unroll
-  for (int p = 0; p < LB; ++p) u[p] = pw[p] >> boff;
-  uint32_t hw[CPT / 2], lw[CPT / 2];
-#pragma unroll
-  for (int k = 0; k < CPT / 2; ++k) {
-    uint32_t pidx = 0;
-#pragma unroll
-    for (int p = 0; p < LB; ++p) pidx |= ((u[p] >> (2 * k)) & 3u) << (2 * p);
-    const uint2 e = ptab[pidx];
-    hw[k] = e.x;
-    lw[k] = e.y;
+  for (int k = 0; k < NP; ++k) {
+    uint32_t pidx = (z01 >> (4 * k)) & 15u;
+    if constexpr (LB >= 3) pidx |= ((z23 >> (4 * k)) & 15u) << 4;
+    hw[k] = tab[pidx];
+    lw[k] = tab[KK + pidx];
   }
 #pragma unroll
-  for (int k = 0; k < CPT / 2; k += 4) {
+  for (int k = 0; k < NP; k += 4) {
     *(uint4 *)(hrow + 2 * k) = make_uint4(hw[k], hw[k + 1], hw[k + 2], hw[k + 3]);
     *(uint4 *)(lrow + 2 * k) = make_uint4(lw[k], lw[k + 1], lw[k + 2], lw[k + 3]);
   }
@@ -164,13 +186,17 @@ __global__ __launch_bounds__(kSearchThreads) void search_score_kernel(ScoreArgs 
   constexpr int CPT = T::CPT;
   constexpr int ROWB = T::ROWB;
   constexpr int NW = kSearchThreads / 64;
-  __shared__ __attribute__((aligned(16))) _Float16 ch[2][32 * PITCH];
-  __shared__ __attribute__((aligned(16))) _Float16 cl[2][32 * PITCH];
-  __shared__ __attribute__((aligned(16))) float kn[2][32];
-  __shared__ uint2 ptab[K * K];
-  // Per-lane candidate slots, lane-minor so a row of slots is one 512-byte
-  // line per wave; reused for the final half-list merge.
-  __shared__ uint2 cbuf[NW * kCand * 64];
+  __shared__ uint32_t ptab[2 * K * K];
+  __shared__ __attribute__((aligned(16))) float kn0[32], kn1[32];
+  // Two statically distinct tile buffers, so that the decode of the next
+  // tile can be interleaved with the products on the current one.
+  __shared__ __attribute__((aligned(16))) _Float16 ch0[32 * PITCH], ch1[32 * PITCH];
+  __shared__ __attribute__((aligned(16))) _Float16 cl0[32 * PITCH], cl1[32 * PITCH];
+  // Per query (32 per wave): one sorted list of kTop packed entries, shared
+  // by the two half-wave lanes that hold the query's scores, and kCand
+  // candidate slots per lane; query-minor, so a row is one line per wave.
+  __shared__ double qlist[NW * kTop * 32];
+  __shared__ double qslot[NW * 2 * kCand * 32];
 
   const int split = blockIdx.x % a.n_splits;
   const int rest = blockIdx.x / a.n_splits;
@@ -184,32 +210,35 @@ __global__ __launch_bounds__(kSearchThreads) void search_score_kernel(ScoreArgs 
   const int m = l & 31;
   const int h = l >> 5;
 
-  const int gq0 = qt * kSearchQueries + 32 * w;          // first query of this wave
-  const bool wave_live = gq0 < a.group;
-  const int gq = gq0 + m;
+  const int gq = qt * kSearchQueries + 32 * w + m;      // query within the GQA group
   const bool qvalid = gq < a.group;
   const int64_t qglob = (int64_t)b * a.n_q_heads + (int64_t)kvh * a.group + (qvalid ? gq : 0);
+  // A negative scale reverses the order: the query is negated instead, which
+  // is exact, and |scale| applied afterwards.
+  const uint32_t qsign = a.scale < 0.0f ? 0x80008000u : 0u;
   half8 qh[KS], ql[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
+    i32x4 vh = {}, vl = {};
     if (qvalid) {
-      qh[s] = *(const half8 *)(a.qh + qglob * D + 16 * s + 8 * h);
-      ql[s] = *(const half8 *)(a.ql + qglob * D + 16 * s + 8 * h);
-    } else {
-      qh[s] = half8{};
-      ql[s] = half8{};
+      vh = *(const i32x4 *)(a.qh + qglob * D + 16 * s + 8 * h);
+      vl = *(const i32x4 *)(a.ql + qglob * D + 16 * s + 8 * h);
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { vh[j] ^= (int)qsign; vl[j] ^= (int)qsign; }
+    __builtin_memcpy(&qh[s], &vh, 16);
+    __builtin_memcpy(&ql[s], &vl, 16);
   }
-  const float qf = qvalid ? a.qfac[qglob] * a.scale : 0.0f;
+  const float qf = qvalid ? a.qfac[qglob] * fabsf(a.scale) : 0.0f;
 
-  // pair table: bits 2p and 2p+1 of the entry index are plane p of the even
-  // and of the odd coordinate of a pair
-  if (tid < K * K) {
+  // pair tables: bits 2p and 2p+1 of the entry index are plane p of the even
+  // and of the odd coordinate of a pair; hi halves, then lo halves
+  for (int e = tid; e < K * K; e += kSearchThreads) {
     uint32_t i0 = 0, i1 = 0;
 #pragma unroll
     for (int p = 0; p < LB; ++p) {
-      i0 |= ((tid >> (2 * p)) & 1u) << p;
-      i1 |= ((tid >> (2 * p + 1)) & 1u) << p;
+      i0 |= ((e >> (2 * p)) & 1u) << p;
+      i1 |= ((e >> (2 * p + 1)) & 1u) << p;
     }
     uint32_t hw = 0, lw = 0;
 #pragma unroll
@@ -223,7 +252,8 @@ __global__ __launch_bounds__(kSearchThreads) void search_score_kernel(ScoreArgs 
       hw |= (uint32_t)hb << (16 * j);
       lw |= (uint32_t)lb << (16 * j);
     }
-    ptab[tid] = make_uint2(hw, lw);
+    ptab[e] = hw;
+    ptab[K * K + e] = lw;
   }
 
   const int64_t k_begin = (int64_t)split * a.keys_per_split;
@@ -241,110 +271,158 @@ __global__ __launch_bounds__(kSearchThreads) void search_score_kernel(ScoreArgs 
   const uint32_t code_off = (uint32_t)dv * ROWB + 4u * LB * (uint32_t)((CPT * dc) >> 5);
   uint32_t pw[LB];
   uint16_t nb = 0;
-  auto load_tile = [&](int t0) {
+  auto load_tile = [&](int t0) __attribute__((always_inline)) {
     buf_load_words<LB, 0>(rcode, (uint32_t)t0 * ROWB + code_off, pw);
-    if (dc == 0) nb = buf_load_u16<0>(rnrm, 2u * (uint32_t)(t0 + dv));
+    nb = buf_load_u16<0>(rnrm, 2u * (uint32_t)(t0 + dv));
   };
-  auto decode_tile = [&](int buf) {
-    decode_pairs<D, LB>(pw, dc, ptab, &ch[buf][dv * PITCH + CPT * dc], &cl[buf][dv * PITCH + CPT * dc]);
-    if (dc == 0) kn[buf][dv] = f16_bits_to_f32(nb);
+  // Branch-free, so that the decode can be interleaved with the products.  A
+  // key past the end gets a NaN norm, so none of its scores passes a test.
+  auto decode_tile = [&](int t0, _Float16 *dh, _Float16 *dl, float *dn) __attribute__((always_inline)) {
+    decode_pairs<D, LB>(pw, dc, ptab, dh + dv * PITCH + CPT * dc, dl + dv * PITCH + CPT * dc);
+    dn[dv] = t0 + dv < n_keys ? f16_bits_to_f32(nb) : __builtin_nanf("");   // same value from 16 lanes
   };
 
-  TopList top;
-  top.init();
+  // A score s = (acc * norm) * qf enters the query's list only if s > thr,
+  // the list's current 16th best.  The products are first tested against
+  // thq, a bound a little below thr / qf, so the exact test runs only on the
+  // few that pass.  qf == 0 (invalid lane or zero scale) gives -inf or NaN:
+  // all scores tie at zero and the first keys stay, as the order requires.
+  double *lq = qlist + (w * kTop) * 32 + m;
+  double *sq = qslot + ((w * 2 + h) * kCand) * 32 + m;
+  {
+    const double empty = pack_entry(-FLT_MAX, kEmptyKey);
+#pragma unroll
+    for (int j = 0; j < kTop; ++j) lq[32 * j] = empty;     // both half-lanes store the same
+  }
   float thr = qvalid ? -FLT_MAX : FLT_MAX;
+  float thq = -INFINITY;
   int cnt = 0;
-  uint2 *slot = cbuf + (w * kCand) * 64 + l;
-  auto flush = [&]() {
-#pragma unroll 1
-    for (int j = 0; j < kCand; ++j) {
-      const uint2 e = slot[64 * j];
-      top.insert(j < cnt ? __uint_as_float(e.x) : -FLT_MAX, (int)e.y);
-    }
-    cnt = 0;
-    thr = qvalid ? top.v[kTop - 1] : FLT_MAX;
+  auto set_bound = [&]() __attribute__((always_inline)) {
+    const float t = thr / qf;
+    thq = t - fabsf(t) * 0x1p-20f;
   };
-
-  load_tile(0);
-  __syncthreads();                     // pair table ready
-  decode_tile(0);
-  load_tile(32);
-  __syncthreads();
-  int buf = 0;
-  for (int t0 = 0; t0 < n_keys; t0 += 32, buf ^= 1) {
-    decode_tile(buf ^ 1);              // tile t0 + 32 (zeros past the end)
-    load_tile(t0 + 64);
-    if (wave_live) {
-      f32x16 acc = {};
-      const _Float16 *hb = &ch[buf][m * PITCH + 8 * h];
-      const _Float16 *lb = &cl[buf][m * PITCH + 8 * h];
+  set_bound();
+  // Both half-lanes of a query merge the slots of both into the shared list
+  // (the same work on the same data) and store the same result.
+  auto flush = [&]() __attribute__((always_inline)) {
+    const int cnt_o = __shfl_xor(cnt, 32);
+    double e[kTop];
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const half8 ah = *(const half8 *)(hb + 16 * s);
-        const half8 al = *(const half8 *)(lb + 16 * s);
-        acc = mfma32(al, qh[s], acc);
-        acc = mfma32(ah, ql[s], acc);
-        acc = mfma32(ah, qh[s], acc);
+    for (int j = 0; j < kTop; ++j) e[j] = lq[32 * j];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int ch = hh == h ? cnt : cnt_o;
+      const double *src_s = qslot + ((w * 2 + hh) * kCand) * 32 + m;
+#pragma unroll 1
+      for (int s = 0; s < kCand; ++s)
+        if (s < ch) list_insert(e, src_s[32 * s]);
+    }
+#pragma unroll
+    for (int j = 0; j < kTop; ++j) lq[32 * j] = e[j];
+    cnt = 0;
+    float t;
+    int ix;
+    unpack_entry(e[kTop - 1], t, ix);
+    thr = qvalid ? t : FLT_MAX;
+    set_bound();
+  };
+  // products on a tile held in (sh, sl)
+  auto products = [&](const _Float16 *sh, const _Float16 *sl) __attribute__((always_inline)) {
+    f32x16 acc = {};
+    const _Float16 *hb = sh + m * PITCH + 8 * h;
+    const _Float16 *lb = sl + m * PITCH + 8 * h;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const half8 ah = *(const half8 *)(hb + 16 * s);
+      const half8 al = *(const half8 *)(lb + 16 * s);
+      acc = mfma32(al, qh[s], acc);
+      acc = mfma32(ah, ql[s], acc);
+      acc = mfma32(ah, qh[s], acc);
+    }
+    return acc;
+  };
+  // selection on tile t0; lane (m, h) holds query m and keys
+  // 8*(r/4) + 4*h + r%4 of the tile
+  const int h4 = 4 * h;
+  auto select = [&](const f32x16 &acc, int t0, const float *sn) __attribute__((always_inline)) {
+    float pr[16];
+    uint64_t rm[16];      // per row: lanes whose product passes the bound
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 k4 = *(const f32x4 *)&sn[8 * g + h4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        pr[4 * g + j] = acc[4 * g + j] * k4[j];
+        rm[4 * g + j] = __ballot(pr[4 * g + j] > thq);
       }
-      // lane (m, h) holds query m and keys 8*(r/4) + 4*h + r%4 of the tile
-      const int nval = n_keys - t0;
-      float sc[16];
-      bool cd[16];
-      int nc = 0;
+    }
+    // Few rows have candidates once the lists are warm: rows are skipped on
+    // their (scalar) masks, and room is made per half of 8 rows (kCand >= 8).
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 k4 = *(const f32x4 *)&kn[buf][8 * g + 4 * h];
+    for (int half = 0; half < 2; ++half) {
+      uint64_t hm = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = 4 * g + j;
-          sc[r] = acc[r] * k4[j] * qf;
-          cd[r] = (8 * g + 4 * h + j < nval) && sc[r] > thr;
-          nc += cd[r] ? 1 : 0;
-        }
-      }
-      if (__ballot(nc > 0) != 0) {
-        if (__ballot(cnt + nc > kCand) != 0) {
-          flush();
-          nc = 0;
+      for (int r = 8 * half; r < 8 * half + 8; ++r) hm |= rm[r];
+      if (hm != 0) {
+        int nc = 0;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            cd[r] = cd[r] && sc[r] > thr;
-            nc += cd[r] ? 1 : 0;
-          }
-        }
+        for (int r = 8 * half; r < 8 * half + 8; ++r)
+          nc += __builtin_amdgcn_inverse_ballot_w64(rm[r]) ? 1 : 0;
+        if (__ballot(cnt + nc > kCand) != 0) flush();
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (cd[r]) {
-            const int key = (int)k_begin + t0 + 8 * (r >> 2) + 4 * h + (r & 3);
-            slot[64 * cnt] = make_uint2(__float_as_uint(sc[r]), (uint32_t)key);
+        for (int r = 8 * half; r < 8 * half + 8; ++r) {
+          if (rm[r] != 0 && __builtin_amdgcn_inverse_ballot_w64(rm[r])) {
+            const int kb = __builtin_amdgcn_readfirstlane((int)k_begin + t0 + 8 * (r >> 2) + (r & 3));
+            sq[32 * cnt] = pack_entry(pr[r] * qf, kb + h4);
             ++cnt;
           }
         }
       }
     }
+  };
+  // The two waves that share a SIMD (w and w + 4 when waves are dealt round
+  // robin, 2k and 2k + 1 when dealt in pairs) take the decode and the
+  // products in opposite orders, so that one decodes while the other keeps
+  // the matrix core busy.
+  const bool decode_first = ((w ^ (w >> 2)) & 1) == 0;
+  auto step = [&](int t0, const _Float16 *sh, const _Float16 *sl, const float *sn, _Float16 *dh,
+                  _Float16 *dl, float *dn) __attribute__((always_inline)) {
+    f32x16 acc;
+    if (decode_first) {
+      decode_tile(t0 + 32, dh, dl, dn);
+      load_tile(t0 + 64);
+      acc = products(sh, sl);
+    } else {
+      acc = products(sh, sl);
+      decode_tile(t0 + 32, dh, dl, dn);
+      load_tile(t0 + 64);
+    }
+    select(acc, t0, sn);
     __syncthreads();
-  }
-  if (wave_live && __ballot(cnt > 0) != 0) flush();
-  // merge the two half-wave lists of each query (slots are private per wave)
-#pragma unroll
-  for (int j = 0; j < kTop; ++j) slot[64 * j] = make_uint2(__float_as_uint(top.v[j]), (uint32_t)top.i[j]);
+  };
+
+  load_tile(0);
+  __syncthreads();                     // pair table ready
+  decode_tile(0, ch0, cl0, kn0);
+  load_tile(32);
   __syncthreads();
+  for (int t0 = 0; t0 < n_keys; t0 += 64) {
+    step(t0, ch0, cl0, kn0, ch1, cl1, kn1);     // tile t0 in buffer 0, decode t0 + 32 into 1
+    if (t0 + 32 >= n_keys) break;
+    step(t0 + 32, ch1, cl1, kn1, ch0, cl0, kn0);
+  }
+  if (__ballot(cnt > 0) != 0) flush();
   if (h == 0 && qvalid) {
-    const uint2 *la = cbuf + (w * kCand) * 64 + m;
-    const uint2 *lb = la + 32;
-    int pa = 0, pb = 0;
     const int64_t qrow = (int64_t)stream * a.group + gq;
     float *outv = a.part_val + ((int64_t)split * a.n_rows + qrow) * kTop;
     int32_t *outi = a.part_idx + ((int64_t)split * a.n_rows + qrow) * kTop;
 #pragma unroll
-    for (int i = 0; i < kTop; ++i) {
-      const uint2 ea = la[64 * pa], eb = lb[64 * pb];
-      const float va = __uint_as_float(ea.x), vb = __uint_as_float(eb.x);
-      const bool ta = better(va, (int)ea.y, vb, (int)eb.y);
-      outv[i] = ta ? va : vb;
-      outi[i] = (int32_t)(ta ? ea.y : eb.y);
-      pa += ta ? 1 : 0;
-      pb += ta ? 0 : 1;
+    for (int j = 0; j < kTop; ++j) {
+      float s;
+      int ix;
+      unpack_entry(lq[32 * j], s, ix);
+      outv[j] = s;
+      outi[j] = ix;
     }
   }
 }
@@ -410,7 +488,9 @@ hipError_t launch_t(const tqi::SearchArgs &sa, hipStream_t s) {
   int64_t kps = (a.seq_len + splits - 1) / splits;
   kps = (kps + 31) / 32 * 32;
   splits = (a.seq_len + kps - 1) / kps;
-  // Per-split byte offsets of the packed codes stay below 2^31.
+  // Key indices fit the packed list entries (30 bits); per-split byte offsets
+  // of the packed codes stay below 2^31.
+  if (a.seq_len >= (1LL << 30)) return hipErrorInvalidValue;
   if ((kps + 64) * (int64_t)(LB * D / 8) >= (1LL << 31)) return hipErrorInvalidValue;
   const int64_t n_rows = n_streams * group;
   const size_t qbytes = (size_t)n_queries * D * sizeof(_Float16);

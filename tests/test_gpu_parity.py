@@ -201,6 +201,54 @@ def test_search_parity(tq, bits):
             assert abs(scores[r, i] - ov[r, -1]) <= tol, (r, i)
 
 
+@pytest.mark.parametrize("scale", [1.0, -0.5, 0.0])
+def test_search_ties_zeros_and_scale(tq, scale):
+    """Exact ties (duplicated database rows), zero rows, a zero query, and a
+    negative or zero scale (d = 128, 3 bits, several key tiles and splits).
+
+    Duplicated rows have identical codes, so their scores tie exactly on both
+    sides and the smaller index must win; with scale 0 (or a zero query)
+    every score is 0 and the top-k are the first k keys."""
+    d, bits, k = 128, 3, 16
+    rng = np.random.default_rng(11)
+    base = rng.standard_normal((700, d))
+    db = base[rng.integers(0, 700, 9000)]               # every vector about 13 times
+    db[[5, 77, 4000]] = 0.0
+    n_db = db.shape[0]
+    qv = rng.standard_normal((37, d))
+    qv[4] = 0.0
+    ot = OracleTables(d, bits, oqz.MODE_MSE)
+    ref = ot.quantize(db)
+    qz = tq.Quantizer(d, bits, oqz.MODE_MSE, seed=0, device=DEV)
+    cache = cache_from_oracle(tq, ref, d, bits, oqz.MODE_MSE, DEV)
+    qt = torch.from_numpy(qv.astype(np.float32).reshape(1, -1, d)).to(DEV)
+    vals, idx = qz.search(qt, cache, n_kv_heads=1, seq_len=n_db, topk=k, scale=scale)
+    vals, idx = vals.cpu().numpy()[0], idx.cpu().numpy()[0]
+    scores = oqz.logits_rotated(qv.astype(np.float32).astype(np.float64), ref["codes"], ref["norm"],
+                                ot.pi, ot.c, oqz.MODE_MSE, scale)
+    ov, oi = oqz.topk(scores, k)
+    # groups of identical packed rows (same codes and norm -> same score)
+    rows = np.concatenate([ref["codes"].view(np.uint8).reshape(n_db, -1),
+                           ref["norm"].view(np.uint8).reshape(n_db, -1)], axis=1)
+    _, group = np.unique(rows, axis=0, return_inverse=True)
+    group = group.reshape(-1)
+    for r in range(qv.shape[0]):
+        assert len(set(idx[r].tolist())) == k
+        got = scores[r, idx[r]]
+        assert np.all(np.abs(vals[r] - got) <= 1e-4 * np.maximum(np.abs(got), 1e-3)), r
+        if scale == 0.0 or r == 4:
+            assert idx[r].tolist() == list(range(k)), (r, idx[r])
+            continue
+        tol = 1e-4 * max(abs(ov[r, -1]), 1e-3)
+        for i in set(idx[r].tolist()) ^ set(oi[r].tolist()):
+            assert abs(scores[r, i] - ov[r, -1]) <= tol, (r, i)
+        # among exact duplicates, the smaller indices are taken first
+        chosen = set(idx[r].tolist())
+        for i in idx[r]:
+            same = np.nonzero(group == group[i])[0]
+            assert all(j in chosen for j in same[same < i]), (r, i)
+
+
 def test_end_to_end_quantize_then_logits(tq):
     """GPU quantise -> GPU logits vs oracle quantise -> oracle logits (keys with identical codes)."""
     d, bits, seq, group = 128, 3, 2000, 4
