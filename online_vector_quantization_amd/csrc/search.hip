@@ -88,9 +88,9 @@ struct ScoreArgs {
   const uint8_t *codes;
   const uint16_t *norm;
   int64_t row_tokens, seq_len, keys_per_split, n_rows;
-  int n_splits, q_tiles, n_kv_heads, n_q_heads, group;
+  int n_splits, q_tiles, n_kv_heads, n_q_heads, group, topk;
   float scale;
-  float *part_val;    // [split][query][kTop]
+  float *part_val;    // [split][query][kTop]; the first topk of each list are exact
   int32_t *part_idx;
 };
 
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(kSearchThreads) void search_score_kernel(ScoreArgs 
   constexpr int ROWB = T::ROWB;
   constexpr int NW = kSearchThreads / 64;
   __shared__ uint32_t ptab[2 * K * K];
-  __shared__ __attribute__((aligned(16))) float kn0[32], kn1[32];
+  __shared__ __attribute__((aligned(16))) float kn[3][32];   // norms of tiles t, t+1, t+2 (mod 3)
   // Two statically distinct tile buffers, so that the decode of the next
   // tile can be interleaved with the products on the current one.
   __shared__ __attribute__((aligned(16))) _Float16 ch0[32 * PITCH], ch1[32 * PITCH];
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(kSearchThreads) void search_score_kernel(ScoreArgs 
   };
 
   // A score s = (acc * norm) * qf enters the query's list only if s > thr,
-  // the list's current 16th best.  The products are first tested against
+  // the list's current topk-th best.  The products are first tested against
   // thq, a bound a little below thr / qf, so the exact test runs only on the
   // few that pass.  qf == 0 (invalid lane or zero scale) gives -inf or NaN:
   // all scores tie at zero and the first keys stay, as the order requires.
@@ -320,9 +320,10 @@ __global__ __launch_bounds__(kSearchThreads) void search_score_kernel(ScoreArgs 
 #pragma unroll
     for (int j = 0; j < kTop; ++j) lq[32 * j] = e[j];
     cnt = 0;
+    // The bound is the topk-th best: the merge reads no further down a list.
     float t;
     int ix;
-    unpack_entry(e[kTop - 1], t, ix);
+    unpack_entry(lq[32 * (a.topk - 1)], t, ix);
     thr = qvalid ? t : FLT_MAX;
     set_bound();
   };
@@ -356,61 +357,72 @@ __global__ __launch_bounds__(kSearchThreads) void search_score_kernel(ScoreArgs 
         rm[4 * g + j] = __ballot(pr[4 * g + j] > thq);
       }
     }
-    // Few rows have candidates once the lists are warm: rows are skipped on
-    // their (scalar) masks, and room is made per half of 8 rows (kCand >= 8).
+    // Few rows have candidates once the lists are warm: a scalar loop visits
+    // only rows with a passing lane, and room is made before each append.
+    uint64_t any = 0;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      uint64_t hm = 0;
+    for (int r = 0; r < 16; ++r) any |= rm[r];
+    if (any != 0) {
+      uint32_t act = 0;
 #pragma unroll
-      for (int r = 8 * half; r < 8 * half + 8; ++r) hm |= rm[r];
-      if (hm != 0) {
-        int nc = 0;
-#pragma unroll
-        for (int r = 8 * half; r < 8 * half + 8; ++r)
-          nc += __builtin_amdgcn_inverse_ballot_w64(rm[r]) ? 1 : 0;
-        if (__ballot(cnt + nc > kCand) != 0) flush();
-#pragma unroll
-        for (int r = 8 * half; r < 8 * half + 8; ++r) {
-          if (rm[r] != 0 && __builtin_amdgcn_inverse_ballot_w64(rm[r])) {
-            const int kb = __builtin_amdgcn_readfirstlane((int)k_begin + t0 + 8 * (r >> 2) + (r & 3));
-            sq[32 * cnt] = pack_entry(pr[r] * qf, kb + h4);
-            ++cnt;
-          }
+      for (int r = 0; r < 16; ++r) act |= (rm[r] != 0 ? 1u : 0u) << r;
+      while (act != 0) {
+        const int r = __builtin_ctz(act);
+        act &= act - 1;
+        if (__ballot(cnt >= kCand) != 0) flush();
+        const float v = pr[r];
+        if (v > thq) {
+          const int kb = (int)k_begin + t0 + 8 * (r >> 2) + (r & 3);
+          sq[32 * cnt] = pack_entry(v * qf, kb + h4);
+          ++cnt;
         }
       }
     }
   };
+
   // The two waves that share a SIMD (w and w + 4 when waves are dealt round
-  // robin, 2k and 2k + 1 when dealt in pairs) take the decode and the
-  // products in opposite orders, so that one decodes while the other keeps
-  // the matrix core busy.
-  const bool decode_first = ((w ^ (w >> 2)) & 1) == 0;
-  auto step = [&](int t0, const _Float16 *sh, const _Float16 *sl, const float *sn, _Float16 *dh,
-                  _Float16 *dl, float *dn) __attribute__((always_inline)) {
-    f32x16 acc;
-    if (decode_first) {
-      decode_tile(t0 + 32, dh, dl, dn);
+  // robin, 2k and 2k + 1 when dealt in pairs) split each tile period so that
+  // one runs its products while the other selects and decodes:
+  //   first wave:  products(t), select(t), decode(t + 1)
+  //   second wave: select(t - 1), decode(t + 1), products(t)
+  // with one barrier per tile.  Tile buffers alternate; norms rotate over
+  // three buffers, so the second wave's select(t - 1) never reads the norms
+  // that decode(t + 1) writes.
+  const bool mfma_first = ((w ^ (w >> 2)) & 1) == 0;
+  f32x16 pend = {};                    // second wave: products of the previous tile
+  auto step = [&](int t0, const _Float16 *sh, const _Float16 *sl, _Float16 *dh, _Float16 *dl)
+      __attribute__((always_inline)) {
+    const int ti = t0 >> 5;
+    float *kn_cur = kn[ti % 3];
+    float *kn_next = kn[(ti + 1) % 3];
+    if (mfma_first) {
+      const f32x16 acc = products(sh, sl);
+      select(acc, t0, kn_cur);
+      decode_tile(t0 + 32, dh, dl, kn_next);
       load_tile(t0 + 64);
-      acc = products(sh, sl);
     } else {
-      acc = products(sh, sl);
-      decode_tile(t0 + 32, dh, dl, dn);
+      if (t0 > 0) select(pend, t0 - 32, kn[(ti + 2) % 3]);
+      decode_tile(t0 + 32, dh, dl, kn_next);
       load_tile(t0 + 64);
+      pend = products(sh, sl);
     }
-    select(acc, t0, sn);
     __syncthreads();
   };
 
   load_tile(0);
   __syncthreads();                     // pair table ready
-  decode_tile(0, ch0, cl0, kn0);
+  decode_tile(0, ch0, cl0, kn[0]);
   load_tile(32);
   __syncthreads();
+  int t_last = 0;
   for (int t0 = 0; t0 < n_keys; t0 += 64) {
-    step(t0, ch0, cl0, kn0, ch1, cl1, kn1);     // tile t0 in buffer 0, decode t0 + 32 into 1
+    step(t0, ch0, cl0, ch1, cl1);      // tile t0 in buffer 0, decode t0 + 32 into 1
+    t_last = t0;
     if (t0 + 32 >= n_keys) break;
-    step(t0 + 32, ch1, cl1, kn1, ch0, cl0, kn0);
+    step(t0 + 32, ch1, cl1, ch0, cl0);
+    t_last = t0 + 32;
   }
+  if (!mfma_first && n_keys > 0) select(pend, t_last, kn[(t_last >> 5) % 3]);
   if (__ballot(cnt > 0) != 0) flush();
   if (h == 0 && qvalid) {
     const int64_t qrow = (int64_t)stream * a.group + gq;
@@ -529,6 +541,7 @@ hipError_t launch_t(const tqi::SearchArgs &sa, hipStream_t s) {
     sc.n_q_heads = a.n_q_heads;
     sc.group = group;
     sc.scale = a.scale;
+    sc.topk = sa.topk;
     sc.part_val = pv;
     sc.part_idx = pi;
     hipLaunchKernelGGL((search_score_kernel<D, LB>), dim3((unsigned)(base_blocks * splits)), dim3(kSearchThreads),
