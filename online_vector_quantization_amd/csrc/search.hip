@@ -44,40 +44,66 @@ struct QPrepArgs {
   float *qfac;        // [n_queries]: 1 / (query scale * centroid scale)
 };
 
+// One workgroup rotates kPrepQueries queries; thread j owns row j of Pi and
+// accumulates q'_j = sum_k Pi[j][k] q[k] for each of them in k order (fp64;
+// the products of fp32 values are exact).
+constexpr int kPrepQueries = 16;
+
 template <int D>
-__global__ __launch_bounds__(256) void search_prep_kernel(QPrepArgs a) {
-  __shared__ float qin[D];
-  __shared__ double qr[D];
-  __shared__ double red[256];
-  const int64_t qi = blockIdx.x;
-  const int tid = threadIdx.x;
-  for (int k = tid; k < D; k += 256)
-    qin[k] = a.q_f32 ? ((const float *)a.q)[qi * D + k] : bf16_to_f32(((const uint16_t *)a.q)[qi * D + k]);
+__global__ __launch_bounds__(D) void search_prep_kernel(QPrepArgs a) {
+  constexpr int QB = kPrepQueries;
+  __shared__ __attribute__((aligned(16))) float qin[QB][D];
+  __shared__ double red[QB][D / 64];
+  const int64_t q0 = (int64_t)blockIdx.x * QB;
+  const int j = threadIdx.x;
+  for (int i = j; i < QB * D; i += D) {
+    const int qi = i / D, k = i % D;
+    const int64_t g = q0 + qi;
+    float v = 0.0f;
+    if (g < a.n_queries)
+      v = a.q_f32 ? ((const float *)a.q)[g * D + k] : bf16_to_f32(((const uint16_t *)a.q)[g * D + k]);
+    qin[qi][k] = v;
+  }
   __syncthreads();
-  double mx = 0.0;
-  for (int j = tid; j < D; j += 256) {
-    const float *row = a.pi + (size_t)j * D;
-    double acc = 0.0;
-    for (int k = 0; k < D; ++k) acc += (double)row[k] * (double)qin[k];
-    qr[j] = acc;
-    mx = fmax(mx, fabs(acc));
+  double acc[QB];
+#pragma unroll
+  for (int qi = 0; qi < QB; ++qi) acc[qi] = 0.0;
+  const f32x4 *row = (const f32x4 *)(a.pi + (size_t)j * D);
+  for (int k4 = 0; k4 < D / 4; ++k4) {
+    const f32x4 p = row[k4];
+#pragma unroll
+    for (int qi = 0; qi < QB; ++qi) {
+      const f32x4 x = *(const f32x4 *)&qin[qi][4 * k4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[qi] = fma((double)p[c], (double)x[c], acc[qi]);
+    }
   }
-  red[tid] = mx;
+  // per query: largest |q'_j| over the rows
+  const int wv = j >> 6;
+#pragma unroll
+  for (int qi = 0; qi < QB; ++qi) {
+    double mx = fabs(acc[qi]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mx = fmax(mx, __shfl_xor(mx, off));
+    if ((j & 63) == 0) red[qi][wv] = mx;
+  }
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) red[tid] = fmax(red[tid], red[tid + s]);
-    __syncthreads();
+#pragma unroll
+  for (int qi = 0; qi < QB; ++qi) {
+    const int64_t g = q0 + qi;
+    if (g >= a.n_queries) break;
+    double mx = red[qi][0];
+#pragma unroll
+    for (int i = 1; i < D / 64; ++i) mx = fmax(mx, red[qi][i]);
+    int e = 0;
+    if (mx > 0.0) frexp(mx, &e);
+    const double sc = ldexp(1.0, 15 - e);   // largest |q'| lands in [2^14, 2^15)
+    const float v = (float)(acc[qi] * sc);
+    const _Float16 hv = (_Float16)v;
+    a.qh[g * D + j] = hv;
+    a.ql[g * D + j] = (_Float16)(v - (float)hv);
+    if (j == 0) a.qfac[g] = (float)(1.0 / (sc * (double)kCenScale));
   }
-  int e = 0;
-  if (red[0] > 0.0) frexp(red[0], &e);
-  const double sc = ldexp(1.0, 15 - e);   // largest |q'| lands in [2^14, 2^15)
-  for (int j = tid; j < D; j += 256) {
-    const float v = (float)(qr[j] * sc);
-    const _Float16 h = (_Float16)v;
-    a.qh[qi * D + j] = h;
-    a.ql[qi * D + j] = (_Float16)(v - (float)h);
-  }
-  if (tid == 0) a.qfac[qi] = (float)(1.0 / (sc * (double)kCenScale));
 }
 
 struct ScoreArgs {
@@ -448,30 +474,44 @@ struct MergeArgs {
   int32_t *out_idx;
 };
 
+// One wave per query: lane s holds the head of split s's sorted list, and
+// each output is the best head (wave butterfly; ties on the key index, then
+// on the split); the winning lane moves to its next entry.
 __global__ __launch_bounds__(256) void search_merge_kernel(MergeArgs a) {
-  const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = lane_id();
   if (row >= a.n_rows) return;
-  // Sorted lists per split; repeatedly take the best head (splits <= 64).
-  int pos[64];
-  for (int s = 0; s < a.n_splits; ++s) pos[s] = 0;
+  const bool has = lane < a.n_splits;
+  const int64_t base = ((int64_t)(has ? lane : 0) * a.n_rows + row) * kTop;
+  const float *pv = a.part_val + base;
+  const int32_t *pi = a.part_idx + base;
+  int pos = 0;
+  float hv = has ? pv[0] : -INFINITY;
+  int hi = has ? pi[0] : 0x7FFFFFFF;
   const int64_t stream = row / a.group;
   const int g = (int)(row % a.group);
   const int64_t b = stream / a.n_kv_heads;
   const int kvh = (int)(stream % a.n_kv_heads);
   const int64_t orow = b * a.n_q_heads + (int64_t)kvh * a.group + g;
   for (int i = 0; i < a.topk; ++i) {
-    int best = -1;
-    float bv = 0.0f;
-    int bi = 0;
-    for (int s = 0; s < a.n_splits; ++s) {
-      if (pos[s] >= kTop) continue;
-      const float v = a.part_val[((int64_t)s * a.n_rows + row) * kTop + pos[s]];
-      const int ix = a.part_idx[((int64_t)s * a.n_rows + row) * kTop + pos[s]];
-      if (best < 0 || better(v, ix, bv, bi)) { best = s; bv = v; bi = ix; }
+    float bv = hv;
+    int bi = hi, bl = lane;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      const int ol = __shfl_xor(bl, off);
+      if (better(ov, oi, bv, bi) || (ov == bv && oi == bi && ol < bl)) { bv = ov; bi = oi; bl = ol; }
     }
-    pos[best] += 1;
-    a.out_val[orow * a.topk + i] = bv;
-    a.out_idx[orow * a.topk + i] = bi;
+    if (lane == 0) {
+      a.out_val[orow * a.topk + i] = bv;
+      a.out_idx[orow * a.topk + i] = bi;
+    }
+    if (lane == bl) {
+      ++pos;
+      hv = pos < kTop ? pv[pos] : -INFINITY;
+      hi = pos < kTop ? pi[pos] : 0x7FFFFFFF;
+    }
   }
 }
 
@@ -521,7 +561,8 @@ hipError_t launch_t(const tqi::SearchArgs &sa, hipStream_t s) {
   pa.qfac = (float *)(ws + 2 * qbytes);
   float *pv = (float *)(ws + 2 * qbytes + ((n_queries * sizeof(float) + 255) / 256) * 256);
   int32_t *pi = (int32_t *)(pv + splits * n_rows * kTop);
-  hipLaunchKernelGGL((search_prep_kernel<D>), dim3((unsigned)n_queries), dim3(256), 0, s, pa);
+  hipLaunchKernelGGL((search_prep_kernel<D>), dim3((unsigned)((n_queries + kPrepQueries - 1) / kPrepQueries)),
+                     dim3(D), 0, s, pa);
   e = hipGetLastError();
   if (e == hipSuccess) {
     ScoreArgs sc;
@@ -560,7 +601,7 @@ hipError_t launch_t(const tqi::SearchArgs &sa, hipStream_t s) {
     ma.n_kv_heads = a.n_kv_heads;
     ma.out_val = a.logits;
     ma.out_idx = sa.topk_idx;
-    hipLaunchKernelGGL(search_merge_kernel, dim3((unsigned)((n_rows + 255) / 256)), dim3(256), 0, s, ma);
+    hipLaunchKernelGGL(search_merge_kernel, dim3((unsigned)((n_rows + 3) / 4)), dim3(256), 0, s, ma);
     e = hipGetLastError();
   }
   return e;
