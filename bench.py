@@ -135,7 +135,7 @@ def decode_workload(torch, tq, args, device):
     }
     rb_k, rb_v = bits * d // 8 + 4, bits * d // 8 + 2
     work = {  # algorithmic HBM bytes and flops per launch, main kernel, sources
-        "quantize_k": (n * (2 * d + rb_k), n * 4 * d * d, "quantize_kernel",
+        "quantize_k": (n * (2 * d + rb_k), n * 4 * d * d, "quantize_pc_kernel",
                        ["quantize.hip", "tq_device.h"]),
         "quantize_v": (n * (2 * d + rb_v), n * 2 * d * d, "quantize_kernel",
                        ["quantize.hip", "tq_device.h"]),
@@ -165,7 +165,7 @@ def prefill_workload(torch, tq, args, device):
         calls["quantize_k_b%d" % b] = lambda qk=qk, ck=ck: qk.quantize(k, out=ck)
         calls["quantize_v_b%d" % b] = lambda qv=qv, cv=cv: qv.quantize(v, out=cv)
         rb = b * d // 8
-        work["quantize_k_b%d" % b] = (n * (2 * d + rb + 4), n * 4 * d * d, "quantize_kernel", src)
+        work["quantize_k_b%d" % b] = (n * (2 * d + rb + 4), n * 4 * d * d, "quantize_pc_kernel", src)
         work["quantize_v_b%d" % b] = (n * (2 * d + rb + 2), n * 2 * d * d, "quantize_kernel", src)
     cfg = {"workload": "prefill quantisation: 65536 new bf16 tokens x 8 KV heads x 128; keys "
                        "inner-product and values MSE at b = 2, 3, 4 (six calls per step)",
