@@ -213,16 +213,27 @@ __device__ __forceinline__ void code_block(const f32x16 &acc, const float *vinv,
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const float u = acc[r] * inv[r];
+    // The codebook is antisymmetric (boundary K/2-1 is 0, boundary K/2-1-j
+    // is minus boundary K/2-1+j), so the cell is the sign s = (u >= 0) and
+    // the magnitude level lvl = #{j >= 1 : |u| >= t[K/2-1+j]}: idx = K/2 + lvl
+    // for s, K/2-1-lvl otherwise, i.e. the low LB-1 bits are lvl, inverted
+    // when u < 0 (u exactly on a negative boundary falls one cell higher
+    // than with the full thermometer; such values are within any rounding
+    // of the boundary).  K/2 compares instead of K-1.
+    constexpr int MID = K / 2;
+    const uint64_t sgn = __ballot(u >= 0.0f);
+    uint64_t g[MID > 1 ? MID - 1 : 1];   // g[j-1]: |u| >= t[MID-1+j]
+#pragma unroll
+    for (int j = 1; j < MID; ++j) g[j - 1] = __ballot(fabsf(u) >= bnd[MID - 1 + j]);
     uint64_t planes[LB];
+    planes[LB - 1] = sgn;
 #pragma unroll
-    for (int p = 0; p < LB; ++p) planes[p] = 0;
-    uint64_t ge[K - 1];   // thermometer masks: bit l = (u >= t_k) in lane l
+    for (int p = 0; p < LB - 1; ++p) {
+      uint64_t lp = 0;                  // bit p of the thermometer count
 #pragma unroll
-    for (int k = 0; k < K - 1; ++k) {
-      ge[k] = __ballot(u >= bnd[k]);
-#pragma unroll
-      for (int p = 0; p < LB; ++p)
-        if (((k + 1) & ((1 << p) - 1)) == 0) planes[p] ^= ge[k];
+      for (int j = 1; j < MID; ++j)
+        if ((j & ((1 << p) - 1)) == 0) lp ^= g[j - 1];   // multiples of 2^p
+      planes[p] = lp ^ ~sgn;
     }
 #pragma unroll
     for (int p = 0; p < LB; ++p) {
@@ -234,17 +245,11 @@ __device__ __forceinline__ void code_block(const f32x16 &acc, const float *vinv,
       }
     }
     if constexpr (PROD) {
-      // Centroid of the chosen cell from the thermometer masks, using the
-      // codebook's antisymmetry c[K/2-1-j] = -c[K/2+j]: pick the magnitude
-      // level j (idx >= K/2+j or idx <= K/2-1-j), then the sign
-      // (idx >= K/2  <=>  u >= t[K/2-1]); the mask logic stays on the scalar
-      // unit.
-      constexpr int MID = K / 2;
+      // centroid of the chosen cell: magnitude cen[MID + lvl], sign of u
       float mag = cen[MID];
 #pragma unroll
-      for (int j = 1; j < MID; ++j)
-        mag = __builtin_amdgcn_inverse_ballot_w64(ge[MID - 1 + j] | ~ge[MID - 1 - j]) ? cen[MID + j] : mag;
-      const float chat = __builtin_amdgcn_inverse_ballot_w64(ge[MID - 1]) ? mag : -mag;
+      for (int j = 1; j < MID; ++j) mag = __builtin_amdgcn_inverse_ballot_w64(g[j - 1]) ? cen[MID + j] : mag;
+      const float chat = __builtin_amdgcn_inverse_ballot_w64(sgn) ? mag : -mag;
       const int v = 8 * (r >> 2) + 4 * h + (r & 3);
       const float rs = (u - chat) * kResScale;
       const _Float16 hv = (_Float16)rs;
