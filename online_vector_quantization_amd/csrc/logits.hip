@@ -78,6 +78,15 @@ struct LLayout {
 template <int D>
 constexpr int prep_threads() { return 512; }
 
+// v from lane (lane ^ off): quad permutes (no LDS) within 4 lanes, the
+// LDS permute unit beyond.
+__device__ __forceinline__ float xor_lanes(float v, int off) {
+  const int b = __float_as_int(v);
+  if (off == 1) return __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0xB1, 0xF, 0xF, false));  // [1,0,3,2]
+  if (off == 2) return __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
+  return __shfl_xor(v, off, 64);
+}
+
 template <int D, int LB, bool PROD>
 __global__ __launch_bounds__(prep_threads<D>()) void logit_prep_kernel(PrepArgs a) {
   using L = LLayout<D, LB, PROD>;
@@ -89,9 +98,9 @@ __global__ __launch_bounds__(prep_threads<D>()) void logit_prep_kernel(PrepArgs 
   constexpr int NW = NT / 64;               // waves
   static_assert(RL >= 1 && RL <= 64 && NP >= 1, "prep layout");
   __shared__ __attribute__((aligned(16))) float qin[4][D];
-  __shared__ double proj[4][D];
+  __shared__ float proj[4][D];
   __shared__ double beta[P];
-  __shared__ double red_max[4][NW], red_sum[4][NW];
+  __shared__ float red_max[4][NW], red_sum[4][NW];
 
   const int stream = blockIdx.x;
   const int rt = blockIdx.y;
@@ -132,7 +141,9 @@ __global__ __launch_bounds__(prep_threads<D>()) void logit_prep_kernel(PrepArgs 
     beta[tid] = acc / K;
   }
   __syncthreads();
-  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  // fp32 accumulation: the products are exact and the sums' rounding
+  // (~1e-7 relative) is far below the logit tolerance.
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll (D <= 128 ? NP : 4)
   for (int i = 0; i < NP; ++i) {
     const int k0 = 4 * (pl + RL * i);
@@ -141,23 +152,23 @@ __global__ __launch_bounds__(prep_threads<D>()) void logit_prep_kernel(PrepArgs 
     for (int g = 0; g < 4; ++g) {
       const f32x4 qv = *(const f32x4 *)&qin[g][k0];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[g] = fma((double)m4[e], (double)qv[e], acc[g]);
+      for (int e = 0; e < 4; ++e) acc[g] = fmaf(m4[e], qv[e], acc[g]);
     }
   }
-  // full row sums in every lane of the row, then max |.| and sum over the
-  // rows of this wave
-  double mx[4], sm[4];
+  // full row sums in every lane of the row (quad permutes for the lanes of a
+  // row), then max |.| and sum over the rows of this wave
+  float mx[4], sm[4];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
 #pragma unroll
-    for (int off = 1; off < RL; off <<= 1) acc[g] += __shfl_xor(acc[g], off, 64);
+    for (int off = 1; off < RL; off <<= 1) acc[g] += xor_lanes(acc[g], off);
     if (pl == 0) proj[g][j] = acc[g];
-    mx[g] = fabs(acc[g]);
-    sm[g] = pl == 0 ? acc[g] : 0.0;
+    mx[g] = fabsf(acc[g]);
+    sm[g] = pl == 0 ? acc[g] : 0.0f;
 #pragma unroll
     for (int off = RL; off < 64; off <<= 1) {
-      mx[g] = fmax(mx[g], __shfl_xor(mx[g], off, 64));
-      sm[g] += __shfl_xor(sm[g], off, 64);
+      mx[g] = fmaxf(mx[g], xor_lanes(mx[g], off));
+      sm[g] += xor_lanes(sm[g], off);
     }
   }
   if ((tid & 63) == 0) {
@@ -170,9 +181,9 @@ __global__ __launch_bounds__(prep_threads<D>()) void logit_prep_kernel(PrepArgs 
   __syncthreads();
   // thread g < 4 folds the per-wave results of query g
   if (tid < 4) {
-    double mq = 0.0, sq = 0.0;
+    float mq = 0.0f, sq = 0.0f;
     for (int wv = 0; wv < NW; ++wv) {
-      mq = fmax(mq, red_max[tid][wv]);
+      mq = fmaxf(mq, red_max[tid][wv]);
       sq += red_sum[tid][wv];
     }
     red_max[tid][0] = mq;
@@ -231,7 +242,7 @@ __global__ __launch_bounds__(prep_threads<D>()) void logit_prep_kernel(PrepArgs 
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib) {
       const int j = 32 * (kg + 4 * q) + 8 * ib + 4 * hh + t;
-      int n = (int)rint(ldexp(wgt * proj[g][j], fexp[g] - s));
+      int n = (int)rint(ldexp(wgt * (double)proj[g][j], fexp[g] - s));
       if (s == 7) n = -n;
       if (!live) n = 0;
       // balanced signed-byte digits: n = sum_p digit_p 256^p, digit_p in [-128, 127]
