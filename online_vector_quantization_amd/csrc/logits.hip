@@ -6,8 +6,7 @@
 // reconstructing the keys:
 //   logit = scale * n * ( <Pi q, c[idx]> + sqrt(pi/2)/d * gamma * <S q, s> ).
 //
-// Reformulation used here (exact in real arithmetic, DESIGN.md "Logit
-// kernel"):
+// Reformulation used here (exact in real arithmetic):
 // * The Lloyd-Max codebook is antisymmetric (c[K-1-i] = -c[i]), so on the
 //   index bits b_0..b_{B-1} it is a sum of odd Walsh functions:
 //   c[idx] = sum_S beta_S (2 P_S - 1), S over the subsets of bit positions of

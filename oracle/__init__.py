@@ -30,8 +30,8 @@ Modules
              dequantise, attention logits, top-k search, recall.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against closed forms,
-textbook special cases, brute force or invariants.  Readings of points the
-page leaves open are listed in DESIGN.md ("Readings of the pages").
+textbook special cases, brute force or invariants.  Points the page leaves
+open are read as stated in each module's docstring.
 """
 
 from . import splitmix, rotation, codebook, quantizer  # noqa: F401

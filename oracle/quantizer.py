@@ -14,7 +14,7 @@ Page "TurboQuant 설명: 무엇인지와 LLM 메모리 6배 절약 구현 방법
 * "벤치마크 및 실제 성능" and "응용 분야 및 미래 영향": top-k inner-product search
   over a quantised database.
 
-Packed format (reading R4 in the design doc; the page fixes no layout):
+Packed format (a reading: the page fixes no layout):
 * MSE mode: b' = b Lloyd-Max bits per coordinate.  Inner-product ("prod")
   mode: b' = b - 1 Lloyd-Max bits plus one QJL sign bit per coordinate.
 * Every coordinate carries a b-bit record: bits 0..b'-1 hold its Lloyd-Max
@@ -34,7 +34,7 @@ Packed format (reading R4 in the design doc; the page fixes no layout):
 Reconstruction: x_hat = n16 * (Pi^T c_hat + kappa * gamma16 * S^T s) with
 s = 2 * bit - 1 and kappa = sqrt(pi/2) / m (m = d rows of S).  Because
 E[(s.q) sgn(s.r)] = sqrt(2/pi) <q, r> / ||r|| for s ~ N(0, I), the QJL term
-is an unbiased estimate of <q, r> (reading R6).  Logit: scale * <q, x_hat>.
+is an unbiased estimate of <q, r>.  Logit: scale * <q, x_hat>.
 """
 
 import math

@@ -6,7 +6,7 @@ from the QR factorisation of a Gaussian matrix.  Section "2단계: QJL 잔차
 보정": the residual is sketched with a Gaussian (Johnson-Lindenstrauss)
 projection and only the sign of each projected coordinate is kept.
 
-Readings (DESIGN.md, R1-R2):
+Readings:
 * Pi = Q diag(sign R_ii) with sign(0) = +1, where G = QR and G is the seeded
   Gaussian matrix of kind 0.  The sign fix makes Pi Haar distributed
   (F. Mezzadri, "How to generate random matrices from the classical compact

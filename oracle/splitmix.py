@@ -3,7 +3,7 @@
 The page ("TurboQuant 설명", section "1단계: 무작위 회전 + PolarQuant 압축")
 only says the rotation comes from the QR factorisation of a Gaussian matrix,
 and section "2단계: QJL 잔차 보정" uses a Gaussian projection.  It fixes no
-generator.  The reading adopted (reading R1):
+generator.  The reading adopted:
 
 * generator: SplitMix64 (G. Steele, D. Lea, C. Flood, "Fast splittable
   pseudorandom number generators", OOPSLA 2014): the state advances by the

@@ -4,8 +4,7 @@ This module holds no arithmetic of the quantiser: it only draws inputs.  The
 pages measure on model KV caches (Gemma / Mistral / Llama / Qwen families on
 LongBench, needle-in-a-haystack, RULER) and on GloVe-200 vector search; none of
 those weights or datasets is available, so every input is drawn here with the
-shapes and value distributions of those workloads (recipes in the design doc,
-"Synthetic inputs").
+shapes and value distributions of those workloads.
 
 Randomness: numpy ``SeedSequence(seed, spawn_key=(config, tensor, batch,
 head))`` streams, so any (batch, head) slice can be regenerated on its own.

@@ -1,6 +1,6 @@
 """Shared helpers of the GPU parity tests: oracle tables, tolerance rules.
 
-Tolerance rules ("Parity rules"):
+Tolerance rules:
 * codes (the per-coordinate records): Lloyd-Max indices bit-exact, except
   coordinates whose oracle value u = y/n lies within
   1e-5 of a decision boundary; those are counted and must stay under 0.01%

@@ -1,4 +1,4 @@
-"""Pins for the oracle's SplitMix64 / Box-Muller streams (reading R1)."""
+"""Pins for the oracle's SplitMix64 / Box-Muller streams (the generator is the reading stated in oracle/splitmix.py)."""
 
 import numpy as np
 import pytest

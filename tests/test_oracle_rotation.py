@@ -1,4 +1,4 @@
-"""Pins for Pi, S and M = S Pi^T (page section "1단계", reading R2)."""
+"""Pins for Pi, S and M = S Pi^T (page section "1단계"; the sign fix and y = Pi x are the readings stated in oracle/rotation.py)."""
 
 import numpy as np
 import pytest
