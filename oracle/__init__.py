@@ -28,10 +28,12 @@ Modules
              cell integrals through the regularised incomplete beta).
   quantizer  quantise (MSE / inner-product mode), bit-plane packing,
              dequantise, attention logits, top-k search, recall.
+  attention  decode attention output softmax(l) . V_hat over a quantised
+             value cache.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against closed forms,
 textbook special cases, brute force or invariants.  Points the page leaves
 open are read as stated in each module's docstring.
 """
 
-from . import splitmix, rotation, codebook, quantizer  # noqa: F401
+from . import splitmix, rotation, codebook, quantizer, attention  # noqa: F401
