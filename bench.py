@@ -12,8 +12,9 @@ keys per second of the whole step (cached keys / step time) with every input
 resident in HBM.  The line also carries the roofline of the dominant kernel
 (algorithmic bytes per launch / its mean duration, measured with HIP events
 on the launch stream), the fp64 CPU oracle timed on a bounded sample of the
-same workload, a per-call breakdown and the long-context logit leg (batch 8,
-8 KV heads, 131072 tokens, 4-bit keys).
+same workload, a per-call breakdown, the long-context logit leg (batch 8,
+8 KV heads, 131072 tokens, 4-bit keys) and, timed beside the step, the decode
+attention output softmax(logits) . V straight from the packed values.
 
 Two more workloads print a line of the same form: ``prefill`` quantises
 65536 new bf16 tokens x 8 KV heads (keys inner-product, values MSE) at b = 2,
@@ -148,7 +149,13 @@ def decode_workload(torch, tq, args, device):
                        "keys inner-product b=3, values MSE b=3; 32 query heads (GQA 4:1)",
            "batch": 1, "kv_heads": heads, "q_heads": qheads, "head_dim": d, "seq_len": seq,
            "key_bits": bits, "value_bits": bits, "units_per_step": n}
-    return calls, work, cfg, n
+    # Timed beside the step, not in it: the attention output softmax(l) . V
+    # straight from the packed values, on the step's logits.
+    attn = torch.empty((1, qheads, d), dtype=torch.float32, device=device)
+    extras = {"attn_output": (lambda: qv.attn_output(logits, cv, heads, seq, out=attn),
+                              n * rb_v + qheads * seq * 4 + qheads * d * 4, "attend_partial_kernel",
+                              ["attend.hip", "tq_device.h"])}
+    return calls, work, cfg, n, extras
 
 
 def prefill_workload(torch, tq, args, device):
@@ -171,7 +178,7 @@ def prefill_workload(torch, tq, args, device):
                        "inner-product and values MSE at b = 2, 3, 4 (six calls per step)",
            "tokens": tokens, "kv_heads": heads, "head_dim": d, "bits": [2, 3, 4],
            "units_per_step": 6 * n}
-    return calls, work, cfg, 6 * n
+    return calls, work, cfg, 6 * n, {}
 
 
 def search_workload(torch, tq, args, device):
@@ -192,7 +199,7 @@ def search_workload(torch, tq, args, device):
                        "MSE b = 2 and 4, fused top-10 (two calls per step)",
            "n_db": n_db, "n_queries": n_q, "head_dim": d, "bits": [2, 4], "topk": k,
            "units_per_step": 2 * n_q * n_db}
-    return calls, work, cfg, 2 * n_q * n_db
+    return calls, work, cfg, 2 * n_q * n_db, {}
 
 
 def _oracle_threads():
@@ -330,7 +337,7 @@ def main():
         del a, b
 
     build = {"decode": decode_workload, "prefill": prefill_workload, "search": search_workload}
-    calls, work, cfg, units = build[args.workload](torch, tq, args, device)
+    calls, work, cfg, units, extras = build[args.workload](torch, tq, args, device)
     unit = {"decode": "keys/s", "prefill": "vectors/s", "search": "keys/s"}[args.workload]
     step = lambda: [fn() for fn in calls.values()]
     for _ in range(args.warmup):
@@ -367,6 +374,17 @@ def main():
             "wall_s_timed": wall, "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "bf16 in; f16 split + i8 MFMA, f32/i32 accumulate",
             "data": "synthetic", "config": cfg, "roofline": roofline, "breakdown": breakdown}
+    if extras:
+        line["extras"] = {}
+        for name, (fn, byts, kern, src) in extras.items():
+            for _ in range(max(args.warmup, 1)):     # first calls size the library's workspace
+                fn()
+            t = timer(fn, args.steps)
+            line["extras"][name] = {"us": t * 1e6, "hbm_gbs": byts / t / 1e9,
+                                    "frac_hbm": byts / t / 1e9 / HBM_PEAK_GBS, "kernel": kern,
+                                    "algorithmic_bytes_per_launch": byts,
+                                    "traffic": _traffic(kern + ":" + name, src),
+                                    "in_step": False}
     if args.workload == "decode" and not args.no_long_context:
         line["long_context_logits"] = long_context_leg(torch, tq, timer, args.steps, device)
     if not args.no_cpu_baseline:

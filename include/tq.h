@@ -156,6 +156,24 @@ tq_status tq_attn_logits(const tq_params *p, const void *q, int32_t q_dtype, int
                          int64_t row_tokens, int64_t seq_len, float scale, float *logits,
                          int32_t topk, int32_t *topk_idx, void *stream);
 
+/* Decode attention output straight from packed values (page: the KV cache
+ * holds keys and values, section "TurboQuant란 무엇인가요?", and attention runs
+ * from the compressed indices, section "2단계", closing paragraph; the output
+ * is standard attention, softmax of the logits times the values).
+ *   logits       device fp32 [batch][n_q_heads][seq_len] (e.g. the output of
+ *                tq_attn_logits; -inf entries are masked tokens)
+ *   v            packed MSE-mode values laid out [batch][n_kv_heads][row_tokens]
+ *   out          device [batch][n_q_heads][d], out_dtype TQ_F32 or TQ_BF16:
+ *                o = sum_t softmax(logits)_t v_hat_t over the seq_len tokens of
+ *                the query head's KV head (GQA as in tq_attn_logits); a head
+ *                whose logits are all -inf, or seq_len == 0, gives o = 0.
+ * Supported: MSE mode, d in {128, 256}, up to 16 query heads per KV head,
+ * 16-byte aligned value codes.  Uses library scratch memory (per device and
+ * stream).  Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED, TQ_ERR_HIP. */
+tq_status tq_attn_output(const tq_params *p, const float *logits, int32_t batch, int32_t n_q_heads,
+                         int32_t n_kv_heads, const tq_packed *v, int64_t row_tokens, int64_t seq_len,
+                         void *out, int32_t out_dtype, void *stream);
+
 /* Reconstruct n_vec vectors (page section "2단계": reconstructed vectors).
  *   out          device [n_vec][d], out_dtype TQ_F32 or TQ_BF16
  * Supported: d in {64, 128, 256} MSE, d in {64, 128} PROD.

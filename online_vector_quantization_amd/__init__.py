@@ -34,7 +34,7 @@ KIND_S = 1
 KIND_M = 2
 
 EXPORTED = ["tq_make_codebook", "tq_make_rotation", "tq_quantize_kv", "tq_attn_logits",
-            "tq_dequantize", "tq_status_string"]
+            "tq_attn_output", "tq_dequantize", "tq_status_string"]
 
 
 class TQError(RuntimeError):
@@ -65,11 +65,13 @@ def _load():
                                    i64, vp]
     lib.tq_attn_logits.argtypes = [ctypes.POINTER(Params), vp, i32, i32, i32, i32,
                                    ctypes.POINTER(Packed), i64, i64, f32, vp, i32, vp, vp]
+    lib.tq_attn_output.argtypes = [ctypes.POINTER(Params), vp, i32, i32, i32, ctypes.POINTER(Packed),
+                                   i64, i64, vp, i32, vp]
     lib.tq_dequantize.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(Packed), i64, vp, i32, vp]
     lib.tq_status_string.argtypes = [i32]
     lib.tq_status_string.restype = ctypes.c_char_p
     for name in ("tq_make_codebook", "tq_make_rotation", "tq_quantize_kv", "tq_attn_logits",
-                 "tq_dequantize"):
+                 "tq_attn_output", "tq_dequantize"):
         getattr(lib, name).restype = i32
     return lib
 
@@ -230,6 +232,20 @@ class Quantizer:
                                 topk, ctypes.c_void_p(idx.data_ptr()), _stream_ptr(self.device))
         _check(st, "tq_attn_logits(topk)")
         return vals, idx
+
+    def attn_output(self, logits, cache, n_kv_heads, seq_len, row_tokens=None, out_dtype=None, out=None):
+        """Decode attention output [batch, n_q_heads, d]: softmax(logits) . values."""
+        torch = _torch()
+        bsz, hq, _ = logits.shape
+        row_tokens = seq_len if row_tokens is None else row_tokens
+        out_dtype = torch.float32 if out_dtype is None else out_dtype
+        if out is None:
+            out = torch.empty((bsz, hq, self.d), dtype=out_dtype, device=self.device)
+        st = LIB.tq_attn_output(ctypes.byref(self._params), ctypes.c_void_p(logits.data_ptr()), bsz, hq,
+                                n_kv_heads, ctypes.byref(cache.struct()), row_tokens, seq_len,
+                                ctypes.c_void_p(out.data_ptr()), _dtype_code(out), _stream_ptr(self.device))
+        _check(st, "tq_attn_output")
+        return out
 
     def dequantize(self, cache, n_vec, out_dtype=None, out=None):
         """Reconstructed vectors [n_vec, d] (fp32 or bf16)."""

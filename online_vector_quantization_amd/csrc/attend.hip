@@ -1,0 +1,476 @@
+// Decode attention output from packed MSE-mode values.
+//
+// Page "TurboQuant 설명: 무엇인지와 LLM 메모리 6배 절약 구현 방법": the KV cache
+// holds the key and the value vectors (section "TurboQuant란 무엇인가요?") and
+// attention runs from the compressed indices without a full dequantisation
+// (section "2단계: QJL 잔차 보정", closing paragraph).  The output of query head
+// h is o = sum_t p_t v_hat_t, p = softmax(l_h) over the valid tokens, with
+// v_hat_t = n_t Pi^T c[idx_t].  Since Pi^T is linear it is applied once per
+// query: o = Pi^T (sum_t e_t n_t c[idx_t]) / sum_t e_t, e_t = exp(l_t - max l).
+//
+// Design (gfx950):
+// * partial kernel: a workgroup owns one split of one (batch, KV head) stream
+//   and all G query heads of that KV head.  Each wave walks 64-token chunks
+//   with a running softmax: lane t loads token t's packed row, norm and
+//   logits (the next chunk's loads fly during this chunk's work), the wave
+//   takes the chunk maximum per head, rescales what it holds when the
+//   maximum rises, and stages the token's plane words and weights e n in LDS,
+//   transposed so that one 16-byte read gives four tokens.  Every lane then
+//   accumulates its coordinate pairs (one pair for d = 128, two for 256) over
+//   the chunk; a pair's two centroid values come from one read of a K^2-entry
+//   table.  The waves meet at the end and leave (max, sum e, accumulator) per
+//   head and split.
+// * combine kernel: one workgroup per query head rescales the splits to the
+//   common maximum, divides by the total weight and applies Pi^T; every load
+//   it needs is issued before its first barrier.
+// The call reads the packed values (b d / 8 + 2 B per token) and the logits
+// (4 B per token and head) once.  The accumulation costs G fused multiply-adds
+// per value coordinate and head on the vector ALUs, which bounds it before
+// HBM does for G >= 4 heads per KV head.
+#include <cfloat>
+
+#include "tq_device.h"
+#include "tq_internal.h"
+
+namespace {
+
+using namespace tqd;
+
+#ifndef TQ_ATT_WAVES
+#define TQ_ATT_WAVES 4
+#endif
+#ifndef TQ_ATT_BLOCKS_PER_CU
+#define TQ_ATT_BLOCKS_PER_CU 2
+#endif
+constexpr int kAttThreads = 64 * TQ_ATT_WAVES;
+constexpr int kChunk = 64;          // tokens per wave step (one per lane)
+
+struct PartArgs {
+  const float *logits;      // [batch][n_q_heads][seq_len]
+  const uint8_t *codes;
+  const uint16_t *norm;
+  const float *centroids;
+  int64_t row_tokens, seq_len, tokens_per_split;
+  int n_splits, n_kv_heads, n_q_heads, group;
+  float *part;              // [stream][split][G][D + 2]: max, sum e, accumulator
+};
+
+// Maximum over the wave (every lane gets it).
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+#pragma unroll
+  for (int off = 4; off < 64; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+#pragma unroll
+  for (int off = 4; off < 64; off <<= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int D, int LB, int G>
+__global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(PartArgs a) {
+  constexpr int K = 1 << LB;
+  constexpr int RB = LB * D / 8;          // packed bytes per token
+  constexpr int RW = RB / 4;              // ... in words
+  constexpr int CPL = D / 64;             // coordinates per lane (2 or 4)
+  constexpr int NW = kAttThreads / 64;
+  constexpr int CS = kChunk + 4;          // row stride of the transposed stage (words), padded against conflicts
+  static_assert(RB % 16 == 0 && CPL % 2 == 0, "layout");
+  __shared__ float2 ptab[K * K];          // (c[i0], c[i1]) of a coordinate pair
+  __shared__ __attribute__((aligned(16))) uint32_t cwt[NW][RW][CS];   // [word][token]
+  __shared__ __attribute__((aligned(16))) float wtt[NW][G][CS];       // [head][token]
+  __shared__ float redm[NW][G];
+  __shared__ float reds[NW][G];
+  __shared__ float accs[G][D];
+
+  const int split = blockIdx.x % a.n_splits;
+  const int stream = blockIdx.x / a.n_splits;
+  const int b = stream / a.n_kv_heads;
+  const int kvh = stream % a.n_kv_heads;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = lane_id();
+
+  const int64_t t_begin = (int64_t)split * a.tokens_per_split;
+  int64_t t_end = t_begin + a.tokens_per_split;
+  if (t_end > a.seq_len) t_end = a.seq_len;
+  const int n_tok = (int)(t_end - t_begin);
+  const float *lrow[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int gg = g < a.group ? g : 0;
+    lrow[g] = a.logits + ((int64_t)b * a.n_q_heads + (int64_t)kvh * a.group + gg) * a.seq_len + t_begin;
+  }
+  const int64_t row0 = (int64_t)stream * a.row_tokens + t_begin;
+  const i32x4 rc = make_rsrc(a.codes + row0 * RB, (uint32_t)n_tok * RB);
+  const i32x4 rn = make_rsrc(a.norm + row0, (uint32_t)n_tok * 2u);
+
+  // Per chunk, lane l owns token c0 + l; past the split's end the codes read
+  // as zeros and the token gets no weight.
+  i32x4 rw[RB / 16];
+  float rl[G];
+  uint16_t rnb = 0;
+  auto load_chunk = [&](int c0) __attribute__((always_inline)) {
+    const int t = c0 + l;
+#pragma unroll
+    for (int i = 0; i < RB / 16; ++i) rw[i] = tq_llvm_buf_ld_b128(rc, (int)((uint32_t)t * RB + 16 * i), 0, 0);
+    rnb = buf_load_u16<0>(rn, 2u * (uint32_t)t);
+    const int tc = t < n_tok ? t : n_tok - 1;
+#pragma unroll
+    for (int g = 0; g < G; ++g) rl[g] = lrow[g][tc];
+  };
+  if (kChunk * w < n_tok) load_chunk(kChunk * w);
+
+  // pair table: bits 2p and 2p+1 of the index are plane p of the even and of
+  // the odd coordinate
+  for (int e = tid; e < K * K; e += kAttThreads) {
+    int i0 = 0, i1 = 0;
+#pragma unroll
+    for (int p = 0; p < LB; ++p) {
+      i0 |= ((e >> (2 * p)) & 1) << p;
+      i1 |= ((e >> (2 * p + 1)) & 1) << p;
+    }
+    ptab[e] = make_float2(a.centroids[i0], a.centroids[i1]);
+  }
+  __syncthreads();
+
+  const int grp = CPL * l / 32;           // coordinate group of this lane
+  const int boff = CPL * l % 32;          // bit of its first coordinate
+  float acc[G][CPL];
+  float esum[G], mrun[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    esum[g] = 0.0f;
+    mrun[g] = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) acc[g][i] = 0.0f;
+  }
+
+  for (int c0 = kChunk * w; c0 < n_tok; c0 += kChunk * NW) {
+    const bool valid = c0 + l < n_tok;
+    // running softmax: chunk maximum, rescale of what the wave holds
+    float e[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float lv = (valid && g < a.group) ? rl[g] : -INFINITY;
+      const float nm = fmaxf(mrun[g], wave_max(lv));
+      if (nm != -INFINITY) {              // uniform over the wave
+        const float sc = expf(mrun[g] - nm);
+        esum[g] *= sc;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) acc[g][i] *= sc;
+        mrun[g] = nm;
+        e[g] = expf(lv - nm);
+      } else {
+        e[g] = 0.0f;
+      }
+    }
+    const float n = f16_bits_to_f32(rnb);
+#pragma unroll
+    for (int i = 0; i < RB / 16; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) cwt[w][4 * i + k][l] = (uint32_t)rw[i][k];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      esum[g] += e[g];
+      wtt[w][g][l] = e[g] * n;
+    }
+    if (c0 + kChunk * NW < n_tok) load_chunk(c0 + kChunk * NW);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // accumulate the chunk, four tokens per LDS read
+#pragma unroll 2
+    for (int t4 = 0; t4 < kChunk / 4; ++t4) {
+      u32x4 pw[LB];
+#pragma unroll
+      for (int p = 0; p < LB; ++p) pw[p] = *(const u32x4 *)&cwt[w][LB * grp + p][4 * t4];
+      f32x4 wg[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) wg[g] = *(const f32x4 *)&wtt[w][g][4 * t4];
+      // all table reads of the four tokens first, then their products
+      float2 cv[4][CPL / 2];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int q = 0; q < CPL / 2; ++q) {
+          // bitfield extracts and shift-ors: 2 LB VALU operations per pair
+          uint32_t pidx = __builtin_amdgcn_ubfe(pw[0][j], boff + 2 * q, 2);
+#pragma unroll
+          for (int p = 1; p < LB; ++p) pidx |= __builtin_amdgcn_ubfe(pw[p][j], boff + 2 * q, 2) << (2 * p);
+          cv[j][q] = ptab[pidx];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int q = 0; q < CPL / 2; ++q) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            acc[g][2 * q] = fmaf(wg[g][j], cv[j][q].x, acc[g][2 * q]);
+            acc[g][2 * q + 1] = fmaf(wg[g][j], cv[j][q].y, acc[g][2 * q + 1]);
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  // the waves meet: common maximum per head, each wave's share rescaled to it
+  if (l == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) redm[w][g] = mrun[g];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float v = redm[0][g];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) v = fmaxf(v, redm[i][g]);
+    const float f = mrun[g] == -INFINITY ? 0.0f : expf(mrun[g] - v);
+    const float s = wave_sum(esum[g]) * f;
+    if (l == 0) reds[w][g] = s;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) acc[g][i] *= f;
+  }
+  for (int i = 0; i < NW; ++i) {
+    if (w == i) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) accs[g][CPL * l + c] = (i == 0 ? 0.0f : accs[g][CPL * l + c]) + acc[g][c];
+    }
+    __syncthreads();
+  }
+  float *dst = a.part + (((int64_t)stream * a.n_splits + split) * G) * (D + 2);
+  for (int i = tid; i < G * (D + 2); i += kAttThreads) {
+    const int g = i / (D + 2), j = i % (D + 2);
+    float v;
+    if (j == 0) {
+      v = redm[0][g];
+#pragma unroll
+      for (int k = 1; k < NW; ++k) v = fmaxf(v, redm[k][g]);
+    } else if (j == 1) {
+      v = 0.0f;
+#pragma unroll
+      for (int k = 0; k < NW; ++k) v += reds[k][g];
+    } else {
+      v = accs[g][j - 2];
+    }
+    dst[i] = v;
+  }
+}
+
+struct CombArgs {
+  const float *part;
+  const float *pi;
+  int64_t n_rows;           // batch * n_q_heads
+  int n_splits, n_kv_heads, n_q_heads, group, gbucket;
+  void *out;
+  bool out_f32;
+};
+
+// One workgroup per query head, 4 groups of D threads: group q takes the
+// splits i = q (mod 4), then rows [q D/4, (q+1) D/4) of Pi; the groups meet
+// in LDS.  The Pi rows, the first kPre splits' accumulators and the split
+// maxima and sums are all requested before the first barrier, so the kernel
+// waits on memory about once.
+constexpr int kPre = 16;
+
+template <int D>
+__global__ __launch_bounds__(4 * D) void attend_combine_kernel(CombArgs a) {
+  constexpr int NWC = 4 * D / 64;
+  __shared__ float fac[256];
+  __shared__ float red[NWC];
+  __shared__ float red2[NWC];
+  __shared__ __attribute__((aligned(16))) float sum4[4][D];
+  __shared__ __attribute__((aligned(16))) float r[D];
+  const int64_t row = blockIdx.x;         // b * n_q_heads + h
+  const int tid = threadIdx.x;
+  const int wv = tid >> 6, l = lane_id();
+  const int q = tid / D, j = tid % D;
+  const int64_t b = row / a.n_q_heads;
+  const int h = (int)(row % a.n_q_heads);
+  const int kvh = h / a.group, g = h % a.group;
+  const int64_t stream = b * a.n_kv_heads + kvh;
+  const int64_t sstride = (int64_t)a.gbucket * (D + 2);
+  const float *src = a.part + (stream * a.n_splits * a.gbucket + g) * (D + 2);
+  const int ns = a.n_splits;              // <= 256 <= 4 D
+  if (ns == 0) {                          // no token at all: the output is zero
+    if (q == 0) {
+      if (a.out_f32)
+        ((float *)a.out)[row * D + j] = 0.0f;
+      else
+        ((uint16_t *)a.out)[row * D + j] = 0;
+    }
+    return;
+  }
+
+  // Loads with clamped indices and a select after them, so none of them
+  // sits behind a branch.
+  float pv[D / 4];
+#pragma unroll
+  for (int k = 0; k < D / 4; ++k) pv[k] = a.pi[(size_t)(q * (D / 4) + k) * D + j];
+  float av[kPre];
+#pragma unroll
+  for (int k = 0; k < kPre; ++k) {
+    const int i = q + 4 * k;
+    const float x = src[(i < ns ? i : ns - 1) * sstride + 2 + j];
+    av[k] = i < ns ? x : 0.0f;
+  }
+  const int ts = tid < ns ? tid : ns - 1;
+  const float fm0 = src[ts * sstride];
+  const float fs0 = src[ts * sstride + 1];
+  const float fm = tid < ns ? fm0 : -INFINITY;
+  const float fs = tid < ns ? fs0 : 0.0f;
+
+  // common maximum, then the rescaled total weight
+  float v = wave_max(fm);
+  if (l == 0) red[wv] = v;
+  __syncthreads();
+  float mm = red[0];
+#pragma unroll
+  for (int i = 1; i < NWC; ++i) mm = fmaxf(mm, red[i]);
+  const float f = (mm == -INFINITY || fm == -INFINITY) ? 0.0f : expf(fm - mm);
+  if (tid < ns) fac[tid] = f;
+  v = wave_sum(fs * f);
+  if (l == 0) red2[wv] = v;
+  __syncthreads();
+  float o = 0.0f;
+  if (mm != -INFINITY) {                  // uniform over the workgroup
+    float ssum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NWC; ++i) ssum += red2[i];
+    float acc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) {
+      const int i = q + 4 * k;
+      acc = fmaf(av[k], fac[i < ns ? i : 0], acc);     // av is 0 past ns
+    }
+    for (int i = q + 4 * kPre; i < ns; i += 4) acc = fmaf(src[i * sstride + 2 + j], fac[i], acc);
+    sum4[q][j] = acc;
+    __syncthreads();
+    if (q == 0) r[j] = (sum4[0][j] + sum4[1][j] + sum4[2][j] + sum4[3][j]) / ssum;
+    __syncthreads();
+    // o = Pi^T r: o_j = sum_k Pi[k][j] r_k, a quarter of the rows per group
+    float oq = 0.0f;
+#pragma unroll
+    for (int k = 0; k < D / 4; k += 4) {
+      const f32x4 rv = *(const f32x4 *)&r[q * (D / 4) + k];
+      oq = fmaf(pv[k], rv[0], oq);
+      oq = fmaf(pv[k + 1], rv[1], oq);
+      oq = fmaf(pv[k + 2], rv[2], oq);
+      oq = fmaf(pv[k + 3], rv[3], oq);
+    }
+    sum4[q][j] = oq;
+    __syncthreads();
+    o = sum4[0][j] + sum4[1][j] + sum4[2][j] + sum4[3][j];
+  }
+  if (q == 0) {
+    if (a.out_f32)
+      ((float *)a.out)[row * D + j] = o;
+    else
+      ((uint16_t *)a.out)[row * D + j] = f32_to_bf16_bits(o);
+  }
+}
+
+template <int D, int LB, int G>
+hipError_t launch_t(const tqi::AttendArgs &aa, hipStream_t s) {
+  const int group = aa.n_q_heads / aa.n_kv_heads;
+  const int64_t n_streams = (int64_t)aa.batch * aa.n_kv_heads;
+  // splits: a few workgroups per CU in all, at least 256 tokens each
+  const int64_t cus = tqi::device_cu_count();
+  int64_t splits = (TQ_ATT_BLOCKS_PER_CU * cus + n_streams - 1) / n_streams;
+  const int64_t max_splits = (aa.seq_len + 255) / 256;
+  if (splits > max_splits) splits = max_splits;
+  if (splits > 256) splits = 256;
+  if (splits < 1) splits = 1;
+  int64_t tps = (aa.seq_len + splits - 1) / splits;
+  tps = (tps + kChunk - 1) / kChunk * kChunk;
+  splits = aa.seq_len > 0 ? (aa.seq_len + tps - 1) / tps : 0;
+  constexpr int RB = LB * D / 8;
+  if ((tps + kChunk) * RB >= (1LL << 31)) return hipErrorInvalidValue;
+  const size_t bytes = (size_t)n_streams * (splits > 0 ? splits : 1) * G * (D + 2) * sizeof(float);
+  float *part = nullptr;
+  hipError_t e = tqi::workspace(s, bytes, (void **)&part);
+  if (e != hipSuccess) return e;
+  if (splits > 0) {
+    PartArgs pa;
+    pa.logits = aa.logits;
+    pa.codes = aa.codes;
+    pa.norm = aa.norm;
+    pa.centroids = aa.centroids;
+    pa.row_tokens = aa.row_tokens;
+    pa.seq_len = aa.seq_len;
+    pa.tokens_per_split = tps;
+    pa.n_splits = (int)splits;
+    pa.n_kv_heads = aa.n_kv_heads;
+    pa.n_q_heads = aa.n_q_heads;
+    pa.group = group;
+    pa.part = part;
+    hipLaunchKernelGGL((attend_partial_kernel<D, LB, G>), dim3((unsigned)(n_streams * splits)), dim3(kAttThreads),
+                       0, s, pa);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  CombArgs ca;
+  ca.part = part;
+  ca.pi = aa.pi;
+  ca.n_rows = (int64_t)aa.batch * aa.n_q_heads;
+  ca.n_splits = (int)splits;
+  ca.n_kv_heads = aa.n_kv_heads;
+  ca.n_q_heads = aa.n_q_heads;
+  ca.group = group;
+  ca.gbucket = G;
+  ca.out = aa.out;
+  ca.out_f32 = aa.out_f32;
+  hipLaunchKernelGGL((attend_combine_kernel<D>), dim3((unsigned)ca.n_rows), dim3(4 * D), 0, s, ca);
+  return hipGetLastError();
+}
+
+template <int D, int LB>
+hipError_t launch_g(const tqi::AttendArgs &a, hipStream_t s, bool *ok) {
+  const int group = a.n_q_heads / a.n_kv_heads;
+  *ok = true;
+  if (group <= 1) return launch_t<D, LB, 1>(a, s);
+  if (group <= 2) return launch_t<D, LB, 2>(a, s);
+  if (group <= 4) return launch_t<D, LB, 4>(a, s);
+  if (group <= 8) return launch_t<D, LB, 8>(a, s);
+  if (group <= 16) return launch_t<D, LB, 16>(a, s);
+  *ok = false;
+  return hipSuccess;
+}
+
+template <int D>
+hipError_t launch_lb(int lb, const tqi::AttendArgs &a, hipStream_t s, bool *ok) {
+  switch (lb) {
+    case 1: return launch_g<D, 1>(a, s, ok);
+    case 2: return launch_g<D, 2>(a, s, ok);
+    case 3: return launch_g<D, 3>(a, s, ok);
+    case 4: return launch_g<D, 4>(a, s, ok);
+  }
+  *ok = false;
+  return hipSuccess;
+}
+
+}  // namespace
+
+namespace tqi {
+
+hipError_t launch_attend(int d, int lbits, const AttendArgs &a, hipStream_t s, bool *supported) {
+  *supported = false;
+  if (d == 128) return launch_lb<128>(lbits, a, s, supported);
+  if (d == 256) return launch_lb<256>(lbits, a, s, supported);
+  return hipSuccess;
+}
+
+}  // namespace tqi

@@ -170,6 +170,40 @@ extern "C" tq_status tq_attn_logits(const tq_params *p, const void *q, int32_t q
   return hip_status(e);
 }
 
+extern "C" tq_status tq_attn_output(const tq_params *p, const float *logits, int32_t batch,
+                                    int32_t n_q_heads, int32_t n_kv_heads, const tq_packed *v,
+                                    int64_t row_tokens, int64_t seq_len, void *out, int32_t out_dtype,
+                                    void *stream) {
+  tq_status st = check_params(p);
+  if (st != TQ_OK) return st;
+  if (v == nullptr || batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0) return TQ_ERR_INVALID;
+  if (n_q_heads % n_kv_heads != 0) return TQ_ERR_INVALID;
+  if (out_dtype != TQ_F32 && out_dtype != TQ_BF16) return TQ_ERR_INVALID;
+  if (seq_len < 0 || row_tokens < seq_len) return TQ_ERR_INVALID;
+  if (batch == 0) return TQ_OK;
+  if (out == nullptr) return TQ_ERR_INVALID;
+  if (seq_len > 0 && (logits == nullptr || v->codes == nullptr || v->norm == nullptr)) return TQ_ERR_INVALID;
+  if (p->mode != TQ_MODE_MSE) return TQ_ERR_UNSUPPORTED;
+  if ((uintptr_t)v->codes & 15u) return TQ_ERR_UNSUPPORTED;
+  tqi::AttendArgs a;
+  a.logits = logits;
+  a.batch = batch;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.pi = p->pi;
+  a.centroids = p->centroids;
+  a.codes = v->codes;
+  a.norm = v->norm;
+  a.row_tokens = row_tokens;
+  a.seq_len = seq_len;
+  a.out = out;
+  a.out_f32 = out_dtype == TQ_F32;
+  bool ok = false;
+  hipError_t e = tqi::launch_attend(p->d, lloyd_bits(p), a, (hipStream_t)stream, &ok);
+  if (!ok) return TQ_ERR_UNSUPPORTED;
+  return hip_status(e);
+}
+
 extern "C" tq_status tq_dequantize(const tq_params *p, const tq_packed *k, int64_t n_vec, void *out,
                                    int32_t out_dtype, void *stream) {
   tq_status st = check_params(p);

@@ -66,6 +66,20 @@ struct DequantArgs {
 hipError_t launch_dequant(int d, int lbits, bool prod, const DequantArgs &a, hipStream_t s,
                           bool *supported);
 
+struct AttendArgs {
+  const float *logits;   // [batch][n_q_heads][seq_len]
+  int batch, n_q_heads, n_kv_heads;
+  const float *pi;
+  const float *centroids;
+  const uint8_t *codes;
+  const uint16_t *norm;
+  int64_t row_tokens, seq_len;
+  void *out;             // [batch][n_q_heads][d]
+  bool out_f32;
+};
+
+hipError_t launch_attend(int d, int lbits, const AttendArgs &a, hipStream_t s, bool *supported);
+
 int device_cu_count();
 
 // Scratch memory for one call on stream `s` of the current device.  The

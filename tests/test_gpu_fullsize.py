@@ -85,7 +85,8 @@ def test_config1_tiny_full(tq):
 def test_config2_decode_full(tq):
     """8 heads x 32768 bf16 tokens: keys prod b=3, values MSE b=3, 32 GQA queries.
 
-    Every code, norm and logit; dequantized values on sampled rows."""
+    Every code, norm and logit; dequantized values on sampled rows; the decode
+    attention output of every head."""
     d, heads, qheads, seq, bits = 128, 8, 32, 32768, 3
     n = heads * seq
     group = qheads // heads
@@ -125,6 +126,13 @@ def test_config2_decode_full(tq):
     check_dequant(got32, want)
     got16 = qv.dequantize(ovc, n, out_dtype=torch.bfloat16).float().cpu().numpy()[rows]
     assert np.all(np.abs(got16 - want) <= 2.0 ** -8 * np.abs(want) + 1e-3 * np.abs(want).max(axis=1, keepdims=True))
+    # decode attention output of all 32 heads from these logits and the oracle-packed values
+    from oracle import attention as oatt
+    got = qv.attn_output(torch.from_numpy(out[None]).to(DEV), ovc, heads, seq).cpu().numpy()
+    ocache = {"codes": refv["codes"].reshape(1, heads, seq, -1), "norm": refv["norm"].reshape(1, heads, seq)}
+    want = oatt.attn_output(out[None].astype(np.float64), ocache, otv.pi, otv.c, oqz.MODE_MSE)
+    err = np.linalg.norm(got - want, axis=2)
+    assert np.all(err <= 1e-4 * np.linalg.norm(want, axis=2) + 1e-6)
 
 
 def test_config3_long_context_full(tq):

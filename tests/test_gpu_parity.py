@@ -282,3 +282,62 @@ def test_empty_and_single(tq):
     assert lg.shape == (1, 4, 1) and torch.isfinite(lg).all()
     empty = qz.attn_logits(torch.ones((1, 4, 128), device=DEV), cache, n_kv_heads=1, seq_len=0, scale=1.0)
     assert empty.shape == (1, 4, 0)
+
+
+ATTN_CASES = [  # d, bits, batch, n_kv_heads, group, seq_len, extra row capacity
+    (128, 3, 1, 2, 4, 1000, 0),      # 15 chunks + a ragged one, two KV heads
+    (128, 2, 2, 3, 1, 33, 5),        # batch 2, no GQA, one partial chunk, row_tokens > seq_len
+    (128, 4, 1, 1, 8, 5000, 0),      # several splits
+    (128, 1, 1, 2, 2, 1, 0),         # a single token
+    (256, 2, 1, 1, 16, 700, 3),      # padded search width, the largest GQA group
+    (256, 4, 2, 1, 3, 2100, 0),      # group padded to 4
+]
+
+
+@pytest.mark.parametrize("d,bits,batch,hkv,group,seq,extra", ATTN_CASES)
+def test_attn_output_parity(tq, d, bits, batch, hkv, group, seq, extra):
+    """softmax(logits) . V_hat from packed MSE values vs the fp64 oracle."""
+    from oracle import attention as oatt
+    rows = seq + extra
+    rng = np.random.default_rng(1000 * d + 10 * bits + group)
+    x = rng.standard_normal((batch * hkv * rows, d)) * rng.uniform(0.2, 4.0, (batch * hkv * rows, 1))
+    x[7 % x.shape[0]] = 0.0
+    ot = OracleTables(d, bits, oqz.MODE_MSE)
+    ref = ot.quantize(x)
+    qz = tq.Quantizer(d, bits, oqz.MODE_MSE, seed=0, device=DEV)
+    cache = cache_from_oracle(tq, ref, d, bits, oqz.MODE_MSE, DEV)
+    hq = hkv * group
+    logits = (rng.standard_normal((batch, hq, seq)) * 3.0).astype(np.float32)
+    logits[:, :, rng.integers(0, seq, max(1, seq // 7))] = -np.inf      # masked tokens
+    if hq > 1:
+        logits[0, hq - 1, :] = -np.inf                                    # a fully masked head
+    lt = torch.from_numpy(logits).to(DEV)
+    got = qz.attn_output(lt, cache, n_kv_heads=hkv, seq_len=seq, row_tokens=rows).cpu().numpy()
+    rb = ref["codes"].shape[1]
+    ocache = {"codes": ref["codes"].reshape(batch, hkv, rows, rb), "norm": ref["norm"].reshape(batch, hkv, rows)}
+    want = oatt.attn_output(logits.astype(np.float64), ocache, ot.pi, ot.c, oqz.MODE_MSE, seq_len=seq)
+    err = np.linalg.norm(got - want, axis=2)
+    scale = np.linalg.norm(want, axis=2)
+    assert np.all(err <= 1e-4 * scale + 1e-6), float(np.max(err - 1e-4 * scale))
+    if hq > 1:
+        assert np.all(got[0, hq - 1] == 0.0)
+    gotb = qz.attn_output(lt, cache, n_kv_heads=hkv, seq_len=seq, row_tokens=rows,
+                          out_dtype=torch.bfloat16).float().cpu().numpy()
+    assert np.all(np.abs(gotb - want) <= 2.0 ** -8 * np.abs(want).max(axis=2, keepdims=True) + 1e-6)
+
+
+def test_attn_output_empty_and_unsupported(tq):
+    d, bits = 128, 3
+    ot = OracleTables(d, bits, oqz.MODE_MSE)
+    ref = ot.quantize(np.random.default_rng(2).standard_normal((64, d)))
+    qz = tq.Quantizer(d, bits, oqz.MODE_MSE, seed=0, device=DEV)
+    cache = cache_from_oracle(tq, ref, d, bits, oqz.MODE_MSE, DEV)
+    out = torch.full((1, 4, d), 7.0, device=DEV)
+    qz.attn_output(torch.zeros((1, 4, 0), device=DEV), cache, n_kv_heads=1, seq_len=0, row_tokens=64, out=out)
+    assert torch.all(out == 0.0)
+    otp = OracleTables(d, bits, oqz.MODE_PROD)
+    refp = otp.quantize(np.random.default_rng(3).standard_normal((64, d)))
+    qp = tq.Quantizer(d, bits, oqz.MODE_PROD, seed=0, device=DEV)
+    cp = cache_from_oracle(tq, refp, d, bits, oqz.MODE_PROD, DEV)
+    with pytest.raises(tq.TQError):
+        qp.attn_output(torch.zeros((1, 4, 64), device=DEV), cp, n_kv_heads=1, seq_len=64)
