@@ -55,21 +55,58 @@ struct PartArgs {
   float *part;              // [stream][split][G][D + 2]: max, sum e, accumulator
 };
 
-// Maximum over the wave (every lane gets it).
-__device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float lane_of(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Maxima (sums) over the wave of N values at once, every lane gets them: DPP
+// steps within rows of 16 lanes (quad permutes, row rotations by 4 and 8),
+// then the four row results read as scalars.  The N reductions are
+// interleaved so their latencies overlap; nothing goes through LDS.
+template <int N>
+__device__ __forceinline__ void wave_max_n(float (&v)[N]) {
 #pragma unroll
-  for (int off = 4; off < 64; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-  return v;
+  for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], dpp<0xB1>(v[i]));
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], dpp<0x4E>(v[i]));
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], dpp<0x124>(v[i]));
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = fmaxf(v[i], dpp<0x128>(v[i]));
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    v[i] = fmaxf(fmaxf(lane_of(v[i], 0), lane_of(v[i], 16)), fmaxf(lane_of(v[i], 32), lane_of(v[i], 48)));
+}
+
+template <int N>
+__device__ __forceinline__ void wave_sum_n(float (&v)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp<0xB1>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp<0x4E>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp<0x124>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp<0x128>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = (lane_of(v[i], 0) + lane_of(v[i], 16)) + (lane_of(v[i], 32) + lane_of(v[i], 48));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  float a[1] = {v};
+  wave_max_n(a);
+  return a[0];
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
-#pragma unroll
-  for (int off = 4; off < 64; off <<= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+  float a[1] = {v};
+  wave_sum_n(a);
+  return a[0];
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -155,22 +192,25 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(PartArgs a)
 
   for (int c0 = kChunk * w; c0 < n_tok; c0 += kChunk * NW) {
     const bool valid = c0 + l < n_tok;
-    // running softmax: chunk maximum, rescale of what the wave holds
-    float e[G];
+    // running softmax: chunk maximum, rescale of what the wave holds (a
+    // head with no finite logit yet keeps factor 1 and weight 0)
+    float e[G], lv[G], cm[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const float lv = (valid && g < a.group) ? rl[g] : -INFINITY;
-      const float nm = fmaxf(mrun[g], wave_max(lv));
-      if (nm != -INFINITY) {              // uniform over the wave
-        const float sc = expf(mrun[g] - nm);
-        esum[g] *= sc;
+      lv[g] = (valid && g < a.group) ? rl[g] : -INFINITY;
+      cm[g] = lv[g];
+    }
+    wave_max_n(cm);
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) acc[g][i] *= sc;
-        mrun[g] = nm;
-        e[g] = expf(lv - nm);
-      } else {
-        e[g] = 0.0f;
-      }
+    for (int g = 0; g < G; ++g) {
+      const float nm = fmaxf(mrun[g], cm[g]);
+      const bool live = nm != -INFINITY;
+      const float sc = __expf(live ? mrun[g] - nm : 0.0f);
+      esum[g] *= sc;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) acc[g][i] *= sc;
+      mrun[g] = nm;
+      e[g] = __expf(live ? lv[g] - nm : -INFINITY);
     }
     const float n = f16_bits_to_f32(rnb);
 #pragma unroll
@@ -231,14 +271,14 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(PartArgs a)
     for (int g = 0; g < G; ++g) redm[w][g] = mrun[g];
   }
   __syncthreads();
+  wave_sum_n(esum);
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     float v = redm[0][g];
 #pragma unroll
     for (int i = 1; i < NW; ++i) v = fmaxf(v, redm[i][g]);
-    const float f = mrun[g] == -INFINITY ? 0.0f : expf(mrun[g] - v);
-    const float s = wave_sum(esum[g]) * f;
-    if (l == 0) reds[w][g] = s;
+    const float f = mrun[g] == -INFINITY ? 0.0f : __expf(mrun[g] - v);
+    if (l == 0) reds[w][g] = esum[g] * f;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) acc[g][i] *= f;
   }
@@ -265,6 +305,274 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(PartArgs a)
       for (int k = 0; k < NW; ++k) v += reds[k][g];
     } else {
       v = accs[g][j - 2];
+    }
+    dst[i] = v;
+  }
+}
+
+// MFMA form of the split kernel, for G >= 4 query heads per KV head.  Per
+// 16-token step and 32-coordinate group, a 16x16x32 fp16 MFMA forms
+// D[m][n] = sum_k A[m][k] B[k][n] with
+//   k = 2 tok + s   (tok: the step's 16 tokens, s: coordinate of the pair),
+//   n = pair p of the group (coordinates 2p, 2p + 1),
+//   m = 2 h + s'    (head h, coordinate parity s'),
+//   A[m][k] = W[h][tok] if s = s' else 0,   B[k][n] = c[idx(tok, 2n + s)],
+// so D[2h + s'][n] = sum_tok W[h][tok] c[idx(tok, 2n + s')].  At staging the
+// lane that loaded a token turns its bit planes into one byte per pair (the
+// pair's 2 LB index bits, spread with shifts and masks, four pairs a word) and
+// stores them transposed by token; a lane's B fragment (four tokens of one
+// pair) is then one 16-byte read, four byte extracts and eight 4-byte reads
+// of the hi and lo pair tables.  Its A fragment is one read of the staged
+// weights.  The running maximum is taken over
+// l + ln n, so the weights W = e n lie in [0, 1]; weights and centroids are
+// split into fp16 hi + lo and three products (hi hi, hi lo, lo hi) keep about
+// 22 bits.
+template <int D, int LB, int G>
+__global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(PartArgs a) {
+  constexpr int K = 1 << LB;
+  constexpr int RB = LB * D / 8;          // packed bytes per token
+  constexpr int NW = kAttThreads / 64;
+  constexpr int MT = (2 * G + 15) / 16;   // 16-row tiles of (head, parity)
+  constexpr int NG = D / 32;              // coordinate groups, 16 pairs each
+  constexpr int PR = 16 * MT - 2 * G;     // padding rows of A (zero)
+  constexpr int CS = kChunk + 4;
+  constexpr int PQ = D / 8;              // words of pair bytes per token
+  constexpr int PS = LB <= 3 ? 2 : 0;     // pair bytes hold idx * 4 when it fits
+  static_assert(G >= 4 && RB % 16 == 0, "layout");
+  __shared__ uint32_t tabh[K * K];        // hi of (c[i0], c[i1]) as an fp16 pair
+  __shared__ uint32_t tabl[K * K];        // lo of the same
+  __shared__ __attribute__((aligned(16))) uint32_t pqt[NW][PQ][CS];        // [pair quad][token]
+  __shared__ __attribute__((aligned(16))) uint32_t awt[NW][2][16 * MT][CS];  // A words [hi/lo][row][token]
+  __shared__ float scs[NW][8 * MT];       // per-head factor read by lane-dependent head
+  __shared__ float redm[NW][G];
+  __shared__ float reds[NW][G];
+
+  const int split = blockIdx.x % a.n_splits;
+  const int stream = blockIdx.x / a.n_splits;
+  const int b = stream / a.n_kv_heads;
+  const int kvh = stream % a.n_kv_heads;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = lane_id();
+  const int q = l >> 4, pn = l & 15;      // MFMA lane coordinates
+
+  const int64_t t_begin = (int64_t)split * a.tokens_per_split;
+  int64_t t_end = t_begin + a.tokens_per_split;
+  if (t_end > a.seq_len) t_end = a.seq_len;
+  const int n_tok = (int)(t_end - t_begin);
+  const float *lrow[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int gg = g < a.group ? g : 0;
+    lrow[g] = a.logits + ((int64_t)b * a.n_q_heads + (int64_t)kvh * a.group + gg) * a.seq_len + t_begin;
+  }
+  const int64_t row0 = (int64_t)stream * a.row_tokens + t_begin;
+  const i32x4 rc = make_rsrc(a.codes + row0 * RB, (uint32_t)n_tok * RB);
+  const i32x4 rn = make_rsrc(a.norm + row0, (uint32_t)n_tok * 2u);
+
+  i32x4 rw[RB / 16];
+  float rl[G];
+  uint16_t rnb = 0;
+  auto load_chunk = [&](int c0) __attribute__((always_inline)) {
+    const int t = c0 + l;
+#pragma unroll
+    for (int i = 0; i < RB / 16; ++i) rw[i] = tq_llvm_buf_ld_b128(rc, (int)((uint32_t)t * RB + 16 * i), 0, 0);
+    rnb = buf_load_u16<0>(rn, 2u * (uint32_t)t);
+    const int tc = t < n_tok ? t : n_tok - 1;
+#pragma unroll
+    for (int g = 0; g < G; ++g) rl[g] = lrow[g][tc];
+  };
+  if (kChunk * w < n_tok) load_chunk(kChunk * w);
+
+  for (int e = tid; e < K * K; e += kAttThreads) {
+    int i0 = 0, i1 = 0;
+#pragma unroll
+    for (int p = 0; p < LB; ++p) {
+      i0 |= ((e >> (2 * p)) & 1) << p;
+      i1 |= ((e >> (2 * p + 1)) & 1) << p;
+    }
+    const float c0 = a.centroids[i0], c1 = a.centroids[i1];
+    const _Float16 h0 = (_Float16)c0, h1 = (_Float16)c1;
+    const _Float16 l0 = (_Float16)(c0 - (float)h0), l1 = (_Float16)(c1 - (float)h1);
+    tabh[e] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+    tabl[e] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+  }
+  if constexpr (PR > 0) {
+    for (int i = tid; i < NW * 2 * PR * CS; i += kAttThreads) {
+      const int col = i % CS, r = (i / CS) % PR, hl = (i / (CS * PR)) % 2, ww = i / (CS * PR * 2);
+      awt[ww][hl][2 * G + r][col] = 0u;
+    }
+  }
+  if (tid < NW * 8 * MT) scs[tid / (8 * MT)][tid % (8 * MT)] = 1.0f;
+  __syncthreads();
+
+  f32x4 acc[MT][NG];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int j = 0; j < NG; ++j) acc[mt][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float esum[G], mrun[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    esum[g] = 0.0f;
+    mrun[g] = -INFINITY;
+  }
+
+  for (int c0 = kChunk * w; c0 < n_tok; c0 += kChunk * NW) {
+    const bool valid = c0 + l < n_tok;
+    const float n = f16_bits_to_f32(rnb);
+    const float lnn = __logf(fmaxf(n, 0x1p-24f));     // n = 0 gives weight 0 whatever the shift
+    float sc[G], lv[G], cm[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      lv[g] = (valid && g < a.group) ? rl[g] : -INFINITY;
+      cm[g] = lv[g] + lnn;
+    }
+    wave_max_n(cm);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      // a head with no finite logit yet keeps factor 1 and weight 0
+      const float nm = fmaxf(mrun[g], cm[g]);
+      const bool live = nm != -INFINITY;
+      sc[g] = __expf(live ? mrun[g] - nm : 0.0f);
+      esum[g] *= sc[g];
+      mrun[g] = nm;
+      const float e = __expf(live ? lv[g] - nm : -INFINITY);
+      esum[g] += e;
+      const float wgt = e * n;
+      const _Float16 hi = (_Float16)wgt;
+      const _Float16 lo = (_Float16)(wgt - (float)hi);
+      const uint32_t hb = __builtin_bit_cast(uint16_t, hi), lb = __builtin_bit_cast(uint16_t, lo);
+      awt[w][0][2 * g][l] = hb;
+      awt[w][0][2 * g + 1][l] = hb << 16;
+      awt[w][1][2 * g][l] = lb;
+      awt[w][1][2 * g + 1][l] = lb << 16;
+    }
+    if (l == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) scs[w][g] = sc[g];
+    }
+    // pair bytes: byte k of word 4 j + o holds the index bits of pair
+    // 4 k + o of group j (bits 2p, 2p + 1 = plane p of its two coordinates),
+    // times 4 when that fits in a byte.  Pair 4 k + o sits at bit 8 k + 2 o of
+    // every plane word, so each plane costs one shift and one masked or.
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+#pragma unroll
+      for (int o = 0; o < 4; ++o) {
+        uint32_t pb = 0;
+#pragma unroll
+        for (int p = 0; p < LB; ++p) {
+          const int wi = LB * j + p;
+          const uint32_t x = (uint32_t)rw[wi / 4][wi % 4];
+          const int sh = 2 * p + PS - 2 * o;              // where the pair's bits go
+          const uint32_t y = sh >= 0 ? x << sh : x >> -sh;
+          pb |= y & (0x03030303u << (2 * p + PS));
+        }
+        pqt[w][4 * j + o][l] = pb;
+      }
+    }
+    if (c0 + kChunk * NW < n_tok) load_chunk(c0 + kChunk * NW);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // rows 4q + r of tile mt hold head 8 mt + 2 q + r / 2
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const float f0 = scs[w][8 * mt + 2 * q], f1 = scs[w][8 * mt + 2 * q + 1];
+#pragma unroll
+      for (int j = 0; j < NG; ++j) {
+        acc[mt][j][0] *= f0;
+        acc[mt][j][1] *= f0;
+        acc[mt][j][2] *= f1;
+        acc[mt][j][3] *= f1;
+      }
+    }
+#pragma unroll 1
+    for (int st = 0; st < kChunk / 16; ++st) {
+      const int tb = 16 * st + 4 * q;     // this lane's four tokens
+      half8 ah[MT], al[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        ah[mt] = __builtin_bit_cast(half8, *(const u32x4 *)&awt[w][0][16 * mt + pn][tb]);
+        al[mt] = __builtin_bit_cast(half8, *(const u32x4 *)&awt[w][1][16 * mt + pn][tb]);
+      }
+#pragma unroll
+      for (int j = 0; j < NG; ++j) {
+        const u32x4 pv = *(const u32x4 *)&pqt[w][4 * j + (pn & 3)][tb];
+        u32x4 bh, bl;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t pb = __builtin_amdgcn_ubfe(pv[t], 8 * (pn >> 2), 8);
+          const uint32_t off = PS == 2 ? pb : pb << 2;          // byte offset into the tables
+          bh[t] = *(const uint32_t *)((const char *)tabh + off);
+          bl[t] = *(const uint32_t *)((const char *)tabl + off);
+        }
+        const half8 bhh = __builtin_bit_cast(half8, bh), bll = __builtin_bit_cast(half8, bl);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[mt], bhh, acc[mt][j], 0, 0, 0);
+          acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[mt], bll, acc[mt][j], 0, 0, 0);
+          acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[mt], bhh, acc[mt][j], 0, 0, 0);
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  // the waves meet: common maximum per head, each wave's share rescaled to it
+  if (l == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) redm[w][g] = mrun[g];
+  }
+  __syncthreads();
+  float fw[G];
+  wave_sum_n(esum);
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float v = redm[0][g];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) v = fmaxf(v, redm[i][g]);
+    fw[g] = mrun[g] == -INFINITY ? 0.0f : __expf(mrun[g] - v);
+    if (l == 0) reds[w][g] = esum[g] * fw[g];
+  }
+  // each wave leaves its rescaled share in its own slab (the staging
+  // memory, free now), then every thread sums the slabs for its outputs
+  float *slab = (float *)&awt[0][0][0][0];                // [NW][G][D]
+  static_assert(NW * G * D <= NW * 2 * 16 * MT * CS, "slab fits");
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int g = 8 * mt + 2 * q + r / 2;
+      if (g < G) {
+        float f = fw[0];
+#pragma unroll
+        for (int gg = 1; gg < G; ++gg) f = g == gg ? fw[gg] : f;
+#pragma unroll
+        for (int j = 0; j < NG; ++j) slab[(w * G + g) * D + 32 * j + 2 * pn + (r & 1)] = acc[mt][j][r] * f;
+      }
+    }
+  }
+  __syncthreads();
+  float *dst = a.part + (((int64_t)stream * a.n_splits + split) * G) * (D + 2);
+  for (int i = tid; i < G * (D + 2); i += kAttThreads) {
+    const int g = i / (D + 2), j = i % (D + 2);
+    float v;
+    if (j == 0) {
+      v = redm[0][g];
+#pragma unroll
+      for (int k = 1; k < NW; ++k) v = fmaxf(v, redm[k][g]);
+    } else if (j == 1) {
+      v = 0.0f;
+#pragma unroll
+      for (int k = 0; k < NW; ++k) v += reds[k][g];
+    } else {
+      v = 0.0f;
+#pragma unroll
+      for (int k = 0; k < NW; ++k) v += slab[(k * G + g) * D + j - 2];
     }
     dst[i] = v;
   }
@@ -417,8 +725,12 @@ hipError_t launch_t(const tqi::AttendArgs &aa, hipStream_t s) {
     pa.n_q_heads = aa.n_q_heads;
     pa.group = group;
     pa.part = part;
-    hipLaunchKernelGGL((attend_partial_kernel<D, LB, G>), dim3((unsigned)(n_streams * splits)), dim3(kAttThreads),
-                       0, s, pa);
+    if constexpr (G >= 4)
+      hipLaunchKernelGGL((attend_mfma_kernel<D, LB, G>), dim3((unsigned)(n_streams * splits)), dim3(kAttThreads),
+                         0, s, pa);
+    else
+      hipLaunchKernelGGL((attend_partial_kernel<D, LB, G>), dim3((unsigned)(n_streams * splits)), dim3(kAttThreads),
+                         0, s, pa);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
