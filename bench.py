@@ -153,7 +153,7 @@ def decode_workload(torch, tq, args, device):
     # straight from the packed values, on the step's logits.
     attn = torch.empty((1, qheads, d), dtype=torch.float32, device=device)
     extras = {"attn_output": (lambda: qv.attn_output(logits, cv, heads, seq, out=attn),
-                              n * rb_v + qheads * seq * 4 + qheads * d * 4, "attend_partial_kernel",
+                              n * rb_v + qheads * seq * 4 + qheads * d * 4, "attend_mfma_kernel",
                               ["attend.hip", "tq_device.h"])}
     return calls, work, cfg, n, extras
 

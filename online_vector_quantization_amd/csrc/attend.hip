@@ -334,15 +334,16 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(PartArgs a) {
   constexpr int NW = kAttThreads / 64;
   constexpr int MT = (2 * G + 15) / 16;   // 16-row tiles of (head, parity)
   constexpr int NG = D / 32;              // coordinate groups, 16 pairs each
-  constexpr int PR = 16 * MT - 2 * G;     // padding rows of A (zero)
   constexpr int CS = kChunk + 4;
   constexpr int PQ = D / 8;              // words of pair bytes per token
   constexpr int PS = LB <= 3 ? 2 : 0;     // pair bytes hold idx * 4 when it fits
   static_assert(G >= 4 && RB % 16 == 0, "layout");
   __shared__ uint32_t tabh[K * K];        // hi of (c[i0], c[i1]) as an fp16 pair
   __shared__ uint32_t tabl[K * K];        // lo of the same
-  __shared__ __attribute__((aligned(16))) uint32_t pqt[NW][PQ][CS];        // [pair quad][token]
-  __shared__ __attribute__((aligned(16))) uint32_t awt[NW][2][16 * MT][CS];  // A words [hi/lo][row][token]
+  // per wave: pair bytes [pair quad][token], then fp16 weights
+  // [hi/lo][head][token] with row G = 0; reused for the waves' slabs at the end
+  constexpr int SW = CS * (PQ + 2 * (G + 1));
+  __shared__ __attribute__((aligned(16))) uint32_t stage[NW][SW];
   __shared__ float scs[NW][8 * MT];       // per-head factor read by lane-dependent head
   __shared__ float redm[NW][G];
   __shared__ float reds[NW][G];
@@ -355,6 +356,9 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(PartArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = lane_id();
   const int q = l >> 4, pn = l & 15;      // MFMA lane coordinates
+  uint32_t *const pqt = &stage[w][0];                 // [PQ][CS]
+  uint32_t *const awh = &stage[w][PQ * CS];           // [G + 1][CS]
+  uint32_t *const awl = &stage[w][(PQ + G + 1) * CS]; // [G + 1][CS]
 
   const int64_t t_begin = (int64_t)split * a.tokens_per_split;
   int64_t t_end = t_begin + a.tokens_per_split;
@@ -397,12 +401,8 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(PartArgs a) {
     tabh[e] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
     tabl[e] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
   }
-  if constexpr (PR > 0) {
-    for (int i = tid; i < NW * 2 * PR * CS; i += kAttThreads) {
-      const int col = i % CS, r = (i / CS) % PR, hl = (i / (CS * PR)) % 2, ww = i / (CS * PR * 2);
-      awt[ww][hl][2 * G + r][col] = 0u;
-    }
-  }
+  for (int i = tid; i < NW * 2 * CS; i += kAttThreads)
+    stage[i / (2 * CS)][PQ * CS + (((i / CS) % 2) * (G + 1) + G) * CS + i % CS] = 0u;
   if (tid < NW * 8 * MT) scs[tid / (8 * MT)][tid % (8 * MT)] = 1.0f;
   __syncthreads();
 
@@ -442,11 +442,8 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(PartArgs a) {
       const float wgt = e * n;
       const _Float16 hi = (_Float16)wgt;
       const _Float16 lo = (_Float16)(wgt - (float)hi);
-      const uint32_t hb = __builtin_bit_cast(uint16_t, hi), lb = __builtin_bit_cast(uint16_t, lo);
-      awt[w][0][2 * g][l] = hb;
-      awt[w][0][2 * g + 1][l] = hb << 16;
-      awt[w][1][2 * g][l] = lb;
-      awt[w][1][2 * g + 1][l] = lb << 16;
+      awh[g * CS + l] = __builtin_bit_cast(uint16_t, hi);
+      awl[g * CS + l] = __builtin_bit_cast(uint16_t, lo);
     }
     if (l == 0) {
 #pragma unroll
@@ -469,7 +466,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(PartArgs a) {
           const uint32_t y = sh >= 0 ? x << sh : x >> -sh;
           pb |= y & (0x03030303u << (2 * p + PS));
         }
-        pqt[w][4 * j + o][l] = pb;
+        pqt[(4 * j + o) * CS + l] = pb;
       }
     }
     if (c0 + kChunk * NW < n_tok) load_chunk(c0 + kChunk * NW);
@@ -488,33 +485,58 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(PartArgs a) {
         acc[mt][j][3] *= f1;
       }
     }
-#pragma unroll 1
+    // Per 16-token step: every LDS read of the step first (A rows, pair
+    // bytes of all groups, then all table entries), then the MFMAs with the
+    // groups interleaved so that no product waits on the previous one.
+#pragma unroll
     for (int st = 0; st < kChunk / 16; ++st) {
       const int tb = 16 * st + 4 * q;     // this lane's four tokens
-      half8 ah[MT], al[MT];
+      u32x4 xh[MT], xl[MT], pv[NG];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        ah[mt] = __builtin_bit_cast(half8, *(const u32x4 *)&awt[w][0][16 * mt + pn][tb]);
-        al[mt] = __builtin_bit_cast(half8, *(const u32x4 *)&awt[w][1][16 * mt + pn][tb]);
+        // A row 16 mt + pn is head (16 mt + pn) / 2 on its parity's half of
+        // each k pair (rows past the heads read the zero row)
+        const int hr = (16 * mt + pn) >> 1;
+        const int row = hr < G ? hr : G;
+        xh[mt] = *(const u32x4 *)&awh[row * CS + tb];
+        xl[mt] = *(const u32x4 *)&awl[row * CS + tb];
       }
 #pragma unroll
+      for (int j = 0; j < NG; ++j) pv[j] = *(const u32x4 *)&pqt[(4 * j + (pn & 3)) * CS + tb];
+      u32x4 bh[NG], bl[NG];
+#pragma unroll
       for (int j = 0; j < NG; ++j) {
-        const u32x4 pv = *(const u32x4 *)&pqt[w][4 * j + (pn & 3)][tb];
-        u32x4 bh, bl;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const uint32_t pb = __builtin_amdgcn_ubfe(pv[t], 8 * (pn >> 2), 8);
+          const uint32_t pb = __builtin_amdgcn_ubfe(pv[j][t], 8 * (pn >> 2), 8);
           const uint32_t off = PS == 2 ? pb : pb << 2;          // byte offset into the tables
-          bh[t] = *(const uint32_t *)((const char *)tabh + off);
-          bl[t] = *(const uint32_t *)((const char *)tabl + off);
+          bh[j][t] = *(const uint32_t *)((const char *)tabh + off);
+          bl[j][t] = *(const uint32_t *)((const char *)tabl + off);
         }
-        const half8 bhh = __builtin_bit_cast(half8, bh), bll = __builtin_bit_cast(half8, bl);
+      }
+      half8 ah[MT], al[MT];
+      const int sh = 16 * (pn & 1);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[mt], bhh, acc[mt][j], 0, 0, 0);
-          acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[mt], bll, acc[mt][j], 0, 0, 0);
-          acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[mt], bhh, acc[mt][j], 0, 0, 0);
+      for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          xh[mt][i] <<= sh;
+          xl[mt][i] <<= sh;
         }
+        ah[mt] = __builtin_bit_cast(half8, xh[mt]);
+        al[mt] = __builtin_bit_cast(half8, xl[mt]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int j = 0; j < NG; ++j)
+          acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[mt], __builtin_bit_cast(half8, bh[j]), acc[mt][j], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < NG; ++j)
+          acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[mt], __builtin_bit_cast(half8, bl[j]), acc[mt][j], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < NG; ++j)
+          acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[mt], __builtin_bit_cast(half8, bh[j]), acc[mt][j], 0, 0, 0);
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -540,8 +562,8 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(PartArgs a) {
   }
   // each wave leaves its rescaled share in its own slab (the staging
   // memory, free now), then every thread sums the slabs for its outputs
-  float *slab = (float *)&awt[0][0][0][0];                // [NW][G][D]
-  static_assert(NW * G * D <= NW * 2 * 16 * MT * CS, "slab fits");
+  float *slab = (float *)&stage[0][0];                    // [NW][G][D]
+  static_assert(G * D <= SW, "slab fits");
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
