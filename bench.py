@@ -152,9 +152,18 @@ def decode_workload(torch, tq, args, device):
     # Timed beside the step, not in it: the attention output softmax(l) . V
     # straight from the packed values, on the step's logits.
     attn = torch.empty((1, qheads, d), dtype=torch.float32, device=device)
+    # The decode step with append: the new key of every head (here token
+    # seq - 1 again, so the cache is unchanged) quantised into the cache by the
+    # logit call, then logits over all seq tokens.
+    x_new = k.view(heads, seq, d)[:, seq - 1].contiguous().view(1, heads, d)
+    logits2 = torch.empty_like(logits)
     extras = {"attn_output": (lambda: qv.attn_output(logits, cv, heads, seq, out=attn),
                               n * rb_v + qheads * seq * 4 + qheads * d * 4, "attend_mfma_kernel",
-                              ["attend.hip", "tq_device.h"])}
+                              ["attend.hip", "tq_device.h"]),
+              "append_attn_logits": (lambda: qk.append_attn_logits(x_new, q, ck, heads, seq - 1, scale,
+                                                                   row_tokens=seq, out=logits2),
+                                     n * (rb_k + 4 * (qheads // heads)) + qheads * d * 2 + heads * (2 * d + rb_k),
+                                     "logit_kernel", ["logits.hip", "tq_device.h"])}
     return calls, work, cfg, n, extras
 
 

@@ -22,7 +22,7 @@
  *     hipStream_t passed as void*, NULL = the null stream).  Launch errors
  *     return TQ_ERR_HIP; faults inside a kernel surface at the caller's next
  *     synchronisation, as with any HIP launch.
- *   - tq_attn_logits needs device scratch memory (query tables, partial top-k
+ *   - tq_attn_logits (and tq_append_attn_logits) needs device scratch memory (query tables, partial top-k
  *     lists).  The library keeps one scratch buffer per (device, stream) pair
  *     between calls: the first call on a stream, or a call that needs more,
  *     synchronises that stream and allocates with hipMalloc; the buffer lives
@@ -155,6 +155,27 @@ tq_status tq_attn_logits(const tq_params *p, const void *q, int32_t q_dtype, int
                          int32_t n_q_heads, int32_t n_kv_heads, const tq_packed *k,
                          int64_t row_tokens, int64_t seq_len, float scale, float *logits,
                          int32_t topk, int32_t *topk_idx, void *stream);
+
+/* Decode step with append: quantise one new key per (batch, kv head) stream
+ * into the cache at token pos, then form the logits over tokens 0..pos of
+ * every stream (quantisation on every cache update, page section
+ * "TurboQuant 구현 방법"; the key is quantised exactly as by tq_quantize_kv,
+ * stages "1단계" and "2단계"; logits as tq_attn_logits).  The append runs
+ * inside the logit call's first launch, so the step costs no extra launch.
+ *   x_new        device [batch][n_kv_heads][d], x_dtype TQ_F32 or TQ_BF16
+ *   k            packed keys laid out [batch][n_kv_heads][row_tokens]; token
+ *                pos of every stream is overwritten, the other rows are only
+ *                read (tokens 0..pos-1 must already hold packed keys)
+ *   pos          0 <= pos < row_tokens
+ *   logits       device fp32 [batch][n_q_heads][pos + 1]
+ * The new key is quantised in fp64 from the fp32 matrices (the inner-product
+ * mode needs p->qjl_rot).  Supported: as dense tq_attn_logits (d in {128,
+ * 256}, up to 16 query heads per KV head).  batch == 0 is a no-op.
+ * Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED, TQ_ERR_HIP. */
+tq_status tq_append_attn_logits(const tq_params *p, const void *x_new, int32_t x_dtype,
+                                const void *q, int32_t q_dtype, int32_t batch, int32_t n_q_heads,
+                                int32_t n_kv_heads, const tq_packed *k, int64_t row_tokens,
+                                int64_t pos, float scale, float *logits, void *stream);
 
 /* Decode attention output straight from packed values (page: the KV cache
  * holds keys and values, section "TurboQuant란 무엇인가요?", and attention runs

@@ -34,7 +34,7 @@ KIND_S = 1
 KIND_M = 2
 
 EXPORTED = ["tq_make_codebook", "tq_make_rotation", "tq_quantize_kv", "tq_attn_logits",
-            "tq_attn_output", "tq_dequantize", "tq_status_string"]
+            "tq_append_attn_logits", "tq_attn_output", "tq_dequantize", "tq_status_string"]
 
 
 class TQError(RuntimeError):
@@ -65,13 +65,15 @@ def _load():
                                    i64, vp]
     lib.tq_attn_logits.argtypes = [ctypes.POINTER(Params), vp, i32, i32, i32, i32,
                                    ctypes.POINTER(Packed), i64, i64, f32, vp, i32, vp, vp]
+    lib.tq_append_attn_logits.argtypes = [ctypes.POINTER(Params), vp, i32, vp, i32, i32, i32, i32,
+                                          ctypes.POINTER(Packed), i64, i64, f32, vp, vp]
     lib.tq_attn_output.argtypes = [ctypes.POINTER(Params), vp, i32, i32, i32, ctypes.POINTER(Packed),
                                    i64, i64, vp, i32, vp]
     lib.tq_dequantize.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(Packed), i64, vp, i32, vp]
     lib.tq_status_string.argtypes = [i32]
     lib.tq_status_string.restype = ctypes.c_char_p
     for name in ("tq_make_codebook", "tq_make_rotation", "tq_quantize_kv", "tq_attn_logits",
-                 "tq_attn_output", "tq_dequantize"):
+                 "tq_append_attn_logits", "tq_attn_output", "tq_dequantize"):
         getattr(lib, name).restype = i32
     return lib
 
@@ -217,6 +219,22 @@ class Quantizer:
                                 row_tokens, seq_len, float(scale), ctypes.c_void_p(out.data_ptr()),
                                 0, None, _stream_ptr(self.device))
         _check(st, "tq_attn_logits")
+        return out
+
+    def append_attn_logits(self, x_new, q, cache, n_kv_heads, pos, scale, row_tokens=None, out=None):
+        """Quantise x_new [batch, n_kv_heads, d] into token ``pos`` of every stream of
+        ``cache`` and return the logits [batch, n_q_heads, pos + 1] (fp32)."""
+        torch = _torch()
+        bsz, hq, _ = q.shape
+        if row_tokens is None:            # the cache split evenly over the streams
+            row_tokens = cache.capacity // max(bsz * n_kv_heads, 1)
+        if out is None:
+            out = torch.empty((bsz, hq, pos + 1), dtype=torch.float32, device=self.device)
+        st = LIB.tq_append_attn_logits(ctypes.byref(self._params), ctypes.c_void_p(x_new.data_ptr()),
+                                       _dtype_code(x_new), ctypes.c_void_p(q.data_ptr()), _dtype_code(q),
+                                       bsz, hq, n_kv_heads, ctypes.byref(cache.struct()), row_tokens, pos,
+                                       float(scale), ctypes.c_void_p(out.data_ptr()), _stream_ptr(self.device))
+        _check(st, "tq_append_attn_logits")
         return out
 
     def search(self, q, cache, n_kv_heads, seq_len, topk, scale=1.0, row_tokens=None):

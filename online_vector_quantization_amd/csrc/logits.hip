@@ -43,6 +43,15 @@ struct PrepArgs {
   const float *centroids;
   int8_t *table;   // [stream][row_tile][chunk][64 lanes][16 bytes]
   float *consts;   // [stream][group][4]
+  // decode-time append (x_new == nullptr: none): one new key per stream,
+  // written at token pos of the stream's rows
+  const void *x_new;       // [stream][D]
+  bool x_f32;
+  const float *boundaries;
+  const float *m_mat;      // M = S Pi^T (PROD)
+  uint8_t *codes_out;
+  uint16_t *norm_out, *rnorm_out;
+  int64_t row_tokens, pos;
 };
 
 template <int LB>
@@ -86,6 +95,106 @@ __device__ __forceinline__ float xor_lanes(float v, int off) {
   return __shfl_xor(v, off, 64);
 }
 
+// Decode-time append: quantise the new key of one stream and write its
+// packed row at token pos, inside the prep launch so that the streaming
+// kernel that follows reads it (page "TurboQuant 설명 ...": quantisation on
+// every cache update, section "TurboQuant 구현 방법"; stage 1 and the QJL
+// stage, sections "1단계" and "2단계").  One vector per workgroup, in fp64
+// from the fp32 matrices: n = ||x|| (sum of exact squares), u = Pi x / n,
+// idx_j = #{k : u_j >= t_k} (ties go up), and in inner-product mode the
+// rotated residual r = u - c[idx] (same norm as u - Pi^T c[idx]), gamma =
+// ||r||, sign_i = [(M r)_i >= 0]; a zero vector keeps the middle index, all
+// signs 1 and gamma = 0.  Rows of Pi and M are read by RL consecutive lanes,
+// as in the query projection.
+__device__ __forceinline__ double shfl_xor_f64(double v, int off) {
+  return __shfl_xor(v, off, 64);
+}
+
+template <int D, int LB, bool PROD>
+__device__ __forceinline__ void append_key(const PrepArgs &a, int stream) {
+  constexpr int NT = prep_threads<D>();
+  constexpr int RL = NT / D;                // lanes per matrix row
+  constexpr int NP = D / 4 / RL;            // 16-byte pieces per lane
+  constexpr int K = 1 << LB;
+  constexpr int RBITS = LB + (PROD ? 1 : 0);
+  __shared__ __attribute__((aligned(16))) float xs[D];
+  __shared__ double rs[D];
+  __shared__ int rec[D];
+  __shared__ double nrm[2];
+  const int tid = threadIdx.x;
+  const int j = tid / RL, pl = tid % RL;
+  const int l = lane_id();
+  const f32x4 *prow = (const f32x4 *)(a.pi + (size_t)j * D);
+  if (tid < D) {
+    const int64_t off = (int64_t)stream * D + tid;
+    xs[tid] = a.x_f32 ? ((const float *)a.x_new)[off] : bf16_to_f32(((const uint16_t *)a.x_new)[off]);
+  }
+  __syncthreads();
+  if (tid < 64) {                           // ||x||^2: exact squares, fp64 sums
+    double s2 = 0.0;
+    for (int k = l; k < D; k += 64) s2 = fma((double)xs[k], (double)xs[k], s2);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s2 += shfl_xor_f64(s2, off);
+    if (l == 0) nrm[0] = sqrt(s2);
+  }
+  double y = 0.0;
+#pragma unroll 4
+  for (int i = 0; i < NP; ++i) {
+    const int k0 = 4 * (pl + RL * i);
+    const f32x4 m4 = prow[pl + RL * i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y = fma((double)m4[e], (double)xs[k0 + e], y);
+  }
+#pragma unroll
+  for (int off = 1; off < RL; off <<= 1) y += shfl_xor_f64(y, off);
+  __syncthreads();
+  const double n = nrm[0];
+  const double u = n > 0.0 ? y / n : 0.0;
+  int idx = 0;
+#pragma unroll
+  for (int k = 0; k < K - 1; ++k) idx += u >= (double)a.boundaries[k] ? 1 : 0;
+  if (pl == 0) {
+    rec[j] = idx;
+    rs[j] = u - (double)a.centroids[idx];
+  }
+  __syncthreads();
+  if constexpr (PROD) {
+    if (tid < 64) {
+      double g2 = 0.0;
+      for (int k = l; k < D; k += 64) g2 = fma(rs[k], rs[k], g2);
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) g2 += shfl_xor_f64(g2, off);
+      if (l == 0) nrm[1] = sqrt(g2);
+    }
+    const f32x4 *mrow = (const f32x4 *)(a.m_mat + (size_t)j * D);
+    double z = 0.0;
+#pragma unroll 4
+    for (int i = 0; i < NP; ++i) {
+      const int k0 = 4 * (pl + RL * i);
+      const f32x4 m4 = mrow[pl + RL * i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) z = fma((double)m4[e], rs[k0 + e], z);
+    }
+#pragma unroll
+    for (int off = 1; off < RL; off <<= 1) z += shfl_xor_f64(z, off);
+    if (pl == 0 && (n == 0.0 || z >= 0.0)) rec[j] |= 1 << LB;
+    __syncthreads();
+  }
+  // bit planes: word p of group g holds bit p of the records 32 g .. 32 g + 31
+  const int64_t row = (int64_t)stream * a.row_tokens + a.pos;
+  if (tid < (D / 32) * RBITS) {
+    const int g = tid / RBITS, p = tid % RBITS;
+    uint32_t word = 0;
+#pragma unroll 8
+    for (int i = 0; i < 32; ++i) word |= (uint32_t)((rec[32 * g + i] >> p) & 1) << i;
+    ((uint32_t *)(a.codes_out + row * (RBITS * D / 8)))[tid] = word;
+  }
+  if (tid == 0) {
+    a.norm_out[row] = f64_to_f16_bits(n);
+    if constexpr (PROD) a.rnorm_out[row] = f64_to_f16_bits(n > 0.0 ? nrm[1] : 0.0);
+  }
+}
+
 template <int D, int LB, bool PROD>
 __global__ __launch_bounds__(prep_threads<D>()) void logit_prep_kernel(PrepArgs a) {
   using L = LLayout<D, LB, PROD>;
@@ -103,7 +212,11 @@ __global__ __launch_bounds__(prep_threads<D>()) void logit_prep_kernel(PrepArgs 
 
   const int stream = blockIdx.x;
   const int rt = blockIdx.y;
-  const int part = blockIdx.z;              // 0: MSE planes, 1: QJL signs
+  const int part = blockIdx.z;              // 0: MSE planes, 1: QJL signs, last: append
+  if (part == (PROD ? 2 : 1)) {             // uniform over the workgroup
+    if (rt == 0) append_key<D, LB, PROD>(a, stream);
+    return;
+  }
   const int b = stream / a.n_kv_heads;
   const int kvh = stream % a.n_kv_heads;
   const int tid = threadIdx.x;
@@ -498,7 +611,17 @@ hipError_t launch_t(const tqi::LogitArgs &a, hipStream_t s) {
   pa.centroids = a.centroids;
   pa.table = (int8_t *)ws;
   pa.consts = (float *)((char *)ws + table_bytes);
-  hipLaunchKernelGGL((logit_prep_kernel<D, LB, PROD>), dim3(n_streams, rts, PROD ? 2 : 1),
+  pa.x_new = a.x_new;
+  pa.x_f32 = a.x_f32;
+  pa.boundaries = a.boundaries;
+  pa.m_mat = a.m_mat;
+  pa.codes_out = a.codes_out;
+  pa.norm_out = a.norm_out;
+  pa.rnorm_out = a.rnorm_out;
+  pa.row_tokens = a.row_tokens;
+  pa.pos = a.pos;
+  const int parts = (PROD ? 2 : 1) + (a.x_new != nullptr ? 1 : 0);
+  hipLaunchKernelGGL((logit_prep_kernel<D, LB, PROD>), dim3(n_streams, rts, parts),
                      dim3(prep_threads<D>()), 0,
                      s, pa);
   e = hipGetLastError();

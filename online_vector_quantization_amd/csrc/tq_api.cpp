@@ -170,6 +170,54 @@ extern "C" tq_status tq_attn_logits(const tq_params *p, const void *q, int32_t q
   return hip_status(e);
 }
 
+extern "C" tq_status tq_append_attn_logits(const tq_params *p, const void *x_new, int32_t x_dtype,
+                                           const void *q, int32_t q_dtype, int32_t batch,
+                                           int32_t n_q_heads, int32_t n_kv_heads, const tq_packed *k,
+                                           int64_t row_tokens, int64_t pos, float scale, float *logits,
+                                           void *stream) {
+  tq_status st = check_params(p);
+  if (st != TQ_OK) return st;
+  const bool prod = p->mode == TQ_MODE_PROD;
+  if (k == nullptr || batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0) return TQ_ERR_INVALID;
+  if (n_q_heads % n_kv_heads != 0) return TQ_ERR_INVALID;
+  if ((q_dtype != TQ_F32 && q_dtype != TQ_BF16) || (x_dtype != TQ_F32 && x_dtype != TQ_BF16))
+    return TQ_ERR_INVALID;
+  if (pos < 0 || pos >= row_tokens) return TQ_ERR_INVALID;
+  if (batch == 0) return TQ_OK;
+  if (x_new == nullptr || q == nullptr || logits == nullptr || k->codes == nullptr || k->norm == nullptr)
+    return TQ_ERR_INVALID;
+  if (prod && (p->qjl == nullptr || p->qjl_rot == nullptr || k->rnorm == nullptr)) return TQ_ERR_INVALID;
+  if ((uintptr_t)k->codes & 3u) return TQ_ERR_UNSUPPORTED;
+  tqi::LogitArgs a;
+  a.q = q;
+  a.q_f32 = q_dtype == TQ_F32;
+  a.batch = batch;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.pi = p->pi;
+  a.s_mat = p->qjl;
+  a.centroids = p->centroids;
+  a.codes = k->codes;
+  a.norm = k->norm;
+  a.rnorm = k->rnorm;
+  a.row_tokens = row_tokens;
+  a.seq_len = pos + 1;
+  a.scale = scale;
+  a.logits = logits;
+  a.x_new = x_new;
+  a.x_f32 = x_dtype == TQ_F32;
+  a.boundaries = p->boundaries;
+  a.m_mat = p->qjl_rot;
+  a.codes_out = k->codes;
+  a.norm_out = k->norm;
+  a.rnorm_out = k->rnorm;
+  a.pos = pos;
+  bool ok = false;
+  const hipError_t e = tqi::launch_logits(p->d, lloyd_bits(p), prod, a, (hipStream_t)stream, &ok);
+  if (!ok) return TQ_ERR_UNSUPPORTED;
+  return hip_status(e);
+}
+
 extern "C" tq_status tq_attn_output(const tq_params *p, const float *logits, int32_t batch,
                                     int32_t n_q_heads, int32_t n_kv_heads, const tq_packed *v,
                                     int64_t row_tokens, int64_t seq_len, void *out, int32_t out_dtype,

@@ -38,6 +38,16 @@ struct LogitArgs {
   int64_t row_tokens, seq_len;
   float scale;
   float *logits;
+  // decode-time append (x_new == nullptr: none): the new key of every stream
+  // is quantised into token pos = seq_len - 1 before the logits are formed
+  const void *x_new = nullptr;
+  bool x_f32 = false;
+  const float *boundaries = nullptr;
+  const float *m_mat = nullptr;
+  uint8_t *codes_out = nullptr;
+  uint16_t *norm_out = nullptr;
+  uint16_t *rnorm_out = nullptr;
+  int64_t pos = 0;
 };
 
 hipError_t launch_logits(int d, int lbits, bool prod, const LogitArgs &a, hipStream_t s,

@@ -30,10 +30,12 @@ Modules
              dequantise, attention logits, top-k search, recall.
   attention  decode attention output softmax(l) . V_hat over a quantised
              value cache.
+  decode     decode step with append: quantise the new key of every stream
+             into the cache at a token position, logits over the prefix.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against closed forms,
 textbook special cases, brute force or invariants.  Points the page leaves
 open are read as stated in each module's docstring.
 """
 
-from . import splitmix, rotation, codebook, quantizer, attention  # noqa: F401
+from . import splitmix, rotation, codebook, quantizer, attention, decode  # noqa: F401

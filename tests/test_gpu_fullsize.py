@@ -118,6 +118,25 @@ def test_config2_decode_full(tq):
         want = oqz.logits_rotated(qq, refk["codes"][sl], refk["norm"][sl], otk.pi, otk.c, oqz.MODE_PROD,
                                   scale, rnorm=refk["rnorm"][sl], s_mat=otk.s)
         check_logits(out[h * group:(h + 1) * group], want, scale, refk["norm"][sl], qq)
+    # decode step with append: the logit call re-quantises token seq - 1 of
+    # every head from its bf16 key and forms the logits over the whole cache
+    xl = np.ascontiguousarray(kb.reshape(heads, seq, d)[:, seq - 1])
+    nref = otk.quantize(bf16_to_f32(xl).astype(np.float64))
+    app = qk.append_attn_logits(_dev_bf16(xl).reshape(1, heads, d), _dev_bf16(qb), okc, heads, seq - 1, scale,
+                                row_tokens=seq).cpu().numpy()[0]
+    new_rows = np.arange(heads) * seq + seq - 1
+    gcodes = okc.codes.cpu().numpy()[new_rows]
+    check_codes(gcodes, nref, otk.lb, d, otk.t, oqz.MODE_PROD)
+    check_signs(gcodes, nref, otk.lb, d)
+    check_norms(okc.norm.cpu().numpy()[new_rows], nref)
+    check_rnorm(okc.rnorm.cpu().numpy()[new_rows], nref)
+    assert np.array_equal(app[:, :seq - 1], out[:, :seq - 1])     # same kernels on the same rows
+    for h in range(heads):
+        if np.array_equal(gcodes[h], nref["codes"][h]):
+            qq = q64[h * group:(h + 1) * group]
+            want = oqz.logits_rotated(qq, nref["codes"][h:h + 1], nref["norm"][h:h + 1], otk.pi, otk.c,
+                                      oqz.MODE_PROD, scale, rnorm=nref["rnorm"][h:h + 1], s_mat=otk.s)
+            check_logits(app[h * group:(h + 1) * group, seq - 1:], want, scale, nref["norm"][h:h + 1], qq)
     # dequantized values (bf16, as in the decode step, and fp32) on sampled rows
     ovc = cache_from_oracle(tq, refv, d, bits, oqz.MODE_MSE, DEV)
     rows = _sample_rows(n, 3000, 21)

@@ -341,3 +341,94 @@ def test_attn_output_empty_and_unsupported(tq):
     cp = cache_from_oracle(tq, refp, d, bits, oqz.MODE_PROD, DEV)
     with pytest.raises(tq.TQError):
         qp.attn_output(torch.zeros((1, 4, 64), device=DEV), cp, n_kv_heads=1, seq_len=64)
+
+
+APPEND_CASES = [
+    # d, bits, mode, batch, kv heads, group, row_tokens, pos, x dtype, q dtype
+    (128, 3, "prod", 1, 8, 4, 600, 437, "bf16", "bf16"),
+    (128, 3, "mse", 2, 2, 4, 300, 0, "f32", "f32"),
+    (128, 5, "prod", 1, 2, 2, 1000, 999, "f32", "bf16"),
+    (128, 2, "prod", 2, 1, 16, 260, 259, "bf16", "f32"),
+    (128, 1, "mse", 1, 3, 1, 70, 33, "bf16", "bf16"),
+    (256, 3, "prod", 1, 1, 4, 513, 512, "bf16", "f32"),
+    (256, 2, "mse", 1, 2, 8, 257, 100, "f32", "f32"),
+]
+
+
+@pytest.mark.parametrize("d,bits,mode,bsz,hkv,group,rows,pos,xdtype,qdtype", APPEND_CASES)
+def test_append_attn_logits_parity(tq, d, bits, mode, bsz, hkv, group, rows, pos, xdtype, qdtype):
+    """New keys quantised into token pos by the logit call: the row against the
+    oracle's quantiser, every other row untouched, logits over tokens 0..pos."""
+    from oracle import decode as odec
+    ot, mcode, keys, q64, qt, ref = _gqa_case(d, bits, mode, bsz, hkv, group, rows, qdtype, row_tokens=rows)
+    rng = np.random.default_rng(pos + 7 * d)
+    x = rng.standard_normal((bsz, hkv, d)) * np.exp(rng.standard_normal((1, hkv, d)))
+    x[0, hkv - 1] = 0.0                                   # a zero key
+    if xdtype == "bf16":
+        xb = bf16_bits(x.astype(np.float32))
+        x64 = bf16_to_f32(xb).astype(np.float64)
+        xt = dev_bf16(xb, DEV)
+    else:
+        x64 = x.astype(np.float32).astype(np.float64)
+        xt = torch.from_numpy(x64.astype(np.float32)).to(DEV)
+    qz = tq.Quantizer(d, bits, mcode, seed=0, device=DEV)
+    cache = cache_from_oracle(tq, ref, d, bits, mcode, DEV)
+    before = {n: getattr(cache, n).cpu().numpy().copy() for n in ("codes", "norm", "rnorm")
+              if getattr(cache, n) is not None}
+    scale = 1.0 / np.sqrt(d)
+    out = qz.append_attn_logits(xt, qt, cache, n_kv_heads=hkv, pos=pos, scale=scale, row_tokens=rows)
+    torch.cuda.synchronize()
+    assert out.shape == (bsz, hkv * group, pos + 1)
+    out = out.cpu().numpy()
+    after = {n: getattr(cache, n).cpu().numpy() for n in before}
+    # every row but token pos of each stream is unchanged
+    keep = np.ones(bsz * hkv * rows, bool)
+    keep[np.arange(bsz * hkv) * rows + pos] = False
+    for n in before:
+        assert np.array_equal(after[n][keep], before[n][keep]), n
+    # the appended rows follow the quantiser's rules
+    oc = {"codes": ref["codes"].reshape(bsz, hkv, rows, -1), "norm": ref["norm"].reshape(bsz, hkv, rows)}
+    if mcode == oqz.MODE_PROD:
+        oc["rnorm"] = ref["rnorm"].reshape(bsz, hkv, rows)
+    ocache, want, nref = odec.append_step(oc, x64, pos, q64, ot.pi, ot.c, ot.t, mcode, scale, s_mat=ot.s)
+    new_rows = np.arange(bsz * hkv) * rows + pos
+    gcodes = after["codes"][new_rows]
+    check_codes(gcodes, nref, ot.lb, d, ot.t, mcode)
+    check_norms(after["norm"][new_rows], nref)
+    if mcode == oqz.MODE_PROD:
+        check_signs(gcodes, nref, ot.lb, d)
+        check_rnorm(after["rnorm"][new_rows], nref)
+        assert after["rnorm"][new_rows][hkv - 1] == 0
+    # logits on identical codes: tokens before pos always, token pos where the
+    # appended record equals the oracle's
+    same = np.all(gcodes == nref["codes"], axis=1)
+    if mcode == oqz.MODE_PROD:
+        same &= after["rnorm"][new_rows].view(np.uint16) == nref["rnorm"]
+    for b in range(bsz):
+        for h in range(hkv):
+            qq = q64[b, h * group:(h + 1) * group]
+            norm = ocache["norm"][b, h, :pos + 1]
+            cols = pos + 1 if same[b * hkv + h] else pos
+            gl = out[b, h * group:(h + 1) * group, :cols]
+            live = norm[:cols] != 0                       # zero keys: logit exactly 0
+            assert np.all(gl[:, ~live] == 0.0)
+            if live.any():
+                check_logits(gl[:, live], want[b, h * group:(h + 1) * group, :cols][:, live], scale,
+                             norm[:cols][live], qq)
+            if not x64[b, h].any():
+                assert np.all(out[b, h * group:(h + 1) * group, pos] == 0.0)
+
+
+def test_append_attn_logits_bounds(tq):
+    d, bits = 128, 3
+    ot = OracleTables(d, bits, oqz.MODE_PROD)
+    ref = ot.quantize(np.random.default_rng(4).standard_normal((2 * 50, d)))
+    qz = tq.Quantizer(d, bits, oqz.MODE_PROD, seed=0, device=DEV)
+    cache = cache_from_oracle(tq, ref, d, bits, oqz.MODE_PROD, DEV)
+    x = torch.zeros((1, 2, d), device=DEV)
+    q = torch.zeros((1, 8, d), device=DEV)
+    for bad in (50, -1):
+        with pytest.raises(tq.TQError):
+            qz.append_attn_logits(x, q, cache, n_kv_heads=2, pos=bad, scale=1.0, row_tokens=50)
+    out = qz.append_attn_logits(x[:0], q[:0], cache, n_kv_heads=2, pos=3, scale=1.0, row_tokens=50)
+    assert out.shape == (0, 8, 4)
