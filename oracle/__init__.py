@@ -32,10 +32,13 @@ Modules
              value cache.
   decode     decode step with append: quantise the new key of every stream
              into the cache at a token position, logits over the prefix.
+  polar      PolarQuant variant of stage 1: recursive polar transform of the
+             rotated unit vector, Lloyd-Max codebooks of the angle laws,
+             packing and reconstruction.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against closed forms,
 textbook special cases, brute force or invariants.  Points the page leaves
 open are read as stated in each module's docstring.
 """
 
-from . import splitmix, rotation, codebook, quantizer, attention, decode  # noqa: F401
+from . import splitmix, rotation, codebook, quantizer, attention, decode, polar  # noqa: F401
