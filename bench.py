@@ -164,6 +164,15 @@ def decode_workload(torch, tq, args, device):
                                                                    row_tokens=seq, out=logits2),
                                      n * (rb_k + 4 * (qheads // heads)) + qheads * d * 2 + heads * (2 * d + rb_k),
                                      "logit_kernel", ["logits.hip", "tq_device.h"])}
+    # The PolarQuant variant of stage 1 on the same values (3 bits per coordinate).
+    qp = tq.Quantizer(d, 3, tq.MODE_POLAR, seed=0, device=device)
+    cp = qp.new_cache(n)
+    vhat_p = torch.empty((n, d), dtype=torch.bfloat16, device=device)
+    rb_p = 3 * d // 8 + 2
+    extras["polar_quantize"] = (lambda: qp.quantize(v, out=cp), n * (2 * d + rb_p), "quantize_polar_kernel",
+                                ["quantize.hip", "tq_device.h"])
+    extras["polar_dequantize"] = (lambda: qp.dequantize(cp, n, out=vhat_p), n * (rb_p + 2 * d), "dequant_kernel",
+                                  ["dequant.hip", "tq_device.h"])
     return calls, work, cfg, n, extras
 
 

@@ -47,6 +47,26 @@
  *   A zero vector gets idx_j = 2^(b'-1), all sign bits 1 and gamma = 0.
  *   Reconstruction: x_hat = norm * (Pi^T c_hat + sqrt(pi/2)/d * rnorm * S^T s),
  *   s = 2*sign_bit - 1.  A row is b*d/8 + 2 (MSE) or b*d/8 + 4 (PROD) bytes.
+ *
+ * Polar format (mode TQ_MODE_POLAR, b = 3, d a power of two >= 64): the
+ * PolarQuant variant of stage 1 (page section "1단계": the unit vector is
+ * paired recursively into polar form).  y = Pi x / ||x||; level 1 turns the
+ * pairs (y_2i, y_2i+1) into angles phi_i = atan2(y_2i+1, y_2i) in [0, 2 pi),
+ * level l >= 2 the pairs of level-(l-1) radii (rho_2i, rho_2i+1) into angles
+ * psi_i = atan2(rho_2i+1, rho_2i) in [0, pi/2].  phi gets 4 bits: sector
+ * floor(16 phi / (2 pi)); psi gets 2 bits: #{k : psi >= t_k} against the 3
+ * boundaries of its level (tq_make_polar_codebook); an angle of a zero pair
+ * or block is 0.
+ *   codes : 3 d/8 bytes: the d/2 level-1 indices as 4 bit planes over groups
+ *           of 32 slots (group g, plane p at word 4 g + p), then the d/2 - 1
+ *           higher indices in level order (level 2 first) plus one zero slot
+ *           as 2 bit planes (group g, plane p at word d/16 + 2 g + p).
+ *   norm  : fp16 bits of ||x||_2 (no rnorm).
+ *   Reconstruction: y_hat from the centroid angles from the top (radius 1)
+ *   down, x_hat = norm * Pi^T y_hat; level-1 centroids are the sector
+ *   midpoints 2 pi (j + 1/2) / 16.
+ *   tq_params.centroids / boundaries hold the levels 2..log2(d) codebooks,
+ *   4 centroids and 3 boundaries per level (angles, fp32), level 2 first.
  */
 #ifndef TQ_H
 #define TQ_H
@@ -67,7 +87,7 @@ enum {
   TQ_ERR_HIP = -4             /* a HIP runtime call or launch failed           */
 };
 
-enum { TQ_MODE_MSE = 0, TQ_MODE_PROD = 1 };
+enum { TQ_MODE_MSE = 0, TQ_MODE_PROD = 1, TQ_MODE_POLAR = 2 };
 enum { TQ_F32 = 0, TQ_BF16 = 1 };
 enum { TQ_KIND_PI = 0, TQ_KIND_S = 1, TQ_KIND_M = 2 };
 
@@ -86,6 +106,19 @@ enum { TQ_KIND_PI = 0, TQ_KIND_S = 1, TQ_KIND_M = 2 };
  * Errors: TQ_ERR_INVALID (bad d/bits/NULL), TQ_ERR_NO_CONVERGENCE. */
 tq_status tq_make_codebook(int32_t d, int32_t bits, double *centroids, double *boundaries,
                            double *mse_per_coord);
+
+/* Angle codebooks of the polar format (page section "1단계": the angle laws
+ * are concentrated and known, so Lloyd-Max codebooks are precomputed).  At
+ * level l >= 2 an angle splits two radii spanning k = 2^(l-1) dimensions
+ * each; for a uniform point on the sphere sin^2 psi ~ Beta(k/2, k/2), density
+ * proportional to (sin psi cos psi)^(k-1) on [0, pi/2].  Host only, fp64:
+ * composite Gauss-Legendre quadrature and Lloyd iteration, returned exactly
+ * symmetric about pi/4.
+ *   d            a power of two >= 64
+ *   centroids    out, 4 (log2 d - 1) doubles: levels 2..log2 d, ascending
+ *   boundaries   out, 3 (log2 d - 1) doubles, midpoints of adjacent centroids
+ * Errors: TQ_ERR_INVALID, TQ_ERR_NO_CONVERGENCE. */
+tq_status tq_make_polar_codebook(int32_t d, double *centroids, double *boundaries);
 
 /* Seeded random matrices (page sections "1단계" and "2단계").  Host only, fp64,
  * row-major d x d written to `out`.
@@ -126,7 +159,8 @@ typedef struct tq_packed {
  *   x            device, n_vec rows of d elements (x_dtype TQ_F32 or
  *                TQ_BF16), consecutive rows x_row_stride elements apart
  *   out          packed arrays; vector i is written at index out_offset + i
- * Supported: d in {64,128} for both modes, d = 256 in MSE mode; b' <= 4.
+ * Supported: d in {64,128} for both modes, d = 256 in MSE mode; b' <= 4;
+ * polar mode with d = 128.
  * n_vec == 0 is a no-op.  Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED,
  * TQ_ERR_HIP. */
 tq_status tq_quantize_kv(const tq_params *p, const void *x, int32_t x_dtype, int64_t n_vec,
@@ -197,7 +231,7 @@ tq_status tq_attn_output(const tq_params *p, const float *logits, int32_t batch,
 
 /* Reconstruct n_vec vectors (page section "2단계": reconstructed vectors).
  *   out          device [n_vec][d], out_dtype TQ_F32 or TQ_BF16
- * Supported: d in {64, 128, 256} MSE, d in {64, 128} PROD.
+ * Supported: d in {64, 128, 256} MSE, d in {64, 128} PROD, d = 128 polar.
  * Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED, TQ_ERR_HIP. */
 tq_status tq_dequantize(const tq_params *p, const tq_packed *k, int64_t n_vec, void *out,
                         int32_t out_dtype, void *stream);

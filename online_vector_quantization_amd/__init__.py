@@ -27,13 +27,14 @@ TQ_ERR_NO_CONVERGENCE = -3
 TQ_ERR_HIP = -4
 MODE_MSE = 0
 MODE_PROD = 1
+MODE_POLAR = 2
 TQ_F32 = 0
 TQ_BF16 = 1
 KIND_PI = 0
 KIND_S = 1
 KIND_M = 2
 
-EXPORTED = ["tq_make_codebook", "tq_make_rotation", "tq_quantize_kv", "tq_attn_logits",
+EXPORTED = ["tq_make_codebook", "tq_make_polar_codebook", "tq_make_rotation", "tq_quantize_kv", "tq_attn_logits",
             "tq_append_attn_logits", "tq_attn_output", "tq_dequantize", "tq_status_string"]
 
 
@@ -60,6 +61,7 @@ def _load():
     lib = ctypes.CDLL(LIB_PATH)
     i32, i64, vp, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
     lib.tq_make_codebook.argtypes = [i32, i32, vp, vp, vp]
+    lib.tq_make_polar_codebook.argtypes = [i32, vp, vp]
     lib.tq_make_rotation.argtypes = [i32, ctypes.c_uint64, i32, vp]
     lib.tq_quantize_kv.argtypes = [ctypes.POINTER(Params), vp, i32, i64, i64, ctypes.POINTER(Packed),
                                    i64, vp]
@@ -72,7 +74,7 @@ def _load():
     lib.tq_dequantize.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(Packed), i64, vp, i32, vp]
     lib.tq_status_string.argtypes = [i32]
     lib.tq_status_string.restype = ctypes.c_char_p
-    for name in ("tq_make_codebook", "tq_make_rotation", "tq_quantize_kv", "tq_attn_logits",
+    for name in ("tq_make_codebook", "tq_make_polar_codebook", "tq_make_rotation", "tq_quantize_kv", "tq_attn_logits",
                  "tq_append_attn_logits", "tq_attn_output", "tq_dequantize"):
         getattr(lib, name).restype = i32
     return lib
@@ -92,6 +94,15 @@ def _check(status, what):
 
 def lloyd_bits(bits, mode):
     return bits if mode == MODE_MSE else bits - 1
+
+
+def make_polar_codebook(d):
+    """Angle codebooks of levels 2..log2(d) of the polar format: (centroids [L-1, 4], boundaries [L-1, 3])."""
+    nl = int(round(math.log2(d))) - 1
+    c = np.zeros(4 * nl)
+    t = np.zeros(3 * nl)
+    _check(LIB.tq_make_polar_codebook(d, c.ctypes.data, t.ctypes.data), "tq_make_polar_codebook")
+    return c.reshape(nl, 4), t.reshape(nl, 3)
 
 
 # ------------------------------------------------------------------ host math
@@ -171,8 +182,14 @@ class Quantizer:
         torch = _torch()
         self.d, self.bits, self.mode, self.seed = d, bits, mode, seed
         self.device = torch.device(device)
-        lb = lloyd_bits(bits, mode)
-        c, t, self.mse_per_coord = make_codebook(d, lb)
+        if mode == MODE_POLAR:
+            if bits != 3:
+                raise ValueError("the polar format has 3 bits per coordinate")
+            c2, t2 = make_polar_codebook(d)
+            c, t, self.mse_per_coord = c2.reshape(-1), t2.reshape(-1), None
+        else:
+            lb = lloyd_bits(bits, mode)
+            c, t, self.mse_per_coord = make_codebook(d, lb)
         self.centroids64, self.boundaries64 = c, t
         self.pi64 = make_rotation(d, seed, KIND_PI)
         f = dict(dtype=torch.float32, device=self.device)

@@ -49,21 +49,34 @@ __device__ void load_columns(const float *__restrict__ mat, int w, half8 (&hi)[D
 }
 
 // Raw inputs of one decoding thread (16 coordinates of one vector): the
-// 16-bit halves of its plane words, and for the first thread of a vector the
-// fp16 norm and residual norm.
+// 16-bit halves of its plane words (polar format: its level-1 group's four
+// plane words and the higher-level plane words), and for the first thread of
+// a vector the fp16 norm and residual norm.
 template <int NPL>
 struct DecodeRaw {
   uint32_t pw[NPL];
   uint32_t nrm, gam;
 };
 
-template <int D, int LB, bool PROD, bool OUT_F32>
+// Polar format (PolarQuant variant of stage 1, page section "1단계"):
+// levels, upper-level groups and the first slot of each higher level.
+template <int D>
+struct DPolar {
+  static constexpr int LV = D == 64 ? 6 : (D == 128 ? 7 : 8);
+  static constexpr int NGU = D / 64;
+  static constexpr int RB = 3 * D / 8;
+  static constexpr int NW = 4 + 2 * NGU;   // words a decoding thread reads
+  __host__ __device__ static constexpr int slot(int level) { return D / 2 - (D >> (level - 1)); }
+};
+
+template <int D, int LB, bool PROD, bool OUT_F32, bool POLAR = false>
 __global__ __launch_bounds__(DLayout<D>::NT) void dequant_kernel(tqi::DequantArgs a) {
   using L = DLayout<D>;
+  using PF = DPolar<D>;
   constexpr int K = 1 << LB;
   constexpr int PB = D / 8;
-  constexpr int NPL = LB + (PROD ? 1 : 0);  // planes per record (sign on top)
-  constexpr int RB = NPL * PB;
+  constexpr int NPL = POLAR ? PF::NW : LB + (PROD ? 1 : 0);  // words read per thread
+  constexpr int RB = POLAR ? PF::RB : NPL * PB;
   constexpr int TILE = 32 * L::PITCH;
   constexpr int OSZ = OUT_F32 ? 4 : 2;      // bytes per output element
   constexpr int OCH = 32 * D * OSZ / 16;    // 16-byte output chunks per tile
@@ -77,6 +90,10 @@ __global__ __launch_bounds__(DLayout<D>::NT) void dequant_kernel(tqi::DequantArg
   __shared__ __attribute__((aligned(16))) float vfac[2][32];
   __shared__ __attribute__((aligned(16))) uint8_t otile[32 * D * OSZ];
   __shared__ uint32_t ctab[K];
+  // polar: cos and sin of the level-1 sector midpoints and of the centroid
+  // angles of levels 2..LV
+  __shared__ float pc1[POLAR ? 16 : 1], ps1[POLAR ? 16 : 1];
+  __shared__ float pcu[POLAR ? PF::LV - 1 : 1][4], psu[POLAR ? PF::LV - 1 : 1][4];
 
   const int tid = threadIdx.x;
   const int w = tid / kWave;
@@ -90,7 +107,18 @@ __global__ __launch_bounds__(DLayout<D>::NT) void dequant_kernel(tqi::DequantArg
   load_columns<D>(a.pi, w, ph, pl);
   half8 sh[PROD ? L::KS : 1], sl[PROD ? L::KS : 1];
   if constexpr (PROD) load_columns<D>(a.s_mat, w, sh, sl);
-  if (tid < K) {
+  if constexpr (POLAR) {
+    if (tid < 16) {
+      const double ph = 2.0 * M_PI * (tid + 0.5) / 16.0;
+      pc1[tid] = (float)cos(ph);
+      ps1[tid] = (float)sin(ph);
+    } else if (tid < 16 + 4 * (PF::LV - 1)) {
+      const int i = tid - 16;
+      const double ps = (double)a.centroids[i];
+      pcu[i / 4][i % 4] = (float)cos(ps);
+      psu[i / 4][i % 4] = (float)sin(ps);
+    }
+  } else if (tid < K) {
     const float cv = a.centroids[tid] * kCenScale;
     const _Float16 hv = (_Float16)cv;
     const _Float16 lv = (_Float16)(cv - (float)hv);
@@ -113,9 +141,20 @@ __global__ __launch_bounds__(DLayout<D>::NT) void dequant_kernel(tqi::DequantArg
   auto load_raw = [&](int64_t tile, DecodeRaw<NPL> &r) {
     const int64_t gv = tile * 32 + dv;
     const uint32_t row = gv < a.n_vec ? (uint32_t)(gv * RB) : kNoStore;
+    if constexpr (POLAR) {
+      // the four level-1 plane words of group dc / 4, then the upper words
+      uint32_t w1[4], wu[2 * PF::NGU];
+      buf_load_words<4>(rc, row == kNoStore ? kNoStore : row + 16 * (dc >> 2), w1);
+      buf_load_words<2 * PF::NGU>(rc, row == kNoStore ? kNoStore : row + 4 * (D / 16), wu);
 #pragma unroll
-    for (int p = 0; p < NPL; ++p)
-      r.pw[p] = buf_load_u16(rc, row + 4 * ((dc >> 1) * NPL + p) + 2 * (dc & 1));
+      for (int p = 0; p < 4; ++p) r.pw[p] = w1[p];
+#pragma unroll
+      for (int i = 0; i < 2 * PF::NGU; ++i) r.pw[4 + i] = wu[i];
+    } else {
+#pragma unroll
+      for (int p = 0; p < NPL; ++p)
+        r.pw[p] = buf_load_u16(rc, row + 4 * ((dc >> 1) * NPL + p) + 2 * (dc & 1));
+    }
     const uint32_t sc = (gv < a.n_vec && dc == 0) ? (uint32_t)(2 * gv) : kNoStore;
     r.nrm = buf_load_u16(rn, sc);
     r.gam = PROD ? buf_load_u16(rg, sc) : 0u;
@@ -125,6 +164,60 @@ __global__ __launch_bounds__(DLayout<D>::NT) void dequant_kernel(tqi::DequantArg
   // 2^10), signs as exact fp16 +-1, and the per-vector factors.
   auto decode = [&](const DecodeRaw<NPL> &r) {
     half8 hv[2], lv[2], sv[2];
+    if constexpr (POLAR) {
+      // y_hat of coordinates [16 dc, 16 dc + 16): the product of the
+      // factors on the path from the root (radius 1) down to each pair
+      auto upper = [&](int level, int node) -> int {
+        const int sl = PF::slot(level) + node;
+        const int g = sl >> 5, b = sl & 31;
+        uint32_t w0 = r.pw[4], w1 = r.pw[5];
+#pragma unroll
+        for (int gg = 1; gg < PF::NGU; ++gg) {
+          w0 = g == gg ? r.pw[4 + 2 * gg] : w0;
+          w1 = g == gg ? r.pw[5 + 2 * gg] : w1;
+        }
+        return (int)(((w0 >> b) & 1u) | (((w1 >> b) & 1u) << 1));
+      };
+      float pf = 1.0f;
+#pragma unroll
+      for (int level = PF::LV; level >= 5; --level) {
+        const int node = dc >> (level - 4);            // node holding this thread
+        const int c = upper(level, node);
+        pf *= ((dc >> (level - 5)) & 1) ? psu[level - 2][c] : pcu[level - 2][c];
+      }
+      float r3[2], r2[4], r1[8];
+      {
+        const int c = upper(4, dc);
+        r3[0] = pf * pcu[2][c];
+        r3[1] = pf * psu[2][c];
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int c = upper(3, 2 * dc + e);
+        r2[2 * e] = r3[e] * pcu[1][c];
+        r2[2 * e + 1] = r3[e] * psu[1][c];
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int c = upper(2, 4 * dc + k);
+        r1[2 * k] = r2[k] * pcu[0][c];
+        r1[2 * k + 1] = r2[k] * psu[0][c];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int b = 8 * (dc & 3) + i;
+        int c = 0;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) c |= (int)((r.pw[p] >> b) & 1u) << p;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float yv = r1[i] * (e ? ps1[c] : pc1[c]) * kCenScale;
+          const _Float16 hf = (_Float16)yv;
+          hv[(2 * i + e) >> 3][(2 * i + e) & 7] = hf;
+          lv[(2 * i + e) >> 3][(2 * i + e) & 7] = (_Float16)(yv - (float)hf);
+        }
+      }
+    } else {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       uint32_t idx = 0;
@@ -138,6 +231,7 @@ __global__ __launch_bounds__(DLayout<D>::NT) void dequant_kernel(tqi::DequantArg
       hv[i >> 3][i & 7] = hf;
       lv[i >> 3][i & 7] = lf;
       if constexpr (PROD) sv[i >> 3][i & 7] = ((r.pw[LB] >> i) & 1u) ? (_Float16)1.0f : (_Float16)-1.0f;
+    }
     }
     const int o = dv * L::PITCH + 16 * dc;
     *(half8 *)&ch[o] = hv[0];
@@ -210,10 +304,10 @@ __global__ __launch_bounds__(DLayout<D>::NT) void dequant_kernel(tqi::DequantArg
   }
 }
 
-template <int D, int LB, bool PROD, bool OUT_F32>
+template <int D, int LB, bool PROD, bool OUT_F32, bool POLAR = false>
 hipError_t launch_t(const tqi::DequantArgs &a, hipStream_t s) {
   using L = DLayout<D>;
-  constexpr int64_t RB = (LB + (PROD ? 1 : 0)) * D / 8;
+  constexpr int64_t RB = POLAR ? DPolar<D>::RB : (LB + (PROD ? 1 : 0)) * D / 8;
   constexpr int64_t OSZ = OUT_F32 ? 4 : 2;
   constexpr int64_t kRange = (int64_t{1} << 31) - 1;   // kernel byte ranges stay below 2^31
   int64_t rows = kRange / (D * OSZ);                    // the output range is the largest
@@ -221,7 +315,7 @@ hipError_t launch_t(const tqi::DequantArgs &a, hipStream_t s) {
   rows &= ~int64_t{31};
   int blocks_per_cu = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      &blocks_per_cu, dequant_kernel<D, LB, PROD, OUT_F32>, L::NT, 0);
+      &blocks_per_cu, dequant_kernel<D, LB, PROD, OUT_F32, POLAR>, L::NT, 0);
   if (e != hipSuccess) return e;
   if (blocks_per_cu < 1) blocks_per_cu = 1;
   for (int64_t start = 0; start < a.n_vec; start += rows) {
@@ -234,7 +328,7 @@ hipError_t launch_t(const tqi::DequantArgs &a, hipStream_t s) {
     const int64_t n_tiles = (c.n_vec + 31) / 32;
     int64_t grid = (int64_t)tqi::device_cu_count() * blocks_per_cu;
     if (grid > n_tiles) grid = n_tiles;
-    hipLaunchKernelGGL((dequant_kernel<D, LB, PROD, OUT_F32>), dim3((unsigned)grid), dim3(L::NT), 0,
+    hipLaunchKernelGGL((dequant_kernel<D, LB, PROD, OUT_F32, POLAR>), dim3((unsigned)grid), dim3(L::NT), 0,
                        s, c);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -263,6 +357,12 @@ hipError_t launch_lb(int lb, const tqi::DequantArgs &a, hipStream_t s, bool *ok)
 }  // namespace
 
 namespace tqi {
+
+hipError_t launch_dequant_polar(int d, const DequantArgs &a, hipStream_t s, bool *supported) {
+  *supported = d == 128;
+  if (d != 128) return hipSuccess;
+  return a.out_f32 ? launch_t<128, 1, false, true, true>(a, s) : launch_t<128, 1, false, false, true>(a, s);
+}
 
 hipError_t launch_dequant(int d, int lbits, bool prod, const DequantArgs &a, hipStream_t s,
                           bool *supported) {

@@ -319,6 +319,102 @@ extern "C" tq_status tq_make_codebook(int32_t d, int32_t bits, double *centroids
   return TQ_OK;
 }
 
+// ------------------------------------------------------- polar angle laws
+// PolarQuant variant (page section "1단계", the recursive polar transform):
+// at level l >= 2 an angle splits two radii that span k = 2^(l-1)
+// dimensions each; for a uniform point on the sphere its density on
+// [0, pi/2] is proportional to (sin t cos t)^(k-1).  Moments over a cell
+// by composite 20-point Gauss-Legendre in t (panels of width at most
+// 0.05/sqrt(k)), normalised numerically; 2-bit Lloyd-Max codebooks by Lloyd
+// iteration from the quantiles of a fine table, made exactly symmetric
+// about pi/4 at the end.
+namespace {
+
+struct AngleLaw {
+  int k;
+  double log_c = 0.0;
+  double panel;
+  GaussLegendre gl;
+  explicit AngleLaw(int k_) : k(k_) {
+    panel = 0.05 / std::sqrt((double)k);
+    double m0, m1;
+    raw(0.0, 0.5 * M_PI, &m0, &m1);
+    log_c = -std::log(m0);
+  }
+  void raw(double a, double b, double *m0, double *m1) const {
+    double s0 = 0.0, s1 = 0.0;
+    if (b > a) {
+      int np = (int)std::ceil((b - a) / panel);
+      if (np < 1) np = 1;
+      const double h = (b - a) / np;
+      for (int p = 0; p < np; ++p) {
+        const double mid = a + (p + 0.5) * h;
+        for (int i = 0; i < 20; ++i) {
+          const double t = mid + 0.5 * h * gl.x[i];
+          const double sc = std::sin(t) * std::cos(t);
+          const double f = sc > 0.0 ? std::exp((k - 1) * std::log(sc) + log_c) : (k == 1 ? std::exp(log_c) : 0.0);
+          const double wgt = 0.5 * h * gl.w[i] * f;
+          s0 += wgt;
+          s1 += wgt * t;
+        }
+      }
+    }
+    *m0 = s0;
+    *m1 = s1;
+  }
+};
+
+}  // namespace
+
+extern "C" tq_status tq_make_polar_codebook(int32_t d, double *centroids, double *boundaries) {
+  if (centroids == nullptr || boundaries == nullptr) return TQ_ERR_INVALID;
+  int levels = 0;
+  while ((1 << levels) < d) ++levels;
+  if (d < 64 || (1 << levels) != d || levels > 20) return TQ_ERR_INVALID;
+  for (int lv = 2; lv <= levels; ++lv) {
+    const AngleLaw law(1 << (lv - 1));
+    // start from the quantiles (i + 1/2)/4 of a 4096-point cdf table
+    double c[4];
+    {
+      const int n = 4096;
+      double acc = 0.0;
+      int q = 0;
+      for (int i = 0; i < n && q < 4; ++i) {
+        const double a = 0.5 * M_PI * i / n, b = 0.5 * M_PI * (i + 1) / n;
+        double m0, m1;
+        law.raw(a, b, &m0, &m1);
+        acc += m0;
+        while (q < 4 && acc >= (q + 0.5) / 4.0) c[q++] = b;
+      }
+      while (q < 4) c[q++] = 0.5 * M_PI;
+    }
+    bool done = false;
+    for (int it = 0; it < 100000 && !done; ++it) {
+      double nc[4], step = 0.0;
+      for (int i = 0; i < 4; ++i) {
+        const double lo = i == 0 ? 0.0 : 0.5 * (c[i - 1] + c[i]);
+        const double hi = i == 3 ? 0.5 * M_PI : 0.5 * (c[i] + c[i + 1]);
+        double m0, m1;
+        law.raw(lo, hi, &m0, &m1);
+        if (!(m0 > 0.0)) return TQ_ERR_NO_CONVERGENCE;
+        nc[i] = m1 / m0;
+        step = std::fmax(step, std::fabs(nc[i] - c[i]));
+      }
+      for (int i = 0; i < 4; ++i) c[i] = nc[i];
+      done = step < 1e-15;
+    }
+    if (!done) return TQ_ERR_NO_CONVERGENCE;
+    for (int i = 0; i < 2; ++i) {
+      const double m = 0.5 * (c[i] + (0.5 * M_PI - c[3 - i]));
+      c[i] = m;
+      c[3 - i] = 0.5 * M_PI - m;
+    }
+    for (int i = 0; i < 4; ++i) centroids[4 * (lv - 2) + i] = c[i];
+    for (int i = 0; i < 3; ++i) boundaries[3 * (lv - 2) + i] = 0.5 * (c[i] + c[i + 1]);
+  }
+  return TQ_OK;
+}
+
 extern "C" const char *tq_status_string(tq_status s) {
   switch (s) {
     case TQ_OK: return "ok";

@@ -527,6 +527,182 @@ __global__ __launch_bounds__(2 * QLayout<D>::NT) void quantize_pc_kernel(tqi::Qu
   }
 }
 
+// PolarQuant variant of stage 1 (page section "1단계": the unit vector is
+// paired recursively into polar form; radii carry magnitude, angles
+// direction).  The tile is staged and rotated as above; the rotated unit
+// coordinates go to LDS and the D/16 staging threads of a vector take 16
+// coordinates each.  No angle is ever evaluated: phi >= beta and psi >= beta
+// are decided on squared radii, which only needs sums of squares --
+//   level 1: the quadrant of (y_2i, y_2i+1) from signs, then within it the
+//     local angle against pi/8, pi/4, 3pi/8 as b^2 >= tan^2(beta) a^2;
+//   level l >= 2: psi >= beta  <=>  R_b >= tan^2(beta) R_a, R the squared
+//     radii of the two halves (an angle of a zero block, R_b = 0, is 0).
+// Levels 2..4 stay inside a thread, the rest pair threads by xor shuffles.
+// Codes: 4 level-1 planes (word 4g + p), then 2 planes of the higher levels
+// in level order (word D/16 + 2g + p); bits are gathered with or-reductions
+// over the vector's threads.
+template <int D>
+struct PolarLayout {
+  static constexpr int LV = D == 64 ? 6 : (D == 128 ? 7 : 8);   // levels
+  static constexpr int TPV = D / 16;        // threads per vector
+  static constexpr int NG1 = D / 64;        // level-1 groups of 32 slots
+  static constexpr int NGU = D / 64;        // upper-level groups
+  static constexpr int RB = 3 * D / 8;      // bytes per row
+  static_assert((1 << LV) == D && TPV >= 4, "polar layout");
+};
+
+// First slot of level l >= 2 among the higher-level slots.
+template <int D>
+__host__ __device__ constexpr int polar_level_slot(int level) {
+  return D / 2 - (D >> (level - 1));
+}
+
+template <int D, bool IN_F32>
+__global__ __launch_bounds__(QLayout<D>::NT) void quantize_polar_kernel(tqi::QuantizeArgs a) {
+  using L = QLayout<D>;
+  using P = PolarLayout<D>;
+  constexpr int TILE = L::TILE;
+  constexpr float kT1 = 0.17157287525381f;    // tan^2(pi/8)  = 3 - 2 sqrt 2
+  constexpr float kT3 = 5.82842712474619f;    // tan^2(3pi/8) = 3 + 2 sqrt 2
+  __shared__ __attribute__((aligned(16))) _Float16 xh[2][TILE];
+  __shared__ __attribute__((aligned(16))) _Float16 xl[IN_F32 ? 2 : 1][IN_F32 ? TILE : 8];
+  __shared__ __attribute__((aligned(16))) float vinv[2][32];
+  __shared__ __attribute__((aligned(16))) float us[32][D + 4];
+  __shared__ float tq2[P::LV - 1][3];
+
+  const int tid = threadIdx.x;
+  const int w = tid / kWave;
+  const int l = lane_id();
+  const int m = l & 31;
+  const int h = l >> 5;
+  const int sv_v = tid / L::TPV;
+  const int sv_c = tid % L::TPV;
+
+  half8 pih[L::KS], pil[L::KS];
+  load_stationary<D>(a.pi, w, pih, pil);
+  if (tid < 3 * (P::LV - 1)) {
+    const double t = tan((double)a.boundaries[tid]);
+    tq2[tid / 3][tid % 3] = (float)(t * t);
+  }
+  const int64_t n_tiles = (a.n_vec + 31) / 32;
+  const i32x4 rx = make_rsrc(a.x, (uint32_t)(((a.n_vec - 1) * a.x_stride + D) * (IN_F32 ? 4 : 2)));
+  const i32x4 rc = make_rsrc(a.codes + a.out_offset * P::RB, (uint32_t)(a.n_vec * P::RB));
+  const i32x4 rn = make_rsrc(a.norm + a.out_offset, (uint32_t)(a.n_vec * 2));
+
+  const int64_t step = gridDim.x;
+  int64_t tile = blockIdx.x;
+  RawInput<IN_F32> raw;
+  load_raw<IN_F32>(rx, a.n_vec, a.x_stride, tile, sv_v, sv_c, raw);
+#pragma unroll
+  for (int i = 0; i < 3; ++i) buf_store_u32<kWriteBack>(rn, kNoStore + 4 * i, 0u);
+  int buf = 0;
+  for (; tile < n_tiles; tile += step, buf ^= 1) {
+    const uint16_t n16 = stage_vector<D, IN_F32>(raw, xh[buf], xl[IN_F32 ? buf : 0], vinv[buf], sv_v, sv_c);
+    load_raw<IN_F32>(rx, a.n_vec, a.x_stride, tile + step, sv_v, sv_c, raw);
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t base = tile * 32;
+    const bool row_ok = base + sv_v < a.n_vec;
+    buf_store_u16<kWriteBack>(rn, (sv_c == 0 && row_ok) ? (uint32_t)(2 * (base + sv_v)) : kNoStore, n16);
+    __syncthreads();
+    const f32x16 acc = rotate_tile<D, IN_F32>(xh[buf], xl[IN_F32 ? buf : 0], pih, pil, m, h);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int v = 8 * (r >> 2) + 4 * h + (r & 3);
+      us[v][32 * w + m] = acc[r] * vinv[buf][v];
+    }
+    __syncthreads();
+
+    // ---- coding of vector sv_v, coordinates [16 sv_c, 16 sv_c + 16)
+    const bool zero = vinv[buf][sv_v] == 0.0f;
+    float y[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 t = *(const f32x4 *)&us[sv_v][16 * sv_c + 4 * q];
+      y[4 * q] = t[0]; y[4 * q + 1] = t[1]; y[4 * q + 2] = t[2]; y[4 * q + 3] = t[3];
+    }
+    float r1[8];
+    uint32_t b1[4] = {0u, 0u, 0u, 0u};      // level-1 bits of this thread, plane p
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float ye = y[2 * i], yo = y[2 * i + 1];
+      const float e2 = ye * ye, o2 = yo * yo;
+      r1[i] = e2 + o2;
+      const bool q0 = ye > 0.0f && yo >= 0.0f, q1 = ye <= 0.0f && yo > 0.0f;
+      const bool q2 = ye < 0.0f && yo <= 0.0f, q3 = ye >= 0.0f && yo < 0.0f;
+      const float A = (q1 || q3) ? o2 : e2;   // squared local x
+      const float B = (q1 || q3) ? e2 : o2;   // squared local y
+      const int sub = (B >= kT1 * A ? 1 : 0) + (B >= A ? 1 : 0) + (B >= kT3 * A ? 1 : 0);
+      int idx = (q1 ? 4 : 0) + (q2 ? 8 : 0) + (q3 ? 12 : 0) + sub;
+      idx = (q0 || q1 || q2 || q3) && !zero ? idx : 0;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) b1[p] |= (uint32_t)((idx >> p) & 1) << i;
+    }
+    // higher levels: bits into the upper-group words of this thread
+    uint32_t bu[P::NGU][2];
+#pragma unroll
+    for (int g = 0; g < P::NGU; ++g) bu[g][0] = bu[g][1] = 0u;
+    auto put = [&](int level, int node, int idx) __attribute__((always_inline)) {
+      const int slot = polar_level_slot<D>(level) + node;
+      idx = zero ? 0 : idx;
+#pragma unroll
+      for (int g = 0; g < P::NGU; ++g)
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+          if (slot / 32 == g) bu[g][p] |= (uint32_t)((idx >> p) & 1) << (slot % 32);
+    };
+    auto angle = [&](float ra, float rb, int level) __attribute__((always_inline)) -> int {
+      const float *t = tq2[level - 2];
+      const int c = (rb >= t[0] * ra ? 1 : 0) + (rb >= t[1] * ra ? 1 : 0) + (rb >= t[2] * ra ? 1 : 0);
+      return rb > 0.0f ? c : 0;
+    };
+    float r2[4], r3[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      put(2, 4 * sv_c + i, angle(r1[2 * i], r1[2 * i + 1], 2));
+      r2[i] = r1[2 * i] + r1[2 * i + 1];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      put(3, 2 * sv_c + i, angle(r2[2 * i], r2[2 * i + 1], 3));
+      r3[i] = r2[2 * i] + r2[2 * i + 1];
+    }
+    put(4, sv_c, angle(r3[0], r3[1], 4));
+    float rr = r3[0] + r3[1];
+#pragma unroll
+    for (int level = 5; level <= P::LV; ++level) {
+      const int span = 1 << (level - 5);     // threads per half at this level
+      const float other = wave_xor(rr, span);
+      if ((sv_c & (2 * span - 1)) == 0) put(level, sv_c >> (level - 4), angle(rr, other, level));
+      rr += other;
+    }
+    // level-1 plane words: 8 bits per thread, 4 threads per 32-slot group
+    uint32_t wl[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      wl[p] = b1[p] << (8 * (sv_c & 3));
+      wl[p] |= wave_xor(wl[p], 1);
+      wl[p] |= wave_xor(wl[p], 2);
+    }
+#pragma unroll
+    for (int g = 0; g < P::NGU; ++g)
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int off = 1; off < L::TPV; off <<= 1) bu[g][p] |= wave_xor(bu[g][p], off);
+    const uint32_t row = (uint32_t)((base + sv_v) * P::RB);
+    uint32_t wv1 = wl[0];
+#pragma unroll
+    for (int p = 1; p < 4; ++p) wv1 = (sv_c & 3) == p ? wl[p] : wv1;
+    buf_store_u32<kWriteBack>(rc, row_ok ? row + 4 * (4 * (sv_c >> 2) + (sv_c & 3)) : kNoStore, wv1);
+    uint32_t wvu = bu[0][0];
+#pragma unroll
+    for (int g = 0; g < P::NGU; ++g)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) wvu = sv_c == 2 * g + p ? bu[g][p] : wvu;
+    buf_store_u32<kWriteBack>(rc, (row_ok && sv_c < 2 * P::NGU) ? row + 4 * (D / 16 + sv_c) : kNoStore, wvu);
+  }
+}
+
 // Rows per launch so that the input, code and norm byte ranges stay below
 // 2^31; 0 if one row's input is already too wide.
 template <int D, int LB, bool PROD, bool IN_F32>
@@ -593,9 +769,27 @@ hipError_t launch_lb(int lb, bool in_f32, const tqi::QuantizeArgs &a, hipStream_
   return hipSuccess;
 }
 
+template <int D, bool IN_F32>
+hipError_t launch_polar_t(const tqi::QuantizeArgs &a, hipStream_t s) {
+  constexpr int64_t ESZ = IN_F32 ? 4 : 2;
+  constexpr int64_t kRange = (int64_t{1} << 31) - 1;
+  if (a.x_stride * ESZ > kRange) return hipErrorInvalidValue;
+  int64_t rows = kRange / (a.x_stride * ESZ);
+  if (rows > kRange / PolarLayout<D>::RB) rows = kRange / PolarLayout<D>::RB;
+  if (rows >= 32) rows &= ~int64_t{31};
+  return launch_chunks(quantize_polar_kernel<D, IN_F32>, QLayout<D>::NT, rows, ESZ, a, s);
+}
+
 }  // namespace
 
 namespace tqi {
+
+hipError_t launch_quantize_polar(int d, bool in_f32, const QuantizeArgs &a, hipStream_t s, bool *supported) {
+  *supported = false;
+  if (d != 128) return hipSuccess;
+  *supported = true;
+  return in_f32 ? launch_polar_t<128, true>(a, s) : launch_polar_t<128, false>(a, s);
+}
 
 hipError_t launch_quantize(int d, int lbits, bool prod, bool in_f32, const QuantizeArgs &a,
                            hipStream_t s, bool *supported) {

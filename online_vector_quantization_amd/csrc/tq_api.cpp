@@ -70,6 +70,7 @@ namespace {
 int lloyd_bits(const tq_params *p) {
   if (p->mode == TQ_MODE_MSE) return (p->bits >= 1 && p->bits <= 4) ? p->bits : -1;
   if (p->mode == TQ_MODE_PROD) return (p->bits >= 2 && p->bits <= 5) ? p->bits - 1 : -1;
+  if (p->mode == TQ_MODE_POLAR) return p->bits == 3 ? 2 : -1;   // 2 bits per higher-level angle
   return -1;
 }
 
@@ -115,8 +116,11 @@ extern "C" tq_status tq_quantize_kv(const tq_params *p, const void *x, int32_t x
   a.rnorm = out->rnorm;
   a.out_offset = out_offset;
   bool ok = false;
-  hipError_t e = tqi::launch_quantize(p->d, lloyd_bits(p), prod, x_dtype == TQ_F32, a,
-                                      (hipStream_t)stream, &ok);
+  hipError_t e;
+  if (p->mode == TQ_MODE_POLAR)
+    e = tqi::launch_quantize_polar(p->d, x_dtype == TQ_F32, a, (hipStream_t)stream, &ok);
+  else
+    e = tqi::launch_quantize(p->d, lloyd_bits(p), prod, x_dtype == TQ_F32, a, (hipStream_t)stream, &ok);
   if (!ok) return TQ_ERR_UNSUPPORTED;
   return hip_status(e);
 }
@@ -128,6 +132,7 @@ extern "C" tq_status tq_attn_logits(const tq_params *p, const void *q, int32_t q
                                     void *stream) {
   tq_status st = check_params(p);
   if (st != TQ_OK) return st;
+  if (p->mode == TQ_MODE_POLAR) return TQ_ERR_UNSUPPORTED;
   const bool prod = p->mode == TQ_MODE_PROD;
   if (k == nullptr || batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || topk < 0) return TQ_ERR_INVALID;
   if (n_q_heads % n_kv_heads != 0) return TQ_ERR_INVALID;
@@ -177,6 +182,7 @@ extern "C" tq_status tq_append_attn_logits(const tq_params *p, const void *x_new
                                            void *stream) {
   tq_status st = check_params(p);
   if (st != TQ_OK) return st;
+  if (p->mode == TQ_MODE_POLAR) return TQ_ERR_UNSUPPORTED;
   const bool prod = p->mode == TQ_MODE_PROD;
   if (k == nullptr || batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0) return TQ_ERR_INVALID;
   if (n_q_heads % n_kv_heads != 0) return TQ_ERR_INVALID;
@@ -224,6 +230,7 @@ extern "C" tq_status tq_attn_output(const tq_params *p, const float *logits, int
                                     void *stream) {
   tq_status st = check_params(p);
   if (st != TQ_OK) return st;
+  if (p->mode == TQ_MODE_POLAR) return TQ_ERR_UNSUPPORTED;
   if (v == nullptr || batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0) return TQ_ERR_INVALID;
   if (n_q_heads % n_kv_heads != 0) return TQ_ERR_INVALID;
   if (out_dtype != TQ_F32 && out_dtype != TQ_BF16) return TQ_ERR_INVALID;
@@ -273,7 +280,13 @@ extern "C" tq_status tq_dequantize(const tq_params *p, const tq_packed *k, int64
   a.out = out;
   a.out_f32 = out_dtype == TQ_F32;
   bool ok = false;
-  hipError_t e = tqi::launch_dequant(p->d, lloyd_bits(p), prod, a, (hipStream_t)stream, &ok);
+  hipError_t e;
+  if (p->mode == TQ_MODE_POLAR) {
+    if (!aligned16(k->codes)) return TQ_ERR_UNSUPPORTED;
+    e = tqi::launch_dequant_polar(p->d, a, (hipStream_t)stream, &ok);
+  } else {
+    e = tqi::launch_dequant(p->d, lloyd_bits(p), prod, a, (hipStream_t)stream, &ok);
+  }
   if (!ok) return TQ_ERR_UNSUPPORTED;
   return hip_status(e);
 }

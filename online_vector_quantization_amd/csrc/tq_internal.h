@@ -24,6 +24,8 @@ struct QuantizeArgs {
 
 hipError_t launch_quantize(int d, int lbits, bool prod, bool in_f32, const QuantizeArgs &a,
                            hipStream_t s, bool *supported);
+// polar format (d = 128): boundaries = the angle boundaries of levels 2..log2 d
+hipError_t launch_quantize_polar(int d, bool in_f32, const QuantizeArgs &a, hipStream_t s, bool *supported);
 
 struct LogitArgs {
   const void *q;
@@ -75,6 +77,8 @@ struct DequantArgs {
 
 hipError_t launch_dequant(int d, int lbits, bool prod, const DequantArgs &a, hipStream_t s,
                           bool *supported);
+// polar format (d = 128): centroids = the angle centroids of levels 2..log2 d
+hipError_t launch_dequant_polar(int d, const DequantArgs &a, hipStream_t s, bool *supported);
 
 struct AttendArgs {
   const float *logits;   // [batch][n_q_heads][seq_len]

@@ -14,6 +14,10 @@ Tolerance rules:
 * logits from identical (oracle-packed) codes: |l_gpu - l_orc| <= 1e-4 *
   max(|l_orc|, 1e-2 * |scale| * n16 * ||q||).
 * dequantize: ||x_gpu - x_orc|| <= 1e-4 ||x_orc|| per vector (fp32 output).
+* polar format: angle indices bit-exact except angles within 1e-5 rad of a
+  cell boundary (level-1 angles also within 1e-6 / rho of it, rho the pair's
+  radius: the angle of a small pair moves by the coordinates' error over
+  rho), each off by one cell; fewer than 0.01% of the angles.
 """
 
 import numpy as np
@@ -120,3 +124,40 @@ def check_dequant(gpu, want):
     rel = np.where(np.linalg.norm(want, axis=1) > 0, num / den, num)
     assert rel.max() <= DEQUANT_RTOL, "dequant error %.3g" % rel.max()
     return float(rel.max())
+
+
+# polar format: angle windows
+POLAR_ANGLE_WINDOW = 1e-5      # radians, plus the conditioning of a small pair
+POLAR_PAIR_EPS = 1e-6          # absolute error of a rotated unit coordinate
+
+
+def check_polar_codes(gpu_codes, ref, d):
+    """Angle indices bit-exact except angles within the window of a cell
+    boundary (level 1 also at 0 = 2 pi), off by one cell; fewer than 0.01%."""
+    from oracle import polar as opq
+    g1, gu = opq.unpack(gpu_codes, d)
+    y = ref["y"]
+    rho = np.hypot(y[:, 0::2], y[:, 1::2])
+    bad1 = g1 != ref["idx1"]
+    if bad1.any():
+        phi = ref["phi"][bad1]
+        bnd = 2 * np.pi * np.arange(17) / 16                 # includes 0 and 2 pi
+        dist = np.min(np.abs(phi[:, None] - bnd[None, :]), axis=1)
+        win = POLAR_ANGLE_WINDOW + POLAR_PAIR_EPS / np.maximum(rho[bad1], 1e-30)
+        assert np.all(dist < win), "level-1 mismatch far from a boundary: %g" % (dist / win).max()
+        step = (g1[bad1] - ref["idx1"][bad1]) % 16
+        assert np.all((step == 1) | (step == 15))
+    badu = gu != ref["idx_up"]
+    if badu.any():
+        books = opq.codebooks(d)
+        psi_all = np.concatenate(ref["psis"], axis=1)
+        lv_of = np.concatenate([np.full(p.shape[1], lv) for lv, p in enumerate(ref["psis"], start=2)])
+        rows, cols = np.nonzero(badu)
+        for r, c in zip(rows, cols):
+            t = books[lv_of[c] - 1][1]
+            assert np.min(np.abs(psi_all[r, c] - t)) < POLAR_ANGLE_WINDOW, "upper-level mismatch far from a boundary"
+            assert abs(int(gu[r, c]) - int(ref["idx_up"][r, c])) == 1
+    n_bad = int(bad1.sum() + badu.sum())
+    total = g1.size + gu.size
+    assert n_bad <= 1e-4 * total, "%d of %d angle indices differ" % (n_bad, total)
+    return n_bad

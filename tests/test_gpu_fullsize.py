@@ -21,7 +21,7 @@ from synthetic import (bf16_to_f32, channel_scales, device_kv, device_queries, g
                        search_vectors, tiny_keys_queries)
 
 from parity import (OracleTables, cache_from_oracle, check_codes, check_dequant, check_logits,
-                    check_norms, check_rnorm, check_signs)
+                    check_norms, check_polar_codes, check_rnorm, check_signs)
 
 pytestmark = pytest.mark.gpu
 
@@ -152,6 +152,33 @@ def test_config2_decode_full(tq):
     want = oatt.attn_output(out[None].astype(np.float64), ocache, otv.pi, otv.c, oqz.MODE_MSE)
     err = np.linalg.norm(got - want, axis=2)
     assert np.all(err <= 1e-4 * np.linalg.norm(want, axis=2) + 1e-6)
+
+
+def test_config2_values_polar_full(tq):
+    """The decode configuration's 262144 values through the polar format: every
+    angle index and norm, and fp32 / bf16 reconstructions on sampled rows."""
+    from oracle import polar as opq
+    from oracle import rotation as orot
+    d, heads, seq = 128, 8, 32768
+    n = heads * seq
+    vb, _ = _host_stream_keys(0, 2, "v", heads, seq, d)
+    x64 = bf16_to_f32(vb).astype(np.float64)
+    pi = orot.haar_rotation(d, 0)
+    ref = opq.quantize(x64, pi)
+    qp = tq.Quantizer(d, 3, tq.MODE_POLAR, seed=0, device=DEV)
+    cp = qp.new_cache(n)
+    qp.quantize(_dev_bf16(vb), out=cp)
+    codes = cp.codes.cpu().numpy()
+    check_polar_codes(codes, ref, d)
+    assert np.array_equal(cp.norm.cpu().numpy().view(np.uint16), ref["norm"])
+    rows = _sample_rows(n, 3000, 41)
+    want = opq.dequantize(ref["codes"][rows], ref["norm"][rows], pi)
+    oc = tq.PackedKV.from_tensors(d, 3, tq.MODE_POLAR, torch.from_numpy(ref["codes"]).to(DEV),
+                                  torch.from_numpy(ref["norm"].view(np.int16)).to(DEV))
+    got = qp.dequantize(oc, n).cpu().numpy()[rows]
+    check_dequant(got, want)
+    got16 = qp.dequantize(oc, n, out_dtype=torch.bfloat16).float().cpu().numpy()[rows]
+    assert np.all(np.abs(got16 - want) <= 2.0 ** -8 * np.abs(want) + 1e-3 * np.abs(want).max(axis=1, keepdims=True))
 
 
 def test_config3_long_context_full(tq):

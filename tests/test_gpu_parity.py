@@ -12,7 +12,7 @@ from oracle import quantizer as oqz
 from synthetic import bf16_bits, bf16_to_f32, channel_scales, kv_block, search_vectors, tiny_keys_queries
 
 from parity import (OracleTables, cache_from_oracle, check_codes, check_dequant, check_logits,
-                    check_norms, check_rnorm, check_signs, dev_bf16)
+                    check_norms, check_polar_codes, check_rnorm, check_signs, dev_bf16, dev_u16)
 
 pytestmark = pytest.mark.gpu
 
@@ -432,3 +432,78 @@ def test_append_attn_logits_bounds(tq):
             qz.append_attn_logits(x, q, cache, n_kv_heads=2, pos=bad, scale=1.0, row_tokens=50)
     out = qz.append_attn_logits(x[:0], q[:0], cache, n_kv_heads=2, pos=3, scale=1.0, row_tokens=50)
     assert out.shape == (0, 8, 4)
+
+
+# ---------------------------------------------------------------- polar format
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_polar_quantize_parity(tq, dtype):
+    from oracle import polar as opq
+    from oracle import rotation as orot
+    d, n = 128, 1000
+    if dtype == "bf16":
+        xb = _keys_bf16(d, n, seed=3)
+        x64 = _special_rows(bf16_to_f32(xb).astype(np.float64))
+        xt = dev_bf16(bf16_bits(x64.astype(np.float32)), DEV)
+    else:
+        rng = np.random.default_rng(11)
+        x64 = _special_rows((rng.standard_normal((n, d)) * np.exp(rng.standard_normal(d))).astype(np.float32)
+                            .astype(np.float64))
+        xt = torch.from_numpy(x64.astype(np.float32)).to(DEV)
+    pi = orot.haar_rotation(d, 0)
+    ref = opq.quantize(x64, pi)
+    qz = tq.Quantizer(d, 3, tq.MODE_POLAR, seed=0, device=DEV)
+    off = 3
+    cache = qz.new_cache(n + 7)
+    qz.quantize(xt, out=cache, out_offset=off)
+    torch.cuda.synchronize()
+    codes = cache.codes.cpu().numpy()[off:off + n]
+    check_polar_codes(codes, ref, d)
+    check_norms(cache.norm.cpu().numpy()[off:off + n], {"norm": ref["norm"]})
+    assert not codes[3].any()                               # the zero vector: every angle 0
+
+
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_polar_dequantize_parity(tq, out_dtype):
+    from oracle import polar as opq
+    from oracle import rotation as orot
+    d, n = 128, 777
+    rng = np.random.default_rng(12)
+    x64 = rng.standard_normal((n, d)) * np.exp(rng.standard_normal(d))
+    x64[5] = 0.0
+    pi = orot.haar_rotation(d, 0)
+    ref = opq.quantize(x64, pi)
+    want = opq.dequantize(ref["codes"], ref["norm"], pi)
+    qz = tq.Quantizer(d, 3, tq.MODE_POLAR, seed=0, device=DEV)
+    cache = tq.PackedKV.from_tensors(d, 3, tq.MODE_POLAR, torch.from_numpy(ref["codes"]).to(DEV),
+                                     dev_u16(ref["norm"], DEV))
+    if out_dtype == "f32":
+        got = qz.dequantize(cache, n).cpu().numpy()
+        check_dequant(got, want)
+    else:
+        got = qz.dequantize(cache, n, out_dtype=torch.bfloat16).float().cpu().numpy()
+        assert np.all(np.abs(got - want) <= 2.0 ** -8 * np.abs(want) + 1e-3 * np.abs(want).max(axis=1, keepdims=True))
+    assert np.all(got[5] == 0.0)
+
+
+def test_polar_round_trip_and_unsupported_calls(tq):
+    """GPU quantise then GPU dequantise against the oracle's reconstruction of
+    the GPU's own codes (decoding is exact given the codes), and the calls the
+    polar format does not have."""
+    from oracle import polar as opq
+    from oracle import rotation as orot
+    d, n = 128, 4096
+    rng = np.random.default_rng(13)
+    x = torch.from_numpy((rng.standard_normal((n, d)) * 2.0).astype(np.float32)).to(DEV)
+    qz = tq.Quantizer(d, 3, tq.MODE_POLAR, seed=0, device=DEV)
+    cache = qz.new_cache(n)
+    qz.quantize(x, out=cache)
+    got = qz.dequantize(cache, n).cpu().numpy()
+    pi = orot.haar_rotation(d, 0)
+    want = opq.dequantize(cache.codes.cpu().numpy(), cache.norm.cpu().numpy().view(np.uint16), pi)
+    check_dequant(got, want)
+    xs = x.cpu().numpy().astype(np.float64)
+    cos = np.sum(xs * got, 1) / np.linalg.norm(xs, axis=1) / np.linalg.norm(got, axis=1)
+    assert 0.98 < cos.mean() < 0.99
+    q = torch.zeros((1, 4, d), device=DEV)
+    with pytest.raises(tq.TQError):
+        qz.attn_logits(q, cache, n_kv_heads=1, seq_len=n, scale=1.0)

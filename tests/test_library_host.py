@@ -120,3 +120,19 @@ def test_device_calls_validate_before_launch(tq):
     pk2 = tq.Packed(dummy, dummy, dummy)
     assert lib.tq_quantize_kv(ctypes.byref(p256), dummy, 0, 1, 256, ctypes.byref(pk2), 0,
                               None) == tq.TQ_ERR_UNSUPPORTED
+
+
+def test_polar_codebooks_match_oracle():
+    """Angle codebooks of the polar format: the library (composite Gauss-Legendre
+    and Lloyd iteration) against the oracle (incomplete beta and adaptive
+    quadrature), levels 2..7 at d = 128."""
+    import online_vector_quantization_amd as tq
+    from oracle import polar as opq
+    c, t = tq.make_polar_codebook(128)
+    assert c.shape == (6, 4) and t.shape == (6, 3)
+    for lv in range(2, 8):
+        oc, ot = opq.angle_codebook(1 << (lv - 1))
+        np.testing.assert_allclose(c[lv - 2], oc, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(t[lv - 2], ot, rtol=0, atol=1e-12)
+    with pytest.raises(tq.TQError):
+        tq.make_polar_codebook(96)
