@@ -9,7 +9,9 @@
 // centroid of every coordinate as fp16 hi + lo (scaled by 2^10) and, in
 // inner-product mode, the sign as an exact fp16 +-1.  Products run on the
 // 32x32x16 fp16 MFMA with fp32 accumulation; the output tile has one column
-// per lane, so each register row is a coalesced 128-byte store.
+// per lane, so each register row is a coalesced 128-byte store.  For bf16
+// output one fp16 product (hi x hi, about 2^-11 relative per element) meets
+// the output precision, so the lo halves are skipped.
 #include "tq_device.h"
 #include "tq_internal.h"
 
@@ -85,7 +87,10 @@ __global__ __launch_bounds__(DLayout<D>::NT) void dequant_kernel(tqi::DequantArg
   // so one decode buffer suffices.  The output tile is written back as full
   // 16-byte pieces of rows.
   __shared__ __attribute__((aligned(16))) _Float16 ch[TILE];
-  __shared__ __attribute__((aligned(16))) _Float16 cl[TILE];
+  // bf16 output needs 8 bits: one fp16 product (about 2^-11 per element)
+  // suffices and the lo halves are not formed; fp32 output uses three.
+  constexpr bool SPLIT = OUT_F32;
+  __shared__ __attribute__((aligned(16))) _Float16 cl[SPLIT ? TILE : 8];
   __shared__ __attribute__((aligned(16))) _Float16 sg[PROD ? TILE : 8];
   __shared__ __attribute__((aligned(16))) float vfac[2][32];
   __shared__ __attribute__((aligned(16))) uint8_t otile[32 * D * OSZ];
@@ -236,8 +241,10 @@ __global__ __launch_bounds__(DLayout<D>::NT) void dequant_kernel(tqi::DequantArg
     const int o = dv * L::PITCH + 16 * dc;
     *(half8 *)&ch[o] = hv[0];
     *(half8 *)&ch[o + 8] = hv[1];
-    *(half8 *)&cl[o] = lv[0];
-    *(half8 *)&cl[o + 8] = lv[1];
+    if constexpr (SPLIT) {
+      *(half8 *)&cl[o] = lv[0];
+      *(half8 *)&cl[o + 8] = lv[1];
+    }
     if constexpr (PROD) {
       *(half8 *)&sg[o] = sv[0];
       *(half8 *)&sg[o + 8] = sv[1];
@@ -269,13 +276,15 @@ __global__ __launch_bounds__(DLayout<D>::NT) void dequant_kernel(tqi::DequantArg
 #pragma unroll
     for (int s = 0; s < L::KS; ++s) {
       const half8 ah = *(const half8 *)&ch[m * L::PITCH + 16 * s + 8 * h];
-      const half8 al = *(const half8 *)&cl[m * L::PITCH + 16 * s + 8 * h];
-      acc = mfma32(al, ph[s], acc);
-      acc = mfma32(ah, pl[s], acc);
+      if constexpr (SPLIT) {
+        const half8 al = *(const half8 *)&cl[m * L::PITCH + 16 * s + 8 * h];
+        acc = mfma32(al, ph[s], acc);
+        acc = mfma32(ah, pl[s], acc);
+      }
       acc = mfma32(ah, ph[s], acc);
       if constexpr (PROD) {
         const half8 as = *(const half8 *)&sg[m * L::PITCH + 16 * s + 8 * h];
-        acc2 = mfma32(as, sl[s], acc2);
+        if constexpr (SPLIT) acc2 = mfma32(as, sl[s], acc2);
         acc2 = mfma32(as, sh[s], acc2);
       }
     }
