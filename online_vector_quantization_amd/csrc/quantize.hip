@@ -89,6 +89,53 @@ __device__ void load_stationary(const float *__restrict__ mat, int w, half8 (&hi
   }
 }
 
+// Reductions over the N = 4, 8 or 16 consecutive lanes that share a vector,
+// all in DPP (no LDS permute): two quad permutes, then the half-row mirror
+// (lane i <-> 7 - i within 8) and the row mirror (lane i <-> 15 - i within
+// 16).  Every lane ends with the same value (each step adds a lane's value
+// to its partner's, so both orders give the same sum).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint64_t r = (uint64_t)dpp_u32<CTRL>((uint32_t)b) | ((uint64_t)dpp_u32<CTRL>((uint32_t)(b >> 32)) << 32);
+  return __builtin_bit_cast(double, r);
+}
+
+template <int N>
+__device__ __forceinline__ double lanes_sum(double v) {
+  static_assert(N == 4 || N == 8 || N == 16, "4, 8 or 16 lanes");
+  v += dpp_f64<0xB1>(v);
+  v += dpp_f64<0x4E>(v);
+  if constexpr (N >= 8) v += dpp_f64<0x141>(v);
+  if constexpr (N >= 16) v += dpp_f64<0x140>(v);
+  return v;
+}
+
+template <int N>
+__device__ __forceinline__ float lanes_sum(float v) {
+  static_assert(N == 4 || N == 8 || N == 16, "4, 8 or 16 lanes");
+  v += __uint_as_float(dpp_u32<0xB1>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<0x4E>(__float_as_uint(v)));
+  if constexpr (N >= 8) v += __uint_as_float(dpp_u32<0x141>(__float_as_uint(v)));
+  if constexpr (N >= 16) v += __uint_as_float(dpp_u32<0x140>(__float_as_uint(v)));
+  return v;
+}
+
+template <int N>
+__device__ __forceinline__ float lanes_max(float v) {
+  static_assert(N == 4 || N == 8 || N == 16, "4, 8 or 16 lanes");
+  v = fmaxf(v, __uint_as_float(dpp_u32<0xB1>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<0x4E>(__float_as_uint(v))));
+  if constexpr (N >= 8) v = fmaxf(v, __uint_as_float(dpp_u32<0x141>(__float_as_uint(v))));
+  if constexpr (N >= 16) v = fmaxf(v, __uint_as_float(dpp_u32<0x140>(__float_as_uint(v))));
+  return v;
+}
+
 // Raw input of one staging thread: 16 consecutive elements of one vector.
 template <bool IN_F32>
 struct RawInput {
@@ -137,11 +184,8 @@ __device__ __forceinline__ uint16_t stage_vector(const RawInput<IN_F32> &r, _Flo
     ss = fma((double)xv[i], (double)xv[i], ss);
     mx = fmaxf(mx, fabsf(xv[i]));
   }
-#pragma unroll
-  for (int off = 1; off < L::TPV; off <<= 1) {
-    ss += wave_xor(ss, off);
-    mx = fmaxf(mx, wave_xor(mx, off));
-  }
+  ss = lanes_sum<L::TPV>(ss);
+  mx = lanes_max<L::TPV>(mx);
   int e = 0;
   if (mx > 0.0f) {
     e = ilogbf(mx);
@@ -344,8 +388,7 @@ __device__ __forceinline__ float residual_norm(const _Float16 *rh, const _Float1
     }
   }
   float ss = s_hh + (2.0f * s_hl + s_ll);
-#pragma unroll
-  for (int off = 1; off < L::TPV; off <<= 1) ss += wave_xor(ss, off);
+  ss = lanes_sum<L::TPV>(ss);
   return vinv[sv_v] == 0.0f ? 0.0f : sqrtf(ss) * (1.0f / kResScale);
 }
 
