@@ -339,7 +339,7 @@ def long_context_leg(torch, tq, timer, reps, device):
 def main():
     args = _args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only (this build has no multi-GPU path); "
+        print("bench.py measures one GPU only (the library has no multi-GPU path); "
               "run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch

@@ -82,7 +82,7 @@ typedef int32_t tq_status;
 enum {
   TQ_OK = 0,
   TQ_ERR_INVALID = -1,        /* NULL pointer, negative size, bad enum value   */
-  TQ_ERR_UNSUPPORTED = -2,    /* valid request this build has no kernel for    */
+  TQ_ERR_UNSUPPORTED = -2,    /* valid request the library has no kernel for  */
   TQ_ERR_NO_CONVERGENCE = -3, /* Lloyd-Max solver did not settle               */
   TQ_ERR_HIP = -4             /* a HIP runtime call or launch failed           */
 };
