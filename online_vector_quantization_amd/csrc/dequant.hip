@@ -271,23 +271,29 @@ __global__ __launch_bounds__(DLayout<D>::NT) void dequant_kernel(tqi::DequantArg
     load_raw(tile + step, raw);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
-    f32x16 acc = {};
+    // fragments read up front; K steps alternate between two accumulators
+    // so that consecutive MFMAs are independent
+    f32x16 accp[2] = {{}, {}};
     f32x16 acc2 = {};
+    half8 ahs[L::KS];
+#pragma unroll
+    for (int s = 0; s < L::KS; ++s) ahs[s] = *(const half8 *)&ch[m * L::PITCH + 16 * s + 8 * h];
 #pragma unroll
     for (int s = 0; s < L::KS; ++s) {
-      const half8 ah = *(const half8 *)&ch[m * L::PITCH + 16 * s + 8 * h];
+      const half8 ah = ahs[s];
       if constexpr (SPLIT) {
         const half8 al = *(const half8 *)&cl[m * L::PITCH + 16 * s + 8 * h];
-        acc = mfma32(al, ph[s], acc);
-        acc = mfma32(ah, pl[s], acc);
+        accp[s & 1] = mfma32(al, ph[s], accp[s & 1]);
+        accp[s & 1] = mfma32(ah, pl[s], accp[s & 1]);
       }
-      acc = mfma32(ah, ph[s], acc);
+      accp[s & 1] = mfma32(ah, ph[s], accp[s & 1]);
       if constexpr (PROD) {
         const half8 as = *(const half8 *)&sg[m * L::PITCH + 16 * s + 8 * h];
         if constexpr (SPLIT) acc2 = mfma32(as, sl[s], acc2);
         acc2 = mfma32(as, sh[s], acc2);
       }
     }
+    const f32x16 acc = accp[0] + accp[1];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int v = 8 * (r >> 2) + 4 * h + (r & 3);

@@ -216,24 +216,29 @@ __device__ __forceinline__ uint16_t stage_vector(const RawInput<IN_F32> &r, _Flo
   return f64_to_f16_bits(sqrt(ss));
 }
 
-// y = X Pi^T for the wave's 32 columns of a staged tile.
+// y = X Pi^T for the wave's 32 columns of a staged tile.  The A fragments
+// are read from LDS up front and the K steps alternate between two
+// accumulators, so consecutive MFMAs do not wait on each other's result.
 template <int D, bool IN_F32>
 __device__ __forceinline__ f32x16 rotate_tile(const _Float16 *xh, const _Float16 *xl,
                                               const half8 (&pih)[D / 16], const half8 (&pil)[D / 16], int m,
                                               int h) {
   using L = QLayout<D>;
-  f32x16 acc = {};
+  f32x16 acc[2] = {{}, {}};
+  half8 ah[L::KS];
+#pragma unroll
+  for (int s = 0; s < L::KS; ++s) ah[s] = *(const half8 *)&xh[m * L::PITCH + 16 * s + 8 * h];
 #pragma unroll
   for (int s = 0; s < L::KS; ++s) {
-    half8 ah = *(const half8 *)&xh[m * L::PITCH + 16 * s + 8 * h];
+    const half8 a0 = ah[s];
     if constexpr (IN_F32) {
       half8 al = *(const half8 *)&xl[m * L::PITCH + 16 * s + 8 * h];
-      acc = mfma32(al, pih[s], acc);
+      acc[s & 1] = mfma32(al, pih[s], acc[s & 1]);
     }
-    acc = mfma32(ah, pil[s], acc);
-    acc = mfma32(ah, pih[s], acc);
+    acc[s & 1] = mfma32(a0, pil[s], acc[s & 1]);
+    acc[s & 1] = mfma32(a0, pih[s], acc[s & 1]);
   }
-  return acc;
+  return acc[0] + acc[1];
 }
 
 // Codes of the wave's 32 x 32 block: plane words go to outw (lane slot
@@ -325,22 +330,24 @@ __device__ __forceinline__ void store_planes(const i32x4 &rc, const uint32_t (&o
   }
 }
 
-// z = R M^T for rows [32wq, 32wq+32) of M, and the sign words of the block:
-// lane 2r + hh holds the word of vector 8(r/4)+4hh+r%4.
+// z = R M^T for rows [32wq, 32wq+32) of M (two alternating accumulators),
+// and the sign words of the block: lane 2r + hh holds the word of vector
+// 8(r/4)+4hh+r%4.
 template <int D>
 __device__ __forceinline__ uint32_t sign_words(const _Float16 *rh, const _Float16 *rl,
                                                const half8 (&mh)[D / 16], const half8 (&ml)[D / 16], int m,
                                                int h) {
   using L = QLayout<D>;
-  f32x16 acc2 = {};
+  f32x16 accs[2] = {{}, {}};
 #pragma unroll
   for (int s = 0; s < L::KS; ++s) {
     half8 ah = *(const half8 *)&rh[m * L::PITCH + 16 * s + 8 * h];
     half8 al = *(const half8 *)&rl[m * L::PITCH + 16 * s + 8 * h];
-    acc2 = mfma32(al, mh[s], acc2);
-    acc2 = mfma32(ah, ml[s], acc2);
-    acc2 = mfma32(ah, mh[s], acc2);
+    accs[s & 1] = mfma32(al, mh[s], accs[s & 1]);
+    accs[s & 1] = mfma32(ah, ml[s], accs[s & 1]);
+    accs[s & 1] = mfma32(ah, mh[s], accs[s & 1]);
   }
+  const f32x16 acc2 = accs[0] + accs[1];
   uint32_t sw = 0u;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
