@@ -2,6 +2,11 @@
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|search]
 
+Without --warmup the untimed warmup runs as many steps as take about one
+second (at least 5): the GPU reaches its sustained clock only after that much
+load, and the timed steps then measure the sustained rate.  The line reports
+the warmup steps actually run.
+
 A step is one pass of the whole path over one batch of synthetic input:
 quantise the keys (inner-product mode) and the values (MSE mode), compute the
 attention logits of every query head straight from the packed keys, and
@@ -42,13 +47,16 @@ HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFS = 2500.0
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "online_vector_quantization_amd", "csrc")
+WARMUP_S = 1.0      # default untimed warmup: the clocks settle under about a second of load
 
 
 def _args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warmup steps (default: as many as take about one second, at least 5; "
+                         "the GPU reaches its sustained clock only under sustained load)")
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "search"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-long-context", action="store_true")
@@ -358,8 +366,21 @@ def main():
     calls, work, cfg, units, extras = build[args.workload](torch, tq, args, device)
     unit = {"decode": "keys/s", "prefill": "vectors/s", "search": "keys/s"}[args.workload]
     step = lambda: [fn() for fn in calls.values()]
-    for _ in range(args.warmup):
-        step()
+    if args.warmup is None:                 # about one second of steps, at least 5
+        for _ in range(3):                  # first calls: workspaces, first touches
+            step()
+        torch.cuda.synchronize()
+        tw = time.perf_counter()
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+        per = max((time.perf_counter() - tw) / 10, 1e-6)
+        args.warmup = 13 + max(5, int(math.ceil(WARMUP_S / per)))
+        for _ in range(args.warmup - 13):
+            step()
+    else:
+        for _ in range(args.warmup):
+            step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     t_step = timer(step, args.steps)
