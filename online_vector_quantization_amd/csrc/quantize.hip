@@ -30,10 +30,13 @@
 // * Two kernels share those steps.  quantize_kernel (MSE mode, and d = 256):
 //   D/32 waves, each tile staged, rotated and coded by the same waves.
 //   quantize_pc_kernel (inner-product mode, d <= 128): D/32 "producer" waves
-//   hold Pi and rotate + code tile k while D/32 "consumer" waves hold M,
-//   stage tile k+1 and run the QJL projection of tile k-1; one barrier per
-//   tile.  Each wave then carries one stationary matrix instead of two, and
-//   the VALU-heavy coding overlaps the MFMA-heavy projection on every SIMD.
+//   hold Pi and rotate + code tile k, D/32 "sketch" waves hold M and run the
+//   QJL projection of tile k-1, D/32 "stage" waves stage tile k+1 and take
+//   the residual norms; one barrier per tile.  No wave carries both
+//   matrices, and with three waves per SIMD each one's latencies are covered
+//   by the others.  (Measured on gfx950: an MFMA of one wave does not run
+//   alongside VALU work of another wave on the same SIMD, so the tile time is
+//   close to the sum of the SIMD's MFMA and VALU time.)
 #include "tq_device.h"
 #include "tq_internal.h"
 
@@ -155,7 +158,7 @@ __device__ __forceinline__ void load_raw(const i32x4 &rx, int64_t n_vec, int64_t
 }
 
 // Stages 16 elements of vector sv_v into an LDS tile (fp16, and fp16 lo for
-// fp32 inputs) after the per-vector power-of-two scale; the first thread of
+// fp32 inputs) after the per-vector power-of-two scale; every thread of
 // a vector writes 1 / (scale * 2^8 * |x|) to vinv.  Returns the fp16 norm.
 template <int D, bool IN_F32>
 __device__ __forceinline__ uint16_t stage_vector(const RawInput<IN_F32> &r, _Float16 *xh, _Float16 *xl,
@@ -186,11 +189,10 @@ __device__ __forceinline__ uint16_t stage_vector(const RawInput<IN_F32> &r, _Flo
   }
   ss = lanes_sum<L::TPV>(ss);
   mx = lanes_max<L::TPV>(mx);
-  int e = 0;
-  if (mx > 0.0f) {
-    e = ilogbf(mx);
-    e = e < -140 ? -140 : (e > 127 ? 127 : e);
-  }
+  // exponent of the largest element (frexp's is one above ilogb's; a zero
+  // vector gets 0 and stays zero)
+  int e = __builtin_amdgcn_frexp_expf(mx) - 1;
+  e = e < -140 ? -140 : (e > 127 ? 127 : e);
   const float sc = ldexpf(1.0f, 14 - e);
   half8 hv[2], lv[2];
 #pragma unroll
@@ -212,18 +214,21 @@ __device__ __forceinline__ uint16_t stage_vector(const RawInput<IN_F32> &r, _Flo
   // so fp32 holds it; v_rsq_f32 is good to about one ulp.
   const float ss_sc = (float)(ss * ((double)sc * (double)sc));
   const float inv_n = ss > 0.0 ? __builtin_amdgcn_rsqf(ss_sc) * (1.0f / kPiScale) : 0.0f;
-  if (sv_c == 0) vinv[sv_v] = inv_n;
+  vinv[sv_v] = inv_n;        // the vector's threads all hold the same value
   return f64_to_f16_bits(sqrt(ss));
 }
 
-// y = X Pi^T for the wave's 32 columns of a staged tile.  The A fragments
-// are read from LDS up front and the K steps alternate between two
-// accumulators, so consecutive MFMAs do not wait on each other's result.
-template <int D, bool IN_F32>
+// y = X Pi^T for the wave's 32 columns of a staged tile (A fragments read
+// from LDS up front).  With NACC = 2 the K steps alternate between two
+// accumulators, so consecutive MFMAs do not wait on each other; that pays
+// where the wave has nothing else to issue meanwhile (the MSE kernel) and
+// costs 16 adds where other waves fill the SIMD (the split kernel).
+template <int D, bool IN_F32, int NACC = 2>
 __device__ __forceinline__ f32x16 rotate_tile(const _Float16 *xh, const _Float16 *xl,
                                               const half8 (&pih)[D / 16], const half8 (&pil)[D / 16], int m,
                                               int h) {
   using L = QLayout<D>;
+  static_assert(NACC == 1 || NACC == 2, "one or two accumulators");
   f32x16 acc[2] = {{}, {}};
   half8 ah[L::KS];
 #pragma unroll
@@ -231,14 +236,16 @@ __device__ __forceinline__ f32x16 rotate_tile(const _Float16 *xh, const _Float16
 #pragma unroll
   for (int s = 0; s < L::KS; ++s) {
     const half8 a0 = ah[s];
+    const int c = s % NACC;
     if constexpr (IN_F32) {
       half8 al = *(const half8 *)&xl[m * L::PITCH + 16 * s + 8 * h];
-      acc[s & 1] = mfma32(al, pih[s], acc[s & 1]);
+      acc[c] = mfma32(al, pih[s], acc[c]);
     }
-    acc[s & 1] = mfma32(a0, pil[s], acc[s & 1]);
-    acc[s & 1] = mfma32(a0, pih[s], acc[s & 1]);
+    acc[c] = mfma32(a0, pil[s], acc[c]);
+    acc[c] = mfma32(a0, pih[s], acc[c]);
   }
-  return acc[0] + acc[1];
+  if constexpr (NACC == 2) return acc[0] + acc[1];
+  return acc[0];
 }
 
 // Codes of the wave's 32 x 32 block: plane words go to outw (lane slot
@@ -308,6 +315,7 @@ __device__ __forceinline__ void code_block(const f32x16 &acc, const float *vinv,
   }
 }
 
+
 // Plane words of the block into their rows (rows past n_vec or a `live`
 // of false are dropped).
 template <int D, int LB, bool PROD>
@@ -330,32 +338,41 @@ __device__ __forceinline__ void store_planes(const i32x4 &rc, const uint32_t (&o
   }
 }
 
-// z = R M^T for rows [32wq, 32wq+32) of M (two alternating accumulators),
-// and the sign words of the block: lane 2r + hh holds the word of vector
-// 8(r/4)+4hh+r%4.
+// z = R M^T for rows [32wq, 32wq+32) of M from a staged residual tile.
 template <int D>
-__device__ __forceinline__ uint32_t sign_words(const _Float16 *rh, const _Float16 *rl,
-                                               const half8 (&mh)[D / 16], const half8 (&ml)[D / 16], int m,
-                                               int h) {
+__device__ __forceinline__ f32x16 sketch_tile(const _Float16 *rh, const _Float16 *rl, const half8 (&mh)[D / 16],
+                                              const half8 (&ml)[D / 16], int m, int h) {
   using L = QLayout<D>;
-  f32x16 accs[2] = {{}, {}};
+  f32x16 acc = {};
 #pragma unroll
   for (int s = 0; s < L::KS; ++s) {
     half8 ah = *(const half8 *)&rh[m * L::PITCH + 16 * s + 8 * h];
     half8 al = *(const half8 *)&rl[m * L::PITCH + 16 * s + 8 * h];
-    accs[s & 1] = mfma32(al, mh[s], accs[s & 1]);
-    accs[s & 1] = mfma32(ah, ml[s], accs[s & 1]);
-    accs[s & 1] = mfma32(ah, mh[s], accs[s & 1]);
+    acc = mfma32(al, mh[s], acc);
+    acc = mfma32(ah, ml[s], acc);
+    acc = mfma32(ah, mh[s], acc);
   }
-  const f32x16 acc2 = accs[0] + accs[1];
+  return acc;
+}
+
+// Sign words of a 32 x 32 block of z: lane 2r + hh holds the word of vector
+// 8(r/4)+4hh+r%4.
+__device__ __forceinline__ uint32_t sign_bits(const f32x16 &z) {
   uint32_t sw = 0u;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const uint64_t mk = __ballot(acc2[r] >= 0.0f);
+    const uint64_t mk = __ballot(z[r] >= 0.0f);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) sw = write_lane(sw, (uint32_t)(mk >> (32 * hh)), 2 * r + hh);
   }
   return sw;
+}
+
+template <int D>
+__device__ __forceinline__ uint32_t sign_words(const _Float16 *rh, const _Float16 *rl,
+                                               const half8 (&mh)[D / 16], const half8 (&ml)[D / 16], int m,
+                                               int h) {
+  return sign_bits(sketch_tile<D>(rh, rl, mh, ml, m, h));
 }
 
 // Sign words into the top plane of group wq (lanes 0..31; zero vectors get
@@ -490,41 +507,43 @@ __global__ __launch_bounds__(QLayout<D>::NT) void quantize_kernel(tqi::QuantizeA
   }
 }
 
-// Inner-product mode, producer / consumer split.  Waves [0, D/32) produce:
-// rotate and code tile k from xh[k%2] (staged in the previous iteration) and
-// write its residual to rh/rl[k%2].  Waves [D/32, D/16) consume: stage tile
-// k+1 into xh[(k+1)%2] and run the QJL projection, signs and residual norm
-// of tile k-1 from rh/rl[(k+1)%2].  Every buffer a side writes in iteration k
-// is read by the other side in iteration k+1, so one barrier per iteration
-// orders everything.  The loop runs one iteration past the last tile to
-// drain the consumers; work on a side's missing tile is done on stale data
-// and its stores are dropped, which keeps the loop free of branches.
+// Inner-product mode, three kinds of wave.  Waves [0, D/32) produce: rotate
+// and code tile k from xh[k%2] (staged in the previous iteration) and write
+// its residual to rh/rl[k%2].  Waves [D/32, D/16) sketch: the QJL projection
+// and sign words of tile k-1 from rh/rl[(k+1)%2].  Waves [D/16, 3D/32) stage:
+// tile k+1 into xh[(k+1)%2] from the prefetched input, then the residual norm
+// of tile k-1.  Every buffer a kind writes in iteration k is read by another
+// kind in a later iteration (vinv is a ring of four), so one barrier per
+// iteration orders everything.  The loop runs one iteration past the last
+// tile to drain the sketch; work on a missing tile is done on stale data and
+// its stores are dropped, which keeps the loop free of branches.  Only
+// producers and sketchers hold a stationary matrix, which keeps the kernel
+// within the 168 VGPRs that three waves per SIMD allow.
 template <int D, int LB, bool IN_F32>
-__global__ __launch_bounds__(2 * QLayout<D>::NT) void quantize_pc_kernel(tqi::QuantizeArgs a) {
+__global__ __launch_bounds__(3 * QLayout<D>::NT) void quantize_pc_kernel(tqi::QuantizeArgs a) {
   using L = QLayout<D>;
   constexpr int K = 1 << LB;
   constexpr int TILE = L::TILE;
-  constexpr int NWP = L::NW;        // producer waves
+  constexpr int NWP = L::NW;        // waves of each kind
   __shared__ __attribute__((aligned(16))) _Float16 xh[2][TILE];
   __shared__ __attribute__((aligned(16))) _Float16 xl[IN_F32 ? 2 : 1][IN_F32 ? TILE : 8];
   __shared__ __attribute__((aligned(16))) _Float16 rh[2][TILE];
   __shared__ __attribute__((aligned(16))) _Float16 rl[2][TILE];
-  __shared__ __attribute__((aligned(16))) float vinv[2][32];   // written by the stagers
-  __shared__ __attribute__((aligned(16))) float rinv[2][32];   // copy that travels with rh/rl
+  __shared__ __attribute__((aligned(16))) float vinv[4][32];   // tile j in slot j % 4
 
   const int tid = threadIdx.x;
   const int w = tid / kWave;
   const int l = lane_id();
   const int m = l & 31;
   const int h = l >> 5;
-  const bool producer = w < NWP;                // wave-uniform
-  const int wq = producer ? w : w - NWP;        // 32-row slice of Pi (producer) or M (consumer)
-  const int ct = tid - NWP * kWave;             // consumer thread: staging / residual-norm mapping
+  const int kind = w / NWP;                     // 0 produce, 1 sketch, 2 stage (wave-uniform)
+  const int wq = w % NWP;                       // 32-row slice of Pi (producer) or M (sketcher)
+  const int ct = tid - 2 * NWP * kWave;         // stager thread: staging / residual-norm mapping
   const int sv_v = ct / L::TPV;
   const int sv_c = ct % L::TPV;
 
   half8 sh[L::KS], sl[L::KS];
-  load_stationary<D>(producer ? a.pi : a.m, wq, sh, sl);
+  if (kind < 2) load_stationary<D>(kind == 0 ? a.pi : a.m, wq, sh, sl);
   float bnd[K - 1];
 #pragma unroll
   for (int k = 0; k < K - 1; ++k) bnd[k] = a.boundaries[k];
@@ -538,7 +557,7 @@ __global__ __launch_bounds__(2 * QLayout<D>::NT) void quantize_pc_kernel(tqi::Qu
   const int64_t t0 = blockIdx.x;
 
   RawInput<IN_F32> raw;
-  if (!producer) {
+  if (kind == 2) {
     load_raw<IN_F32>(res.rx, a.n_vec, a.x_stride, t0, sv_v, sv_c, raw);
     const uint16_t n16 = stage_vector<D, IN_F32>(raw, xh[0], xl[0], vinv[0], sv_v, sv_c);
     buf_store_u16<kWriteBack>(res.rn, (sv_c == 0 && t0 * 32 + sv_v < a.n_vec) ? (uint32_t)(2 * (t0 * 32 + sv_v)) : kNoStore,
@@ -548,28 +567,27 @@ __global__ __launch_bounds__(2 * QLayout<D>::NT) void quantize_pc_kernel(tqi::Qu
   __syncthreads();
   for (int k = 0;; ++k) {
     const int64_t tp = t0 + k * step;               // the producers' tile
-    if (tp >= n_tiles + step) break;                // consumers have drained
+    if (tp >= n_tiles + step) break;                // the sketch has drained
     const int kb = k & 1;
-    if (producer) {
-      const f32x16 acc = rotate_tile<D, IN_F32>(xh[kb], xl[IN_F32 ? kb : 0], sh, sl, m, h);
+    const int64_t tc = tp - step;                   // the sketch's tile
+    const bool live = k > 0;
+    if (kind == 0) {
+      const f32x16 acc = rotate_tile<D, IN_F32, 1>(xh[kb], xl[IN_F32 ? kb : 0], sh, sl, m, h);
       uint32_t outw[2];
-      code_block<D, LB, true>(acc, vinv[kb], bnd, cen, rh[kb], rl[kb], wq, m, h, outw);
+      code_block<D, LB, true>(acc, vinv[k & 3], bnd, cen, rh[kb], rl[kb], wq, m, h, outw);
       store_planes<D, LB, true>(res.rc, outw, tp * 32, a.n_vec, tp < n_tiles, wq, l);
-      if (tid < 32) rinv[kb][tid] = vinv[kb][tid];
+    } else if (kind == 1) {
+      const uint32_t sw = sign_words<D>(rh[kb ^ 1], rl[kb ^ 1], sh, sl, m, h);
+      store_signs<D, LB>(res.rc, sw, vinv[(k + 3) & 3], tc * 32, a.n_vec, live, wq, l);
     } else {
       // stage tile tp + step (zeros past the end), prefetch the one after
       const int64_t ts = tp + step;
-      const uint16_t n16 = stage_vector<D, IN_F32>(raw, xh[kb ^ 1], xl[IN_F32 ? kb ^ 1 : 0], vinv[kb ^ 1], sv_v, sv_c);
+      const uint16_t n16 = stage_vector<D, IN_F32>(raw, xh[kb ^ 1], xl[IN_F32 ? kb ^ 1 : 0], vinv[(k + 1) & 3], sv_v, sv_c);
       load_raw<IN_F32>(res.rx, a.n_vec, a.x_stride, ts + step, sv_v, sv_c, raw);
       __builtin_amdgcn_sched_barrier(0);
       buf_store_u16<kWriteBack>(res.rn, (sv_c == 0 && ts * 32 + sv_v < a.n_vec) ? (uint32_t)(2 * (ts * 32 + sv_v)) : kNoStore,
                                 n16);
-      // QJL projection of tile tp - step (from the previous iteration)
-      const int64_t tc = tp - step;
-      const bool live = k > 0;
-      const uint32_t sw = sign_words<D>(rh[kb ^ 1], rl[kb ^ 1], sh, sl, m, h);
-      store_signs<D, LB>(res.rc, sw, rinv[kb ^ 1], tc * 32, a.n_vec, live, wq, l);
-      const float gam = residual_norm<D>(rh[kb ^ 1], rl[kb ^ 1], rinv[kb ^ 1], sv_v, sv_c);
+      const float gam = residual_norm<D>(rh[kb ^ 1], rl[kb ^ 1], vinv[(k + 3) & 3], sv_v, sv_c);
       buf_store_u16<kWriteBack>(res.rr, (live && sv_c == 0 && tc * 32 + sv_v < a.n_vec) ? (uint32_t)(2 * (tc * 32 + sv_v)) : kNoStore,
                                 f32_to_f16_bits(gam));
     }
@@ -795,7 +813,7 @@ hipError_t launch_t(const tqi::QuantizeArgs &a, hipStream_t s) {
   const int64_t rows = rows_per_launch<D, LB, PROD, IN_F32>(a.x_stride);
   const int64_t esz = IN_F32 ? 4 : 2;
   if constexpr (PROD && D <= 128)
-    return launch_chunks(quantize_pc_kernel<D, LB, IN_F32>, 2 * L::NT, rows, esz, a, s);
+    return launch_chunks(quantize_pc_kernel<D, LB, IN_F32>, 3 * L::NT, rows, esz, a, s);
   else
     return launch_chunks(quantize_kernel<D, LB, PROD, IN_F32>, L::NT, rows, esz, a, s);
 }
