@@ -294,16 +294,24 @@ __global__ __launch_bounds__(DLayout<D>::NT) void dequant_kernel(tqi::DequantArg
       }
     }
     const f32x16 acc = accp[0] + accp[1];
+    // registers r and r + 1 hold rows v and v + 1 of the same column
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < 16; r += 2) {
       const int v = 8 * (r >> 2) + 4 * h + (r & 3);
-      float val = acc[r] * vfac[0][v];
-      if constexpr (PROD) val += acc2[r] * vfac[1][v];
+      float val0 = acc[r] * vfac[0][v], val1 = acc[r + 1] * vfac[0][v + 1];
+      if constexpr (PROD) {
+        val0 += acc2[r] * vfac[1][v];
+        val1 += acc2[r + 1] * vfac[1][v + 1];
+      }
       const int e = v * D + 32 * w + m;
-      if constexpr (OUT_F32)
-        ((float *)otile)[e] = val;
-      else
-        ((uint16_t *)otile)[e] = f32_to_bf16_bits(val);
+      if constexpr (OUT_F32) {
+        ((float *)otile)[e] = val0;
+        ((float *)otile)[e + D] = val1;
+      } else {
+        const uint32_t pk = f32x2_to_bf16x2_bits(val0, val1);
+        ((uint16_t *)otile)[e] = (uint16_t)pk;
+        ((uint16_t *)otile)[e + D] = (uint16_t)(pk >> 16);
+      }
     }
     __syncthreads();
     // 16-byte pieces of whole output rows; rows past n_vec are dropped

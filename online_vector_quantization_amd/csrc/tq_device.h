@@ -48,11 +48,17 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
   return b;
 }
 
+// fp32 -> bf16, round to nearest even (gfx950's v_cvt_pk_bf16_f32; NaN stays
+// NaN).  The pair form converts two values with one instruction: a in the low
+// half, b in the high half.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_bits(float a, float b) {
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
-  uint32_t u = __float_as_uint(v);
-  if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0xFFFF) ? 0x40 : 0));
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)v);
 }
 
 // Correctly rounded (nearest even) fp64 -> fp16 bits.  The value is first
