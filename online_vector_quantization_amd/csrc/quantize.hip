@@ -129,14 +129,18 @@ __device__ __forceinline__ float lanes_sum(float v) {
   return v;
 }
 
+// Maximum of non-negative values (magnitudes): on their bit patterns the
+// unsigned integer order is the float order, and 0 (the DPP fill value) is
+// the identity, so each step is a single v_max_u32 with a DPP operand.
 template <int N>
 __device__ __forceinline__ float lanes_max(float v) {
   static_assert(N == 4 || N == 8 || N == 16, "4, 8 or 16 lanes");
-  v = fmaxf(v, __uint_as_float(dpp_u32<0xB1>(__float_as_uint(v))));
-  v = fmaxf(v, __uint_as_float(dpp_u32<0x4E>(__float_as_uint(v))));
-  if constexpr (N >= 8) v = fmaxf(v, __uint_as_float(dpp_u32<0x141>(__float_as_uint(v))));
-  if constexpr (N >= 16) v = fmaxf(v, __uint_as_float(dpp_u32<0x140>(__float_as_uint(v))));
-  return v;
+  uint32_t u = __float_as_uint(v);
+  u = max(u, dpp_u32<0xB1>(u));
+  u = max(u, dpp_u32<0x4E>(u));
+  if constexpr (N >= 8) u = max(u, dpp_u32<0x141>(u));
+  if constexpr (N >= 16) u = max(u, dpp_u32<0x140>(u));
+  return __uint_as_float(u);
 }
 
 // Raw input of one staging thread: 16 consecutive elements of one vector.
