@@ -81,6 +81,31 @@ def test_quantize_parity(tq, d, bits, mode, dtype):
         assert cache.rnorm.cpu().numpy()[off + 3] == 0
 
 
+@pytest.mark.parametrize("mode", ["prod", "mse"])
+def test_quantize_parity_several_tiles_per_workgroup(tq, mode):
+    """Every output against the oracle when each workgroup of the persistent
+    grid loops over several tiles (at least four per workgroup at up to three
+    workgroups per CU, plus a ragged tail), so the kernels' buffer rotation
+    wraps several times."""
+    mcode = oqz.MODE_PROD if mode == "prod" else oqz.MODE_MSE
+    d, bits = 128, 3
+    n = 4 * 32 * 3 * torch.cuda.get_device_properties(DEV).multi_processor_count + 17
+    xb = _keys_bf16(d, n, seed=5)
+    x64 = _special_rows(bf16_to_f32(xb).astype(np.float64))
+    xt = dev_bf16(bf16_bits(x64.astype(np.float32)), DEV)
+    ot = OracleTables(d, bits, mcode)
+    ref = ot.quantize(x64)
+    qz = tq.Quantizer(d, bits, mcode, seed=0, device=DEV)
+    cache = qz.quantize(xt)
+    torch.cuda.synchronize()
+    codes = cache.codes.cpu().numpy()
+    check_codes(codes, ref, ot.lb, d, ot.t, mcode)
+    check_norms(cache.norm.cpu().numpy(), ref)
+    if mcode == oqz.MODE_PROD:
+        check_signs(codes, ref, ot.lb, d)
+        check_rnorm(cache.rnorm.cpu().numpy(), ref)
+
+
 def _gqa_case(d, bits, mode, bsz, hkv, group, seq, qdtype, seed=0, row_tokens=None):
     """Oracle-packed cache [bsz, hkv, row_tokens] and queries; returns everything."""
     mcode = oqz.MODE_PROD if mode == "prod" else oqz.MODE_MSE
