@@ -533,7 +533,7 @@ __global__ __launch_bounds__(3 * QLayout<D>::NT) void quantize_pc_kernel(tqi::Qu
   __shared__ __attribute__((aligned(16))) _Float16 xl[IN_F32 ? 2 : 1][IN_F32 ? TILE : 8];
   __shared__ __attribute__((aligned(16))) _Float16 rh[2][TILE];
   __shared__ __attribute__((aligned(16))) _Float16 rl[2][TILE];
-  __shared__ __attribute__((aligned(16))) float vinv[4][32];   // tile j in slot j % 4
+  __shared__ __attribute__((aligned(16))) float vinv[4][32];   // this workgroup's k-th tile in slot k % 4
 
   const int tid = threadIdx.x;
   const int w = tid / kWave;
