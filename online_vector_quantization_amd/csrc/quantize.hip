@@ -143,6 +143,29 @@ __device__ __forceinline__ float lanes_max(float v) {
   return __uint_as_float(u);
 }
 
+// OR over the N consecutive lanes of a vector (same DPP steps as lanes_sum).
+template <int N>
+__device__ __forceinline__ uint32_t lanes_or(uint32_t v) {
+  static_assert(N == 4 || N == 8 || N == 16, "4, 8 or 16 lanes");
+  v |= dpp_u32<0xB1>(v);
+  v |= dpp_u32<0x4E>(v);
+  if constexpr (N >= 8) v |= dpp_u32<0x141>(v);
+  if constexpr (N >= 16) v |= dpp_u32<0x140>(v);
+  return v;
+}
+
+// Value of a lane in the other half of this lane's aligned group of
+// 2 * SPAN lanes (SPAN = 1, 2, 4, 8): the pair neighbour, the other pair of
+// the quad, the mirrored lane of the 8 (7 - i) or of the 16 (15 - i).  Where
+// the values are uniform over aligned groups of SPAN lanes, this is the
+// value of the group's partner group.
+template <int SPAN>
+__device__ __forceinline__ float partner_half(float v) {
+  static_assert(SPAN == 1 || SPAN == 2 || SPAN == 4 || SPAN == 8, "span");
+  constexpr int CTRL = SPAN == 1 ? 0xB1 : SPAN == 2 ? 0x4E : SPAN == 4 ? 0x141 : 0x140;
+  return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+
 // Raw input of one staging thread: 16 consecutive elements of one vector.
 template <bool IN_F32>
 struct RawInput {
@@ -739,28 +762,27 @@ __global__ __launch_bounds__(QLayout<D>::NT) void quantize_polar_kernel(tqi::Qua
       r3[i] = r2[2 * i] + r2[2 * i + 1];
     }
     put(4, sv_c, angle(r3[0], r3[1], 4));
+    // levels 5..LV across threads: rr is uniform over each aligned group of
+    // `span` threads, so any lane of the partner group supplies its radius
     float rr = r3[0] + r3[1];
-#pragma unroll
-    for (int level = 5; level <= P::LV; ++level) {
-      const int span = 1 << (level - 5);     // threads per half at this level
-      const float other = wave_xor(rr, span);
+    auto level_step = [&](auto span_c, int level) __attribute__((always_inline)) {
+      constexpr int span = decltype(span_c)::value;   // threads per half at this level
+      const float other = partner_half<span>(rr);
       if ((sv_c & (2 * span - 1)) == 0) put(level, sv_c >> (level - 4), angle(rr, other, level));
       rr += other;
-    }
+    };
+    level_step(std::integral_constant<int, 1>(), 5);
+    if constexpr (P::LV >= 6) level_step(std::integral_constant<int, 2>(), 6);
+    if constexpr (P::LV >= 7) level_step(std::integral_constant<int, 4>(), 7);
+    if constexpr (P::LV >= 8) level_step(std::integral_constant<int, 8>(), 8);
     // level-1 plane words: 8 bits per thread, 4 threads per 32-slot group
     uint32_t wl[4];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      wl[p] = b1[p] << (8 * (sv_c & 3));
-      wl[p] |= wave_xor(wl[p], 1);
-      wl[p] |= wave_xor(wl[p], 2);
-    }
+    for (int p = 0; p < 4; ++p) wl[p] = lanes_or<4>(b1[p] << (8 * (sv_c & 3)));
 #pragma unroll
     for (int g = 0; g < P::NGU; ++g)
 #pragma unroll
-      for (int p = 0; p < 2; ++p)
-#pragma unroll
-        for (int off = 1; off < L::TPV; off <<= 1) bu[g][p] |= wave_xor(bu[g][p], off);
+      for (int p = 0; p < 2; ++p) bu[g][p] = lanes_or<L::TPV>(bu[g][p]);
     const uint32_t row = (uint32_t)((base + sv_v) * P::RB);
     uint32_t wv1 = wl[0];
 #pragma unroll
