@@ -217,14 +217,16 @@ __device__ __forceinline__ uint16_t stage_vector(const RawInput<IN_F32> &r, _Flo
   ss = lanes_sum<L::TPV>(ss);
   mx = lanes_max<L::TPV>(mx);
   // exponent of the largest element (frexp's is one above ilogb's; a zero
-  // vector gets 0 and stays zero)
+  // vector gets -1 and stays zero).  The scale 2^se can exceed the fp32
+  // range for tiny vectors (se up to 163), so it is applied with v_ldexp_f32,
+  // which is exact without forming 2^se.
   int e = __builtin_amdgcn_frexp_expf(mx) - 1;
-  e = e < -140 ? -140 : (e > 127 ? 127 : e);
-  const float sc = ldexpf(1.0f, 14 - e);
+  e = e < -149 ? -149 : (e > 127 ? 127 : e);
+  const int se = 14 - e;
   half8 hv[2], lv[2];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const float sv = xv[i] * sc;
+    const float sv = ldexpf(xv[i], se);
     const _Float16 hh = (_Float16)sv;
     hv[i >> 3][i & 7] = hh;
     if constexpr (IN_F32) lv[i >> 3][i & 7] = (_Float16)(sv - (float)hh);
@@ -239,7 +241,7 @@ __device__ __forceinline__ uint16_t stage_vector(const RawInput<IN_F32> &r, _Flo
   }
   // 1 / (sc * 2^8 * |x|): the scaled sum of squares lies in [2^28, 2^37),
   // so fp32 holds it; v_rsq_f32 is good to about one ulp.
-  const float ss_sc = (float)(ss * ((double)sc * (double)sc));
+  const float ss_sc = (float)ldexp(ss, 2 * se);
   const float inv_n = ss > 0.0 ? __builtin_amdgcn_rsqf(ss_sc) * (1.0f / kPiScale) : 0.0f;
   vinv[sv_v] = inv_n;        // the vector's threads all hold the same value
   return f64_to_f16_bits(sqrt(ss));

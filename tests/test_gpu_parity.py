@@ -36,6 +36,14 @@ def _special_rows(x64):
     x64[3] = 0.0                     # zero vector
     x64[7] = 0.0
     x64[7, 5] = 2.5                  # one nonzero coordinate
+    d = x64.shape[1]
+    j = np.arange(d)
+    sign = np.where(j % 3 == 0, -1.0, 1.0)
+    # tiny vectors, exact in bf16 and fp32: normal numbers with the largest
+    # exponent -118, and subnormals k * 2^-133 (bf16's smallest step); their
+    # fp16 norms round to 0, their directions still define the codes
+    x64[11] = sign * (1.0 + (j * 37 % 128) / 128.0) * np.ldexp(1.0, -118 - (j % 5))
+    x64[13] = sign * (1 + j * 11 % 127) * np.ldexp(1.0, -133)
     return x64
 
 
