@@ -1,0 +1,50 @@
+"""Host-side checks of bench.py's command-line contract and its traffic table.
+
+These run without a GPU: bench.py measures one GPU only and must refuse more
+before it touches the device; the committed HBM-traffic table must be well
+formed, and where its entry for the dominant kernel is current (taken on the
+present sources; otherwise bench.py reports null) it must match the kernel's
+algorithmic bytes.
+"""
+
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+@pytest.mark.parametrize("n", [2, 8])
+def test_more_than_one_gpu_is_refused(n):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", str(n)],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_traffic_table_has_counters_and_calibration():
+    with open(os.path.join(ROOT, "profiles", "hbm_traffic.json")) as f:
+        table = json.load(f)
+    entries = {k: v for k, v in table.items() if not k.startswith("_")}
+    assert "quantize_pc_kernel:quantize_k" in entries
+    for key, e in entries.items():
+        assert e["fetch_kib"] > 0 and e["write_kib"] > 0, key
+        assert 1.5 < e["fetch_scale"] < 2.5 and 0.5 < e["write_scale"] < 1.5, key
+        assert len(e["source_sha"]) == 16 and e["dispatches"] >= 1, key
+
+
+def test_traffic_of_the_dominant_kernel_matches_its_algorithmic_bytes():
+    # the decode step's dominant call: the counters were taken on these sources
+    t = bench._traffic("quantize_pc_kernel:quantize_k", ["quantize.hip", "tq_device.h"])
+    if t is None:
+        pytest.skip("kernel sources changed since the counters were taken (bench reports null)")
+    # within a few percent of the algorithmic bytes per launch (262144 keys:
+    # 256 B read, 48 B of codes and signs and 4 B of norms written)
+    assert abs(t / (262144 * (256 + 48 + 4)) - 1.0) < 0.05
