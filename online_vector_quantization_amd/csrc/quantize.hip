@@ -634,10 +634,10 @@ __global__ __launch_bounds__(3 * QLayout<D>::NT) void quantize_pc_kernel(tqi::Qu
 //     local angle against pi/8, pi/4, 3pi/8 as b^2 >= tan^2(beta) a^2;
 //   level l >= 2: psi >= beta  <=>  R_b >= tan^2(beta) R_a, R the squared
 //     radii of the two halves (an angle of a zero block, R_b = 0, is 0).
-// Levels 2..4 stay inside a thread, the rest pair threads by xor shuffles.
+// Levels 2..4 stay inside a thread, the rest pair threads by DPP steps.
 // Codes: 4 level-1 planes (word 4g + p), then 2 planes of the higher levels
 // in level order (word D/16 + 2g + p); bits are gathered with or-reductions
-// over the vector's threads.
+// over the vector's threads (DPP steps as well).
 template <int D>
 struct PolarLayout {
   static constexpr int LV = D == 64 ? 6 : (D == 128 ? 7 : 8);   // levels

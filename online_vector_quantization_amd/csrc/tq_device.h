@@ -178,9 +178,4 @@ __device__ __forceinline__ void buf_store_u16(i32x4 rsrc, uint32_t off, uint16_t
   tq_llvm_buf_st_b16((short)v, rsrc, (int)off, 0, AUX);
 }
 
-template <typename T>
-__device__ __forceinline__ T wave_xor(T v, int mask) {
-  return __shfl_xor(v, mask, kWave);
-}
-
 }  // namespace tqd
