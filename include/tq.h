@@ -22,13 +22,18 @@
  *     hipStream_t passed as void*, NULL = the null stream).  Launch errors
  *     return TQ_ERR_HIP; faults inside a kernel surface at the caller's next
  *     synchronisation, as with any HIP launch.
- *   - tq_attn_logits (and tq_append_attn_logits) needs device scratch memory (query tables, partial top-k
- *     lists).  The library keeps one scratch buffer per (device, stream) pair
- *     between calls: the first call on a stream, or a call that needs more,
- *     synchronises that stream and allocates with hipMalloc; the buffer lives
- *     until the process ends.  Work on one stream runs in order, so calls on
- *     the same stream share their buffer safely; other streams get their own.
- *   - Apart from that cache the library keeps no state; calls are thread-safe.
+ *   - The library never allocates or frees memory, never synchronises and
+ *     keeps no state between calls (apart from a per-device cache of the
+ *     compute-unit count, set once).  Calls that need device scratch memory
+ *     (tq_attn_logits, tq_append_attn_logits, tq_attn_output) take a
+ *     caller-owned `workspace` of `workspace_bytes` bytes: 256-byte aligned
+ *     device memory of at least the size the matching *_workspace_size query
+ *     gives for the same arguments on the current device.  It is borrowed
+ *     until the queued work completes, so calls that may overlap in time
+ *     (other streams, other host threads) need workspaces of their own.  A
+ *     NULL workspace is accepted where the query returns 0.
+ *   - Calls are reentrant and thread-safe: nothing is shared between calls
+ *     except what the caller passes in.
  *
  * Packed format of one vector (d coordinates, b total bits per coordinate)
  *   mode TQ_MODE_MSE : b' = b Lloyd-Max bits.     1 <= b <= 4
@@ -71,6 +76,7 @@
 #ifndef TQ_H
 #define TQ_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -167,6 +173,16 @@ tq_status tq_quantize_kv(const tq_params *p, const void *x, int32_t x_dtype, int
                          int64_t x_row_stride, const tq_packed *out, int64_t out_offset,
                          void *stream);
 
+/* Device scratch that tq_attn_logits needs for these arguments on the current
+ * device (the same validation as the call itself: an unsupported shape
+ * returns TQ_ERR_UNSUPPORTED).  Dense logits need the query tables: a few KB
+ * per (batch, kv head) stream; top-k search needs its partial lists.  The
+ * size for tq_append_attn_logits is this query with seq_len = pos + 1 and
+ * topk = 0.  *bytes is 0 for empty calls.
+ * Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED. */
+tq_status tq_attn_logits_workspace_size(const tq_params *p, int32_t batch, int32_t n_q_heads,
+                                        int32_t n_kv_heads, int64_t seq_len, int32_t topk, size_t *bytes);
+
 /* Attention logits straight from packed keys (page: the query is rotated
  * once and logits come from the indices without reconstructing the keys).
  *   q            device [batch][n_q_heads][d], q_dtype TQ_F32 or TQ_BF16
@@ -179,16 +195,22 @@ tq_status tq_quantize_kv(const tq_params *p, const void *x, int32_t x_dtype, int
  *                ties to the smaller token index, descending; logits is
  *                fp32 [batch][n_q_heads][topk] and topk_idx int32 of the same
  *                shape.  Needs seq_len >= topk.
+ *   workspace    device scratch of tq_attn_logits_workspace_size bytes
  * GQA: query head h reads KV head h / (n_q_heads / n_kv_heads); n_q_heads
  * must be a multiple of n_kv_heads.  Dense logits support d in {128, 256},
- * up to 16 query heads per KV head, and streams whose packed codes and
- * logits each stay under 4 GiB; top-k supports MSE mode, d in {128, 256},
- * topk <= 16.  seq_len == 0 is a no-op.
+ * up to 16 query heads per KV head, streams whose packed codes stay under
+ * 2 GiB and whose logits (group x seq_len fp32) stay under 2 GiB; top-k
+ * supports MSE mode, d in {128, 256}, topk <= 16, seq_len < 2^30.
+ * (d = 64 keys are quantised and reconstructed but have no logit kernel.)
+ * seq_len == 0 is a no-op.  A workspace smaller than the query's size, or
+ * NULL where it is not 0, is TQ_ERR_INVALID; a misaligned one
+ * TQ_ERR_UNSUPPORTED.
  * Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED, TQ_ERR_HIP. */
 tq_status tq_attn_logits(const tq_params *p, const void *q, int32_t q_dtype, int32_t batch,
                          int32_t n_q_heads, int32_t n_kv_heads, const tq_packed *k,
                          int64_t row_tokens, int64_t seq_len, float scale, float *logits,
-                         int32_t topk, int32_t *topk_idx, void *stream);
+                         int32_t topk, int32_t *topk_idx, void *workspace, size_t workspace_bytes,
+                         void *stream);
 
 /* Decode step with append: quantise one new key per (batch, kv head) stream
  * into the cache at token pos, then form the logits over tokens 0..pos of
@@ -202,6 +224,8 @@ tq_status tq_attn_logits(const tq_params *p, const void *q, int32_t q_dtype, int
  *                read (tokens 0..pos-1 must already hold packed keys)
  *   pos          0 <= pos < row_tokens
  *   logits       device fp32 [batch][n_q_heads][pos + 1]
+ *   workspace    device scratch of tq_attn_logits_workspace_size(p, batch,
+ *                n_q_heads, n_kv_heads, pos + 1, 0) bytes
  * The new key is quantised in fp64 from the fp32 matrices (the inner-product
  * mode needs p->qjl_rot).  Supported: as dense tq_attn_logits (d in {128,
  * 256}, up to 16 query heads per KV head).  batch == 0 is a no-op.
@@ -209,7 +233,8 @@ tq_status tq_attn_logits(const tq_params *p, const void *q, int32_t q_dtype, int
 tq_status tq_append_attn_logits(const tq_params *p, const void *x_new, int32_t x_dtype,
                                 const void *q, int32_t q_dtype, int32_t batch, int32_t n_q_heads,
                                 int32_t n_kv_heads, const tq_packed *k, int64_t row_tokens,
-                                int64_t pos, float scale, float *logits, void *stream);
+                                int64_t pos, float scale, float *logits, void *workspace,
+                                size_t workspace_bytes, void *stream);
 
 /* Decode attention output straight from packed values (page: the KV cache
  * holds keys and values, section "TurboQuant란 무엇인가요?", and attention runs
@@ -222,12 +247,21 @@ tq_status tq_append_attn_logits(const tq_params *p, const void *x_new, int32_t x
  *                o = sum_t softmax(logits)_t v_hat_t over the seq_len tokens of
  *                the query head's KV head (GQA as in tq_attn_logits); a head
  *                whose logits are all -inf, or seq_len == 0, gives o = 0.
+ *   workspace    device scratch of tq_attn_output_workspace_size bytes (the
+ *                per-split partial maxima, sums and accumulators)
  * Supported: MSE mode, d in {128, 256}, up to 16 query heads per KV head,
- * 16-byte aligned value codes.  Uses library scratch memory (per device and
- * stream).  Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED, TQ_ERR_HIP. */
+ * 16-byte aligned value codes, packed values of one stream under 2 GiB.
+ * Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED, TQ_ERR_HIP. */
 tq_status tq_attn_output(const tq_params *p, const float *logits, int32_t batch, int32_t n_q_heads,
                          int32_t n_kv_heads, const tq_packed *v, int64_t row_tokens, int64_t seq_len,
-                         void *out, int32_t out_dtype, void *stream);
+                         void *out, int32_t out_dtype, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/* Device scratch that tq_attn_output needs for these arguments on the
+ * current device; 0 when seq_len or batch is 0.
+ * Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED. */
+tq_status tq_attn_output_workspace_size(const tq_params *p, int32_t batch, int32_t n_q_heads,
+                                        int32_t n_kv_heads, int64_t seq_len, size_t *bytes);
 
 /* Reconstruct n_vec vectors (page section "2단계": reconstructed vectors).
  *   out          device [n_vec][d], out_dtype TQ_F32 or TQ_BF16

@@ -34,8 +34,9 @@ KIND_PI = 0
 KIND_S = 1
 KIND_M = 2
 
-EXPORTED = ["tq_make_codebook", "tq_make_polar_codebook", "tq_make_rotation", "tq_quantize_kv", "tq_attn_logits",
-            "tq_append_attn_logits", "tq_attn_output", "tq_dequantize", "tq_status_string"]
+EXPORTED = ["tq_make_codebook", "tq_make_polar_codebook", "tq_make_rotation", "tq_quantize_kv",
+            "tq_attn_logits_workspace_size", "tq_attn_logits", "tq_append_attn_logits",
+            "tq_attn_output_workspace_size", "tq_attn_output", "tq_dequantize", "tq_status_string"]
 
 
 class TQError(RuntimeError):
@@ -65,17 +66,19 @@ def _load():
     lib.tq_make_rotation.argtypes = [i32, ctypes.c_uint64, i32, vp]
     lib.tq_quantize_kv.argtypes = [ctypes.POINTER(Params), vp, i32, i64, i64, ctypes.POINTER(Packed),
                                    i64, vp]
+    sz, psz = ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)
+    lib.tq_attn_logits_workspace_size.argtypes = [ctypes.POINTER(Params), i32, i32, i32, i64, i32, psz]
     lib.tq_attn_logits.argtypes = [ctypes.POINTER(Params), vp, i32, i32, i32, i32,
-                                   ctypes.POINTER(Packed), i64, i64, f32, vp, i32, vp, vp]
+                                   ctypes.POINTER(Packed), i64, i64, f32, vp, i32, vp, vp, sz, vp]
     lib.tq_append_attn_logits.argtypes = [ctypes.POINTER(Params), vp, i32, vp, i32, i32, i32, i32,
-                                          ctypes.POINTER(Packed), i64, i64, f32, vp, vp]
+                                          ctypes.POINTER(Packed), i64, i64, f32, vp, vp, sz, vp]
+    lib.tq_attn_output_workspace_size.argtypes = [ctypes.POINTER(Params), i32, i32, i32, i64, psz]
     lib.tq_attn_output.argtypes = [ctypes.POINTER(Params), vp, i32, i32, i32, ctypes.POINTER(Packed),
-                                   i64, i64, vp, i32, vp]
+                                   i64, i64, vp, i32, vp, sz, vp]
     lib.tq_dequantize.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(Packed), i64, vp, i32, vp]
     lib.tq_status_string.argtypes = [i32]
     lib.tq_status_string.restype = ctypes.c_char_p
-    for name in ("tq_make_codebook", "tq_make_polar_codebook", "tq_make_rotation", "tq_quantize_kv", "tq_attn_logits",
-                 "tq_append_attn_logits", "tq_attn_output", "tq_dequantize"):
+    for name in EXPORTED[:-1]:
         getattr(lib, name).restype = i32
     return lib
 
@@ -207,6 +210,40 @@ class Quantizer:
                               self.s.data_ptr() if self.s is not None else None,
                               self.m.data_ptr() if self.m is not None else None,
                               self.centroids.data_ptr(), self.boundaries.data_ptr())
+        self._ws = {}       # stream handle -> uint8 device tensor (workspace of the calls on it)
+
+    def logits_workspace_size(self, batch, n_q_heads, n_kv_heads, seq_len, topk=0):
+        """Bytes of device scratch tq_attn_logits needs for this shape."""
+        n = ctypes.c_size_t(0)
+        _check(LIB.tq_attn_logits_workspace_size(ctypes.byref(self._params), batch, n_q_heads, n_kv_heads,
+                                                 seq_len, topk, ctypes.byref(n)), "tq_attn_logits_workspace_size")
+        return n.value
+
+    def attn_output_workspace_size(self, batch, n_q_heads, n_kv_heads, seq_len):
+        """Bytes of device scratch tq_attn_output needs for this shape."""
+        n = ctypes.c_size_t(0)
+        _check(LIB.tq_attn_output_workspace_size(ctypes.byref(self._params), batch, n_q_heads, n_kv_heads,
+                                                 seq_len, ctypes.byref(n)), "tq_attn_output_workspace_size")
+        return n.value
+
+    def _workspace(self, nbytes, workspace):
+        """(pointer, bytes) of a workspace of at least nbytes: the caller's
+        tensor, or a device buffer kept per stream (calls queued on one stream
+        run in order, so they can share it)."""
+        if workspace is not None:
+            if workspace.numel() * workspace.element_size() < nbytes:
+                raise ValueError("workspace holds %d bytes, the call needs %d"
+                                 % (workspace.numel() * workspace.element_size(), nbytes))
+            return ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
+        if nbytes == 0:
+            return None, 0
+        torch = _torch()
+        key = torch.cuda.current_stream(self.device).cuda_stream
+        buf = self._ws.get(key)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+            self._ws[key] = buf
+        return ctypes.c_void_p(buf.data_ptr()), buf.numel()
 
     def new_cache(self, capacity):
         return PackedKV(self.d, self.bits, self.mode, capacity, self.device)
@@ -224,21 +261,23 @@ class Quantizer:
         _check(st, "tq_quantize_kv")
         return out
 
-    def attn_logits(self, q, cache, n_kv_heads, seq_len, scale, row_tokens=None, out=None):
+    def attn_logits(self, q, cache, n_kv_heads, seq_len, scale, row_tokens=None, out=None, workspace=None):
         """Dense logits [batch, n_q_heads, seq_len] (fp32)."""
         torch = _torch()
         bsz, hq, _ = q.shape
         row_tokens = seq_len if row_tokens is None else row_tokens
         if out is None:
             out = torch.empty((bsz, hq, seq_len), dtype=torch.float32, device=self.device)
+        ws, wsb = self._workspace(self.logits_workspace_size(bsz, hq, n_kv_heads, seq_len), workspace)
         st = LIB.tq_attn_logits(ctypes.byref(self._params), ctypes.c_void_p(q.data_ptr()),
                                 _dtype_code(q), bsz, hq, n_kv_heads, ctypes.byref(cache.struct()),
                                 row_tokens, seq_len, float(scale), ctypes.c_void_p(out.data_ptr()),
-                                0, None, _stream_ptr(self.device))
+                                0, None, ws, wsb, _stream_ptr(self.device))
         _check(st, "tq_attn_logits")
         return out
 
-    def append_attn_logits(self, x_new, q, cache, n_kv_heads, pos, scale, row_tokens=None, out=None):
+    def append_attn_logits(self, x_new, q, cache, n_kv_heads, pos, scale, row_tokens=None, out=None,
+                           workspace=None):
         """Quantise x_new [batch, n_kv_heads, d] into token ``pos`` of every stream of
         ``cache`` and return the logits [batch, n_q_heads, pos + 1] (fp32)."""
         torch = _torch()
@@ -247,28 +286,33 @@ class Quantizer:
             row_tokens = cache.capacity // max(bsz * n_kv_heads, 1)
         if out is None:
             out = torch.empty((bsz, hq, pos + 1), dtype=torch.float32, device=self.device)
+        need = self.logits_workspace_size(bsz, hq, n_kv_heads, pos + 1) if 0 <= pos < row_tokens else 0
+        ws, wsb = self._workspace(need, workspace)
         st = LIB.tq_append_attn_logits(ctypes.byref(self._params), ctypes.c_void_p(x_new.data_ptr()),
                                        _dtype_code(x_new), ctypes.c_void_p(q.data_ptr()), _dtype_code(q),
                                        bsz, hq, n_kv_heads, ctypes.byref(cache.struct()), row_tokens, pos,
-                                       float(scale), ctypes.c_void_p(out.data_ptr()), _stream_ptr(self.device))
+                                       float(scale), ctypes.c_void_p(out.data_ptr()), ws, wsb,
+                                       _stream_ptr(self.device))
         _check(st, "tq_append_attn_logits")
         return out
 
-    def search(self, q, cache, n_kv_heads, seq_len, topk, scale=1.0, row_tokens=None):
+    def search(self, q, cache, n_kv_heads, seq_len, topk, scale=1.0, row_tokens=None, workspace=None):
         """Top-k (scores, indices), each [batch, n_q_heads, topk]."""
         torch = _torch()
         bsz, hq, _ = q.shape
         row_tokens = seq_len if row_tokens is None else row_tokens
         vals = torch.empty((bsz, hq, topk), dtype=torch.float32, device=self.device)
         idx = torch.empty((bsz, hq, topk), dtype=torch.int32, device=self.device)
+        ws, wsb = self._workspace(self.logits_workspace_size(bsz, hq, n_kv_heads, seq_len, topk), workspace)
         st = LIB.tq_attn_logits(ctypes.byref(self._params), ctypes.c_void_p(q.data_ptr()),
                                 _dtype_code(q), bsz, hq, n_kv_heads, ctypes.byref(cache.struct()),
                                 row_tokens, seq_len, float(scale), ctypes.c_void_p(vals.data_ptr()),
-                                topk, ctypes.c_void_p(idx.data_ptr()), _stream_ptr(self.device))
+                                topk, ctypes.c_void_p(idx.data_ptr()), ws, wsb, _stream_ptr(self.device))
         _check(st, "tq_attn_logits(topk)")
         return vals, idx
 
-    def attn_output(self, logits, cache, n_kv_heads, seq_len, row_tokens=None, out_dtype=None, out=None):
+    def attn_output(self, logits, cache, n_kv_heads, seq_len, row_tokens=None, out_dtype=None, out=None,
+                    workspace=None):
         """Decode attention output [batch, n_q_heads, d]: softmax(logits) . values."""
         torch = _torch()
         bsz, hq, _ = logits.shape
@@ -276,9 +320,11 @@ class Quantizer:
         out_dtype = torch.float32 if out_dtype is None else out_dtype
         if out is None:
             out = torch.empty((bsz, hq, self.d), dtype=out_dtype, device=self.device)
+        ws, wsb = self._workspace(self.attn_output_workspace_size(bsz, hq, n_kv_heads, seq_len), workspace)
         st = LIB.tq_attn_output(ctypes.byref(self._params), ctypes.c_void_p(logits.data_ptr()), bsz, hq,
                                 n_kv_heads, ctypes.byref(cache.struct()), row_tokens, seq_len,
-                                ctypes.c_void_p(out.data_ptr()), _dtype_code(out), _stream_ptr(self.device))
+                                ctypes.c_void_p(out.data_ptr()), _dtype_code(out), ws, wsb,
+                                _stream_ptr(self.device))
         _check(st, "tq_attn_output")
         return out
 

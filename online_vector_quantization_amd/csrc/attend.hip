@@ -36,13 +36,9 @@ namespace {
 
 using namespace tqd;
 
-#ifndef TQ_ATT_WAVES
-#define TQ_ATT_WAVES 4
-#endif
-#ifndef TQ_ATT_BLOCKS_PER_CU
-#define TQ_ATT_BLOCKS_PER_CU 2
-#endif
-constexpr int kAttThreads = 64 * TQ_ATT_WAVES;
+constexpr int kAttWaves = 4;         // waves per split workgroup
+constexpr int kAttBlocksPerCu = 2;   // split workgroups per CU the launch aims for
+constexpr int kAttThreads = 64 * kAttWaves;
 constexpr int kChunk = 64;          // tokens per wave step (one per lane)
 
 struct PartArgs {
@@ -713,26 +709,41 @@ __global__ __launch_bounds__(4 * D) void attend_combine_kernel(CombArgs a) {
   }
 }
 
+// Token splits of one call: a few workgroups per CU in all, at least 256
+// tokens each, a whole number of chunks per split.
+struct AttendPlan {
+  int64_t splits, tps;
+};
+
+AttendPlan attend_plan(int64_t n_streams, int64_t seq_len) {
+  const int64_t cus = tqi::device_cu_count();
+  int64_t splits = (kAttBlocksPerCu * cus + n_streams - 1) / n_streams;
+  const int64_t max_splits = (seq_len + 255) / 256;
+  if (splits > max_splits) splits = max_splits;
+  if (splits > 256) splits = 256;
+  if (splits < 1) splits = 1;
+  int64_t tps = (seq_len + splits - 1) / splits;
+  tps = (tps + kChunk - 1) / kChunk * kChunk;
+  AttendPlan p;
+  p.tps = tps;
+  p.splits = seq_len > 0 ? (seq_len + tps - 1) / tps : 0;
+  return p;
+}
+
+int group_bucket(int group) {
+  return group <= 1 ? 1 : group <= 2 ? 2 : group <= 4 ? 4 : group <= 8 ? 8 : 16;
+}
+
 template <int D, int LB, int G>
 hipError_t launch_t(const tqi::AttendArgs &aa, hipStream_t s) {
   const int group = aa.n_q_heads / aa.n_kv_heads;
   const int64_t n_streams = (int64_t)aa.batch * aa.n_kv_heads;
-  // splits: a few workgroups per CU in all, at least 256 tokens each
-  const int64_t cus = tqi::device_cu_count();
-  int64_t splits = (TQ_ATT_BLOCKS_PER_CU * cus + n_streams - 1) / n_streams;
-  const int64_t max_splits = (aa.seq_len + 255) / 256;
-  if (splits > max_splits) splits = max_splits;
-  if (splits > 256) splits = 256;
-  if (splits < 1) splits = 1;
-  int64_t tps = (aa.seq_len + splits - 1) / splits;
-  tps = (tps + kChunk - 1) / kChunk * kChunk;
-  splits = aa.seq_len > 0 ? (aa.seq_len + tps - 1) / tps : 0;
-  constexpr int RB = LB * D / 8;
-  if ((tps + kChunk) * RB >= (1LL << 31)) return hipErrorInvalidValue;
-  const size_t bytes = (size_t)n_streams * (splits > 0 ? splits : 1) * G * (D + 2) * sizeof(float);
-  float *part = nullptr;
-  hipError_t e = tqi::workspace(s, bytes, (void **)&part);
-  if (e != hipSuccess) return e;
+  const AttendPlan plan = attend_plan(n_streams, aa.seq_len);
+  const int64_t splits = plan.splits, tps = plan.tps;
+  const size_t bytes = (size_t)n_streams * splits * G * (D + 2) * sizeof(float);
+  if (aa.workspace_bytes < bytes) return hipErrorInvalidValue;    // checked by the caller
+  float *part = (float *)aa.workspace;
+  hipError_t e = hipSuccess;
   if (splits > 0) {
     PartArgs pa;
     pa.logits = aa.logits;
@@ -772,39 +783,52 @@ hipError_t launch_t(const tqi::AttendArgs &aa, hipStream_t s) {
 }
 
 template <int D, int LB>
-hipError_t launch_g(const tqi::AttendArgs &a, hipStream_t s, bool *ok) {
-  const int group = a.n_q_heads / a.n_kv_heads;
-  *ok = true;
-  if (group <= 1) return launch_t<D, LB, 1>(a, s);
-  if (group <= 2) return launch_t<D, LB, 2>(a, s);
-  if (group <= 4) return launch_t<D, LB, 4>(a, s);
-  if (group <= 8) return launch_t<D, LB, 8>(a, s);
-  if (group <= 16) return launch_t<D, LB, 16>(a, s);
-  *ok = false;
-  return hipSuccess;
+hipError_t launch_g(const tqi::AttendArgs &a, hipStream_t s) {
+  switch (group_bucket(a.n_q_heads / a.n_kv_heads)) {
+    case 1: return launch_t<D, LB, 1>(a, s);
+    case 2: return launch_t<D, LB, 2>(a, s);
+    case 4: return launch_t<D, LB, 4>(a, s);
+    case 8: return launch_t<D, LB, 8>(a, s);
+  }
+  return launch_t<D, LB, 16>(a, s);
 }
 
 template <int D>
-hipError_t launch_lb(int lb, const tqi::AttendArgs &a, hipStream_t s, bool *ok) {
+hipError_t launch_lb(int lb, const tqi::AttendArgs &a, hipStream_t s) {
   switch (lb) {
-    case 1: return launch_g<D, 1>(a, s, ok);
-    case 2: return launch_g<D, 2>(a, s, ok);
-    case 3: return launch_g<D, 3>(a, s, ok);
-    case 4: return launch_g<D, 4>(a, s, ok);
+    case 1: return launch_g<D, 1>(a, s);
+    case 2: return launch_g<D, 2>(a, s);
+    case 3: return launch_g<D, 3>(a, s);
+    case 4: return launch_g<D, 4>(a, s);
   }
-  *ok = false;
-  return hipSuccess;
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 namespace tqi {
 
-hipError_t launch_attend(int d, int lbits, const AttendArgs &a, hipStream_t s, bool *supported) {
-  *supported = false;
-  if (d == 128) return launch_lb<128>(lbits, a, s, supported);
-  if (d == 256) return launch_lb<256>(lbits, a, s, supported);
-  return hipSuccess;
+bool attend_supported(int d, int lbits, int group, int64_t seq_len) {
+  if (d != 128 && d != 256) return false;
+  if (lbits < 1 || lbits > 4 || group < 1 || group > 16) return false;
+  // 32-bit byte offsets within one split of the packed values (plus a chunk)
+  const int64_t rb = (int64_t)lbits * d / 8;
+  return (seq_len + kChunk) * rb < (1LL << 31);
+}
+
+size_t attend_workspace_bytes(int d, int lbits, int batch, int n_q_heads, int n_kv_heads, int64_t seq_len) {
+  (void)lbits;
+  const int64_t n_streams = (int64_t)batch * n_kv_heads;
+  const int g = group_bucket(n_q_heads / n_kv_heads);
+  const AttendPlan plan = attend_plan(n_streams, seq_len);
+  return ws_align((size_t)n_streams * plan.splits * g * (d + 2) * sizeof(float));
+}
+
+hipError_t launch_attend(int d, int lbits, const AttendArgs &a, hipStream_t s) {
+  if (d == 128) return launch_lb<128>(lbits, a, s);
+  if (d == 256) return launch_lb<256>(lbits, a, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace tqi
+

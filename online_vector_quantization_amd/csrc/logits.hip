@@ -386,9 +386,8 @@ struct StreamArgs {
   float *logits;
 };
 
-#ifndef TQ_LOGIT_GROUPS
-#define TQ_LOGIT_GROUPS 4
-#endif
+constexpr int kLogitGroups = 4;        // 16-token groups per wave and loop iteration
+constexpr int kLogitBlocksPerCu = 8;   // streaming workgroups per CU the launch aims for
 
 
 // Registers of one 16-token group as loaded by one lane: the plane words of
@@ -416,7 +415,7 @@ __global__ __launch_bounds__(256) void logit_kernel(StreamArgs a) {
   constexpr int NPL = LB + (PROD ? 1 : 0);  // planes per record (sign on top)
   constexpr int RB = NPL * PB;              // bytes per packed row
   constexpr int NQ = D / 128;            // plane words per lane and plane
-  constexpr int U = TQ_LOGIT_GROUPS;     // 16-token groups per wave and iteration
+  constexpr int U = kLogitGroups;     // 16-token groups per wave and iteration
   constexpr int NB = U / 4;              // 64-token norm blocks per iteration
   static_assert(U % 4 == 0, "groups come in fours (64 tokens)");
   __shared__ __attribute__((aligned(16))) float stage[4][4 * RT][16 * U];
@@ -595,10 +594,8 @@ hipError_t launch_t(const tqi::LogitArgs &a, hipStream_t s) {
   const int rts = (group + 3) / 4;
   const int n_streams = a.batch * a.n_kv_heads;
   const size_t table_bytes = (size_t)n_streams * rts * L::NCH * 64 * 16;
-  const size_t const_bytes = (size_t)n_streams * group * 4 * sizeof(float);
-  void *ws = nullptr;
-  hipError_t e = tqi::workspace(s, table_bytes + const_bytes, &ws);
-  if (e != hipSuccess) return e;
+  void *ws = a.workspace;
+  hipError_t e = hipSuccess;
   PrepArgs pa;
   pa.q = a.q;
   pa.q_f32 = a.q_f32;
@@ -610,7 +607,7 @@ hipError_t launch_t(const tqi::LogitArgs &a, hipStream_t s) {
   pa.s_mat = a.s_mat;
   pa.centroids = a.centroids;
   pa.table = (int8_t *)ws;
-  pa.consts = (float *)((char *)ws + table_bytes);
+  pa.consts = (float *)((char *)ws + tqi::ws_align(table_bytes));
   pa.x_new = a.x_new;
   pa.x_f32 = a.x_f32;
   pa.boundaries = a.boundaries;
@@ -640,11 +637,8 @@ hipError_t launch_t(const tqi::LogitArgs &a, hipStream_t s) {
     sa.row_tiles = rts;
     sa.scale = a.scale;
     sa.logits = a.logits;
-#ifndef TQ_LOGIT_BLOCKS_PER_CU
-#define TQ_LOGIT_BLOCKS_PER_CU 8
-#endif
-    const int64_t target_blocks = (int64_t)TQ_LOGIT_BLOCKS_PER_CU * tqi::device_cu_count();
-    const int64_t n_chunks = (a.seq_len + 4 * 16 * TQ_LOGIT_GROUPS - 1) / (4 * 16 * TQ_LOGIT_GROUPS);
+    const int64_t target_blocks = (int64_t)kLogitBlocksPerCu * tqi::device_cu_count();
+    const int64_t n_chunks = (a.seq_len + 4 * 16 * kLogitGroups - 1) / (4 * 16 * kLogitGroups);
     int64_t splits = (target_blocks + n_streams - 1) / n_streams;
     if (splits > n_chunks) splits = n_chunks;
     if (splits < 1) splits = 1;
@@ -662,38 +656,44 @@ hipError_t launch_t(const tqi::LogitArgs &a, hipStream_t s) {
 }
 
 template <int D, bool PROD>
-hipError_t launch_lb(int lb, const tqi::LogitArgs &a, hipStream_t s, bool *ok) {
-  *ok = true;
+hipError_t launch_lb(int lb, const tqi::LogitArgs &a, hipStream_t s) {
   switch (lb) {
     case 1: return launch_t<D, 1, PROD>(a, s);
     case 2: return launch_t<D, 2, PROD>(a, s);
     case 3: return launch_t<D, 3, PROD>(a, s);
     case 4: return launch_t<D, 4, PROD>(a, s);
   }
-  *ok = false;
-  return hipSuccess;
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 namespace tqi {
 
-hipError_t launch_logits(int d, int lbits, bool prod, const LogitArgs &a, hipStream_t s,
-                         bool *supported) {
-  *supported = false;
-  const int64_t group = a.n_q_heads / a.n_kv_heads;
-  if (group > 16) return hipSuccess;
-  // The streaming kernel addresses one stream's codes and logits with 32-bit
-  // byte offsets; its prefetch runs up to one block stride (<= seq_len + 255
-  // tokens) past the end, which must not wrap either.
-  if ((2 * a.seq_len + 256) * (int64_t)((lbits + (prod ? 1 : 0)) * d / 8) >= (1LL << 32) ||
-      group * a.seq_len * 4 >= (1LL << 32))
-    return hipSuccess;
-  if (d == 128) return prod ? launch_lb<128, true>(lbits, a, s, supported)
-                            : launch_lb<128, false>(lbits, a, s, supported);
-  if (d == 256) return prod ? launch_lb<256, true>(lbits, a, s, supported)
-                            : launch_lb<256, false>(lbits, a, s, supported);
-  return hipSuccess;
+bool logits_supported(int d, int lbits, bool prod, int group, int64_t seq_len) {
+  if (d != 128 && d != 256) return false;
+  if (lbits < 1 || lbits > 4 || group < 1 || group > 16) return false;
+  // The streaming kernel addresses one stream's codes with 32-bit byte
+  // offsets, and its prefetch runs up to one block stride (<= seq_len + 255
+  // tokens) past the end, which must not wrap.  Its logit stores drop
+  // lanes through the offset 2^31 (kNoStore), so the logits of one stream
+  // (group x seq_len fp32) must stay below 2^31 bytes.
+  if ((2 * seq_len + 256) * (int64_t)((lbits + (prod ? 1 : 0)) * d / 8) >= (1LL << 32)) return false;
+  if ((int64_t)group * seq_len * 4 >= (1LL << 31)) return false;
+  return true;
+}
+
+size_t logits_workspace_bytes(int d, int lbits, bool prod, int64_t n_streams, int group) {
+  const int64_t rts = (group + 3) / 4;
+  const int64_t nch = ((1 << (lbits - 1)) + (prod ? 1 : 0)) * (d / 64);
+  const size_t table = (size_t)(n_streams * rts * nch * 64 * 16);
+  return ws_align(table) + ws_align((size_t)n_streams * group * 4 * sizeof(float));
+}
+
+hipError_t launch_logits(int d, int lbits, bool prod, const LogitArgs &a, hipStream_t s) {
+  if (d == 128) return prod ? launch_lb<128, true>(lbits, a, s) : launch_lb<128, false>(lbits, a, s);
+  if (d == 256) return prod ? launch_lb<256, true>(lbits, a, s) : launch_lb<256, false>(lbits, a, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace tqi

@@ -239,10 +239,15 @@ __device__ __forceinline__ uint16_t stage_vector(const RawInput<IN_F32> &r, _Flo
     dl[0] = lv[0];
     dl[1] = lv[1];
   }
-  // 1 / (sc * 2^8 * |x|): the scaled sum of squares lies in [2^28, 2^37),
-  // so fp32 holds it; v_rsq_f32 is good to about one ulp.
-  const float ss_sc = (float)ldexp(ss, 2 * se);
-  const float inv_n = ss > 0.0 ? __builtin_amdgcn_rsqf(ss_sc) * (1.0f / kPiScale) : 0.0f;
+  // 1 / (sc * 2^8 * |x|), correctly rounded to fp32: the scaled sum of
+  // squares lies in [2^28, 2^37); v_rsq_f32 (about one ulp) is refined by one
+  // Newton step in fp64 (error ~2^-45) before the single rounding to fp32.
+  // The unit coordinates u = y * inv_n carry this rounding as a common
+  // factor, which enters the residual norm gamma one to one.
+  const double ss_sc = ldexp(ss, 2 * se);
+  const double r0 = (double)__builtin_amdgcn_rsqf((float)ss_sc);
+  const double r1 = fma(r0, fma(-0.5 * ss_sc, r0 * r0, 0.5), r0);
+  const float inv_n = ss > 0.0 ? (float)r1 * (1.0f / kPiScale) : 0.0f;
   vinv[sv_v] = inv_n;        // the vector's threads all hold the same value
   return f64_to_f16_bits(sqrt(ss));
 }

@@ -518,20 +518,25 @@ __global__ __launch_bounds__(256) void search_merge_kernel(MergeArgs a) {
   }
 }
 
-template <int D, int LB>
-hipError_t launch_t(const tqi::SearchArgs &sa, hipStream_t s) {
-  const tqi::LogitArgs &a = sa.base;
-  const int group = a.n_q_heads / a.n_kv_heads;
-  const int64_t n_streams = (int64_t)a.batch * a.n_kv_heads;
-  const int64_t n_queries = (int64_t)a.batch * a.n_q_heads;
-  const int q_tiles = (group + kSearchQueries - 1) / kSearchQueries;
-  const int64_t base_blocks = n_streams * q_tiles;
-  // Split the keys so that the workgroups fill the chip in whole rounds: the
-  // cost of a split count is (rounds of resident workgroups) x (tiles per
-  // split + a fixed allowance for filling the lists).
+// Launch plan of one search call: key splits (so that the workgroups fill
+// the chip in whole rounds: the cost of a split count is (rounds of resident
+// workgroups) x (tiles per split + a fixed allowance for filling the lists))
+// and the workspace layout.
+struct SearchPlan {
+  int64_t splits, kps, n_rows, n_queries, q_tiles;
+  size_t qbytes, qfac_off, pv_off, pi_off, bytes;
+};
+
+SearchPlan search_plan(int batch, int n_q_heads, int n_kv_heads, int64_t seq_len, int d) {
+  SearchPlan p;
+  const int group = n_q_heads / n_kv_heads;
+  const int64_t n_streams = (int64_t)batch * n_kv_heads;
+  p.n_queries = (int64_t)batch * n_q_heads;
+  p.q_tiles = (group + kSearchQueries - 1) / kSearchQueries;
+  const int64_t base_blocks = n_streams * p.q_tiles;
   const int64_t cus = tqi::device_cu_count();
-  const int64_t n_tiles = (a.seq_len + 31) / 32;
-  int64_t max_splits = (a.seq_len + 4095) / 4096;
+  const int64_t n_tiles = (seq_len + 31) / 32;
+  int64_t max_splits = (seq_len + 4095) / 4096;
   if (max_splits > 64) max_splits = 64;
   if (max_splits < 1) max_splits = 1;
   int64_t splits = 1, best = -1;
@@ -540,30 +545,45 @@ hipError_t launch_t(const tqi::SearchArgs &sa, hipStream_t s) {
     const int64_t cost = rounds * ((n_tiles + sp - 1) / sp + 16);
     if (best < 0 || cost < best) { best = cost; splits = sp; }
   }
-  int64_t kps = (a.seq_len + splits - 1) / splits;
+  int64_t kps = (seq_len + splits - 1) / splits;
   kps = (kps + 31) / 32 * 32;
-  splits = (a.seq_len + kps - 1) / kps;
+  p.kps = kps > 0 ? kps : 32;
+  p.splits = seq_len > 0 ? (seq_len + p.kps - 1) / p.kps : 1;
+  p.n_rows = n_streams * group;
+  p.qbytes = tqi::ws_align((size_t)p.n_queries * d * sizeof(_Float16));
+  p.qfac_off = 2 * p.qbytes;
+  p.pv_off = p.qfac_off + tqi::ws_align((size_t)p.n_queries * sizeof(float));
+  p.pi_off = p.pv_off + tqi::ws_align((size_t)p.splits * p.n_rows * kTop * sizeof(float));
+  p.bytes = p.pi_off + tqi::ws_align((size_t)p.splits * p.n_rows * kTop * sizeof(int32_t));
+  return p;
+}
+
+template <int D, int LB>
+hipError_t launch_t(const tqi::SearchArgs &sa, hipStream_t s) {
+  const tqi::LogitArgs &a = sa.base;
+  const int group = a.n_q_heads / a.n_kv_heads;
+  const int64_t n_streams = (int64_t)a.batch * a.n_kv_heads;
+  const SearchPlan plan = search_plan(a.batch, a.n_q_heads, a.n_kv_heads, a.seq_len, D);
+  const int64_t n_queries = plan.n_queries;
+  const int q_tiles = (int)plan.q_tiles;
+  const int64_t base_blocks = n_streams * q_tiles;
+  const int64_t splits = plan.splits, kps = plan.kps;
   // Key indices fit the packed list entries (30 bits); per-split byte offsets
-  // of the packed codes stay below 2^31.
-  if (a.seq_len >= (1LL << 30)) return hipErrorInvalidValue;
-  if ((kps + 64) * (int64_t)(LB * D / 8) >= (1LL << 31)) return hipErrorInvalidValue;
-  const int64_t n_rows = n_streams * group;
-  const size_t qbytes = (size_t)n_queries * D * sizeof(_Float16);
-  const size_t bytes = 2 * qbytes + (size_t)n_queries * sizeof(float) +
-                       (size_t)splits * n_rows * kTop * (sizeof(float) + sizeof(int32_t)) + 256;
-  char *ws = nullptr;
-  hipError_t e = tqi::workspace(s, bytes, (void **)&ws);
-  if (e != hipSuccess) return e;
+  // of the packed codes stay below 2^31 (both checked by search_supported).
+  const int64_t n_rows = plan.n_rows;
+  if (a.workspace_bytes < plan.bytes) return hipErrorInvalidValue;
+  char *ws = (char *)a.workspace;
+  hipError_t e = hipSuccess;
   QPrepArgs pa;
   pa.q = a.q;
   pa.q_f32 = a.q_f32;
   pa.n_queries = n_queries;
   pa.pi = a.pi;
   pa.qh = (_Float16 *)ws;
-  pa.ql = (_Float16 *)(ws + qbytes);
-  pa.qfac = (float *)(ws + 2 * qbytes);
-  float *pv = (float *)(ws + 2 * qbytes + ((n_queries * sizeof(float) + 255) / 256) * 256);
-  int32_t *pi = (int32_t *)(pv + splits * n_rows * kTop);
+  pa.ql = (_Float16 *)(ws + plan.qbytes);
+  pa.qfac = (float *)(ws + plan.qfac_off);
+  float *pv = (float *)(ws + plan.pv_off);
+  int32_t *pi = (int32_t *)(ws + plan.pi_off);
   hipLaunchKernelGGL((search_prep_kernel<D>), dim3((unsigned)((n_queries + kPrepQueries - 1) / kPrepQueries)),
                      dim3(D), 0, s, pa);
   e = hipGetLastError();
@@ -611,28 +631,39 @@ hipError_t launch_t(const tqi::SearchArgs &sa, hipStream_t s) {
 }
 
 template <int D>
-hipError_t launch_lb(int lb, const tqi::SearchArgs &a, hipStream_t s, bool *ok) {
-  *ok = true;
+hipError_t launch_lb(int lb, const tqi::SearchArgs &a, hipStream_t s) {
   switch (lb) {
     case 1: return launch_t<D, 1>(a, s);
     case 2: return launch_t<D, 2>(a, s);
     case 3: return launch_t<D, 3>(a, s);
     case 4: return launch_t<D, 4>(a, s);
   }
-  *ok = false;
-  return hipSuccess;
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 namespace tqi {
 
-hipError_t launch_search(int d, int lbits, const SearchArgs &a, hipStream_t s, bool *supported) {
-  *supported = false;
-  if (a.topk > kTop) return hipSuccess;
-  if (d == 128) return launch_lb<128>(lbits, a, s, supported);
-  if (d == 256) return launch_lb<256>(lbits, a, s, supported);
-  return hipSuccess;
+bool search_supported(int d, int lbits, int topk, int batch, int n_q_heads, int n_kv_heads, int64_t seq_len) {
+  if (d != 128 && d != 256) return false;
+  if (lbits < 1 || lbits > 4 || topk < 1 || topk > kTop) return false;
+  if (seq_len >= (1LL << 30)) return false;        // key index in 30 bits of a list entry
+  // per-split byte offsets of the packed codes (one split plus one tile of
+  // prefetch) below 2^31
+  const SearchPlan p = search_plan(batch, n_q_heads, n_kv_heads, seq_len, d);
+  return (p.kps + 64) * (int64_t)(lbits * d / 8) < (1LL << 31);
+}
+
+size_t search_workspace_bytes(int d, int lbits, int batch, int n_q_heads, int n_kv_heads, int64_t seq_len) {
+  (void)lbits;
+  return search_plan(batch, n_q_heads, n_kv_heads, seq_len, d).bytes;
+}
+
+hipError_t launch_search(int d, int lbits, const SearchArgs &a, hipStream_t s) {
+  if (d == 128) return launch_lb<128>(lbits, a, s);
+  if (d == 256) return launch_lb<256>(lbits, a, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace tqi

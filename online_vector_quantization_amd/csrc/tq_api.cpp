@@ -4,9 +4,6 @@
 
 #include <atomic>
 #include <cstdint>
-#include <map>
-#include <mutex>
-#include <utility>
 
 #include "tq.h"
 #include "tq_internal.h"
@@ -26,40 +23,6 @@ int device_cu_count() {
     cu = 256;
   if (dev < 64) cache[dev].store(cu, std::memory_order_relaxed);
   return cu;
-}
-
-hipError_t workspace(hipStream_t s, size_t bytes, void **out) {
-  struct Buf {
-    void *ptr = nullptr;
-    size_t size = 0;
-  };
-  static std::mutex mu;
-  static std::map<std::pair<int, hipStream_t>, Buf> bufs;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  std::lock_guard<std::mutex> lock(mu);
-  Buf &b = bufs[std::make_pair(dev, s)];
-  if (b.size < bytes) {
-    if (b.ptr != nullptr) {
-      e = hipStreamSynchronize(s);
-      if (e != hipSuccess) return e;
-      e = hipFree(b.ptr);
-      if (e != hipSuccess) return e;
-      b.ptr = nullptr;
-      b.size = 0;
-    }
-    size_t want = bytes + bytes / 4;
-    want = (want + (1u << 20) - 1) & ~(size_t)((1u << 20) - 1);
-    e = hipMalloc(&b.ptr, want);
-    if (e != hipSuccess) {
-      b.ptr = nullptr;
-      return e;
-    }
-    b.size = want;
-  }
-  *out = b.ptr;
-  return hipSuccess;
 }
 
 }  // namespace tqi
@@ -85,6 +48,59 @@ tq_status check_params(const tq_params *p) {
 }
 
 tq_status hip_status(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_ERR_HIP; }
+
+// Argument checks common to the logit, append and search calls (before any
+// shape or workspace check).
+tq_status check_logit_args(const tq_params *p, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                           int64_t seq_len, int32_t topk) {
+  tq_status st = check_params(p);
+  if (st != TQ_OK) return st;
+  if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || topk < 0 || seq_len < 0) return TQ_ERR_INVALID;
+  if (n_q_heads % n_kv_heads != 0) return TQ_ERR_INVALID;
+  return TQ_OK;
+}
+
+// TQ_OK when a kernel takes the shape, TQ_ERR_UNSUPPORTED otherwise.
+tq_status logits_shape(const tq_params *p, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                       int64_t seq_len, int32_t topk) {
+  if (p->mode == TQ_MODE_POLAR) return TQ_ERR_UNSUPPORTED;
+  const bool prod = p->mode == TQ_MODE_PROD;
+  if (topk > 0) {
+    if (prod) return TQ_ERR_UNSUPPORTED;
+    return tqi::search_supported(p->d, lloyd_bits(p), topk, batch, n_q_heads, n_kv_heads, seq_len)
+               ? TQ_OK : TQ_ERR_UNSUPPORTED;
+  }
+  return tqi::logits_supported(p->d, lloyd_bits(p), prod, n_q_heads / n_kv_heads, seq_len) ? TQ_OK
+                                                                                           : TQ_ERR_UNSUPPORTED;
+}
+
+size_t logits_ws_bytes(const tq_params *p, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                       int64_t seq_len, int32_t topk) {
+  if (batch == 0 || seq_len == 0) return 0;
+  if (topk > 0) return tqi::search_workspace_bytes(p->d, lloyd_bits(p), batch, n_q_heads, n_kv_heads, seq_len);
+  return tqi::logits_workspace_bytes(p->d, lloyd_bits(p), p->mode == TQ_MODE_PROD,
+                                     (int64_t)batch * n_kv_heads, n_q_heads / n_kv_heads);
+}
+
+tq_status check_attend_args(const tq_params *p, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                            int64_t seq_len) {
+  tq_status st = check_params(p);
+  if (st != TQ_OK) return st;
+  if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || seq_len < 0) return TQ_ERR_INVALID;
+  if (n_q_heads % n_kv_heads != 0) return TQ_ERR_INVALID;
+  if (p->mode != TQ_MODE_MSE) return TQ_ERR_UNSUPPORTED;
+  return tqi::attend_supported(p->d, lloyd_bits(p), n_q_heads / n_kv_heads, seq_len) ? TQ_OK
+                                                                                     : TQ_ERR_UNSUPPORTED;
+}
+
+// A workspace of `need` bytes: NULL is fine when nothing is needed;
+// otherwise at least `need` bytes, 256-byte aligned.
+tq_status check_workspace(const void *ws, size_t have, size_t need) {
+  if (need == 0) return TQ_OK;
+  if (ws == nullptr || have < need) return TQ_ERR_INVALID;
+  if ((uintptr_t)ws & 255u) return TQ_ERR_UNSUPPORTED;
+  return TQ_OK;
+}
 
 }  // namespace
 
@@ -125,23 +141,37 @@ extern "C" tq_status tq_quantize_kv(const tq_params *p, const void *x, int32_t x
   return hip_status(e);
 }
 
+extern "C" tq_status tq_attn_logits_workspace_size(const tq_params *p, int32_t batch, int32_t n_q_heads,
+                                                   int32_t n_kv_heads, int64_t seq_len, int32_t topk,
+                                                   size_t *bytes) {
+  if (bytes == nullptr) return TQ_ERR_INVALID;
+  *bytes = 0;
+  tq_status st = check_logit_args(p, batch, n_q_heads, n_kv_heads, seq_len, topk);
+  if (st != TQ_OK) return st;
+  st = logits_shape(p, batch, n_q_heads, n_kv_heads, seq_len, topk);
+  if (st != TQ_OK) return st;
+  *bytes = logits_ws_bytes(p, batch, n_q_heads, n_kv_heads, seq_len, topk);
+  return TQ_OK;
+}
+
 extern "C" tq_status tq_attn_logits(const tq_params *p, const void *q, int32_t q_dtype,
                                     int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
                                     const tq_packed *k, int64_t row_tokens, int64_t seq_len,
                                     float scale, float *logits, int32_t topk, int32_t *topk_idx,
-                                    void *stream) {
-  tq_status st = check_params(p);
+                                    void *workspace, size_t workspace_bytes, void *stream) {
+  tq_status st = check_logit_args(p, batch, n_q_heads, n_kv_heads, seq_len, topk);
   if (st != TQ_OK) return st;
-  if (p->mode == TQ_MODE_POLAR) return TQ_ERR_UNSUPPORTED;
   const bool prod = p->mode == TQ_MODE_PROD;
-  if (k == nullptr || batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || topk < 0) return TQ_ERR_INVALID;
-  if (n_q_heads % n_kv_heads != 0) return TQ_ERR_INVALID;
+  if (k == nullptr || row_tokens < seq_len) return TQ_ERR_INVALID;
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_ERR_INVALID;
-  if (seq_len < 0 || row_tokens < seq_len) return TQ_ERR_INVALID;
+  st = logits_shape(p, batch, n_q_heads, n_kv_heads, seq_len, topk);
+  if (st != TQ_OK) return st;
   if (batch == 0 || seq_len == 0) return TQ_OK;
   if (q == nullptr || logits == nullptr || k->codes == nullptr || k->norm == nullptr) return TQ_ERR_INVALID;
   if (prod && (p->qjl == nullptr || k->rnorm == nullptr)) return TQ_ERR_INVALID;
   if (topk > 0 && (topk_idx == nullptr || seq_len < topk)) return TQ_ERR_INVALID;
+  st = check_workspace(workspace, workspace_bytes, logits_ws_bytes(p, batch, n_q_heads, n_kv_heads, seq_len, topk));
+  if (st != TQ_OK) return st;
   if ((uintptr_t)k->codes & 3u) return TQ_ERR_UNSUPPORTED;
   tqi::LogitArgs a;
   a.q = q;
@@ -159,19 +189,18 @@ extern "C" tq_status tq_attn_logits(const tq_params *p, const void *q, int32_t q
   a.seq_len = seq_len;
   a.scale = scale;
   a.logits = logits;
-  bool ok = false;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
   hipError_t e;
   if (topk > 0) {
-    if (prod) return TQ_ERR_UNSUPPORTED;
     tqi::SearchArgs sa;
     sa.base = a;
     sa.topk = topk;
     sa.topk_idx = topk_idx;
-    e = tqi::launch_search(p->d, lloyd_bits(p), sa, (hipStream_t)stream, &ok);
+    e = tqi::launch_search(p->d, lloyd_bits(p), sa, (hipStream_t)stream);
   } else {
-    e = tqi::launch_logits(p->d, lloyd_bits(p), prod, a, (hipStream_t)stream, &ok);
+    e = tqi::launch_logits(p->d, lloyd_bits(p), prod, a, (hipStream_t)stream);
   }
-  if (!ok) return TQ_ERR_UNSUPPORTED;
   return hip_status(e);
 }
 
@@ -179,20 +208,22 @@ extern "C" tq_status tq_append_attn_logits(const tq_params *p, const void *x_new
                                            const void *q, int32_t q_dtype, int32_t batch,
                                            int32_t n_q_heads, int32_t n_kv_heads, const tq_packed *k,
                                            int64_t row_tokens, int64_t pos, float scale, float *logits,
-                                           void *stream) {
-  tq_status st = check_params(p);
+                                           void *workspace, size_t workspace_bytes, void *stream) {
+  tq_status st = check_logit_args(p, batch, n_q_heads, n_kv_heads, 0, 0);
   if (st != TQ_OK) return st;
-  if (p->mode == TQ_MODE_POLAR) return TQ_ERR_UNSUPPORTED;
   const bool prod = p->mode == TQ_MODE_PROD;
-  if (k == nullptr || batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0) return TQ_ERR_INVALID;
-  if (n_q_heads % n_kv_heads != 0) return TQ_ERR_INVALID;
+  if (k == nullptr) return TQ_ERR_INVALID;
   if ((q_dtype != TQ_F32 && q_dtype != TQ_BF16) || (x_dtype != TQ_F32 && x_dtype != TQ_BF16))
     return TQ_ERR_INVALID;
   if (pos < 0 || pos >= row_tokens) return TQ_ERR_INVALID;
+  st = logits_shape(p, batch, n_q_heads, n_kv_heads, pos + 1, 0);
+  if (st != TQ_OK) return st;
   if (batch == 0) return TQ_OK;
   if (x_new == nullptr || q == nullptr || logits == nullptr || k->codes == nullptr || k->norm == nullptr)
     return TQ_ERR_INVALID;
   if (prod && (p->qjl == nullptr || p->qjl_rot == nullptr || k->rnorm == nullptr)) return TQ_ERR_INVALID;
+  st = check_workspace(workspace, workspace_bytes, logits_ws_bytes(p, batch, n_q_heads, n_kv_heads, pos + 1, 0));
+  if (st != TQ_OK) return st;
   if ((uintptr_t)k->codes & 3u) return TQ_ERR_UNSUPPORTED;
   tqi::LogitArgs a;
   a.q = q;
@@ -218,27 +249,38 @@ extern "C" tq_status tq_append_attn_logits(const tq_params *p, const void *x_new
   a.norm_out = k->norm;
   a.rnorm_out = k->rnorm;
   a.pos = pos;
-  bool ok = false;
-  const hipError_t e = tqi::launch_logits(p->d, lloyd_bits(p), prod, a, (hipStream_t)stream, &ok);
-  if (!ok) return TQ_ERR_UNSUPPORTED;
-  return hip_status(e);
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
+  return hip_status(tqi::launch_logits(p->d, lloyd_bits(p), prod, a, (hipStream_t)stream));
+}
+
+extern "C" tq_status tq_attn_output_workspace_size(const tq_params *p, int32_t batch, int32_t n_q_heads,
+                                                   int32_t n_kv_heads, int64_t seq_len, size_t *bytes) {
+  if (bytes == nullptr) return TQ_ERR_INVALID;
+  *bytes = 0;
+  const tq_status st = check_attend_args(p, batch, n_q_heads, n_kv_heads, seq_len);
+  if (st != TQ_OK) return st;
+  if (batch > 0)
+    *bytes = tqi::attend_workspace_bytes(p->d, lloyd_bits(p), batch, n_q_heads, n_kv_heads, seq_len);
+  return TQ_OK;
 }
 
 extern "C" tq_status tq_attn_output(const tq_params *p, const float *logits, int32_t batch,
                                     int32_t n_q_heads, int32_t n_kv_heads, const tq_packed *v,
                                     int64_t row_tokens, int64_t seq_len, void *out, int32_t out_dtype,
-                                    void *stream) {
+                                    void *workspace, size_t workspace_bytes, void *stream) {
   tq_status st = check_params(p);
   if (st != TQ_OK) return st;
-  if (p->mode == TQ_MODE_POLAR) return TQ_ERR_UNSUPPORTED;
-  if (v == nullptr || batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0) return TQ_ERR_INVALID;
-  if (n_q_heads % n_kv_heads != 0) return TQ_ERR_INVALID;
+  if (v == nullptr || row_tokens < seq_len) return TQ_ERR_INVALID;
   if (out_dtype != TQ_F32 && out_dtype != TQ_BF16) return TQ_ERR_INVALID;
-  if (seq_len < 0 || row_tokens < seq_len) return TQ_ERR_INVALID;
+  st = check_attend_args(p, batch, n_q_heads, n_kv_heads, seq_len);
+  if (st != TQ_OK) return st;
   if (batch == 0) return TQ_OK;
   if (out == nullptr) return TQ_ERR_INVALID;
   if (seq_len > 0 && (logits == nullptr || v->codes == nullptr || v->norm == nullptr)) return TQ_ERR_INVALID;
-  if (p->mode != TQ_MODE_MSE) return TQ_ERR_UNSUPPORTED;
+  st = check_workspace(workspace, workspace_bytes,
+                       tqi::attend_workspace_bytes(p->d, lloyd_bits(p), batch, n_q_heads, n_kv_heads, seq_len));
+  if (st != TQ_OK) return st;
   if ((uintptr_t)v->codes & 15u) return TQ_ERR_UNSUPPORTED;
   tqi::AttendArgs a;
   a.logits = logits;
@@ -253,10 +295,9 @@ extern "C" tq_status tq_attn_output(const tq_params *p, const float *logits, int
   a.seq_len = seq_len;
   a.out = out;
   a.out_f32 = out_dtype == TQ_F32;
-  bool ok = false;
-  hipError_t e = tqi::launch_attend(p->d, lloyd_bits(p), a, (hipStream_t)stream, &ok);
-  if (!ok) return TQ_ERR_UNSUPPORTED;
-  return hip_status(e);
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
+  return hip_status(tqi::launch_attend(p->d, lloyd_bits(p), a, (hipStream_t)stream));
 }
 
 extern "C" tq_status tq_dequantize(const tq_params *p, const tq_packed *k, int64_t n_vec, void *out,

@@ -123,10 +123,7 @@ __device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t bytes) {
 // Cache-policy bits of the buffer instructions.  Streams that are read or
 // written exactly once use the non-temporal policy (bit 1), which keeps them
 // from displacing reused data in L2 and lifts streaming bandwidth.
-#ifndef TQ_STREAM_POLICY
-#define TQ_STREAM_POLICY 2
-#endif
-constexpr int kStream = TQ_STREAM_POLICY;
+constexpr int kStream = 2;
 
 template <int N, int AUX = kStream>
 __device__ __forceinline__ void buf_load_words(i32x4 rsrc, uint32_t off, uint32_t (&out)[N]) {

@@ -50,10 +50,16 @@ struct LogitArgs {
   uint16_t *norm_out = nullptr;
   uint16_t *rnorm_out = nullptr;
   int64_t pos = 0;
+  // caller-owned device scratch (query tables / partial lists)
+  void *workspace = nullptr;
+  size_t workspace_bytes = 0;
 };
 
-hipError_t launch_logits(int d, int lbits, bool prod, const LogitArgs &a, hipStream_t s,
-                         bool *supported);
+// Shapes the dense logit kernels take (GQA group <= 16, d in {128, 256},
+// 32-bit byte offsets of one stream's codes and logits below 2^31).
+bool logits_supported(int d, int lbits, bool prod, int group, int64_t seq_len);
+size_t logits_workspace_bytes(int d, int lbits, bool prod, int64_t n_streams, int group);
+hipError_t launch_logits(int d, int lbits, bool prod, const LogitArgs &a, hipStream_t s);
 
 struct SearchArgs {
   LogitArgs base;
@@ -61,7 +67,10 @@ struct SearchArgs {
   int32_t *topk_idx;
 };
 
-hipError_t launch_search(int d, int lbits, const SearchArgs &a, hipStream_t s, bool *supported);
+// Top-k search: shapes it takes and the scratch it needs on the current device.
+bool search_supported(int d, int lbits, int topk, int batch, int n_q_heads, int n_kv_heads, int64_t seq_len);
+size_t search_workspace_bytes(int d, int lbits, int batch, int n_q_heads, int n_kv_heads, int64_t seq_len);
+hipError_t launch_search(int d, int lbits, const SearchArgs &a, hipStream_t s);
 
 struct DequantArgs {
   const float *pi;
@@ -90,17 +99,19 @@ struct AttendArgs {
   int64_t row_tokens, seq_len;
   void *out;             // [batch][n_q_heads][d]
   bool out_f32;
+  void *workspace = nullptr;   // caller-owned device scratch (per-split partials)
+  size_t workspace_bytes = 0;
 };
 
-hipError_t launch_attend(int d, int lbits, const AttendArgs &a, hipStream_t s, bool *supported);
+bool attend_supported(int d, int lbits, int group, int64_t seq_len);
+size_t attend_workspace_bytes(int d, int lbits, int batch, int n_q_heads, int n_kv_heads, int64_t seq_len);
+hipError_t launch_attend(int d, int lbits, const AttendArgs &a, hipStream_t s);
 
+// Compute units of the current device (cached per device; 256 when the
+// runtime cannot say).
 int device_cu_count();
 
-// Scratch memory for one call on stream `s` of the current device.  The
-// library keeps one buffer per (device, stream), grows it with hipMalloc when
-// a call needs more (after synchronising that stream, whose queued work may
-// still read the old buffer) and keeps it until the process ends.  Work on
-// one stream runs in order, so successive calls on it can share the buffer.
-hipError_t workspace(hipStream_t s, size_t bytes, void **out);
+// Bytes rounded up to the 256-byte alignment of every workspace piece.
+constexpr size_t ws_align(size_t bytes) { return (bytes + 255) & ~(size_t)255; }
 
 }  // namespace tqi

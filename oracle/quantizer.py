@@ -239,6 +239,38 @@ def topk(scores, k):
     return np.take_along_axis(scores, out_idx, axis=1), out_idx
 
 
+def exact_topk(q, db, k, block=65536):
+    """Per query, the k largest exact inner products <q, x_i> over the
+    unquantised database rows, in fp64 (ties to the smaller index): the
+    reference that recall is measured against (page sections "벤치마크 및 실제
+    성능" and "응용 분야 및 미래 영향": top-k inner-product search over a
+    quantised database).
+
+    The database is scored block by block; within a block every row whose
+    score reaches the block's k-th largest (ties included) is a candidate, and
+    the candidates are merged with the running top-k by ``topk``'s order.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    n_q = q.shape[0]
+    best_v = np.full((n_q, 0), -np.inf)
+    best_i = np.zeros((n_q, 0), dtype=np.int64)
+    for start in range(0, db.shape[0], block):
+        blk = np.asarray(db[start:start + block], dtype=np.float64)
+        sc = q @ blk.T
+        kk = min(k, sc.shape[1])
+        thr = np.partition(sc, sc.shape[1] - kk, axis=1)[:, sc.shape[1] - kk]
+        new_v, new_i = [], []
+        for r in range(n_q):
+            cand = np.nonzero(sc[r] >= thr[r])[0]
+            v = np.concatenate([best_v[r], sc[r, cand]])
+            i = np.concatenate([best_i[r], start + cand])
+            order = np.lexsort((i, -v))[:k]
+            new_v.append(v[order])
+            new_i.append(i[order])
+        best_v, best_i = np.array(new_v), np.array(new_i)
+    return best_v, best_i
+
+
 def recall_at_k(found, exact):
     """Mean over queries of |found ∩ exact| / k."""
     found = np.asarray(found)

@@ -9,8 +9,26 @@ Tolerance rules:
   signs sketch the residual of the chosen index, so a row where a
   near-boundary index legitimately went the other way has a different
   residual and its signs are not comparable (such rows are counted).
-* norm: bit-exact fp16.  rnorm: within one fp16 ulp (the residual is formed
-  from fp32 sums on the device); flips counted.
+* norm: bit-exact fp16.
+* rnorm (fp16 of gamma), on the rows whose Lloyd-Max indices equal the
+  oracle's: bit-exact, except rows whose oracle gamma lies within a relative
+  window RNORM_WINDOW = 2^-20 of the rounding midpoint between the oracle's
+  fp16 value and the GPU's (the GPU rounded to the other neighbour of that
+  midpoint); such flips are counted and number at most MAX_RNORM_FLIP_FRAC =
+  0.05% of the compared rows (at least one allowed).  Derivation: the device
+  forms gamma from the fp32 rotation (fp32 accumulation of 22-bit products),
+  the correctly rounded fp32 1/||x|| (a common factor of the vector) and
+  fp32 sums of the staged residual; emulating those roundings gives a
+  relative error of gamma of std 5e-8 (b' = 2) to 8e-8 (b' = 3), largest
+  4e-7 in 2e4 vectors, so the window is over twice the largest error.  A
+  flip needs the error to reach past the midpoint: with fp16 midpoints
+  2^-11..2^-10 apart (relative) the expected flip rate is about
+  2 E|err| / 2^-10.5 = 0.013% to 0.017%, and the bound allows three times
+  that.
+* a row whose packed record (codes and rnorm) differs from the oracle's
+  carries at least one of the counted mismatches above; ``check_records``
+  asserts that and returns the mask of identical rows, on which logits and
+  reconstructions are then compared.
 * logits from identical (oracle-packed) codes: |l_gpu - l_orc| <= 1e-4 *
   max(|l_orc|, 1e-2 * |scale| * n16 * ||q||).
 * dequantize: ||x_gpu - x_orc|| <= 1e-4 ||x_orc|| per vector (fp32 output).
@@ -29,6 +47,8 @@ from oracle import rotation as orot
 
 CODE_WINDOW = 1e-5
 MAX_MISMATCH_FRAC = 1e-4
+RNORM_WINDOW = 2.0 ** -20
+MAX_RNORM_FLIP_FRAC = 5e-4
 LOGIT_RTOL = 1e-4
 LOGIT_FLOOR = 1e-2
 DEQUANT_RTOL = 1e-4
@@ -97,12 +117,72 @@ def check_norms(gpu_norm, ref):
     assert np.array_equal(g, ref["norm"]), "norm differs in %d rows" % int(np.sum(g != ref["norm"]))
 
 
-def check_rnorm(gpu_rnorm, ref):
-    g = np.asarray(gpu_rnorm).view(np.uint16).astype(np.int64)
-    o = ref["rnorm"].astype(np.int64)
-    diff = np.abs(g - o)
-    assert diff.max() <= 1, "rnorm off by %d ulp" % diff.max()
-    return int(np.sum(diff > 0))
+def allowed_mismatches(total, frac=MAX_MISMATCH_FRAC):
+    return max(1, int(np.ceil(frac * total)))
+
+
+def rnorm_flip_distance(gamma, oracle_bits, gpu_bits):
+    """Relative distance of the oracle's fp64 gamma to the midpoint between
+    the oracle's fp16 value and the GPU's (the rounding point the two sides
+    fell on either side of); infinite where that is not a rounding flip."""
+    o = oqz.from_fp16_bits(oracle_bits)
+    g = oqz.from_fp16_bits(gpu_bits)
+    adjacent = np.abs(np.asarray(oracle_bits, np.int64) - np.asarray(gpu_bits, np.int64)) == 1
+    mid = 0.5 * (o + g)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        dist = np.abs(gamma - mid) / gamma
+    return np.where(adjacent & (gamma > 0) & np.isfinite(dist), dist, np.inf)
+
+
+def check_rnorm(gpu_rnorm, ref, rows=None):
+    """rnorm rule on the rows selected by ``rows`` (default: all); returns the
+    number of counted flips."""
+    g = np.asarray(gpu_rnorm).view(np.uint16)
+    o = ref["rnorm"]
+    gam = ref["gamma"]
+    if rows is not None:
+        g, o, gam = g[rows], o[rows], gam[rows]
+    bad = g != o
+    n_bad = int(bad.sum())
+    if n_bad:
+        dist = rnorm_flip_distance(gam[bad], o[bad], g[bad])
+        assert np.all(dist < RNORM_WINDOW), "rnorm differs beyond a rounding flip: %.3g" % dist.max()
+    assert n_bad <= allowed_mismatches(g.size, MAX_RNORM_FLIP_FRAC), "%d of %d rnorm values differ" % (n_bad, g.size)
+    return n_bad
+
+
+def check_records(gpu_codes, gpu_norm, gpu_rnorm, ref, ot, report=None):
+    """Every per-vector rule (codes, signs, norm, rnorm) on a block of rows.
+
+    Returns the mask of rows whose packed record (code row and rnorm) equals
+    the oracle's.  Every other row must carry a counted mismatch that its rule
+    accepted: a Lloyd-Max index within the boundary window, a sign within the
+    window of 0, or an rnorm flip next to a rounding midpoint.  ``report``
+    (a dict) receives the counts.
+    """
+    gpu_codes = np.asarray(gpu_codes)
+    n_code, _ = check_codes(gpu_codes, ref, ot.lb, ot.d, ot.t, ot.mode)
+    check_norms(gpu_norm, ref)
+    gi, gs = oqz.unpack_records(gpu_codes, ot.lb, ot.mode, ot.d)
+    idx_ok = np.all(gi == ref["idx"], axis=1)
+    same = np.all(gpu_codes == ref["codes"], axis=1)
+    counts = {"rows": int(len(gpu_codes)), "code_mismatches": n_code, "rows_index_mismatch": int(np.sum(~idx_ok))}
+    explained = ~idx_ok
+    if ot.mode == oqz.MODE_PROD:
+        n_sign, _ = check_signs(gpu_codes, ref, ot.lb, ot.d)
+        n_rn = check_rnorm(gpu_rnorm, ref, rows=idx_ok)
+        rn_diff = np.asarray(gpu_rnorm).view(np.uint16) != ref["rnorm"]
+        same &= ~rn_diff
+        sign_diff = np.any(gs.astype(bool) != ref["sign_bits"], axis=1)
+        explained = explained | (idx_ok & (sign_diff | rn_diff))
+        counts.update(sign_mismatches=n_sign, rnorm_flips=n_rn)
+    unexplained = ~same & ~explained
+    assert not unexplained.any(), "%d rows differ without a counted mismatch" % int(unexplained.sum())
+    counts["rows_differing"] = int(np.sum(~same))
+    if report is not None:
+        report.update(counts)
+    print("record parity:", counts)
+    return same
 
 
 def logit_floor(scale, norm16, q):

@@ -30,7 +30,8 @@ def test_exports_every_declared_symbol(tq):
     header = open(os.path.join(ROOT, "include", "tq.h")).read()
     declared = set(re.findall(r"^\s*(?:tq_status|const char \*)\s*(tq_\w+)\s*\(", header, re.M))
     assert {"tq_make_codebook", "tq_make_rotation", "tq_quantize_kv", "tq_attn_logits",
-            "tq_dequantize"} <= declared
+            "tq_dequantize", "tq_attn_logits_workspace_size", "tq_attn_output_workspace_size"} <= declared
+    assert declared == set(tq.EXPORTED)
     for name in declared:
         assert hasattr(tq.LIB, name), name
 
@@ -104,14 +105,16 @@ def test_device_calls_validate_before_launch(tq):
     assert lib.tq_dequantize(ctypes.byref(p), ctypes.byref(pk), 0, None, 0, None) == tq.TQ_OK
     # logits: GQA divisibility, seq_len > row_tokens, top-k larger than seq_len
     f = ctypes.c_float(1.0)
+    ws = ctypes.c_void_p(1 << 20)          # 256-byte aligned stand-in, never dereferenced here
+    big = 1 << 30
     assert lib.tq_attn_logits(ctypes.byref(p), dummy, 0, 1, 6, 4, ctypes.byref(pk), 10, 10, f, dummy,
-                              0, None, None) == tq.TQ_ERR_INVALID
+                              0, None, ws, big, None) == tq.TQ_ERR_INVALID
     assert lib.tq_attn_logits(ctypes.byref(p), dummy, 0, 1, 4, 4, ctypes.byref(pk), 5, 10, f, dummy,
-                              0, None, None) == tq.TQ_ERR_INVALID
+                              0, None, ws, big, None) == tq.TQ_ERR_INVALID
     assert lib.tq_attn_logits(ctypes.byref(p), dummy, 0, 1, 4, 4, ctypes.byref(pk), 10, 5, f, dummy,
-                              10, dummy, None) == tq.TQ_ERR_INVALID
+                              10, dummy, ws, big, None) == tq.TQ_ERR_INVALID
     assert lib.tq_attn_logits(ctypes.byref(p), dummy, 0, 1, 4, 4, ctypes.byref(pk), 10, 0, f, dummy,
-                              0, None, None) == tq.TQ_OK
+                              0, None, None, 0, None) == tq.TQ_OK
     # misaligned input rows are refused, not read
     assert lib.tq_quantize_kv(ctypes.byref(p), ctypes.c_void_p(18), 1, 4, 128, ctypes.byref(pk), 0,
                               None) == tq.TQ_ERR_UNSUPPORTED
@@ -136,3 +139,73 @@ def test_polar_codebooks_match_oracle():
         np.testing.assert_allclose(t[lv - 2], ot, rtol=0, atol=1e-12)
     with pytest.raises(tq.TQError):
         tq.make_polar_codebook(96)
+
+
+def _size(fn, *args):
+    n = ctypes.c_size_t(7)
+    st = fn(*args, ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_queries_and_checks(tq):
+    """Caller-owned scratch: the size queries, and the calls refuse a missing,
+    short or misaligned workspace before any launch."""
+    lib = tq.LIB
+    dummy = ctypes.c_void_p(16)
+    f = ctypes.c_float(1.0)
+    pp = tq.Params(128, 3, tq.MODE_PROD, 0, dummy, dummy, dummy, dummy, dummy)
+    pm = tq.Params(128, 3, tq.MODE_MSE, 0, dummy, None, None, dummy, dummy)
+    pk = tq.Packed(dummy, dummy, dummy)
+    # dense logits: query tables of every (batch, kv head) stream, independent of seq_len
+    st, n8 = _size(lib.tq_attn_logits_workspace_size, ctypes.byref(pp), 1, 32, 8, 32768, 0)
+    assert st == tq.TQ_OK and n8 > 0 and n8 % 256 == 0
+    st, n64 = _size(lib.tq_attn_logits_workspace_size, ctypes.byref(pp), 8, 32, 8, 131072, 0)
+    assert st == tq.TQ_OK and n64 >= 8 * n8 - 8 * 256
+    assert _size(lib.tq_attn_logits_workspace_size, ctypes.byref(pp), 1, 32, 8, 5, 0) == (tq.TQ_OK, n8)
+    assert _size(lib.tq_attn_logits_workspace_size, ctypes.byref(pp), 0, 32, 8, 5, 0) == (tq.TQ_OK, 0)
+    assert _size(lib.tq_attn_logits_workspace_size, ctypes.byref(pp), 1, 32, 8, 0, 0) == (tq.TQ_OK, 0)
+    assert _size(lib.tq_attn_logits_workspace_size, ctypes.byref(pp), 1, 30, 8, 5, 0)[0] == tq.TQ_ERR_INVALID
+    assert lib.tq_attn_logits_workspace_size(ctypes.byref(pp), 1, 32, 8, 5, 0, None) == tq.TQ_ERR_INVALID
+    # top-k search (MSE only): partial lists grow with the query count
+    st, s1 = _size(lib.tq_attn_logits_workspace_size, ctypes.byref(pm), 1, 1000, 1, 100000, 10)
+    st2, s2 = _size(lib.tq_attn_logits_workspace_size, ctypes.byref(pm), 1, 2000, 1, 100000, 10)
+    assert st == st2 == tq.TQ_OK and 0 < s1 < s2
+    assert _size(lib.tq_attn_logits_workspace_size, ctypes.byref(pp), 1, 4, 1, 100, 10)[0] == tq.TQ_ERR_UNSUPPORTED
+    assert _size(lib.tq_attn_logits_workspace_size, ctypes.byref(pm), 1, 4, 1, 100, 17)[0] == tq.TQ_ERR_UNSUPPORTED
+    # attention output: MSE only
+    st, na = _size(lib.tq_attn_output_workspace_size, ctypes.byref(pm), 1, 32, 8, 32768)
+    assert st == tq.TQ_OK and na > 0
+    assert _size(lib.tq_attn_output_workspace_size, ctypes.byref(pm), 1, 32, 8, 0) == (tq.TQ_OK, 0)
+    assert _size(lib.tq_attn_output_workspace_size, ctypes.byref(pp), 1, 32, 8, 100)[0] == tq.TQ_ERR_UNSUPPORTED
+    # the calls: NULL / short workspace -> invalid, misaligned -> unsupported
+    args = (ctypes.byref(pp), dummy, 0, 1, 32, 8, ctypes.byref(pk), 64, 64, f, dummy, 0, None)
+    assert lib.tq_attn_logits(*args, None, 0, None) == tq.TQ_ERR_INVALID
+    assert lib.tq_attn_logits(*args, ctypes.c_void_p(1 << 20), n8 - 1, None) == tq.TQ_ERR_INVALID
+    assert lib.tq_attn_logits(*args, ctypes.c_void_p((1 << 20) + 16), n8, None) == tq.TQ_ERR_UNSUPPORTED
+    app = (ctypes.byref(pp), dummy, 0, dummy, 0, 1, 32, 8, ctypes.byref(pk), 64, 10, f, dummy)
+    assert lib.tq_append_attn_logits(*app, None, 0, None) == tq.TQ_ERR_INVALID
+    pv = tq.Packed(ctypes.c_void_p(1 << 20), dummy, None)
+    att = (ctypes.byref(pm), dummy, 1, 32, 8, ctypes.byref(pv), 32768, 32768, dummy, 0)
+    assert lib.tq_attn_output(*att, None, 0, None) == tq.TQ_ERR_INVALID
+    assert lib.tq_attn_output(*att, ctypes.c_void_p(1 << 20), na - 1, None) == tq.TQ_ERR_INVALID
+
+
+def test_logit_ranges_stay_below_2_31(tq):
+    """The streaming kernel drops lanes' stores through the byte offset 2^31,
+    so one stream's logits (group x seq_len fp32) must stay below 2^31 bytes:
+    larger calls are refused before any launch (no buffers needed)."""
+    lib = tq.LIB
+    dummy = ctypes.c_void_p(16)
+    f = ctypes.c_float(1.0)
+    for bits, mode, group in ((3, tq.MODE_PROD, 16), (1, tq.MODE_MSE, 8)):
+        p = tq.Params(128, bits, mode, 0, dummy, dummy, dummy, dummy, dummy)
+        pk = tq.Packed(dummy, dummy, dummy)
+        limit = (1 << 31) // (4 * group)                  # tokens at which the logits reach 2^31 bytes
+        assert _size(lib.tq_attn_logits_workspace_size, ctypes.byref(p), 1, group, 1, limit - 1, 0)[0] == tq.TQ_OK
+        assert _size(lib.tq_attn_logits_workspace_size, ctypes.byref(p), 1, group, 1, limit, 0)[0] == \
+            tq.TQ_ERR_UNSUPPORTED
+        assert lib.tq_attn_logits(ctypes.byref(p), dummy, 0, 1, group, 1, ctypes.byref(pk), limit, limit, f,
+                                  dummy, 0, None, ctypes.c_void_p(1 << 20), 1 << 30, None) == tq.TQ_ERR_UNSUPPORTED
+        assert lib.tq_append_attn_logits(ctypes.byref(p), dummy, 0, dummy, 0, 1, group, 1, ctypes.byref(pk),
+                                         limit, limit - 1, f, dummy, ctypes.c_void_p(1 << 20), 1 << 30,
+                                         None) == tq.TQ_ERR_UNSUPPORTED

@@ -268,3 +268,21 @@ def test_topk_brute_force_with_ties():
 
 def test_recall():
     assert qz.recall_at_k([[1, 2, 3]], [[3, 2, 9]]) == pytest.approx(2 / 3)
+
+
+def test_exact_topk_equals_full_sort_across_blocks():
+    """Blockwise exact top-k = a full sort of all inner products (topk, itself
+    pinned by brute force), including exact ties split across blocks."""
+    rng = np.random.default_rng(7)
+    db = rng.standard_normal((1000, 12))
+    db /= np.linalg.norm(db, axis=1, keepdims=True)
+    db[700] = db[3]                       # the same row in two blocks: an exact tie
+    db[999] = db[3]
+    q = rng.standard_normal((9, 12))
+    q[2] = db[3] * 5.0                    # rows 3, 700, 999 top this query, tied
+    want_v, want_i = qz.topk(q @ db.T, 10)
+    for block in (64, 333, 1000):
+        got_v, got_i = qz.exact_topk(q, db, 10, block=block)
+        np.testing.assert_array_equal(got_i, want_i)
+        np.testing.assert_allclose(got_v, want_v, rtol=1e-13, atol=0)
+    assert list(want_i[2][:3]) == [3, 700, 999]
