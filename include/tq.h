@@ -257,6 +257,24 @@ tq_status tq_attn_output(const tq_params *p, const float *logits, int32_t batch,
                          void *out, int32_t out_dtype, void *workspace, size_t workspace_bytes,
                          void *stream);
 
+/* tq_attn_output for callers that cannot allocate memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same arguments, validation, kernels and results, but the per-split
+ * partials live in a fixed device array of the library instead of a caller
+ * workspace.  The array holds TQ_NOALLOC_SCRATCH_BYTES (4 MiB); every device
+ * the call runs on holds its own copy until the process ends (its address is
+ * looked up on the first call on each device).  Calls whose
+ * tq_attn_output_workspace_size exceeds that return TQ_ERR_UNSUPPORTED
+ * before any launch.  Every call on one device shares the array: calls that
+ * overlap in time on a device (several streams, several host threads) race
+ * and give wrong results, so queue them on one stream.  Nothing in the array
+ * needs clearing: every call writes all it reads.
+ * Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED, TQ_ERR_HIP. */
+#define TQ_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+tq_status tq_attn_output_noalloc(const tq_params *p, const float *logits, int32_t batch, int32_t n_q_heads,
+                                 int32_t n_kv_heads, const tq_packed *v, int64_t row_tokens, int64_t seq_len,
+                                 void *out, int32_t out_dtype, void *stream);
+
 /* Device scratch that tq_attn_output needs for these arguments on the
  * current device; 0 when seq_len or batch is 0.
  * Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED. */

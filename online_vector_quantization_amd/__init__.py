@@ -36,7 +36,9 @@ KIND_M = 2
 
 EXPORTED = ["tq_make_codebook", "tq_make_polar_codebook", "tq_make_rotation", "tq_quantize_kv",
             "tq_attn_logits_workspace_size", "tq_attn_logits", "tq_append_attn_logits",
-            "tq_attn_output_workspace_size", "tq_attn_output", "tq_dequantize", "tq_status_string"]
+            "tq_attn_output_workspace_size", "tq_attn_output", "tq_attn_output_noalloc", "tq_dequantize",
+            "tq_status_string"]
+NOALLOC_SCRATCH_BYTES = 4 << 20
 
 
 class TQError(RuntimeError):
@@ -75,6 +77,8 @@ def _load():
     lib.tq_attn_output_workspace_size.argtypes = [ctypes.POINTER(Params), i32, i32, i32, i64, psz]
     lib.tq_attn_output.argtypes = [ctypes.POINTER(Params), vp, i32, i32, i32, ctypes.POINTER(Packed),
                                    i64, i64, vp, i32, vp, sz, vp]
+    lib.tq_attn_output_noalloc.argtypes = [ctypes.POINTER(Params), vp, i32, i32, i32, ctypes.POINTER(Packed),
+                                           i64, i64, vp, i32, vp]
     lib.tq_dequantize.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(Packed), i64, vp, i32, vp]
     lib.tq_status_string.argtypes = [i32]
     lib.tq_status_string.restype = ctypes.c_char_p
@@ -326,6 +330,17 @@ class Quantizer:
                                 ctypes.c_void_p(out.data_ptr()), _dtype_code(out), ws, wsb,
                                 _stream_ptr(self.device))
         _check(st, "tq_attn_output")
+        return out
+
+    def attn_output_noalloc(self, logits, cache, n_kv_heads, seq_len, out, row_tokens=None):
+        """attn_output into ``out`` with no workspace: the library's fixed
+        device array holds the partials (see tq_attn_output_noalloc)."""
+        bsz, hq, _ = logits.shape
+        row_tokens = seq_len if row_tokens is None else row_tokens
+        st = LIB.tq_attn_output_noalloc(ctypes.byref(self._params), ctypes.c_void_p(logits.data_ptr()), bsz, hq,
+                                        n_kv_heads, ctypes.byref(cache.struct()), row_tokens, seq_len,
+                                        ctypes.c_void_p(out.data_ptr()), _dtype_code(out), _stream_ptr(self.device))
+        _check(st, "tq_attn_output_noalloc")
         return out
 
     def dequantize(self, cache, n_vec, out_dtype=None, out=None):

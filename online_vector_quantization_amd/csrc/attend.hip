@@ -28,6 +28,7 @@
 // per value coordinate and head on the vector ALUs, which bounds it before
 // HBM does for G >= 4 heads per KV head.
 #include <cfloat>
+#include <mutex>
 
 #include "tq_device.h"
 #include "tq_internal.h"
@@ -832,3 +833,31 @@ hipError_t launch_attend(int d, int lbits, const AttendArgs &a, hipStream_t s) {
 
 }  // namespace tqi
 
+// Per-split partials of tq_attn_output_noalloc: a fixed array in device
+// memory instead of a caller workspace (each device that runs the library
+// holds its own copy until the process ends).  Host code never passes the
+// array's name to a kernel: that name is a host-side stand-in, not a device
+// address; the device address comes from hipGetSymbolAddress below.
+static __device__ __align__(256) unsigned char scratch[tqi::kNoAllocScratchBytes];
+
+namespace tqi {
+
+hipError_t noalloc_scratch(void **out) {
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {        // once per device, with that device current
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
+}  // namespace tqi

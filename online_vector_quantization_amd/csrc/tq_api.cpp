@@ -265,10 +265,14 @@ extern "C" tq_status tq_attn_output_workspace_size(const tq_params *p, int32_t b
   return TQ_OK;
 }
 
-extern "C" tq_status tq_attn_output(const tq_params *p, const float *logits, int32_t batch,
-                                    int32_t n_q_heads, int32_t n_kv_heads, const tq_packed *v,
-                                    int64_t row_tokens, int64_t seq_len, void *out, int32_t out_dtype,
-                                    void *workspace, size_t workspace_bytes, void *stream) {
+namespace {
+
+// tq_attn_output and its no-allocation variant: the same validation, the
+// same kernels; `noalloc` takes the library's fixed array as the workspace.
+tq_status attn_output_call(const tq_params *p, const float *logits, int32_t batch, int32_t n_q_heads,
+                           int32_t n_kv_heads, const tq_packed *v, int64_t row_tokens, int64_t seq_len,
+                           void *out, int32_t out_dtype, void *workspace, size_t workspace_bytes,
+                           bool noalloc, void *stream) {
   tq_status st = check_params(p);
   if (st != TQ_OK) return st;
   if (v == nullptr || row_tokens < seq_len) return TQ_ERR_INVALID;
@@ -278,10 +282,19 @@ extern "C" tq_status tq_attn_output(const tq_params *p, const float *logits, int
   if (batch == 0) return TQ_OK;
   if (out == nullptr) return TQ_ERR_INVALID;
   if (seq_len > 0 && (logits == nullptr || v->codes == nullptr || v->norm == nullptr)) return TQ_ERR_INVALID;
-  st = check_workspace(workspace, workspace_bytes,
-                       tqi::attend_workspace_bytes(p->d, lloyd_bits(p), batch, n_q_heads, n_kv_heads, seq_len));
-  if (st != TQ_OK) return st;
+  const size_t need = tqi::attend_workspace_bytes(p->d, lloyd_bits(p), batch, n_q_heads, n_kv_heads, seq_len);
+  if (noalloc) {
+    if (need > tqi::kNoAllocScratchBytes) return TQ_ERR_UNSUPPORTED;
+  } else {
+    st = check_workspace(workspace, workspace_bytes, need);
+    if (st != TQ_OK) return st;
+  }
   if ((uintptr_t)v->codes & 15u) return TQ_ERR_UNSUPPORTED;
+  if (noalloc) {
+    const hipError_t e = tqi::noalloc_scratch(&workspace);
+    if (e != hipSuccess) return TQ_ERR_HIP;
+    workspace_bytes = tqi::kNoAllocScratchBytes;
+  }
   tqi::AttendArgs a;
   a.logits = logits;
   a.batch = batch;
@@ -298,6 +311,24 @@ extern "C" tq_status tq_attn_output(const tq_params *p, const float *logits, int
   a.workspace = workspace;
   a.workspace_bytes = workspace_bytes;
   return hip_status(tqi::launch_attend(p->d, lloyd_bits(p), a, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" tq_status tq_attn_output(const tq_params *p, const float *logits, int32_t batch,
+                                    int32_t n_q_heads, int32_t n_kv_heads, const tq_packed *v,
+                                    int64_t row_tokens, int64_t seq_len, void *out, int32_t out_dtype,
+                                    void *workspace, size_t workspace_bytes, void *stream) {
+  return attn_output_call(p, logits, batch, n_q_heads, n_kv_heads, v, row_tokens, seq_len, out, out_dtype,
+                          workspace, workspace_bytes, false, stream);
+}
+
+extern "C" tq_status tq_attn_output_noalloc(const tq_params *p, const float *logits, int32_t batch,
+                                            int32_t n_q_heads, int32_t n_kv_heads, const tq_packed *v,
+                                            int64_t row_tokens, int64_t seq_len, void *out, int32_t out_dtype,
+                                            void *stream) {
+  return attn_output_call(p, logits, batch, n_q_heads, n_kv_heads, v, row_tokens, seq_len, out, out_dtype,
+                          nullptr, 0, true, stream);
 }
 
 extern "C" tq_status tq_dequantize(const tq_params *p, const tq_packed *k, int64_t n_vec, void *out,

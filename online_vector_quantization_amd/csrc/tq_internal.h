@@ -104,6 +104,12 @@ struct AttendArgs {
 };
 
 bool attend_supported(int d, int lbits, int group, int64_t seq_len);
+
+// Fixed device array behind tq_attn_output_noalloc: its size, and its device
+// address on the current device (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = TQ_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+hipError_t noalloc_scratch(void **out);
 size_t attend_workspace_bytes(int d, int lbits, int batch, int n_q_heads, int n_kv_heads, int64_t seq_len);
 hipError_t launch_attend(int d, int lbits, const AttendArgs &a, hipStream_t s);
 

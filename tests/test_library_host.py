@@ -209,3 +209,24 @@ def test_logit_ranges_stay_below_2_31(tq):
         assert lib.tq_append_attn_logits(ctypes.byref(p), dummy, 0, dummy, 0, 1, group, 1, ctypes.byref(pk),
                                          limit, limit - 1, f, dummy, ctypes.c_void_p(1 << 20), 1 << 30,
                                          None) == tq.TQ_ERR_UNSUPPORTED
+
+
+def test_noalloc_entry_validates_before_launch(tq):
+    """tq_attn_output_noalloc: the same argument checks as tq_attn_output, and
+    shapes whose partials exceed its fixed array are refused before any HIP
+    call (the array's address is only looked up once a call is accepted)."""
+    lib = tq.LIB
+    dummy = ctypes.c_void_p(16)
+    pm = tq.Params(256, 3, tq.MODE_MSE, 0, dummy, None, None, dummy, dummy)
+    pv = tq.Packed(ctypes.c_void_p(1 << 20), dummy, None)
+    st, need = _size(lib.tq_attn_output_workspace_size, ctypes.byref(pm), 64, 1024, 64, 256)
+    assert st == tq.TQ_OK and need > tq.NOALLOC_SCRATCH_BYTES
+    assert lib.tq_attn_output_noalloc(ctypes.byref(pm), dummy, 64, 1024, 64, ctypes.byref(pv), 256, 256, dummy, 0,
+                                      None) == tq.TQ_ERR_UNSUPPORTED
+    assert lib.tq_attn_output_noalloc(ctypes.byref(pm), dummy, 1, 6, 4, ctypes.byref(pv), 256, 256, dummy, 0,
+                                      None) == tq.TQ_ERR_INVALID
+    assert lib.tq_attn_output_noalloc(None, dummy, 1, 4, 4, ctypes.byref(pv), 256, 256, dummy, 0,
+                                      None) == tq.TQ_ERR_INVALID
+    pp = tq.Params(128, 3, tq.MODE_PROD, 0, dummy, dummy, dummy, dummy, dummy)
+    assert lib.tq_attn_output_noalloc(ctypes.byref(pp), dummy, 1, 4, 4, ctypes.byref(pv), 256, 256, dummy, 0,
+                                      None) == tq.TQ_ERR_UNSUPPORTED
