@@ -86,3 +86,75 @@ def test_zero_key_and_position_bounds():
     np.testing.assert_array_equal(logits[1, 0:2, 0], 0.0)  # a zero key has logit 0
     with pytest.raises(ValueError):
         dec.append_step(cache, x, cache["codes"].shape[2], q, pi, c, t, mode, 1.0, s_mat=s_mat)
+
+
+def _paged_from(cache, page_tokens, n_pages_spare, seed):
+    """Scatter a contiguous cache [B, Hkv, R, ...] into a pool of pages in a
+    random order (with spare pages never referenced); returns (pool, table)."""
+    bsz, hkv, rows = cache["norm"].shape
+    per_seq = -(-rows // page_tokens)
+    n_pages = bsz * per_seq + n_pages_spare
+    order = np.random.default_rng(seed).permutation(n_pages)
+    table = order[:bsz * per_seq].reshape(bsz, per_seq)
+    rng = np.random.default_rng(seed + 1)
+    pool = {}
+    for name, arr in cache.items():
+        shape = (n_pages * hkv * page_tokens,) + arr.shape[3:]
+        pool[name] = rng.integers(0, 255, size=shape).astype(arr.dtype)      # garbage in unused rows
+    for b in range(bsz):
+        for h in range(hkv):
+            r = dec.paged_rows(table, page_tokens, hkv, b, h, np.arange(rows))
+            for name in cache:
+                pool[name][r] = cache[name][b, h]
+    return pool, table
+
+
+@pytest.mark.parametrize("mode", [qz.MODE_MSE, qz.MODE_PROD])
+def test_paged_step_equals_contiguous_step_after_gather(mode):
+    """A decode step on a paged pool (pages in random order, spare pages full
+    of garbage) gives exactly the logits and records of the same step on the
+    contiguous cache; gathering the pool through the block table gives back
+    the contiguous cache."""
+    pi, s_mat, c, t, keys, q, cache = _setup(mode, rows=12)
+    bsz, hkv, rows, d = keys.shape
+    cache, _, _ = dec.append_step(cache, keys[:, :, 0], 0, q, pi, c, t, mode, 0.5, s_mat=s_mat)
+    for pos in range(1, 7):
+        cache, _, _ = dec.append_step(cache, keys[:, :, pos], pos, q, pi, c, t, mode, 0.5, s_mat=s_mat)
+    pool, table = _paged_from(cache, 4, 3, seed=mode + 3)
+    g = dec.gather_paged(pool, table, 4, hkv, rows)
+    for name in cache:
+        np.testing.assert_array_equal(g[name], cache[name])
+    pos = 7
+    ccache, clog, cref = dec.append_step(cache, keys[:, :, pos], pos, q, pi, c, t, mode, 0.5, s_mat=s_mat)
+    ppool, plog, pref = dec.append_step_paged(pool, table, 4, keys[:, :, pos], pos, q, pi, c, t, mode, 0.5,
+                                              s_mat=s_mat)
+    np.testing.assert_array_equal(plog, clog)
+    np.testing.assert_array_equal(pref["codes"], cref["codes"])
+    g = dec.gather_paged(ppool, table, 4, hkv, rows)
+    for name in cache:
+        np.testing.assert_array_equal(g[name], ccache[name])
+
+
+def test_paged_step_touches_only_the_new_rows():
+    """Every pool row but the new token's row of each (sequence, KV head) is
+    bit-identical after the step, including the spare pages."""
+    mode = qz.MODE_PROD
+    pi, s_mat, c, t, keys, q, cache = _setup(mode, rows=12)
+    bsz, hkv, rows, d = keys.shape
+    pool, table = _paged_from(cache, 4, 2, seed=11)
+    pos = 9
+    new, _, _ = dec.append_step_paged(pool, table, 4, keys[:, :, pos], pos, q, pi, c, t, mode, 1.0, s_mat=s_mat)
+    changed = np.zeros(len(pool["norm"]), bool)
+    for b in range(bsz):
+        for h in range(hkv):
+            changed[dec.paged_rows(table, 4, hkv, b, h, [pos])] = True
+    for name in pool:
+        assert np.array_equal(new[name][~changed], pool[name][~changed]), name
+    assert changed.sum() == bsz * hkv
+
+
+def test_paged_rows_layout():
+    """Page g holds every KV head's rows of its tokens, head-major."""
+    table = np.array([[5, 2], [0, 7]])
+    assert list(dec.paged_rows(table, 64, 8, 0, 0, [0, 63, 64, 127])) == [5 * 512, 5 * 512 + 63, 2 * 512, 2 * 512 + 63]
+    assert list(dec.paged_rows(table, 64, 8, 1, 3, [65])) == [(7 * 8 + 3) * 64 + 1]
