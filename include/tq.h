@@ -25,7 +25,7 @@
  *   - The library never allocates or frees memory, never synchronises and
  *     keeps no state between calls (apart from a per-device cache of the
  *     compute-unit count, set once).  Calls that need device scratch memory
- *     (tq_attn_logits, tq_append_attn_logits, tq_attn_output) take a
+ *     (tq_attn_logits with top-k, tq_attn_output) take a
  *     caller-owned `workspace` of `workspace_bytes` bytes: 256-byte aligned
  *     device memory of at least the size the matching *_workspace_size query
  *     gives for the same arguments on the current device.  It is borrowed
@@ -175,10 +175,9 @@ tq_status tq_quantize_kv(const tq_params *p, const void *x, int32_t x_dtype, int
 
 /* Device scratch that tq_attn_logits needs for these arguments on the current
  * device (the same validation as the call itself: an unsupported shape
- * returns TQ_ERR_UNSUPPORTED).  Dense logits need the query tables: a few KB
- * per (batch, kv head) stream; top-k search needs its partial lists.  The
- * size for tq_append_attn_logits is this query with seq_len = pos + 1 and
- * topk = 0.  *bytes is 0 for empty calls.
+ * returns TQ_ERR_UNSUPPORTED).  Dense logits need none (each workgroup
+ * builds its query tables in LDS): *bytes is 0 for topk == 0 and for empty
+ * calls; top-k search needs its rotated queries and partial lists.
  * Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED. */
 tq_status tq_attn_logits_workspace_size(const tq_params *p, int32_t batch, int32_t n_q_heads,
                                         int32_t n_kv_heads, int64_t seq_len, int32_t topk, size_t *bytes);
@@ -195,7 +194,8 @@ tq_status tq_attn_logits_workspace_size(const tq_params *p, int32_t batch, int32
  *                ties to the smaller token index, descending; logits is
  *                fp32 [batch][n_q_heads][topk] and topk_idx int32 of the same
  *                shape.  Needs seq_len >= topk.
- *   workspace    device scratch of tq_attn_logits_workspace_size bytes
+ *   workspace    device scratch of tq_attn_logits_workspace_size bytes (NULL
+ *                and 0 for dense logits)
  * GQA: query head h reads KV head h / (n_q_heads / n_kv_heads); n_q_heads
  * must be a multiple of n_kv_heads.  Dense logits support d in {128, 256},
  * up to 16 query heads per KV head, streams whose packed codes stay under
@@ -224,8 +224,6 @@ tq_status tq_attn_logits(const tq_params *p, const void *q, int32_t q_dtype, int
  *                read (tokens 0..pos-1 must already hold packed keys)
  *   pos          0 <= pos < row_tokens
  *   logits       device fp32 [batch][n_q_heads][pos + 1]
- *   workspace    device scratch of tq_attn_logits_workspace_size(p, batch,
- *                n_q_heads, n_kv_heads, pos + 1, 0) bytes
  * The new key is quantised in fp64 from the fp32 matrices (the inner-product
  * mode needs p->qjl_rot).  Supported: as dense tq_attn_logits (d in {128,
  * 256}, up to 16 query heads per KV head).  batch == 0 is a no-op.
@@ -233,8 +231,43 @@ tq_status tq_attn_logits(const tq_params *p, const void *q, int32_t q_dtype, int
 tq_status tq_append_attn_logits(const tq_params *p, const void *x_new, int32_t x_dtype,
                                 const void *q, int32_t q_dtype, int32_t batch, int32_t n_q_heads,
                                 int32_t n_kv_heads, const tq_packed *k, int64_t row_tokens,
-                                int64_t pos, float scale, float *logits, void *workspace,
-                                size_t workspace_bytes, void *stream);
+                                int64_t pos, float scale, float *logits, void *stream);
+
+/* Paged key cache (a serving cache of fixed-size pages; the page reads
+ * "quantise on every cache update", section "TurboQuant 구현 방법").  The
+ * pool is one tq_packed of n_pages * n_kv_heads * page_tokens rows; page g
+ * holds the rows of every KV head for its tokens, head-major: token t of KV
+ * head h of sequence b is pool row
+ *     (block_table[b * max_pages + t / page_tokens] * n_kv_heads + h)
+ *     * page_tokens + t % page_tokens.
+ * Sequences own disjoint pages in any order.  A block-table entry outside
+ * [0, n_pages) never faults: its rows read as zero keys and an append into
+ * it writes nothing. */
+typedef struct tq_pages {
+  const int32_t *block_table; /* device [batch][max_pages]                        */
+  int32_t page_tokens;        /* tokens per page, a positive multiple of 64       */
+  int32_t max_pages;          /* block-table entries per sequence                 */
+  int64_t n_pages;            /* pages in the pool                                */
+} tq_pages;
+
+/* tq_attn_logits (dense, topk = 0) over a paged key cache: the first seq_len
+ * tokens of every sequence, read through its block table; logits as
+ * tq_attn_logits, [batch][n_q_heads][seq_len].  Needs seq_len <=
+ * max_pages * page_tokens and the pool's packed codes under 2 GiB.  Same
+ * support and errors as tq_attn_logits; no scratch. */
+tq_status tq_attn_logits_paged(const tq_params *p, const void *q, int32_t q_dtype, int32_t batch,
+                               int32_t n_q_heads, int32_t n_kv_heads, const tq_packed *pool,
+                               const tq_pages *pages, int64_t seq_len, float scale, float *logits,
+                               void *stream);
+
+/* tq_append_attn_logits over a paged key cache: the new key of every
+ * (sequence, KV head) goes to the pool row of token pos (its page must be in
+ * the block table: pos < max_pages * page_tokens), then the logits over tokens
+ * 0..pos, [batch][n_q_heads][pos + 1].  One launch, no scratch. */
+tq_status tq_append_attn_logits_paged(const tq_params *p, const void *x_new, int32_t x_dtype,
+                                      const void *q, int32_t q_dtype, int32_t batch, int32_t n_q_heads,
+                                      int32_t n_kv_heads, const tq_packed *pool, const tq_pages *pages,
+                                      int64_t pos, float scale, float *logits, void *stream);
 
 /* Decode attention output straight from packed values (page: the KV cache
  * holds keys and values, section "TurboQuant란 무엇인가요?", and attention runs

@@ -35,7 +35,8 @@ KIND_S = 1
 KIND_M = 2
 
 EXPORTED = ["tq_make_codebook", "tq_make_polar_codebook", "tq_make_rotation", "tq_quantize_kv",
-            "tq_attn_logits_workspace_size", "tq_attn_logits", "tq_append_attn_logits",
+            "tq_attn_logits_workspace_size", "tq_attn_logits", "tq_append_attn_logits", "tq_attn_logits_paged",
+            "tq_append_attn_logits_paged",
             "tq_attn_output_workspace_size", "tq_attn_output", "tq_attn_output_noalloc", "tq_dequantize",
             "tq_status_string"]
 NOALLOC_SCRATCH_BYTES = 4 << 20
@@ -58,6 +59,11 @@ class Packed(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("norm", ctypes.c_void_p), ("rnorm", ctypes.c_void_p)]
 
 
+class Pages(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("page_tokens", ctypes.c_int32), ("max_pages", ctypes.c_int32),
+                ("n_pages", ctypes.c_int64)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError("libtq.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
@@ -73,7 +79,11 @@ def _load():
     lib.tq_attn_logits.argtypes = [ctypes.POINTER(Params), vp, i32, i32, i32, i32,
                                    ctypes.POINTER(Packed), i64, i64, f32, vp, i32, vp, vp, sz, vp]
     lib.tq_append_attn_logits.argtypes = [ctypes.POINTER(Params), vp, i32, vp, i32, i32, i32, i32,
-                                          ctypes.POINTER(Packed), i64, i64, f32, vp, vp, sz, vp]
+                                          ctypes.POINTER(Packed), i64, i64, f32, vp, vp]
+    lib.tq_attn_logits_paged.argtypes = [ctypes.POINTER(Params), vp, i32, i32, i32, i32, ctypes.POINTER(Packed),
+                                         ctypes.POINTER(Pages), i64, f32, vp, vp]
+    lib.tq_append_attn_logits_paged.argtypes = [ctypes.POINTER(Params), vp, i32, vp, i32, i32, i32, i32,
+                                                ctypes.POINTER(Packed), ctypes.POINTER(Pages), i64, f32, vp, vp]
     lib.tq_attn_output_workspace_size.argtypes = [ctypes.POINTER(Params), i32, i32, i32, i64, psz]
     lib.tq_attn_output.argtypes = [ctypes.POINTER(Params), vp, i32, i32, i32, ctypes.POINTER(Packed),
                                    i64, i64, vp, i32, vp, sz, vp]
@@ -280,8 +290,7 @@ class Quantizer:
         _check(st, "tq_attn_logits")
         return out
 
-    def append_attn_logits(self, x_new, q, cache, n_kv_heads, pos, scale, row_tokens=None, out=None,
-                           workspace=None):
+    def append_attn_logits(self, x_new, q, cache, n_kv_heads, pos, scale, row_tokens=None, out=None):
         """Quantise x_new [batch, n_kv_heads, d] into token ``pos`` of every stream of
         ``cache`` and return the logits [batch, n_q_heads, pos + 1] (fp32)."""
         torch = _torch()
@@ -290,14 +299,44 @@ class Quantizer:
             row_tokens = cache.capacity // max(bsz * n_kv_heads, 1)
         if out is None:
             out = torch.empty((bsz, hq, pos + 1), dtype=torch.float32, device=self.device)
-        need = self.logits_workspace_size(bsz, hq, n_kv_heads, pos + 1) if 0 <= pos < row_tokens else 0
-        ws, wsb = self._workspace(need, workspace)
         st = LIB.tq_append_attn_logits(ctypes.byref(self._params), ctypes.c_void_p(x_new.data_ptr()),
                                        _dtype_code(x_new), ctypes.c_void_p(q.data_ptr()), _dtype_code(q),
                                        bsz, hq, n_kv_heads, ctypes.byref(cache.struct()), row_tokens, pos,
-                                       float(scale), ctypes.c_void_p(out.data_ptr()), ws, wsb,
-                                       _stream_ptr(self.device))
+                                       float(scale), ctypes.c_void_p(out.data_ptr()), _stream_ptr(self.device))
         _check(st, "tq_append_attn_logits")
+        return out
+
+    def _pages(self, block_table, page_tokens, n_pages):
+        return Pages(block_table.data_ptr(), page_tokens, block_table.shape[1], n_pages)
+
+    def attn_logits_paged(self, q, pool, block_table, page_tokens, n_kv_heads, seq_len, scale, out=None):
+        """Dense logits [batch, n_q_heads, seq_len] over a paged pool; block_table
+        is an int32 device tensor [batch, max_pages]; the pool holds
+        pool.capacity // (n_kv_heads * page_tokens) pages."""
+        torch = _torch()
+        bsz, hq, _ = q.shape
+        if out is None:
+            out = torch.empty((bsz, hq, seq_len), dtype=torch.float32, device=self.device)
+        pg = self._pages(block_table, page_tokens, pool.capacity // (n_kv_heads * page_tokens))
+        st = LIB.tq_attn_logits_paged(ctypes.byref(self._params), ctypes.c_void_p(q.data_ptr()), _dtype_code(q),
+                                      bsz, hq, n_kv_heads, ctypes.byref(pool.struct()), ctypes.byref(pg), seq_len,
+                                      float(scale), ctypes.c_void_p(out.data_ptr()), _stream_ptr(self.device))
+        _check(st, "tq_attn_logits_paged")
+        return out
+
+    def append_attn_logits_paged(self, x_new, q, pool, block_table, page_tokens, n_kv_heads, pos, scale, out=None):
+        """Quantise x_new [batch, n_kv_heads, d] into token ``pos`` of every
+        sequence of a paged pool and return the logits [batch, n_q_heads, pos + 1]."""
+        torch = _torch()
+        bsz, hq, _ = q.shape
+        if out is None:
+            out = torch.empty((bsz, hq, pos + 1), dtype=torch.float32, device=self.device)
+        pg = self._pages(block_table, page_tokens, pool.capacity // (n_kv_heads * page_tokens))
+        st = LIB.tq_append_attn_logits_paged(ctypes.byref(self._params), ctypes.c_void_p(x_new.data_ptr()),
+                                             _dtype_code(x_new), ctypes.c_void_p(q.data_ptr()), _dtype_code(q),
+                                             bsz, hq, n_kv_heads, ctypes.byref(pool.struct()), ctypes.byref(pg), pos,
+                                             float(scale), ctypes.c_void_p(out.data_ptr()), _stream_ptr(self.device))
+        _check(st, "tq_append_attn_logits_paged")
         return out
 
     def search(self, q, cache, n_kv_heads, seq_len, topk, scale=1.0, row_tokens=None, workspace=None):

@@ -76,10 +76,9 @@ tq_status logits_shape(const tq_params *p, int32_t batch, int32_t n_q_heads, int
 
 size_t logits_ws_bytes(const tq_params *p, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
                        int64_t seq_len, int32_t topk) {
-  if (batch == 0 || seq_len == 0) return 0;
-  if (topk > 0) return tqi::search_workspace_bytes(p->d, lloyd_bits(p), batch, n_q_heads, n_kv_heads, seq_len);
-  return tqi::logits_workspace_bytes(p->d, lloyd_bits(p), p->mode == TQ_MODE_PROD,
-                                     (int64_t)batch * n_kv_heads, n_q_heads / n_kv_heads);
+  // dense logits build their query tables in LDS: only search needs scratch
+  if (batch == 0 || seq_len == 0 || topk == 0) return 0;
+  return tqi::search_workspace_bytes(p->d, lloyd_bits(p), batch, n_q_heads, n_kv_heads, seq_len);
 }
 
 tq_status check_attend_args(const tq_params *p, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
@@ -208,7 +207,7 @@ extern "C" tq_status tq_append_attn_logits(const tq_params *p, const void *x_new
                                            const void *q, int32_t q_dtype, int32_t batch,
                                            int32_t n_q_heads, int32_t n_kv_heads, const tq_packed *k,
                                            int64_t row_tokens, int64_t pos, float scale, float *logits,
-                                           void *workspace, size_t workspace_bytes, void *stream) {
+                                           void *stream) {
   tq_status st = check_logit_args(p, batch, n_q_heads, n_kv_heads, 0, 0);
   if (st != TQ_OK) return st;
   const bool prod = p->mode == TQ_MODE_PROD;
@@ -222,8 +221,6 @@ extern "C" tq_status tq_append_attn_logits(const tq_params *p, const void *x_new
   if (x_new == nullptr || q == nullptr || logits == nullptr || k->codes == nullptr || k->norm == nullptr)
     return TQ_ERR_INVALID;
   if (prod && (p->qjl == nullptr || p->qjl_rot == nullptr || k->rnorm == nullptr)) return TQ_ERR_INVALID;
-  st = check_workspace(workspace, workspace_bytes, logits_ws_bytes(p, batch, n_q_heads, n_kv_heads, pos + 1, 0));
-  if (st != TQ_OK) return st;
   if ((uintptr_t)k->codes & 3u) return TQ_ERR_UNSUPPORTED;
   tqi::LogitArgs a;
   a.q = q;
@@ -249,8 +246,111 @@ extern "C" tq_status tq_append_attn_logits(const tq_params *p, const void *x_new
   a.norm_out = k->norm;
   a.rnorm_out = k->rnorm;
   a.pos = pos;
-  a.workspace = workspace;
-  a.workspace_bytes = workspace_bytes;
+  return hip_status(tqi::launch_logits(p->d, lloyd_bits(p), prod, a, (hipStream_t)stream));
+}
+
+namespace {
+
+// Checks of a paged call: the table and page shape, tokens within the table,
+// the pool's codes addressable with 32-bit offsets (plus one block of
+// prefetch).  On success fills the paged fields of `a`.
+tq_status paged_args(const tq_params *p, int32_t batch, int32_t n_kv_heads, const tq_pages *pg,
+                     int64_t tokens, tqi::LogitArgs &a) {
+  if (pg == nullptr || pg->block_table == nullptr) return TQ_ERR_INVALID;
+  if (pg->page_tokens <= 0 || pg->page_tokens % 64 != 0 || pg->max_pages <= 0 || pg->n_pages <= 0)
+    return TQ_ERR_INVALID;
+  if (tokens > (int64_t)pg->max_pages * pg->page_tokens) return TQ_ERR_INVALID;
+  const int64_t rows = pg->n_pages * n_kv_heads * (int64_t)pg->page_tokens;
+  const int64_t rb = (int64_t)p->bits * p->d / 8;
+  if ((rows + 64) * rb >= (1LL << 31) || rows >= (1LL << 31)) return TQ_ERR_UNSUPPORTED;
+  (void)batch;
+  a.block_table = pg->block_table;
+  a.page_tokens = pg->page_tokens;
+  a.max_pages = pg->max_pages;
+  a.pool_rows = rows;
+  a.row_tokens = 0;
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" tq_status tq_attn_logits_paged(const tq_params *p, const void *q, int32_t q_dtype, int32_t batch,
+                                          int32_t n_q_heads, int32_t n_kv_heads, const tq_packed *pool,
+                                          const tq_pages *pages, int64_t seq_len, float scale, float *logits,
+                                          void *stream) {
+  tq_status st = check_logit_args(p, batch, n_q_heads, n_kv_heads, seq_len, 0);
+  if (st != TQ_OK) return st;
+  const bool prod = p->mode == TQ_MODE_PROD;
+  if (pool == nullptr) return TQ_ERR_INVALID;
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_ERR_INVALID;
+  st = logits_shape(p, batch, n_q_heads, n_kv_heads, seq_len, 0);
+  if (st != TQ_OK) return st;
+  tqi::LogitArgs a;
+  st = paged_args(p, batch, n_kv_heads, pages, seq_len, a);
+  if (st != TQ_OK) return st;
+  if (batch == 0 || seq_len == 0) return TQ_OK;
+  if (q == nullptr || logits == nullptr || pool->codes == nullptr || pool->norm == nullptr) return TQ_ERR_INVALID;
+  if (prod && (p->qjl == nullptr || pool->rnorm == nullptr)) return TQ_ERR_INVALID;
+  if ((uintptr_t)pool->codes & 3u) return TQ_ERR_UNSUPPORTED;
+  a.q = q;
+  a.q_f32 = q_dtype == TQ_F32;
+  a.batch = batch;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.pi = p->pi;
+  a.s_mat = p->qjl;
+  a.centroids = p->centroids;
+  a.codes = pool->codes;
+  a.norm = pool->norm;
+  a.rnorm = pool->rnorm;
+  a.seq_len = seq_len;
+  a.scale = scale;
+  a.logits = logits;
+  return hip_status(tqi::launch_logits(p->d, lloyd_bits(p), prod, a, (hipStream_t)stream));
+}
+
+extern "C" tq_status tq_append_attn_logits_paged(const tq_params *p, const void *x_new, int32_t x_dtype,
+                                                 const void *q, int32_t q_dtype, int32_t batch, int32_t n_q_heads,
+                                                 int32_t n_kv_heads, const tq_packed *pool, const tq_pages *pages,
+                                                 int64_t pos, float scale, float *logits, void *stream) {
+  tq_status st = check_logit_args(p, batch, n_q_heads, n_kv_heads, 0, 0);
+  if (st != TQ_OK) return st;
+  const bool prod = p->mode == TQ_MODE_PROD;
+  if (pool == nullptr || pos < 0) return TQ_ERR_INVALID;
+  if ((q_dtype != TQ_F32 && q_dtype != TQ_BF16) || (x_dtype != TQ_F32 && x_dtype != TQ_BF16))
+    return TQ_ERR_INVALID;
+  st = logits_shape(p, batch, n_q_heads, n_kv_heads, pos + 1, 0);
+  if (st != TQ_OK) return st;
+  tqi::LogitArgs a;
+  st = paged_args(p, batch, n_kv_heads, pages, pos + 1, a);
+  if (st != TQ_OK) return st;
+  if (batch == 0) return TQ_OK;
+  if (x_new == nullptr || q == nullptr || logits == nullptr || pool->codes == nullptr || pool->norm == nullptr)
+    return TQ_ERR_INVALID;
+  if (prod && (p->qjl == nullptr || p->qjl_rot == nullptr || pool->rnorm == nullptr)) return TQ_ERR_INVALID;
+  if ((uintptr_t)pool->codes & 3u) return TQ_ERR_UNSUPPORTED;
+  a.q = q;
+  a.q_f32 = q_dtype == TQ_F32;
+  a.batch = batch;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.pi = p->pi;
+  a.s_mat = p->qjl;
+  a.centroids = p->centroids;
+  a.codes = pool->codes;
+  a.norm = pool->norm;
+  a.rnorm = pool->rnorm;
+  a.seq_len = pos + 1;
+  a.scale = scale;
+  a.logits = logits;
+  a.x_new = x_new;
+  a.x_f32 = x_dtype == TQ_F32;
+  a.boundaries = p->boundaries;
+  a.m_mat = p->qjl_rot;
+  a.codes_out = pool->codes;
+  a.norm_out = pool->norm;
+  a.rnorm_out = pool->rnorm;
+  a.pos = pos;
   return hip_status(tqi::launch_logits(p->d, lloyd_bits(p), prod, a, (hipStream_t)stream));
 }
 

@@ -50,7 +50,11 @@ struct LogitArgs {
   uint16_t *norm_out = nullptr;
   uint16_t *rnorm_out = nullptr;
   int64_t pos = 0;
-  // caller-owned device scratch (query tables / partial lists)
+  // paged cache (block_table == nullptr: contiguous rows per stream)
+  const int32_t *block_table = nullptr;
+  int page_tokens = 0, max_pages = 0;
+  int64_t pool_rows = 0;
+  // caller-owned device scratch (top-k search: query tables, partial lists)
   void *workspace = nullptr;
   size_t workspace_bytes = 0;
 };
@@ -58,7 +62,6 @@ struct LogitArgs {
 // Shapes the dense logit kernels take (GQA group <= 16, d in {128, 256},
 // 32-bit byte offsets of one stream's codes and logits below 2^31).
 bool logits_supported(int d, int lbits, bool prod, int group, int64_t seq_len);
-size_t logits_workspace_bytes(int d, int lbits, bool prod, int64_t n_streams, int group);
 hipError_t launch_logits(int d, int lbits, bool prod, const LogitArgs &a, hipStream_t s);
 
 struct SearchArgs {

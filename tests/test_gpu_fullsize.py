@@ -128,6 +128,9 @@ def test_config2_decode_full(tq):
             want = oqz.logits_rotated(qq, nref["codes"][h:h + 1], nref["norm"][h:h + 1], otk.pi, otk.c,
                                       oqz.MODE_PROD, scale, rnorm=nref["rnorm"][h:h + 1], s_mat=otk.s)
             check_logits(app[h * group:(h + 1) * group, seq - 1:], want, scale, nref["norm"][h:h + 1], qq)
+    # the same cache as a pool of 256-token pages in a random order: the
+    # logits (and the append into it) equal the contiguous results exactly
+    _check_paged_decode(tq, qk, refk, kb, qb, heads, seq, scale, out, app)
     # dequantized values (bf16, as in the decode step, and fp32) on sampled rows
     ovc = cache_from_oracle(tq, refv, d, bits, oqz.MODE_MSE, DEV)
     rows = _sample_rows(n, 3000, 21)
@@ -143,6 +146,33 @@ def test_config2_decode_full(tq):
     want = oatt.attn_output(out[None].astype(np.float64), ocache, otv.pi, otv.c, oqz.MODE_MSE)
     err = np.linalg.norm(got - want, axis=2)
     assert np.all(err <= 1e-4 * np.linalg.norm(want, axis=2) + 1e-6)
+
+
+def _check_paged_decode(tq, qk, refk, kb, qb, heads, seq, scale, out, app):
+    from oracle import decode as odec
+    page = 256
+    per_seq = seq // page
+    n_pages = per_seq + 16
+    table = np.random.default_rng(77).permutation(n_pages)[:per_seq].reshape(1, per_seq).astype(np.int32)
+    rows = n_pages * heads * page
+    codes = np.zeros((rows, refk["codes"].shape[1]), np.uint8)
+    norm = np.zeros(rows, np.uint16)
+    rnorm = np.zeros(rows, np.uint16)
+    for h in range(heads):
+        r = odec.paged_rows(table, page, heads, 0, h, np.arange(seq))
+        codes[r] = refk["codes"][h * seq:(h + 1) * seq]
+        norm[r] = refk["norm"][h * seq:(h + 1) * seq]
+        rnorm[r] = refk["rnorm"][h * seq:(h + 1) * seq]
+    pool = tq.PackedKV.from_tensors(128, qk.bits, qk.mode, torch.from_numpy(codes).to(DEV),
+                                    torch.from_numpy(norm.view(np.int16)).to(DEV),
+                                    torch.from_numpy(rnorm.view(np.int16)).to(DEV))
+    tt = torch.from_numpy(table).to(DEV)
+    got = qk.attn_logits_paged(_dev_bf16(qb), pool, tt, page, heads, seq, scale).cpu().numpy()[0]
+    assert np.array_equal(got, out)
+    xl = np.ascontiguousarray(kb.reshape(heads, seq, 128)[:, seq - 1])
+    gapp = qk.append_attn_logits_paged(_dev_bf16(xl).reshape(1, heads, 128), _dev_bf16(qb), pool, tt, page, heads,
+                                       seq - 1, scale).cpu().numpy()[0]
+    assert np.array_equal(gapp, app)
 
 
 def test_config2_values_polar_full(tq):

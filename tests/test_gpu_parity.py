@@ -544,3 +544,96 @@ def test_polar_round_trip_and_unsupported_calls(tq):
     q = torch.zeros((1, 4, d), device=DEV)
     with pytest.raises(tq.TQError):
         qz.attn_logits(q, cache, n_kv_heads=1, seq_len=n, scale=1.0)
+
+
+# ---------------------------------------------------------------- paged cache
+PAGED_CASES = [
+    # d, bits, mode, batch, kv heads, group, page tokens, seq, append pos, q dtype
+    (128, 3, "prod", 2, 3, 4, 64, 1000, 777, "bf16"),
+    (128, 4, "prod", 1, 2, 4, 256, 2049, 2048, "f32"),
+    (128, 2, "mse", 2, 2, 2, 128, 700, 300, "bf16"),
+    (256, 2, "mse", 1, 1, 4, 64, 300, 0, "f32"),
+]
+
+
+def _scatter_pool(ref, d, bits, mode, bsz, hkv, seq, page_tokens, spare, seed):
+    """Oracle-packed rows [bsz, hkv, seq] scattered into a pool of pages in a
+    random order; unused rows hold garbage.  Returns (pool dict, table)."""
+    from oracle import decode as odec
+    per_seq = -(-seq // page_tokens)
+    n_pages = bsz * per_seq + spare
+    rng = np.random.default_rng(seed)
+    table = rng.permutation(n_pages)[:bsz * per_seq].reshape(bsz, per_seq).astype(np.int32)
+    rows = n_pages * hkv * page_tokens
+    pool = {"codes": rng.integers(0, 256, (rows, ref["codes"].shape[1])).astype(np.uint8),
+            "norm": rng.integers(0, 0x7C00, rows).astype(np.uint16)}
+    if mode == oqz.MODE_PROD:
+        pool["rnorm"] = rng.integers(0, 0x3C00, rows).astype(np.uint16)
+    for b in range(bsz):
+        for h in range(hkv):
+            r = odec.paged_rows(table, page_tokens, hkv, b, h, np.arange(seq))
+            src = slice((b * hkv + h) * seq, (b * hkv + h + 1) * seq)
+            pool["codes"][r] = ref["codes"][src]
+            pool["norm"][r] = ref["norm"][src]
+            if mode == oqz.MODE_PROD:
+                pool["rnorm"][r] = ref["rnorm"][src]
+    return pool, table
+
+
+@pytest.mark.parametrize("d,bits,mode,bsz,hkv,group,page,seq,pos,qdtype", PAGED_CASES)
+def test_paged_logits_and_append_parity(tq, d, bits, mode, bsz, hkv, group, page, seq, pos, qdtype):
+    """Logits over a paged pool (pages in random order, garbage in unused
+    rows) against the oracle; then a decode step with append into the pool:
+    the new rows follow the quantiser's rules, every other pool row stays
+    bit-identical, and the logits over tokens 0..pos match the oracle's."""
+    from oracle import decode as odec
+    ot, mcode, keys, q64, qt, ref = _gqa_case(d, bits, mode, bsz, hkv, group, seq, qdtype)
+    pool, table = _scatter_pool(ref, d, bits, mcode, bsz, hkv, seq, page, 5, seed=seq)
+    qz = tq.Quantizer(d, bits, mcode, seed=0, device=DEV)
+    cache = tq.PackedKV.from_tensors(d, bits, mcode, torch.from_numpy(pool["codes"]).to(DEV),
+                                     dev_u16(pool["norm"], DEV),
+                                     dev_u16(pool["rnorm"], DEV) if mcode == oqz.MODE_PROD else None)
+    tt = torch.from_numpy(table).to(DEV)
+    scale = 1.0 / np.sqrt(d)
+    out = qz.attn_logits_paged(qt, cache, tt, page, hkv, seq, scale).cpu().numpy()
+    codes = ref["codes"].reshape(bsz, hkv, seq, -1)
+    norm = ref["norm"].reshape(bsz, hkv, seq)
+    for b in range(bsz):
+        for h in range(hkv):
+            kw = {}
+            if mcode == oqz.MODE_PROD:
+                kw = dict(rnorm=ref["rnorm"].reshape(bsz, hkv, seq)[b, h], s_mat=ot.s)
+            qq = q64[b, h * group:(h + 1) * group]
+            want = oqz.logits_rotated(qq, codes[b, h], norm[b, h], ot.pi, ot.c, mcode, scale, **kw)
+            check_logits(out[b, h * group:(h + 1) * group], want, scale, norm[b, h], qq)
+    # decode step with append into the pool
+    rng = np.random.default_rng(pos + 3)
+    x = (rng.standard_normal((bsz, hkv, d)) * 2.0).astype(np.float32)
+    x[0, 0] = 0.0
+    x64 = x.astype(np.float64)
+    new_pool, want, nref = odec.append_step_paged(pool, table, page, x64, pos, q64, ot.pi, ot.c, ot.t, mcode,
+                                                  scale, s_mat=ot.s)
+    got = qz.append_attn_logits_paged(torch.from_numpy(x).to(DEV), qt, cache, tt, page, hkv, pos, scale)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    after = {"codes": cache.codes.cpu().numpy(), "norm": cache.norm.cpu().numpy().view(np.uint16)}
+    if mcode == oqz.MODE_PROD:
+        after["rnorm"] = cache.rnorm.cpu().numpy().view(np.uint16)
+    new_rows = np.array([odec.paged_rows(table, page, hkv, b, h, [pos])[0] for b in range(bsz) for h in range(hkv)])
+    keep = np.ones(len(pool["norm"]), bool)
+    keep[new_rows] = False
+    for name in pool:
+        assert np.array_equal(after[name][keep], pool[name][keep]), name
+    same = check_records(after["codes"][new_rows], after["norm"][new_rows],
+                         after["rnorm"][new_rows] if mcode == oqz.MODE_PROD else None, nref, ot)
+    for b in range(bsz):
+        for h in range(hkv):
+            qq = q64[b, h * group:(h + 1) * group]
+            rows = odec.paged_rows(table, page, hkv, b, h, np.arange(pos + 1))
+            cols = pos + 1 if same[b * hkv + h] else pos
+            nrm = new_pool["norm"][rows][:cols]
+            live = nrm != 0
+            gl = got[b, h * group:(h + 1) * group, :cols]
+            assert np.all(gl[:, ~live] == 0.0)
+            if live.any():
+                check_logits(gl[:, live], want[b, h * group:(h + 1) * group, :cols][:, live], scale, nrm[live], qq)

@@ -156,14 +156,9 @@ def test_workspace_queries_and_checks(tq):
     pp = tq.Params(128, 3, tq.MODE_PROD, 0, dummy, dummy, dummy, dummy, dummy)
     pm = tq.Params(128, 3, tq.MODE_MSE, 0, dummy, None, None, dummy, dummy)
     pk = tq.Packed(dummy, dummy, dummy)
-    # dense logits: query tables of every (batch, kv head) stream, independent of seq_len
-    st, n8 = _size(lib.tq_attn_logits_workspace_size, ctypes.byref(pp), 1, 32, 8, 32768, 0)
-    assert st == tq.TQ_OK and n8 > 0 and n8 % 256 == 0
-    st, n64 = _size(lib.tq_attn_logits_workspace_size, ctypes.byref(pp), 8, 32, 8, 131072, 0)
-    assert st == tq.TQ_OK and n64 >= 8 * n8 - 8 * 256
-    assert _size(lib.tq_attn_logits_workspace_size, ctypes.byref(pp), 1, 32, 8, 5, 0) == (tq.TQ_OK, n8)
-    assert _size(lib.tq_attn_logits_workspace_size, ctypes.byref(pp), 0, 32, 8, 5, 0) == (tq.TQ_OK, 0)
-    assert _size(lib.tq_attn_logits_workspace_size, ctypes.byref(pp), 1, 32, 8, 0, 0) == (tq.TQ_OK, 0)
+    # dense logits build their query tables in LDS: no scratch, at any shape
+    for args in ((1, 32, 8, 32768), (8, 32, 8, 131072), (1, 32, 8, 5), (0, 32, 8, 5), (1, 32, 8, 0)):
+        assert _size(lib.tq_attn_logits_workspace_size, ctypes.byref(pp), *args, 0) == (tq.TQ_OK, 0)
     assert _size(lib.tq_attn_logits_workspace_size, ctypes.byref(pp), 1, 30, 8, 5, 0)[0] == tq.TQ_ERR_INVALID
     assert lib.tq_attn_logits_workspace_size(ctypes.byref(pp), 1, 32, 8, 5, 0, None) == tq.TQ_ERR_INVALID
     # top-k search (MSE only): partial lists grow with the query count
@@ -178,12 +173,10 @@ def test_workspace_queries_and_checks(tq):
     assert _size(lib.tq_attn_output_workspace_size, ctypes.byref(pm), 1, 32, 8, 0) == (tq.TQ_OK, 0)
     assert _size(lib.tq_attn_output_workspace_size, ctypes.byref(pp), 1, 32, 8, 100)[0] == tq.TQ_ERR_UNSUPPORTED
     # the calls: NULL / short workspace -> invalid, misaligned -> unsupported
-    args = (ctypes.byref(pp), dummy, 0, 1, 32, 8, ctypes.byref(pk), 64, 64, f, dummy, 0, None)
-    assert lib.tq_attn_logits(*args, None, 0, None) == tq.TQ_ERR_INVALID
-    assert lib.tq_attn_logits(*args, ctypes.c_void_p(1 << 20), n8 - 1, None) == tq.TQ_ERR_INVALID
-    assert lib.tq_attn_logits(*args, ctypes.c_void_p((1 << 20) + 16), n8, None) == tq.TQ_ERR_UNSUPPORTED
-    app = (ctypes.byref(pp), dummy, 0, dummy, 0, 1, 32, 8, ctypes.byref(pk), 64, 10, f, dummy)
-    assert lib.tq_append_attn_logits(*app, None, 0, None) == tq.TQ_ERR_INVALID
+    sargs = (ctypes.byref(pm), dummy, 0, 1, 1000, 1, ctypes.byref(pk), 100000, 100000, f, dummy, 10, dummy)
+    assert lib.tq_attn_logits(*sargs, None, 0, None) == tq.TQ_ERR_INVALID
+    assert lib.tq_attn_logits(*sargs, ctypes.c_void_p(1 << 20), s1 - 1, None) == tq.TQ_ERR_INVALID
+    assert lib.tq_attn_logits(*sargs, ctypes.c_void_p((1 << 20) + 16), s1, None) == tq.TQ_ERR_UNSUPPORTED
     pv = tq.Packed(ctypes.c_void_p(1 << 20), dummy, None)
     att = (ctypes.byref(pm), dummy, 1, 32, 8, ctypes.byref(pv), 32768, 32768, dummy, 0)
     assert lib.tq_attn_output(*att, None, 0, None) == tq.TQ_ERR_INVALID
@@ -207,8 +200,7 @@ def test_logit_ranges_stay_below_2_31(tq):
         assert lib.tq_attn_logits(ctypes.byref(p), dummy, 0, 1, group, 1, ctypes.byref(pk), limit, limit, f,
                                   dummy, 0, None, ctypes.c_void_p(1 << 20), 1 << 30, None) == tq.TQ_ERR_UNSUPPORTED
         assert lib.tq_append_attn_logits(ctypes.byref(p), dummy, 0, dummy, 0, 1, group, 1, ctypes.byref(pk),
-                                         limit, limit - 1, f, dummy, ctypes.c_void_p(1 << 20), 1 << 30,
-                                         None) == tq.TQ_ERR_UNSUPPORTED
+                                         limit, limit - 1, f, dummy, None) == tq.TQ_ERR_UNSUPPORTED
 
 
 def test_noalloc_entry_validates_before_launch(tq):
@@ -230,3 +222,29 @@ def test_noalloc_entry_validates_before_launch(tq):
     pp = tq.Params(128, 3, tq.MODE_PROD, 0, dummy, dummy, dummy, dummy, dummy)
     assert lib.tq_attn_output_noalloc(ctypes.byref(pp), dummy, 1, 4, 4, ctypes.byref(pv), 256, 256, dummy, 0,
                                       None) == tq.TQ_ERR_UNSUPPORTED
+
+
+def test_paged_calls_validate_before_launch(tq):
+    lib = tq.LIB
+    dummy = ctypes.c_void_p(16)
+    f = ctypes.c_float(1.0)
+    pp = tq.Params(128, 3, tq.MODE_PROD, 0, dummy, dummy, dummy, dummy, dummy)
+    pk = tq.Packed(dummy, dummy, dummy)
+
+    def call(pages, seq_len=1000):
+        return lib.tq_attn_logits_paged(ctypes.byref(pp), dummy, 0, 1, 32, 8, ctypes.byref(pk),
+                                        ctypes.byref(pages) if pages is not None else None, seq_len, f, dummy, None)
+
+    assert call(None) == tq.TQ_ERR_INVALID
+    assert call(tq.Pages(None, 64, 16, 100)) == tq.TQ_ERR_INVALID                  # no table
+    assert call(tq.Pages(dummy, 48, 32, 100)) == tq.TQ_ERR_INVALID                 # page not a multiple of 64
+    assert call(tq.Pages(dummy, 64, 15, 100)) == tq.TQ_ERR_INVALID                 # 1000 tokens > 15 pages of 64
+    assert call(tq.Pages(dummy, 64, 16, 0)) == tq.TQ_ERR_INVALID                   # empty pool
+    assert call(tq.Pages(dummy, 256, 16, 1 << 20)) == tq.TQ_ERR_UNSUPPORTED        # pool codes past 2^31 bytes
+    assert call(tq.Pages(dummy, 64, 16, 100), seq_len=0) == tq.TQ_OK                # empty: no-op
+    app = lib.tq_append_attn_logits_paged
+    pg = tq.Pages(dummy, 64, 16, 100)
+    assert app(ctypes.byref(pp), dummy, 0, dummy, 0, 1, 32, 8, ctypes.byref(pk), ctypes.byref(pg), 1024, f, dummy,
+               None) == tq.TQ_ERR_INVALID                                           # pos 1024: past 16 pages of 64
+    assert app(ctypes.byref(pp), dummy, 0, dummy, 0, 1, 32, 8, ctypes.byref(pk), ctypes.byref(pg), -1, f, dummy,
+               None) == tq.TQ_ERR_INVALID
