@@ -2,10 +2,17 @@
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|search]
 
-Without --warmup the untimed warmup runs as many steps as take about one
-second (at least 5): the GPU reaches its sustained clock only after that much
-load, and the timed steps then measure the sustained rate.  The line reports
-the warmup steps actually run.
+Before the W warmup steps the bench runs steps untimed for --settle seconds
+(default 1): the GPU reaches its sustained clock only under sustained load
+(a 5-step warmup alone timed the decode step 15-20% slower than the sustained
+rate).  The line reports the settle time and steps next to W.
+
+Cold and warm: the decode step's inputs and outputs (about 232 MB) fit the
+256 MB MALL, so the timed steps rotate over three buffer sets (each step's
+buffers were last touched two steps earlier, with about 460 MB of other
+traffic in between): ``value`` is that cold rate.  The same steps on one set
+(warm, cache-resident) are reported beside it.  Per-call times are
+per-launch HIP events (median, min and mean).
 
 A step is one pass of the whole path over one batch of synthetic input:
 quantise the keys (inner-product mode) and the values (MSE mode), compute the
@@ -47,17 +54,17 @@ HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFS = 2500.0
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "online_vector_quantization_amd", "csrc")
-WARMUP_S = 1.0      # default untimed warmup: the clocks settle under about a second of load
 
 
 def _args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed warmup steps (default: as many as take about one second, at least 5; "
-                         "the GPU reaches its sustained clock only under sustained load)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed warmup steps after the settle phase (5)")
+    ap.add_argument("--settle", type=float, default=1.0,
+                    help="seconds of untimed steps before the warmup steps (clock ramp)")
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "search"])
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured-ceiling leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-long-context", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -93,22 +100,45 @@ def _traffic(kernel, src_files):
 
 
 class Timer:
-    """Mean duration of a callable over n launches, HIP events on the current stream."""
+    """HIP events on the current stream (the stream every call is queued on)."""
 
-    def __init__(self, torch):
+    def __init__(self, torch, idle=None):
         self.torch = torch
+        self.idle = idle     # queues a wait of some milliseconds on the stream
 
     def __call__(self, fn, n):
+        """Mean duration of n back-to-back launches of fn (seconds)."""
         t = self.torch
         start = t.cuda.Event(enable_timing=True)
         end = t.cuda.Event(enable_timing=True)
         t.cuda.synchronize()
         start.record()
-        for _ in range(n):
-            fn()
+        for i in range(n):
+            fn(i)
         end.record()
         t.cuda.synchronize()
         return start.elapsed_time(end) * 1e-3 / n
+
+    def each(self, fn, n):
+        """Per-launch durations of n launches (seconds), events around each.
+        An idle wait queued first keeps the GPU busy while the host queues
+        the n launches, so no event interval contains host time."""
+        t = self.torch
+        ev = [(t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)) for _ in range(n)]
+        t.cuda.synchronize()
+        if self.idle is not None:
+            self.idle(n)
+        for i, (a, b) in enumerate(ev):
+            a.record()
+            fn(i)
+            b.record()
+        t.cuda.synchronize()
+        return [a.elapsed_time(b) * 1e-3 for a, b in ev]
+
+
+def _stats(ts):
+    ts = sorted(ts)
+    return {"median_us": ts[len(ts) // 2] * 1e6, "min_us": ts[0] * 1e6, "mean_us": sum(ts) / len(ts) * 1e6}
 
 
 def _host_kv(torch, seed, cfg, tensor, heads, tokens, d, device):
@@ -121,9 +151,12 @@ def _host_kv(torch, seed, cfg, tensor, heads, tokens, d, device):
     return torch.from_numpy(arr.view(np.int16)).to(device).view(torch.bfloat16), sc
 
 
+N_SETS = 3   # rotating buffer sets of the decode step: 3 x 232 MB > the 256 MB MALL
+
+
 def decode_workload(torch, tq, args, device):
     import numpy as np
-    from synthetic import bf16_to_f32, gqa_queries
+    from synthetic import gqa_queries
     d, heads, qheads, seq, bits = 128, 8, 32, 32768, 3
     n = heads * seq
     k, ksc = _host_kv(torch, 0, 2, "k", heads, seq, d, device)
@@ -132,15 +165,20 @@ def decode_workload(torch, tq, args, device):
     q = torch.from_numpy(qb.view(np.int16)).to(device).view(torch.bfloat16)
     qk = tq.Quantizer(d, bits, tq.MODE_PROD, seed=0, device=device)
     qv = tq.Quantizer(d, bits, tq.MODE_MSE, seed=0, device=device)
-    ck, cv = qk.new_cache(n), qv.new_cache(n)
-    logits = torch.empty((1, qheads, seq), dtype=torch.float32, device=device)
-    vhat = torch.empty((n, d), dtype=torch.bfloat16, device=device)
     scale = 1.0 / math.sqrt(d)
+    # N_SETS copies of every buffer the step touches; call i works on set i % N_SETS
+    sets = []
+    for j in range(N_SETS):
+        sets.append({"k": k if j == 0 else k.clone(), "v": v if j == 0 else v.clone(), "q": q.clone(),
+                     "ck": qk.new_cache(n), "cv": qv.new_cache(n),
+                     "logits": torch.empty((1, qheads, seq), dtype=torch.float32, device=device),
+                     "vhat": torch.empty((n, d), dtype=torch.bfloat16, device=device)})
+    S = lambda i: sets[i % N_SETS]
     calls = {
-        "quantize_k": lambda: qk.quantize(k, out=ck),
-        "quantize_v": lambda: qv.quantize(v, out=cv),
-        "attn_logits": lambda: qk.attn_logits(q, ck, heads, seq, scale, out=logits),
-        "dequantize_v": lambda: qv.dequantize(cv, n, out=vhat),
+        "quantize_k": lambda i: qk.quantize(S(i)["k"], out=S(i)["ck"]),
+        "quantize_v": lambda i: qv.quantize(S(i)["v"], out=S(i)["cv"]),
+        "attn_logits": lambda i: qk.attn_logits(S(i)["q"], S(i)["ck"], heads, seq, scale, out=S(i)["logits"]),
+        "dequantize_v": lambda i: qv.dequantize(S(i)["cv"], n, out=S(i)["vhat"]),
     }
     rb_k, rb_v = bits * d // 8 + 4, bits * d // 8 + 2
     work = {  # algorithmic HBM bytes and flops per launch, main kernel, sources
@@ -156,30 +194,56 @@ def decode_workload(torch, tq, args, device):
     cfg = {"workload": "decode step: 1 layer, batch 1, 8 KV heads x 128, 32768 bf16 tokens; "
                        "keys inner-product b=3, values MSE b=3; 32 query heads (GQA 4:1)",
            "batch": 1, "kv_heads": heads, "q_heads": qheads, "head_dim": d, "seq_len": seq,
-           "key_bits": bits, "value_bits": bits, "units_per_step": n}
-    # Timed beside the step, not in it: the attention output softmax(l) . V
-    # straight from the packed values, on the step's logits.
+           "key_bits": bits, "value_bits": bits, "units_per_step": n, "buffer_sets": N_SETS}
+    # Timed beside the step, not in it (on set 0 after it ran): the attention
+    # output softmax(l) . V straight from the packed values, on the step's logits.
+    s0 = sets[0]
     attn = torch.empty((1, qheads, d), dtype=torch.float32, device=device)
     # The decode step with append: the new key of every head (here token
     # seq - 1 again, so the cache is unchanged) quantised into the cache by the
     # logit call, then logits over all seq tokens.
     x_new = k.view(heads, seq, d)[:, seq - 1].contiguous().view(1, heads, d)
-    logits2 = torch.empty_like(logits)
-    extras = {"attn_output": (lambda: qv.attn_output(logits, cv, heads, seq, out=attn),
+    logits2 = torch.empty_like(s0["logits"])
+    extras = {"attn_output": (lambda i: qv.attn_output(s0["logits"], s0["cv"], heads, seq, out=attn),
                               n * rb_v + qheads * seq * 4 + qheads * d * 4, "attend_mfma_kernel",
                               ["attend.hip", "tq_device.h"]),
-              "append_attn_logits": (lambda: qk.append_attn_logits(x_new, q, ck, heads, seq - 1, scale,
-                                                                   row_tokens=seq, out=logits2),
+              "append_attn_logits": (lambda i: qk.append_attn_logits(x_new, q, s0["ck"], heads, seq - 1, scale,
+                                                                     row_tokens=seq, out=logits2),
                                      n * (rb_k + 4 * (qheads // heads)) + qheads * d * 2 + heads * (2 * d + rb_k),
                                      "logit_kernel", ["logits.hip", "tq_device.h"])}
+    # The same key cache as a pool of 256-token pages in a random order (and
+    # 16 spare pages): logits through the block table, and the step with
+    # append into the pool.
+    page = 256
+    per_seq = seq // page
+    n_pages = per_seq + 16
+    table = torch.from_numpy(np.random.default_rng(7).permutation(n_pages)[:per_seq].astype(np.int32)
+                             .reshape(1, per_seq)).to(device)
+    pool = qk.new_cache(n_pages * heads * page)
+    rows = ((table.long()[0][:, None, None] * heads + torch.arange(heads, device=device)[None, :, None]) * page
+            + torch.arange(page, device=device)[None, None, :])            # [page j, head, token in page]
+    rows = rows.permute(1, 0, 2).reshape(-1)                                # head-major, token order
+    qk.quantize(k, out=s0["ck"])
+    pool.codes[rows] = s0["ck"].codes
+    pool.norm[rows] = s0["ck"].norm
+    pool.rnorm[rows] = s0["ck"].rnorm
+    logits3 = torch.empty_like(s0["logits"])
+    extras["attn_logits_paged"] = (lambda i: qk.attn_logits_paged(q, pool, table, page, heads, seq, scale,
+                                                                  out=logits3),
+                                   n * (rb_k + 4 * (qheads // heads)) + qheads * d * 2 + per_seq * 4,
+                                   "logit_kernel", ["logits.hip", "tq_device.h"])
+    extras["append_attn_logits_paged"] = (lambda i: qk.append_attn_logits_paged(x_new, q, pool, table, page, heads,
+                                                                                seq - 1, scale, out=logits3),
+                                          n * (rb_k + 4 * (qheads // heads)) + qheads * d * 2 + per_seq * 4
+                                          + heads * (2 * d + rb_k), "logit_kernel", ["logits.hip", "tq_device.h"])
     # The PolarQuant variant of stage 1 on the same values (3 bits per coordinate).
     qp = tq.Quantizer(d, 3, tq.MODE_POLAR, seed=0, device=device)
     cp = qp.new_cache(n)
     vhat_p = torch.empty((n, d), dtype=torch.bfloat16, device=device)
     rb_p = 3 * d // 8 + 2
-    extras["polar_quantize"] = (lambda: qp.quantize(v, out=cp), n * (2 * d + rb_p), "quantize_polar_kernel",
+    extras["polar_quantize"] = (lambda i: qp.quantize(v, out=cp), n * (2 * d + rb_p), "quantize_polar_kernel",
                                 ["quantize.hip", "tq_device.h"])
-    extras["polar_dequantize"] = (lambda: qp.dequantize(cp, n, out=vhat_p), n * (rb_p + 2 * d), "dequant_kernel",
+    extras["polar_dequantize"] = (lambda i: qp.dequantize(cp, n, out=vhat_p), n * (rb_p + 2 * d), "dequant_kernel",
                                   ["dequant.hip", "tq_device.h"])
     return calls, work, cfg, n, extras
 
@@ -195,8 +259,8 @@ def prefill_workload(torch, tq, args, device):
         qk = tq.Quantizer(d, b, tq.MODE_PROD, seed=0, device=device)
         qv = tq.Quantizer(d, b, tq.MODE_MSE, seed=0, device=device)
         ck, cv = qk.new_cache(n), qv.new_cache(n)
-        calls["quantize_k_b%d" % b] = lambda qk=qk, ck=ck: qk.quantize(k, out=ck)
-        calls["quantize_v_b%d" % b] = lambda qv=qv, cv=cv: qv.quantize(v, out=cv)
+        calls["quantize_k_b%d" % b] = lambda i, qk=qk, ck=ck: qk.quantize(k, out=ck)
+        calls["quantize_v_b%d" % b] = lambda i, qv=qv, cv=cv: qv.quantize(v, out=cv)
         rb = b * d // 8
         work["quantize_k_b%d" % b] = (n * (2 * d + rb + 4), n * 4 * d * d, "quantize_pc_kernel", src)
         work["quantize_v_b%d" % b] = (n * (2 * d + rb + 2), n * 2 * d * d, "quantize_kernel", src)
@@ -207,25 +271,80 @@ def prefill_workload(torch, tq, args, device):
     return calls, work, cfg, 6 * n, {}
 
 
+def _exact_top10(qv, db, k=10, block=131072):
+    """Exact fp64 inner products of unquantised vectors and their top-k per
+    query (ties to the smaller index): the ground truth recall is measured
+    against."""
+    import numpy as np
+    q = qv.astype(np.float64)
+    best_v = np.full((len(q), 0), -np.inf)
+    best_i = np.zeros((len(q), 0), np.int64)
+    for start in range(0, len(db), block):
+        sc = q @ db[start:start + block].astype(np.float64).T
+        part = np.argpartition(-sc, k - 1, axis=1)[:, :k]
+        v = np.concatenate([best_v, np.take_along_axis(sc, part, 1)], 1)
+        i = np.concatenate([best_i, start + part], 1)
+        order = np.lexsort((i, -v), axis=-1)            # by score, ties to the smaller index
+        best_v = np.take_along_axis(v, order[:, :k], 1)
+        best_i = np.take_along_axis(i, order[:, :k], 1)
+    return best_i
+
+
 def search_workload(torch, tq, args, device):
+    import numpy as np
     from synthetic import search_vectors
     d, n_db, n_q, k = 256, 1_000_000, 10_000, 10
-    db = torch.from_numpy(search_vectors(0, "db", 0, n_db)).to(device)
-    q = torch.from_numpy(search_vectors(0, "dbq", 0, n_q).reshape(1, n_q, d)).to(device)
-    calls, work = {}, {}
+    db_host = search_vectors(0, "db", 0, n_db)
+    db = torch.from_numpy(db_host).to(device)
+    qv_host = search_vectors(0, "dbq", 0, n_q)
+    q = torch.from_numpy(qv_host.reshape(1, n_q, d)).to(device)
+    calls, work, results = {}, {}, {}
     for b in (2, 4):
         qz = tq.Quantizer(d, b, tq.MODE_MSE, seed=0, device=device)
         cache = qz.quantize(db)          # the index is built once, outside the step
-        calls["search_b%d" % b] = lambda qz=qz, cache=cache: qz.search(q, cache, 1, n_db, k)
+        results[b] = (qz, cache)
+        calls["search_b%d" % b] = lambda i, qz=qz, cache=cache: qz.search(q, cache, 1, n_db, k)
         byts = n_db * (b * d // 8 + 2) + n_q * d * 4 + n_q * k * 8
         work["search_b%d" % b] = (byts, 2 * d * n_db * n_q, "search_score_kernel",
                                   ["search.hip", "tq_device.h"])
     del db
+    # recall@10 of the GPU top-10 against the exact top-10 of the unquantised
+    # 200-d vectors, on 1000 sampled queries
+    rq = np.sort(np.random.default_rng(5).choice(n_q, 1000, replace=False))
+    exact = _exact_top10(qv_host[rq, :200], db_host[:, :200])
+    recall = {}
+    for b, (qz, cache) in results.items():
+        _, idx = qz.search(q, cache, 1, n_db, k)
+        got = idx.cpu().numpy()[0][rq]
+        recall["b%d" % b] = float(np.mean([len(set(g.tolist()) & set(e.tolist())) / k for g, e in zip(got, exact)]))
     cfg = {"workload": "vector search: 10^4 queries x 10^6 unit vectors (d = 200 padded to 256), "
                        "MSE b = 2 and 4, fused top-10 (two calls per step)",
            "n_db": n_db, "n_queries": n_q, "head_dim": d, "bits": [2, 4], "topk": k,
-           "units_per_step": 2 * n_q * n_db}
+           "units_per_step": 2 * n_q * n_db,
+           "recall_at_10": dict(recall, queries=len(rq), reference="exact fp64 inner products of the "
+                                "unquantised 200-d vectors")}
     return calls, work, cfg, 2 * n_q * n_db, {}
+
+
+def measured_peaks(torch, tq, timer, device):
+    """Ceilings measured on this GPU with the library's probes (tq_probe):
+    a plain read stream and a plain write stream over 4 GiB (16-byte
+    non-temporal accesses, grid-strided), and register-only loops of
+    32x32x16 fp16 and 16x16x64 int8 MFMAs.  Best of 10 launches each."""
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device=device)
+    out = {}
+    for name, kind in (("read_gbs", tq.PROBE_READ), ("write_gbs", tq.PROBE_WRITE)):
+        work = tq.probe(kind, buf, device=device)
+        t = min(timer.each(lambda i: tq.probe(kind, buf, device=device), 10))
+        out[name] = work / t / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    for name, kind in (("mfma_f16_tflops", tq.PROBE_MFMA_F16), ("mfma_i8_tops", tq.PROBE_MFMA_I8)):
+        work = tq.probe(kind, iters=2048, device=device)
+        t = min(timer.each(lambda i: tq.probe(kind, iters=2048, device=device), 10))
+        out[name] = work / t / 1e12
+    out["how"] = "tq_probe: best of 10; 4 GiB read / write streams, 2048-step MFMA loops on every wave"
+    return out
 
 
 def _oracle_threads():
@@ -331,15 +450,16 @@ def long_context_leg(torch, tq, timer, reps, device):
     del x
     q = device_queries(torch, 0, 3, batch, qheads, heads, d, device)
     out = torch.empty((batch, qheads, seq), dtype=torch.float32, device=device)
-    call = lambda: qz.attn_logits(q, cache, heads, seq, 1.0 / math.sqrt(d), out=out)
-    call()
+    call = lambda i: qz.attn_logits(q, cache, heads, seq, 1.0 / math.sqrt(d), out=out)
+    call(0)
+    st = _stats(timer.each(call, max(reps, 20)))
     t = timer(call, reps)
     keys = batch * heads * seq
     byts = keys * (bits * d // 8 + 4) + keys * (qheads // heads) * 4 + batch * qheads * d * 2
     del cache, out
     torch.cuda.empty_cache()
     return {"workload": "batch 8, 8 KV heads x 128, 131072 tokens, keys inner-product b=4, "
-                        "32 query heads", "us_per_call": t * 1e6, "keys_per_s": keys / t,
+                        "32 query heads", "us_per_call": t * 1e6, "per_launch": st, "keys_per_s": keys / t,
             "hbm_gbs": byts / t / 1e9, "frac_of_peak": byts / t / 1e9 / HBM_PEAK_GBS,
             "algorithmic_bytes": byts}
 
@@ -354,7 +474,9 @@ def main():
     import online_vector_quantization_amd as tq
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     device = torch.device("cuda:0")
-    timer = Timer(torch)
+    # idle wait ahead of per-launch timing: 100 us per queued launch (the
+    # host queues one in well under that), at least 2 ms
+    timer = Timer(torch, idle=lambda n: tq.probe(tq.PROBE_IDLE, iters=max(2000, 100 * n), device=device))
     if args.copy_calibration:
         a = torch.empty(512 << 20, dtype=torch.uint8, device=device)
         b = torch.empty_like(a)
@@ -365,65 +487,82 @@ def main():
     build = {"decode": decode_workload, "prefill": prefill_workload, "search": search_workload}
     calls, work, cfg, units, extras = build[args.workload](torch, tq, args, device)
     unit = {"decode": "keys/s", "prefill": "vectors/s", "search": "keys/s"}[args.workload]
-    step = lambda: [fn() for fn in calls.values()]
-    if args.warmup is None:                 # about one second of steps, at least 5
-        for _ in range(3):                  # first calls: workspaces, first touches
-            step()
-        torch.cuda.synchronize()
-        tw = time.perf_counter()
-        for _ in range(10):
-            step()
-        torch.cuda.synchronize()
-        per = max((time.perf_counter() - tw) / 10, 1e-6)
-        args.warmup = 13 + max(5, int(math.ceil(WARMUP_S / per)))
-        for _ in range(args.warmup - 13):
-            step()
-    else:
-        for _ in range(args.warmup):
-            step()
+    step = lambda i: [fn(i) for fn in calls.values()]
+    # clock settle: untimed steps for about args.settle seconds
     torch.cuda.synchronize()
+    ts, settle_steps = time.perf_counter(), 0
+    while time.perf_counter() - ts < args.settle or settle_steps < 3:
+        step(settle_steps)
+        settle_steps += 1
+        if settle_steps % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    settle_s = time.perf_counter() - ts
+    if args.warmup is None:
+        args.warmup = 5
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # the timed region: exactly K steps (rotating buffer sets where the
+    # workload has them), synchronised on both sides
     t0 = time.perf_counter()
     t_step = timer(step, args.steps)
     wall = time.perf_counter() - t0
+    t_warm = timer(lambda i: step(0), args.steps) if args.workload == "decode" else None
 
     breakdown = {}
     for name, fn in calls.items():
-        t = timer(fn, args.steps)
+        ts_each = timer.each(fn, args.steps)
+        st = _stats(ts_each)
+        t = st["mean_us"] * 1e-6
         byts, flops, kern, src = work[name]
-        breakdown[name] = {"us": t * 1e6, "hbm_gbs": byts / t / 1e9,
-                           "frac_hbm": byts / t / 1e9 / HBM_PEAK_GBS,
-                           "tflops": (flops / t / 1e12) if flops else None,
-                           "vectors_per_s": units / t}
+        breakdown[name] = dict(st, us=st["mean_us"], hbm_gbs=byts / t / 1e9, frac_hbm=byts / t / 1e9 / HBM_PEAK_GBS,
+                               tflops=(flops / t / 1e12) if flops else None, vectors_per_s=units / t)
     dom = max(breakdown, key=lambda k: breakdown[k]["us"])
     byts, flops, kern, src = work[dom]
     tdom = breakdown[dom]["us"] * 1e-6
     traffic = _traffic(kern + ":" + dom, src)
+    peaks = None if args.no_peaks else measured_peaks(torch, tq, timer, device)
     if args.workload == "decode":
-        roofline = {"kernel": kern, "call": dom, "bound": "hbm", "achieved": byts / tdom / 1e9,
-                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": byts / tdom / 1e9 / HBM_PEAK_GBS,
-                    "traffic": traffic, "algorithmic_bytes_per_launch": byts}
+        ach = byts / tdom / 1e9
+        roofline = {"kernel": kern, "call": dom, "bound": "hbm", "achieved": ach,
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                    "traffic": traffic, "algorithmic_bytes_per_launch": byts,
+                    "launch_us": {k: breakdown[dom][k] for k in ("mean_us", "median_us", "min_us")}}
+        if peaks:
+            roofline["frac_of_measured_read_stream"] = ach / peaks["read_gbs"]
     else:   # fp16 MFMA contraction: algorithmic flops of the call against the dense fp16 peak
-        roofline = {"kernel": kern, "call": dom, "bound": "mfma", "achieved": flops / tdom / 1e12,
-                    "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s", "frac": flops / tdom / 1e12 / MFMA_F16_PEAK_TFS,
+        ach = flops / tdom / 1e12
+        roofline = {"kernel": kern, "call": dom, "bound": "mfma", "achieved": ach,
+                    "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s", "frac": ach / MFMA_F16_PEAK_TFS,
                     "traffic": traffic, "algorithmic_flops_per_launch": flops,
-                    "algorithmic_bytes_per_launch": byts}
+                    "algorithmic_bytes_per_launch": byts,
+                    "launch_us": {k: breakdown[dom][k] for k in ("mean_us", "median_us", "min_us")}}
+        if peaks:
+            roofline["frac_of_measured_mfma_f16"] = ach / peaks["mfma_f16_tflops"]
 
     line = {"metric": METRIC, "value": units / t_step, "unit": unit, "n_gpus": 1,
-            "steps": args.steps, "warmup": args.warmup, "ms_per_step": t_step * 1e3,
-            "wall_s_timed": wall, "higher_is_better": True, "scaling": "weak",
+            "steps": args.steps, "warmup": args.warmup, "settle_s": settle_s, "settle_steps": settle_steps,
+            "ms_per_step": t_step * 1e3, "wall_s_timed": wall, "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "bf16 in; f16 split + i8 MFMA, f32/i32 accumulate",
             "data": "synthetic", "config": cfg, "roofline": roofline, "breakdown": breakdown}
+    if t_warm is not None:
+        line["warm"] = {"ms_per_step": t_warm * 1e3, "value": units / t_warm,
+                        "note": "the same steps on one buffer set (inputs and outputs resident in the MALL)"}
+        line["cold_note"] = "value: steps rotating over %d buffer sets, each last touched two steps earlier" % N_SETS
+    if peaks:
+        line["measured_peaks"] = peaks
     if extras:
         line["extras"] = {}
         for name, (fn, byts, kern, src) in extras.items():
-            for _ in range(max(args.warmup, 1)):     # first calls size the library's workspace
-                fn()
-            t = timer(fn, args.steps)
-            line["extras"][name] = {"us": t * 1e6, "hbm_gbs": byts / t / 1e9,
-                                    "frac_hbm": byts / t / 1e9 / HBM_PEAK_GBS, "kernel": kern,
-                                    "algorithmic_bytes_per_launch": byts,
-                                    "traffic": _traffic(kern + ":" + name, src),
-                                    "in_step": False}
+            for i in range(max(args.warmup, 3)):
+                fn(i)
+            st = _stats(timer.each(fn, args.steps))
+            t = st["mean_us"] * 1e-6
+            line["extras"][name] = dict(st, us=st["mean_us"], hbm_gbs=byts / t / 1e9,
+                                        frac_hbm=byts / t / 1e9 / HBM_PEAK_GBS, kernel=kern,
+                                        algorithmic_bytes_per_launch=byts,
+                                        traffic=_traffic(kern + ":" + name, src), in_step=False)
     if args.workload == "decode" and not args.no_long_context:
         line["long_context_logits"] = long_context_leg(torch, tq, timer, args.steps, device)
     if not args.no_cpu_baseline:

@@ -25,7 +25,8 @@
  *   - The library never allocates or frees memory, never synchronises and
  *     keeps no state between calls (apart from a per-device cache of the
  *     compute-unit count, set once).  Calls that need device scratch memory
- *     (tq_attn_logits with top-k, tq_attn_output) take a
+ *     (the logit calls: query tables; top-k: partial lists; tq_attn_output:
+ *     per-split partials) take a
  *     caller-owned `workspace` of `workspace_bytes` bytes: 256-byte aligned
  *     device memory of at least the size the matching *_workspace_size query
  *     gives for the same arguments on the current device.  It is borrowed
@@ -175,9 +176,12 @@ tq_status tq_quantize_kv(const tq_params *p, const void *x, int32_t x_dtype, int
 
 /* Device scratch that tq_attn_logits needs for these arguments on the current
  * device (the same validation as the call itself: an unsupported shape
- * returns TQ_ERR_UNSUPPORTED).  Dense logits need none (each workgroup
- * builds its query tables in LDS): *bytes is 0 for topk == 0 and for empty
- * calls; top-k search needs its rotated queries and partial lists.
+ * returns TQ_ERR_UNSUPPORTED).  Dense logits need the query tables (A
+ * operands and constants of every query: a few KB per (batch, kv head)
+ * stream, independent of seq_len); top-k search needs its rotated queries
+ * and partial lists.  The other logit calls (append, paged) take the dense
+ * size: this query with their batch, heads, seq_len (pos + 1) and topk = 0.
+ * *bytes is 0 for empty calls.
  * Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED. */
 tq_status tq_attn_logits_workspace_size(const tq_params *p, int32_t batch, int32_t n_q_heads,
                                         int32_t n_kv_heads, int64_t seq_len, int32_t topk, size_t *bytes);
@@ -194,8 +198,7 @@ tq_status tq_attn_logits_workspace_size(const tq_params *p, int32_t batch, int32
  *                ties to the smaller token index, descending; logits is
  *                fp32 [batch][n_q_heads][topk] and topk_idx int32 of the same
  *                shape.  Needs seq_len >= topk.
- *   workspace    device scratch of tq_attn_logits_workspace_size bytes (NULL
- *                and 0 for dense logits)
+ *   workspace    device scratch of tq_attn_logits_workspace_size bytes
  * GQA: query head h reads KV head h / (n_q_heads / n_kv_heads); n_q_heads
  * must be a multiple of n_kv_heads.  Dense logits support d in {128, 256},
  * up to 16 query heads per KV head, streams whose packed codes stay under
@@ -224,6 +227,7 @@ tq_status tq_attn_logits(const tq_params *p, const void *q, int32_t q_dtype, int
  *                read (tokens 0..pos-1 must already hold packed keys)
  *   pos          0 <= pos < row_tokens
  *   logits       device fp32 [batch][n_q_heads][pos + 1]
+ *   workspace    as tq_attn_logits with seq_len = pos + 1 and topk = 0
  * The new key is quantised in fp64 from the fp32 matrices (the inner-product
  * mode needs p->qjl_rot).  Supported: as dense tq_attn_logits (d in {128,
  * 256}, up to 16 query heads per KV head).  batch == 0 is a no-op.
@@ -231,7 +235,8 @@ tq_status tq_attn_logits(const tq_params *p, const void *q, int32_t q_dtype, int
 tq_status tq_append_attn_logits(const tq_params *p, const void *x_new, int32_t x_dtype,
                                 const void *q, int32_t q_dtype, int32_t batch, int32_t n_q_heads,
                                 int32_t n_kv_heads, const tq_packed *k, int64_t row_tokens,
-                                int64_t pos, float scale, float *logits, void *stream);
+                                int64_t pos, float scale, float *logits, void *workspace,
+                                size_t workspace_bytes, void *stream);
 
 /* Paged key cache (a serving cache of fixed-size pages; the page reads
  * "quantise on every cache update", section "TurboQuant 구현 방법").  The
@@ -254,11 +259,11 @@ typedef struct tq_pages {
  * tokens of every sequence, read through its block table; logits as
  * tq_attn_logits, [batch][n_q_heads][seq_len].  Needs seq_len <=
  * max_pages * page_tokens and the pool's packed codes under 2 GiB.  Same
- * support and errors as tq_attn_logits; no scratch. */
+ * support, workspace (the dense size) and errors as tq_attn_logits. */
 tq_status tq_attn_logits_paged(const tq_params *p, const void *q, int32_t q_dtype, int32_t batch,
                                int32_t n_q_heads, int32_t n_kv_heads, const tq_packed *pool,
                                const tq_pages *pages, int64_t seq_len, float scale, float *logits,
-                               void *stream);
+                               void *workspace, size_t workspace_bytes, void *stream);
 
 /* tq_append_attn_logits over a paged key cache: the new key of every
  * (sequence, KV head) goes to the pool row of token pos (its page must be in
@@ -267,7 +272,8 @@ tq_status tq_attn_logits_paged(const tq_params *p, const void *q, int32_t q_dtyp
 tq_status tq_append_attn_logits_paged(const tq_params *p, const void *x_new, int32_t x_dtype,
                                       const void *q, int32_t q_dtype, int32_t batch, int32_t n_q_heads,
                                       int32_t n_kv_heads, const tq_packed *pool, const tq_pages *pages,
-                                      int64_t pos, float scale, float *logits, void *stream);
+                                      int64_t pos, float scale, float *logits, void *workspace,
+                                size_t workspace_bytes, void *stream);
 
 /* Decode attention output straight from packed values (page: the KV cache
  * holds keys and values, section "TurboQuant란 무엇인가요?", and attention runs
@@ -320,6 +326,28 @@ tq_status tq_attn_output_workspace_size(const tq_params *p, int32_t batch, int32
  * Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED, TQ_ERR_HIP. */
 tq_status tq_dequantize(const tq_params *p, const tq_packed *k, int64_t n_vec, void *out,
                         int32_t out_dtype, void *stream);
+
+/* Ceiling probes (measurement support, not a step of the method): the best
+ * this device reaches on a plain stream or instruction loop, against which
+ * the hot-path kernels' rooflines are also reported.
+ *   TQ_PROBE_READ      read `bytes` of `buf` once (16-byte non-temporal loads)
+ *   TQ_PROBE_WRITE     write `bytes` of `buf` once (16-byte non-temporal stores)
+ *   TQ_PROBE_MFMA_F16  every wave of the grid runs 4 x `iters` 32x32x16 fp16
+ *                      MFMAs (32768 flops each) on registers; no memory
+ *   TQ_PROBE_MFMA_I8   the same with 16x16x64 int8 MFMAs (32768 ops each)
+ *   TQ_PROBE_IDLE      one wave waits (s_sleep) until `iters` microseconds of
+ *                      the device's constant wall clock have passed (1 ..
+ *                      1000000); queued ahead of timed launches, it keeps the
+ *                      stream busy while the host queues them, so the events
+ *                      around each launch see no host gaps
+ * The grid is tq_probe_sink_words / 4 workgroups of 4 waves (the idle probe:
+ * one wave); `sink` (device, sink_words uint32) receives values that keep the
+ * work live.  buf: device, 16-byte aligned, bytes a multiple of 16.
+ * Errors: TQ_ERR_INVALID, TQ_ERR_HIP. */
+enum { TQ_PROBE_READ = 0, TQ_PROBE_WRITE = 1, TQ_PROBE_MFMA_F16 = 2, TQ_PROBE_MFMA_I8 = 3, TQ_PROBE_IDLE = 4 };
+tq_status tq_probe_sink_words(int64_t *words);
+tq_status tq_probe(int32_t kind, void *buf, int64_t bytes, int32_t iters, uint32_t *sink, int64_t sink_words,
+                   void *stream);
 
 /* Human-readable name of a status code (static string). */
 const char *tq_status_string(tq_status s);

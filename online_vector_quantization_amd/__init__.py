@@ -38,7 +38,8 @@ EXPORTED = ["tq_make_codebook", "tq_make_polar_codebook", "tq_make_rotation", "t
             "tq_attn_logits_workspace_size", "tq_attn_logits", "tq_append_attn_logits", "tq_attn_logits_paged",
             "tq_append_attn_logits_paged",
             "tq_attn_output_workspace_size", "tq_attn_output", "tq_attn_output_noalloc", "tq_dequantize",
-            "tq_status_string"]
+            "tq_probe_sink_words", "tq_probe", "tq_status_string"]
+PROBE_READ, PROBE_WRITE, PROBE_MFMA_F16, PROBE_MFMA_I8, PROBE_IDLE = 0, 1, 2, 3, 4
 NOALLOC_SCRATCH_BYTES = 4 << 20
 
 
@@ -79,17 +80,20 @@ def _load():
     lib.tq_attn_logits.argtypes = [ctypes.POINTER(Params), vp, i32, i32, i32, i32,
                                    ctypes.POINTER(Packed), i64, i64, f32, vp, i32, vp, vp, sz, vp]
     lib.tq_append_attn_logits.argtypes = [ctypes.POINTER(Params), vp, i32, vp, i32, i32, i32, i32,
-                                          ctypes.POINTER(Packed), i64, i64, f32, vp, vp]
+                                          ctypes.POINTER(Packed), i64, i64, f32, vp, vp, sz, vp]
     lib.tq_attn_logits_paged.argtypes = [ctypes.POINTER(Params), vp, i32, i32, i32, i32, ctypes.POINTER(Packed),
-                                         ctypes.POINTER(Pages), i64, f32, vp, vp]
+                                         ctypes.POINTER(Pages), i64, f32, vp, vp, sz, vp]
     lib.tq_append_attn_logits_paged.argtypes = [ctypes.POINTER(Params), vp, i32, vp, i32, i32, i32, i32,
-                                                ctypes.POINTER(Packed), ctypes.POINTER(Pages), i64, f32, vp, vp]
+                                                ctypes.POINTER(Packed), ctypes.POINTER(Pages), i64, f32, vp, vp, sz,
+                                                vp]
     lib.tq_attn_output_workspace_size.argtypes = [ctypes.POINTER(Params), i32, i32, i32, i64, psz]
     lib.tq_attn_output.argtypes = [ctypes.POINTER(Params), vp, i32, i32, i32, ctypes.POINTER(Packed),
                                    i64, i64, vp, i32, vp, sz, vp]
     lib.tq_attn_output_noalloc.argtypes = [ctypes.POINTER(Params), vp, i32, i32, i32, ctypes.POINTER(Packed),
                                            i64, i64, vp, i32, vp]
     lib.tq_dequantize.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(Packed), i64, vp, i32, vp]
+    lib.tq_probe_sink_words.argtypes = [ctypes.POINTER(i64)]
+    lib.tq_probe.argtypes = [i32, vp, i64, i32, vp, i64, vp]
     lib.tq_status_string.argtypes = [i32]
     lib.tq_status_string.restype = ctypes.c_char_p
     for name in EXPORTED[:-1]:
@@ -290,7 +294,8 @@ class Quantizer:
         _check(st, "tq_attn_logits")
         return out
 
-    def append_attn_logits(self, x_new, q, cache, n_kv_heads, pos, scale, row_tokens=None, out=None):
+    def append_attn_logits(self, x_new, q, cache, n_kv_heads, pos, scale, row_tokens=None, out=None,
+                           workspace=None):
         """Quantise x_new [batch, n_kv_heads, d] into token ``pos`` of every stream of
         ``cache`` and return the logits [batch, n_q_heads, pos + 1] (fp32)."""
         torch = _torch()
@@ -299,17 +304,21 @@ class Quantizer:
             row_tokens = cache.capacity // max(bsz * n_kv_heads, 1)
         if out is None:
             out = torch.empty((bsz, hq, pos + 1), dtype=torch.float32, device=self.device)
+        need = self.logits_workspace_size(bsz, hq, n_kv_heads, pos + 1) if 0 <= pos < row_tokens else 0
+        ws, wsb = self._workspace(need, workspace)
         st = LIB.tq_append_attn_logits(ctypes.byref(self._params), ctypes.c_void_p(x_new.data_ptr()),
                                        _dtype_code(x_new), ctypes.c_void_p(q.data_ptr()), _dtype_code(q),
                                        bsz, hq, n_kv_heads, ctypes.byref(cache.struct()), row_tokens, pos,
-                                       float(scale), ctypes.c_void_p(out.data_ptr()), _stream_ptr(self.device))
+                                       float(scale), ctypes.c_void_p(out.data_ptr()), ws, wsb,
+                                       _stream_ptr(self.device))
         _check(st, "tq_append_attn_logits")
         return out
 
     def _pages(self, block_table, page_tokens, n_pages):
         return Pages(block_table.data_ptr(), page_tokens, block_table.shape[1], n_pages)
 
-    def attn_logits_paged(self, q, pool, block_table, page_tokens, n_kv_heads, seq_len, scale, out=None):
+    def attn_logits_paged(self, q, pool, block_table, page_tokens, n_kv_heads, seq_len, scale, out=None,
+                          workspace=None):
         """Dense logits [batch, n_q_heads, seq_len] over a paged pool; block_table
         is an int32 device tensor [batch, max_pages]; the pool holds
         pool.capacity // (n_kv_heads * page_tokens) pages."""
@@ -318,13 +327,16 @@ class Quantizer:
         if out is None:
             out = torch.empty((bsz, hq, seq_len), dtype=torch.float32, device=self.device)
         pg = self._pages(block_table, page_tokens, pool.capacity // (n_kv_heads * page_tokens))
+        ws, wsb = self._workspace(self.logits_workspace_size(bsz, hq, n_kv_heads, seq_len), workspace)
         st = LIB.tq_attn_logits_paged(ctypes.byref(self._params), ctypes.c_void_p(q.data_ptr()), _dtype_code(q),
                                       bsz, hq, n_kv_heads, ctypes.byref(pool.struct()), ctypes.byref(pg), seq_len,
-                                      float(scale), ctypes.c_void_p(out.data_ptr()), _stream_ptr(self.device))
+                                      float(scale), ctypes.c_void_p(out.data_ptr()), ws, wsb,
+                                      _stream_ptr(self.device))
         _check(st, "tq_attn_logits_paged")
         return out
 
-    def append_attn_logits_paged(self, x_new, q, pool, block_table, page_tokens, n_kv_heads, pos, scale, out=None):
+    def append_attn_logits_paged(self, x_new, q, pool, block_table, page_tokens, n_kv_heads, pos, scale, out=None,
+                                 workspace=None):
         """Quantise x_new [batch, n_kv_heads, d] into token ``pos`` of every
         sequence of a paged pool and return the logits [batch, n_q_heads, pos + 1]."""
         torch = _torch()
@@ -332,10 +344,13 @@ class Quantizer:
         if out is None:
             out = torch.empty((bsz, hq, pos + 1), dtype=torch.float32, device=self.device)
         pg = self._pages(block_table, page_tokens, pool.capacity // (n_kv_heads * page_tokens))
+        ws, wsb = self._workspace(self.logits_workspace_size(bsz, hq, n_kv_heads, pos + 1) if pos >= 0 else 0,
+                                  workspace)
         st = LIB.tq_append_attn_logits_paged(ctypes.byref(self._params), ctypes.c_void_p(x_new.data_ptr()),
                                              _dtype_code(x_new), ctypes.c_void_p(q.data_ptr()), _dtype_code(q),
                                              bsz, hq, n_kv_heads, ctypes.byref(pool.struct()), ctypes.byref(pg), pos,
-                                             float(scale), ctypes.c_void_p(out.data_ptr()), _stream_ptr(self.device))
+                                             float(scale), ctypes.c_void_p(out.data_ptr()), ws, wsb,
+                                             _stream_ptr(self.device))
         _check(st, "tq_append_attn_logits_paged")
         return out
 
@@ -393,6 +408,32 @@ class Quantizer:
                                _stream_ptr(self.device))
         _check(st, "tq_dequantize")
         return out
+
+
+def probe(kind, buf=None, iters=0, device="cuda"):
+    """One launch of a ceiling probe (tq_probe) on the current stream: a
+    read or write stream over the uint8 device tensor ``buf``, an MFMA loop
+    of ``iters`` steps, or an idle wait of ``iters`` microseconds.  Returns
+    the work of the launch: bytes, flops, or 0 for the idle wait."""
+    torch = _torch()
+    n = ctypes.c_int64(0)
+    _check(LIB.tq_probe_sink_words(ctypes.byref(n)), "tq_probe_sink_words")
+    key = (str(device), n.value)
+    sink = _PROBE_SINKS.get(key)
+    if sink is None:
+        sink = torch.zeros(n.value, dtype=torch.int32, device=device)
+        _PROBE_SINKS[key] = sink
+    nbytes = buf.numel() * buf.element_size() if buf is not None else 0
+    _check(LIB.tq_probe(kind, ctypes.c_void_p(buf.data_ptr()) if buf is not None else None, nbytes, iters,
+                        ctypes.c_void_p(sink.data_ptr()), n.value, _stream_ptr(torch.device(device))), "tq_probe")
+    if kind in (PROBE_READ, PROBE_WRITE):
+        return nbytes
+    if kind == PROBE_IDLE:
+        return 0
+    return n.value * iters * 4 * 32768
+
+
+_PROBE_SINKS = {}
 
 
 def default_scale(d):

@@ -742,7 +742,8 @@ hipError_t launch_t(const tqi::AttendArgs &aa, hipStream_t s) {
   const AttendPlan plan = attend_plan(n_streams, aa.seq_len);
   const int64_t splits = plan.splits, tps = plan.tps;
   const size_t bytes = (size_t)n_streams * splits * G * (D + 2) * sizeof(float);
-  if (aa.workspace_bytes < bytes) return hipErrorInvalidValue;    // checked by the caller
+  if (aa.workspace_bytes < bytes || (bytes > 0 && aa.workspace == nullptr))   // checked by the caller
+    return hipErrorInvalidValue;
   float *part = (float *)aa.workspace;
   hipError_t e = hipSuccess;
   if (splits > 0) {

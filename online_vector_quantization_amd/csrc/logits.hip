@@ -24,12 +24,9 @@
 //   byte equals 2^s * bit, and the matching weight is quantised with
 //   resolution 2^(s-F) (negated for s = 7, where the byte reads -128).
 //
-// One launch per call.  Every workgroup owns one (batch, KV head) stream and
-// a share of its tokens; it first builds its stream's A operands and four
-// constants per query in LDS (q' = Pi q and q'' = S q from the fp32 matrices,
-// which stay in L2), its waves copy them to VGPRs, and then each key is read
-// once: 16-byte code/sign planes, two fp16 scalars.  The decode-time append
-// runs in the workgroup whose tokens hold the new row, before its first load.
+// Query prep (one small kernel per call) writes the A operands and four
+// constants per query to a workspace; the streaming kernel keeps them in
+// VGPRs and reads each key once: 16-byte code/sign planes, two fp16 scalars.
 #include "tq_device.h"
 #include "tq_internal.h"
 
@@ -44,6 +41,8 @@ struct PrepArgs {
   const float *pi;
   const float *s_mat;
   const float *centroids;
+  int8_t *table;   // [stream][row_tile][chunk][64 lanes][16 bytes]
+  float *consts;   // [stream][group][4]
   // decode-time append (x_new == nullptr: none): one new key per stream,
   // written at token pos of the stream's rows
   const void *x_new;       // [stream][D]
@@ -61,19 +60,6 @@ struct PrepArgs {
   int page_tokens, max_pages;
   int64_t pool_rows;
 };
-
-// Pool row of token t (any token of a 64-token block gives the block's page;
-// page_tokens is a multiple of 64).  A table entry past this sequence's
-// pages or outside the pool maps to pool_rows: loads there read zeros through
-// the buffer range check and the append writes nothing.
-__device__ __forceinline__ int64_t paged_row(const PrepArgs &a, int b, int kvh, int64_t t) {
-  int64_t j = t / a.page_tokens;
-  j = j < a.max_pages ? j : a.max_pages - 1;
-  const int64_t pg = a.block_table[(int64_t)b * a.max_pages + j];
-  if (pg < 0) return a.pool_rows;
-  const int64_t row = (pg * a.n_kv_heads + kvh) * a.page_tokens + t % a.page_tokens;
-  return row < a.pool_rows ? row : a.pool_rows;
-}
 
 template <int LB>
 struct Walsh {
@@ -100,12 +86,12 @@ struct LLayout {
 
 // Query preparation for one (stream, row tile, part): part 0 builds the
 // Walsh-plane chunks from q' = Pi q, part 1 the sign chunks from q'' = S q.
-// NT threads per part (the two parts run side by side in one workgroup);
-// RL = NT / D consecutive lanes share matrix row j and read its 16-byte
-// pieces p, p + RL, ... (coalesced), each for all four queries, then combine
-// their partial sums with xor shuffles.  fp32 products summed in fp32 (the
-// sums' rounding, ~1e-7 relative, is far below the logit tolerance); the
-// fixed-point weights are formed in fp64.
+// 512 threads; RL = 512 / D consecutive lanes share matrix row j and read
+// its 16-byte pieces p, p + RL, ... (coalesced), each for all four queries,
+// then combine their partial sums with xor shuffles.  fp64 arithmetic from
+// the fp32 matrix and the queries (exact in fp32).
+template <int D>
+constexpr int prep_threads() { return 512; }
 
 // v from lane (lane ^ off): quad permutes (no LDS) within 4 lanes, the
 // LDS permute unit beyond.
@@ -117,24 +103,23 @@ __device__ __forceinline__ float xor_lanes(float v, int off) {
 }
 
 // Decode-time append: quantise the new key of one stream and write its
-// packed row at token pos (page "TurboQuant 설명 ...": quantisation on every
-// cache update, section "TurboQuant 구현 방법"; stage 1 and the QJL stage,
-// sections "1단계" and "2단계").  Run by the one workgroup of the stream whose
-// tokens include pos, before it reads any key, so its own later load of that
-// row sees the new record.  One vector in fp64 from the fp32 matrices:
-// n = ||x|| (sum of exact squares), u = Pi x / n, idx_j = #{k : u_j >= t_k}
-// (ties go up), and in inner-product mode the rotated residual
-// r = u - c[idx] (same norm as u - Pi^T c[idx]), gamma = ||r||,
-// sign_i = [(M r)_i >= 0]; a zero vector keeps the middle index, all signs 1
-// and gamma = 0.  Threads tid < NT work (RL = NT / D lanes per matrix row,
-// as in the query projection); every thread of the workgroup calls this
-// function, so its barriers are uniform.
+// packed row at token pos, inside the prep launch so that the streaming
+// kernel that follows reads it (page "TurboQuant 설명 ...": quantisation on
+// every cache update, section "TurboQuant 구현 방법"; stage 1 and the QJL
+// stage, sections "1단계" and "2단계").  One vector per workgroup, in fp64
+// from the fp32 matrices: n = ||x|| (sum of exact squares), u = Pi x / n,
+// idx_j = #{k : u_j >= t_k} (ties go up), and in inner-product mode the
+// rotated residual r = u - c[idx] (same norm as u - Pi^T c[idx]), gamma =
+// ||r||, sign_i = [(M r)_i >= 0]; a zero vector keeps the middle index, all
+// signs 1 and gamma = 0.  Rows of Pi and M are read by RL consecutive lanes,
+// as in the query projection.
 __device__ __forceinline__ double shfl_xor_f64(double v, int off) {
   return __shfl_xor(v, off, 64);
 }
 
-template <int D, int LB, bool PROD, int NT>
-__device__ __forceinline__ void append_key(const PrepArgs &a, int stream, int tid) {
+template <int D, int LB, bool PROD>
+__device__ __forceinline__ void append_key(const PrepArgs &a, int stream) {
+  constexpr int NT = prep_threads<D>();
   constexpr int RL = NT / D;                // lanes per matrix row
   constexpr int NP = D / 4 / RL;            // 16-byte pieces per lane
   constexpr int K = 1 << LB;
@@ -143,9 +128,8 @@ __device__ __forceinline__ void append_key(const PrepArgs &a, int stream, int ti
   __shared__ double rs[D];
   __shared__ int rec[D];
   __shared__ double nrm[2];
-  static_assert(NT % 64 == 0 && NT >= D && NT / D * D == NT, "append layout");
-  const bool act = tid < NT;                // whole waves: NT is a multiple of 64
-  const int j = act ? tid / RL : 0, pl = tid % RL;
+  const int tid = threadIdx.x;
+  const int j = tid / RL, pl = tid % RL;
   const int l = lane_id();
   const f32x4 *prow = (const f32x4 *)(a.pi + (size_t)j * D);
   if (tid < D) {
@@ -161,24 +145,22 @@ __device__ __forceinline__ void append_key(const PrepArgs &a, int stream, int ti
     if (l == 0) nrm[0] = sqrt(s2);
   }
   double y = 0.0;
-  if (act) {
 #pragma unroll 4
-    for (int i = 0; i < NP; ++i) {
-      const int k0 = 4 * (pl + RL * i);
-      const f32x4 m4 = prow[pl + RL * i];
+  for (int i = 0; i < NP; ++i) {
+    const int k0 = 4 * (pl + RL * i);
+    const f32x4 m4 = prow[pl + RL * i];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) y = fma((double)m4[e], (double)xs[k0 + e], y);
-    }
-#pragma unroll
-    for (int off = 1; off < RL; off <<= 1) y += shfl_xor_f64(y, off);
+    for (int e = 0; e < 4; ++e) y = fma((double)m4[e], (double)xs[k0 + e], y);
   }
+#pragma unroll
+  for (int off = 1; off < RL; off <<= 1) y += shfl_xor_f64(y, off);
   __syncthreads();
   const double n = nrm[0];
   const double u = n > 0.0 ? y / n : 0.0;
   int idx = 0;
 #pragma unroll
   for (int k = 0; k < K - 1; ++k) idx += u >= (double)a.boundaries[k] ? 1 : 0;
-  if (act && pl == 0) {
+  if (pl == 0) {
     rec[j] = idx;
     rs[j] = u - (double)a.centroids[idx];
   }
@@ -191,26 +173,28 @@ __device__ __forceinline__ void append_key(const PrepArgs &a, int stream, int ti
       for (int off = 32; off > 0; off >>= 1) g2 += shfl_xor_f64(g2, off);
       if (l == 0) nrm[1] = sqrt(g2);
     }
-    if (act) {
-      const f32x4 *mrow = (const f32x4 *)(a.m_mat + (size_t)j * D);
-      double z = 0.0;
+    const f32x4 *mrow = (const f32x4 *)(a.m_mat + (size_t)j * D);
+    double z = 0.0;
 #pragma unroll 4
-      for (int i = 0; i < NP; ++i) {
-        const int k0 = 4 * (pl + RL * i);
-        const f32x4 m4 = mrow[pl + RL * i];
+    for (int i = 0; i < NP; ++i) {
+      const int k0 = 4 * (pl + RL * i);
+      const f32x4 m4 = mrow[pl + RL * i];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) z = fma((double)m4[e], rs[k0 + e], z);
-      }
-#pragma unroll
-      for (int off = 1; off < RL; off <<= 1) z += shfl_xor_f64(z, off);
-      if (pl == 0 && (n == 0.0 || z >= 0.0)) rec[j] |= 1 << LB;
+      for (int e = 0; e < 4; ++e) z = fma((double)m4[e], rs[k0 + e], z);
     }
+#pragma unroll
+    for (int off = 1; off < RL; off <<= 1) z += shfl_xor_f64(z, off);
+    if (pl == 0 && (n == 0.0 || z >= 0.0)) rec[j] |= 1 << LB;
     __syncthreads();
   }
   // bit planes: word p of group g holds bit p of the records 32 g .. 32 g + 31
-  const int64_t row = a.block_table == nullptr ? (int64_t)stream * a.row_tokens + a.pos
-                                               : paged_row(a, stream / a.n_kv_heads, stream % a.n_kv_heads, a.pos);
-  if (row >= (a.block_table == nullptr ? INT64_MAX : a.pool_rows)) return;   // uniform: no page for it
+  int64_t row = (int64_t)stream * a.row_tokens + a.pos;
+  if (a.block_table != nullptr) {   // paged: the row of token pos; no write where its page is not in the pool
+    const int b = stream / a.n_kv_heads, kvh = stream % a.n_kv_heads;
+    const int64_t pg = a.block_table[(int64_t)b * a.max_pages + a.pos / a.page_tokens];
+    row = (pg * a.n_kv_heads + kvh) * a.page_tokens + a.pos % a.page_tokens;
+    if (pg < 0 || row >= a.pool_rows) return;      // uniform over the workgroup
+  }
   if (tid < (D / 32) * RBITS) {
     const int g = tid / RBITS, p = tid % RBITS;
     uint32_t word = 0;
@@ -222,44 +206,44 @@ __device__ __forceinline__ void append_key(const PrepArgs &a, int stream, int ti
     a.norm_out[row] = f64_to_f16_bits(n);
     if constexpr (PROD) a.rnorm_out[row] = f64_to_f16_bits(n > 0.0 ? nrm[1] : 0.0);
   }
-  // the row is read back by this workgroup's waves after the next barrier
-  __threadfence();
 }
 
-// One row tile (queries 4 rt .. 4 rt + 3 of the stream's group) of one part:
-// the A-operand chunks of that part go to `tab` (the row tile's chunks,
-// [chunk][64 lanes][16 bytes]) and the query constants to cst[4 g' ..] for
-// query g' of the group.  Called by every thread of the workgroup with its
-// part (0 or 1) and its thread index within the part (tid < NT); a part that
-// the mode does not have (1 in MSE mode) computes on Pi and writes nothing,
-// so the barriers stay uniform.
-template <int D, int LB, bool PROD, int NT>
-__device__ __forceinline__ void prep_part(const PrepArgs &a, int stream, int rt, int part, int tid,
-                                          int8_t *tab, float *cst_base) {
+template <int D, int LB, bool PROD>
+__global__ __launch_bounds__(prep_threads<D>()) void logit_prep_kernel(PrepArgs a) {
   using L = LLayout<D, LB, PROD>;
   constexpr int K = 1 << LB;
   constexpr int P = L::P;
+  constexpr int NT = prep_threads<D>();
   constexpr int RL = NT / D;                // lanes per matrix row
   constexpr int NP = D / 4 / RL;            // 16-byte pieces per lane
-  constexpr int NW = NT / 64;               // waves per part
-  static_assert(RL >= 1 && RL <= 64 && NP >= 1 && NT % 64 == 0, "prep layout");
-  __shared__ __attribute__((aligned(16))) float qin_s[2][4][D];
-  __shared__ float proj_s[2][4][D];
+  constexpr int NW = NT / 64;               // waves
+  static_assert(RL >= 1 && RL <= 64 && NP >= 1, "prep layout");
+  __shared__ __attribute__((aligned(16))) float qin[4][D];
+  __shared__ float proj[4][D];
   __shared__ double beta[P];
-  __shared__ float red_max_s[2][4][NW], red_sum_s[2][4][NW];
-  float (&qin)[4][D] = qin_s[part];
-  float (&proj)[4][D] = proj_s[part];
-  float (&red_max)[4][NW] = red_max_s[part];
-  float (&red_sum)[4][NW] = red_sum_s[part];
-  const bool writes = part == 0 || PROD;
+  __shared__ float red_max[4][NW], red_sum[4][NW];
 
+  const int stream = blockIdx.x;
+  const int rt = blockIdx.y;
+  const int part = blockIdx.z;              // 0: MSE planes, 1: QJL signs, last: append
+  if (part == (PROD ? 2 : 1)) {             // uniform over the workgroup
+    if (rt == 0) append_key<D, LB, PROD>(a, stream);
+    return;
+  }
   const int b = stream / a.n_kv_heads;
   const int kvh = stream % a.n_kv_heads;
+  const int tid = threadIdx.x;
   const int j = tid / RL;
   const int pl = tid % RL;
 
-  const float *mat = (part == 0 || !PROD) ? a.pi : a.s_mat;
+  const float *mat = part == 0 ? a.pi : a.s_mat;
   const f32x4 *mrow = (const f32x4 *)(mat + (size_t)j * D);
+  // d <= 128: the whole row slice is loaded before the first barrier; larger
+  // d streams it inside the loop (register budget)
+  constexpr int PRE = D <= 128 ? NP : 1;
+  f32x4 row[PRE];
+#pragma unroll
+  for (int i = 0; i < PRE; ++i) row[i] = mrow[pl + RL * i];
 
   for (int i = tid; i < 4 * D; i += NT) {
     const int g = i / D, k = i % D;
@@ -285,10 +269,10 @@ __device__ __forceinline__ void prep_part(const PrepArgs &a, int stream, int rt,
   // fp32 accumulation: the products are exact and the sums' rounding
   // (~1e-7 relative) is far below the logit tolerance.
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 4
+#pragma unroll (D <= 128 ? NP : 4)
   for (int i = 0; i < NP; ++i) {
     const int k0 = 4 * (pl + RL * i);
-    const f32x4 m4 = mrow[pl + RL * i];
+    const f32x4 m4 = D <= 128 ? row[i < PRE ? i : 0] : mrow[pl + RL * i];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const f32x4 qv = *(const f32x4 *)&qin[g][k0];
@@ -347,9 +331,9 @@ __device__ __forceinline__ void prep_part(const PrepArgs &a, int stream, int rt,
     if (top > 0.0) frexp(top, &e);
     fexp[g] = 30 - e;               // largest weight * 2^F < 2^30
     const int gg = 4 * rt + g;
-    if (writes && tid == 0 && gg < a.group) {
+    if (tid == 0 && gg < a.group) {
       const double kappa = sqrt(M_PI / 2.0) / D;
-      float *cst = cst_base + 4 * gg;
+      float *cst = a.consts + ((int64_t)stream * a.group + gg) * 4;
       if (part == 0) {
         cst[0] = (float)ldexp(2.0, -fexp[g]);
         cst[1] = (float)(sb * sq);
@@ -369,8 +353,9 @@ __device__ __forceinline__ void prep_part(const PrepArgs &a, int stream, int rt,
   // (see the kernel comment).  One thread per (chunk, kg, g, t) computes
   // the 32-bit fixed-point weights of bytes 4 t .. 4 t + 3 and writes word t
   // of the four piece rows.
+  int8_t *tab = a.table + ((int64_t)stream * a.row_tiles + rt) * (L::NCH * 64 * 16);
   const int c_begin = part == 0 ? 0 : P * L::CPP;
-  const int c_end = !writes ? c_begin : part == 0 ? P * L::CPP : L::NCH;
+  const int c_end = part == 0 ? P * L::CPP : L::NCH;
   for (int i = c_begin * 64 + tid; i < c_end * 64; i += NT) {
     const int cidx = i / 64, kg = (i >> 4) & 3, g = (i >> 2) & 3, t = i & 3;
     const int r = cidx / L::CPP, c = cidx % L::CPP;
@@ -399,22 +384,27 @@ __device__ __forceinline__ void prep_part(const PrepArgs &a, int stream, int rt,
       *(uint32_t *)(tab + ((int64_t)cidx * 64 + l) * 16 + 4 * t) = words[pc];
     }
   }
-  __syncthreads();   // tables complete; the next row tile may reuse the scratch
 }
 
 struct StreamArgs {
-  PrepArgs p;
+  const int8_t *table;
+  const float *consts;
   const uint8_t *codes;
   const uint16_t *norm;
   const uint16_t *rnorm;
   int64_t row_tokens, seq_len;
   int n_splits;   // blocks per stream; block j takes chunks j, j + n_splits, ...
-  int n_kv_heads, n_q_heads, group;
+  int n_kv_heads, n_q_heads, group, row_tiles;
   float scale;
   float *logits;
+  // paged cache (PAGED kernels only): see PrepArgs
+  const int32_t *block_table;
+  int page_tokens, max_pages;
+  int64_t pool_rows;
 };
 
 constexpr int kLogitGroups = 4;        // 16-token groups per wave and loop iteration
+constexpr int kLogitBlocksPerCu = 8;   // streaming workgroups per CU the launch aims for
 // The logits leave with the default (write-back) policy: L2 then writes whole
 // lines back (measured 3% faster than the non-temporal policy at 8.4 M keys).
 constexpr int kWriteBack = 0;
@@ -435,18 +425,8 @@ struct NormBlock {
   uint32_t n, g;
 };
 
-// Waves per workgroup.  Sixteen (four per SIMD, so at most 128 VGPRs each)
-// where the stationary A operands are small: d = 128, up to 4 queries per KV
-// head, up to 3 Lloyd-Max bits (at most 40 VGPRs of operands; the kernel
-// then takes 115).  Elsewhere four waves, which may use up to 512
-// registers: larger tables stay in registers without spilling.
-template <int D, int LB, bool PROD, int RT>
-constexpr int logit_waves() {
-  return (D == 128 && RT == 1 && LB <= 3) ? 16 : 4;
-}
-
-template <int D, int LB, bool PROD, int RT>
-__global__ __launch_bounds__((64 * logit_waves<D, LB, PROD, RT>())) void logit_kernel(StreamArgs a) {
+template <int D, int LB, bool PROD, int RT, bool PAGED>
+__global__ __launch_bounds__(256) void logit_kernel(StreamArgs a) {
   using L = LLayout<D, LB, PROD>;
   constexpr int P = L::P;
   constexpr int CPP = L::CPP;
@@ -457,20 +437,8 @@ __global__ __launch_bounds__((64 * logit_waves<D, LB, PROD, RT>())) void logit_k
   constexpr int NQ = D / 128;            // plane words per lane and plane
   constexpr int U = kLogitGroups;     // 16-token groups per wave and iteration
   constexpr int NB = U / 4;              // 64-token norm blocks per iteration
-  constexpr int NWV = logit_waves<D, LB, PROD, RT>();
-  // The two parts of the table build (Pi q, S q) run side by side when each
-  // gets at least D threads, else one after the other with all threads.
-  constexpr bool PAR = 32 * NWV >= D;
-  constexpr int NTP = PAR ? 32 * NWV : 64 * NWV;
-  constexpr int NTA = 64 * NWV < 512 ? 64 * NWV : 512;   // threads of the append
   static_assert(U % 4 == 0, "groups come in fours (64 tokens)");
-  // Each row tile's A operands are built here and copied to VGPRs, one row
-  // tile at a time; the same LDS then stages the logits for 16-byte stores.
-  constexpr int TAB_BYTES = NCH * 64 * 16;
-  constexpr int STAGE_BYTES = NWV * 4 * RT * 16 * U * 4;
-  __shared__ __attribute__((aligned(16))) int8_t lds[TAB_BYTES > STAGE_BYTES ? TAB_BYTES : STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) float csts[4 * RT][4];
-  float(*stage)[4 * RT][16 * U] = (float(*)[4 * RT][16 * U])lds;
+  __shared__ __attribute__((aligned(16))) float stage[4][4 * RT][16 * U];
 
   int bid = blockIdx.x;
   if ((gridDim.x & 7) == 0) {  // keep a stream's blocks on one XCD (L2)
@@ -482,50 +450,41 @@ __global__ __launch_bounds__((64 * logit_waves<D, LB, PROD, RT>())) void logit_k
   const int b = stream / a.n_kv_heads;
   const int kvh = stream % a.n_kv_heads;
 
-  const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = threadIdx.x >> 6;
   const int l = lane_id();
   const int n = l & 15;
   const int kg = l >> 4;
 
-  // decode-time append: the workgroup whose chunks hold token pos writes the
-  // stream's new row before any of its waves reads a key
-  if (a.p.x_new != nullptr && split == (int)((a.p.pos / (NWV * 16 * U)) % a.n_splits))
-    append_key<D, LB, PROD, NTA>(a.p, stream, tid);
   i32x4 areg[RT][NCH];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    if constexpr (PAR) {
-      prep_part<D, LB, PROD, NTP>(a.p, stream, rt, tid / NTP, tid % NTP, lds, &csts[0][0]);
-    } else {
-      prep_part<D, LB, PROD, NTP>(a.p, stream, rt, 0, tid, lds, &csts[0][0]);
-      if constexpr (PROD) prep_part<D, LB, PROD, NTP>(a.p, stream, rt, 1, tid, lds, &csts[0][0]);
-    }
-    const i32x4 *src = (const i32x4 *)lds;
+    const i32x4 *src = (const i32x4 *)(a.table + ((int64_t)stream * a.row_tiles + rt) * (NCH * 64 * 16));
 #pragma unroll
     for (int c = 0; c < NCH; ++c) areg[rt][c] = src[c * 64 + l];
-    if (rt + 1 < RT) __syncthreads();   // read before the next row tile is built
   }
   f32x4 cst[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int g = 4 * rt + kg;
-    cst[rt] = g < a.group ? *(const f32x4 *)&csts[g][0] : f32x4{0.f, 0.f, 0.f, 0.f};
+    cst[rt] = g < a.group ? *(const f32x4 *)(a.consts + ((int64_t)stream * a.group + g) * 4)
+                          : f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  __syncthreads();   // every wave holds its operands: the LDS becomes the logit stage
 
   // Buffer resources: SGPR bases, 32-bit per-lane offsets.  Contiguous
   // streams: the ranges end at seq_len, so loads of tokens past the stream
   // read zeros.  Paged: the ranges cover the pool; tokens past seq_len read
-  // whatever rows their page holds (their logits are never stored).  Stores
-  // past seq_len are dropped in both.
-  const bool paged = a.p.block_table != nullptr;
-  const int64_t key0 = paged ? 0 : (int64_t)stream * a.row_tokens;
+  // whatever rows their page holds (their logits are never stored), and a
+  // page outside the pool reads zeros.  Stores past seq_len are dropped.
+  const int64_t key0 = PAGED ? 0 : (int64_t)stream * a.row_tokens;
   const uint32_t nvalid = (uint32_t)a.seq_len;
-  const uint32_t nrows = paged ? (uint32_t)a.p.pool_rows : nvalid;
+  const uint32_t nrows = PAGED ? (uint32_t)a.pool_rows : nvalid;
   const i32x4 rc = make_rsrc(a.codes + key0 * RB, nrows * RB);
   const i32x4 rn = make_rsrc(a.norm + key0, nrows * 2);
   const i32x4 rg = make_rsrc(PROD ? a.rnorm + key0 : a.norm, PROD ? nrows * 2 : 0u);
+  // this sequence's block-table row, read with scalar loads (entries past
+  // the row read 0 through the range check)
+  const i32x4 rbt = make_rsrc(PAGED ? a.block_table + (int64_t)b * a.max_pages : a.block_table,
+                              PAGED ? (uint32_t)a.max_pages * 4 : 0u);
   const i32x4 ro = make_rsrc(a.logits + ((int64_t)b * a.n_q_heads + (int64_t)kvh * a.group) * a.seq_len,
                              (uint32_t)(a.group * a.seq_len * 4));
   const uint32_t t_end32 = nvalid;
@@ -535,7 +494,13 @@ __global__ __launch_bounds__((64 * logit_waves<D, LB, PROD, RT>())) void logit_k
   // lane l reads the two fp16 scalars of token l of each 64-token block.
   auto load = [&](uint32_t tok0, KeyGroup<NPL, NQ>(&kgp)[U], NormBlock(&nb)[NB]) {
     // first row of the wave's 64 tokens (one page holds all of them)
-    const uint32_t row0 = paged ? (uint32_t)paged_row(a.p, b, kvh, tok0) : tok0;
+    uint32_t row0 = tok0;
+    if constexpr (PAGED) {
+      const int pg = tq_llvm_s_buf_ld_b32(rbt, (int)(4 * (tok0 / (uint32_t)a.page_tokens)), 0);
+      const uint64_t r = ((uint64_t)(uint32_t)pg * (uint32_t)a.n_kv_heads + (uint32_t)kvh) * (uint32_t)a.page_tokens +
+                         tok0 % (uint32_t)a.page_tokens;
+      row0 = (pg >= 0 && r < (uint64_t)a.pool_rows) ? (uint32_t)r : (uint32_t)a.pool_rows;
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t tok = row0 + 16 * u + n;
@@ -626,13 +591,13 @@ __global__ __launch_bounds__((64 * logit_waves<D, LB, PROD, RT>())) void logit_k
     }
   };
 
-  // The blocks of a stream take its chunks of NWV x 16U tokens round-robin
+  // The blocks of a stream take its chunks of 4 x 16U tokens round-robin
   // (block j: chunks j, j + n_splits, ...), so the blocks running at any
   // moment stream through adjacent memory instead of n_splits distant
   // ranges in lockstep.  Wave w of a block takes the w-th 16U tokens of each
   // chunk.  Loop bounds are wave-uniform (scalar).
-  const uint32_t stride = NWV * 16 * U * (uint32_t)a.n_splits;
-  uint32_t base = (uint32_t)__builtin_amdgcn_readfirstlane((int)(16 * U * (NWV * split + w)));
+  const uint32_t stride = 4 * 16 * U * (uint32_t)a.n_splits;
+  uint32_t base = (uint32_t)__builtin_amdgcn_readfirstlane((int)(16 * U * (4 * split + w)));
   // Ping-pong over two register sets: the next iteration's loads are issued
   // before the current one is consumed.  The scheduling barriers keep each
   // prefetch ahead of the compute that hides its latency.
@@ -657,35 +622,21 @@ __global__ __launch_bounds__((64 * logit_waves<D, LB, PROD, RT>())) void logit_k
   }
 }
 
-template <int D, int LB, bool PROD, int RT>
-hipError_t launch_rt(const StreamArgs &sa, int n_streams, hipStream_t s) {
-  constexpr int NWV = logit_waves<D, LB, PROD, RT>();
-  auto kernel = logit_kernel<D, LB, PROD, RT>;
-  // One round of resident workgroups: every one builds its stream's tables
-  // once and then streams n_splits-strided chunks of NWV x 64 tokens.
-  int per_cu = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64 * NWV, 0);
-  if (e != hipSuccess) return e;
-  if (per_cu < 1) per_cu = 1;
-  const int64_t target = (int64_t)per_cu * tqi::device_cu_count();
-  const int64_t chunk = (int64_t)NWV * 16 * kLogitGroups;
-  const int64_t n_chunks = (sa.seq_len + chunk - 1) / chunk;
-  int64_t splits = (target + n_streams - 1) / n_streams;
-  if (splits > n_chunks) splits = n_chunks;
-  if (splits < 1) splits = 1;
-  StreamArgs a = sa;
-  a.n_splits = (int)splits;
-  hipLaunchKernelGGL(kernel, dim3((unsigned)(n_streams * splits)), dim3(64 * NWV), 0, s, a);
-  return hipGetLastError();
-}
-
 template <int D, int LB, bool PROD>
 hipError_t launch_t(const tqi::LogitArgs &a, hipStream_t s) {
+  using L = LLayout<D, LB, PROD>;
   const int group = a.n_q_heads / a.n_kv_heads;
   const int rts = (group + 3) / 4;
   const int n_streams = a.batch * a.n_kv_heads;
-  StreamArgs sa;
-  PrepArgs &pa = sa.p;
+  const size_t table_bytes = (size_t)n_streams * rts * L::NCH * 64 * 16;
+  // query tables and constants live in the caller's workspace; without it
+  // nothing is launched
+  if (a.workspace == nullptr ||
+      a.workspace_bytes < tqi::logits_workspace_bytes(D, LB, PROD, n_streams, group))
+    return hipErrorInvalidValue;
+  void *ws = a.workspace;
+  hipError_t e = hipSuccess;
+  PrepArgs pa;
   pa.q = a.q;
   pa.q_f32 = a.q_f32;
   pa.n_q_heads = a.n_q_heads;
@@ -695,6 +646,8 @@ hipError_t launch_t(const tqi::LogitArgs &a, hipStream_t s) {
   pa.pi = a.pi;
   pa.s_mat = a.s_mat;
   pa.centroids = a.centroids;
+  pa.table = (int8_t *)ws;
+  pa.consts = (float *)((char *)ws + tqi::ws_align(table_bytes));
   pa.x_new = a.x_new;
   pa.x_f32 = a.x_f32;
   pa.boundaries = a.boundaries;
@@ -708,22 +661,55 @@ hipError_t launch_t(const tqi::LogitArgs &a, hipStream_t s) {
   pa.page_tokens = a.page_tokens;
   pa.max_pages = a.max_pages;
   pa.pool_rows = a.pool_rows;
-  sa.codes = a.codes;
-  sa.norm = a.norm;
-  sa.rnorm = a.rnorm;
-  sa.row_tokens = a.row_tokens;
-  sa.seq_len = a.seq_len;
-  sa.n_kv_heads = a.n_kv_heads;
-  sa.n_q_heads = a.n_q_heads;
-  sa.group = group;
-  sa.scale = a.scale;
-  sa.logits = a.logits;
-  switch (rts) {
-    case 1: return launch_rt<D, LB, PROD, 1>(sa, n_streams, s);
-    case 2: return launch_rt<D, LB, PROD, 2>(sa, n_streams, s);
-    case 3: return launch_rt<D, LB, PROD, 3>(sa, n_streams, s);
-    default: return launch_rt<D, LB, PROD, 4>(sa, n_streams, s);
+  const int parts = (PROD ? 2 : 1) + (a.x_new != nullptr ? 1 : 0);
+  hipLaunchKernelGGL((logit_prep_kernel<D, LB, PROD>), dim3(n_streams, rts, parts),
+                     dim3(prep_threads<D>()), 0,
+                     s, pa);
+  e = hipGetLastError();
+  if (e == hipSuccess) {
+    StreamArgs sa;
+    sa.table = pa.table;
+    sa.consts = pa.consts;
+    sa.codes = a.codes;
+    sa.norm = a.norm;
+    sa.rnorm = a.rnorm;
+    sa.row_tokens = a.row_tokens;
+    sa.seq_len = a.seq_len;
+    sa.n_kv_heads = a.n_kv_heads;
+    sa.n_q_heads = a.n_q_heads;
+    sa.group = group;
+    sa.row_tiles = rts;
+    sa.scale = a.scale;
+    sa.logits = a.logits;
+    const int64_t target_blocks = (int64_t)kLogitBlocksPerCu * tqi::device_cu_count();
+    const int64_t n_chunks = (a.seq_len + 4 * 16 * kLogitGroups - 1) / (4 * 16 * kLogitGroups);
+    int64_t splits = (target_blocks + n_streams - 1) / n_streams;
+    if (splits > n_chunks) splits = n_chunks;
+    if (splits < 1) splits = 1;
+    sa.n_splits = (int)splits;
+    const int64_t blocks = (int64_t)n_streams * sa.n_splits;
+    sa.block_table = a.block_table;
+    sa.page_tokens = a.page_tokens;
+    sa.max_pages = a.max_pages;
+    sa.pool_rows = a.pool_rows;
+    if (a.block_table != nullptr) {
+      switch (rts) {
+        case 1: hipLaunchKernelGGL((logit_kernel<D, LB, PROD, 1, true>), dim3((unsigned)blocks), dim3(256), 0, s, sa); break;
+        case 2: hipLaunchKernelGGL((logit_kernel<D, LB, PROD, 2, true>), dim3((unsigned)blocks), dim3(256), 0, s, sa); break;
+        case 3: hipLaunchKernelGGL((logit_kernel<D, LB, PROD, 3, true>), dim3((unsigned)blocks), dim3(256), 0, s, sa); break;
+        default: hipLaunchKernelGGL((logit_kernel<D, LB, PROD, 4, true>), dim3((unsigned)blocks), dim3(256), 0, s, sa); break;
+      }
+    } else {
+      switch (rts) {
+        case 1: hipLaunchKernelGGL((logit_kernel<D, LB, PROD, 1, false>), dim3((unsigned)blocks), dim3(256), 0, s, sa); break;
+        case 2: hipLaunchKernelGGL((logit_kernel<D, LB, PROD, 2, false>), dim3((unsigned)blocks), dim3(256), 0, s, sa); break;
+        case 3: hipLaunchKernelGGL((logit_kernel<D, LB, PROD, 3, false>), dim3((unsigned)blocks), dim3(256), 0, s, sa); break;
+        default: hipLaunchKernelGGL((logit_kernel<D, LB, PROD, 4, false>), dim3((unsigned)blocks), dim3(256), 0, s, sa); break;
+      }
+    }
+    e = hipGetLastError();
   }
+  return e;
 }
 
 template <int D, bool PROD>
@@ -752,6 +738,13 @@ bool logits_supported(int d, int lbits, bool prod, int group, int64_t seq_len) {
   if ((2 * seq_len + 256) * (int64_t)((lbits + (prod ? 1 : 0)) * d / 8) >= (1LL << 32)) return false;
   if ((int64_t)group * seq_len * 4 >= (1LL << 31)) return false;
   return true;
+}
+
+size_t logits_workspace_bytes(int d, int lbits, bool prod, int64_t n_streams, int group) {
+  const int64_t rts = (group + 3) / 4;
+  const int64_t nch = ((1 << (lbits - 1)) + (prod ? 1 : 0)) * (d / 64);
+  const size_t table = (size_t)(n_streams * rts * nch * 64 * 16);
+  return ws_align(table) + ws_align((size_t)n_streams * group * 4 * sizeof(float));
 }
 
 hipError_t launch_logits(int d, int lbits, bool prod, const LogitArgs &a, hipStream_t s) {

@@ -571,7 +571,7 @@ hipError_t launch_t(const tqi::SearchArgs &sa, hipStream_t s) {
   // Key indices fit the packed list entries (30 bits); per-split byte offsets
   // of the packed codes stay below 2^31 (both checked by search_supported).
   const int64_t n_rows = plan.n_rows;
-  if (a.workspace_bytes < plan.bytes) return hipErrorInvalidValue;
+  if (a.workspace_bytes < plan.bytes || (plan.bytes > 0 && a.workspace == nullptr)) return hipErrorInvalidValue;
   char *ws = (char *)a.workspace;
   hipError_t e = hipSuccess;
   QPrepArgs pa;

@@ -76,9 +76,10 @@ tq_status logits_shape(const tq_params *p, int32_t batch, int32_t n_q_heads, int
 
 size_t logits_ws_bytes(const tq_params *p, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
                        int64_t seq_len, int32_t topk) {
-  // dense logits build their query tables in LDS: only search needs scratch
-  if (batch == 0 || seq_len == 0 || topk == 0) return 0;
-  return tqi::search_workspace_bytes(p->d, lloyd_bits(p), batch, n_q_heads, n_kv_heads, seq_len);
+  if (batch == 0 || seq_len == 0) return 0;
+  if (topk > 0) return tqi::search_workspace_bytes(p->d, lloyd_bits(p), batch, n_q_heads, n_kv_heads, seq_len);
+  return tqi::logits_workspace_bytes(p->d, lloyd_bits(p), p->mode == TQ_MODE_PROD,
+                                     (int64_t)batch * n_kv_heads, n_q_heads / n_kv_heads);
 }
 
 tq_status check_attend_args(const tq_params *p, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
@@ -207,7 +208,7 @@ extern "C" tq_status tq_append_attn_logits(const tq_params *p, const void *x_new
                                            const void *q, int32_t q_dtype, int32_t batch,
                                            int32_t n_q_heads, int32_t n_kv_heads, const tq_packed *k,
                                            int64_t row_tokens, int64_t pos, float scale, float *logits,
-                                           void *stream) {
+                                           void *workspace, size_t workspace_bytes, void *stream) {
   tq_status st = check_logit_args(p, batch, n_q_heads, n_kv_heads, 0, 0);
   if (st != TQ_OK) return st;
   const bool prod = p->mode == TQ_MODE_PROD;
@@ -221,8 +222,12 @@ extern "C" tq_status tq_append_attn_logits(const tq_params *p, const void *x_new
   if (x_new == nullptr || q == nullptr || logits == nullptr || k->codes == nullptr || k->norm == nullptr)
     return TQ_ERR_INVALID;
   if (prod && (p->qjl == nullptr || p->qjl_rot == nullptr || k->rnorm == nullptr)) return TQ_ERR_INVALID;
+  st = check_workspace(workspace, workspace_bytes, logits_ws_bytes(p, batch, n_q_heads, n_kv_heads, pos + 1, 0));
+  if (st != TQ_OK) return st;
   if ((uintptr_t)k->codes & 3u) return TQ_ERR_UNSUPPORTED;
   tqi::LogitArgs a;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
   a.q = q;
   a.q_f32 = q_dtype == TQ_F32;
   a.batch = batch;
@@ -277,7 +282,7 @@ tq_status paged_args(const tq_params *p, int32_t batch, int32_t n_kv_heads, cons
 extern "C" tq_status tq_attn_logits_paged(const tq_params *p, const void *q, int32_t q_dtype, int32_t batch,
                                           int32_t n_q_heads, int32_t n_kv_heads, const tq_packed *pool,
                                           const tq_pages *pages, int64_t seq_len, float scale, float *logits,
-                                          void *stream) {
+                                          void *workspace, size_t workspace_bytes, void *stream) {
   tq_status st = check_logit_args(p, batch, n_q_heads, n_kv_heads, seq_len, 0);
   if (st != TQ_OK) return st;
   const bool prod = p->mode == TQ_MODE_PROD;
@@ -291,7 +296,11 @@ extern "C" tq_status tq_attn_logits_paged(const tq_params *p, const void *q, int
   if (batch == 0 || seq_len == 0) return TQ_OK;
   if (q == nullptr || logits == nullptr || pool->codes == nullptr || pool->norm == nullptr) return TQ_ERR_INVALID;
   if (prod && (p->qjl == nullptr || pool->rnorm == nullptr)) return TQ_ERR_INVALID;
+  st = check_workspace(workspace, workspace_bytes, logits_ws_bytes(p, batch, n_q_heads, n_kv_heads, seq_len, 0));
+  if (st != TQ_OK) return st;
   if ((uintptr_t)pool->codes & 3u) return TQ_ERR_UNSUPPORTED;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
   a.q = q;
   a.q_f32 = q_dtype == TQ_F32;
   a.batch = batch;
@@ -312,7 +321,8 @@ extern "C" tq_status tq_attn_logits_paged(const tq_params *p, const void *q, int
 extern "C" tq_status tq_append_attn_logits_paged(const tq_params *p, const void *x_new, int32_t x_dtype,
                                                  const void *q, int32_t q_dtype, int32_t batch, int32_t n_q_heads,
                                                  int32_t n_kv_heads, const tq_packed *pool, const tq_pages *pages,
-                                                 int64_t pos, float scale, float *logits, void *stream) {
+                                                 int64_t pos, float scale, float *logits, void *workspace,
+                                                 size_t workspace_bytes, void *stream) {
   tq_status st = check_logit_args(p, batch, n_q_heads, n_kv_heads, 0, 0);
   if (st != TQ_OK) return st;
   const bool prod = p->mode == TQ_MODE_PROD;
@@ -328,7 +338,11 @@ extern "C" tq_status tq_append_attn_logits_paged(const tq_params *p, const void 
   if (x_new == nullptr || q == nullptr || logits == nullptr || pool->codes == nullptr || pool->norm == nullptr)
     return TQ_ERR_INVALID;
   if (prod && (p->qjl == nullptr || p->qjl_rot == nullptr || pool->rnorm == nullptr)) return TQ_ERR_INVALID;
+  st = check_workspace(workspace, workspace_bytes, logits_ws_bytes(p, batch, n_q_heads, n_kv_heads, pos + 1, 0));
+  if (st != TQ_OK) return st;
   if ((uintptr_t)pool->codes & 3u) return TQ_ERR_UNSUPPORTED;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
   a.q = q;
   a.q_f32 = q_dtype == TQ_F32;
   a.batch = batch;
@@ -351,6 +365,8 @@ extern "C" tq_status tq_append_attn_logits_paged(const tq_params *p, const void 
   a.norm_out = pool->norm;
   a.rnorm_out = pool->rnorm;
   a.pos = pos;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
   return hip_status(tqi::launch_logits(p->d, lloyd_bits(p), prod, a, (hipStream_t)stream));
 }
 
@@ -461,4 +477,21 @@ extern "C" tq_status tq_dequantize(const tq_params *p, const tq_packed *k, int64
   }
   if (!ok) return TQ_ERR_UNSUPPORTED;
   return hip_status(e);
+}
+
+extern "C" tq_status tq_probe_sink_words(int64_t *words) {
+  if (words == nullptr) return TQ_ERR_INVALID;
+  *words = (int64_t)tqi::probe_blocks() * 4;
+  return TQ_OK;
+}
+
+extern "C" tq_status tq_probe(int32_t kind, void *buf, int64_t bytes, int32_t iters, uint32_t *sink,
+                              int64_t sink_words, void *stream) {
+  if (kind < TQ_PROBE_READ || kind > TQ_PROBE_IDLE || sink == nullptr) return TQ_ERR_INVALID;
+  if (sink_words < (int64_t)tqi::probe_blocks() * 4) return TQ_ERR_INVALID;
+  if (kind <= TQ_PROBE_WRITE && (buf == nullptr || bytes < 16 || bytes % 16 != 0 || ((uintptr_t)buf & 15u)))
+    return TQ_ERR_INVALID;
+  if (kind >= TQ_PROBE_MFMA_F16 && iters <= 0) return TQ_ERR_INVALID;
+  if (kind == TQ_PROBE_IDLE && iters > 1000000) return TQ_ERR_INVALID;
+  return hip_status(tqi::launch_probe(kind, buf, bytes, iters, sink, (hipStream_t)stream));
 }

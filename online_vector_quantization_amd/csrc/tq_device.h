@@ -105,6 +105,9 @@ __device__ void tq_llvm_buf_st_f32(float v, i32x4 rsrc, int voff, int soff, int 
 __device__ void tq_llvm_buf_st_v4f32(f32x4 v, i32x4 rsrc, int voff, int soff, int aux) __asm("llvm.amdgcn.raw.buffer.store.v4f32");
 __device__ void tq_llvm_buf_st_b32(int v, i32x4 rsrc, int voff, int soff, int aux) __asm("llvm.amdgcn.raw.buffer.store.i32");
 __device__ void tq_llvm_buf_st_b16(short v, i32x4 rsrc, int voff, int soff, int aux) __asm("llvm.amdgcn.raw.buffer.store.i16");
+// Scalar buffer load (s_buffer_load_dword): a wave-uniform word through the
+// scalar data cache, counted apart from the vector loads in flight.
+__device__ int tq_llvm_s_buf_ld_b32(i32x4 rsrc, int off, int aux) __asm("llvm.amdgcn.s.buffer.load.i32");
 
 // A byte offset that every resource built here treats as out of range (the
 // ranges are kept below 2^31), so a lane can drop its store without a branch.

@@ -54,7 +54,7 @@ struct LogitArgs {
   const int32_t *block_table = nullptr;
   int page_tokens = 0, max_pages = 0;
   int64_t pool_rows = 0;
-  // caller-owned device scratch (top-k search: query tables, partial lists)
+  // caller-owned device scratch (query tables; for top-k also partial lists)
   void *workspace = nullptr;
   size_t workspace_bytes = 0;
 };
@@ -62,6 +62,7 @@ struct LogitArgs {
 // Shapes the dense logit kernels take (GQA group <= 16, d in {128, 256},
 // 32-bit byte offsets of one stream's codes and logits below 2^31).
 bool logits_supported(int d, int lbits, bool prod, int group, int64_t seq_len);
+size_t logits_workspace_bytes(int d, int lbits, bool prod, int64_t n_streams, int group);
 hipError_t launch_logits(int d, int lbits, bool prod, const LogitArgs &a, hipStream_t s);
 
 struct SearchArgs {
@@ -115,6 +116,11 @@ constexpr int kMaxDevices = 64;
 hipError_t noalloc_scratch(void **out);
 size_t attend_workspace_bytes(int d, int lbits, int batch, int n_q_heads, int n_kv_heads, int64_t seq_len);
 hipError_t launch_attend(int d, int lbits, const AttendArgs &a, hipStream_t s);
+
+// Ceiling probes (probes.hip): kind 0 read stream, 1 write stream, 2 fp16
+// MFMA loop, 3 int8 MFMA loop; probe_blocks() workgroups of 4 waves.
+int probe_blocks();
+hipError_t launch_probe(int kind, void *buf, int64_t bytes, int iters, uint32_t *sink, hipStream_t s);
 
 // Compute units of the current device (cached per device; 256 when the
 // runtime cannot say).

@@ -156,9 +156,14 @@ def test_workspace_queries_and_checks(tq):
     pp = tq.Params(128, 3, tq.MODE_PROD, 0, dummy, dummy, dummy, dummy, dummy)
     pm = tq.Params(128, 3, tq.MODE_MSE, 0, dummy, None, None, dummy, dummy)
     pk = tq.Packed(dummy, dummy, dummy)
-    # dense logits build their query tables in LDS: no scratch, at any shape
-    for args in ((1, 32, 8, 32768), (8, 32, 8, 131072), (1, 32, 8, 5), (0, 32, 8, 5), (1, 32, 8, 0)):
-        assert _size(lib.tq_attn_logits_workspace_size, ctypes.byref(pp), *args, 0) == (tq.TQ_OK, 0)
+    # dense logits: query tables of every (batch, kv head) stream, independent of seq_len
+    st, n8 = _size(lib.tq_attn_logits_workspace_size, ctypes.byref(pp), 1, 32, 8, 32768, 0)
+    assert st == tq.TQ_OK and n8 > 0 and n8 % 256 == 0
+    st, n64 = _size(lib.tq_attn_logits_workspace_size, ctypes.byref(pp), 8, 32, 8, 131072, 0)
+    assert st == tq.TQ_OK and n64 >= 8 * n8 - 8 * 256
+    assert _size(lib.tq_attn_logits_workspace_size, ctypes.byref(pp), 1, 32, 8, 5, 0) == (tq.TQ_OK, n8)
+    assert _size(lib.tq_attn_logits_workspace_size, ctypes.byref(pp), 0, 32, 8, 5, 0) == (tq.TQ_OK, 0)
+    assert _size(lib.tq_attn_logits_workspace_size, ctypes.byref(pp), 1, 32, 8, 0, 0) == (tq.TQ_OK, 0)
     assert _size(lib.tq_attn_logits_workspace_size, ctypes.byref(pp), 1, 30, 8, 5, 0)[0] == tq.TQ_ERR_INVALID
     assert lib.tq_attn_logits_workspace_size(ctypes.byref(pp), 1, 32, 8, 5, 0, None) == tq.TQ_ERR_INVALID
     # top-k search (MSE only): partial lists grow with the query count
@@ -173,6 +178,12 @@ def test_workspace_queries_and_checks(tq):
     assert _size(lib.tq_attn_output_workspace_size, ctypes.byref(pm), 1, 32, 8, 0) == (tq.TQ_OK, 0)
     assert _size(lib.tq_attn_output_workspace_size, ctypes.byref(pp), 1, 32, 8, 100)[0] == tq.TQ_ERR_UNSUPPORTED
     # the calls: NULL / short workspace -> invalid, misaligned -> unsupported
+    args = (ctypes.byref(pp), dummy, 0, 1, 32, 8, ctypes.byref(pk), 64, 64, f, dummy, 0, None)
+    assert lib.tq_attn_logits(*args, None, 0, None) == tq.TQ_ERR_INVALID
+    assert lib.tq_attn_logits(*args, ctypes.c_void_p(1 << 20), n8 - 1, None) == tq.TQ_ERR_INVALID
+    assert lib.tq_attn_logits(*args, ctypes.c_void_p((1 << 20) + 16), n8, None) == tq.TQ_ERR_UNSUPPORTED
+    app = (ctypes.byref(pp), dummy, 0, dummy, 0, 1, 32, 8, ctypes.byref(pk), 64, 10, f, dummy)
+    assert lib.tq_append_attn_logits(*app, None, 0, None) == tq.TQ_ERR_INVALID
     sargs = (ctypes.byref(pm), dummy, 0, 1, 1000, 1, ctypes.byref(pk), 100000, 100000, f, dummy, 10, dummy)
     assert lib.tq_attn_logits(*sargs, None, 0, None) == tq.TQ_ERR_INVALID
     assert lib.tq_attn_logits(*sargs, ctypes.c_void_p(1 << 20), s1 - 1, None) == tq.TQ_ERR_INVALID
@@ -200,7 +211,8 @@ def test_logit_ranges_stay_below_2_31(tq):
         assert lib.tq_attn_logits(ctypes.byref(p), dummy, 0, 1, group, 1, ctypes.byref(pk), limit, limit, f,
                                   dummy, 0, None, ctypes.c_void_p(1 << 20), 1 << 30, None) == tq.TQ_ERR_UNSUPPORTED
         assert lib.tq_append_attn_logits(ctypes.byref(p), dummy, 0, dummy, 0, 1, group, 1, ctypes.byref(pk),
-                                         limit, limit - 1, f, dummy, None) == tq.TQ_ERR_UNSUPPORTED
+                                         limit, limit - 1, f, dummy, ctypes.c_void_p(1 << 20), 1 << 30,
+                                         None) == tq.TQ_ERR_UNSUPPORTED
 
 
 def test_noalloc_entry_validates_before_launch(tq):
@@ -231,9 +243,12 @@ def test_paged_calls_validate_before_launch(tq):
     pp = tq.Params(128, 3, tq.MODE_PROD, 0, dummy, dummy, dummy, dummy, dummy)
     pk = tq.Packed(dummy, dummy, dummy)
 
+    ws = ctypes.c_void_p(1 << 20)
+
     def call(pages, seq_len=1000):
         return lib.tq_attn_logits_paged(ctypes.byref(pp), dummy, 0, 1, 32, 8, ctypes.byref(pk),
-                                        ctypes.byref(pages) if pages is not None else None, seq_len, f, dummy, None)
+                                        ctypes.byref(pages) if pages is not None else None, seq_len, f, dummy,
+                                        ws, 1 << 30, None)
 
     assert call(None) == tq.TQ_ERR_INVALID
     assert call(tq.Pages(None, 64, 16, 100)) == tq.TQ_ERR_INVALID                  # no table
@@ -245,6 +260,34 @@ def test_paged_calls_validate_before_launch(tq):
     app = lib.tq_append_attn_logits_paged
     pg = tq.Pages(dummy, 64, 16, 100)
     assert app(ctypes.byref(pp), dummy, 0, dummy, 0, 1, 32, 8, ctypes.byref(pk), ctypes.byref(pg), 1024, f, dummy,
-               None) == tq.TQ_ERR_INVALID                                           # pos 1024: past 16 pages of 64
+               ws, 1 << 30, None) == tq.TQ_ERR_INVALID                              # pos 1024: past 16 pages of 64
     assert app(ctypes.byref(pp), dummy, 0, dummy, 0, 1, 32, 8, ctypes.byref(pk), ctypes.byref(pg), -1, f, dummy,
-               None) == tq.TQ_ERR_INVALID
+               ws, 1 << 30, None) == tq.TQ_ERR_INVALID
+
+
+
+def test_probe_calls_validate_before_launch(tq):
+    """tq_probe refuses bad kinds, short sinks, unaligned or empty stream
+    buffers and out-of-range loop counts before any launch."""
+    lib = tq.LIB
+    words = ctypes.c_int64(0)
+    assert lib.tq_probe_sink_words(ctypes.byref(words)) == tq.TQ_OK and words.value > 0
+    assert lib.tq_probe_sink_words(None) == tq.TQ_ERR_INVALID
+    sink = ctypes.c_void_p(1 << 20)
+    buf = ctypes.c_void_p(1 << 24)
+    n = words.value
+
+    def probe(kind, b=buf, nbytes=1 << 20, iters=1, s=sink, sw=n):
+        return lib.tq_probe(kind, b, nbytes, iters, s, sw, None)
+
+    assert probe(-1) == tq.TQ_ERR_INVALID
+    assert probe(tq.PROBE_IDLE + 1) == tq.TQ_ERR_INVALID
+    assert probe(tq.PROBE_READ, s=None) == tq.TQ_ERR_INVALID
+    assert probe(tq.PROBE_READ, sw=n - 1) == tq.TQ_ERR_INVALID
+    assert probe(tq.PROBE_READ, b=None) == tq.TQ_ERR_INVALID
+    assert probe(tq.PROBE_WRITE, nbytes=24) == tq.TQ_ERR_INVALID
+    assert probe(tq.PROBE_WRITE, b=ctypes.c_void_p((1 << 24) + 8)) == tq.TQ_ERR_INVALID
+    assert probe(tq.PROBE_MFMA_F16, iters=0) == tq.TQ_ERR_INVALID
+    assert probe(tq.PROBE_MFMA_I8, iters=-3) == tq.TQ_ERR_INVALID
+    assert probe(tq.PROBE_IDLE, iters=0) == tq.TQ_ERR_INVALID
+    assert probe(tq.PROBE_IDLE, iters=1000001) == tq.TQ_ERR_INVALID
