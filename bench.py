@@ -69,6 +69,8 @@ def _args():
     ap.add_argument("--no-long-context", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 512 MiB device copy first (reference kernel for HBM counters)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/hbm_traffic.json from two rocprofv3 --pmc output folders and exit")
     return ap.parse_args()
 
 
@@ -99,12 +101,89 @@ def _traffic(kernel, src_files):
     return kib * 1024.0
 
 
+# The kernel instance (as rocprofv3 names it, template arguments included)
+# and the sources behind each traffic entry that bench.py reports.  Calls
+# that run the same instance on the same shape share its counters.
+_Q, _L, _D, _A = (["quantize.hip", "tq_device.h"], ["logits.hip", "tq_device.h"], ["dequant.hip", "tq_device.h"],
+                  ["attend.hip", "tq_device.h"])
+TRAFFIC_INSTANCES = {
+    "quantize_pc_kernel:quantize_k": ("quantize_pc_kernel<128, 2, false>", _Q),
+    "quantize_kernel:quantize_v": ("quantize_kernel<128, 3, false, false>", _Q),
+    "logit_kernel:attn_logits": ("logit_kernel<128, 2, true, 1, false>", _L),
+    "logit_kernel:append_attn_logits": ("logit_kernel<128, 2, true, 1, false>", _L),
+    "logit_kernel:attn_logits_paged": ("logit_kernel<128, 2, true, 1, true>", _L),
+    "logit_kernel:append_attn_logits_paged": ("logit_kernel<128, 2, true, 1, true>", _L),
+    "dequant_kernel:dequantize_v": ("dequant_kernel<128, 3, false, false, false>", _D),
+    "logit_kernel:long_context": ("logit_kernel<128, 3, true, 1, false>", _L),
+    "attend_mfma_kernel:attn_output": ("attend_mfma_kernel<128, 3, 4>", _A),
+    "attend_combine_kernel:attn_output": ("attend_combine_kernel<128>", _A),
+    "quantize_polar_kernel:polar_quantize": ("quantize_polar_kernel<128, false>", _Q),
+    "dequant_kernel:polar_dequantize": ("dequant_kernel<128, 1, false, false, true>", _D),
+}
+
+
+def write_traffic(fetch_dir, write_dir, out_path=None):
+    """profiles/hbm_traffic.json from two rocprofv3 --pmc runs (CSV output) of
+    `bench.py --copy-calibration`: FETCH_SIZE in fetch_dir, WRITE_SIZE in
+    write_dir.  The first copy kernel of each run is the 512 MiB calibration
+    copy; each counter is scaled by 512 MiB over its reading there.  Prints
+    the table of the summary."""
+    import csv
+    import glob
+
+    def load(d, counter):
+        rows = {}
+        for path in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    if r["Counter_Name"] != counter:
+                        continue
+                    key = (path, int(r["Dispatch_Id"]))
+                    name, v = rows.get(key, (r["Kernel_Name"], 0.0))
+                    rows[key] = (name, v + float(r["Counter_Value"]))
+        if not rows:
+            raise SystemExit("no %s rows under %s" % (counter, d))
+        return rows
+
+    fetch, write = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
+
+    def scale(rows, counter):
+        copies = sorted((k, v) for k, (n, v) in rows.items() if "copy" in n.lower())
+        if not copies:
+            raise SystemExit("no calibration copy among the %s dispatches" % counter)
+        return 524288.0 / copies[0][1], copies[0][1]
+
+    fs, f_cal = scale(fetch, "FETCH_SIZE")
+    ws, w_cal = scale(write, "WRITE_SIZE")
+    table = {"_note": "HBM bytes per dispatch from two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of "
+                      "'python bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-peaks --copy-calibration'; "
+                      "each counter is scaled by 512 MiB / its reading for the 512 MiB calibration copy in the "
+                      "same run (fetch x%.4f, write x%.4f). source_sha is the hash of the kernel sources the "
+                      "counters were taken on." % (fs, ws)}
+    print("calibration copy: FETCH_SIZE %.1f KiB, WRITE_SIZE %.1f KiB (x%.4f, x%.4f)" % (f_cal, w_cal, fs, ws))
+    print("| kernel (call) | instance | dispatches | FETCH KiB raw | WRITE KiB raw | HBM MB scaled |")
+    print("|---|---|---|---|---|---|")
+    for key, (inst, src) in TRAFFIC_INSTANCES.items():
+        fv = [v for n, v in fetch.values() if inst in n]
+        wv = [v for n, v in write.values() if inst in n]
+        if not fv or not wv:
+            continue
+        ent = {"fetch_kib": sum(fv) / len(fv), "fetch_scale": fs, "write_kib": sum(wv) / len(wv),
+               "write_scale": ws, "source_sha": _source_hash(src), "dispatches": min(len(fv), len(wv))}
+        table[key] = ent
+        mb = (ent["fetch_kib"] * fs + ent["write_kib"] * ws) * 1024 / 1e6
+        print("| %s | %s | %d | %.1f | %.1f | %.2f |" % (key, inst, ent["dispatches"], ent["fetch_kib"],
+                                                       ent["write_kib"], mb))
+    with open(out_path or os.path.join(PROFILES, "hbm_traffic.json"), "w") as f:
+        json.dump(table, f, indent=1)
+        f.write("\n")
+
+
 class Timer:
     """HIP events on the current stream (the stream every call is queued on)."""
 
-    def __init__(self, torch, idle=None):
+    def __init__(self, torch):
         self.torch = torch
-        self.idle = idle     # queues a wait of some milliseconds on the stream
 
     def __call__(self, fn, n):
         """Mean duration of n back-to-back launches of fn (seconds)."""
@@ -119,21 +198,39 @@ class Timer:
         t.cuda.synchronize()
         return start.elapsed_time(end) * 1e-3 / n
 
-    def each(self, fn, n):
-        """Per-launch durations of n launches (seconds), events around each.
-        An idle wait queued first keeps the GPU busy while the host queues
-        the n launches, so no event interval contains host time."""
+    def each(self, fn, n, filler=None):
+        """Per-launch durations of n launches of fn (seconds), events around
+        each.  With a filler (work queued before each launch, outside its
+        events) the GPU stays busy while the host queues the next launch, so
+        no event interval of a short call contains host time."""
         t = self.torch
         ev = [(t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)) for _ in range(n)]
         t.cuda.synchronize()
-        if self.idle is not None:
-            self.idle(n)
         for i, (a, b) in enumerate(ev):
+            if filler is not None:
+                filler(i)
             a.record()
             fn(i)
             b.record()
         t.cuda.synchronize()
         return [a.elapsed_time(b) * 1e-3 for a, b in ev]
+
+    def in_steps(self, calls, n, skip=2):
+        """Per-call durations (seconds) from events around every call of n
+        steps run back to back, as in the timed region; the first `skip`
+        steps (while the host fills the queue) are dropped."""
+        t = self.torch
+        ev = {k: [] for k in calls}
+        t.cuda.synchronize()
+        for i in range(n + skip):
+            for k, fn in calls.items():
+                a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+                a.record()
+                fn(i)
+                b.record()
+                ev[k].append((a, b))
+        t.cuda.synchronize()
+        return {k: [a.elapsed_time(b) * 1e-3 for a, b in v[skip:]] for k, v in ev.items()}
 
 
 def _stats(ts):
@@ -441,7 +538,20 @@ def cpu_baseline_decode(budget_s=12.0):
                       (heads, seq, t_used)}
 
 
-def long_context_leg(torch, tq, timer, reps, device):
+def _settle(torch, fn, seconds):
+    """Untimed calls of fn for about `seconds` (the clocks reach their
+    sustained level only under sustained load)."""
+    torch.cuda.synchronize()
+    t0, i = time.perf_counter(), 0
+    while time.perf_counter() - t0 < seconds or i < 3:
+        fn(i)
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
+def long_context_leg(torch, tq, timer, reps, device, settle=1.0):
     d, batch, heads, qheads, seq, bits = 128, 8, 8, 32, 131072, 4
     from synthetic import device_kv, device_queries
     x = device_kv(torch, 0, 3, "k", batch, heads, seq, d, device)
@@ -451,7 +561,7 @@ def long_context_leg(torch, tq, timer, reps, device):
     q = device_queries(torch, 0, 3, batch, qheads, heads, d, device)
     out = torch.empty((batch, qheads, seq), dtype=torch.float32, device=device)
     call = lambda i: qz.attn_logits(q, cache, heads, seq, 1.0 / math.sqrt(d), out=out)
-    call(0)
+    _settle(torch, call, settle)
     st = _stats(timer.each(call, max(reps, 20)))
     t = timer(call, reps)
     keys = batch * heads * seq
@@ -461,11 +571,14 @@ def long_context_leg(torch, tq, timer, reps, device):
     return {"workload": "batch 8, 8 KV heads x 128, 131072 tokens, keys inner-product b=4, "
                         "32 query heads", "us_per_call": t * 1e6, "per_launch": st, "keys_per_s": keys / t,
             "hbm_gbs": byts / t / 1e9, "frac_of_peak": byts / t / 1e9 / HBM_PEAK_GBS,
-            "algorithmic_bytes": byts}
+            "algorithmic_bytes": byts, "traffic": _traffic("logit_kernel:long_context", _L)}
 
 
 def main():
     args = _args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only (the library has no multi-GPU path); "
               "run it with --gpus 1", file=sys.stderr)
@@ -474,9 +587,7 @@ def main():
     import online_vector_quantization_amd as tq
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     device = torch.device("cuda:0")
-    # idle wait ahead of per-launch timing: 100 us per queued launch (the
-    # host queues one in well under that), at least 2 ms
-    timer = Timer(torch, idle=lambda n: tq.probe(tq.PROBE_IDLE, iters=max(2000, 100 * n), device=device))
+    timer = Timer(torch)
     if args.copy_calibration:
         a = torch.empty(512 << 20, dtype=torch.uint8, device=device)
         b = torch.empty_like(a)
@@ -510,10 +621,11 @@ def main():
     wall = time.perf_counter() - t0
     t_warm = timer(lambda i: step(0), args.steps) if args.workload == "decode" else None
 
+    # per-call durations: events around every call of steps like the timed ones
+    per_call = timer.in_steps(calls, args.steps)
     breakdown = {}
     for name, fn in calls.items():
-        ts_each = timer.each(fn, args.steps)
-        st = _stats(ts_each)
+        st = _stats(per_call[name])
         t = st["mean_us"] * 1e-6
         byts, flops, kern, src = work[name]
         breakdown[name] = dict(st, us=st["mean_us"], hbm_gbs=byts / t / 1e9, frac_hbm=byts / t / 1e9 / HBM_PEAK_GBS,
@@ -557,14 +669,14 @@ def main():
         for name, (fn, byts, kern, src) in extras.items():
             for i in range(max(args.warmup, 3)):
                 fn(i)
-            st = _stats(timer.each(fn, args.steps))
+            st = _stats(timer.each(fn, args.steps, filler=step))
             t = st["mean_us"] * 1e-6
             line["extras"][name] = dict(st, us=st["mean_us"], hbm_gbs=byts / t / 1e9,
                                         frac_hbm=byts / t / 1e9 / HBM_PEAK_GBS, kernel=kern,
                                         algorithmic_bytes_per_launch=byts,
                                         traffic=_traffic(kern + ":" + name, src), in_step=False)
     if args.workload == "decode" and not args.no_long_context:
-        line["long_context_logits"] = long_context_leg(torch, tq, timer, args.steps, device)
+        line["long_context_logits"] = long_context_leg(torch, tq, timer, args.steps, device, args.settle)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = {"decode": cpu_baseline_decode, "prefill": cpu_baseline_prefill,
                                 "search": cpu_baseline_search}[args.workload]()

@@ -335,16 +335,11 @@ tq_status tq_dequantize(const tq_params *p, const tq_packed *k, int64_t n_vec, v
  *   TQ_PROBE_MFMA_F16  every wave of the grid runs 4 x `iters` 32x32x16 fp16
  *                      MFMAs (32768 flops each) on registers; no memory
  *   TQ_PROBE_MFMA_I8   the same with 16x16x64 int8 MFMAs (32768 ops each)
- *   TQ_PROBE_IDLE      one wave waits (s_sleep) until `iters` microseconds of
- *                      the device's constant wall clock have passed (1 ..
- *                      1000000); queued ahead of timed launches, it keeps the
- *                      stream busy while the host queues them, so the events
- *                      around each launch see no host gaps
- * The grid is tq_probe_sink_words / 4 workgroups of 4 waves (the idle probe:
- * one wave); `sink` (device, sink_words uint32) receives values that keep the
- * work live.  buf: device, 16-byte aligned, bytes a multiple of 16.
+ * The grid is tq_probe_sink_words / 4 workgroups of 4 waves; `sink` (device,
+ * sink_words uint32) receives values that keep the work live.  buf: device,
+ * 16-byte aligned, bytes a multiple of 16.
  * Errors: TQ_ERR_INVALID, TQ_ERR_HIP. */
-enum { TQ_PROBE_READ = 0, TQ_PROBE_WRITE = 1, TQ_PROBE_MFMA_F16 = 2, TQ_PROBE_MFMA_I8 = 3, TQ_PROBE_IDLE = 4 };
+enum { TQ_PROBE_READ = 0, TQ_PROBE_WRITE = 1, TQ_PROBE_MFMA_F16 = 2, TQ_PROBE_MFMA_I8 = 3 };
 tq_status tq_probe_sink_words(int64_t *words);
 tq_status tq_probe(int32_t kind, void *buf, int64_t bytes, int32_t iters, uint32_t *sink, int64_t sink_words,
                    void *stream);

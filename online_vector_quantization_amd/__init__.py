@@ -39,7 +39,7 @@ EXPORTED = ["tq_make_codebook", "tq_make_polar_codebook", "tq_make_rotation", "t
             "tq_append_attn_logits_paged",
             "tq_attn_output_workspace_size", "tq_attn_output", "tq_attn_output_noalloc", "tq_dequantize",
             "tq_probe_sink_words", "tq_probe", "tq_status_string"]
-PROBE_READ, PROBE_WRITE, PROBE_MFMA_F16, PROBE_MFMA_I8, PROBE_IDLE = 0, 1, 2, 3, 4
+PROBE_READ, PROBE_WRITE, PROBE_MFMA_F16, PROBE_MFMA_I8 = 0, 1, 2, 3
 NOALLOC_SCRATCH_BYTES = 4 << 20
 
 
@@ -412,9 +412,8 @@ class Quantizer:
 
 def probe(kind, buf=None, iters=0, device="cuda"):
     """One launch of a ceiling probe (tq_probe) on the current stream: a
-    read or write stream over the uint8 device tensor ``buf``, an MFMA loop
-    of ``iters`` steps, or an idle wait of ``iters`` microseconds.  Returns
-    the work of the launch: bytes, flops, or 0 for the idle wait."""
+    read or write stream over the uint8 device tensor ``buf``, or an MFMA loop
+    of ``iters`` steps.  Returns the work of the launch: bytes, or flops."""
     torch = _torch()
     n = ctypes.c_int64(0)
     _check(LIB.tq_probe_sink_words(ctypes.byref(n)), "tq_probe_sink_words")
@@ -428,8 +427,6 @@ def probe(kind, buf=None, iters=0, device="cuda"):
                         ctypes.c_void_p(sink.data_ptr()), n.value, _stream_ptr(torch.device(device))), "tq_probe")
     if kind in (PROBE_READ, PROBE_WRITE):
         return nbytes
-    if kind == PROBE_IDLE:
-        return 0
     return n.value * iters * 4 * 32768
 
 

@@ -1,7 +1,6 @@
 // Ceiling probes: the best this GPU does on a plain read stream, a plain
 // write stream and a loop of matrix-core instructions with no memory
-// traffic; and an idle wait that keeps a stream busy while a timed sequence
-// of launches is queued behind it.  The rooflines of the hot-path kernels are reported as fractions
+// traffic.  The rooflines of the hot-path kernels are reported as fractions
 // of these measured ceilings next to the published peaks (an HBM read
 // stream, not the vendor's 8 TB/s, is what a streaming kernel can reach).
 #include "tq_device.h"
@@ -87,20 +86,6 @@ __global__ __launch_bounds__(kProbeThreads) void mfma_i8_loop_kernel(int iters, 
   if (s == 12345) sink[blockIdx.x * (kProbeThreads / 64) + threadIdx.x / 64] = 1u;
 }
 
-// One wave sleeps until `ticks` periods of the constant wall clock have
-// passed since it started; the loop ends because that clock only advances.
-__global__ __launch_bounds__(64) void idle_kernel(uint64_t ticks, uint32_t *__restrict__ sink) {
-  const uint64_t t0 = wall_clock64();
-  uint64_t t = t0;
-  uint32_t n = 0;
-  while (t - t0 < ticks) {
-    __builtin_amdgcn_s_sleep(64);
-    t = wall_clock64();
-    ++n;
-  }
-  if (n == 0xFFFFFFFFu) sink[threadIdx.x] = n;   // keeps the loop live
-}
-
 }  // namespace
 
 namespace tqi {
@@ -124,16 +109,6 @@ hipError_t launch_probe(int kind, void *buf, int64_t bytes, int iters, uint32_t 
     case 3:
       hipLaunchKernelGGL(mfma_i8_loop_kernel, dim3(blocks), dim3(kProbeThreads), 0, s, iters, sink);
       break;
-    case 4: {
-      int khz = 0;    // wall-clock rate of the current device
-      int dev = 0;
-      hipError_t e = hipGetDevice(&dev);
-      if (e == hipSuccess) e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
-      if (e != hipSuccess) return e;
-      if (khz <= 0) khz = 100000;
-      hipLaunchKernelGGL(idle_kernel, dim3(1), dim3(64), 0, s, (uint64_t)iters * (uint64_t)khz / 1000u, sink);
-      break;
-    }
     default:
       return hipErrorInvalidValue;
   }

@@ -487,11 +487,10 @@ extern "C" tq_status tq_probe_sink_words(int64_t *words) {
 
 extern "C" tq_status tq_probe(int32_t kind, void *buf, int64_t bytes, int32_t iters, uint32_t *sink,
                               int64_t sink_words, void *stream) {
-  if (kind < TQ_PROBE_READ || kind > TQ_PROBE_IDLE || sink == nullptr) return TQ_ERR_INVALID;
+  if (kind < TQ_PROBE_READ || kind > TQ_PROBE_MFMA_I8 || sink == nullptr) return TQ_ERR_INVALID;
   if (sink_words < (int64_t)tqi::probe_blocks() * 4) return TQ_ERR_INVALID;
   if (kind <= TQ_PROBE_WRITE && (buf == nullptr || bytes < 16 || bytes % 16 != 0 || ((uintptr_t)buf & 15u)))
     return TQ_ERR_INVALID;
   if (kind >= TQ_PROBE_MFMA_F16 && iters <= 0) return TQ_ERR_INVALID;
-  if (kind == TQ_PROBE_IDLE && iters > 1000000) return TQ_ERR_INVALID;
   return hip_status(tqi::launch_probe(kind, buf, bytes, iters, sink, (hipStream_t)stream));
 }

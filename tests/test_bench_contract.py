@@ -48,3 +48,36 @@ def test_traffic_of_the_dominant_kernel_matches_its_algorithmic_bytes():
     # within a few percent of the algorithmic bytes per launch (262144 keys:
     # 256 B read, 48 B of codes and signs and 4 B of norms written)
     assert abs(t / (262144 * (256 + 48 + 4)) - 1.0) < 0.05
+
+
+def _counter_csv(path, counter, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for did, name, v in rows:
+            f.write('%d,"%s",%s,%r\n' % (did, name, counter, v))
+
+
+def test_write_traffic_scales_by_the_first_copy(tmp_path):
+    """--write-traffic: the first copy kernel is the 512 MiB calibration, each
+    entry is the mean over its instance's dispatches, rows of one dispatch add."""
+    inst = bench.TRAFFIC_INSTANCES["quantize_pc_kernel:quantize_k"][0]
+    other = "void ns::logit_kernel<128, 3, true, 1, false>(Args)"
+    fetch = [(1, "void at::native::direct_copy_kernel(...)", 262144.0),
+             (2, "void at::native::direct_copy_kernel(...)", 999999.0),     # a later, larger copy
+             (3, "void ns::%s(Args)" % inst, 30000.0), (4, "void ns::%s(Args)" % inst, 34000.0),
+             (5, other, 1000.0), (5, other, 500.0)]
+    write = [(1, "void at::native::direct_copy_kernel(...)", 524288.0),
+             (3, "void ns::%s(Args)" % inst, 13000.0), (4, "void ns::%s(Args)" % inst, 13000.0),
+             (5, other, 100.0)]
+    _counter_csv(str(tmp_path / "f" / "host" / "p_counter_collection.csv"), "FETCH_SIZE", fetch)
+    _counter_csv(str(tmp_path / "w" / "host" / "p_counter_collection.csv"), "WRITE_SIZE", write)
+    out = tmp_path / "t.json"
+    bench.write_traffic(str(tmp_path / "f"), str(tmp_path / "w"), str(out))
+    table = json.loads(out.read_text())
+    e = table["quantize_pc_kernel:quantize_k"]
+    assert e["fetch_scale"] == 2.0 and e["write_scale"] == 1.0
+    assert e["fetch_kib"] == 32000.0 and e["write_kib"] == 13000.0 and e["dispatches"] == 2
+    lc = table["logit_kernel:long_context"]
+    assert lc["fetch_kib"] == 1500.0 and lc["write_kib"] == 100.0 and lc["dispatches"] == 1
+    assert "dequant_kernel:dequantize_v" not in table

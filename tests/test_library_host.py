@@ -281,7 +281,7 @@ def test_probe_calls_validate_before_launch(tq):
         return lib.tq_probe(kind, b, nbytes, iters, s, sw, None)
 
     assert probe(-1) == tq.TQ_ERR_INVALID
-    assert probe(tq.PROBE_IDLE + 1) == tq.TQ_ERR_INVALID
+    assert probe(tq.PROBE_MFMA_I8 + 1) == tq.TQ_ERR_INVALID
     assert probe(tq.PROBE_READ, s=None) == tq.TQ_ERR_INVALID
     assert probe(tq.PROBE_READ, sw=n - 1) == tq.TQ_ERR_INVALID
     assert probe(tq.PROBE_READ, b=None) == tq.TQ_ERR_INVALID
@@ -289,5 +289,3 @@ def test_probe_calls_validate_before_launch(tq):
     assert probe(tq.PROBE_WRITE, b=ctypes.c_void_p((1 << 24) + 8)) == tq.TQ_ERR_INVALID
     assert probe(tq.PROBE_MFMA_F16, iters=0) == tq.TQ_ERR_INVALID
     assert probe(tq.PROBE_MFMA_I8, iters=-3) == tq.TQ_ERR_INVALID
-    assert probe(tq.PROBE_IDLE, iters=0) == tq.TQ_ERR_INVALID
-    assert probe(tq.PROBE_IDLE, iters=1000001) == tq.TQ_ERR_INVALID
