@@ -220,7 +220,8 @@ tq_status tq_attn_logits(const tq_params *p, const void *q, int32_t q_dtype, int
  * every stream (quantisation on every cache update, page section
  * "TurboQuant 구현 방법"; the key is quantised exactly as by tq_quantize_kv,
  * stages "1단계" and "2단계"; logits as tq_attn_logits).  The append runs
- * inside the logit call's first launch, so the step costs no extra launch.
+ * inside the logit call's first (query preparation) launch, so the step costs
+ * no extra launch.
  *   x_new        device [batch][n_kv_heads][d], x_dtype TQ_F32 or TQ_BF16
  *   k            packed keys laid out [batch][n_kv_heads][row_tokens]; token
  *                pos of every stream is overwritten, the other rows are only
@@ -268,12 +269,14 @@ tq_status tq_attn_logits_paged(const tq_params *p, const void *q, int32_t q_dtyp
 /* tq_append_attn_logits over a paged key cache: the new key of every
  * (sequence, KV head) goes to the pool row of token pos (its page must be in
  * the block table: pos < max_pages * page_tokens), then the logits over tokens
- * 0..pos, [batch][n_q_heads][pos + 1].  One launch, no scratch. */
+ * 0..pos, [batch][n_q_heads][pos + 1].  Same support and errors as
+ * tq_attn_logits_paged; workspace as tq_attn_logits with seq_len = pos + 1
+ * and topk = 0. */
 tq_status tq_append_attn_logits_paged(const tq_params *p, const void *x_new, int32_t x_dtype,
                                       const void *q, int32_t q_dtype, int32_t batch, int32_t n_q_heads,
                                       int32_t n_kv_heads, const tq_packed *pool, const tq_pages *pages,
                                       int64_t pos, float scale, float *logits, void *workspace,
-                                size_t workspace_bytes, void *stream);
+                                      size_t workspace_bytes, void *stream);
 
 /* Decode attention output straight from packed values (page: the KV cache
  * holds keys and values, section "TurboQuant란 무엇인가요?", and attention runs
