@@ -102,6 +102,17 @@ __device__ __forceinline__ float xor_lanes(float v, int off) {
   return __shfl_xor(v, off, 64);
 }
 
+// One DPP step of the prep's wave reductions: v[0..3] take the maximum with
+// the CTRL partner lane, v[4..7] the sum.
+template <int CTRL>
+__device__ __forceinline__ void wave_fold(float (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float o = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v[i]), CTRL, 0xF, 0xF, false));
+    v[i] = i < 4 ? fmaxf(v[i], o) : v[i] + o;
+  }
+}
+
 // Decode-time append: quantise the new key of one stream and write its
 // packed row at token pos, inside the prep launch so that the streaming
 // kernel that follows reads it (page "TurboQuant 설명 ...": quantisation on
@@ -221,7 +232,7 @@ __global__ __launch_bounds__(prep_threads<D>()) void logit_prep_kernel(PrepArgs 
   __shared__ __attribute__((aligned(16))) float qin[4][D];
   __shared__ float proj[4][D];
   __shared__ double beta[P];
-  __shared__ float red_max[4][NW], red_sum[4][NW];
+  __shared__ __attribute__((aligned(16))) float red_max[4][NW], red_sum[4][NW];
 
   const int stream = blockIdx.x;
   const int rt = blockIdx.y;
@@ -281,38 +292,37 @@ __global__ __launch_bounds__(prep_threads<D>()) void logit_prep_kernel(PrepArgs 
     }
   }
   // full row sums in every lane of the row (quad permutes for the lanes of a
-  // row), then max |.| and sum over the rows of this wave
-  float mx[4], sm[4];
+  // row), then max |.| and sum over the rows of this wave: the eight values
+  // interleaved through DPP steps within rows of 16 lanes and four
+  // readlanes (no LDS permutes); then every thread folds the waves' results
+  // after one barrier
+  float v[8];                               // max |q'_j| (g), sum q'_j (4 + g)
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
 #pragma unroll
     for (int off = 1; off < RL; off <<= 1) acc[g] += xor_lanes(acc[g], off);
     if (pl == 0) proj[g][j] = acc[g];
-    mx[g] = fabsf(acc[g]);
-    sm[g] = pl == 0 ? acc[g] : 0.0f;
+    v[g] = fabsf(acc[g]);
+    v[4 + g] = pl == 0 ? acc[g] : 0.0f;
+  }
+  wave_fold<0xB1>(v);
+  wave_fold<0x4E>(v);
+  wave_fold<0x124>(v);
+  wave_fold<0x128>(v);
 #pragma unroll
-    for (int off = RL; off < 64; off <<= 1) {
-      mx[g] = fmaxf(mx[g], xor_lanes(mx[g], off));
-      sm[g] += xor_lanes(sm[g], off);
-    }
+  for (int g = 0; g < 4; ++g) {
+    const int m = __float_as_int(v[g]), q = __float_as_int(v[4 + g]);
+    v[g] = fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(m, 0)), __int_as_float(__builtin_amdgcn_readlane(m, 16))),
+                 fmaxf(__int_as_float(__builtin_amdgcn_readlane(m, 32)), __int_as_float(__builtin_amdgcn_readlane(m, 48))));
+    v[4 + g] = (__int_as_float(__builtin_amdgcn_readlane(q, 0)) + __int_as_float(__builtin_amdgcn_readlane(q, 16))) +
+               (__int_as_float(__builtin_amdgcn_readlane(q, 32)) + __int_as_float(__builtin_amdgcn_readlane(q, 48)));
   }
   if ((tid & 63) == 0) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      red_max[g][tid >> 6] = mx[g];
-      red_sum[g][tid >> 6] = sm[g];
+      red_max[g][tid >> 6] = v[g];
+      red_sum[g][tid >> 6] = v[4 + g];
     }
-  }
-  __syncthreads();
-  // thread g < 4 folds the per-wave results of query g
-  if (tid < 4) {
-    float mq = 0.0f, sq = 0.0f;
-    for (int wv = 0; wv < NW; ++wv) {
-      mq = fmaxf(mq, red_max[tid][wv]);
-      sq += red_sum[tid][wv];
-    }
-    red_max[tid][0] = mq;
-    red_sum[tid][0] = sq;
   }
   __syncthreads();
   double mb = 0.0, sb = 0.0;
@@ -325,7 +335,13 @@ __global__ __launch_bounds__(prep_threads<D>()) void logit_prep_kernel(PrepArgs 
   int fexp[4];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    const double mq = red_max[g][0], sq = red_sum[g][0];
+    float mqf = red_max[g][0], sqf = red_sum[g][0];
+#pragma unroll
+    for (int wv = 1; wv < NW; ++wv) {
+      mqf = fmaxf(mqf, red_max[g][wv]);
+      sqf += red_sum[g][wv];
+    }
+    const double mq = mqf, sq = sqf;
     const double top = part == 0 ? mq * mb : mq;
     int e = 0;
     if (top > 0.0) frexp(top, &e);
@@ -363,21 +379,23 @@ __global__ __launch_bounds__(prep_threads<D>()) void logit_prep_kernel(PrepArgs 
     const double wgt = part == 0 ? beta[r < P ? r : 0] : 1.0;
     const bool live = 4 * rt + g < a.group;
     const int s = 4 * hh + t;
-    uint32_t words[4] = {0u, 0u, 0u, 0u};   // [piece]
+    uint32_t e[4];                           // [ib]: the four digits of weight ib
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib) {
       const int j = 32 * (kg + 4 * q) + 8 * ib + 4 * hh + t;
       int n = (int)rint(ldexp(wgt * (double)proj[g][j], fexp[g] - s));
       if (s == 7) n = -n;
       if (!live) n = 0;
-      // balanced signed-byte digits: n = sum_p digit_p 256^p, digit_p in [-128, 127]
-#pragma unroll
-      for (int pc = 0; pc < 4; ++pc) {
-        const int dd = (int)(int8_t)(n & 0xFF);
-        words[pc] |= (uint32_t)(uint8_t)dd << (8 * ib);
-        n = (n - dd) >> 8;
-      }
+      // balanced signed-byte digits n = sum_p d_p 256^p, d_p in [-128, 127]
+      // (|n| <= 2^30): the bytes of n + 0x80808080 are the d_p + 128, with
+      // no carries, so those of (n + 0x80808080) ^ 0x80808080 are the d_p
+      e[ib] = ((uint32_t)n + 0x80808080u) ^ 0x80808080u;
     }
+    uint32_t words[4];                       // [piece]: digit piece of the four weights
+#pragma unroll
+    for (int pc = 0; pc < 4; ++pc)
+      words[pc] = ((e[0] >> (8 * pc)) & 0xFFu) | (((e[1] >> (8 * pc)) & 0xFFu) << 8) |
+                  (((e[2] >> (8 * pc)) & 0xFFu) << 16) | (((e[3] >> (8 * pc)) & 0xFFu) << 24);
 #pragma unroll
     for (int pc = 0; pc < 4; ++pc) {
       const int l = 16 * kg + 4 * g + pc;
