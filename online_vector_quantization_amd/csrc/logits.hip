@@ -93,12 +93,15 @@ struct LLayout {
 template <int D>
 constexpr int prep_threads() { return 512; }
 
-// v from lane (lane ^ off): quad permutes (no LDS) within 4 lanes, the
-// LDS permute unit beyond.
+// A partner lane's v for sums over aligned groups of 2, 4 or 8 lanes: the
+// quad permutes [1,0,3,2] and [2,3,0,1], then the half-row mirror (lane i of
+// 8 with lane 7 - i, which pairs the group's two quads); beyond 8 lanes the
+// LDS permute unit (lane ^ off).
 __device__ __forceinline__ float xor_lanes(float v, int off) {
   const int b = __float_as_int(v);
-  if (off == 1) return __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0xB1, 0xF, 0xF, false));  // [1,0,3,2]
-  if (off == 2) return __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
+  if (off == 1) return __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0xB1, 0xF, 0xF, false));
+  if (off == 2) return __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0x4E, 0xF, 0xF, false));
+  if (off == 4) return __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0x141, 0xF, 0xF, false));
   return __shfl_xor(v, off, 64);
 }
 
@@ -225,10 +228,10 @@ __global__ __launch_bounds__(prep_threads<D>()) void logit_prep_kernel(PrepArgs 
   constexpr int K = 1 << LB;
   constexpr int P = L::P;
   constexpr int NT = prep_threads<D>();
-  constexpr int RL = NT / D;                // lanes per matrix row
-  constexpr int NP = D / 4 / RL;            // 16-byte pieces per lane
+  constexpr int RL = 2 * NT / D;            // lanes per pair of matrix rows (j, j + D/2)
+  constexpr int NP = D / 4 / RL;            // 16-byte pieces per lane and row
   constexpr int NW = NT / 64;               // waves
-  static_assert(RL >= 1 && RL <= 64 && NP >= 1, "prep layout");
+  static_assert(RL >= 2 && RL <= 8 && NP >= 1, "prep layout");
   __shared__ __attribute__((aligned(16))) float qin[4][D];
   __shared__ float proj[4][D];
   __shared__ double beta[P];
@@ -244,17 +247,21 @@ __global__ __launch_bounds__(prep_threads<D>()) void logit_prep_kernel(PrepArgs 
   const int b = stream / a.n_kv_heads;
   const int kvh = stream % a.n_kv_heads;
   const int tid = threadIdx.x;
-  const int j = tid / RL;
-  const int pl = tid % RL;
+  const int j = tid / RL;                   // rows j and j + D/2: each staged
+  const int pl = tid % RL;                  // query read feeds two rows
 
   const float *mat = part == 0 ? a.pi : a.s_mat;
-  const f32x4 *mrow = (const f32x4 *)(mat + (size_t)j * D);
-  // d <= 128: the whole row slice is loaded before the first barrier; larger
-  // d streams it inside the loop (register budget)
+  const f32x4 *mrow0 = (const f32x4 *)(mat + (size_t)j * D);
+  const f32x4 *mrow1 = (const f32x4 *)(mat + (size_t)(j + D / 2) * D);
+  // d <= 128: the whole row slices are loaded before the first barrier;
+  // larger d streams them inside the loop (register budget)
   constexpr int PRE = D <= 128 ? NP : 1;
-  f32x4 row[PRE];
+  f32x4 row0[PRE], row1[PRE];
 #pragma unroll
-  for (int i = 0; i < PRE; ++i) row[i] = mrow[pl + RL * i];
+  for (int i = 0; i < PRE; ++i) {
+    row0[i] = mrow0[pl + RL * i];
+    row1[i] = mrow1[pl + RL * i];
+  }
 
   for (int i = tid; i < 4 * D; i += NT) {
     const int g = i / D, k = i % D;
@@ -279,16 +286,20 @@ __global__ __launch_bounds__(prep_threads<D>()) void logit_prep_kernel(PrepArgs 
   __syncthreads();
   // fp32 accumulation: the products are exact and the sums' rounding
   // (~1e-7 relative) is far below the logit tolerance.
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float acc0[4] = {0.0f, 0.0f, 0.0f, 0.0f}, acc1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll (D <= 128 ? NP : 4)
   for (int i = 0; i < NP; ++i) {
     const int k0 = 4 * (pl + RL * i);
-    const f32x4 m4 = D <= 128 ? row[i < PRE ? i : 0] : mrow[pl + RL * i];
+    const f32x4 m0 = D <= 128 ? row0[i < PRE ? i : 0] : mrow0[pl + RL * i];
+    const f32x4 m1 = D <= 128 ? row1[i < PRE ? i : 0] : mrow1[pl + RL * i];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const f32x4 qv = *(const f32x4 *)&qin[g][k0];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[g] = fmaf(m4[e], qv[e], acc[g]);
+      for (int e = 0; e < 4; ++e) {
+        acc0[g] = fmaf(m0[e], qv[e], acc0[g]);
+        acc1[g] = fmaf(m1[e], qv[e], acc1[g]);
+      }
     }
   }
   // full row sums in every lane of the row (quad permutes for the lanes of a
@@ -300,10 +311,16 @@ __global__ __launch_bounds__(prep_threads<D>()) void logit_prep_kernel(PrepArgs 
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
 #pragma unroll
-    for (int off = 1; off < RL; off <<= 1) acc[g] += xor_lanes(acc[g], off);
-    if (pl == 0) proj[g][j] = acc[g];
-    v[g] = fabsf(acc[g]);
-    v[4 + g] = pl == 0 ? acc[g] : 0.0f;
+    for (int off = 1; off < RL; off <<= 1) {
+      acc0[g] += xor_lanes(acc0[g], off);
+      acc1[g] += xor_lanes(acc1[g], off);
+    }
+    if (pl == 0) {
+      proj[g][j] = acc0[g];
+      proj[g][j + D / 2] = acc1[g];
+    }
+    v[g] = fmaxf(fabsf(acc0[g]), fabsf(acc1[g]));
+    v[4 + g] = pl == 0 ? acc0[g] + acc1[g] : 0.0f;
   }
   wave_fold<0xB1>(v);
   wave_fold<0x4E>(v);
