@@ -200,11 +200,10 @@ tq_status tq_attn_logits_workspace_size(const tq_params *p, int32_t batch, int32
  *                shape.  Needs seq_len >= topk.
  *   workspace    device scratch of tq_attn_logits_workspace_size bytes
  * GQA: query head h reads KV head h / (n_q_heads / n_kv_heads); n_q_heads
- * must be a multiple of n_kv_heads.  Dense logits support d in {128, 256},
- * up to 16 query heads per KV head, streams whose packed codes stay under
- * 2 GiB and whose logits (group x seq_len fp32) stay under 2 GiB; top-k
- * supports MSE mode, d in {128, 256}, topk <= 16, seq_len < 2^30.
- * (d = 64 keys are quantised and reconstructed but have no logit kernel.)
+ * must be a multiple of n_kv_heads.  Dense logits support d in {64, 128,
+ * 256}, up to 16 query heads per KV head, streams whose packed codes stay
+ * under 2 GiB and whose logits (group x seq_len fp32) stay under 2 GiB;
+ * top-k supports MSE mode, d in {64, 128, 256}, topk <= 16, seq_len < 2^30.
  * seq_len == 0 is a no-op.  A workspace smaller than the query's size, or
  * NULL where it is not 0, is TQ_ERR_INVALID; a misaligned one
  * TQ_ERR_UNSUPPORTED.
@@ -291,7 +290,7 @@ tq_status tq_append_attn_logits_paged(const tq_params *p, const void *x_new, int
  *                whose logits are all -inf, or seq_len == 0, gives o = 0.
  *   workspace    device scratch of tq_attn_output_workspace_size bytes (the
  *                per-split partial maxima, sums and accumulators)
- * Supported: MSE mode, d in {128, 256}, up to 16 query heads per KV head,
+ * Supported: MSE mode, d in {64, 128, 256}, up to 16 query heads per KV head,
  * 16-byte aligned value codes, packed values of one stream under 2 GiB.
  * Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED, TQ_ERR_HIP. */
 tq_status tq_attn_output(const tq_params *p, const float *logits, int32_t batch, int32_t n_q_heads,

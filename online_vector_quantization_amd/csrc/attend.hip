@@ -16,10 +16,11 @@
 //   takes the chunk maximum per head, rescales what it holds when the
 //   maximum rises, and stages the token's plane words and weights e n in LDS,
 //   transposed so that one 16-byte read gives four tokens.  Every lane then
-//   accumulates its coordinate pairs (one pair for d = 128, two for 256) over
-//   the chunk; a pair's two centroid values come from one read of a K^2-entry
-//   table.  The waves meet at the end and leave (max, sum e, accumulator) per
-//   head and split.
+//   accumulates its coordinate pairs (one pair for d = 128, two for 256; at
+//   d = 64 one pair over half the chunk's tokens, the two halves summed at
+//   the end) over the chunk; a pair's two centroid values come from one read
+//   of a K^2-entry table.  The waves meet at the end and leave (max, sum e,
+//   accumulator) per head and split.
 // * combine kernel: one workgroup per query head rescales the splits to the
 //   common maximum, divides by the total weight and applies Pi^T; every load
 //   it needs is issued before its first barrier.
@@ -108,15 +109,35 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// One token's packed row (RW words): 16-byte loads when the row is a whole
+// number of them, else (d = 64 at an odd bit width) 4- to 12-byte loads.
+template <int RW>
+__device__ __forceinline__ void load_row(i32x4 rc, uint32_t off, uint32_t (&out)[RW]) {
+  if constexpr (RW % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < RW / 4; ++i) {
+      const i32x4 v = tq_llvm_buf_ld_b128(rc, (int)(off + 16 * i), 0, 0);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) out[4 * i + k] = (uint32_t)v[k];
+    }
+  } else {
+    buf_load_words<RW, 0>(rc, off, out);
+  }
+}
+
 template <int D, int LB, int G>
 __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(PartArgs a) {
   constexpr int K = 1 << LB;
   constexpr int RB = LB * D / 8;          // packed bytes per token
   constexpr int RW = RB / 4;              // ... in words
-  constexpr int CPL = D / 64;             // coordinates per lane (2 or 4)
+  // d >= 128: every lane owns D / 64 coordinates and takes all the chunk's
+  // tokens; d = 64: lanes l and l + 32 own the same two coordinates and take
+  // the first and the second half of the chunk's tokens
+  constexpr int TH = D == 64 ? 2 : 1;     // token halves
+  constexpr int CPL = TH * D / 64;        // coordinates per lane (2 or 4)
   constexpr int NW = kAttThreads / 64;
   constexpr int CS = kChunk + 4;          // row stride of the transposed stage (words), padded against conflicts
-  static_assert(RB % 16 == 0 && CPL % 2 == 0, "layout");
+  static_assert(RB % 4 == 0 && CPL % 2 == 0 && CPL * 64 == TH * D, "layout");
   __shared__ float2 ptab[K * K];          // (c[i0], c[i1]) of a coordinate pair
   __shared__ __attribute__((aligned(16))) uint32_t cwt[NW][RW][CS];   // [word][token]
   __shared__ __attribute__((aligned(16))) float wtt[NW][G][CS];       // [head][token]
@@ -148,13 +169,12 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(PartArgs a)
 
   // Per chunk, lane l owns token c0 + l; past the split's end the codes read
   // as zeros and the token gets no weight.
-  i32x4 rw[RB / 16];
+  uint32_t rw[RW];
   float rl[G];
   uint16_t rnb = 0;
   auto load_chunk = [&](int c0) __attribute__((always_inline)) {
     const int t = c0 + l;
-#pragma unroll
-    for (int i = 0; i < RB / 16; ++i) rw[i] = tq_llvm_buf_ld_b128(rc, (int)((uint32_t)t * RB + 16 * i), 0, 0);
+    load_row<RW>(rc, (uint32_t)t * RB, rw);
     rnb = buf_load_u16<0>(rn, 2u * (uint32_t)t);
     const int tc = t < n_tok ? t : n_tok - 1;
 #pragma unroll
@@ -175,8 +195,10 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(PartArgs a)
   }
   __syncthreads();
 
-  const int grp = CPL * l / 32;           // coordinate group of this lane
-  const int boff = CPL * l % 32;          // bit of its first coordinate
+  const int lc = l % (64 / TH);           // coordinate slot of this lane
+  const int th = l / (64 / TH);           // its token half
+  const int grp = CPL * lc / 32;          // coordinate group of this lane
+  const int boff = CPL * lc % 32;         // bit of its first coordinate
   float acc[G][CPL];
   float esum[G], mrun[G];
 #pragma unroll
@@ -211,9 +233,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(PartArgs a)
     }
     const float n = f16_bits_to_f32(rnb);
 #pragma unroll
-    for (int i = 0; i < RB / 16; ++i)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) cwt[w][4 * i + k][l] = (uint32_t)rw[i][k];
+    for (int i = 0; i < RW; ++i) cwt[w][i][l] = rw[i];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       esum[g] += e[g];
@@ -223,9 +243,9 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(PartArgs a)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // accumulate the chunk, four tokens per LDS read
+    // accumulate the chunk (this lane's half of it), four tokens per LDS read
 #pragma unroll 2
-    for (int t4 = 0; t4 < kChunk / 4; ++t4) {
+    for (int t4 = th * (kChunk / 4 / TH); t4 < (th + 1) * (kChunk / 4 / TH); ++t4) {
       u32x4 pw[LB];
 #pragma unroll
       for (int p = 0; p < LB; ++p) pw[p] = *(const u32x4 *)&cwt[w][LB * grp + p][4 * t4];
@@ -277,14 +297,17 @@ __global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(PartArgs a)
     const float f = mrun[g] == -INFINITY ? 0.0f : __expf(mrun[g] - v);
     if (l == 0) reds[w][g] = esum[g] * f;
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) acc[g][i] *= f;
+    for (int i = 0; i < CPL; ++i) {
+      acc[g][i] *= f;
+      if constexpr (TH == 2) acc[g][i] += __shfl_xor(acc[g][i], 32, 64);   // the two token halves
+    }
   }
   for (int i = 0; i < NW; ++i) {
-    if (w == i) {
+    if (w == i && th == 0) {
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) accs[g][CPL * l + c] = (i == 0 ? 0.0f : accs[g][CPL * l + c]) + acc[g][c];
+        for (int c = 0; c < CPL; ++c) accs[g][CPL * lc + c] = (i == 0 ? 0.0f : accs[g][CPL * lc + c]) + acc[g][c];
     }
     __syncthreads();
   }
@@ -334,7 +357,8 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(PartArgs a) {
   constexpr int CS = kChunk + 4;
   constexpr int PQ = D / 8;              // words of pair bytes per token
   constexpr int PS = LB <= 3 ? 2 : 0;     // pair bytes hold idx * 4 when it fits
-  static_assert(G >= 4 && RB % 16 == 0, "layout");
+  constexpr int RW = RB / 4;              // packed words per token
+  static_assert(G >= 4 && RB % 4 == 0, "layout");
   __shared__ uint32_t tabh[K * K];        // hi of (c[i0], c[i1]) as an fp16 pair
   __shared__ uint32_t tabl[K * K];        // lo of the same
   // per wave: pair bytes [pair quad][token], then fp16 weights
@@ -371,13 +395,12 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(PartArgs a) {
   const i32x4 rc = make_rsrc(a.codes + row0 * RB, (uint32_t)n_tok * RB);
   const i32x4 rn = make_rsrc(a.norm + row0, (uint32_t)n_tok * 2u);
 
-  i32x4 rw[RB / 16];
+  uint32_t rw[RW];
   float rl[G];
   uint16_t rnb = 0;
   auto load_chunk = [&](int c0) __attribute__((always_inline)) {
     const int t = c0 + l;
-#pragma unroll
-    for (int i = 0; i < RB / 16; ++i) rw[i] = tq_llvm_buf_ld_b128(rc, (int)((uint32_t)t * RB + 16 * i), 0, 0);
+    load_row<RW>(rc, (uint32_t)t * RB, rw);
     rnb = buf_load_u16<0>(rn, 2u * (uint32_t)t);
     const int tc = t < n_tok ? t : n_tok - 1;
 #pragma unroll
@@ -458,7 +481,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(PartArgs a) {
 #pragma unroll
         for (int p = 0; p < LB; ++p) {
           const int wi = LB * j + p;
-          const uint32_t x = (uint32_t)rw[wi / 4][wi % 4];
+          const uint32_t x = rw[wi];
           const int sh = 2 * p + PS - 2 * o;              // where the pair's bits go
           const uint32_t y = sh >= 0 ? x << sh : x >> -sh;
           pb |= y & (0x03030303u << (2 * p + PS));
@@ -811,7 +834,7 @@ hipError_t launch_lb(int lb, const tqi::AttendArgs &a, hipStream_t s) {
 namespace tqi {
 
 bool attend_supported(int d, int lbits, int group, int64_t seq_len) {
-  if (d != 128 && d != 256) return false;
+  if (d != 64 && d != 128 && d != 256) return false;
   if (lbits < 1 || lbits > 4 || group < 1 || group > 16) return false;
   // 32-bit byte offsets within one split of the packed values (plus a chunk)
   const int64_t rb = (int64_t)lbits * d / 8;
@@ -827,6 +850,7 @@ size_t attend_workspace_bytes(int d, int lbits, int batch, int n_q_heads, int n_
 }
 
 hipError_t launch_attend(int d, int lbits, const AttendArgs &a, hipStream_t s) {
+  if (d == 64) return launch_lb<64>(lbits, a, s);
   if (d == 128) return launch_lb<128>(lbits, a, s);
   if (d == 256) return launch_lb<256>(lbits, a, s);
   return hipErrorInvalidValue;

@@ -76,22 +76,32 @@ struct Walsh {
   }
 };
 
+// K positions of the MFMA chunks.  Lane group kg (lanes 16 kg .. 16 kg + 15)
+// of chunk c of a plane holds the 16 coordinates 32 grp + 8 i + 4 hh + t
+// (i, t = 0..3) of 32-coordinate group grp, as bit hh 4 + t of byte i of the
+// group's plane word.  d >= 128: the four lane groups take four different
+// words and the chunk picks the nibble (hh = c & 1, grp = kg + 4 (c >> 1));
+// d = 64 (one chunk per plane): lanes kg and kg ^ 1 share word kg >> 1 and
+// split its nibbles (hh = kg & 1).
 template <int D, int LB, bool PROD>
 struct LLayout {
   static constexpr int P = Walsh<LB>::P;
   static constexpr int CPP = D / 64;                    // MFMA chunks per plane
   static constexpr int NCH = (P + (PROD ? 1 : 0)) * CPP;
   static constexpr int PB = D / 8;
+  static constexpr bool SPLIT = D == 64;                // lanes split a word's nibbles
+  __host__ __device__ static constexpr int half(int c, int kg) { return SPLIT ? (kg & 1) : (c & 1); }
+  __host__ __device__ static constexpr int group(int c, int kg) { return SPLIT ? (kg >> 1) : kg + 4 * (c >> 1); }
 };
 
 // Query preparation for one (stream, row tile, part): part 0 builds the
 // Walsh-plane chunks from q' = Pi q, part 1 the sign chunks from q'' = S q.
-// 512 threads; RL = 512 / D consecutive lanes share matrix row j and read
-// its 16-byte pieces p, p + RL, ... (coalesced), each for all four queries,
-// then combine their partial sums with xor shuffles.  fp64 arithmetic from
-// the fp32 matrix and the queries (exact in fp32).
+// NT threads (512; 256 at d = 64); RL = 2 NT / D consecutive lanes share the
+// matrix rows j and j + D/2 and read their 16-byte pieces p, p + RL, ...
+// (coalesced), each for all four queries, then combine their partial sums
+// with lane permutes.  The fixed-point weights are formed in fp64.
 template <int D>
-constexpr int prep_threads() { return 512; }
+constexpr int prep_threads() { return D >= 128 ? 512 : 256; }
 
 // A partner lane's v for sums over aligned groups of 2, 4 or 8 lanes: the
 // quad permutes [1,0,3,2] and [2,3,0,1], then the half-row mirror (lane i of
@@ -382,8 +392,8 @@ __global__ __launch_bounds__(prep_threads<D>()) void logit_prep_kernel(PrepArgs 
   }
   // A-operand chunks of this part.  Lane l = 16 kg + 4 g + piece supplies
   // row (query g, byte piece); its byte e = 4 t + i pairs with coordinate
-  // 32 (kg + 4 q) + 8 i + 4 h + t, whose key byte carries weight 2^(4 h + t)
-  // (see the kernel comment).  One thread per (chunk, kg, g, t) computes
+  // 32 grp + 8 i + 4 hh + t (LLayout), whose key byte carries weight
+  // 2^(4 hh + t) (see the kernel comment).  One thread per (chunk, kg, g, t) computes
   // the 32-bit fixed-point weights of bytes 4 t .. 4 t + 3 and writes word t
   // of the four piece rows.
   int8_t *tab = a.table + ((int64_t)stream * a.row_tiles + rt) * (L::NCH * 64 * 16);
@@ -392,14 +402,14 @@ __global__ __launch_bounds__(prep_threads<D>()) void logit_prep_kernel(PrepArgs 
   for (int i = c_begin * 64 + tid; i < c_end * 64; i += NT) {
     const int cidx = i / 64, kg = (i >> 4) & 3, g = (i >> 2) & 3, t = i & 3;
     const int r = cidx / L::CPP, c = cidx % L::CPP;
-    const int q = c >> 1, hh = c & 1;
+    const int hh = L::half(c, kg), grp = L::group(c, kg);
     const double wgt = part == 0 ? beta[r < P ? r : 0] : 1.0;
     const bool live = 4 * rt + g < a.group;
     const int s = 4 * hh + t;
     uint32_t e[4];                           // [ib]: the four digits of weight ib
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib) {
-      const int j = 32 * (kg + 4 * q) + 8 * ib + 4 * hh + t;
+      const int j = 32 * grp + 8 * ib + 4 * hh + t;
       int n = (int)rint(ldexp(wgt * (double)proj[g][j], fexp[g] - s));
       if (s == 7) n = -n;
       if (!live) n = 0;
@@ -469,7 +479,7 @@ __global__ __launch_bounds__(256) void logit_kernel(StreamArgs a) {
   constexpr int PB = L::PB;
   constexpr int NPL = LB + (PROD ? 1 : 0);  // planes per record (sign on top)
   constexpr int RB = NPL * PB;              // bytes per packed row
-  constexpr int NQ = D / 128;            // plane words per lane and plane
+  constexpr int NQ = D >= 128 ? D / 128 : 1;   // plane words per lane and plane
   constexpr int U = kLogitGroups;     // 16-token groups per wave and iteration
   constexpr int NB = U / 4;              // 64-token norm blocks per iteration
   static_assert(U % 4 == 0, "groups come in fours (64 tokens)");
@@ -489,6 +499,8 @@ __global__ __launch_bounds__(256) void logit_kernel(StreamArgs a) {
   const int l = lane_id();
   const int n = l & 15;
   const int kg = l >> 4;
+  // byte masks of the four B dwords at d = 64, where the nibble is per lane
+  const uint32_t msplit = 0x01010101u << (4 * L::half(0, kg));
 
   i32x4 areg[RT][NCH];
 #pragma unroll
@@ -525,8 +537,9 @@ __global__ __launch_bounds__(256) void logit_kernel(StreamArgs a) {
   const uint32_t t_end32 = nvalid;
 
   // Lane (n, kg) reads, for token n of each group, the NPL plane words of
-  // 32-coordinate group kg + 4 qd (one contiguous load: 16 bytes at b = 4);
-  // lane l reads the two fp16 scalars of token l of each 64-token block.
+  // its 32-coordinate group of chunk pair qd (one contiguous load: 16 bytes
+  // at b = 4); lane l reads the two fp16 scalars of token l of each 64-token
+  // block.
   auto load = [&](uint32_t tok0, KeyGroup<NPL, NQ>(&kgp)[U], NormBlock(&nb)[NB]) {
     // first row of the wave's 64 tokens (one page holds all of them)
     uint32_t row0 = tok0;
@@ -541,13 +554,25 @@ __global__ __launch_bounds__(256) void logit_kernel(StreamArgs a) {
       const uint32_t tok = row0 + 16 * u + n;
 #pragma unroll
       for (int qd = 0; qd < NQ; ++qd)
-        buf_load_words<NPL>(rc, tok * RB + 4 * NPL * (kg + 4 * qd), kgp[u].w[qd]);
+        buf_load_words<NPL>(rc, tok * RB + 4 * NPL * L::group(2 * qd, kg), kgp[u].w[qd]);
     }
 #pragma unroll
     for (int q = 0; q < NB; ++q) {
       const uint32_t tok = row0 + 64 * q + l;
       nb[q].n = buf_load_u16(rn, 2 * tok);
       if constexpr (PROD) nb[q].g = buf_load_u16(rg, 2 * tok);
+    }
+  };
+
+  // B operand of chunk c from a plane word: dword t keeps bit 4 hh + t of
+  // each byte (byte value 2^(4 hh + t) * bit)
+  auto expand = [&](uint32_t x, int c) -> i32x4 {
+    if constexpr (L::SPLIT) {
+      return {(int)(x & msplit), (int)(x & (msplit << 1)), (int)(x & (msplit << 2)), (int)(x & (msplit << 3))};
+    } else {
+      const int sh = 4 * (c & 1);
+      return {(int)(x & (0x01010101u << sh)), (int)(x & (0x01010101u << (sh + 1))),
+              (int)(x & (0x01010101u << (sh + 2))), (int)(x & (0x01010101u << (sh + 3)))};
     }
   };
 
@@ -566,9 +591,7 @@ __global__ __launch_bounds__(256) void logit_kernel(StreamArgs a) {
 #pragma unroll
           for (int p = 0; p < LB; ++p)
             if (sub & (1 << p)) x ^= kgp[u].w[c >> 1][p];
-          const int sh = 4 * (c & 1);
-          const i32x4 bv = {(int)(x & (0x01010101u << sh)), (int)(x & (0x01010101u << (sh + 1))),
-                            (int)(x & (0x01010101u << (sh + 2))), (int)(x & (0x01010101u << (sh + 3)))};
+          const i32x4 bv = expand(x, c);
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) am[rt] = mfma_i8(areg[rt][r * CPP + c], bv, am[rt]);
         }
@@ -576,10 +599,7 @@ __global__ __launch_bounds__(256) void logit_kernel(StreamArgs a) {
       if constexpr (PROD) {
 #pragma unroll
         for (int c = 0; c < CPP; ++c) {
-          const uint32_t x = kgp[u].w[c >> 1][LB];
-          const int sh = 4 * (c & 1);
-          const i32x4 bv = {(int)(x & (0x01010101u << sh)), (int)(x & (0x01010101u << (sh + 1))),
-                            (int)(x & (0x01010101u << (sh + 2))), (int)(x & (0x01010101u << (sh + 3)))};
+          const i32x4 bv = expand(kgp[u].w[c >> 1][LB], c);
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) aq[rt] = mfma_i8(areg[rt][P * CPP + c], bv, aq[rt]);
         }
@@ -763,7 +783,7 @@ hipError_t launch_lb(int lb, const tqi::LogitArgs &a, hipStream_t s) {
 namespace tqi {
 
 bool logits_supported(int d, int lbits, bool prod, int group, int64_t seq_len) {
-  if (d != 128 && d != 256) return false;
+  if (d != 64 && d != 128 && d != 256) return false;
   if (lbits < 1 || lbits > 4 || group < 1 || group > 16) return false;
   // The streaming kernel addresses one stream's codes with 32-bit byte
   // offsets, and its prefetch runs up to one block stride (<= seq_len + 255
@@ -783,6 +803,7 @@ size_t logits_workspace_bytes(int d, int lbits, bool prod, int64_t n_streams, in
 }
 
 hipError_t launch_logits(int d, int lbits, bool prod, const LogitArgs &a, hipStream_t s) {
+  if (d == 64) return prod ? launch_lb<64, true>(lbits, a, s) : launch_lb<64, false>(lbits, a, s);
   if (d == 128) return prod ? launch_lb<128, true>(lbits, a, s) : launch_lb<128, false>(lbits, a, s);
   if (d == 256) return prod ? launch_lb<256, true>(lbits, a, s) : launch_lb<256, false>(lbits, a, s);
   return hipErrorInvalidValue;

@@ -164,8 +164,11 @@ __device__ __forceinline__ uint32_t spread2(uint32_t x) {
   if constexpr (NP == 8) {
     x &= 0xFFFFu;
     x = (x | (x << 8)) & 0x00FF00FFu;
-  } else {
+  } else if constexpr (NP == 4) {
     x &= 0xFFu;
+  } else {
+    static_assert(NP == 2, "pairs per thread");
+    x &= 0xFu;
   }
   x = (x | (x << 4)) & 0x0F0F0F0Fu;
   x = (x | (x << 2)) & 0x33333333u;
@@ -196,10 +199,15 @@ __device__ __forceinline__ void decode_pairs(const uint32_t (&pw)[LB], int c, co
     hw[k] = tab[pidx];
     lw[k] = tab[KK + pidx];
   }
+  if constexpr (NP == 2) {                 // d = 64: four coordinates
+    *(uint2 *)hrow = make_uint2(hw[0], hw[1]);
+    *(uint2 *)lrow = make_uint2(lw[0], lw[1]);
+  } else {
 #pragma unroll
-  for (int k = 0; k < NP; k += 4) {
-    *(uint4 *)(hrow + 2 * k) = make_uint4(hw[k], hw[k + 1], hw[k + 2], hw[k + 3]);
-    *(uint4 *)(lrow + 2 * k) = make_uint4(lw[k], lw[k + 1], lw[k + 2], lw[k + 3]);
+    for (int k = 0; k < NP; k += 4) {
+      *(uint4 *)(hrow + 2 * k) = make_uint4(hw[k], hw[k + 1], hw[k + 2], hw[k + 3]);
+      *(uint4 *)(lrow + 2 * k) = make_uint4(lw[k], lw[k + 1], lw[k + 2], lw[k + 3]);
+    }
   }
 }
 
@@ -646,7 +654,7 @@ hipError_t launch_lb(int lb, const tqi::SearchArgs &a, hipStream_t s) {
 namespace tqi {
 
 bool search_supported(int d, int lbits, int topk, int batch, int n_q_heads, int n_kv_heads, int64_t seq_len) {
-  if (d != 128 && d != 256) return false;
+  if (d != 64 && d != 128 && d != 256) return false;
   if (lbits < 1 || lbits > 4 || topk < 1 || topk > kTop) return false;
   if (seq_len >= (1LL << 30)) return false;        // key index in 30 bits of a list entry
   // per-split byte offsets of the packed codes (one split plus one tile of
@@ -661,6 +669,7 @@ size_t search_workspace_bytes(int d, int lbits, int batch, int n_q_heads, int n_
 }
 
 hipError_t launch_search(int d, int lbits, const SearchArgs &a, hipStream_t s) {
+  if (d == 64) return launch_lb<64>(lbits, a, s);
   if (d == 128) return launch_lb<128>(lbits, a, s);
   if (d == 256) return launch_lb<256>(lbits, a, s);
   return hipErrorInvalidValue;

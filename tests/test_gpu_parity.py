@@ -158,6 +158,11 @@ LOGIT_CASES = [
     (128, 3, "prod", 1, 1, 13, 300, "f32"),
     (256, 2, "mse", 1, 1, 4, 1100, "f32"),
     (256, 3, "prod", 1, 2, 4, 777, "bf16"),
+    (64, 3, "prod", 1, 2, 4, 1300, "bf16"),
+    (64, 5, "prod", 1, 1, 6, 517, "f32"),
+    (64, 2, "prod", 2, 1, 16, 640, "bf16"),
+    (64, 1, "mse", 1, 2, 1, 999, "f32"),
+    (64, 4, "mse", 1, 1, 12, 2000, "bf16"),
 ]
 
 
@@ -242,6 +247,37 @@ def test_search_parity(tq, bits):
         diff = set(idx[r].tolist()) ^ set(oi[r].tolist())
         for i in diff:
             assert abs(scores[r, i] - ov[r, -1]) <= tol, (r, i)
+
+
+@pytest.mark.parametrize("d,bits", [(64, 3), (64, 1), (128, 4)])
+def test_search_parity_gqa(tq, d, bits):
+    """Top-k over two KV heads of 3001 keys each (a ragged last tile), 40
+    query heads per KV head, at d = 64 and 128."""
+    hkv, group, n_db, k = 2, 40, 3001, 10
+    rng = np.random.default_rng(d + bits)
+    scales = np.exp(0.5 * rng.standard_normal((hkv, d)))
+    db = rng.standard_normal((hkv, n_db, d)) * scales[:, None, :]
+    qv = (rng.standard_normal((hkv * group, d)) * np.repeat(scales, group, axis=0)).astype(np.float32)
+    ot = OracleTables(d, bits, oqz.MODE_MSE)
+    ref = ot.quantize(db.reshape(-1, d))
+    qz = tq.Quantizer(d, bits, oqz.MODE_MSE, seed=0, device=DEV)
+    cache = cache_from_oracle(tq, ref, d, bits, oqz.MODE_MSE, DEV)
+    qt = torch.from_numpy(qv.reshape(1, hkv * group, d)).to(DEV)
+    vals, idx = qz.search(qt, cache, n_kv_heads=hkv, seq_len=n_db, topk=k)
+    vals, idx = vals.cpu().numpy()[0], idx.cpu().numpy()[0]
+    for h in range(hkv):
+        sl = slice(h * n_db, (h + 1) * n_db)
+        qq = qv[h * group:(h + 1) * group].astype(np.float64)
+        scores = oqz.logits_rotated(qq, ref["codes"][sl], ref["norm"][sl], ot.pi, ot.c, oqz.MODE_MSE, 1.0)
+        ov, oi = oqz.topk(scores, k)
+        for r in range(group):
+            row = h * group + r
+            got = scores[r, idx[row]]
+            assert np.all(np.abs(vals[row] - got) <= 1e-4 * np.maximum(np.abs(got), 1e-3)), row
+            assert np.all(np.diff(vals[row]) <= 1e-6)
+            tol = 1e-4 * max(abs(ov[r, -1]), 1e-3)
+            for i in set(idx[row].tolist()) ^ set(oi[r].tolist()):
+                assert abs(scores[r, i] - ov[r, -1]) <= tol, (row, i)
 
 
 @pytest.mark.parametrize("scale", [1.0, -0.5, 0.0])
@@ -333,6 +369,10 @@ ATTN_CASES = [  # d, bits, batch, n_kv_heads, group, seq_len, extra row capacity
     (128, 1, 1, 2, 2, 1, 0),         # a single token
     (256, 2, 1, 1, 16, 700, 3),      # padded search width, the largest GQA group
     (256, 4, 2, 1, 3, 2100, 0),      # group padded to 4
+    (64, 3, 1, 2, 2, 1500, 2),       # d = 64: two token halves per lane, 24-byte rows
+    (64, 1, 2, 1, 1, 70, 0),         # d = 64, 8-byte rows, a chunk and a partial one
+    (64, 4, 1, 1, 6, 3000, 0),       # d = 64 on the matrix-core kernel, group padded to 8
+    (64, 3, 1, 3, 16, 999, 1),       # d = 64, the largest group, odd bit width
 ]
 
 
@@ -394,6 +434,8 @@ APPEND_CASES = [
     (128, 1, "mse", 1, 3, 1, 70, 33, "bf16", "bf16"),
     (256, 3, "prod", 1, 1, 4, 513, 512, "bf16", "f32"),
     (256, 2, "mse", 1, 2, 8, 257, 100, "f32", "f32"),
+    (64, 3, "prod", 2, 2, 4, 400, 399, "bf16", "bf16"),
+    (64, 3, "mse", 1, 3, 2, 129, 64, "f32", "bf16"),
 ]
 
 
@@ -553,6 +595,7 @@ PAGED_CASES = [
     (128, 4, "prod", 1, 2, 4, 256, 2049, 2048, "f32"),
     (128, 2, "mse", 2, 2, 2, 128, 700, 300, "bf16"),
     (256, 2, "mse", 1, 1, 4, 64, 300, 0, "f32"),
+    (64, 4, "prod", 2, 2, 8, 64, 650, 649, "bf16"),
 ]
 
 
