@@ -31,23 +31,28 @@ struct DLayout {
   static constexpr int TPV = D / 16;
 };
 
-// B fragments of columns [32w, 32w+32) of a d x d matrix (B[k][n] = mat[k][32w+n]).
+// B fragment for K step s of columns [32w, 32w+32) of a d x d matrix
+// (B[k][n] = mat[k][32w+n]), as fp16 hi + lo of the entries scaled by 2^8.
 template <int D>
-__device__ void load_columns(const float *__restrict__ mat, int w, half8 (&hi)[D / 16],
-                             half8 (&lo)[D / 16]) {
+__device__ __forceinline__ void column_fragment(const float *__restrict__ mat, int w, int s, half8 &hi,
+                                                half8 &lo) {
   const int l = lane_id();
   const int col = 32 * w + (l & 31);
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int k = 16 * s + 8 * (l >> 5) + i;
-      const float sv = mat[(size_t)k * D + col] * kMatScale;
-      const _Float16 h = (_Float16)sv;
-      hi[s][i] = h;
-      lo[s][i] = (_Float16)(sv - (float)h);
-    }
+  for (int i = 0; i < 8; ++i) {
+    const int k = 16 * s + 8 * (l >> 5) + i;
+    const float sv = mat[(size_t)k * D + col] * kMatScale;
+    const _Float16 h = (_Float16)sv;
+    hi[i] = h;
+    lo[i] = (_Float16)(sv - (float)h);
   }
+}
+
+template <int D>
+__device__ void load_columns(const float *__restrict__ mat, int w, half8 (&hi)[D / 16],
+                             half8 (&lo)[D / 16]) {
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) column_fragment<D>(mat, w, s, hi[s], lo[s]);
 }
 
 // Raw inputs of one decoding thread (16 coordinates of one vector): the
@@ -110,8 +115,11 @@ __global__ __launch_bounds__(DLayout<D>::NT) void dequant_kernel(tqi::DequantArg
 
   half8 ph[L::KS], pl[L::KS];
   load_columns<D>(a.pi, w, ph, pl);
-  half8 sh[PROD ? L::KS : 1], sl[PROD ? L::KS : 1];
-  if constexpr (PROD) load_columns<D>(a.s_mat, w, sh, sl);
+  // inner-product mode: S's columns stationary too, except at d = 256, where
+  // they do not fit beside Pi's and are read (from L2) per tile
+  constexpr bool HOLD_S = PROD && D <= 128;
+  half8 sh[HOLD_S ? L::KS : 1], sl[HOLD_S ? L::KS : 1];
+  if constexpr (HOLD_S) load_columns<D>(a.s_mat, w, sh, sl);
   if constexpr (POLAR) {
     if (tid < 16) {
       const double ph = 2.0 * M_PI * (tid + 0.5) / 16.0;
@@ -287,10 +295,21 @@ __global__ __launch_bounds__(DLayout<D>::NT) void dequant_kernel(tqi::DequantArg
         accp[s & 1] = mfma32(ah, pl[s], accp[s & 1]);
       }
       accp[s & 1] = mfma32(ah, ph[s], accp[s & 1]);
-      if constexpr (PROD) {
+      if constexpr (HOLD_S) {
         const half8 as = *(const half8 *)&sg[m * L::PITCH + 16 * s + 8 * h];
         if constexpr (SPLIT) acc2 = mfma32(as, sl[s], acc2);
         acc2 = mfma32(as, sh[s], acc2);
+      }
+    }
+    if constexpr (PROD && !HOLD_S) {
+      // a few K steps' fragments in flight at a time
+#pragma unroll 2
+      for (int s = 0; s < L::KS; ++s) {
+        half8 bh, bl;
+        column_fragment<D>(a.s_mat, w, s, bh, bl);
+        const half8 as = *(const half8 *)&sg[m * L::PITCH + 16 * s + 8 * h];
+        if constexpr (SPLIT) acc2 = mfma32(as, bl, acc2);
+        acc2 = mfma32(as, bh, acc2);
       }
     }
     const f32x16 acc = accp[0] + accp[1];
@@ -394,7 +413,8 @@ hipError_t launch_dequant(int d, int lbits, bool prod, const DequantArgs &a, hip
                            : launch_lb<64, false>(lbits, a, s, supported);
   if (d == 128) return prod ? launch_lb<128, true>(lbits, a, s, supported)
                             : launch_lb<128, false>(lbits, a, s, supported);
-  if (d == 256 && !prod) return launch_lb<256, false>(lbits, a, s, supported);
+  if (d == 256) return prod ? launch_lb<256, true>(lbits, a, s, supported)
+                            : launch_lb<256, false>(lbits, a, s, supported);
   return hipSuccess;
 }
 

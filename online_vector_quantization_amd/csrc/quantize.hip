@@ -28,7 +28,9 @@
 //   stationary M slice; sign masks are ballots of z >= 0 and become the top
 //   bit plane of each coordinate's record.
 // * Two kernels share those steps.  quantize_kernel (MSE mode, and d = 256):
-//   D/32 waves, each tile staged, rotated and coded by the same waves.
+//   D/32 waves, each tile staged, rotated and coded by the same waves (at
+//   d = 256 in inner-product mode the M slice does not fit beside Pi's, so
+//   its fragments are read from L2 and split per tile).
 //   quantize_pc_kernel (inner-product mode, d <= 128): D/32 "producer" waves
 //   hold Pi and rotate + code tile k, D/32 "sketch" waves hold M and run the
 //   QJL projection of tile k-1, D/32 "stage" waves stage tile k+1 and take
@@ -69,27 +71,35 @@ struct QFormat {
   static constexpr int RB = NPL * D / 8;             // bytes per packed row
 };
 
-// Load this lane's B fragments (hi, lo) of rows [32w, 32w+32) of a d x d
-// fp32 matrix scaled by 2^8: lane l holds row 32w + l%32, columns
-// 16s + 8(l/32) + 0..7 for K step s.
+// This lane's B fragment (hi, lo) for K step s of rows [32w, 32w+32) of a
+// d x d fp32 matrix scaled by 2^8: lane l holds row 32w + l%32, columns
+// 16s + 8(l/32) + 0..7.
+template <int D>
+__device__ __forceinline__ const float *fragment_row(const float *__restrict__ mat, int w) {
+  const int l = lane_id();
+  return mat + (size_t)(32 * w + (l & 31)) * D + 8 * (l >> 5);
+}
+
+__device__ __forceinline__ void split_fragment(const float *row, int s, half8 &hi, half8 &lo) {
+  const f32x4 v0 = *(const f32x4 *)(row + 16 * s);
+  const f32x4 v1 = *(const f32x4 *)(row + 16 * s + 4);
+  const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float sv = v[i] * kPiScale;
+    const _Float16 h = (_Float16)sv;
+    hi[i] = h;
+    lo[i] = (_Float16)(sv - (float)h);
+  }
+}
+
+// All K steps' fragments, held in VGPRs for the whole launch.
 template <int D>
 __device__ void load_stationary(const float *__restrict__ mat, int w, half8 (&hi)[D / 16],
                                 half8 (&lo)[D / 16]) {
-  const int l = lane_id();
-  const float *row = mat + (size_t)(32 * w + (l & 31)) * D + 8 * (l >> 5);
+  const float *row = fragment_row<D>(mat, w);
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    f32x4 v0 = *(const f32x4 *)(row + 16 * s);
-    f32x4 v1 = *(const f32x4 *)(row + 16 * s + 4);
-    float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float sv = v[i] * kPiScale;
-      _Float16 h = (_Float16)sv;
-      hi[s][i] = h;
-      lo[s][i] = (_Float16)(sv - (float)h);
-    }
-  }
+  for (int s = 0; s < D / 16; ++s) split_fragment(row, s, hi[s], lo[s]);
 }
 
 // Reductions over the N = 4, 8 or 16 consecutive lanes that share a vector,
@@ -409,6 +419,28 @@ __device__ __forceinline__ uint32_t sign_words(const _Float16 *rh, const _Float1
   return sign_bits(sketch_tile<D>(rh, rl, mh, ml, m, h));
 }
 
+// The same product with M's fragments read (from L2) and split per tile
+// instead of held: for d = 256, where the Pi and M slices together would
+// take every VGPR of a wave.
+template <int D>
+__device__ __forceinline__ uint32_t sign_words_streamed(const _Float16 *rh, const _Float16 *rl,
+                                                        const float *__restrict__ mat, int w, int m, int h) {
+  using L = QLayout<D>;
+  const float *row = fragment_row<D>(mat, w);
+  f32x16 acc = {};
+#pragma unroll 2
+  for (int s = 0; s < L::KS; ++s) {
+    half8 bh, bl;
+    split_fragment(row, s, bh, bl);
+    const half8 ah = *(const half8 *)&rh[m * L::PITCH + 16 * s + 8 * h];
+    const half8 al = *(const half8 *)&rl[m * L::PITCH + 16 * s + 8 * h];
+    acc = mfma32(al, bh, acc);
+    acc = mfma32(ah, bl, acc);
+    acc = mfma32(ah, bh, acc);
+  }
+  return sign_bits(acc);
+}
+
 // Sign words into the top plane of group wq (lanes 0..31; zero vectors get
 // all signs +1).
 template <int D, int LB>
@@ -492,8 +524,11 @@ __global__ __launch_bounds__(QLayout<D>::NT) void quantize_kernel(tqi::QuantizeA
 
   half8 pih[L::KS], pil[L::KS];
   load_stationary<D>(a.pi, w, pih, pil);
-  half8 mh[PROD ? L::KS : 1], ml[PROD ? L::KS : 1];
-  if constexpr (PROD) load_stationary<D>(a.m, w, mh, ml);
+  // inner-product mode: M's slice stationary too, except at d = 256 (read
+  // per tile, see sign_words_streamed)
+  constexpr bool HOLD_M = PROD && D <= 128;
+  half8 mh[HOLD_M ? L::KS : 1], ml[HOLD_M ? L::KS : 1];
+  if constexpr (HOLD_M) load_stationary<D>(a.m, w, mh, ml);
 
   float bnd[K - 1];
 #pragma unroll
@@ -532,7 +567,11 @@ __global__ __launch_bounds__(QLayout<D>::NT) void quantize_kernel(tqi::QuantizeA
     store_planes<D, LB, PROD>(res.rc, outw, base, a.n_vec, true, w, l);
     if constexpr (PROD) {
       __syncthreads();
-      const uint32_t sw = sign_words<D>(rh[buf], rl[buf], mh, ml, m, h);
+      uint32_t sw;
+      if constexpr (HOLD_M)
+        sw = sign_words<D>(rh[buf], rl[buf], mh, ml, m, h);
+      else
+        sw = sign_words_streamed<D>(rh[buf], rl[buf], a.m, w, m, h);
       store_signs<D, LB>(res.rc, sw, vinv[buf], base, a.n_vec, true, w, l);
       const float gam = residual_norm<D>(rh[buf], rl[buf], vinv[buf], sv_v, sv_c);
       buf_store_u16<kWriteBack>(res.rr, (sv_c == 0 && base + sv_v < a.n_vec) ? (uint32_t)(2 * (base + sv_v)) : kNoStore,
@@ -899,7 +938,8 @@ hipError_t launch_quantize(int d, int lbits, bool prod, bool in_f32, const Quant
                            : launch_lb<64, false>(lbits, in_f32, a, s, supported);
   if (d == 128) return prod ? launch_lb<128, true>(lbits, in_f32, a, s, supported)
                             : launch_lb<128, false>(lbits, in_f32, a, s, supported);
-  if (d == 256 && !prod) return launch_lb<256, false>(lbits, in_f32, a, s, supported);
+  if (d == 256) return prod ? launch_lb<256, true>(lbits, in_f32, a, s, supported)
+                            : launch_lb<256, false>(lbits, in_f32, a, s, supported);
   return hipSuccess;
 }
 

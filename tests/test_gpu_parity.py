@@ -62,7 +62,8 @@ NONFINITE_ROWS = [19, 23]
 QUANT_CASES = [(128, b, "mse", dt) for b in (1, 2, 3, 4) for dt in ("bf16", "f32")] + \
               [(128, b, "prod", dt) for b in (2, 3, 4, 5) for dt in ("bf16", "f32")] + \
               [(64, 3, "mse", "bf16"), (64, 3, "prod", "bf16"), (64, 5, "prod", "f32"),
-               (256, 2, "mse", "f32"), (256, 4, "mse", "f32"), (256, 3, "mse", "bf16")]
+               (256, 2, "mse", "f32"), (256, 4, "mse", "f32"), (256, 3, "mse", "bf16"),
+               (256, 3, "prod", "bf16"), (256, 5, "prod", "f32"), (256, 2, "prod", "bf16")]
 
 
 @pytest.mark.parametrize("d,bits,mode,dtype", QUANT_CASES)
@@ -103,14 +104,14 @@ def test_quantize_parity(tq, d, bits, mode, dtype):
         assert cache.rnorm.cpu().numpy()[off + 3] == 0
 
 
-@pytest.mark.parametrize("mode", ["prod", "mse"])
-def test_quantize_parity_several_tiles_per_workgroup(tq, mode):
+@pytest.mark.parametrize("d,mode", [(128, "prod"), (128, "mse"), (256, "prod")])
+def test_quantize_parity_several_tiles_per_workgroup(tq, d, mode):
     """Every output against the oracle when each workgroup of the persistent
     grid loops over several tiles (at least four per workgroup at up to three
     workgroups per CU, plus a ragged tail), so the kernels' buffer rotation
     wraps several times."""
     mcode = oqz.MODE_PROD if mode == "prod" else oqz.MODE_MSE
-    d, bits = 128, 3
+    bits = 3
     n = 4 * 32 * 3 * torch.cuda.get_device_properties(DEV).multi_processor_count + 17
     xb = _keys_bf16(d, n, seed=5)
     x64 = _special_rows(bf16_to_f32(xb).astype(np.float64))
@@ -202,7 +203,8 @@ def test_logits_row_tokens_capacity(tq):
 
 
 DEQ_CASES = [(128, b, "mse") for b in (1, 2, 3, 4)] + [(128, b, "prod") for b in (2, 3, 4, 5)] + \
-            [(64, 3, "mse"), (64, 4, "prod"), (256, 2, "mse"), (256, 4, "mse")]
+            [(64, 3, "mse"), (64, 4, "prod"), (256, 2, "mse"), (256, 4, "mse"), (256, 3, "prod"),
+             (256, 5, "prod")]
 
 
 @pytest.mark.parametrize("d,bits,mode", DEQ_CASES)

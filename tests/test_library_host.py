@@ -118,11 +118,16 @@ def test_device_calls_validate_before_launch(tq):
     # misaligned input rows are refused, not read
     assert lib.tq_quantize_kv(ctypes.byref(p), ctypes.c_void_p(18), 1, 4, 128, ctypes.byref(pk), 0,
                               None) == tq.TQ_ERR_UNSUPPORTED
-    # d without a kernel (prod at d = 256) is reported before any launch
-    p256 = tq.Params(256, 3, tq.MODE_PROD, 0, dummy, dummy, dummy, dummy, dummy)
+    # a d without kernels (96: neither 64, 128 nor 256) is reported before any launch
     pk2 = tq.Packed(dummy, dummy, dummy)
-    assert lib.tq_quantize_kv(ctypes.byref(p256), dummy, 0, 1, 256, ctypes.byref(pk2), 0,
-                              None) == tq.TQ_ERR_UNSUPPORTED
+    for mode in (tq.MODE_MSE, tq.MODE_PROD):
+        p96 = tq.Params(96, 3, mode, 0, dummy, dummy, dummy, dummy, dummy)
+        assert lib.tq_quantize_kv(ctypes.byref(p96), dummy, 0, 1, 96, ctypes.byref(pk2), 0,
+                                  None) == tq.TQ_ERR_UNSUPPORTED
+        assert lib.tq_dequantize(ctypes.byref(p96), ctypes.byref(pk2), 1, dummy, 0,
+                                 None) == tq.TQ_ERR_UNSUPPORTED
+        assert lib.tq_attn_logits(ctypes.byref(p96), dummy, 0, 1, 4, 1, ctypes.byref(pk2), 64, 64, f, dummy,
+                                  0, None, ws, big, None) == tq.TQ_ERR_UNSUPPORTED
 
 
 def test_polar_codebooks_match_oracle():
