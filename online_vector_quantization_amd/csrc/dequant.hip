@@ -6,12 +6,16 @@
 // Layout mirrors the quantiser: D/32 waves, wave w owns output columns
 // [32w, 32w+32) and keeps its columns of Pi (and S) in VGPRs as fp16 hi + lo
 // (scaled by 2^8).  Each 32-vector tile is decoded once into LDS: the
-// centroid of every coordinate as fp16 hi + lo (scaled by 2^10) and, in
-// inner-product mode, the sign as an exact fp16 +-1.  Products run on the
-// 32x32x16 fp16 MFMA with fp32 accumulation; the output tile has one column
-// per lane, so each register row is a coalesced 128-byte store.  For bf16
-// output one fp16 product (hi x hi, about 2^-11 relative per element) meets
-// the output precision, so the lo halves are skipped.
+// centroid of every coordinate as fp16 hi + lo (scaled by 2^10), two
+// coordinates per read of a K^2-entry pair table, and, in inner-product
+// mode, the sign as an exact fp16 +-1.  Products run on the 32x32x16 fp16
+// MFMA with fp32 accumulation, with the matrix as the A operand, so that a
+// lane's accumulators are 16 coordinates (four runs of four) of one vector:
+// the per-vector factor is one value per lane, and each run goes to the
+// LDS output tile as one 8-byte (bf16) or 16-byte (fp32) write, from which
+// whole rows leave as 16-byte stores.  For bf16 output one fp16 product
+// (hi x hi, about 2^-11 relative per element) meets the output precision, so
+// the lo halves are skipped.
 #include "tq_device.h"
 #include "tq_internal.h"
 
@@ -30,6 +34,18 @@ struct DLayout {
   static constexpr int PITCH = D + 8;
   static constexpr int TPV = D / 16;
 };
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// The 16 low bits of x (one plane of 16 coordinates) with bit pair k
+// (coordinates 2k and 2k + 1) moved to bits 4k and 4k + 1.
+__device__ __forceinline__ uint32_t spread_pairs(uint32_t x) {
+  x &= 0xFFFFu;
+  x = (x | (x << 8)) & 0x00FF00FFu;
+  x = (x | (x << 4)) & 0x0F0F0F0Fu;
+  x = (x | (x << 2)) & 0x33333333u;
+  return x;
+}
 
 // B fragment for K step s of columns [32w, 32w+32) of a d x d matrix
 // (B[k][n] = mat[k][32w+n]), as fp16 hi + lo of the entries scaled by 2^8.
@@ -87,6 +103,8 @@ __global__ __launch_bounds__(DLayout<D>::NT) void dequant_kernel(tqi::DequantArg
   constexpr int TILE = 32 * L::PITCH;
   constexpr int OSZ = OUT_F32 ? 4 : 2;      // bytes per output element
   constexpr int OCH = 32 * D * OSZ / 16;    // 16-byte output chunks per tile
+  constexpr int OPITCH = D * OSZ + 16;      // bytes per output tile row (the pad spreads a run's banks)
+  constexpr int KK = K * K;
   // Two barriers per tile: decoded tile -> products, output tile -> stores.
   // The second also orders this tile's products before the next decoding,
   // so one decode buffer suffices.  The output tile is written back as full
@@ -98,8 +116,11 @@ __global__ __launch_bounds__(DLayout<D>::NT) void dequant_kernel(tqi::DequantArg
   __shared__ __attribute__((aligned(16))) _Float16 cl[SPLIT ? TILE : 8];
   __shared__ __attribute__((aligned(16))) _Float16 sg[PROD ? TILE : 8];
   __shared__ __attribute__((aligned(16))) float vfac[2][32];
-  __shared__ __attribute__((aligned(16))) uint8_t otile[32 * D * OSZ];
-  __shared__ uint32_t ctab[K];
+  __shared__ __attribute__((aligned(16))) uint8_t otile[32 * OPITCH];
+  // pair table: entry e holds the (even, odd) coordinates' centroids as two
+  // fp16 (hi halves, then at KK + e the lo halves); bits 2p and 2p + 1 of e
+  // are plane p of the even and of the odd coordinate
+  __shared__ uint32_t ptab[POLAR ? 1 : (SPLIT ? 2 : 1) * KK];
   // polar: cos and sin of the level-1 sector midpoints and of the centroid
   // angles of levels 2..LV
   __shared__ float pc1[POLAR ? 16 : 1], ps1[POLAR ? 16 : 1];
@@ -131,14 +152,23 @@ __global__ __launch_bounds__(DLayout<D>::NT) void dequant_kernel(tqi::DequantArg
       pcu[i / 4][i % 4] = (float)cos(ps);
       psu[i / 4][i % 4] = (float)sin(ps);
     }
-  } else if (tid < K) {
-    const float cv = a.centroids[tid] * kCenScale;
-    const _Float16 hv = (_Float16)cv;
-    const _Float16 lv = (_Float16)(cv - (float)hv);
-    uint16_t hb, lb;
-    __builtin_memcpy(&hb, &hv, 2);
-    __builtin_memcpy(&lb, &lv, 2);
-    ctab[tid] = (uint32_t)hb | ((uint32_t)lb << 16);
+  } else {
+    for (int e = tid; e < KK; e += L::NT) {
+      int i0 = 0, i1 = 0;
+#pragma unroll
+      for (int p = 0; p < LB; ++p) {
+        i0 |= ((e >> (2 * p)) & 1) << p;
+        i1 |= ((e >> (2 * p + 1)) & 1) << p;
+      }
+      const float c0 = a.centroids[i0] * kCenScale, c1 = a.centroids[i1] * kCenScale;
+      const _Float16 h0 = (_Float16)c0, h1 = (_Float16)c1;
+      ptab[e] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+      if constexpr (SPLIT) {
+        const _Float16 l0 = (_Float16)(c0 - (float)h0), l1 = (_Float16)(c1 - (float)h1);
+        ptab[KK + e] =
+            (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+      }
+    }
   }
   const float kappa = (float)(1.2533141373155003 / D);  // sqrt(pi/2) / d
 
@@ -231,20 +261,34 @@ __global__ __launch_bounds__(DLayout<D>::NT) void dequant_kernel(tqi::DequantArg
         }
       }
     } else {
+      // pair indices of the 8 pairs: the planes' bit pairs spread to a
+      // 4-bit pitch (planes 0-1 in z01, 2-3 in z23), one nibble per pair
+      uint32_t z01 = spread_pairs(r.pw[0]);
+      if constexpr (LB >= 2) z01 |= spread_pairs(r.pw[1]) << 2;
+      uint32_t z23 = 0;
+      if constexpr (LB >= 3) z23 = spread_pairs(r.pw[2]);
+      if constexpr (LB >= 4) z23 |= spread_pairs(r.pw[3]) << 2;
+      uint32_t hw[8], lw[8];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      uint32_t idx = 0;
+      for (int k = 0; k < 8; ++k) {
+        uint32_t pidx = (z01 >> (4 * k)) & 15u;
+        if constexpr (LB >= 3) pidx |= ((z23 >> (4 * k)) & 15u) << 4;
+        hw[k] = ptab[pidx];
+        if constexpr (SPLIT) lw[k] = ptab[KK + pidx];
+      }
+      const u32x4 h0 = {hw[0], hw[1], hw[2], hw[3]}, h1 = {hw[4], hw[5], hw[6], hw[7]};
+      hv[0] = __builtin_bit_cast(half8, h0);
+      hv[1] = __builtin_bit_cast(half8, h1);
+      if constexpr (SPLIT) {
+        const u32x4 l0 = {lw[0], lw[1], lw[2], lw[3]}, l1 = {lw[4], lw[5], lw[6], lw[7]};
+        lv[0] = __builtin_bit_cast(half8, l0);
+        lv[1] = __builtin_bit_cast(half8, l1);
+      }
+      if constexpr (PROD) {
 #pragma unroll
-      for (int p = 0; p < LB; ++p) idx |= ((r.pw[p] >> i) & 1u) << p;
-      const uint32_t e = ctab[idx];
-      const uint16_t hb = (uint16_t)(e & 0xFFFF), lb = (uint16_t)(e >> 16);
-      _Float16 hf, lf;
-      __builtin_memcpy(&hf, &hb, 2);
-      __builtin_memcpy(&lf, &lb, 2);
-      hv[i >> 3][i & 7] = hf;
-      lv[i >> 3][i & 7] = lf;
-      if constexpr (PROD) sv[i >> 3][i & 7] = ((r.pw[LB] >> i) & 1u) ? (_Float16)1.0f : (_Float16)-1.0f;
-    }
+        for (int i = 0; i < 16; ++i)
+          sv[i >> 3][i & 7] = ((r.pw[LB] >> i) & 1u) ? (_Float16)1.0f : (_Float16)-1.0f;
+      }
     }
     const int o = dv * L::PITCH + 16 * dc;
     *(half8 *)&ch[o] = hv[0];
@@ -268,7 +312,7 @@ __global__ __launch_bounds__(DLayout<D>::NT) void dequant_kernel(tqi::DequantArg
   int64_t tile = blockIdx.x;
   DecodeRaw<NPL> raw;
   load_raw(tile, raw);
-  __syncthreads();   // ctab
+  __syncthreads();   // tables
   // Range-dropped stores: on entry, as on every later iteration, stores
   // follow the pending loads (see the loop), so the compiler waits for the
   // loads alone.
@@ -291,14 +335,14 @@ __global__ __launch_bounds__(DLayout<D>::NT) void dequant_kernel(tqi::DequantArg
       const half8 ah = ahs[s];
       if constexpr (SPLIT) {
         const half8 al = *(const half8 *)&cl[m * L::PITCH + 16 * s + 8 * h];
-        accp[s & 1] = mfma32(al, ph[s], accp[s & 1]);
-        accp[s & 1] = mfma32(ah, pl[s], accp[s & 1]);
+        accp[s & 1] = mfma32(ph[s], al, accp[s & 1]);
+        accp[s & 1] = mfma32(pl[s], ah, accp[s & 1]);
       }
-      accp[s & 1] = mfma32(ah, ph[s], accp[s & 1]);
+      accp[s & 1] = mfma32(ph[s], ah, accp[s & 1]);
       if constexpr (HOLD_S) {
         const half8 as = *(const half8 *)&sg[m * L::PITCH + 16 * s + 8 * h];
-        if constexpr (SPLIT) acc2 = mfma32(as, sl[s], acc2);
-        acc2 = mfma32(as, sh[s], acc2);
+        if constexpr (SPLIT) acc2 = mfma32(sl[s], as, acc2);
+        acc2 = mfma32(sh[s], as, acc2);
       }
     }
     if constexpr (PROD && !HOLD_S) {
@@ -308,28 +352,30 @@ __global__ __launch_bounds__(DLayout<D>::NT) void dequant_kernel(tqi::DequantArg
         half8 bh, bl;
         column_fragment<D>(a.s_mat, w, s, bh, bl);
         const half8 as = *(const half8 *)&sg[m * L::PITCH + 16 * s + 8 * h];
-        if constexpr (SPLIT) acc2 = mfma32(as, bl, acc2);
-        acc2 = mfma32(as, bh, acc2);
+        if constexpr (SPLIT) acc2 = mfma32(bl, as, acc2);
+        acc2 = mfma32(bh, as, acc2);
       }
     }
     const f32x16 acc = accp[0] + accp[1];
-    // registers r and r + 1 hold rows v and v + 1 of the same column
+    // this lane's vector m: registers 4q .. 4q + 3 are its coordinates
+    // 32w + 8q + 4h + 0..3
+    const float f0 = vfac[0][m];
+    const float f1 = PROD ? vfac[1][m] : 0.0f;
+    uint8_t *orow = otile + m * OPITCH;
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const int v = 8 * (r >> 2) + 4 * h + (r & 3);
-      float val0 = acc[r] * vfac[0][v], val1 = acc[r + 1] * vfac[0][v + 1];
-      if constexpr (PROD) {
-        val0 += acc2[r] * vfac[1][v];
-        val1 += acc2[r + 1] * vfac[1][v + 1];
+    for (int q = 0; q < 4; ++q) {
+      float val[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        val[e] = acc[4 * q + e] * f0;
+        if constexpr (PROD) val[e] = fmaf(acc2[4 * q + e], f1, val[e]);
       }
-      const int e = v * D + 32 * w + m;
+      const int col = 32 * w + 8 * q + 4 * h;
       if constexpr (OUT_F32) {
-        ((float *)otile)[e] = val0;
-        ((float *)otile)[e + D] = val1;
+        *(f32x4 *)(orow + 4 * col) = f32x4{val[0], val[1], val[2], val[3]};
       } else {
-        const uint32_t pk = f32x2_to_bf16x2_bits(val0, val1);
-        ((uint16_t *)otile)[e] = (uint16_t)pk;
-        ((uint16_t *)otile)[e + D] = (uint16_t)(pk >> 16);
+        *(uint2 *)(orow + 2 * col) = make_uint2(f32x2_to_bf16x2_bits(val[0], val[1]),
+                                                f32x2_to_bf16x2_bits(val[2], val[3]));
       }
     }
     __syncthreads();
@@ -340,7 +386,7 @@ __global__ __launch_bounds__(DLayout<D>::NT) void dequant_kernel(tqi::DequantArg
       const int ck = tid + DLayout<D>::NT * i;
       const int v = ck / (D * OSZ / 16);
       const int64_t gv = base + v;
-      const f32x4 val = *(const f32x4 *)&otile[16 * ck];
+      const f32x4 val = *(const f32x4 *)&otile[v * OPITCH + 16 * (ck % (D * OSZ / 16))];
       buf_store_f32x4(ro, gv < a.n_vec ? (uint32_t)(base * D * OSZ + 16 * ck) : kNoStore, val);
     }
   }
