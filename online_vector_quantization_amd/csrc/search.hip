@@ -114,8 +114,12 @@ struct ScoreArgs {
   const uint8_t *codes;
   const uint16_t *norm;
   int64_t row_tokens, seq_len, keys_per_split, n_rows;
+  int64_t key_base;   // this pass scores keys [key_base, key_base + seq_len)
   int n_splits, q_tiles, n_kv_heads, n_q_heads, group, topk;
+  int split_base;     // its lists are splits [split_base, split_base + n_splits)
   float scale;
+  const float *seed;  // [query][topk] scores whose last is a lower bound of the
+                      // query's topk-th best (nullptr: none)
   float *part_val;    // [split][query][kTop]; the first topk of each list are exact
   int32_t *part_idx;
 };
@@ -294,7 +298,7 @@ __global__ __launch_bounds__(kSearchThreads) void search_score_kernel(ScoreArgs 
   int64_t k_end = k_begin + a.keys_per_split;
   if (k_end > a.seq_len) k_end = a.seq_len;
   const int n_keys = (int)(k_end - k_begin);
-  const int64_t key0 = (int64_t)stream * a.row_tokens + k_begin;
+  const int64_t key0 = (int64_t)stream * a.row_tokens + a.key_base + k_begin;
   // Keys past the split's end fall outside these ranges and load as zero.
   const i32x4 rcode = make_rsrc(a.codes + key0 * ROWB, (uint32_t)n_keys * ROWB);
   const i32x4 rnrm = make_rsrc(a.norm + key0, (uint32_t)n_keys * 2u);
@@ -328,7 +332,12 @@ __global__ __launch_bounds__(kSearchThreads) void search_score_kernel(ScoreArgs 
 #pragma unroll
     for (int j = 0; j < kTop; ++j) lq[32 * j] = empty;     // both half-lanes store the same
   }
-  float thr = qvalid ? -FLT_MAX : FLT_MAX;
+  // A seed (the topk-th best over a sample of the keys scored before) is a
+  // lower bound of the final topk-th best: a key at or below it cannot
+  // make the top-k (the sample's keys have smaller indices and win ties).
+  const float seed = (a.seed != nullptr && qvalid)
+                         ? a.seed[((int64_t)stream * a.group + gq) * a.topk + a.topk - 1] : -FLT_MAX;
+  float thr = qvalid ? seed : FLT_MAX;
   float thq = -INFINITY;
   int cnt = 0;
   auto set_bound = [&]() __attribute__((always_inline)) {
@@ -358,27 +367,61 @@ __global__ __launch_bounds__(kSearchThreads) void search_score_kernel(ScoreArgs 
     float t;
     int ix;
     unpack_entry(lq[32 * (a.topk - 1)], t, ix);
-    thr = qvalid ? t : FLT_MAX;
+    thr = qvalid ? fmaxf(t, seed) : FLT_MAX;
     set_bound();
   };
-  // products on a tile held in (sh, sl)
-  auto products = [&](const _Float16 *sh, const _Float16 *sl) __attribute__((always_inline)) {
+  // Products on a tile held in (sh, sl), norms sn: the hi x hi product
+  // first, then, only where some lane's score could pass its bound, the two
+  // lo products.  The lo halves are at most 2^-11 of their hi halves (fp16
+  // rounding; the query's subnormal halves add an absolute term below
+  // 2^-17 max|c|), so the three-product sum differs from hi x hi by at most
+  // 2^-10 sum_k |qh_k| |ch_k| <= 2^-10 max|c| ||qh||_1 (scaled centroids);
+  // marg adds 1/8 of that for the fp32 roundings of both sums (products
+  // are exact, at most 64 roundings of 2^-24 each, relative to the same
+  // sum).  A lane whose hi x hi product plus marg does not pass cannot pass
+  // with all three.  Returns whether the three products were formed.
+  const int h4 = 4 * h;
+  float marg;
+  {
+    float q1 = 0.0f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q1 += fabsf((float)qh[s][i]);
+    q1 += __shfl_xor(q1, 32);                         // the other half of the coordinates
+    const float cmax = fmaxf(fabsf(a.centroids[0]), fabsf(a.centroids[K - 1])) * kCenScale;
+    marg = 0x1.2p-10f * cmax * q1;
+  }
+  auto products = [&](const _Float16 *sh, const _Float16 *sl, const float *sn, bool &exact)
+      __attribute__((always_inline)) {
     f32x16 acc = {};
     const _Float16 *hb = sh + m * PITCH + 8 * h;
     const _Float16 *lb = sl + m * PITCH + 8 * h;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const half8 ah = *(const half8 *)(hb + 16 * s);
-      const half8 al = *(const half8 *)(lb + 16 * s);
-      acc = mfma32(al, qh[s], acc);
-      acc = mfma32(ah, ql[s], acc);
-      acc = mfma32(ah, qh[s], acc);
+    for (int s = 0; s < KS; ++s) acc = mfma32(*(const half8 *)(hb + 16 * s), qh[s], acc);
+    bool pass = false;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 k4 = *(const f32x4 *)&sn[8 * g + h4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pass = pass || (acc[4 * g + j] + marg) * k4[j] > thq;
+    }
+    exact = __ballot(pass) != 0;
+    if (exact) {
+      // fragments of four K steps in flight at a time (register budget)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const half8 ah = *(const half8 *)(hb + 16 * s);
+        const half8 al = *(const half8 *)(lb + 16 * s);
+        acc = mfma32(al, qh[s], acc);
+        acc = mfma32(ah, ql[s], acc);
+        if ((s & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+      }
     }
     return acc;
   };
-  // selection on tile t0; lane (m, h) holds query m and keys
-  // 8*(r/4) + 4*h + r%4 of the tile
-  const int h4 = 4 * h;
+  // selection on tile t0 (three-product scores); lane (m, h) holds query m
+  // and keys 8*(r/4) + 4*h + r%4 of the tile
   auto select = [&](const f32x16 &acc, int t0, const float *sn) __attribute__((always_inline)) {
     float pr[16];
     uint64_t rm[16];      // per row: lanes whose product passes the bound
@@ -406,7 +449,7 @@ __global__ __launch_bounds__(kSearchThreads) void search_score_kernel(ScoreArgs 
         if (__ballot(cnt >= kCand) != 0) flush();
         const float v = pr[r];
         if (v > thq) {
-          const int kb = (int)k_begin + t0 + 8 * (r >> 2) + (r & 3);
+          const int kb = (int)(a.key_base + k_begin) + t0 + 8 * (r >> 2) + (r & 3);
           sq[32 * cnt] = pack_entry(v * qf, kb + h4);
           ++cnt;
         }
@@ -425,23 +468,27 @@ __global__ __launch_bounds__(kSearchThreads) void search_score_kernel(ScoreArgs 
   // LDS and the barrier at the same moments.  Tile buffers alternate; norms rotate over
   // three buffers, so the second wave's select(t - 1) never reads the norms
   // that decode(t + 1) writes.
+  // A tile whose products stopped at hi x hi has no lane that passes (the
+  // bounds only rise), so its selection is skipped.
   const bool mfma_first = ((w ^ (w >> 2)) & 1) == 0;
   f32x16 pend = {};                    // second wave: products of the previous tile
+  bool pend_exact = false;
   auto step = [&](int t0, const _Float16 *sh, const _Float16 *sl, _Float16 *dh, _Float16 *dl)
       __attribute__((always_inline)) {
     const int ti = t0 >> 5;
     float *kn_cur = kn[ti % 3];
     float *kn_next = kn[(ti + 1) % 3];
     if (mfma_first) {
-      const f32x16 acc = products(sh, sl);
-      select(acc, t0, kn_cur);
+      bool exact;
+      const f32x16 acc = products(sh, sl, kn_cur, exact);
+      if (exact) select(acc, t0, kn_cur);
       decode_tile(t0 + 32, dh, dl, kn_next);
       load_tile(t0 + 64);
     } else {
-      if (t0 > 0) select(pend, t0 - 32, kn[(ti + 2) % 3]);
+      if (t0 > 0 && pend_exact) select(pend, t0 - 32, kn[(ti + 2) % 3]);
       decode_tile(t0 + 32, dh, dl, kn_next);
       load_tile(t0 + 64);
-      pend = products(sh, sl);
+      pend = products(sh, sl, kn_cur, pend_exact);
     }
     __syncthreads();
   };
@@ -459,12 +506,12 @@ __global__ __launch_bounds__(kSearchThreads) void search_score_kernel(ScoreArgs 
     step(t0 + 32, ch1, cl1, ch0, cl0);
     t_last = t0 + 32;
   }
-  if (!mfma_first && n_keys > 0) select(pend, t_last, kn[(t_last >> 5) % 3]);
+  if (!mfma_first && n_keys > 0 && pend_exact) select(pend, t_last, kn[(t_last >> 5) % 3]);
   if (__ballot(cnt > 0) != 0) flush();
   if (h == 0 && qvalid) {
     const int64_t qrow = (int64_t)stream * a.group + gq;
-    float *outv = a.part_val + ((int64_t)split * a.n_rows + qrow) * kTop;
-    int32_t *outi = a.part_idx + ((int64_t)split * a.n_rows + qrow) * kTop;
+    float *outv = a.part_val + ((int64_t)(a.split_base + split) * a.n_rows + qrow) * kTop;
+    int32_t *outi = a.part_idx + ((int64_t)(a.split_base + split) * a.n_rows + qrow) * kTop;
 #pragma unroll
     for (int j = 0; j < kTop; ++j) {
       float s;
@@ -526,26 +573,33 @@ __global__ __launch_bounds__(256) void search_merge_kernel(MergeArgs a) {
   }
 }
 
-// Launch plan of one search call: key splits (so that the workgroups fill
-// the chip in whole rounds: the cost of a split count is (rounds of resident
-// workgroups) x (tiles per split + a fixed allowance for filling the lists))
-// and the workspace layout.
-struct SearchPlan {
-  int64_t splits, kps, n_rows, n_queries, q_tiles;
-  size_t qbytes, qfac_off, pv_off, pi_off, bytes;
+// Launch plan of one search call.  A sample pass scores the first
+// 1/16 of every stream's keys exactly and merges its lists into a seed, the
+// topk-th best of the sample per query; the main pass scores the rest with
+// the lists' bounds starting at the seed, so that after the sample almost
+// no tile needs more than the hi x hi product.  A final merge takes the
+// lists of both passes.  Each pass has its own key splits (so that the
+// workgroups fill the chip in whole rounds: the cost of a split count is
+// (rounds of resident workgroups) x (tiles per split + a fixed allowance for
+// filling the lists)); together at most 64 (lanes of the merge).
+struct SearchPass {
+  int64_t key_base, seq_len, splits, kps;
 };
 
-SearchPlan search_plan(int batch, int n_q_heads, int n_kv_heads, int64_t seq_len, int d) {
-  SearchPlan p;
-  const int group = n_q_heads / n_kv_heads;
-  const int64_t n_streams = (int64_t)batch * n_kv_heads;
-  p.n_queries = (int64_t)batch * n_q_heads;
-  p.q_tiles = (group + kSearchQueries - 1) / kSearchQueries;
-  const int64_t base_blocks = n_streams * p.q_tiles;
+struct SearchPlan {
+  SearchPass sample, main;
+  int64_t n_rows, n_queries, q_tiles;
+  size_t qbytes, qfac_off, seed_val_off, seed_idx_off, pv_off, pi_off, bytes;
+};
+
+SearchPass plan_pass(int64_t base_blocks, int64_t key_base, int64_t seq_len, int64_t cap) {
+  SearchPass p;
+  p.key_base = key_base;
+  p.seq_len = seq_len;
   const int64_t cus = tqi::device_cu_count();
   const int64_t n_tiles = (seq_len + 31) / 32;
   int64_t max_splits = (seq_len + 4095) / 4096;
-  if (max_splits > 64) max_splits = 64;
+  if (max_splits > cap) max_splits = cap;
   if (max_splits < 1) max_splits = 1;
   int64_t splits = 1, best = -1;
   for (int64_t sp = 1; sp <= max_splits; ++sp) {
@@ -556,13 +610,31 @@ SearchPlan search_plan(int batch, int n_q_heads, int n_kv_heads, int64_t seq_len
   int64_t kps = (seq_len + splits - 1) / splits;
   kps = (kps + 31) / 32 * 32;
   p.kps = kps > 0 ? kps : 32;
-  p.splits = seq_len > 0 ? (seq_len + p.kps - 1) / p.kps : 1;
+  p.splits = seq_len > 0 ? (seq_len + p.kps - 1) / p.kps : 0;
+  return p;
+}
+
+SearchPlan search_plan(int batch, int n_q_heads, int n_kv_heads, int64_t seq_len, int d) {
+  SearchPlan p;
+  const int group = n_q_heads / n_kv_heads;
+  const int64_t n_streams = (int64_t)batch * n_kv_heads;
+  p.n_queries = (int64_t)batch * n_q_heads;
+  p.q_tiles = (group + kSearchQueries - 1) / kSearchQueries;
+  const int64_t base_blocks = n_streams * p.q_tiles;
+  // sample: a whole number of 32-key tiles, none below 1024 keys
+  const int64_t n_sample = seq_len >= 1024 ? ((seq_len + 15) / 16 + 31) / 32 * 32 : 0;
+  p.sample = plan_pass(base_blocks, 0, n_sample, 16);
+  p.main = plan_pass(base_blocks, n_sample, seq_len - n_sample, 64 - p.sample.splits);
   p.n_rows = n_streams * group;
+  const int64_t total = p.sample.splits + p.main.splits;
   p.qbytes = tqi::ws_align((size_t)p.n_queries * d * sizeof(_Float16));
   p.qfac_off = 2 * p.qbytes;
-  p.pv_off = p.qfac_off + tqi::ws_align((size_t)p.n_queries * sizeof(float));
-  p.pi_off = p.pv_off + tqi::ws_align((size_t)p.splits * p.n_rows * kTop * sizeof(float));
-  p.bytes = p.pi_off + tqi::ws_align((size_t)p.splits * p.n_rows * kTop * sizeof(int32_t));
+  p.seed_val_off = p.qfac_off + tqi::ws_align((size_t)p.n_queries * sizeof(float));
+  const size_t seed_bytes = p.sample.splits > 0 ? tqi::ws_align((size_t)p.n_rows * kTop * sizeof(float)) : 0;
+  p.seed_idx_off = p.seed_val_off + seed_bytes;
+  p.pv_off = p.seed_idx_off + seed_bytes;
+  p.pi_off = p.pv_off + tqi::ws_align((size_t)total * p.n_rows * kTop * sizeof(float));
+  p.bytes = p.pi_off + tqi::ws_align((size_t)total * p.n_rows * kTop * sizeof(int32_t));
   return p;
 }
 
@@ -575,7 +647,6 @@ hipError_t launch_t(const tqi::SearchArgs &sa, hipStream_t s) {
   const int64_t n_queries = plan.n_queries;
   const int q_tiles = (int)plan.q_tiles;
   const int64_t base_blocks = n_streams * q_tiles;
-  const int64_t splits = plan.splits, kps = plan.kps;
   // Key indices fit the packed list entries (30 bits); per-split byte offsets
   // of the packed codes stay below 2^31 (both checked by search_supported).
   const int64_t n_rows = plan.n_rows;
@@ -590,12 +661,14 @@ hipError_t launch_t(const tqi::SearchArgs &sa, hipStream_t s) {
   pa.qh = (_Float16 *)ws;
   pa.ql = (_Float16 *)(ws + plan.qbytes);
   pa.qfac = (float *)(ws + plan.qfac_off);
+  float *seed_val = (float *)(ws + plan.seed_val_off);
+  int32_t *seed_idx = (int32_t *)(ws + plan.seed_idx_off);
   float *pv = (float *)(ws + plan.pv_off);
   int32_t *pi = (int32_t *)(ws + plan.pi_off);
   hipLaunchKernelGGL((search_prep_kernel<D>), dim3((unsigned)((n_queries + kPrepQueries - 1) / kPrepQueries)),
                      dim3(D), 0, s, pa);
   e = hipGetLastError();
-  if (e == hipSuccess) {
+  auto score = [&](const SearchPass &ps, int split_base, const float *seed) {
     ScoreArgs sc;
     sc.qh = pa.qh;
     sc.ql = pa.ql;
@@ -604,37 +677,47 @@ hipError_t launch_t(const tqi::SearchArgs &sa, hipStream_t s) {
     sc.codes = a.codes;
     sc.norm = a.norm;
     sc.row_tokens = a.row_tokens;
-    sc.seq_len = a.seq_len;
-    sc.keys_per_split = kps;
+    sc.seq_len = ps.seq_len;
+    sc.keys_per_split = ps.kps;
     sc.n_rows = n_rows;
-    sc.n_splits = (int)splits;
+    sc.key_base = ps.key_base;
+    sc.n_splits = (int)ps.splits;
     sc.q_tiles = q_tiles;
     sc.n_kv_heads = a.n_kv_heads;
     sc.n_q_heads = a.n_q_heads;
     sc.group = group;
+    sc.split_base = split_base;
     sc.scale = a.scale;
     sc.topk = sa.topk;
+    sc.seed = seed;
     sc.part_val = pv;
     sc.part_idx = pi;
-    hipLaunchKernelGGL((search_score_kernel<D, LB>), dim3((unsigned)(base_blocks * splits)), dim3(kSearchThreads),
-                       0, s, sc);
-    e = hipGetLastError();
-  }
-  if (e == hipSuccess) {
+    hipLaunchKernelGGL((search_score_kernel<D, LB>), dim3((unsigned)(base_blocks * ps.splits)),
+                       dim3(kSearchThreads), 0, s, sc);
+    return hipGetLastError();
+  };
+  auto merge = [&](int n_splits, float *out_val, int32_t *out_idx) {
     MergeArgs ma;
     ma.part_val = pv;
     ma.part_idx = pi;
     ma.n_rows = n_rows;
-    ma.n_splits = (int)splits;
+    ma.n_splits = n_splits;
     ma.topk = sa.topk;
     ma.group = group;
     ma.n_q_heads = a.n_q_heads;
     ma.n_kv_heads = a.n_kv_heads;
-    ma.out_val = a.logits;
-    ma.out_idx = sa.topk_idx;
+    ma.out_val = out_val;
+    ma.out_idx = out_idx;
     hipLaunchKernelGGL(search_merge_kernel, dim3((unsigned)((n_rows + 3) / 4)), dim3(256), 0, s, ma);
-    e = hipGetLastError();
-  }
+    return hipGetLastError();
+  };
+  // (the main pass is never empty: the sample is at most seq_len / 16 + 32
+  // keys, and a call has seq_len >= topk >= 1)
+  const int ns = (int)plan.sample.splits;
+  if (e == hipSuccess && ns > 0) e = score(plan.sample, 0, nullptr);
+  if (e == hipSuccess && ns > 0) e = merge(ns, seed_val, seed_idx);
+  if (e == hipSuccess) e = score(plan.main, ns, ns > 0 ? seed_val : nullptr);
+  if (e == hipSuccess) e = merge(ns + (int)plan.main.splits, a.logits, sa.topk_idx);
   return e;
 }
 
@@ -660,7 +743,8 @@ bool search_supported(int d, int lbits, int topk, int batch, int n_q_heads, int 
   // per-split byte offsets of the packed codes (one split plus one tile of
   // prefetch) below 2^31
   const SearchPlan p = search_plan(batch, n_q_heads, n_kv_heads, seq_len, d);
-  return (p.kps + 64) * (int64_t)(lbits * d / 8) < (1LL << 31);
+  const int64_t kps = p.main.kps > p.sample.kps ? p.main.kps : p.sample.kps;
+  return (kps + 64) * (int64_t)(lbits * d / 8) < (1LL << 31);
 }
 
 size_t search_workspace_bytes(int d, int lbits, int batch, int n_q_heads, int n_kv_heads, int64_t seq_len) {

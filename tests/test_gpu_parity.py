@@ -251,11 +251,12 @@ def test_search_parity(tq, bits):
             assert abs(scores[r, i] - ov[r, -1]) <= tol, (r, i)
 
 
-@pytest.mark.parametrize("d,bits", [(64, 3), (64, 1), (128, 4)])
-def test_search_parity_gqa(tq, d, bits):
-    """Top-k over two KV heads of 3001 keys each (a ragged last tile), 40
-    query heads per KV head, at d = 64 and 128."""
-    hkv, group, n_db, k = 2, 40, 3001, 10
+@pytest.mark.parametrize("d,bits,n_db", [(64, 3, 3001), (64, 1, 3001), (128, 4, 3001), (128, 2, 700)])
+def test_search_parity_gqa(tq, d, bits, n_db):
+    """Top-k over two KV heads of n_db keys each (a ragged last tile), 40
+    query heads per KV head, at d = 64 and 128: 3001 keys take a sample pass
+    (192 keys) that seeds the bounds of the main pass, 700 keys one pass."""
+    hkv, group, k = 2, 40, 10
     rng = np.random.default_rng(d + bits)
     scales = np.exp(0.5 * rng.standard_normal((hkv, d)))
     db = rng.standard_normal((hkv, n_db, d)) * scales[:, None, :]
