@@ -452,6 +452,20 @@ def _oracle_threads():
         return os.cpu_count()
 
 
+def _host_info():
+    """The host the oracle ran on: CPU model, logical CPUs, BLAS threads."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "blas_threads": _oracle_threads()}
+
+
 def cpu_baseline_prefill(budget_s=12.0):
     """The oracle quantising whole KV heads of the prefill workload (b = 3) until the budget is spent."""
     import numpy as np
@@ -683,6 +697,7 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = {"decode": cpu_baseline_decode, "prefill": cpu_baseline_prefill,
                                 "search": cpu_baseline_search}[args.workload]()
+        line["cpu_baseline"]["host"] = _host_info()
     print(json.dumps(line), flush=True)
 
 
