@@ -59,7 +59,7 @@ struct LogitArgs {
   size_t workspace_bytes = 0;
 };
 
-// Shapes the dense logit kernels take (GQA group <= 16, d in {128, 256},
+// Shapes the dense logit kernels take (GQA group <= 16, d in {64, 128, 256},
 // 32-bit byte offsets of one stream's codes and logits below 2^31).
 bool logits_supported(int d, int lbits, bool prod, int group, int64_t seq_len);
 size_t logits_workspace_bytes(int d, int lbits, bool prod, int64_t n_streams, int group);
