@@ -166,8 +166,8 @@ typedef struct tq_packed {
  *   x            device, n_vec rows of d elements (x_dtype TQ_F32 or
  *                TQ_BF16), consecutive rows x_row_stride elements apart
  *   out          packed arrays; vector i is written at index out_offset + i
- * Supported: d in {64, 128, 256} for both modes; b' <= 4; polar mode with
- * d = 128.
+ * Supported: d in {64, 128, 256} for all three modes; b' <= 4 (polar: 3
+ * bits per coordinate).
  * n_vec == 0 is a no-op.  Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED,
  * TQ_ERR_HIP. */
 tq_status tq_quantize_kv(const tq_params *p, const void *x, int32_t x_dtype, int64_t n_vec,
@@ -324,7 +324,7 @@ tq_status tq_attn_output_workspace_size(const tq_params *p, int32_t batch, int32
 
 /* Reconstruct n_vec vectors (page section "2단계": reconstructed vectors).
  *   out          device [n_vec][d], out_dtype TQ_F32 or TQ_BF16
- * Supported: d in {64, 128, 256} in both modes, d = 128 polar.
+ * Supported: d in {64, 128, 256} in all three modes.
  * Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED, TQ_ERR_HIP. */
 tq_status tq_dequantize(const tq_params *p, const tq_packed *k, int64_t n_vec, void *out,
                         int32_t out_dtype, void *stream);

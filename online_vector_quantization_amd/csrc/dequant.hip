@@ -447,9 +447,11 @@ hipError_t launch_lb(int lb, const tqi::DequantArgs &a, hipStream_t s, bool *ok)
 namespace tqi {
 
 hipError_t launch_dequant_polar(int d, const DequantArgs &a, hipStream_t s, bool *supported) {
-  *supported = d == 128;
-  if (d != 128) return hipSuccess;
-  return a.out_f32 ? launch_t<128, 1, false, true, true>(a, s) : launch_t<128, 1, false, false, true>(a, s);
+  *supported = d == 64 || d == 128 || d == 256;
+  if (d == 64) return a.out_f32 ? launch_t<64, 1, false, true, true>(a, s) : launch_t<64, 1, false, false, true>(a, s);
+  if (d == 128) return a.out_f32 ? launch_t<128, 1, false, true, true>(a, s) : launch_t<128, 1, false, false, true>(a, s);
+  if (d == 256) return a.out_f32 ? launch_t<256, 1, false, true, true>(a, s) : launch_t<256, 1, false, false, true>(a, s);
+  return hipSuccess;
 }
 
 hipError_t launch_dequant(int d, int lbits, bool prod, const DequantArgs &a, hipStream_t s,

@@ -925,10 +925,11 @@ hipError_t launch_polar_t(const tqi::QuantizeArgs &a, hipStream_t s) {
 namespace tqi {
 
 hipError_t launch_quantize_polar(int d, bool in_f32, const QuantizeArgs &a, hipStream_t s, bool *supported) {
-  *supported = false;
-  if (d != 128) return hipSuccess;
-  *supported = true;
-  return in_f32 ? launch_polar_t<128, true>(a, s) : launch_polar_t<128, false>(a, s);
+  *supported = d == 64 || d == 128 || d == 256;
+  if (d == 64) return in_f32 ? launch_polar_t<64, true>(a, s) : launch_polar_t<64, false>(a, s);
+  if (d == 128) return in_f32 ? launch_polar_t<128, true>(a, s) : launch_polar_t<128, false>(a, s);
+  if (d == 256) return in_f32 ? launch_polar_t<256, true>(a, s) : launch_polar_t<256, false>(a, s);
+  return hipSuccess;
 }
 
 hipError_t launch_quantize(int d, int lbits, bool prod, bool in_f32, const QuantizeArgs &a,

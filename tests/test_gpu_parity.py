@@ -517,11 +517,12 @@ def test_append_attn_logits_bounds(tq):
 
 
 # ---------------------------------------------------------------- polar format
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_polar_quantize_parity(tq, dtype):
+@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (128, "f32"), (64, "bf16"), (64, "f32"), (256, "bf16"),
+                                     (256, "f32")])
+def test_polar_quantize_parity(tq, d, dtype):
     from oracle import polar as opq
     from oracle import rotation as orot
-    d, n = 128, 1000
+    n = 1000
     if dtype == "bf16":
         xb = _keys_bf16(d, n, seed=3)
         x64 = _special_rows(bf16_to_f32(xb).astype(np.float64))
@@ -544,11 +545,11 @@ def test_polar_quantize_parity(tq, dtype):
     assert not codes[3].any()                               # the zero vector: every angle 0
 
 
-@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
-def test_polar_dequantize_parity(tq, out_dtype):
+@pytest.mark.parametrize("d,out_dtype", [(128, "f32"), (128, "bf16"), (64, "f32"), (256, "f32"), (256, "bf16")])
+def test_polar_dequantize_parity(tq, d, out_dtype):
     from oracle import polar as opq
     from oracle import rotation as orot
-    d, n = 128, 777
+    n = 777
     rng = np.random.default_rng(12)
     x64 = rng.standard_normal((n, d)) * np.exp(rng.standard_normal(d))
     x64[5] = 0.0
@@ -589,6 +590,29 @@ def test_polar_round_trip_and_unsupported_calls(tq):
     q = torch.zeros((1, 4, d), device=DEV)
     with pytest.raises(tq.TQError):
         qz.attn_logits(q, cache, n_kv_heads=1, seq_len=n, scale=1.0)
+
+
+@pytest.mark.parametrize("d", [64, 256])
+def test_polar_round_trip_other_widths(tq, d):
+    """GPU quantise then GPU dequantise at d = 64 and 256 (6 and 8 levels):
+    the reconstruction against the oracle's decoding of the GPU's own codes,
+    and the codes against the oracle's."""
+    from oracle import polar as opq
+    from oracle import rotation as orot
+    n = 2048
+    rng = np.random.default_rng(14 + d)
+    x64 = (rng.standard_normal((n, d)) * 2.0).astype(np.float32).astype(np.float64)
+    x = torch.from_numpy(x64.astype(np.float32)).to(DEV)
+    qz = tq.Quantizer(d, 3, tq.MODE_POLAR, seed=0, device=DEV)
+    cache = qz.new_cache(n)
+    qz.quantize(x, out=cache)
+    pi = orot.haar_rotation(d, 0)
+    check_polar_codes(cache.codes.cpu().numpy(), opq.quantize(x64, pi), d)
+    got = qz.dequantize(cache, n).cpu().numpy()
+    want = opq.dequantize(cache.codes.cpu().numpy(), cache.norm.cpu().numpy().view(np.uint16), pi)
+    check_dequant(got, want)
+    cos = np.sum(x64 * got, 1) / np.linalg.norm(x64, axis=1) / np.linalg.norm(got, axis=1)
+    assert cos.mean() > 0.97
 
 
 # ---------------------------------------------------------------- paged cache

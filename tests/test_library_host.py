@@ -142,6 +142,14 @@ def test_polar_codebooks_match_oracle():
         oc, ot = opq.angle_codebook(1 << (lv - 1))
         np.testing.assert_allclose(c[lv - 2], oc, rtol=0, atol=1e-12)
         np.testing.assert_allclose(t[lv - 2], ot, rtol=0, atol=1e-12)
+    # d = 256 adds level 8 (k = 128); d = 64 stops at level 6
+    c256, t256 = tq.make_polar_codebook(256)
+    assert c256.shape == (7, 4) and np.array_equal(c256[:6], c)
+    oc, ot = opq.angle_codebook(128)
+    np.testing.assert_allclose(c256[6], oc, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(t256[6], ot, rtol=0, atol=1e-12)
+    c64, _ = tq.make_polar_codebook(64)
+    assert c64.shape == (5, 4) and np.array_equal(c64, c[:5])
     with pytest.raises(tq.TQError):
         tq.make_polar_codebook(96)
 
