@@ -9,15 +9,18 @@
 // memory, so selection is fused into the scoring kernel.
 // * prep: q' = Pi q per query (fp64 accumulate), scaled by a power of two and
 //   split into fp16 hi + lo.
-// * score: a workgroup owns 128 queries (4 waves x 32) and one slice of the
+// * score: a workgroup owns 256 queries (8 waves x 32) and one slice of the
 //   database.  Each 32-key tile is decoded once into LDS (centroid values as
 //   fp16 hi + lo) and multiplied on the 32x32x16 fp16 MFMA by every wave's
-//   stationary query fragments (3 products: hi*hi + hi*lo + lo*hi).  In the
-//   accumulator layout a lane holds one query and 16 keys, so each lane keeps
-//   a sorted running top-16 of its query in registers and only touches it when
-//   a score beats its current 16th best.
-// * merge: per query, the sorted lists of the two half-waves and of all
-//   database slices are merged; ties go to the smaller key index.
+//   stationary query fragments: hi*hi first, hi*lo + lo*hi only where some
+//   lane's score could still enter its list (a rigorous margin covers the lo
+//   products).  In the accumulator layout a lane holds one query and 16 keys;
+//   passing scores go to per-lane candidate slots, merged into the query's
+//   sorted list of 16 in LDS when the slots fill.
+// * two passes: a sample pass over the first 1/16 of the keys, whose merged
+//   topk-th scores seed the lists' bounds for the main pass over the rest.
+// * merge: per query, the sorted lists of all database slices of both passes
+//   are merged; ties go to the smaller key index.
 #include <cfloat>
 
 #include "tq_device.h"
