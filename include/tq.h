@@ -24,7 +24,8 @@
  *     synchronisation, as with any HIP launch.
  *   - The library never allocates or frees memory, never synchronises and
  *     keeps no state between calls (apart from a per-device cache of the
- *     compute-unit count, set once).  Calls that need device scratch memory
+ *     compute-unit count, set once, and the fixed per-device array that
+ *     tq_attn_output_noalloc uses instead of a workspace).  Calls that need device scratch memory
  *     (the logit calls: query tables; top-k: partial lists; tq_attn_output:
  *     per-split partials) take a
  *     caller-owned `workspace` of `workspace_bytes` bytes: 256-byte aligned
@@ -34,7 +35,8 @@
  *     (other streams, other host threads) need workspaces of their own.  A
  *     NULL workspace is accepted where the query returns 0.
  *   - Calls are reentrant and thread-safe: nothing is shared between calls
- *     except what the caller passes in.
+ *     except what the caller passes in (tq_attn_output_noalloc excepted: its
+ *     calls share the array, see there).
  *
  * Packed format of one vector (d coordinates, b total bits per coordinate)
  *   mode TQ_MODE_MSE : b' = b Lloyd-Max bits.     1 <= b <= 4
