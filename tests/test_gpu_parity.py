@@ -615,6 +615,40 @@ def test_polar_round_trip_other_widths(tq, d):
     assert cos.mean() > 0.97
 
 
+def test_cache_save_and_reload_round_trip(tq):
+    """A packed cache is its bytes plus (d, b, mode, seed): the page keeps no
+    stored constants, Pi and S regenerate from the seed.  Raw bytes copied to
+    the host and back, read by a quantiser built afresh from the same seed,
+    give bit-identical logits and reconstructions; another seed does not."""
+    d, bits, n, hkv, group = 128, 3, 2000, 2, 4
+    rng = np.random.default_rng(21)
+    x = torch.from_numpy((rng.standard_normal((n, d)) * 3.0).astype(np.float32)).to(DEV)
+    q = torch.from_numpy(rng.standard_normal((1, hkv * group, d)).astype(np.float32)).to(DEV)
+    qz = tq.Quantizer(d, bits, tq.MODE_PROD, seed=5, device=DEV)
+    cache = qz.quantize(x)
+    seq = n // hkv
+    want_l = qz.attn_logits(q, cache, n_kv_heads=hkv, seq_len=seq, scale=0.25).cpu().numpy()
+    want_x = qz.dequantize(cache, n).cpu().numpy()
+    saved = {k: getattr(cache, k).cpu().numpy().tobytes() for k in ("codes", "norm", "rnorm")}
+    del cache, qz
+    torch.cuda.synchronize()
+
+    def load(name, dtype, shape):
+        return torch.from_numpy(np.frombuffer(saved[name], dtype=dtype).reshape(shape).copy()).to(DEV)
+
+    rb = bits * d // 8
+    qz2 = tq.Quantizer(d, bits, tq.MODE_PROD, seed=5, device=DEV)
+    cache2 = tq.PackedKV.from_tensors(d, bits, tq.MODE_PROD, load("codes", np.uint8, (n, rb)),
+                                      load("norm", np.int16, (n,)), load("rnorm", np.int16, (n,)))
+    got_l = qz2.attn_logits(q, cache2, n_kv_heads=hkv, seq_len=seq, scale=0.25).cpu().numpy()
+    got_x = qz2.dequantize(cache2, n).cpu().numpy()
+    assert np.array_equal(got_l, want_l)
+    assert np.array_equal(got_x, want_x)
+    qz3 = tq.Quantizer(d, bits, tq.MODE_PROD, seed=6, device=DEV)
+    other = qz3.dequantize(cache2, n).cpu().numpy()
+    assert not np.allclose(other, want_x, atol=1e-3)
+
+
 # ---------------------------------------------------------------- paged cache
 PAGED_CASES = [
     # d, bits, mode, batch, kv heads, group, page tokens, seq, append pos, q dtype
