@@ -283,6 +283,31 @@ def test_search_parity_gqa(tq, d, bits, n_db):
                 assert abs(scores[r, i] - ov[r, -1]) <= tol, (row, i)
 
 
+@pytest.mark.parametrize("k", [1, 16])
+def test_search_topk_extremes(tq, k):
+    """topk = 1 and the largest list (16) over 5000 keys (sample and main
+    passes), 300 queries, d = 128, b = 3."""
+    d, bits, n_db, n_q = 128, 3, 5000, 300
+    rng = np.random.default_rng(40 + k)
+    db = rng.standard_normal((n_db, d)) * np.exp(0.5 * rng.standard_normal(d))
+    qv = (rng.standard_normal((n_q, d)) * np.exp(0.5 * rng.standard_normal(d))).astype(np.float32)
+    ot = OracleTables(d, bits, oqz.MODE_MSE)
+    ref = ot.quantize(db)
+    qz = tq.Quantizer(d, bits, oqz.MODE_MSE, seed=0, device=DEV)
+    cache = cache_from_oracle(tq, ref, d, bits, oqz.MODE_MSE, DEV)
+    vals, idx = qz.search(torch.from_numpy(qv.reshape(1, n_q, d)).to(DEV), cache, n_kv_heads=1, seq_len=n_db, topk=k)
+    vals, idx = vals.cpu().numpy()[0], idx.cpu().numpy()[0]
+    scores = oqz.logits_rotated(qv.astype(np.float64), ref["codes"], ref["norm"], ot.pi, ot.c, oqz.MODE_MSE, 1.0)
+    ov, oi = oqz.topk(scores, k)
+    for r in range(n_q):
+        got = scores[r, idx[r]]
+        assert np.all(np.abs(vals[r] - got) <= 1e-4 * np.maximum(np.abs(got), 1e-3)), r
+        assert np.all(np.diff(vals[r]) <= 1e-6)
+        tol = 1e-4 * max(abs(ov[r, -1]), 1e-3)
+        for i in set(idx[r].tolist()) ^ set(oi[r].tolist()):
+            assert abs(scores[r, i] - ov[r, -1]) <= tol, (r, i)
+
+
 @pytest.mark.parametrize("scale", [1.0, -0.5, 0.0])
 def test_search_ties_zeros_and_scale(tq, scale):
     """Exact ties (duplicated database rows), zero rows, a zero query, and a
