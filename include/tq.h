@@ -279,6 +279,43 @@ tq_status tq_append_attn_logits_paged(const tq_params *p, const void *x_new, int
                                       int64_t pos, float scale, float *logits, void *workspace,
                                       size_t workspace_bytes, void *stream);
 
+/* The query rotation on its own (page: the query is rotated once, closing
+ * paragraph of "2단계" and "TurboQuant 구현 방법"): the first launch of a dense
+ * tq_attn_logits, which turns the queries into the tables the streaming
+ * launch reads (Pi q, S q and their fixed-point weights).  One preparation
+ * then serves any number of tq_attn_logits_prepared calls, e.g. over a
+ * shared-prefix cache and a per-sequence cache, or over a cache scored in
+ * segments.
+ *   q, q_dtype, batch, n_q_heads, n_kv_heads   as tq_attn_logits
+ *   workspace    device scratch of tq_attn_logits_workspace_size(p, batch,
+ *                n_q_heads, n_kv_heads, 1, 0) bytes (the dense size, which
+ *                does not depend on seq_len); the tables are written into it
+ * Supported: as dense tq_attn_logits.  batch == 0 is a no-op.
+ * Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED, TQ_ERR_HIP. */
+tq_status tq_prepare_queries(const tq_params *p, const void *q, int32_t q_dtype, int32_t batch,
+                             int32_t n_q_heads, int32_t n_kv_heads, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/* Dense logits from queries prepared by tq_prepare_queries: the streaming
+ * launch of tq_attn_logits alone, whose results it gives bit for bit.
+ *   k, row_tokens, seq_len, scale, logits   as tq_attn_logits with topk = 0
+ *   pages        NULL: k holds contiguous streams of row_tokens rows;
+ *                otherwise k is a paged pool read as by tq_attn_logits_paged
+ *                (row_tokens is then ignored)
+ *   workspace    a workspace that tq_prepare_queries filled with the same
+ *                quantiser (p), batch and heads, queued before this call on
+ *                this stream or completed; it is only read, so calls on
+ *                several streams may share it once it is filled.  Tables of
+ *                another shape or quantiser give wrong logits; every access
+ *                still stays inside the workspace.
+ * Supported: as dense tq_attn_logits (paged: as tq_attn_logits_paged).
+ * batch == 0 or seq_len == 0 is a no-op.
+ * Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED, TQ_ERR_HIP. */
+tq_status tq_attn_logits_prepared(const tq_params *p, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                  const tq_packed *k, int64_t row_tokens, const tq_pages *pages,
+                                  int64_t seq_len, float scale, float *logits, const void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
 /* Decode attention output straight from packed values (page: the KV cache
  * holds keys and values, section "TurboQuant란 무엇인가요?", and attention runs
  * from the compressed indices, section "2단계", closing paragraph; the output

@@ -36,7 +36,7 @@ KIND_M = 2
 
 EXPORTED = ["tq_make_codebook", "tq_make_polar_codebook", "tq_make_rotation", "tq_quantize_kv",
             "tq_attn_logits_workspace_size", "tq_attn_logits", "tq_append_attn_logits", "tq_attn_logits_paged",
-            "tq_append_attn_logits_paged",
+            "tq_append_attn_logits_paged", "tq_prepare_queries", "tq_attn_logits_prepared",
             "tq_attn_output_workspace_size", "tq_attn_output", "tq_attn_output_noalloc", "tq_dequantize",
             "tq_probe_sink_words", "tq_probe", "tq_status_string"]
 PROBE_READ, PROBE_WRITE, PROBE_MFMA_F16, PROBE_MFMA_I8 = 0, 1, 2, 3
@@ -86,6 +86,9 @@ def _load():
     lib.tq_append_attn_logits_paged.argtypes = [ctypes.POINTER(Params), vp, i32, vp, i32, i32, i32, i32,
                                                 ctypes.POINTER(Packed), ctypes.POINTER(Pages), i64, f32, vp, vp, sz,
                                                 vp]
+    lib.tq_prepare_queries.argtypes = [ctypes.POINTER(Params), vp, i32, i32, i32, i32, vp, sz, vp]
+    lib.tq_attn_logits_prepared.argtypes = [ctypes.POINTER(Params), i32, i32, i32, ctypes.POINTER(Packed), i64,
+                                            ctypes.POINTER(Pages), i64, f32, vp, vp, sz, vp]
     lib.tq_attn_output_workspace_size.argtypes = [ctypes.POINTER(Params), i32, i32, i32, i64, psz]
     lib.tq_attn_output.argtypes = [ctypes.POINTER(Params), vp, i32, i32, i32, ctypes.POINTER(Packed),
                                    i64, i64, vp, i32, vp, sz, vp]
@@ -190,6 +193,14 @@ class PackedKV:
 
     def bytes_per_vector(self):
         return self.bits * self.d // 8 + (4 if self.mode == MODE_PROD else 2)
+
+
+class PreparedQueries:
+    """Query tables written by Quantizer.prepare_queries (device workspace)
+    and the shape they were prepared for."""
+
+    def __init__(self, workspace, batch, n_q_heads, n_kv_heads):
+        self.workspace, self.batch, self.n_q_heads, self.n_kv_heads = workspace, batch, n_q_heads, n_kv_heads
 
 
 class Quantizer:
@@ -352,6 +363,43 @@ class Quantizer:
                                              float(scale), ctypes.c_void_p(out.data_ptr()), ws, wsb,
                                              _stream_ptr(self.device))
         _check(st, "tq_append_attn_logits_paged")
+        return out
+
+    def prepare_queries(self, q, n_kv_heads, workspace=None):
+        """Run the query preparation of the dense logit call once; returns a
+        PreparedQueries that attn_logits_prepared reads.  ``workspace`` (a
+        uint8 device tensor) receives the tables; by default a new one."""
+        torch = _torch()
+        bsz, hq, _ = q.shape
+        need = self.logits_workspace_size(bsz, hq, n_kv_heads, 1)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=self.device)
+        ws, wsb = self._workspace(need, workspace)
+        st = LIB.tq_prepare_queries(ctypes.byref(self._params), ctypes.c_void_p(q.data_ptr()), _dtype_code(q),
+                                    bsz, hq, n_kv_heads, ws, wsb, _stream_ptr(self.device))
+        _check(st, "tq_prepare_queries")
+        return PreparedQueries(workspace, bsz, hq, n_kv_heads)
+
+    def attn_logits_prepared(self, prepared, cache, seq_len, scale, row_tokens=None, out=None, block_table=None,
+                             page_tokens=None):
+        """Dense logits [batch, n_q_heads, seq_len] of prepared queries over a
+        contiguous cache, or over a paged pool when block_table is given."""
+        torch = _torch()
+        bsz, hq, hkv = prepared.batch, prepared.n_q_heads, prepared.n_kv_heads
+        if out is None:
+            out = torch.empty((bsz, hq, seq_len), dtype=torch.float32, device=self.device)
+        pg = None
+        if block_table is not None:
+            pg = ctypes.byref(self._pages(block_table, page_tokens, cache.capacity // (hkv * page_tokens)))
+            row_tokens = 0
+        elif row_tokens is None:
+            row_tokens = seq_len
+        ws = prepared.workspace
+        st = LIB.tq_attn_logits_prepared(ctypes.byref(self._params), bsz, hq, hkv, ctypes.byref(cache.struct()),
+                                         row_tokens, pg, seq_len, float(scale), ctypes.c_void_p(out.data_ptr()),
+                                         ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
+                                         _stream_ptr(self.device))
+        _check(st, "tq_attn_logits_prepared")
         return out
 
     def search(self, q, cache, n_kv_heads, seq_len, topk, scale=1.0, row_tokens=None, workspace=None):

@@ -717,11 +717,13 @@ hipError_t launch_t(const tqi::LogitArgs &a, hipStream_t s) {
   pa.max_pages = a.max_pages;
   pa.pool_rows = a.pool_rows;
   const int parts = (PROD ? 2 : 1) + (a.x_new != nullptr ? 1 : 0);
-  hipLaunchKernelGGL((logit_prep_kernel<D, LB, PROD>), dim3(n_streams, rts, parts),
-                     dim3(prep_threads<D>()), 0,
-                     s, pa);
-  e = hipGetLastError();
-  if (e == hipSuccess) {
+  if (a.run_prep) {
+    hipLaunchKernelGGL((logit_prep_kernel<D, LB, PROD>), dim3(n_streams, rts, parts),
+                       dim3(prep_threads<D>()), 0,
+                       s, pa);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess && a.run_stream) {
     StreamArgs sa;
     sa.table = pa.table;
     sa.consts = pa.consts;

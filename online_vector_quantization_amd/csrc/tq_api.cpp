@@ -370,6 +370,87 @@ extern "C" tq_status tq_append_attn_logits_paged(const tq_params *p, const void 
   return hip_status(tqi::launch_logits(p->d, lloyd_bits(p), prod, a, (hipStream_t)stream));
 }
 
+extern "C" tq_status tq_prepare_queries(const tq_params *p, const void *q, int32_t q_dtype, int32_t batch,
+                                        int32_t n_q_heads, int32_t n_kv_heads, void *workspace,
+                                        size_t workspace_bytes, void *stream) {
+  tq_status st = check_logit_args(p, batch, n_q_heads, n_kv_heads, 1, 0);
+  if (st != TQ_OK) return st;
+  const bool prod = p->mode == TQ_MODE_PROD;
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_ERR_INVALID;
+  st = logits_shape(p, batch, n_q_heads, n_kv_heads, 1, 0);
+  if (st != TQ_OK) return st;
+  if (batch == 0) return TQ_OK;
+  if (q == nullptr) return TQ_ERR_INVALID;
+  if (prod && p->qjl == nullptr) return TQ_ERR_INVALID;
+  st = check_workspace(workspace, workspace_bytes, logits_ws_bytes(p, batch, n_q_heads, n_kv_heads, 1, 0));
+  if (st != TQ_OK) return st;
+  tqi::LogitArgs a;
+  a.q = q;
+  a.q_f32 = q_dtype == TQ_F32;
+  a.batch = batch;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.pi = p->pi;
+  a.s_mat = p->qjl;
+  a.centroids = p->centroids;
+  a.codes = nullptr;
+  a.norm = nullptr;
+  a.rnorm = nullptr;
+  a.row_tokens = 0;
+  a.seq_len = 0;
+  a.scale = 0.0f;
+  a.logits = nullptr;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
+  a.run_stream = false;
+  return hip_status(tqi::launch_logits(p->d, lloyd_bits(p), prod, a, (hipStream_t)stream));
+}
+
+extern "C" tq_status tq_attn_logits_prepared(const tq_params *p, int32_t batch, int32_t n_q_heads,
+                                             int32_t n_kv_heads, const tq_packed *k, int64_t row_tokens,
+                                             const tq_pages *pages, int64_t seq_len, float scale, float *logits,
+                                             const void *workspace, size_t workspace_bytes, void *stream) {
+  tq_status st = check_logit_args(p, batch, n_q_heads, n_kv_heads, seq_len, 0);
+  if (st != TQ_OK) return st;
+  const bool prod = p->mode == TQ_MODE_PROD;
+  if (k == nullptr) return TQ_ERR_INVALID;
+  if (pages == nullptr && row_tokens < seq_len) return TQ_ERR_INVALID;
+  st = logits_shape(p, batch, n_q_heads, n_kv_heads, seq_len, 0);
+  if (st != TQ_OK) return st;
+  tqi::LogitArgs a;
+  if (pages != nullptr) {
+    st = paged_args(p, batch, n_kv_heads, pages, seq_len, a);
+    if (st != TQ_OK) return st;
+  } else {
+    a.row_tokens = row_tokens;
+  }
+  if (batch == 0 || seq_len == 0) return TQ_OK;
+  if (logits == nullptr || k->codes == nullptr || k->norm == nullptr) return TQ_ERR_INVALID;
+  if (prod && k->rnorm == nullptr) return TQ_ERR_INVALID;
+  st = check_workspace(workspace, workspace_bytes, logits_ws_bytes(p, batch, n_q_heads, n_kv_heads, seq_len, 0));
+  if (st != TQ_OK) return st;
+  if ((uintptr_t)k->codes & 3u) return TQ_ERR_UNSUPPORTED;
+  a.q = nullptr;
+  a.q_f32 = false;
+  a.batch = batch;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.pi = p->pi;
+  a.s_mat = p->qjl;
+  a.centroids = p->centroids;
+  a.codes = k->codes;
+  a.norm = k->norm;
+  a.rnorm = k->rnorm;
+  a.seq_len = seq_len;
+  a.scale = scale;
+  a.logits = logits;
+  // the streaming launch only reads the tables
+  a.workspace = const_cast<void *>(workspace);
+  a.workspace_bytes = workspace_bytes;
+  a.run_prep = false;
+  return hip_status(tqi::launch_logits(p->d, lloyd_bits(p), prod, a, (hipStream_t)stream));
+}
+
 extern "C" tq_status tq_attn_output_workspace_size(const tq_params *p, int32_t batch, int32_t n_q_heads,
                                                    int32_t n_kv_heads, int64_t seq_len, size_t *bytes) {
   if (bytes == nullptr) return TQ_ERR_INVALID;

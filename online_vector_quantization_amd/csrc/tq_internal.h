@@ -57,6 +57,11 @@ struct LogitArgs {
   // caller-owned device scratch (query tables; for top-k also partial lists)
   void *workspace = nullptr;
   size_t workspace_bytes = 0;
+  // dense logits run two launches: the query preparation, which writes the
+  // tables into the workspace, and the streaming launch, which reads them;
+  // either can run alone (q is unused without the first, codes and logits
+  // without the second)
+  bool run_prep = true, run_stream = true;
 };
 
 // Shapes the dense logit kernels take (GQA group <= 16, d in {64, 128, 256},

@@ -766,3 +766,56 @@ def test_paged_logits_and_append_parity(tq, d, bits, mode, bsz, hkv, group, page
             assert np.all(gl[:, ~live] == 0.0)
             if live.any():
                 check_logits(gl[:, live], want[b, h * group:(h + 1) * group, :cols][:, live], scale, nrm[live], qq)
+
+
+PREPARED_CASES = [
+    # d, bits, mode, batch, kv heads, group, seq, q dtype
+    (128, 4, "prod", 2, 2, 4, 2049, "bf16"),
+    (128, 3, "mse", 1, 2, 5, 1000, "f32"),
+    (64, 3, "prod", 1, 2, 4, 700, "bf16"),
+    (256, 2, "mse", 1, 1, 8, 513, "f32"),
+]
+
+
+@pytest.mark.parametrize("d,bits,mode,bsz,hkv,group,seq,qdtype", PREPARED_CASES)
+def test_prepared_logits_match_one_shot(tq, d, bits, mode, bsz, hkv, group, seq, qdtype):
+    """One query preparation serves three streaming calls: the cache it came
+    with (checked against the oracle), a second cache scored with another
+    scale, and the first cache scattered into a paged pool.  Each result equals
+    the matching one-shot call bit for bit."""
+    ot, mcode, keys, q64, qt, ref = _gqa_case(d, bits, mode, bsz, hkv, group, seq, qdtype)
+    qz = tq.Quantizer(d, bits, mcode, seed=0, device=DEV)
+    cache = cache_from_oracle(tq, ref, d, bits, mcode, DEV)
+    scale = 1.0 / np.sqrt(d)
+    prep = qz.prepare_queries(qt, n_kv_heads=hkv)
+    got = qz.attn_logits_prepared(prep, cache, seq, scale)
+    one = qz.attn_logits(qt, cache, n_kv_heads=hkv, seq_len=seq, scale=scale)
+    assert torch.equal(got, one)
+    got = got.cpu().numpy()
+    codes = ref["codes"].reshape(bsz, hkv, seq, -1)
+    norm = ref["norm"].reshape(bsz, hkv, seq)
+    for b in range(bsz):
+        for h in range(hkv):
+            kw = {}
+            if mcode == oqz.MODE_PROD:
+                kw = dict(rnorm=ref["rnorm"].reshape(bsz, hkv, seq)[b, h], s_mat=ot.s)
+            qq = q64[b, h * group:(h + 1) * group]
+            want = oqz.logits_rotated(qq, codes[b, h], norm[b, h], ot.pi, ot.c, mcode, scale, **kw)
+            check_logits(got[b, h * group:(h + 1) * group], want, scale, norm[b, h], qq)
+    # a second cache (other keys, a shorter prefix of rows) and another scale
+    rng = np.random.default_rng(seq + 11)
+    seq2 = seq // 2 + 1
+    keys2 = rng.standard_normal((bsz * hkv * seq2, d)).astype(np.float32)
+    cache2 = qz.quantize(torch.from_numpy(keys2).to(DEV))
+    got2 = qz.attn_logits_prepared(prep, cache2, seq2, -0.75)
+    assert torch.equal(got2, qz.attn_logits(qt, cache2, n_kv_heads=hkv, seq_len=seq2, scale=-0.75))
+    # the first cache as a paged pool
+    page = 64
+    pool, table = _scatter_pool(ref, d, bits, mcode, bsz, hkv, seq, page, 3, seed=seq + 1)
+    pc = tq.PackedKV.from_tensors(d, bits, mcode, torch.from_numpy(pool["codes"]).to(DEV),
+                                  dev_u16(pool["norm"], DEV),
+                                  dev_u16(pool["rnorm"], DEV) if mcode == oqz.MODE_PROD else None)
+    tt = torch.from_numpy(table).to(DEV)
+    got3 = qz.attn_logits_prepared(prep, pc, seq, scale, block_table=tt, page_tokens=page)
+    assert torch.equal(got3, qz.attn_logits_paged(qt, pc, tt, page, hkv, seq, scale))
+    assert torch.equal(got3, one)

@@ -279,6 +279,56 @@ def test_paged_calls_validate_before_launch(tq):
 
 
 
+def test_prepared_calls_validate_before_launch(tq):
+    """tq_prepare_queries / tq_attn_logits_prepared: bad arguments, short or
+    misaligned workspaces, unsupported shapes and bad pages are refused
+    before any launch; empty calls are no-ops."""
+    lib = tq.LIB
+    dummy = ctypes.c_void_p(16)
+    f = ctypes.c_float(1.0)
+    pp = tq.Params(128, 3, tq.MODE_PROD, 0, dummy, dummy, dummy, dummy, dummy)
+    pk = tq.Packed(dummy, dummy, dummy)
+    need = ctypes.c_size_t(0)
+    assert lib.tq_attn_logits_workspace_size(ctypes.byref(pp), 2, 32, 8, 1, 0, ctypes.byref(need)) == tq.TQ_OK
+    ws = ctypes.c_void_p(1 << 20)
+
+    def prep(batch=2, hq=32, hkv=8, q=dummy, dt=0, w=ws, nb=need.value, params=pp):
+        return lib.tq_prepare_queries(ctypes.byref(params), q, dt, batch, hq, hkv, w, nb, None)
+
+    assert prep(hq=30) == tq.TQ_ERR_INVALID                       # heads not a multiple of KV heads
+    assert prep(batch=-1) == tq.TQ_ERR_INVALID
+    assert prep(dt=7) == tq.TQ_ERR_INVALID
+    assert prep(q=None) == tq.TQ_ERR_INVALID
+    assert prep(nb=need.value - 1) == tq.TQ_ERR_INVALID           # short workspace
+    assert prep(w=None) == tq.TQ_ERR_INVALID
+    assert prep(w=ctypes.c_void_p((1 << 20) + 64)) == tq.TQ_ERR_UNSUPPORTED   # misaligned
+    assert prep(hq=136) == tq.TQ_ERR_UNSUPPORTED                  # 17 query heads per KV head
+    assert prep(batch=0, q=None, w=None, nb=0) == tq.TQ_OK        # empty: no-op
+    polar = tq.Params(128, 3, tq.MODE_POLAR, 0, dummy, dummy, dummy, dummy, dummy)
+    assert prep(params=polar) == tq.TQ_ERR_UNSUPPORTED
+    no_s = tq.Params(128, 3, tq.MODE_PROD, 0, dummy, None, dummy, dummy, dummy)
+    assert prep(params=no_s) == tq.TQ_ERR_INVALID
+
+    def run(batch=2, hq=32, hkv=8, k=pk, row_tokens=4096, pages=None, seq_len=4096, out=dummy, w=ws,
+            nb=need.value):
+        return lib.tq_attn_logits_prepared(ctypes.byref(pp), batch, hq, hkv, ctypes.byref(k) if k else None,
+                                           row_tokens, ctypes.byref(pages) if pages is not None else None,
+                                           seq_len, f, out, w, nb, None)
+
+    assert run(k=None) == tq.TQ_ERR_INVALID
+    assert run(row_tokens=4095) == tq.TQ_ERR_INVALID              # seq_len past the stream's rows
+    assert run(out=None) == tq.TQ_ERR_INVALID
+    assert run(nb=need.value - 1) == tq.TQ_ERR_INVALID
+    assert run(k=tq.Packed(dummy, dummy, None)) == tq.TQ_ERR_INVALID   # inner-product keys need rnorm
+    assert run(k=tq.Packed(ctypes.c_void_p(18), dummy, dummy)) == tq.TQ_ERR_UNSUPPORTED   # codes not 4-byte aligned
+    assert run(seq_len=0, out=None, w=None, nb=0) == tq.TQ_OK
+    assert run(batch=0, out=None, w=None, nb=0) == tq.TQ_OK
+    assert run(pages=tq.Pages(dummy, 48, 64, 100)) == tq.TQ_ERR_INVALID          # page not a multiple of 64
+    assert run(pages=tq.Pages(dummy, 64, 63, 100)) == tq.TQ_ERR_INVALID          # 4096 tokens > 63 pages of 64
+    assert run(pages=tq.Pages(dummy, 256, 16, 1 << 20)) == tq.TQ_ERR_UNSUPPORTED  # pool codes past 2^31 bytes
+    assert run(row_tokens=0, pages=tq.Pages(dummy, 64, 64, 100), seq_len=0, out=None, w=None, nb=0) == tq.TQ_OK
+
+
 def test_probe_calls_validate_before_launch(tq):
     """tq_probe refuses bad kinds, short sinks, unaligned or empty stream
     buffers and out-of-range loop counts before any launch."""
