@@ -819,3 +819,23 @@ def test_prepared_logits_match_one_shot(tq, d, bits, mode, bsz, hkv, group, seq,
     got3 = qz.attn_logits_prepared(prep, pc, seq, scale, block_table=tt, page_tokens=page)
     assert torch.equal(got3, qz.attn_logits_paged(qt, pc, tt, page, hkv, seq, scale))
     assert torch.equal(got3, one)
+
+
+def test_prepared_queries_shared_by_two_streams(tq):
+    """Tables prepared once are only read by the streaming calls: two calls
+    queued on two other streams at once give the one-shot results."""
+    d, bits, mode, bsz, hkv, group, seq = 128, 3, "prod", 1, 2, 4, 3000
+    ot, mcode, keys, q64, qt, ref = _gqa_case(d, bits, mode, bsz, hkv, group, seq, "bf16")
+    qz = tq.Quantizer(d, bits, mcode, seed=0, device=DEV)
+    cache = cache_from_oracle(tq, ref, d, bits, mcode, DEV)
+    one = qz.attn_logits(qt, cache, n_kv_heads=hkv, seq_len=seq, scale=0.125)
+    prep = qz.prepare_queries(qt, n_kv_heads=hkv)
+    torch.cuda.synchronize()
+    outs = []
+    streams = [torch.cuda.Stream(device=DEV) for _ in range(2)]
+    for st in streams:
+        with torch.cuda.stream(st):
+            outs.append(qz.attn_logits_prepared(prep, cache, seq, 0.125))
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o, one)
