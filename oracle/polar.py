@@ -39,6 +39,8 @@ Readings (the page gives the idea only):
   angle 0 (atan2(0, 0) = 0); it reconstructs to 0 through n = 0.
 * Reconstruction: y_hat from the centroid angles from the top down (radius
   1), x_hat = n16 Pi^T y_hat; y_hat is a unit vector by construction.
+* Logits: scale * <q, x_hat> (``logits``, the definition); ``logits_rotated``
+  reaches the same value from the rotated query without forming x_hat.
 """
 
 import functools
@@ -221,3 +223,36 @@ def dequantize(codes, norm, pi):
         off += cnt
     y = from_angles(phi, psis)
     return qz.from_fp16_bits(norm)[:, None] * (y @ pi)
+
+
+def logits(q, codes, norm, pi, scale):
+    """scale * <q, x_hat> for every query row of q [m, d] and packed key row:
+    the plain definition, through the reconstruction (logits [m, n])."""
+    q = np.asarray(q, dtype=np.float64)
+    return scale * (q @ dequantize(codes, norm, pi).T)
+
+
+def logits_rotated(q, codes, norm, pi, scale):
+    """The same logits through the query rotated once (page: the query is
+    rotated once, section "2단계" closing paragraph) and a bottom-up pass over
+    the angle tree, without forming y_hat: a level-1 pair i contributes
+    a_i = q'_2i cos(phi_i) + q'_2i+1 sin(phi_i); an angle psi of level l joins
+    the partial sums of the two nodes it splits as cos(psi) a_2i + sin(psi)
+    a_2i+1; the last one left is <q', y_hat>, and the logit is
+    scale * n16 * <q', y_hat> with q' = Pi q."""
+    q = np.asarray(q, dtype=np.float64)
+    d = pi.shape[0]
+    L = n_levels(d)
+    books = codebooks(d)
+    idx1, idx_up = unpack(codes, d)
+    qr = q @ pi.T                                        # rows of Pi q
+    phi = books[0][0][idx1]                              # [n, d/2]
+    # [m, n, d/2]: level-1 partial sums of every query and key
+    a = qr[:, None, 0::2] * np.cos(phi)[None] + qr[:, None, 1::2] * np.sin(phi)[None]
+    off = 0
+    for level in range(2, L + 1):
+        cnt = d >> level
+        psi = books[level - 1][0][idx_up[:, off:off + cnt]][None]    # [1, n, cnt]
+        a = np.cos(psi) * a[:, :, 0::2] + np.sin(psi) * a[:, :, 1::2]
+        off += cnt
+    return scale * qz.from_fp16_bits(norm)[None, :] * a[:, :, 0]

@@ -154,3 +154,59 @@ def test_zero_vector_and_distortion():
     assert 0.98 < cos.mean() < 0.99                     # the page: about 0.983 at 3 bits
     yh = xh[1:] @ pi.T / qz.from_fp16_bits(ref["norm"][1:])[:, None]
     np.testing.assert_allclose(np.linalg.norm(yh, axis=1), 1.0, rtol=1e-13)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_logits_rotated_form_equals_dequantize_then_dot(d):
+    """The bottom-up pass over the angle tree with the rotated query equals
+    the plain definition (reconstruct x_hat, then dot): a dropped level, a
+    swapped cos/sin or a wrong slot in either fails."""
+    pi = rot.haar_rotation(d, 3)
+    rng = np.random.default_rng(d)
+    x = rng.standard_normal((300, d)) * np.exp(rng.standard_normal(d))
+    x[7] = 0.0
+    ref = pq.quantize(x, pi)
+    q = rng.standard_normal((5, d))
+    want = pq.logits(q, ref["codes"], ref["norm"], pi, 0.3)
+    got = pq.logits_rotated(q, ref["codes"], ref["norm"], pi, 0.3)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+    assert np.all(got[:, 7] == 0.0)
+
+
+def test_logits_closed_case():
+    """Pi = I, x = 3 e_0 and x = e_1 + e_2 at d = 64: every angle is known by hand.
+    e_0: every level-1 angle is 0 (sector 0, midpoint pi/16), every higher
+    angle 0 (lowest cell), so y_hat_0 = cos(pi/16) prod_l cos(c_l[0]),
+    y_hat_1 = sin(pi/16) prod_l cos(c_l[0]) and y_hat_2 = cos(pi/16)
+    sin(c_2[0]) prod_{l>2} cos(c_l[0]).  e_1 + e_2: pair 0 has angle
+    pi/2 (sector 4), pair 1 angle 0 (sector 0), the level-2 angle of pairs 0
+    and 1 is pi/4 (cell 2 of its 4: the law is symmetric about pi/4 and ties
+    go up), every higher angle 0."""
+    d = 64
+    pi = np.eye(d)
+    books = pq.codebooks(d)
+    up0 = np.prod([math.cos(books[lv - 1][0][0]) for lv in range(2, pq.n_levels(d) + 1)])
+    x = np.zeros((2, d))
+    x[0, 0] = 3.0
+    x[1, 1] = x[1, 2] = 1.0
+    ref = pq.quantize(x, pi)
+    n16 = qz.from_fp16_bits(ref["norm"])
+    assert n16[0] == 3.0
+    q = np.zeros((3, d))
+    q[0, 0] = 1.0
+    q[1, 1] = 1.0
+    q[2, 2] = 1.0
+    got = pq.logits_rotated(q, ref["codes"], ref["norm"], pi, 0.5)
+    c16, s16 = math.cos(math.pi / 16), math.sin(math.pi / 16)
+    assert abs(got[0, 0] - 0.5 * 3.0 * c16 * up0) < 1e-14
+    assert abs(got[1, 0] - 0.5 * 3.0 * s16 * up0) < 1e-14
+    # coordinate 2 is pair 1 (angle 0, sector 0): its radius takes sin of the
+    # level-2 centroid, not cos, and the reconstruction does not vanish there
+    rest = np.prod([math.cos(books[lv - 1][0][0]) for lv in range(3, pq.n_levels(d) + 1)])
+    assert abs(got[2, 0] - 0.5 * 3.0 * math.sin(books[1][0][0]) * rest * c16) < 1e-14
+    # e_1 + e_2: y_hat_1 = cos(psi_2) * rest * sin(9 pi/16), y_hat_2 = sin(psi_2) * rest * cos(pi/16)
+    assert ref["idx1"][1, 0] == 4 and ref["idx1"][1, 1] == 0 and ref["idx_up"][1, 0] == 2
+    c2 = books[1][0][2]
+    sq2 = n16[1]
+    assert abs(got[1, 1] - 0.5 * sq2 * math.cos(c2) * rest * math.sin(9 * math.pi / 16)) < 1e-14
+    assert abs(got[2, 1] - 0.5 * sq2 * math.sin(c2) * rest * math.cos(math.pi / 16)) < 1e-14
