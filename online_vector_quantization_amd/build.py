@@ -18,7 +18,7 @@ LIB = os.path.join(LIBDIR, "libtq.so")
 BUILD = os.path.join(ROOT, "_build")
 
 SOURCES = ["host_math.cpp", "tq_api.cpp", "quantize.hip", "logits.hip", "dequant.hip", "search.hip",
-           "attend.hip", "probes.hip"]
+           "attend.hip", "probes.hip", "polar_logits.hip"]
 
 # Packed-fp32 VALU ops are disabled for all device code (they are avoided on
 # this hardware); the host pass warns that it does not know the feature.

@@ -63,7 +63,11 @@ tq_status check_logit_args(const tq_params *p, int32_t batch, int32_t n_q_heads,
 // TQ_OK when a kernel takes the shape, TQ_ERR_UNSUPPORTED otherwise.
 tq_status logits_shape(const tq_params *p, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
                        int64_t seq_len, int32_t topk) {
-  if (p->mode == TQ_MODE_POLAR) return TQ_ERR_UNSUPPORTED;
+  if (p->mode == TQ_MODE_POLAR) {
+    if (topk > 0) return TQ_ERR_UNSUPPORTED;
+    return tqi::polar_logits_supported(p->d, n_q_heads / n_kv_heads, seq_len, (int64_t)batch * n_kv_heads)
+               ? TQ_OK : TQ_ERR_UNSUPPORTED;
+  }
   const bool prod = p->mode == TQ_MODE_PROD;
   if (topk > 0) {
     if (prod) return TQ_ERR_UNSUPPORTED;
@@ -77,6 +81,8 @@ tq_status logits_shape(const tq_params *p, int32_t batch, int32_t n_q_heads, int
 size_t logits_ws_bytes(const tq_params *p, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
                        int64_t seq_len, int32_t topk) {
   if (batch == 0 || seq_len == 0) return 0;
+  if (p->mode == TQ_MODE_POLAR)
+    return tqi::polar_logits_workspace_bytes(p->d, (int64_t)batch * n_kv_heads, n_q_heads / n_kv_heads);
   if (topk > 0) return tqi::search_workspace_bytes(p->d, lloyd_bits(p), batch, n_q_heads, n_kv_heads, seq_len);
   return tqi::logits_workspace_bytes(p->d, lloyd_bits(p), p->mode == TQ_MODE_PROD,
                                      (int64_t)batch * n_kv_heads, n_q_heads / n_kv_heads);
@@ -198,6 +204,8 @@ extern "C" tq_status tq_attn_logits(const tq_params *p, const void *q, int32_t q
     sa.topk = topk;
     sa.topk_idx = topk_idx;
     e = tqi::launch_search(p->d, lloyd_bits(p), sa, (hipStream_t)stream);
+  } else if (p->mode == TQ_MODE_POLAR) {
+    e = tqi::launch_polar_logits(p->d, a, (hipStream_t)stream);
   } else {
     e = tqi::launch_logits(p->d, lloyd_bits(p), prod, a, (hipStream_t)stream);
   }
@@ -216,6 +224,7 @@ extern "C" tq_status tq_append_attn_logits(const tq_params *p, const void *x_new
   if ((q_dtype != TQ_F32 && q_dtype != TQ_BF16) || (x_dtype != TQ_F32 && x_dtype != TQ_BF16))
     return TQ_ERR_INVALID;
   if (pos < 0 || pos >= row_tokens) return TQ_ERR_INVALID;
+  if (p->mode == TQ_MODE_POLAR) return TQ_ERR_UNSUPPORTED;   // dense one-shot logits only
   st = logits_shape(p, batch, n_q_heads, n_kv_heads, pos + 1, 0);
   if (st != TQ_OK) return st;
   if (batch == 0) return TQ_OK;
@@ -288,6 +297,7 @@ extern "C" tq_status tq_attn_logits_paged(const tq_params *p, const void *q, int
   const bool prod = p->mode == TQ_MODE_PROD;
   if (pool == nullptr) return TQ_ERR_INVALID;
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_ERR_INVALID;
+  if (p->mode == TQ_MODE_POLAR) return TQ_ERR_UNSUPPORTED;   // dense one-shot logits only
   st = logits_shape(p, batch, n_q_heads, n_kv_heads, seq_len, 0);
   if (st != TQ_OK) return st;
   tqi::LogitArgs a;
@@ -329,6 +339,7 @@ extern "C" tq_status tq_append_attn_logits_paged(const tq_params *p, const void 
   if (pool == nullptr || pos < 0) return TQ_ERR_INVALID;
   if ((q_dtype != TQ_F32 && q_dtype != TQ_BF16) || (x_dtype != TQ_F32 && x_dtype != TQ_BF16))
     return TQ_ERR_INVALID;
+  if (p->mode == TQ_MODE_POLAR) return TQ_ERR_UNSUPPORTED;   // dense one-shot logits only
   st = logits_shape(p, batch, n_q_heads, n_kv_heads, pos + 1, 0);
   if (st != TQ_OK) return st;
   tqi::LogitArgs a;
@@ -377,6 +388,7 @@ extern "C" tq_status tq_prepare_queries(const tq_params *p, const void *q, int32
   if (st != TQ_OK) return st;
   const bool prod = p->mode == TQ_MODE_PROD;
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_ERR_INVALID;
+  if (p->mode == TQ_MODE_POLAR) return TQ_ERR_UNSUPPORTED;   // dense one-shot logits only
   st = logits_shape(p, batch, n_q_heads, n_kv_heads, 1, 0);
   if (st != TQ_OK) return st;
   if (batch == 0) return TQ_OK;
@@ -415,6 +427,7 @@ extern "C" tq_status tq_attn_logits_prepared(const tq_params *p, int32_t batch, 
   const bool prod = p->mode == TQ_MODE_PROD;
   if (k == nullptr) return TQ_ERR_INVALID;
   if (pages == nullptr && row_tokens < seq_len) return TQ_ERR_INVALID;
+  if (p->mode == TQ_MODE_POLAR) return TQ_ERR_UNSUPPORTED;   // dense one-shot logits only
   st = logits_shape(p, batch, n_q_heads, n_kv_heads, seq_len, 0);
   if (st != TQ_OK) return st;
   tqi::LogitArgs a;

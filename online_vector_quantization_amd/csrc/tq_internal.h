@@ -70,6 +70,14 @@ bool logits_supported(int d, int lbits, bool prod, int group, int64_t seq_len);
 size_t logits_workspace_bytes(int d, int lbits, bool prod, int64_t n_streams, int group);
 hipError_t launch_logits(int d, int lbits, bool prod, const LogitArgs &a, hipStream_t s);
 
+// Dense logits from polar-format keys (d in {64, 128, 256}, GQA group <= 16,
+// 32-bit byte ranges of one stream's codes and logits): query preparation
+// and streaming launch; the workspace holds the rotated queries and the
+// cos/sin table of the centroid angles.
+bool polar_logits_supported(int d, int group, int64_t seq_len, int64_t n_streams);
+size_t polar_logits_workspace_bytes(int d, int64_t n_streams, int group);
+hipError_t launch_polar_logits(int d, const LogitArgs &a, hipStream_t s);
+
 struct SearchArgs {
   LogitArgs base;
   int topk;

@@ -612,9 +612,18 @@ def test_polar_round_trip_and_unsupported_calls(tq):
     xs = x.cpu().numpy().astype(np.float64)
     cos = np.sum(xs * got, 1) / np.linalg.norm(xs, axis=1) / np.linalg.norm(got, axis=1)
     assert 0.98 < cos.mean() < 0.99
+    # the polar format has dense one-shot logits only: no top-k, append,
+    # paged or prepared-query calls
     q = torch.zeros((1, 4, d), device=DEV)
     with pytest.raises(tq.TQError):
-        qz.attn_logits(q, cache, n_kv_heads=1, seq_len=n, scale=1.0)
+        qz.search(q, cache, n_kv_heads=1, seq_len=n, topk=10)
+    with pytest.raises(tq.TQError):
+        qz.append_attn_logits(x[:1].view(1, 1, d), q, cache, n_kv_heads=1, pos=0, scale=1.0, row_tokens=n)
+    with pytest.raises(tq.TQError):
+        qz.prepare_queries(q, n_kv_heads=1)
+    table = torch.zeros((1, n // 64), dtype=torch.int32, device=DEV)
+    with pytest.raises(tq.TQError):
+        qz.attn_logits_paged(q, cache, table, 64, 1, n, 1.0)
 
 
 @pytest.mark.parametrize("d", [64, 256])
@@ -839,3 +848,83 @@ def test_prepared_queries_shared_by_two_streams(tq):
     torch.cuda.synchronize()
     for o in outs:
         assert torch.equal(o, one)
+
+
+POLAR_LOGIT_CASES = [
+    # d, batch, kv heads, group, seq, q dtype
+    (128, 1, 2, 4, 3000, "bf16"),
+    (128, 2, 1, 8, 1000, "f32"),
+    (128, 1, 1, 1, 257, "f32"),
+    (64, 1, 2, 3, 777, "bf16"),
+    (64, 1, 1, 16, 513, "f32"),
+    (256, 1, 2, 4, 700, "bf16"),
+    (256, 1, 1, 12, 300, "f32"),
+]
+
+
+@pytest.mark.parametrize("d,bsz,hkv,group,seq,qdtype", POLAR_LOGIT_CASES)
+def test_polar_logits_parity(tq, d, bsz, hkv, group, seq, qdtype):
+    """Dense logits from oracle-packed polar keys (zero rows included) against
+    the oracle's definition, scale * <q, x_hat>: GQA groups 1 to 16, ragged
+    lengths, bf16 and fp32 queries, d = 64, 128, 256."""
+    from oracle import polar as opq
+    from oracle import rotation as orot
+    pi = orot.haar_rotation(d, 0)
+    rng = np.random.default_rng(200 + seq + group)
+    scales = np.exp(rng.standard_normal((hkv, d)))
+    keys = (rng.standard_normal((bsz, hkv, seq, d)) * scales[None, :, None, :]).reshape(-1, d)
+    keys[5] = 0.0
+    ref = opq.quantize(keys, pi)
+    q = rng.standard_normal((bsz, hkv * group, d)) * np.repeat(scales, group, axis=0)[None]
+    if qdtype == "bf16":
+        qb = bf16_bits(q.astype(np.float32))
+        q64 = bf16_to_f32(qb).astype(np.float64)
+        qt = dev_bf16(qb, DEV)
+    else:
+        q64 = q.astype(np.float32).astype(np.float64)
+        qt = torch.from_numpy(q64.astype(np.float32)).to(DEV)
+    qz = tq.Quantizer(d, 3, tq.MODE_POLAR, seed=0, device=DEV)
+    cache = tq.PackedKV.from_tensors(d, 3, tq.MODE_POLAR, torch.from_numpy(ref["codes"]).to(DEV),
+                                     dev_u16(ref["norm"], DEV))
+    scale = 1.0 / np.sqrt(d)
+    out = qz.attn_logits(qt, cache, n_kv_heads=hkv, seq_len=seq, scale=scale).cpu().numpy()
+    codes = ref["codes"].reshape(bsz, hkv, seq, -1)
+    norm = ref["norm"].reshape(bsz, hkv, seq)
+    for b in range(bsz):
+        for h in range(hkv):
+            qq = q64[b, h * group:(h + 1) * group]
+            want = opq.logits(qq, codes[b, h], norm[b, h], pi, scale)
+            live = norm[b, h] != 0                     # zero keys: logit exactly 0
+            got = out[b, h * group:(h + 1) * group]
+            check_logits(got[:, live], want[:, live], scale, norm[b, h][live], qq)
+            assert np.all(got[:, ~live] == 0.0)
+    assert norm[0, 0, 5] == 0
+
+
+def test_polar_logits_end_to_end_and_row_capacity(tq):
+    """GPU polar quantisation, then logits over streams of capacity 600 holding
+    437 tokens, against the oracle's logits of the GPU's own codes (decoding
+    is exact given the codes) and against the unquantised inner products
+    (cosine of the logit rows)."""
+    from oracle import polar as opq
+    from oracle import rotation as orot
+    d, hkv, group, cap, seq = 128, 2, 4, 600, 437
+    rng = np.random.default_rng(77)
+    x = (rng.standard_normal((hkv * cap, d)) * 1.5).astype(np.float32)
+    qz = tq.Quantizer(d, 3, tq.MODE_POLAR, seed=0, device=DEV)
+    cache = qz.quantize(torch.from_numpy(x).to(DEV))
+    q = rng.standard_normal((1, hkv * group, d)).astype(np.float32)
+    out = qz.attn_logits(torch.from_numpy(q).to(DEV), cache, n_kv_heads=hkv, seq_len=seq, scale=1.0,
+                         row_tokens=cap).cpu().numpy()
+    assert out.shape == (1, hkv * group, seq)
+    pi = orot.haar_rotation(d, 0)
+    codes = cache.codes.cpu().numpy()
+    norm = cache.norm.cpu().numpy().view(np.uint16)
+    for h in range(hkv):
+        sl = slice(h * cap, h * cap + seq)
+        qq = q[0, h * group:(h + 1) * group].astype(np.float64)
+        want = opq.logits(qq, codes[sl], norm[sl], pi, 1.0)
+        check_logits(out[0, h * group:(h + 1) * group], want, 1.0, norm[sl], qq)
+        exact = qq @ x[sl].astype(np.float64).T
+        cos = np.sum(exact * want, 1) / np.linalg.norm(exact, axis=1) / np.linalg.norm(want, axis=1)
+        assert np.all(cos > 0.95)

@@ -329,6 +329,33 @@ def test_prepared_calls_validate_before_launch(tq):
     assert run(row_tokens=0, pages=tq.Pages(dummy, 64, 64, 100), seq_len=0, out=None, w=None, nb=0) == tq.TQ_OK
 
 
+def test_polar_logit_shapes_and_workspace(tq):
+    """Polar-format keys: dense logits take d in {64, 128, 256} and GQA groups
+    up to 16; the workspace holds the rotated queries (fp32) and the cos/sin
+    table of the centroid angles; top-k is refused."""
+    lib = tq.LIB
+    dummy = ctypes.c_void_p(16)
+
+    def size(d, batch=2, hq=32, hkv=8, seq=4096, topk=0):
+        pp = tq.Params(d, 3, tq.MODE_POLAR, 0, dummy, None, None, dummy, dummy)
+        n = ctypes.c_size_t(0)
+        st = lib.tq_attn_logits_workspace_size(ctypes.byref(pp), batch, hq, hkv, seq, topk, ctypes.byref(n))
+        return st, n.value
+
+    def al(x):
+        return (x + 255) // 256 * 256
+
+    for d, levels in ((64, 6), (128, 7), (256, 8)):
+        st, n = size(d)
+        assert st == tq.TQ_OK and n == al(16 * 4 * d * 4) + al((16 + 4 * (levels - 1)) * 8)
+    assert size(128, hq=8 * 17)[0] == tq.TQ_ERR_UNSUPPORTED        # 17 query heads per KV head
+    assert size(96)[0] == tq.TQ_ERR_UNSUPPORTED
+    assert size(128, topk=10)[0] == tq.TQ_ERR_UNSUPPORTED
+    assert size(128, seq=0) == (tq.TQ_OK, 0)
+    # logits of one stream past 2^31 bytes
+    assert size(128, batch=1, hq=16, hkv=1, seq=1 << 25)[0] == tq.TQ_ERR_UNSUPPORTED
+
+
 def test_probe_calls_validate_before_launch(tq):
     """tq_probe refuses bad kinds, short sinks, unaligned or empty stream
     buffers and out-of-range loop counts before any launch."""
