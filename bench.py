@@ -342,6 +342,14 @@ def decode_workload(torch, tq, args, device):
                                 ["quantize.hip", "tq_device.h"])
     extras["polar_dequantize"] = (lambda i: qp.dequantize(cp, n, out=vhat_p), n * (rb_p + 2 * d), "dequant_kernel",
                                   ["dequant.hip", "tq_device.h"])
+    # Logits straight from polar-format keys (the same keys, 3 bits per
+    # coordinate): the angle-tree walk, one key per thread.
+    cpk = qp.new_cache(n)
+    qp.quantize(k, out=cpk)
+    logits4 = torch.empty_like(s0["logits"])
+    extras["polar_attn_logits"] = (lambda i: qp.attn_logits(q, cpk, heads, seq, scale, out=logits4),
+                                   n * (rb_p + 4 * (qheads // heads)) + qheads * d * 2, "polar_logit_kernel",
+                                   ["polar_logits.hip", "tq_device.h"])
     return calls, work, cfg, n, extras
 
 

@@ -204,7 +204,9 @@ tq_status tq_attn_logits_workspace_size(const tq_params *p, int32_t batch, int32
  * GQA: query head h reads KV head h / (n_q_heads / n_kv_heads); n_q_heads
  * must be a multiple of n_kv_heads.  Dense logits support d in {64, 128,
  * 256}, up to 16 query heads per KV head, streams whose packed codes stay
- * under 2 GiB and whose logits (group x seq_len fp32) stay under 2 GiB;
+ * under 2 GiB and whose logits (group x seq_len fp32) stay under 2 GiB, in
+ * all three modes (polar keys: logit = scale * n * <Pi q, y_hat>, y_hat the
+ * unit vector the key's angle codes describe, "1단계");
  * top-k supports MSE mode, d in {64, 128, 256}, topk <= 16, seq_len < 2^30.
  * seq_len == 0 is a no-op.  A workspace smaller than the query's size, or
  * NULL where it is not 0, is TQ_ERR_INVALID; a misaligned one
