@@ -119,6 +119,7 @@ TRAFFIC_INSTANCES = {
     "attend_combine_kernel:attn_output": ("attend_combine_kernel<128>", _A),
     "quantize_polar_kernel:polar_quantize": ("quantize_polar_kernel<128, false>", _Q),
     "dequant_kernel:polar_dequantize": ("dequant_kernel<128, 1, false, false, true>", _D),
+    "polar_logit_kernel:polar_attn_logits": ("polar_logit_kernel<128, 4>", ["polar_logits.hip", "tq_device.h"]),
 }
 
 

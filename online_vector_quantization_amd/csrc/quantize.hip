@@ -16,8 +16,11 @@
 //   a persistent grid.
 // * Inputs are staged once per tile in LDS as fp16, scaled per vector by a
 //   power of two so the largest element sits in [2^14, 2^15); bf16 inputs
-//   are then exact, fp32 inputs are split into hi + lo.  The norm is
-//   accumulated in fp64 from the exact inputs and rounded once to fp16.
+//   are then exact, fp32 inputs are split into hi + lo.  The fp16 norm is
+//   the nearest-even rounding of the exact norm: fp64 sums of the exact
+//   squares, or (bf16 inputs in the one-kind kernels) fp32 sums of the
+//   staged squares with the exact fp64 sum taken only where the fp32 result
+//   cannot decide the rounding.
 // * y = X Pi^T runs on 32x32x16 fp16 MFMA (fp32 accumulate); the output tile
 //   has one coordinate per lane, so each boundary comparison is a single
 //   v_cmp whose 64-bit lane mask is a piece of the thermometer code; the
@@ -196,8 +199,11 @@ __device__ __forceinline__ void load_raw(const i32x4 &rx, int64_t n_vec, int64_t
 
 // Stages 16 elements of vector sv_v into an LDS tile (fp16, and fp16 lo for
 // fp32 inputs) after the per-vector power-of-two scale; every thread of
-// a vector writes 1 / (scale * 2^8 * |x|) to vinv.  Returns the fp16 norm.
-template <int D, bool IN_F32>
+// a vector writes 1 / (scale * 2^8 * |x|) to vinv.  Returns the fp16 norm,
+// the nearest-even rounding of the exact |x|.  FP32_SUMS (bf16 inputs):
+// sums of squares in fp32 with an exact fp64 fallback near fp16 midpoints,
+// else fp64 throughout.
+template <int D, bool IN_F32, bool FP32_SUMS = true>
 __device__ __forceinline__ uint16_t stage_vector(const RawInput<IN_F32> &r, _Float16 *xh, _Float16 *xl,
                                                  float *vinv, int sv_v, int sv_c) {
   using L = QLayout<D>;
@@ -217,14 +223,17 @@ __device__ __forceinline__ uint16_t stage_vector(const RawInput<IN_F32> &r, _Flo
         xv[8 * q + 2 * e + 1] = __uint_as_float(u & 0xFFFF0000u);
       }
   }
+  // fp32 inputs: the squares are not exact in fp32, so the sum of squares
+  // runs in fp64 from the start
+  constexpr bool F64 = IN_F32 || !FP32_SUMS;
   double ss = 0.0;
   float mx = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    ss = fma((double)xv[i], (double)xv[i], ss);
+    if constexpr (F64) ss = fma((double)xv[i], (double)xv[i], ss);
     mx = fmaxf(mx, fabsf(xv[i]));
   }
-  ss = lanes_sum<L::TPV>(ss);
+  if constexpr (F64) ss = lanes_sum<L::TPV>(ss);
   mx = lanes_max<L::TPV>(mx);
   // exponent of the largest element (frexp's is one above ilogb's; a zero
   // vector gets -1 and stays zero).  The scale 2^se can exceed the fp32
@@ -249,17 +258,56 @@ __device__ __forceinline__ uint16_t stage_vector(const RawInput<IN_F32> &r, _Flo
     dl[0] = lv[0];
     dl[1] = lv[1];
   }
-  // 1 / (sc * 2^8 * |x|), correctly rounded to fp32: the scaled sum of
-  // squares lies in [2^28, 2^37); v_rsq_f32 (about one ulp) is refined by one
-  // Newton step in fp64 (error ~2^-45) before the single rounding to fp32.
-  // The unit coordinates u = y * inv_n carry this rounding as a common
-  // factor, which enters the residual norm gamma one to one.
-  const double ss_sc = ldexp(ss, 2 * se);
-  const double r0 = (double)__builtin_amdgcn_rsqf((float)ss_sc);
-  const double r1 = fma(r0, fma(-0.5 * ss_sc, r0 * r0, 0.5), r0);
-  const float inv_n = ss > 0.0 ? (float)r1 * (1.0f / kPiScale) : 0.0f;
-  vinv[sv_v] = inv_n;        // the vector's threads all hold the same value
-  return f64_to_f16_bits(sqrt(ss));
+  if constexpr (F64) {
+    // 1 / (sc * 2^8 * |x|), correctly rounded to fp32: the scaled sum of
+    // squares lies in [2^28, 2^37); v_rsq_f32 (about one ulp) is refined by
+    // one Newton step in fp64 (error ~2^-45) before the single rounding.
+    const double ss_sc = ldexp(ss, 2 * se);
+    const double r0 = (double)__builtin_amdgcn_rsqf((float)ss_sc);
+    const double r1 = fma(r0, fma(-0.5 * ss_sc, r0 * r0, 0.5), r0);
+    vinv[sv_v] = ss > 0.0 ? (float)r1 * (1.0f / kPiScale) : 0.0f;   // the vector's threads all hold it
+    return f64_to_f16_bits(sqrt(ss));
+  } else {
+    // bf16 inputs: the staged fp16 values are the scaled inputs exactly
+    // (8 significant bits; only elements below 2^-28 of the largest, in the
+    // fp16 subnormal range, round), so their squares are exact in fp32 and
+    // the scaled sum of squares s2 in [2^28, 2^37) is formed with two-wide
+    // fp16 dot products in fp32: at most 19 roundings of partial sums no
+    // larger than s2, i.e. a relative error below 19 * 2^-24.
+    float s2 = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const half2 h2 = {hv[q][2 * i], hv[q][2 * i + 1]};
+        s2 = __builtin_amdgcn_fdot2(h2, h2, s2, false);
+      }
+    s2 = lanes_sum<L::TPV>(s2);
+    // 1 / (sc * 2^8 * |x|): v_rsq_f32 and one Newton step in fp32 (a common
+    // factor of the vector's unit coordinates; its error, about 2^-23
+    // relative, enters the residual norm gamma one to one)
+    const float r0 = __builtin_amdgcn_rsqf(s2);
+    const float r1 = fmaf(r0, fmaf(-0.5f * s2, r0 * r0, 0.5f), r0);
+    vinv[sv_v] = s2 > 0.0f ? r1 * (1.0f / kPiScale) : 0.0f;
+    // The scaled norm n32 = sqrt(s2) (v_sqrt_f32, one ulp) is within about
+    // 12.5 * 2^-24 of the exact one, so the exact norm lies between
+    // n32 (1 - 2^-19) and n32 (1 + 2^-19).  Where both ends round to the
+    // same fp16 (nearest even is monotone) that is the answer; otherwise
+    // (about 0.5% of vectors: the norm is near an fp16 midpoint) the wave
+    // forms the exact sum of squares in fp64 and rounds it once.
+    const float n32 = __builtin_amdgcn_sqrtf(s2);
+    const uint16_t lo16 = f32_to_f16_bits(ldexpf(n32 * (1.0f - 0x1p-19f), -se));
+    const uint16_t hi16 = f32_to_f16_bits(ldexpf(n32 * (1.0f + 0x1p-19f), -se));
+    uint16_t n16 = lo16;
+    if (__builtin_expect(__ballot(lo16 != hi16) != 0, 0)) {   // wave-uniform branch
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ss = fma((double)xv[i], (double)xv[i], ss);
+      ss = lanes_sum<L::TPV>(ss);
+      const uint16_t exact = f64_to_f16_bits(sqrt(ss));
+      n16 = lo16 == hi16 ? lo16 : exact;
+    }
+    return n16;
+  }
 }
 
 // y = X Pi^T for the wave's 32 columns of a staged tile (A fragments read
@@ -630,9 +678,12 @@ __global__ __launch_bounds__(3 * QLayout<D>::NT) void quantize_pc_kernel(tqi::Qu
   const int64_t t0 = blockIdx.x;
 
   RawInput<IN_F32> raw;
+  // The stage waves keep the fp64 sums of squares: with fp32 sums and the
+  // midpoint fallback this kernel measured 0.5 us slower (its stage waves
+  // are not what bounds it), the one-kind kernels about 2 us faster.
   if (kind == 2) {
     load_raw<IN_F32>(res.rx, a.n_vec, a.x_stride, t0, sv_v, sv_c, raw);
-    const uint16_t n16 = stage_vector<D, IN_F32>(raw, xh[0], xl[0], vinv[0], sv_v, sv_c);
+    const uint16_t n16 = stage_vector<D, IN_F32, false>(raw, xh[0], xl[0], vinv[0], sv_v, sv_c);
     buf_store_u16<kWriteBack>(res.rn, (sv_c == 0 && t0 * 32 + sv_v < a.n_vec) ? (uint32_t)(2 * (t0 * 32 + sv_v)) : kNoStore,
                               n16);
     load_raw<IN_F32>(res.rx, a.n_vec, a.x_stride, t0 + step, sv_v, sv_c, raw);
@@ -655,7 +706,7 @@ __global__ __launch_bounds__(3 * QLayout<D>::NT) void quantize_pc_kernel(tqi::Qu
     } else {
       // stage tile tp + step (zeros past the end), prefetch the one after
       const int64_t ts = tp + step;
-      const uint16_t n16 = stage_vector<D, IN_F32>(raw, xh[kb ^ 1], xl[IN_F32 ? kb ^ 1 : 0], vinv[(k + 1) & 3], sv_v, sv_c);
+      const uint16_t n16 = stage_vector<D, IN_F32, false>(raw, xh[kb ^ 1], xl[IN_F32 ? kb ^ 1 : 0], vinv[(k + 1) & 3], sv_v, sv_c);
       load_raw<IN_F32>(res.rx, a.n_vec, a.x_stride, ts + step, sv_v, sv_c, raw);
       __builtin_amdgcn_sched_barrier(0);
       buf_store_u16<kWriteBack>(res.rn, (sv_c == 0 && ts * 32 + sv_v < a.n_vec) ? (uint32_t)(2 * (ts * 32 + sv_v)) : kNoStore,
