@@ -376,6 +376,51 @@ def test_end_to_end_quantize_then_logits(tq):
     check_logits(out[:, same], want[:, same], 1 / np.sqrt(d), ref["norm"][same], q64)
 
 
+def _midpoint_rows(d):
+    """bf16 rows whose exact norms sit on or next to fp16 rounding midpoints.
+    (1, 2^-5, 2^-11) has |x|^2 = (1 + 2^-11)^2: exactly halfway between fp16
+    1 and 1 + 2^-10, so nearest-even gives 1 (0x3C00); one more element of
+    2^-20 lifts it past the midpoint (0x3C01) by 2^-41 relative, which an
+    fp32 sum of the squares loses and the fp64 sums keep.  (1, 2^-5 x 3, 2^-11 x 9) has
+    |x| = 1 + 3 * 2^-11, halfway between 1 + 2^-10 and 1 + 2^-9, so the tie goes
+    up to the even 0x3C02.  Each row also appears scaled by 2^-10 and 2^12
+    (exact in bf16, still fp16 normals; the exponent field moves by -10 and
+    +12).  Returns
+    the rows and the expected fp16 norm bits."""
+    base = []
+    r = np.zeros(d); r[0], r[1], r[2] = 1.0, 2.0 ** -5, 2.0 ** -11
+    base.append((r, 0x3C00))
+    r = r.copy(); r[3] = 2.0 ** -20
+    base.append((r, 0x3C01))
+    r = np.zeros(d); r[0] = 1.0; r[1:4] = 2.0 ** -5; r[4:13] = 2.0 ** -11
+    base.append((r, 0x3C02))
+    rows, want = [], []
+    for k in (0, -10, 12):
+        for r, bits in base:
+            rows.append(r * 2.0 ** k)
+            want.append(bits + (k << 10))
+    return np.array(rows), np.array(want, dtype=np.uint16)
+
+
+@pytest.mark.parametrize("d,mode", [(128, oqz.MODE_MSE), (128, oqz.MODE_PROD), (64, oqz.MODE_MSE), (256, oqz.MODE_PROD)])
+def test_norm_rounding_at_fp16_midpoints(tq, d, mode):
+    """The fp16 norm is the nearest-even rounding of the exact norm on exact
+    ties and just past them, wherever the kernel forms its sums of squares
+    (fp32 with an exact fallback in the one-kind kernels, fp64 in the split
+    key kernel); checked against the hand values and the oracle."""
+    x64, want = _midpoint_rows(d)
+    xb = bf16_bits(x64.astype(np.float32))
+    assert np.array_equal(bf16_to_f32(xb).astype(np.float64), x64)      # exact in bf16
+    ot = OracleTables(d, 3, mode)
+    ref = ot.quantize(x64)
+    assert np.array_equal(ref["norm"].view(np.uint16), want)
+    qz = tq.Quantizer(d, 3, mode, seed=0, device=DEV)
+    cache = qz.quantize(dev_bf16(xb, DEV))
+    torch.cuda.synchronize()
+    got = cache.norm.cpu().numpy().view(np.uint16)[:len(want)]
+    assert np.array_equal(got, want), (got, want)
+
+
 def test_empty_and_single(tq):
     qz = tq.Quantizer(128, 3, oqz.MODE_PROD, seed=0, device=DEV)
     cache = qz.new_cache(4)
