@@ -180,8 +180,9 @@ tq_status tq_quantize_kv(const tq_params *p, const void *x, int32_t x_dtype, int
  * device (the same validation as the call itself: an unsupported shape
  * returns TQ_ERR_UNSUPPORTED).  Dense logits need the query tables (A
  * operands and constants of every query: a few KB per (batch, kv head)
- * stream, independent of seq_len); top-k search needs its rotated queries
- * and partial lists.  The other logit calls (append, paged) take the dense
+ * stream, independent of seq_len; polar-format keys: the rotated queries and
+ * the cos/sin tables of the angle codebooks); top-k search needs its rotated
+ * queries and partial lists.  The other logit calls (append, paged) take the dense
  * size: this query with their batch, heads, seq_len (pos + 1) and topk = 0.
  * *bytes is 0 for empty calls.
  * Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED. */
